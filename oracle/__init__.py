@@ -1,0 +1,40 @@
+"""CPU oracle for the scaled FP8 GEMM: TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, float64 reference of what the GPU path computes: e4m3fn and E8M0
+decoding by table, round-to-nearest-even encoding by table search, per-tensor,
+row-wise and 32-element microscaled quantisation, the scaled GEMM with its
+error bound, and the grouped (mixture-of-experts) form.
+
+Only ``tests/``, the smoke check in ``__graft_entry__`` and the CPU-baseline
+leg of ``bench.py`` may import this package.  The library under
+``block_scaled_gemm_fp8gemm_amd`` never does, and this package imports nothing
+from it: the two share no code.
+
+Sources.  The pages behind this work name the formats but do not define them
+bit by bit: "E4M3" and "E5M2" (the JAX/Triton Blackwell FP8 GEMM post, second
+paragraph), the dtype ``torch.float8_e4m3fn`` (the Cutlass-named Triton FP8
+post, parameter list, precision settings) and MXFP8 micro-scaling
+("Hopper/Blackwell architecture features" §12.6.1, hardware table).  The bit
+layouts therefore follow the public standards those names refer to: the OCP
+8-bit floating point specification (OFP8, E4M3 with no infinities, one NaN
+pattern per sign, max 448) and the OCP Microscaling (MX) formats
+specification v1.0 (E8M0 shared scale, 32-element blocks, scale exponent =
+floor(log2(amax)) - emax of the element format).
+
+Parity pins.  Every function here is pinned by ``tests/test_oracle_*.py``
+against exhaustive enumeration, exact rational arithmetic, integer-exact
+products, closed forms or the specifications' tabulated points
+(``tests/golden/``).  No function is "parity unpinned".
+"""
+from .formats import (E4M3_DECODE, E4M3_MAX, E8M0_DECODE, decode_e4m3, decode_e8m0,
+                      encode_e4m3)
+from .quant import quantize, quantize_mx, quantize_rowwise, quantize_tensor
+from .gemm import (dequantize, gemm_reference, grouped_reference, output_ulp, tolerance,
+                   within_bound, round_to_output)
+
+__all__ = [
+    "E4M3_DECODE", "E4M3_MAX", "E8M0_DECODE", "decode_e4m3", "decode_e8m0", "encode_e4m3",
+    "quantize", "quantize_mx", "quantize_rowwise", "quantize_tensor",
+    "dequantize", "gemm_reference", "grouped_reference", "output_ulp", "tolerance",
+    "within_bound", "round_to_output",
+]
