@@ -1,0 +1,255 @@
+"""Python binding of libfp8gemm: the MI355X (gfx950) scaled FP8 GEMM library.
+
+Two layers, both argument marshalling only (every step of the computation runs
+in the library's HIP kernels; there is no fallback):
+
+* ``fp8gemm_quantize``, ``fp8gemm_run``, ``fp8gemm_grouped_run`` and the
+  workspace-size queries mirror the C ABI in ``include/fp8gemm.h`` one to one:
+  device pointers and sizes as Python ints, a non-success status raises
+  :class:`Fp8GemmError`.
+* ``quantize``, ``gemm`` and ``grouped_gemm`` take PyTorch CUDA tensors
+  (PyTorch supplies device memory and the current stream), allocate the outputs
+  and call the ABI functions.
+
+Layouts: A is row-major [M, K]; B is column-major [K, N], passed as its
+[N, K] row-major transpose; C is row-major [M, N].  Operand codes are OCP
+e4m3fn bytes held in ``torch.uint8`` tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = [
+    "Fp8GemmError", "SCALE_MODES", "OUT_DTYPES", "library_path", "load_library",
+    "fp8gemm_quantize_workspace_size", "fp8gemm_quantize", "fp8gemm_workspace_size",
+    "fp8gemm_run", "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run",
+    "fp8gemm_status_string", "fp8gemm_version", "quantize", "gemm", "grouped_gemm",
+    "exported_symbols",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "fp8gemm.h")
+
+SCALE_MODES = {"tensor": 0, "rowwise": 1, "mx32": 2}
+OUT_DTYPES = {"f16": 0, "bf16": 1}
+
+_STATUS_NAMES = {
+    0: "FP8GEMM_SUCCESS", 1: "FP8GEMM_ERROR_INVALID_VALUE", 2: "FP8GEMM_ERROR_MISALIGNED",
+    3: "FP8GEMM_ERROR_NOT_SUPPORTED", 4: "FP8GEMM_ERROR_WORKSPACE", 5: "FP8GEMM_ERROR_LAUNCH",
+}
+
+
+class Fp8GemmError(RuntimeError):
+    """A libfp8gemm call returned a non-success status."""
+
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func} failed: {_STATUS_NAMES.get(status, status)}")
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libfp8gemm.so")
+
+
+_lib = None
+
+_i64, _i32, _sz, _p, _int = (ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p,
+                             ctypes.c_int)
+
+_SIGNATURES = {
+    "fp8gemm_quantize_workspace_size": (_sz, [_i64, _i64, _int]),
+    "fp8gemm_quantize": (_int, [_p, _i64, _i64, _i64, _int, _p, _i64, _p, _p, _sz, _p]),
+    "fp8gemm_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
+    "fp8gemm_run": (_int, [_i64, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _p, _p, _i64, _int,
+                           _p, _sz, _p]),
+    "fp8gemm_grouped_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _int]),
+    "fp8gemm_grouped_run": (_int, [_i32, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _i64, _int,
+                                   _p, _p, _p, _i64, _int, _p, _sz, _p]),
+    "fp8gemm_status_string": (ctypes.c_char_p, [_int]),
+    "fp8gemm_version": (_int, []),
+}
+
+
+def load_library():
+    """Load libfp8gemm.so from this package directory (built in-tree).
+
+    Raises RuntimeError when it has not been built: there is no other path.
+    """
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m block_scaled_gemm_fp8gemm_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def exported_symbols() -> list:
+    """Function names declared in include/fp8gemm.h."""
+    with open(_HEADER) as fh:
+        text = fh.read()
+    return re.findall(r"^\s*(?:size_t|fp8gemm_status|const char\*|int)\s+(fp8gemm_\w+)\s*\(",
+                      text, flags=re.M)
+
+
+def _check(name: str, status: int):
+    if status != 0:
+        raise Fp8GemmError(name, status)
+
+
+# ---- one-to-one ABI mirrors -------------------------------------------------
+def fp8gemm_quantize_workspace_size(rows: int, k: int, mode: int) -> int:
+    return load_library().fp8gemm_quantize_workspace_size(rows, k, mode)
+
+
+def fp8gemm_quantize(x: int, rows: int, k: int, ldx: int, mode: int, q: int, ldq: int,
+                     scales: int, workspace: int, workspace_bytes: int, stream: int) -> None:
+    _check("fp8gemm_quantize", load_library().fp8gemm_quantize(
+        x, rows, k, ldx, mode, q, ldq, scales, workspace, workspace_bytes, stream))
+
+
+def fp8gemm_workspace_size(M: int, N: int, K: int, mode: int) -> int:
+    return load_library().fp8gemm_workspace_size(M, N, K, mode)
+
+
+def fp8gemm_run(M: int, N: int, K: int, A: int, lda: int, B: int, ldb: int, mode: int,
+                scale_a: int, scale_b: int, C: int, ldc: int, out_dtype: int, workspace: int,
+                workspace_bytes: int, stream: int) -> None:
+    _check("fp8gemm_run", load_library().fp8gemm_run(
+        M, N, K, A, lda, B, ldb, mode, scale_a, scale_b, C, ldc, out_dtype, workspace,
+        workspace_bytes, stream))
+
+
+def fp8gemm_grouped_workspace_size(num_groups: int, total_m: int, N: int, K: int,
+                                   mode: int) -> int:
+    return load_library().fp8gemm_grouped_workspace_size(num_groups, total_m, N, K, mode)
+
+
+def fp8gemm_grouped_run(num_groups: int, total_m: int, N: int, K: int, A: int, lda: int,
+                        offsets: int, B: int, ldb: int, stride_b: int, mode: int, scale_a: int,
+                        scale_b: int, C: int, ldc: int, out_dtype: int, workspace: int,
+                        workspace_bytes: int, stream: int) -> None:
+    _check("fp8gemm_grouped_run", load_library().fp8gemm_grouped_run(
+        num_groups, total_m, N, K, A, lda, offsets, B, ldb, stride_b, mode, scale_a, scale_b, C,
+        ldc, out_dtype, workspace, workspace_bytes, stream))
+
+
+def fp8gemm_status_string(status: int) -> str:
+    return load_library().fp8gemm_status_string(status).decode()
+
+
+def fp8gemm_version() -> int:
+    return load_library().fp8gemm_version()
+
+
+# ---- PyTorch conveniences ---------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_cuda(t, name, dtype=None, dim=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must be {dim}-D")
+    if t.dim() and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dimension")
+
+
+def _ptr(t) -> int:
+    return t.data_ptr() if t is not None else 0
+
+
+def quantize(x, mode: str = "tensor", out=None, scales=None, workspace=None):
+    """fp32 [R, K] CUDA tensor -> (codes uint8 [R, K], scales).
+
+    scales: float32 [1] (tensor), float32 [R] (rowwise) or uint8 [R, K/32] (mx32).
+    """
+    torch = _torch()
+    _require_cuda(x, "x", torch.float32, 2)
+    m = SCALE_MODES[mode]
+    R, K = x.shape
+    if out is None:
+        ldq = (K + 15) // 16 * 16
+        out = torch.empty((R, ldq), dtype=torch.uint8, device=x.device)[:, :K]
+    if scales is None:
+        if mode == "tensor":
+            scales = torch.empty(1, dtype=torch.float32, device=x.device)
+        elif mode == "rowwise":
+            scales = torch.empty(R, dtype=torch.float32, device=x.device)
+        else:
+            scales = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+    need = fp8gemm_quantize_workspace_size(R, K, m)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    fp8gemm_quantize(_ptr(x), R, K, x.stride(0), m, _ptr(out), out.stride(0), _ptr(scales),
+                     _ptr(workspace) if need else 0, workspace.numel() if need else 0,
+                     _stream_handle(x.device))
+    return out, scales
+
+
+def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None,
+         workspace=None):
+    """C [M, N] = dq(qa [M, K]) @ dq(qb [N, K])^T, returned as fp16 / bf16."""
+    torch = _torch()
+    _require_cuda(qa, "qa", torch.uint8, 2)
+    _require_cuda(qb, "qb", torch.uint8, 2)
+    M, K = qa.shape
+    N, Kb = qb.shape
+    if K != Kb:
+        raise ValueError("qa and qb must share K")
+    tdt = torch.float16 if out_dtype == "f16" else torch.bfloat16
+    if out is None:
+        ldc = (N + 7) // 8 * 8
+        out = torch.empty((M, ldc), dtype=tdt, device=qa.device)[:, :N]
+    m = SCALE_MODES[mode]
+    need = fp8gemm_workspace_size(M, N, K, m)
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=qa.device)
+    fp8gemm_run(M, N, K, _ptr(qa), qa.stride(0), _ptr(qb), qb.stride(0), m, _ptr(sa), _ptr(sb),
+                _ptr(out), out.stride(0), OUT_DTYPES[out_dtype],
+                _ptr(workspace) if need else 0, workspace.numel() if need else 0,
+                _stream_handle(qa.device))
+    return out
+
+
+def grouped_gemm(qa, sa, offsets, qb, sb, mode: str = "rowwise", out_dtype: str = "bf16",
+                 out=None, workspace=None):
+    """Grouped GEMM: rows [offsets[g], offsets[g+1]) of qa use expert qb[g] ([G, N, K])."""
+    torch = _torch()
+    _require_cuda(qa, "qa", torch.uint8, 2)
+    _require_cuda(qb, "qb", torch.uint8, 3)
+    _require_cuda(offsets, "offsets", torch.int32, 1)
+    total_m, K = qa.shape
+    G, N, Kb = qb.shape
+    if K != Kb or offsets.numel() != G + 1:
+        raise ValueError("shape mismatch between qa, qb and offsets")
+    tdt = torch.float16 if out_dtype == "f16" else torch.bfloat16
+    if out is None:
+        ldc = (N + 7) // 8 * 8
+        out = torch.empty((total_m, ldc), dtype=tdt, device=qa.device)[:, :N]
+    m = SCALE_MODES[mode]
+    need = fp8gemm_grouped_workspace_size(G, total_m, N, K, m)
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=qa.device)
+    fp8gemm_grouped_run(G, total_m, N, K, _ptr(qa), qa.stride(0), _ptr(offsets), _ptr(qb),
+                        qb.stride(1), qb.stride(0), m, _ptr(sa), _ptr(sb), _ptr(out),
+                        out.stride(0), OUT_DTYPES[out_dtype], _ptr(workspace) if need else 0,
+                        workspace.numel() if need else 0, _stream_handle(qa.device))
+    return out

@@ -1,0 +1,195 @@
+// C ABI of the scaled FP8 GEMM library: argument validation and kernel dispatch.
+//
+// Every check runs on the host before the first HIP call, so an invalid call
+// returns its status without touching the device (this is also what lets the
+// error paths be tested on machines without a GPU).  The rules follow the
+// descriptor constraints of "Hopper/Blackwell architecture features" §12.2.3
+// (16-byte aligned base, unit stride in the last dimension, other strides a
+// multiple of 16 bytes): here they are requirements of the 16-byte vector and
+// direct-to-LDS loads, and a violation is an error rather than a slow path.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp8gemm.h"
+#include "launch.h"
+
+namespace {
+
+using fp8gemm::kMx32;
+using fp8gemm::kRowwise;
+using fp8gemm::kTensor;
+
+constexpr int64_t kMaxDim = INT32_MAX;
+constexpr int kMaxGroups = 1024;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_mode(int mode) { return mode == kTensor || mode == kRowwise || mode == kMx32; }
+bool valid_out(int out) { return out == FP8GEMM_OUT_F16 || out == FP8GEMM_OUT_BF16; }
+
+fp8gemm_status from_hip(hipError_t e) {
+  return e == hipSuccess ? FP8GEMM_SUCCESS : FP8GEMM_ERROR_LAUNCH;
+}
+
+// Checks shared by the dense and grouped GEMM (M is the number of A rows).
+fp8gemm_status check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                 const uint8_t* B, int64_t ldb, int mode, const void* scale_a,
+                                 const void* scale_b, const void* C, int64_t ldc, int out) {
+  if (!A || !B || !C || !scale_a || !scale_b) return FP8GEMM_ERROR_INVALID_VALUE;
+  if (lda < K || ldb < K || ldc < N) return FP8GEMM_ERROR_INVALID_VALUE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim || lda > kMaxDim || ldb > kMaxDim ||
+      ldc > kMaxDim)
+    return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if (K % 16 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if (mode == kMx32 && K % 32 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  // the grid is one workgroup per 128 x 128 tile at most: keep it below 2^31
+  if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16)) return FP8GEMM_ERROR_MISALIGNED;
+  if (lda % 16 != 0 || ldb % 16 != 0 || (ldc * 2) % 16 != 0) return FP8GEMM_ERROR_MISALIGNED;
+  if (!aligned(scale_a, 4) || !aligned(scale_b, 4)) return FP8GEMM_ERROR_MISALIGNED;
+  (void)out;
+  return FP8GEMM_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fp8gemm_quantize_workspace_size(int64_t rows, int64_t k, int mode) {
+  (void)rows;
+  (void)k;
+  return mode == kTensor ? sizeof(float) * fp8gemm::kQuantPartials : 0;
+}
+
+fp8gemm_status fp8gemm_quantize(const float* x, int64_t rows, int64_t k, int64_t ldx, int mode,
+                                uint8_t* q, int64_t ldq, void* scales, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!valid_mode(mode) || rows < 0 || k <= 0) return FP8GEMM_ERROR_INVALID_VALUE;
+  if (rows == 0) return FP8GEMM_SUCCESS;
+  if (!x || !q || !scales) return FP8GEMM_ERROR_INVALID_VALUE;
+  if (ldx < k || ldq < k) return FP8GEMM_ERROR_INVALID_VALUE;
+  if (k % 16 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if (mode == kMx32 && k % 32 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  // 32-bit unit indexing inside the kernels: at most 2^32 - 1 elements per call
+  if (rows > kMaxDim || ldx > kMaxDim || ldq > kMaxDim || rows * k >= (int64_t(1) << 32))
+    return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 16)) return FP8GEMM_ERROR_MISALIGNED;
+  if ((ldx * 4) % 16 != 0 || ldq % 16 != 0) return FP8GEMM_ERROR_MISALIGNED;
+  if (mode != kMx32 && !aligned(scales, 4)) return FP8GEMM_ERROR_MISALIGNED;
+  const size_t need = fp8gemm_quantize_workspace_size(rows, k, mode);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4)))
+    return FP8GEMM_ERROR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mode == kTensor)
+    return from_hip(fp8gemm::launch_quantize_tensor(x, rows, k, ldx, q, ldq,
+                                                    static_cast<float*>(scales),
+                                                    static_cast<float*>(workspace), s));
+  if (mode == kRowwise)
+    return from_hip(fp8gemm::launch_quantize_rowwise(x, rows, k, ldx, q, ldq,
+                                                     static_cast<float*>(scales), s));
+  return from_hip(
+      fp8gemm::launch_quantize_mx(x, rows, k, ldx, q, ldq, static_cast<uint8_t*>(scales), s));
+}
+
+size_t fp8gemm_workspace_size(int64_t M, int64_t N, int64_t K, int mode) {
+  (void)M;
+  (void)N;
+  (void)K;
+  (void)mode;
+  return 0;
+}
+
+fp8gemm_status fp8gemm_run(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                           const uint8_t* B, int64_t ldb, int mode, const void* scale_a,
+                           const void* scale_b, void* C, int64_t ldc, int out_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_mode(mode) || !valid_out(out_dtype) || M < 0 || N < 0 || K <= 0)
+    return FP8GEMM_ERROR_INVALID_VALUE;
+  if (M == 0 || N == 0) return FP8GEMM_SUCCESS;
+  fp8gemm_status st =
+      check_gemm_common(M, N, K, A, lda, B, ldb, mode, scale_a, scale_b, C, ldc, out_dtype);
+  if (st != FP8GEMM_SUCCESS) return st;
+  const size_t need = fp8gemm_workspace_size(M, N, K, mode);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FP8GEMM_ERROR_WORKSPACE;
+
+  fp8gemm::GemmProblem p;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.A = A;
+  p.lda = lda;
+  p.B = B;
+  p.ldb = ldb;
+  p.scale_a = scale_a;
+  p.scale_b = scale_b;
+  p.C = C;
+  p.ldc = ldc;
+  return from_hip(fp8gemm::launch_gemm(p, mode, out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t fp8gemm_grouped_workspace_size(int32_t num_groups, int64_t total_m, int64_t N, int64_t K,
+                                      int mode) {
+  (void)num_groups;
+  (void)total_m;
+  (void)N;
+  (void)K;
+  (void)mode;
+  return 0;
+}
+
+fp8gemm_status fp8gemm_grouped_run(int32_t num_groups, int64_t total_m, int64_t N, int64_t K,
+                                   const uint8_t* A, int64_t lda, const int32_t* offsets,
+                                   const uint8_t* B, int64_t ldb, int64_t stride_b, int mode,
+                                   const void* scale_a, const void* scale_b, void* C,
+                                   int64_t ldc, int out_dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!valid_mode(mode) || !valid_out(out_dtype) || num_groups < 1 || total_m < 0 || N < 0 ||
+      K <= 0)
+    return FP8GEMM_ERROR_INVALID_VALUE;
+  if (num_groups > kMaxGroups) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if (total_m == 0 || N == 0) return FP8GEMM_SUCCESS;
+  if (!offsets) return FP8GEMM_ERROR_INVALID_VALUE;
+  fp8gemm_status st = check_gemm_common(total_m, N, K, A, lda, B, ldb, mode, scale_a, scale_b, C,
+                                        ldc, out_dtype);
+  if (st != FP8GEMM_SUCCESS) return st;
+  if (stride_b < N * ldb) return FP8GEMM_ERROR_INVALID_VALUE;
+  if (stride_b % 16 != 0) return FP8GEMM_ERROR_MISALIGNED;
+  if (!aligned(offsets, 4)) return FP8GEMM_ERROR_MISALIGNED;
+  const size_t need = fp8gemm_grouped_workspace_size(num_groups, total_m, N, K, mode);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FP8GEMM_ERROR_WORKSPACE;
+
+  fp8gemm::GroupedProblem p;
+  p.groups = num_groups;
+  p.total_m = (int)total_m;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.A = A;
+  p.lda = lda;
+  p.offsets = offsets;
+  p.B = B;
+  p.ldb = ldb;
+  p.stride_b = stride_b;
+  p.scale_a = scale_a;
+  p.scale_b = scale_b;
+  p.C = C;
+  p.ldc = ldc;
+  return from_hip(
+      fp8gemm::launch_grouped_gemm(p, mode, out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+const char* fp8gemm_status_string(int status) {
+  switch (status) {
+    case FP8GEMM_SUCCESS: return "FP8GEMM_SUCCESS";
+    case FP8GEMM_ERROR_INVALID_VALUE: return "FP8GEMM_ERROR_INVALID_VALUE";
+    case FP8GEMM_ERROR_MISALIGNED: return "FP8GEMM_ERROR_MISALIGNED";
+    case FP8GEMM_ERROR_NOT_SUPPORTED: return "FP8GEMM_ERROR_NOT_SUPPORTED";
+    case FP8GEMM_ERROR_WORKSPACE: return "FP8GEMM_ERROR_WORKSPACE";
+    case FP8GEMM_ERROR_LAUNCH: return "FP8GEMM_ERROR_LAUNCH";
+    default: return "FP8GEMM_ERROR_UNKNOWN";
+  }
+}
+
+int fp8gemm_version(void) { return FP8GEMM_VERSION; }
+
+}  // extern "C"

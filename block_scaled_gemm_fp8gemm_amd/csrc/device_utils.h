@@ -1,0 +1,77 @@
+// Device helpers shared by the gfx950 kernels of the scaled FP8 GEMM library.
+//
+// Format facts used here (OCP OFP8 E4M3 "fn", the operand format the JAX/Triton
+// Blackwell FP8 GEMM post prefers; OCP MX v1.0 E8M0 for the MXFP8 scales named in
+// "Hopper/Blackwell architecture features" §12.6.1):
+//   * e4m3fn has no infinity; its largest finite magnitude is 448.
+//   * gfx950's v_cvt_pk_fp8_f32 rounds to nearest even onto OCP e4m3fn, including
+//     subnormals and ties, but turns magnitudes above 464 into NaN, so every value
+//     is clamped to [-448, 448] first (448 is what round-then-saturate gives).
+//   * E8M0 code c encodes 2^(c-127).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8gemm {
+
+constexpr float kE4M3Max = 448.0f;
+
+__device__ __forceinline__ float clamp448(float v) {
+  return fminf(fmaxf(v, -kE4M3Max), kE4M3Max);
+}
+
+// Four fp32 values -> four e4m3fn codes packed little-endian into 32 bits
+// (round to nearest even, saturating, sign of zero kept).
+__device__ __forceinline__ uint32_t encode4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
+  return (uint32_t)w;
+}
+
+// E8M0 code of a 32-element block from its largest magnitude: floor(log2 amax)
+// read from the binary32 exponent field, minus 8 (the largest e4m3 exponent),
+// biased by 127 and clamped to [0, 254]; an all-zero block gets 127.
+__device__ __forceinline__ uint32_t mx_code_from_amax(float amax) {
+  if (amax == 0.0f) return 127u;
+  int ef = (int)(__float_as_uint(amax) >> 23);  // amax >= 0: no sign bit
+  int code = ef - 8;
+  return (uint32_t)(code < 0 ? 0 : code);
+}
+
+// Largest value over the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Largest value over the `width` lanes of an aligned lane group (width <= 64).
+__device__ __forceinline__ float group_max(float v, int width) {
+  for (int off = width >> 1; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// fp32 -> output element, round to nearest even.
+template <typename OutT>
+__device__ __forceinline__ OutT to_out(float v);
+
+template <>
+__device__ __forceinline__ _Float16 to_out<_Float16>(float v) {
+  return (_Float16)v;
+}
+template <>
+__device__ __forceinline__ __bf16 to_out<__bf16>(float v) {
+  return (__bf16)v;
+}
+
+// Four consecutive outputs packed into 8 bytes.
+template <typename OutT>
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  OutT o[4] = {to_out<OutT>(a), to_out<OutT>(b), to_out<OutT>(c), to_out<OutT>(d)};
+  uint2 r;
+  __builtin_memcpy(&r, o, 8);
+  return r;
+}
+
+}  // namespace fp8gemm

@@ -1,0 +1,53 @@
+// Internal launch entry points of the gfx950 kernels (host side).  Arguments are
+// validated by the C ABI layer (api.cpp) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8gemm {
+
+// Per-tensor quantisation keeps one partial maximum per workgroup of its first pass.
+constexpr int kQuantPartials = 1024;
+
+hipError_t launch_quantize_tensor(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
+                                  int64_t ldq, float* scale, float* partials, hipStream_t stream);
+hipError_t launch_quantize_rowwise(const float* x, int64_t rows, int64_t k, int64_t ldx,
+                                   uint8_t* q, int64_t ldq, float* scales, hipStream_t stream);
+hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
+                              int64_t ldq, uint8_t* codes, hipStream_t stream);
+
+enum ScaleMode : int { kTensor = 0, kRowwise = 1, kMx32 = 2 };
+enum OutType : int { kF16 = 0, kBF16 = 1 };
+
+struct GemmProblem {
+  int M, N, K;
+  const uint8_t* A;
+  int64_t lda;
+  const uint8_t* B;
+  int64_t ldb;
+  const void* scale_a;
+  const void* scale_b;
+  void* C;
+  int64_t ldc;
+};
+
+hipError_t launch_gemm(const GemmProblem& p, int mode, int out, hipStream_t stream);
+
+struct GroupedProblem {
+  int groups;
+  int total_m, N, K;
+  const uint8_t* A;
+  int64_t lda;
+  const int32_t* offsets;
+  const uint8_t* B;
+  int64_t ldb, stride_b;
+  const void* scale_a;
+  const void* scale_b;
+  void* C;
+  int64_t ldc;
+};
+
+hipError_t launch_grouped_gemm(const GroupedProblem& p, int mode, int out, hipStream_t stream);
+
+}  // namespace fp8gemm

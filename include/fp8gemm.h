@@ -1,0 +1,158 @@
+/*
+ * fp8gemm.h - C ABI of the MI355X (gfx950) scaled FP8 GEMM library.
+ *
+ * The library computes C = (sA . A_e4m3)(sB . B_e4m3) with fp32 accumulation and
+ * an fp16 / bf16 epilogue, for per-tensor, row-wise and 32-element microscaled
+ * (MX, E8M0 block-scale) operands, and the grouped (mixture-of-experts) form.
+ *
+ * Sources: the kernels in "Hopper/Blackwell architecture features" §12.7.1 and
+ * §12.7.2 take raw pointers, sizes and strides, accumulate into an fp32 tile and
+ * cast it on store; the JAX/Triton Blackwell FP8 GEMM post's kernel pseudocode
+ * does the same with E4M3 operands and an fp16 result, and its MoE paragraph
+ * extends the GEMM to grouped experts.  §12.2.3 of the first page requires 16-byte
+ * aligned bases and row strides (16-byte multiples, unit stride in the last
+ * dimension); §12.4.3 treats a resource overflow as an error; the Cutlass-named
+ * Triton FP8 post's monitoring list asks for launch errors to be checked.
+ *
+ * Conventions for every entry point
+ *   - All data pointers are DEVICE pointers (HIP device memory of the current
+ *     device).  Sizes and strides are host integers.  `stream` is a hipStream_t
+ *     (NULL = the default stream).
+ *   - Calls are asynchronous on `stream`: they validate their arguments on the
+ *     host, enqueue kernels and return.  The library never allocates, frees or
+ *     synchronizes, and keeps no state between calls.  The caller owns every
+ *     buffer and must keep it alive until the enqueued work completes.
+ *   - Validation runs before any HIP call; a non-SUCCESS status means nothing
+ *     was enqueued (except FP8GEMM_ERROR_LAUNCH, which reports a failed launch).
+ *   - A is row-major [M,K] (element (m,k) at A[m*lda+k]).  B is column-major
+ *     [K,N], i.e. stored as N rows of K contiguous bytes (element (k,n) at
+ *     B[n*ldb+k]).  C is row-major [M,N] (element (m,n) at C[m*ldc+n]).
+ *   - Operand codes are OCP e4m3fn bytes (bias 7, no infinity, NaN = S.1111.111,
+ *     max 448).  E8M0 scale codes encode 2^(code-127); 0xFF (NaN) is never
+ *     produced by fp8gemm_quantize.
+ *   - Inputs are expected finite; NaN/Inf inputs give unspecified results.
+ *   - Thread safety: calls from several host threads are safe; calls whose
+ *     buffers overlap must be ordered by the caller.
+ */
+#ifndef FP8GEMM_H_
+#define FP8GEMM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8GEMM_VERSION 100 /* 1.0.0 */
+
+typedef enum fp8gemm_status {
+  FP8GEMM_SUCCESS = 0,
+  FP8GEMM_ERROR_INVALID_VALUE = 1, /* null pointer, negative size, ld too small, bad enum */
+  FP8GEMM_ERROR_MISALIGNED = 2,    /* pointer or row pitch (bytes) not a multiple of 16   */
+  FP8GEMM_ERROR_NOT_SUPPORTED = 3, /* K not a multiple of 16 (32 for MX), or mode not offered */
+  FP8GEMM_ERROR_WORKSPACE = 4,     /* workspace missing or smaller than the size query    */
+  FP8GEMM_ERROR_LAUNCH = 5         /* a kernel launch failed (hipGetLastError)            */
+} fp8gemm_status;
+
+typedef enum fp8gemm_scale_mode {
+  FP8GEMM_SCALE_TENSOR = 0,  /* one fp32 scale per operand                         */
+  FP8GEMM_SCALE_ROWWISE = 1, /* fp32 scale per row of A / per column of B           */
+  FP8GEMM_SCALE_MX32 = 2     /* E8M0 scale per 32 contiguous K elements (MXFP8)     */
+} fp8gemm_scale_mode;
+
+typedef enum fp8gemm_out_dtype {
+  FP8GEMM_OUT_F16 = 0, /* IEEE binary16, round to nearest even */
+  FP8GEMM_OUT_BF16 = 1 /* bfloat16, round to nearest even      */
+} fp8gemm_out_dtype;
+
+/* ------------------------------------------------------------------------- */
+/* Quantisation: fp32 -> e4m3fn codes + scales.                                */
+/*                                                                           */
+/* Computes the scale and codes the JAX/Triton Blackwell FP8 GEMM post asks for  */
+/* (E4M3 operands with per-block scale factors, fine-grained against            */
+/* underflow) under these rules:                                              */
+/*   TENSOR : amax over all rows*k elements, s = fl32(amax/448) (1 if amax=0),   */
+/*            q = RNE_sat(fl32(x/s)); scales -> float[1].                        */
+/*   ROWWISE: the same per row (reduction over k); scales -> float[rows].        */
+/*            Quantise A with rows=M; quantise a column-major B with rows=N, so */
+/*            this gives one scale per column of B.                             */
+/*   MX32   : per (row, 32-element block): e = floor(log2 amax) - 8, code =     */
+/*            clamp(e+127, 0, 254) (127 if amax = 0), q = RNE_sat(x * 2^-e);    */
+/*            scales -> uint8 [rows][k/32], row-major, k/32 bytes per row.     */
+/* RNE_sat rounds to the nearest e4m3fn value, ties to even, and saturates to   */
+/* +-448; the sign of zero is kept.  Results are bit-exact (deterministic).     */
+/*                                                                           */
+/* x      : device fp32, element (r,i) at x[r*ldx+i]; ldx >= k, ldx*4 % 16 == 0.  */
+/* q      : device uint8 codes, element (r,i) at q[r*ldq+i]; ldq >= k, ldq % 16 == 0.*/
+/* k      : > 0, multiple of 16 (of 32 for MX32).  rows >= 0 (0: no work).       */
+/* workspace: device memory of fp8gemm_quantize_workspace_size() bytes, 16-byte  */
+/*          aligned (NULL allowed when the size is 0).  Contents are scratch.    */
+/* Errors : INVALID_VALUE, MISALIGNED, NOT_SUPPORTED, WORKSPACE, LAUNCH.        */
+/* ------------------------------------------------------------------------- */
+size_t fp8gemm_quantize_workspace_size(int64_t rows, int64_t k, int mode);
+
+fp8gemm_status fp8gemm_quantize(const float* x, int64_t rows, int64_t k, int64_t ldx, int mode,
+                                uint8_t* q, int64_t ldq, void* scales, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Dense scaled GEMM: C[m,n] = cast( sum_k dq_a(m,k) * dq_b(k,n) ).             */
+/*                                                                           */
+/* The tiled fp32-accumulating GEMM of "Hopper/Blackwell architecture features"  */
+/* §12.7 with FP8 operands and the scale applied in the epilogue (TENSOR,      */
+/* ROWWISE) or inside the matrix instruction per 32-K block (MX32).             */
+/*   TENSOR : scale_a, scale_b -> device float[1] each.                         */
+/*   ROWWISE: scale_a -> device float[M], scale_b -> device float[N].          */
+/*   MX32   : scale_a -> device uint8 [M][K/32], scale_b -> uint8 [N][K/32].   */
+/* M, N >= 0 (either 0: SUCCESS, nothing enqueued).  K > 0, multiple of 16     */
+/* (32 for MX32).  lda, ldb >= K and multiples of 16; ldc >= N with ldc*2 a     */
+/* multiple of 16; A, B, C 16-byte aligned; scale arrays 4-byte aligned.        */
+/* workspace: fp8gemm_workspace_size() bytes (may be 0 -> NULL allowed); it must */
+/* be zero-filled before its first use and is left zero-filled by every call.   */
+/* Accuracy: |C - C_ref| <= 1e-3 * sum_k|dq_a*dq_b| + 1 ulp of the output type. */
+/* ------------------------------------------------------------------------- */
+size_t fp8gemm_workspace_size(int64_t M, int64_t N, int64_t K, int mode);
+
+fp8gemm_status fp8gemm_run(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                           const uint8_t* B, int64_t ldb, int mode, const void* scale_a,
+                           const void* scale_b, void* C, int64_t ldc, int out_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Grouped (mixture-of-experts) GEMM, the grouped form in the MoE paragraph of   */
+/* the JAX/Triton Blackwell FP8 GEMM post: rows of A are sorted by expert and    */
+/* expert g owns rows [offsets[g], offsets[g+1]):                               */
+/*   C[m,:] = cast( dq_a(m,:) . dq_{B_g} )  for offsets[g] <= m < offsets[g+1]. */
+/* offsets: DEVICE int32[num_groups+1], offsets[0] = 0, non-decreasing,          */
+/*          offsets[num_groups] = total_m.  The host never reads it (no sync);   */
+/*          rows outside [0, total_m) are never touched, but values violating    */
+/*          these rules give unspecified C.  Empty experts are allowed.          */
+/* B_g = B + g*stride_b (column-major N x K per expert, ldb >= K), stride_b >=   */
+/*          N*ldb and a multiple of 16.                                         */
+/*   TENSOR : scale_a float[1], scale_b float[num_groups].                      */
+/*   ROWWISE: scale_a float[total_m], scale_b float[num_groups*N] (expert-major).*/
+/*   MX32   : scale_a uint8 [total_m][K/32], scale_b uint8 [num_groups][N][K/32]. */
+/* num_groups >= 1, total_m >= 0, other rules as fp8gemm_run.                   */
+/* ------------------------------------------------------------------------- */
+size_t fp8gemm_grouped_workspace_size(int32_t num_groups, int64_t total_m, int64_t N, int64_t K,
+                                      int mode);
+
+fp8gemm_status fp8gemm_grouped_run(int32_t num_groups, int64_t total_m, int64_t N, int64_t K,
+                                   const uint8_t* A, int64_t lda, const int32_t* offsets,
+                                   const uint8_t* B, int64_t ldb, int64_t stride_b, int mode,
+                                   const void* scale_a, const void* scale_b, void* C,
+                                   int64_t ldc, int out_dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fp8gemm_status_string(int status);
+
+/* FP8GEMM_VERSION of the built library. */
+int fp8gemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8GEMM_H_ */

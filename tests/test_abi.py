@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments with the documented status
+before making any HIP call (so no device is touched).
+
+Fake device addresses below are never dereferenced: every call either fails
+validation or has no work (M or N = 0).
+"""
+import ctypes
+import os
+
+import pytest
+
+import block_scaled_gemm_fp8gemm_amd as F
+
+SUCCESS, INVALID, MISALIGNED, NOT_SUPPORTED, WORKSPACE = 0, 1, 2, 3, 4
+P = 0x10000          # a 16-byte aligned fake device address
+P2 = 0x20000
+P3 = 0x30000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(F.library_path()):
+        from block_scaled_gemm_fp8gemm_amd.build import build
+        build()
+    return F.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = F.exported_symbols()
+    assert set(names) == {
+        "fp8gemm_quantize_workspace_size", "fp8gemm_quantize", "fp8gemm_workspace_size",
+        "fp8gemm_run", "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run",
+        "fp8gemm_status_string", "fp8gemm_version"}
+    raw = ctypes.CDLL(F.library_path())
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert F.fp8gemm_version() == 100
+    for code, name in [(0, "FP8GEMM_SUCCESS"), (1, "FP8GEMM_ERROR_INVALID_VALUE"),
+                       (2, "FP8GEMM_ERROR_MISALIGNED"), (3, "FP8GEMM_ERROR_NOT_SUPPORTED"),
+                       (4, "FP8GEMM_ERROR_WORKSPACE"), (5, "FP8GEMM_ERROR_LAUNCH"),
+                       (99, "FP8GEMM_ERROR_UNKNOWN")]:
+        assert F.fp8gemm_status_string(code) == name
+
+
+def test_workspace_queries(lib):
+    assert F.fp8gemm_quantize_workspace_size(4096, 4096, 0) > 0
+    assert F.fp8gemm_quantize_workspace_size(4096, 4096, 1) == 0
+    assert F.fp8gemm_quantize_workspace_size(4096, 4096, 2) == 0
+    assert F.fp8gemm_workspace_size(4096, 4096, 4096, 2) >= 0
+    assert F.fp8gemm_grouped_workspace_size(8, 16384, 14336, 4096, 1) >= 0
+
+
+def _quant(lib, x=P, rows=64, k=256, ldx=256, mode=1, q=P2, ldq=256, scales=P3, ws=0, wsb=0):
+    return lib.fp8gemm_quantize(x, rows, k, ldx, mode, q, ldq, scales, ws, wsb, None)
+
+
+def test_quantize_validation(lib):
+    assert _quant(lib, mode=3) == INVALID
+    assert _quant(lib, rows=-1) == INVALID
+    assert _quant(lib, k=0) == INVALID
+    assert _quant(lib, rows=0) == SUCCESS                 # nothing to do, nothing enqueued
+    assert _quant(lib, x=0) == INVALID
+    assert _quant(lib, q=0) == INVALID
+    assert _quant(lib, scales=0) == INVALID
+    assert _quant(lib, ldx=128) == INVALID                 # ldx < k
+    assert _quant(lib, ldq=128) == INVALID
+    assert _quant(lib, k=40, ldx=48, ldq=48) == NOT_SUPPORTED          # k % 16
+    assert _quant(lib, k=48, ldx=48, ldq=48, mode=2) == NOT_SUPPORTED  # MX: k % 32
+    assert _quant(lib, rows=1 << 20, k=4096, ldx=4096, ldq=4096) == NOT_SUPPORTED  # >= 2^32 elems
+    assert _quant(lib, x=P + 4) == MISALIGNED
+    assert _quant(lib, q=P2 + 8) == MISALIGNED
+    assert _quant(lib, ldx=258) == MISALIGNED
+    assert _quant(lib, ldq=264) == MISALIGNED
+    assert _quant(lib, scales=P3 + 2) == MISALIGNED
+    assert _quant(lib, mode=0) == WORKSPACE                 # per-tensor needs a workspace
+    need = F.fp8gemm_quantize_workspace_size(64, 256, 0)
+    assert _quant(lib, mode=0, ws=P, wsb=need - 4) == WORKSPACE
+
+
+def _run(lib, M=64, N=64, K=128, A=P, lda=128, B=P2, ldb=128, mode=1, sa=P3, sb=P3 + 256,
+         C=P3 + 4096, ldc=64, out=1):
+    return lib.fp8gemm_run(M, N, K, A, lda, B, ldb, mode, sa, sb, C, ldc, out, 0, 0, None)
+
+
+def test_run_validation(lib):
+    assert _run(lib, mode=7) == INVALID
+    assert _run(lib, out=2) == INVALID
+    assert _run(lib, M=-1) == INVALID
+    assert _run(lib, K=0) == INVALID
+    assert _run(lib, M=0) == SUCCESS
+    assert _run(lib, N=0) == SUCCESS
+    for kw in ("A", "B", "C", "sa", "sb"):
+        assert _run(lib, **{kw: 0}) == INVALID, kw
+    assert _run(lib, lda=64) == INVALID
+    assert _run(lib, ldb=64) == INVALID
+    assert _run(lib, ldc=32) == INVALID
+    assert _run(lib, K=120, lda=128, ldb=128) == NOT_SUPPORTED
+    assert _run(lib, K=112, lda=112, ldb=112, mode=2) == NOT_SUPPORTED
+    assert _run(lib, A=P + 1) == MISALIGNED
+    assert _run(lib, B=P2 + 8) == MISALIGNED
+    assert _run(lib, C=P3 + 4096 + 2) == MISALIGNED
+    assert _run(lib, lda=136) == MISALIGNED
+    assert _run(lib, ldc=68) == MISALIGNED
+    assert _run(lib, sa=P3 + 1) == MISALIGNED
+    assert _run(lib, M=1 << 31) == NOT_SUPPORTED
+
+
+def _grouped(lib, G=8, total_m=256, N=64, K=128, A=P, lda=128, off=P3 + 8192, B=P2, ldb=128,
+             stride_b=64 * 128, mode=1, sa=P3, sb=P3 + 1024, C=P3 + 16384, ldc=64, out=1):
+    return lib.fp8gemm_grouped_run(G, total_m, N, K, A, lda, off, B, ldb, stride_b, mode, sa, sb,
+                                   C, ldc, out, 0, 0, None)
+
+
+def test_grouped_validation(lib):
+    assert _grouped(lib, G=0) == INVALID
+    assert _grouped(lib, G=2000) == NOT_SUPPORTED
+    assert _grouped(lib, mode=5) == INVALID
+    assert _grouped(lib, total_m=-1) == INVALID
+    assert _grouped(lib, total_m=0) == SUCCESS
+    assert _grouped(lib, N=0) == SUCCESS
+    assert _grouped(lib, off=0) == INVALID
+    assert _grouped(lib, stride_b=64 * 128 - 16) == INVALID
+    assert _grouped(lib, stride_b=64 * 128 + 8) == MISALIGNED
+    assert _grouped(lib, off=P3 + 8192 + 2) == MISALIGNED
+    assert _grouped(lib, K=100, lda=128, ldb=128) == NOT_SUPPORTED
+    assert _grouped(lib, A=P + 8) == MISALIGNED
+
+
+def test_python_wrapper_raises(lib):
+    with pytest.raises(F.Fp8GemmError) as ei:
+        F.fp8gemm_run(-1, 1, 16, P, 16, P, 16, 0, P, P, P, 16, 0, 0, 0, 0)
+    assert ei.value.status == INVALID

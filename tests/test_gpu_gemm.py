@@ -1,0 +1,140 @@
+"""GPU GEMM parity: |C - C_ref| <= 1e-3 * sum|a*b| + 1 output ulp against the oracle.
+
+Operands are quantised by the oracle (so the GEMM is checked on its own) and,
+in the end-to-end cases, by the GPU (checked bit-exact against the oracle
+first).  Shapes span several tiles, ragged M / N / K edges, the single-element
+case, both tile configurations, all scale modes and both output types; the
+dense workloads run at full size (the 8192^3 MX case on sampled 128 x 128
+tiles).  Determinism and out-of-bounds stores (guard canaries) are checked too.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_gemm_fp8gemm_amd as F
+import oracle as O
+from oracle import quant as Q
+from workloads import WORKLOADS, dense_inputs, random_inputs
+
+from gpu_support import DEV, announce, assert_within_bound, scale_to_dev, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["tensor", "rowwise", "mx32"]
+
+
+def _oracle_operands(M, N, K, mode, seed, dist="outlier"):
+    A, B = random_inputs(M, N, K, seed, dist)
+    qa, sa = Q.quantize(A, mode)
+    qb, sb = Q.quantize(B, mode)
+    return qa, sa, qb, sb
+
+
+def _run_gpu(qa, sa, qb, sb, mode, out):
+    return F.gemm(to_dev(qa, 16), scale_to_dev(sa, mode), to_dev(qb, 16), scale_to_dev(sb, mode),
+                  mode, out)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("out", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 1, 32), (33, 70, 64), (256, 256, 256), (300, 520, 384),
+                                   (257, 263, 4160), (129, 1000, 96)])
+def test_gemm_small_shapes(mode, out, shape):
+    M, N, K = shape
+    qa, sa, qb, sb = _oracle_operands(M, N, K, mode, seed=M + 3 * N + 7 * K)
+    announce("gemm", mode, out, shape)
+    C = to_host(_run_gpu(qa, sa, qb, sb, mode, out))
+    Cr, Ar = O.gemm_reference(qa, sa, qb, sb, mode)
+    assert_within_bound(C, Cr, Ar, out, f"{mode}/{out}/{shape}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", [(4096, 4096, 256), (4000, 4100, 192)])
+def test_gemm_big_tiles(mode, shape):
+    """Shapes with >= 256 tiles of 256 x 256 take the large-tile kernel (ragged edges too)."""
+    M, N, K = shape
+    qa, sa, qb, sb = _oracle_operands(M, N, K, mode, seed=11, dist="mx_block")
+    announce("gemm big", mode, shape)
+    C = to_host(_run_gpu(qa, sa, qb, sb, mode, "bf16"))
+    Cr, Ar = O.gemm_reference(qa, sa, qb, sb, mode)
+    assert_within_bound(C, Cr, Ar, "bf16", f"big {mode} {shape}")
+
+
+def test_gemm_k16_tail_with_canaries():
+    """K = 16 (one partial chunk pair) and guard bands around C must stay untouched."""
+    M, N, K = 70, 90, 16
+    qa, sa, qb, sb = _oracle_operands(M, N, K, "rowwise", seed=5)
+    announce("gemm canary", (M, N, K))
+    ldc = 128
+    sentinel = 12352.0                       # exactly representable in bfloat16
+    buf = torch.full((M + 2, ldc), sentinel, dtype=torch.bfloat16, device=DEV)
+    out = buf[1:M + 1, :N]
+    F.gemm(to_dev(qa, 16), scale_to_dev(sa, "rowwise"), to_dev(qb, 16),
+           scale_to_dev(sb, "rowwise"), "rowwise", "bf16", out=out)
+    torch.cuda.synchronize()
+    host = to_host(buf)
+    assert np.all(host[0] == sentinel) and np.all(host[-1] == sentinel)
+    assert np.all(host[1:M + 1, N:] == sentinel)
+    Cr, Ar = O.gemm_reference(qa, sa, qb, sb, "rowwise")
+    assert_within_bound(host[1:M + 1, :N], Cr, Ar, "bf16", "canary")
+
+
+def test_gemm_deterministic():
+    qa, sa, qb, sb = _oracle_operands(1024, 1024, 1024, "mx32", seed=9, dist="mx_block")
+    announce("gemm determinism")
+    c1 = _run_gpu(qa, sa, qb, sb, "mx32", "bf16")
+    c2 = _run_gpu(qa, sa, qb, sb, "mx32", "bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+
+
+def _end_to_end(name, rows=None, cols=None, tiles=None):
+    """GPU quantize + GEMM on a workload; oracle on the same (sampled) rows/columns."""
+    w = WORKLOADS[name]
+    A, B = dense_inputs(w)
+    announce("end-to-end", name, w.mode, (w.M, w.N, w.K))
+    qa_d, sa_d = F.quantize(to_dev(A), w.mode)
+    qb_d, sb_d = F.quantize(to_dev(B), w.mode)
+    C_d = F.gemm(qa_d, sa_d, qb_d, sb_d, w.mode, w.out)
+    torch.cuda.synchronize()
+    qa_g, qb_g = to_host(qa_d), to_host(qb_d)
+    if tiles is None:
+        qa, sa = Q.quantize(A, w.mode)
+        qb, sb = Q.quantize(B, w.mode)
+        assert np.array_equal(qa_g, qa) and np.array_equal(qb_g, qb)
+        Cr, Ar = O.gemm_reference(qa, sa, qb, sb, w.mode)
+        assert_within_bound(to_host(C_d), Cr, Ar, w.out, name)
+        return
+    # sampled tiles: row-local (MX / row-wise) quantisation lets the oracle work on
+    # just the rows of A and B a tile needs
+    assert w.mode in ("mx32", "rowwise")
+    C_full = C_d
+    for (r0, c0) in tiles:
+        rows_i = np.arange(r0, min(r0 + 128, w.M))
+        cols_i = np.arange(c0, min(c0 + 128, w.N))
+        qa, sa = Q.quantize(A[rows_i], w.mode)
+        qb, sb = Q.quantize(B[cols_i], w.mode)
+        assert np.array_equal(qa_g[rows_i], qa) and np.array_equal(qb_g[cols_i], qb)
+        Cr, Ar = O.gemm_reference(qa, sa, qb, sb, w.mode)
+        Cg = to_host(C_full[r0:r0 + 128, c0:c0 + 128])
+        assert_within_bound(Cg, Cr, Ar, w.out, f"{name} tile {(r0, c0)}")
+
+
+def test_workload_pertensor256():
+    _end_to_end("pertensor256")
+
+
+def test_workload_skinny128():
+    _end_to_end("skinny128")
+
+
+def test_workload_rowwise4096():
+    _end_to_end("rowwise4096")
+
+
+def test_workload_mx8192_sampled_tiles():
+    w = WORKLOADS["mx8192"]
+    rng = np.random.default_rng(404)
+    corners = [(0, 0), (0, w.N - 128), (w.M - 128, 0), (w.M - 128, w.N - 128)]
+    rand = [(int(r) * 128, int(c) * 128) for r, c in rng.integers(0, w.M // 128, size=(12, 2))]
+    _end_to_end("mx8192", tiles=corners + rand)
