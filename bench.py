@@ -1,0 +1,263 @@
+"""Benchmark of the scaled FP8 GEMM hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input already resident in
+HBM: quantise A and B (amax / scale and e4m3 encoding) and run the GEMM (MFMA
+mainloop, scale/cast epilogue, tile scheduling); the grouped workload runs the
+grouped GEMM instead.  W untimed warm-up steps, then K timed steps between two
+``torch.cuda.synchronize()``; one JSON line goes to stdout.
+
+``value`` is 2*M*N*K per step over the wall time of the timed steps (TFLOP/s,
+the formula of the Cutlass-named Triton FP8 post's monitoring list).  The
+``roofline`` object describes the dominant kernel (the GEMM): its algorithmic
+FLOPs per launch over its average duration, measured with HIP events recorded
+on the stream it is launched on, against the MI355X dense FP8 MFMA peak.
+``cpu_baseline`` times the CPU oracle (numpy, float64) on a bounded sample of
+the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import WORKLOADS, dense_inputs, grouped_inputs  # noqa: E402
+
+PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 MFMA peak (no sparsity)
+PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
+DEFAULT_WORKLOAD = "mx8192"
+KERNEL_SOURCES = ["block_scaled_gemm_fp8gemm_amd/csrc/gemm_tile.h",
+                  "block_scaled_gemm_fp8gemm_amd/csrc/gemm.hip",
+                  "block_scaled_gemm_fp8gemm_amd/csrc/grouped.hip",
+                  "block_scaled_gemm_fp8gemm_amd/csrc/tile_order.h",
+                  "block_scaled_gemm_fp8gemm_amd/csrc/device_utils.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary.
+
+    None when there is no summary for this workload or the kernel sources have
+    changed since the counters were taken.
+    """
+    path = os.path.join(ROOT, "profiles", f"gemm_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def gemm_bytes(w) -> int:
+    """Algorithmic bytes of one GEMM launch: A + B codes, scales, C."""
+    mb = w.M * w.K + (w.groups or 1) * w.N * w.K
+    if w.mode == "mx32":
+        mb += (w.M + (w.groups or 1) * w.N) * (w.K // 32)
+    elif w.mode == "rowwise":
+        mb += 4 * (w.M + (w.groups or 1) * w.N)
+    else:
+        mb += 8
+    return mb + 2 * w.M * w.N
+
+
+def cpu_baseline(w, rows: int):
+    """Oracle on a bounded sample: quantise `rows` rows of A and of B, then the
+    float64 GEMM reference of that rows x rows x K block (value and sum|a*b|)."""
+    import numpy as np
+    import oracle as O
+    from oracle import quant as Q
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    if w.groups:
+        counts, A, W = grouped_inputs(w, experts=(0,))
+        Bs = W[0][:rows]
+    else:
+        A, B = dense_inputs(w)
+        Bs = B[:rows]
+    As = A[:rows]
+    t0 = time.perf_counter()
+    qa, sa = Q.quantize(As, w.mode)
+    qb, sb = Q.quantize(Bs, w.mode)
+    if w.mode == "tensor":   # the sample's own scales; the work is the same
+        pass
+    O.gemm_reference(qa, sa, qb, sb, w.mode)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * rows * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows} rows of A and {rows} columns of B (K={w.K}): quantise both, "
+                      f"float64 GEMM reference with sum|a*b|; {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="rows of A / columns of B in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_gemm_fp8gemm_amd as F
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    F.load_library()
+    log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} mode={w.mode} out={w.out} groups={w.groups}")
+
+    # ---- synthetic inputs, resident in HBM before timing -------------------------
+    if w.groups:
+        counts, A, W = grouped_inputs(w)
+        import numpy as np
+        offsets = torch.from_numpy(
+            np.concatenate([[0], np.cumsum(counts)]).astype("int32")).to(dev)
+        Ad = torch.from_numpy(A).to(dev)
+        Bd = torch.from_numpy(W).to(dev).view(w.groups * w.N, w.K)
+        del A, W
+    else:
+        A, B = dense_inputs(w)
+        Ad = torch.from_numpy(A).to(dev)
+        Bd = torch.from_numpy(B).to(dev)
+        del A, B
+    rows_b = Bd.shape[0]
+
+    # ---- outputs and workspaces allocated once ---------------------------------
+    qa = torch.empty((w.M, w.K), dtype=torch.uint8, device=dev)
+    qb = torch.empty((rows_b, w.K), dtype=torch.uint8, device=dev)
+    if w.mode == "tensor":
+        sa = torch.empty(1, dtype=torch.float32, device=dev)
+        sb = torch.empty(1, dtype=torch.float32, device=dev)
+    elif w.mode == "rowwise":
+        sa = torch.empty(w.M, dtype=torch.float32, device=dev)
+        sb = torch.empty(rows_b, dtype=torch.float32, device=dev)
+    else:
+        sa = torch.empty((w.M, w.K // 32), dtype=torch.uint8, device=dev)
+        sb = torch.empty((rows_b, w.K // 32), dtype=torch.uint8, device=dev)
+    mode_id = F.SCALE_MODES[w.mode]
+    ws_a = ws_b = None
+    if F.fp8gemm_quantize_workspace_size(w.M, w.K, mode_id):
+        ws_a = torch.empty(F.fp8gemm_quantize_workspace_size(w.M, w.K, mode_id),
+                           dtype=torch.uint8, device=dev)
+        ws_b = torch.empty_like(ws_a)
+    tdt = torch.bfloat16 if w.out == "bf16" else torch.float16
+    C = torch.empty((w.M, w.N), dtype=tdt, device=dev)
+
+    def run_gemm():
+        if w.groups:
+            if w.mode == "tensor":
+                raise SystemExit("grouped per-tensor benchmarking is not configured")
+            F.grouped_gemm(qa, sa, offsets, qb.view(w.groups, w.N, w.K),
+                           sb.view(w.groups, -1) if w.mode == "mx32" else sb.view(w.groups, w.N),
+                           w.mode, w.out, out=C)
+        else:
+            F.gemm(qa, sa, qb, sb, w.mode, w.out, out=C)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        F.quantize(Ad, w.mode, out=qa, scales=sa, workspace=ws_a)
+        if ev is not None:
+            ev[1].record()
+        F.quantize(Bd, w.mode, out=qb, scales=sb, workspace=ws_b)
+        if ev is not None:
+            ev[2].record()
+        run_gemm()
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warm-up done ({args.warmup} steps)")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
+
+    qa_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    qb_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    gemm_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    ms_per_step = elapsed * 1e3 / args.steps
+    flops = w.flops
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    quant_bytes_a = w.M * w.K * 5 + (w.M * w.K // 32 if w.mode == "mx32" else 4 * w.M)
+    quant_bytes_b = rows_b * w.K * 5 + (rows_b * w.K // 32 if w.mode == "mx32" else 4 * rows_b)
+    if w.mode == "tensor":  # the amax pass reads the input once more
+        quant_bytes_a += w.M * w.K * 4
+        quant_bytes_b += rows_b * w.K * 4
+
+    result = {
+        "metric": "FP8 GEMM TFLOPS (% of MI355X FP8 peak) at 4096^3/8192^3; GB/s at M=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "scale": w.mode,
+                   "out": w.out, "groups": w.groups,
+                   "step": "quantize A + quantize B + GEMM"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name)},
+        "kernels": {
+            "gemm": {"ms": round(gemm_ms, 4), "tflops": round(achieved, 1),
+                     "gbs_algorithmic": round(gemm_bytes(w) / (gemm_ms * 1e-3) / 1e9, 1)},
+            "quantize_a": {"ms": round(qa_ms, 4),
+                           "gbs": round(quant_bytes_a / (qa_ms * 1e-3) / 1e9, 1)},
+            "quantize_b": {"ms": round(qb_ms, 4),
+                           "gbs": round(quant_bytes_b / (qb_ms * 1e-3) / 1e9, 1)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        del Ad, Bd
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
