@@ -36,31 +36,37 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libfp8gemm.so)")
 
 
-def _compile(hipcc: str, src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(hipcc: str, src: str, defines=(), tag: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + tag + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc, *FLAGS, *[f"-D{d}" for d in defines], *lang, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libfp8gemm.so; returns its path."""
+def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
+    """Compile every source for gfx950 and link the library (default libfp8gemm.so).
+
+    ``defines`` are extra preprocessor definitions (tuning switches); ``out`` is
+    the path of the shared library to write.
+    """
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
+    tag = "" if not defines else "." + "_".join(d.replace("=", "") for d in defines)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(hipcc, s), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(hipcc, s, defines, tag), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -17,7 +17,8 @@ namespace fp8gemm {
 namespace {
 
 template <class Cfg, int MODE, typename OutT, bool KALIGNED>
-__global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(GemmProblem p, int tiles_m,
+__global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void gemm_kernel(GemmProblem p,
+                                                                              int tiles_m,
                                                               int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::kLdsBytes];
   int tm, tn;
@@ -32,20 +33,22 @@ __global__ __launch_bounds__(Cfg::kThreads) void gemm_kernel(GemmProblem p, int 
   op.ldb = p.ldb;
   op.b_rows = p.N - n0;
   op.K = p.K;
+  const float* fsa = static_cast<const float*>(p.scale_a);
+  const float* fsb = static_cast<const float*>(p.scale_b);
+  op.sa = op.sb = nullptr;
+  op.ra = op.rb = nullptr;
   if (MODE == kMx32) {
     op.sa = static_cast<const uint8_t*>(p.scale_a) + (int64_t)m0 * (p.K / 32);
     op.sb = static_cast<const uint8_t*>(p.scale_b) + (int64_t)n0 * (p.K / 32);
-  } else {
-    op.sa = op.sb = nullptr;
+  }
+  if (MODE == kRowwise) {
+    op.ra = fsa + m0;
+    op.rb = fsb + n0;
   }
 
-  v16f acc[Cfg::kFragM][Cfg::kFragN];
-  mainloop<Cfg, MODE, KALIGNED>(op, lds, acc);
-
-  const float* fsa = static_cast<const float*>(p.scale_a);
-  const float* fsb = static_cast<const float*>(p.scale_b);
   const float ts = (MODE == kTensor) ? fsa[0] * fsb[0] : 1.0f;
-  epilogue<Cfg, MODE, OutT>(acc, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N, ts, fsa, fsb);
+  gemm_tile<Cfg, MODE, OutT, KALIGNED>(op, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N,
+                                       ts);
 }
 
 template <class Cfg, int MODE, typename OutT>
@@ -53,7 +56,7 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   const int tiles_m = (p.M + Cfg::BM - 1) / Cfg::BM;
   const int tiles_n = (p.N + Cfg::BN - 1) / Cfg::BN;
   const int grid = tiles_m * tiles_n;
-  if (p.K % Cfg::kBK == 0)
+  if (p.K % 128 == 0)
     hipLaunchKernelGGL((gemm_kernel<Cfg, MODE, OutT, true>), dim3(grid), dim3(Cfg::kThreads), 0,
                        stream, p, tiles_m, tiles_n);
   else
@@ -62,15 +65,27 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-using Big = TileCfg<256, 256, 128, 128>;
-using Mid = TileCfg<128, 128, 64, 64>;
+// Large-problem tile.  FP8GEMM_BIG_CFG selects it (tuning switch):
+//   0: 256 x 256, 4 wavefronts of 128 x 128, one workgroup per CU, 4-slot ring
+//   1: 256 x 128, 4 wavefronts of 128 x 64, two workgroups per CU, 3-slot ring
+#ifndef FP8GEMM_BIG_CFG
+#define FP8GEMM_BIG_CFG 0
+#endif
+#if FP8GEMM_BIG_CFG == 0
+using Big = TileCfg<256, 256, 128, 128, 4, 1>;
+#else
+using Big = TileCfg<256, 128, 128, 64, 3, 2>;
+#endif
+using Mid = TileCfg<128, 128, 64, 64, 4, 2>;
 
 template <int MODE, typename OutT>
 hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
   // Large tiles when they still give at least one tile per CU; otherwise smaller
   // tiles for more parallelism.
-  const int64_t big_tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (big_tiles >= 256) return launch_cfg<Big, MODE, OutT>(p, stream);
+  const int64_t big_tiles = (int64_t)((p.M + Big::BM - 1) / Big::BM) * ((p.N + Big::BN - 1) / Big::BN);
+  // MX with K % 128 != 0 reads its codes into registers: the large tile would spill
+  const bool mx_ragged = MODE == kMx32 && p.K % 128 != 0;
+  if (big_tiles >= 256 * Big::kWgPerCu && !mx_ragged) return launch_cfg<Big, MODE, OutT>(p, stream);
   return launch_cfg<Mid, MODE, OutT>(p, stream);
 }
 

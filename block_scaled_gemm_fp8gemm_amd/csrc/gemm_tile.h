@@ -4,61 +4,98 @@
 //
 // Prior art and what is kept.  "Hopper/Blackwell architecture features" §12.7
 // tiles C into BLOCK_M x BLOCK_N tiles, walks K in BLOCK_K steps accumulating
-// fp32 and casts on store; §12.4 overlaps the load of the next K tile with the
-// math on the current one through a multi-stage shared-memory ring whose size
-// per stage is (BLOCK_M + BLOCK_N) * BLOCK_K * element size (§12.4.3).  The
+// fp32 and casts on store; §12.4 overlaps the load of later K tiles with the math
+// on the current one through a multi-stage shared-memory ring whose size per
+// stage is (BLOCK_M + BLOCK_N) * BLOCK_K * element size (§12.4.3).  The
 // TMA/mbarrier/warp-specialised machinery of §12.2/§12.3 has no CDNA
-// counterpart; instead every wavefront both loads and computes:
-//   * K tiles of 128 bytes are copied global -> LDS with gfx950's direct
-//     `global_load_lds_dwordx4` (16 bytes per lane, no VGPR staging) into a
-//     two-stage ring: (BM + BN) * 128 bytes per stage (64 KiB for 256 x 256).
-//   * LDS rows are 128 bytes; the sixteen-byte chunk c of row r is stored at
-//     chunk position c ^ (r & 7), so the eight rows a group of lanes reads
-//     together fall on distinct banks.  The XOR is applied on the load side by
-//     choosing which global chunk each lane fetches.
-//   * Each wavefront owns a WM x WN sub-tile made of 32 x 32 MFMA blocks and
-//     runs V_MFMA_SCALE_F32_32X32X64_F8F6F4 on e4m3 operands.  Per lane an
+// counterpart; here every wavefront both copies and computes:
+//   * K is walked in 64-byte sub-tiles (one V_MFMA_SCALE_F32_32X32X64_F8F6F4 K
+//     step).  A ring of four LDS slots of (BM + BN) * 64 bytes (32 KiB for
+//     256 x 256) is filled by gfx950's direct `global_load_lds_dwordx4` copies
+//     (16 bytes per lane, no VGPR staging) issued four sub-tiles ahead.  Each
+//     sub-tile waits only for the copies of the next one (an s_waitcnt vmcnt
+//     count that leaves the two newer sub-tiles in flight) and one workgroup
+//     barrier, so 64-96 KiB stay in flight per CU; with a single 64 KiB stage the
+//     copy stream stalls on latency at about half the rate it sustains here.
+//   * LDS rows are 64 bytes; 16-byte chunk c of tile row r is stored at chunk
+//     c ^ ((r >> 2) & 3).  A fragment read touches 16 consecutive rows at one
+//     logical chunk per 16-lane group, and the XOR spreads them over all 64
+//     banks.  The XOR is applied on the copy side by choosing which global chunk
+//     each lane fetches.
+//   * Each wavefront owns a WM x WN sub-tile of 32 x 32 MFMA blocks.  Per lane an
 //     operand fragment is two 16-byte K chunks, k = 32*(byte/16) + 16*(lane/32)
-//     + byte%16, for row lane%32; the E8M0 scale of (row r, 32-K block b) is
-//     byte 0 of the scale register of lane r + 32*b.  Per-tensor and row-wise
-//     operands pass constant zero scales (the plain MFMA); MX operands pass the
-//     E8M0 codes so the block scales are applied inside the instruction.
-//   * The instruction is issued with B as its first operand, so the fp32 result
-//     is C transposed: a lane holds four consecutive output columns of one row,
-//     which are scaled, rounded to fp16/bf16 and stored as 8 bytes.
-//   * Rows past the matrix edge are read from the last valid row (and never
-//     stored); K chunks past K are read from column 0 and zeroed in registers
-//     before use, together with their scales (set to 2^0).
+//     + byte%16, of row lane%32; the E8M0 scale of (row r, 32-K block b) is byte
+//     0 of the scale register of lane r + 32*b.  Per-tensor and row-wise operands
+//     use the unscaled MFMA; MX operands pass the E8M0 codes, so block scales are
+//     applied inside the instruction.  MX codes travel through LDS next to their
+//     tile (one dword = four blocks per row per 128 K).
+//   * Fragments are double-buffered in registers: the LDS reads of sub-tile t+1
+//     are interleaved with the MFMAs of sub-tile t.
+//   * The instruction takes B as its first operand, so the accumulator holds C^T
+//     blocks: a lane has four consecutive output columns of one row.  The
+//     epilogue scales them (row-wise scales come from LDS, copied at tile start),
+//     rounds to fp16/bf16, transposes the tile through LDS and writes C with
+//     fully coalesced 16-byte stores.
+//   * Rows past the matrix edge are read from the last valid row and never
+//     stored; K chunks past K are read from column 0 and zeroed in registers,
+//     their MX scales set to 2^0.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_utils.h"
 #include "launch.h"
+
+#ifndef FP8GEMM_SCHED
+#define FP8GEMM_SCHED 1
+#endif
 
 namespace fp8gemm {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-template <int BM_, int BN_, int WM_, int WN_>
+// BM x BN output tile, WM x WN per wavefront, SLOTS-deep LDS ring, and the number
+// of workgroups meant to share a CU (their waves then share each SIMD, so one
+// workgroup's barrier waits are covered by the other's MFMAs).
+template <int BM_, int BN_, int WM_, int WN_, int SLOTS_ = 4, int WG_PER_CU_ = 1>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr int kBK = 128;
+  static constexpr int kBK = 64;                              // K bytes per sub-tile
+  static constexpr int kSlots = SLOTS_;                       // LDS ring depth
+  static constexpr int kWgPerCu = WG_PER_CU_;
   static constexpr int kWavesM = BM / WM, kWavesN = BN / WN;
   static constexpr int kWaves = kWavesM * kWavesN;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kFragM = WM / 32, kFragN = WN / 32;
-  static constexpr int kStageBytes = (BM + BN) * kBK;
-  static constexpr int kStages = 2;
-  static constexpr int kLdsBytes = kStages * kStageBytes;
-  static constexpr int kLoadsA = BM / 8 / kWaves;  // 1 KiB (8 rows) per load instruction
-  static constexpr int kLoadsB = BN / 8 / kWaves;
-  static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "whole load instructions");
+  static constexpr int kSlotBytes = (BM + BN) * kBK;
+  static constexpr int kScaleSlotBytes = (BM + BN) * 4;       // MX: 4 codes per row per 128 K
+  static constexpr int kScaleSlots = 2;
+  static constexpr int kRowScaleBytes = (BM + BN) * 4;        // row-wise: fp32 per row / column
+  static constexpr int kScaleOff = kSlots * kSlotBytes;
+  static constexpr int kRowScaleOff = kScaleOff + kScaleSlots * kScaleSlotBytes;
+  static constexpr int kLdsBytes = kRowScaleOff + kRowScaleBytes;
+  // copies per sub-tile and wavefront: 1 KiB (16 rows of 64 bytes) per instruction
+  static constexpr int kTileLoads = (BM + BN) * kBK / 1024 / kWaves;
+  // dword copies (MX codes per 128 K, row-wise scales) per wavefront: one dword per
+  // row, 64 rows per instruction; waves without a full share repeat the last one
+  static constexpr int kScaleInsts = (BM + BN) / 64;
+  static constexpr int kScaleLoads = (kScaleInsts + kWaves - 1) / kWaves;
+  // epilogue staging: 32 rows of one wavefront's columns (+16 bytes against conflicts)
+  static constexpr int kStagePitch = WN * 2 + 16;
+  static_assert((BM + BN) * kBK % (1024 * kWaves) == 0, "equal copy share per wavefront");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "whole copy instructions per operand");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
-  static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
+  static_assert(kWaves * 32 * kStagePitch <= kSlots * kSlotBytes, "epilogue staging fits");
+  static_assert(kLdsBytes * kWgPerCu <= 160 * 1024, "LDS per CU");
+  static_assert(kSlots >= 3, "ring keeps one sub-tile being read and one in flight");
+  // waves per SIMD, for __launch_bounds__ (caps registers at 512 / this)
+  static constexpr int kWavesPerEu = kWgPerCu * kWaves / 4 > 0 ? kWgPerCu * kWaves / 4 : 1;
 };
 
 // Where a tile's operands live and how many of its rows are valid.
@@ -71,6 +108,8 @@ struct TileOperands {
   int b_rows;           // valid B rows (output columns) from B (>= 1)
   const uint8_t* sa;    // MX: E8M0 codes of A's first tile row, K/32 per row
   const uint8_t* sb;    // MX: E8M0 codes of B's first tile row
+  const float* ra;      // row-wise: fp32 scale of A's first tile row
+  const float* rb;      // row-wise: fp32 scale of B's first tile row
   int K;
 };
 
@@ -79,71 +118,227 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* g, uint8_t* lds) {
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+__device__ __forceinline__ void lds_dma4(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+// Chunk swizzle of a 64-byte LDS row.
+__device__ __forceinline__ int lds_swz(int r) { return (r >> 2) & 3; }
+
+// s_waitcnt with vmcnt(n) (n < 64), lgkmcnt(0), no expcnt wait (gfx9 encoding).
+#define FP8GEMM_WAIT_VM_LGKM0(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | ((((n) >> 4) & 3) << 14))
+
+// Copies of sub-tile s (K bytes [64 s, 64 s + 64)) into an LDS slot: A rows, then
+// B rows; instruction g covers tile rows 16 g .. 16 g + 15 of [A; B].
 template <class Cfg, bool KTAIL>
-__device__ __forceinline__ void load_stage(const TileOperands& op, uint8_t* stage, int k0, int wave,
-                                           int lane) {
-  const int sub = lane >> 3;                  // row within the 8-row group
-  const int chunk = (lane & 7) ^ sub;         // logical K chunk fetched (XOR layout)
-  int kc = k0 + 16 * chunk;
-  if (KTAIL && kc >= op.K) kc = 0;            // in-bounds dummy, zeroed later
+__device__ __forceinline__ void copy_subtile(const TileOperands& op, uint8_t* slot, int s,
+                                             int wave, int lane) {
+  constexpr int nA = Cfg::BM / 16;
+  const int sub = lane >> 2;                    // row within the 16-row group
 #pragma unroll
-  for (int t = 0; t < Cfg::kLoadsA; ++t) {
-    const int grp = wave * Cfg::kLoadsA + t;
-    int row = grp * 8 + sub;
-    row = row < op.a_rows ? row : op.a_rows - 1;
-    lds_dma16(op.A + (int64_t)row * op.lda + kc, stage + grp * 1024);
+  for (int j = 0; j < Cfg::kTileLoads; ++j) {
+    const int g = wave * Cfg::kTileLoads + j;   // wave-uniform instruction index
+    const bool isA = g < nA;
+    const int row_t = (isA ? g : g - nA) * 16 + sub;
+    const int chunk = (lane & 3) ^ lds_swz(row_t);
+    int kc = s * Cfg::kBK + 16 * chunk;
+    if (KTAIL && kc >= op.K) kc = 0;            // in-bounds dummy, zeroed before use
+    const uint8_t* base = isA ? op.A : op.B;
+    const int64_t ld = isA ? op.lda : op.ldb;
+    const int rows = isA ? op.a_rows : op.b_rows;
+    const int row = row_t < rows ? row_t : rows - 1;
+    lds_dma16(base + (int64_t)row * ld + kc, slot + g * 1024);
   }
-  uint8_t* stageB = stage + Cfg::BM * Cfg::kBK;
+}
+
+// Dword copies (one lane per row, 64 rows per instruction) of every A row and then
+// every B row of a tile, spread over the wavefronts without branches: every wave
+// issues kScaleLoads instructions (so copy counts stay uniform for the vmcnt
+// waits); indices past the last instruction repeat it, rewriting the same bytes.
+// Row r of A lands at dst[4 r], row r of B at dst[4 (BM + r)].
+template <class Cfg>
+__device__ __forceinline__ void dword_rows_ab(const uint8_t* pa, int64_t lda, int a_rows,
+                                              const uint8_t* pb, int64_t ldb, int b_rows,
+                                              int byte_off, uint8_t* dst, int wave, int lane) {
+  constexpr int nA = Cfg::BM / 64;
 #pragma unroll
-  for (int t = 0; t < Cfg::kLoadsB; ++t) {
-    const int grp = wave * Cfg::kLoadsB + t;
-    int row = grp * 8 + sub;
-    row = row < op.b_rows ? row : op.b_rows - 1;
-    lds_dma16(op.B + (int64_t)row * op.ldb + kc, stageB + grp * 1024);
+  for (int j = 0; j < Cfg::kScaleLoads; ++j) {
+    int i = wave * Cfg::kScaleLoads + j;         // wave-uniform
+    i = i < Cfg::kScaleInsts ? i : Cfg::kScaleInsts - 1;
+    const bool isA = i < nA;
+    const uint8_t* base = isA ? pa : pb;
+    const int64_t ld = isA ? lda : ldb;
+    const int rows = isA ? a_rows : b_rows;
+    const int row_t = (isA ? i : i - nA) * 64 + lane;
+    const int row = row_t < rows ? row_t : rows - 1;
+    lds_dma4(base + (int64_t)row * ld + byte_off, dst + i * 256);
   }
 }
 
-// Raw scale bytes of one fragment row for K tile kt, as loaded.  Nothing is done
-// with them until the next K step (after its wait), so the loads stay in flight
-// together with the LDS prefetch; mx_scale_word() then arranges them.
-struct MxRaw {
-  uint32_t lo, hi;
-};
+// The j-th of this wave's tile copy instructions for sub-tile s (see copy_subtile).
+template <class Cfg, bool KTAIL>
+__device__ __forceinline__ void copy_one(const TileOperands& op, uint8_t* slot, int s, int j,
+                                         int wave, int lane) {
+  constexpr int nA = Cfg::BM / 16;
+  const int g = wave * Cfg::kTileLoads + j;     // wave-uniform instruction index
+  const bool isA = g < nA;
+  const int row_t = (isA ? g : g - nA) * 16 + (lane >> 2);
+  const int chunk = (lane & 3) ^ lds_swz(row_t);
+  int kc = s * Cfg::kBK + 16 * chunk;
+  if (KTAIL && kc >= op.K) kc = 0;
+  const uint8_t* base = isA ? op.A : op.B;
+  const int64_t ld = isA ? op.lda : op.ldb;
+  const int rows = isA ? op.a_rows : op.b_rows;
+  const int row = row_t < rows ? row_t : rows - 1;
+  lds_dma16(base + (int64_t)row * ld + kc, slot + g * 1024);
+}
 
-template <bool KALIGNED>
-__device__ __forceinline__ MxRaw load_mx_scales(const uint8_t* s, int row, int kt, int nblk,
-                                                int h) {
-  const uint8_t* p = s + (int64_t)row * nblk;
-  MxRaw r;
-  if (KALIGNED) {
-    r.lo = *reinterpret_cast<const uint32_t*>(p + 4 * kt);  // blocks 4kt .. 4kt+3
-    r.hi = 0;
-  } else {
-    const int b0 = 4 * kt + h, b1 = b0 + 2;
-    r.lo = b0 < nblk ? p[b0] : 127u;
-    r.hi = b1 < nblk ? p[b1] : 127u;
+// The j-th of this wave's dword copy instructions (see dword_rows_ab).
+template <class Cfg>
+__device__ __forceinline__ void dword_one(const uint8_t* pa, int64_t lda, int a_rows,
+                                          const uint8_t* pb, int64_t ldb, int b_rows, int byte_off,
+                                          uint8_t* dst, int j, int wave, int lane) {
+  constexpr int nA = Cfg::BM / 64;
+  int i = wave * Cfg::kScaleLoads + j;
+  i = i < Cfg::kScaleInsts ? i : Cfg::kScaleInsts - 1;
+  const bool isA = i < nA;
+  const uint8_t* base = isA ? pa : pb;
+  const int64_t ld = isA ? lda : ldb;
+  const int rows = isA ? a_rows : b_rows;
+  const int row_t = (isA ? i : i - nA) * 64 + lane;
+  const int row = row_t < rows ? row_t : rows - 1;
+  lds_dma4(base + (int64_t)row * ld + byte_off, dst + i * 256);
+}
+
+// One 16-byte fragment read: r < 2*FM -> A fragment r/2, else B fragment; r odd ->
+// the second K chunk.  Zeroed when it lies past K (KTAIL).
+template <class Cfg, bool KTAIL>
+__device__ __forceinline__ v4i read_one(const uint8_t* slot, int r, int k0, int K,
+                                        const int (&arow)[Cfg::kFragM],
+                                        const int (&brow)[Cfg::kFragN], int h) {
+  const bool isA = r < 2 * Cfg::kFragM;
+  const int idx = isA ? r >> 1 : (r - 2 * Cfg::kFragM) >> 1;
+  const int row = isA ? arow[idx] : Cfg::BM + brow[idx];
+  const int c = h + 2 * (r & 1);
+  v4i v = *reinterpret_cast<const v4i*>(slot + row * Cfg::kBK + 16 * (c ^ lds_swz(row)));
+  if (KTAIL && k0 + 16 * c >= K) v = v4i{};
+  return v;
+}
+
+// Operand fragments of one sub-tile for all of a wave's MFMA blocks.
+template <class Cfg, bool KTAIL>
+__device__ __forceinline__ void read_frags(const uint8_t* slot, int k0, int K,
+                                           const int (&arow)[Cfg::kFragM],
+                                           const int (&brow)[Cfg::kFragN], int h,
+                                           v8i (&af)[Cfg::kFragM], v8i (&bf)[Cfg::kFragN]) {
+  const int c0 = h, c1 = h + 2;
+  bool z0 = false, z1 = false;
+  if (KTAIL) {
+    z0 = k0 + 16 * c0 >= K;
+    z1 = k0 + 16 * c1 >= K;
   }
-  return r;
+  const uint8_t* sB = slot + Cfg::BM * Cfg::kBK;
+#pragma unroll
+  for (int i = 0; i < Cfg::kFragM; ++i) {
+    const uint8_t* rowp = slot + arow[i] * Cfg::kBK;
+    const int sw = lds_swz(arow[i]);
+    v4i lo = *reinterpret_cast<const v4i*>(rowp + 16 * (c0 ^ sw));
+    v4i hi = *reinterpret_cast<const v4i*>(rowp + 16 * (c1 ^ sw));
+    if (KTAIL) {
+      if (z0) lo = v4i{};
+      if (z1) hi = v4i{};
+    }
+    af[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+#pragma unroll
+  for (int j = 0; j < Cfg::kFragN; ++j) {
+    const uint8_t* rowp = sB + brow[j] * Cfg::kBK;
+    const int sw = lds_swz(brow[j]);
+    v4i lo = *reinterpret_cast<const v4i*>(rowp + 16 * (c0 ^ sw));
+    v4i hi = *reinterpret_cast<const v4i*>(rowp + 16 * (c1 ^ sw));
+    if (KTAIL) {
+      if (z0) lo = v4i{};
+      if (z1) hi = v4i{};
+    }
+    bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
 }
 
-// Scale register for both MFMA K halves of a K tile: byte0 = block 4kt + h (first
-// half), byte2 = block 4kt + 2 + h (second half), h = lane/32.
-template <bool KALIGNED>
-__device__ __forceinline__ uint32_t mx_scale_word(MxRaw r, int h) {
-  if (KALIGNED) return r.lo >> (8 * h);
-  return r.lo | (r.hi << 16);
+// All MFMA blocks of a wave for one sub-tile.  B is the instruction's first
+// operand (rows n), A the second (columns m): the accumulators hold C^T blocks.
+template <class Cfg, int MODE>
+__device__ __forceinline__ void mfma_subtile(v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                             const v8i (&af)[Cfg::kFragM],
+                                             const v8i (&bf)[Cfg::kFragN],
+                                             const uint32_t (&sa)[Cfg::kFragM],
+                                             const uint32_t (&sb)[Cfg::kFragN]) {
+#pragma unroll
+  for (int i = 0; i < Cfg::kFragM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::kFragN; ++j) {
+      if (MODE == kMx32) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            bf[j], af[i], acc[i][j], 0, 0, 0, (int)sb[j], 0, (int)sa[i]);
+      } else {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], 0,
+                                                                    0, 0, 0, 0, 0);
+      }
+    }
 }
 
+// Interleaving hint for one sub-tile region (AMDGPU scheduler group masks: 0x008
+// MFMA, 0x020 VMEM read, 0x100 DS read): LDS reads early, copies spread out.
+template <class Cfg, int NVMEM, int NDS>
+__device__ __forceinline__ void sched_subtile() {
+#if FP8GEMM_SCHED
+  constexpr int kMfma = Cfg::kFragM * Cfg::kFragN;
+  constexpr int kD = (NDS + kMfma / 2 - 1) / (kMfma / 2);   // reads in the first half
+  constexpr int kV = (NVMEM + kMfma - 1) / kMfma;
+#pragma unroll
+  for (int i = 0; i < kMfma; ++i) {
+    if (i < kMfma / 2) __builtin_amdgcn_sched_group_barrier(0x100, kD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, kV, 0);
+  }
+#endif
+}
+
+// The K loop of one tile.  Per sub-tile t (64 K):
+//   wait: own copies of sub-tile t+1 landed (the S-2 newer sub-tiles may stay
+//         in flight) and own LDS reads done; workgroup barrier
+//   copy sub-tile t+S into slot t%S (free: its fragments are in registers) and,
+//         every 128 K, the MX codes of that K tile
+//   LDS reads of sub-tile t+1 (and MX codes)     || MFMAs of sub-tile t
+// The loop runs an even number of sub-tiles (K tails are zero-filled) and copies
+// past the end re-fetch the last sub-tile, so counts per sub-tile are constant.
+// With K % 128 != 0 the MX codes are read with byte loads and every wait drains
+// all copies (a rarely used, simpler path).
 template <class Cfg, int MODE, bool KALIGNED>
 __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
                                          v16f (&acc)[Cfg::kFragM][Cfg::kFragN]) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   constexpr bool KTAIL = !KALIGNED;
+  constexpr bool kMxLds = (MODE == kMx32) && KALIGNED;
+  constexpr bool kMxReg = (MODE == kMx32) && !KALIGNED;
+  // copies issued per sub-tile by this wave: even sub-tiles also carry MX codes
+  constexpr int S = Cfg::kSlots;
+  constexpr int kLoadsOdd = Cfg::kTileLoads;
+  constexpr int kLoadsEven = Cfg::kTileLoads + (kMxLds ? Cfg::kScaleLoads : 0);
+  // copies allowed in flight at the barrier of an even / odd sub-tile t: those of
+  // sub-tiles t+2 .. t+S-1; in the prologue: sub-tiles 1 .. S-1
+  constexpr int kWaitEven = ((S - 2) / 2) * (kLoadsOdd + kLoadsEven) + ((S - 2) % 2) * kLoadsEven;
+  constexpr int kWaitOdd = ((S - 2) / 2) * (kLoadsOdd + kLoadsEven) + ((S - 2) % 2) * kLoadsOdd;
+  constexpr int kWaitPrologue = ((S - 1) / 2) * (kLoadsOdd + kLoadsEven) + ((S - 1) % 2) * kLoadsOdd;
+  static_assert(kWaitPrologue < 64, "vmcnt range");
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
   const int h = lane >> 5;
-  const int nk = (op.K + Cfg::kBK - 1) / Cfg::kBK;
+  const int nsub = ((op.K + 127) / 128) * 2;     // even number of 64-K sub-tiles
+  const int nvalid = (op.K + Cfg::kBK - 1) / Cfg::kBK;
   const int nblk = op.K / 32;
 
 #pragma unroll
@@ -151,144 +346,519 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
-  // fragment rows (tile-local) of this lane
-  int arow[FM], brow[FN];
+  int arow[FM], brow[FN];        // tile-local fragment rows of this lane
 #pragma unroll
   for (int i = 0; i < FM; ++i) arow[i] = wm * Cfg::WM + i * 32 + (lane & 31);
 #pragma unroll
   for (int j = 0; j < FN; ++j) brow[j] = wn * Cfg::WN + j * 32 + (lane & 31);
 
-  MxRaw sa_nxt[FM], sb_nxt[FN];
-  uint32_t sa_cur[FM], sb_cur[FN];
-  auto load_scales = [&](int kt) {
-    if (MODE == kMx32) {
+  auto slot_ptr = [&](int s) { return lds + (s % S) * Cfg::kSlotBytes; };
+  auto copy = [&](int s) {
+    const int sc = s < nvalid ? s : nvalid - 1;  // past the end: harmless re-fetch
+    copy_subtile<Cfg, KTAIL>(op, slot_ptr(s), sc, wave, lane);
+    if (kMxLds && (s & 1) == 0) {
+      dword_rows_ab<Cfg>(op.sa, nblk, op.a_rows, op.sb, nblk, op.b_rows, 4 * (sc >> 1),
+                         lds + Cfg::kScaleOff + ((s >> 1) & 1) * Cfg::kScaleSlotBytes, wave,
+                         lane);
+    }
+  };
+
+  // MX scale registers.  K % 128 == 0: one word per fragment row and K tile,
+  // pre-shifted so byte 0 / byte 2 are the codes of its even / odd sub-tile
+  // (cur = this K tile, nxt = the next).  Otherwise: the code of the current /
+  // next sub-tile in byte 0.
+  uint32_t sa_cur[FM], sb_cur[FN], sa_nxt[FM], sb_nxt[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = arow[i] < op.a_rows ? arow[i] : op.a_rows - 1;
-        sa_nxt[i] = load_mx_scales<KALIGNED>(op.sa, r, kt, nblk, h);
+  for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i] = 0;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) sb_cur[j] = sb_nxt[j] = 0;
+  // words of K tile kt (resident in scale slot kt & 1)
+  auto read_lds_codes = [&](int kt, uint32_t (&a)[FM], uint32_t (&b)[FN]) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(lds + Cfg::kScaleOff +
+                                                          (kt & 1) * Cfg::kScaleSlotBytes);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) a[i] = w[arow[i]] >> (8 * h);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b[j] = w[Cfg::BM + brow[j]] >> (8 * h);
+  };
+  // codes of sub-tile s straight from global memory (K % 128 != 0): block 2s + h
+  auto load_reg_codes = [&](int s, uint32_t (&a)[FM], uint32_t (&b)[FN]) {
+    const int blk = 2 * s + h;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = arow[i] < op.a_rows ? arow[i] : op.a_rows - 1;
+      a[i] = blk < nblk ? op.sa[(int64_t)r * nblk + blk] : 127u;
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = brow[j] < op.b_rows ? brow[j] : op.b_rows - 1;
+      b[j] = blk < nblk ? op.sb[(int64_t)r * nblk + blk] : 127u;
+    }
+  };
+
+  v8i af0[FM], bf0[FN], af1[FM], bf1[FN];
+
+  // prologue: sub-tiles 0..3 in flight; wait for sub-tile 0; its fragments in registers
+  if (MODE == kRowwise) {
+    dword_rows_ab<Cfg>(reinterpret_cast<const uint8_t*>(op.ra), 4, op.a_rows,
+                       reinterpret_cast<const uint8_t*>(op.rb), 4, op.b_rows, 0,
+                       lds + Cfg::kRowScaleOff, wave, lane);
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s) copy(s);
+  if (KALIGNED) FP8GEMM_WAIT_VM_LGKM0(kWaitPrologue);
+  else __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  read_frags<Cfg, KTAIL>(slot_ptr(0), 0, op.K, arow, brow, h, af0, bf0);
+  if (kMxLds) read_lds_codes(0, sa_cur, sb_cur);
+  if (kMxReg) load_reg_codes(0, sa_cur, sb_cur);
+
+  // One sub-tile, issued in a fixed order (sched_barrier fences): for each MFMA q,
+  // the MFMA, then its share of the copy instructions of sub-tile t+S and of the
+  // LDS reads of sub-tile t+1.  The matrix pipe never waits behind a burst of
+  // memory instructions, and the copies / reads trickle out between MFMAs.
+  constexpr int kMfma = FM * FN;
+  constexpr int kReads = 2 * (FM + FN);
+  auto step = [&](int t, v8i (&fa)[FM], v8i (&fb)[FN], v8i (&na)[FM], v8i (&nb)[FN],
+                  auto odd_c) {
+    constexpr bool odd = decltype(odd_c)::value;
+    constexpr int kVmem = Cfg::kTileLoads + ((kMxLds && !odd) ? Cfg::kScaleLoads : 0);
+    constexpr int kDs = kReads + ((kMxLds && odd) ? FM + FN : 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!KALIGNED) __builtin_amdgcn_s_waitcnt(0);     // copies of sub-tile t+1 landed
+    else if (odd) FP8GEMM_WAIT_VM_LGKM0(kWaitOdd);
+    else FP8GEMM_WAIT_VM_LGKM0(kWaitEven);
+    __builtin_amdgcn_s_barrier();                      // ... for every wave; slot t%S free
+    __builtin_amdgcn_sched_barrier(0);
+    if (kMxReg) load_reg_codes(t + 1, sa_nxt, sb_nxt);
+    const int sn = t + S;                              // sub-tile to copy
+    const int sc = sn < nvalid ? sn : nvalid - 1;      // past the end: harmless re-fetch
+    uint8_t* cslot = slot_ptr(sn);
+    uint8_t* sslot = lds + Cfg::kScaleOff + ((sn >> 1) & 1) * Cfg::kScaleSlotBytes;
+    const uint8_t* rslot = slot_ptr(t + 1);
+    const int rk0 = (t + 1) * Cfg::kBK;
+    const uint32_t* wsc = reinterpret_cast<const uint32_t*>(
+        lds + Cfg::kScaleOff + (((t + 1) >> 1) & 1) * Cfg::kScaleSlotBytes);
+    v4i rd[kReads];
+#pragma unroll
+    for (int q = 0; q < kMfma; ++q) {
+      const int i = q / FN, j = q % FN;
+      if (MODE == kMx32) {
+        const uint32_t sa = (kMxLds && odd) ? sa_cur[i] >> 16 : sa_cur[i];
+        const uint32_t sb = (kMxLds && odd) ? sb_cur[j] >> 16 : sb_cur[j];
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0,
+                                                                    0, (int)sb, 0, (int)sa);
+      } else {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0,
+                                                                    0, 0, 0, 0, 0);
       }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = brow[j] < op.b_rows ? brow[j] : op.b_rows - 1;
-        sb_nxt[j] = load_mx_scales<KALIGNED>(op.sb, r, kt, nblk, h);
+      for (int v = q * kVmem / kMfma; v < (q + 1) * kVmem / kMfma; ++v) {
+        if (v < Cfg::kTileLoads) {
+          copy_one<Cfg, KTAIL>(op, cslot, sc, v, wave, lane);
+        } else if (kMxLds) {
+          dword_one<Cfg>(op.sa, nblk, op.a_rows, op.sb, nblk, op.b_rows, 4 * (sc >> 1), sslot,
+                         v - Cfg::kTileLoads, wave, lane);
+        }
+      }
+#pragma unroll
+      for (int d = q * kDs / kMfma; d < (q + 1) * kDs / kMfma; ++d) {
+        if (d < kReads) {
+          rd[d] = read_one<Cfg, KTAIL>(rslot, d, rk0, op.K, arow, brow, h);
+        } else if (kMxLds) {
+          const int e = d - kReads;
+          if (e < FM) sa_nxt[e] = wsc[arow[e]] >> (8 * h);
+          else sb_nxt[e - FM] = wsc[Cfg::BM + brow[e - FM]] >> (8 * h);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) na[i] = __builtin_shufflevector(rd[2 * i], rd[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      nb[j] = __builtin_shufflevector(rd[2 * FM + 2 * j], rd[2 * FM + 2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    if (kMxReg || (kMxLds && odd)) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sb_cur[j] = sb_nxt[j];
+    }
+  };
+
+  for (int t = 0; t < nsub; t += 2) {
+    step(t, af0, bf0, af1, bf1, std::false_type{});
+    step(t + 1, af1, bf1, af0, bf0, std::true_type{});
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0);     // no copy may still target LDS
+  __builtin_amdgcn_s_barrier();      // every wave is done with the ring
+}
+
+// ---------------------------------------------------------------------------
+// Interior tiles: the same ring, waits and barriers as mainloop(), with no
+// vector-ALU work inside the K loop.  On gfx950 every VALU instruction that the
+// single wavefront of a SIMD issues between its MFMAs delays the next MFMA, so
+// all per-sub-tile addressing is moved to scalar registers and instruction
+// offsets:
+//   * copies go through buffer descriptors of the tile's A / B rows: the lane
+//     offset (row within the 16-row block, swizzled chunk) is the same for every
+//     instruction and sub-tile, the row block and K offset are a scalar soffset;
+//   * the loop is unrolled over the 4-slot ring, so the slot of every LDS read is
+//     a constant folded into the ds_read offset field;
+//   * MX codes are read from LDS as single bytes (the one of this lane's 32-K
+//     block), so the MFMA takes them without a shift.
+// Conditions: every row of the tile is valid, K % 128 == 0, and the byte span of
+// a tile's rows fits a 32-bit buffer offset.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  // gfx9 raw buffer descriptor: no stride, no swizzle, 32-bit data format word
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ void buffer_dma16(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int voff,
+                                             int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ void buffer_dma4(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int voff,
+                                            int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 4,
+                                           voff, soff, 0, 0);
+}
+
+// An opaque copy of v: the compiler cannot fold constants through it, so an LDS
+// base stays in one register and the slot offsets stay in the ds_read offset field.
+__device__ __forceinline__ int opaque(int v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
+// Whether a tile takes the interior path (uniform over the workgroup).
+template <class Cfg>
+__device__ __forceinline__ bool interior_tile(const TileOperands& op) {
+  return op.a_rows >= Cfg::BM && op.b_rows >= Cfg::BN && op.K % 128 == 0 &&
+         (int64_t)Cfg::BM * op.lda + op.K < ((int64_t)1 << 31) &&
+         (int64_t)Cfg::BN * op.ldb + op.K < ((int64_t)1 << 31);
+}
+
+#ifndef FP8GEMM_READ_SPAN
+#define FP8GEMM_READ_SPAN 8    // eighths of a sub-tile's MFMAs over which its reads are spread
+#endif
+
+template <class Cfg, int MODE>
+__device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_t* lds,
+                                                  v16f (&acc)[Cfg::kFragM][Cfg::kFragN]) {
+  constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN, S = Cfg::kSlots;
+  constexpr bool kMx = MODE == kMx32;
+  constexpr int nA = Cfg::BM / 16;               // 16-row copy blocks of A
+  static_assert(S == 4, "the loop is unrolled over a 4-slot ring");
+  static_assert(nA % Cfg::kTileLoads == 0, "each wave copies rows of one operand only");
+  constexpr int kLoadsOdd = Cfg::kTileLoads;
+  constexpr int kLoadsEven = Cfg::kTileLoads + (kMx ? Cfg::kScaleLoads : 0);
+  // in flight at a sub-tile's barrier: the copies of the next two sub-tiles but one
+  constexpr int kWait = kLoadsOdd + kLoadsEven;
+  constexpr int kWaitPrologue = 2 * kLoadsOdd + kLoadsEven;
+  static_assert(kWaitPrologue < 64, "vmcnt range");
+  // LDS slots reachable from one base register through the 16-bit offset field
+  constexpr int kMaxImm = (FM > FN ? FM - 1 : FN - 1) * 32 * Cfg::kBK;
+  constexpr int kPerBase = (3 * Cfg::kSlotBytes + kMaxImm < 65536)   ? 4
+                           : (Cfg::kSlotBytes + kMaxImm < 65536)     ? 2
+                                                                     : 1;
+  constexpr int kBases = S / kPerBase;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
+  const int h = lane >> 5;
+  const int nsub = op.K / Cfg::kBK;              // even
+  const int nblk = op.K / 32;
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
+
+  // ---- copy side (scalar except one lane offset) ----
+  const int g0 = wave * Cfg::kTileLoads;         // first 16-row block of this wave
+  const bool cpA = g0 < nA;
+  const int blk0 = cpA ? g0 : g0 - nA;
+  const int ld = cpA ? (int)op.lda : (int)op.ldb;
+  const __amdgpu_buffer_rsrc_t rs =
+      cpA ? buffer_rsrc(op.A, (uint32_t)((Cfg::BM - 1) * op.lda + op.K))
+          : buffer_rsrc(op.B, (uint32_t)((Cfg::BN - 1) * op.ldb + op.K));
+  const int sub = lane >> 2;
+  const int voff = sub * ld + 16 * ((lane & 3) ^ ((sub >> 2) & 3));
+  uint8_t* const cdst = lds + g0 * 1024;
+  // MX codes: one dword (four 32-K blocks) per row and 128 K; 64 rows per instruction
+  const __amdgpu_buffer_rsrc_t rcA = buffer_rsrc(op.sa, (uint32_t)(Cfg::BM * nblk));
+  const __amdgpu_buffer_rsrc_t rcB = buffer_rsrc(op.sb, (uint32_t)(Cfg::BN * nblk));
+  const int cvoff = lane * nblk;
+  auto copy = [&](int s, auto slot_c) {          // sub-tile s (clamped) into ring slot P
+    constexpr int P = decltype(slot_c)::value;
+    const int sc = s < nsub ? s : nsub - 1;      // past the end: harmless re-fetch
+#pragma unroll
+    for (int j = 0; j < Cfg::kTileLoads; ++j)
+      buffer_dma16(rs, cdst + P * Cfg::kSlotBytes + j * 1024, voff,
+                     (blk0 + j) * 16 * ld + sc * Cfg::kBK);
+    if (kMx && (P & 1) == 0) {
+#pragma unroll
+      for (int jj = 0; jj < Cfg::kScaleLoads; ++jj) {
+        int i = wave * Cfg::kScaleLoads + jj;
+        i = i < Cfg::kScaleInsts ? i : Cfg::kScaleInsts - 1;
+        const bool isA = i < Cfg::BM / 64;
+        const int li = isA ? i : i - Cfg::BM / 64;
+        buffer_dma4(isA ? rcA : rcB,
+                      lds + Cfg::kScaleOff + ((P >> 1) & 1) * Cfg::kScaleSlotBytes + i * 256, cvoff,
+                      li * 64 * nblk + 4 * (sc >> 1));
       }
     }
   };
 
-  load_stage<Cfg, KTAIL>(op, lds, 0, wave, lane);
-  load_scales(0);
+  // ---- read side: per-lane LDS bases, constant offsets ----
+  const int swz = (lane >> 2) & 3;
+  const int ra = (wm * Cfg::WM + (lane & 31)) * Cfg::kBK;
+  const int rb = (Cfg::BM + wn * Cfg::WN + (lane & 31)) * Cfg::kBK;
+  const int clo = 16 * (h ^ swz), chi = 16 * ((h + 2) ^ swz);
+  int bal[kBases], bah[kBases], bbl[kBases], bbh[kBases];
+#pragma unroll
+  for (int b = 0; b < kBases; ++b) {
+    const int o = b * kPerBase * Cfg::kSlotBytes;
+    bal[b] = opaque(ra + clo + o);
+    bah[b] = opaque(ra + chi + o);
+    bbl[b] = opaque(rb + clo + o);
+    bbh[b] = opaque(rb + chi + o);
+  }
+  const int csa = opaque(Cfg::kScaleOff + (wm * Cfg::WM + (lane & 31)) * 4 + h);
+  const int csb = opaque(Cfg::kScaleOff + (Cfg::BM + wn * Cfg::WN + (lane & 31)) * 4 + h);
+  auto rd16 = [&](int addr) { return *reinterpret_cast<const v4i*>(lds + addr); };
+  auto rd8 = [&](int addr) { return (uint32_t)lds[addr]; };
 
-  for (int kt = 0; kt < nk; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of stage kt have landed
-    __syncthreads();                 // ... and everyone's; stage kt+1's slot is free
-    if (MODE == kMx32) {
+  // codes[set][parity][fragment]: set = K tile parity, parity = sub-tile in K tile
+  uint32_t ca[2][2][FM], cb[2][2][FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) sa_cur[i] = mx_scale_word<KALIGNED>(sa_nxt[i], h);
+  for (int z = 0; z < 2; ++z)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sb_cur[j] = mx_scale_word<KALIGNED>(sb_nxt[j], h);
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) ca[z][p][i] = 0;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) cb[z][p][j] = 0;
     }
-    if (kt + 1 < nk) {
-      load_stage<Cfg, KTAIL>(op, lds + ((kt + 1) & 1) * Cfg::kStageBytes, (kt + 1) * Cfg::kBK,
-                             wave, lane);
-      load_scales(kt + 1);
-    }
-    const uint8_t* sA = lds + (kt & 1) * Cfg::kStageBytes;
-    const uint8_t* sB = sA + Cfg::BM * Cfg::kBK;
-    const int k0 = kt * Cfg::kBK;
+  // codes of the K tile resident in scale slot z into set zz
+  auto read_codes = [&](int z, uint32_t (&a)[2][FM], uint32_t (&b)[2][FN], int e) {
+    // e-th of the 2 * (FM + FN) byte reads
+    const int p = e / (FM + FN), f = e % (FM + FN);
+    const int off = z * Cfg::kScaleSlotBytes + 2 * p;
+    if (f < FM) a[p][f] = rd8(csa + off + f * 128);
+    else b[p][f - FM] = rd8(csb + off + (f - FM) * 128);
+  };
+
+  v8i af0[FM], bf0[FN], af1[FM], bf1[FN];
+  auto read_frag = [&](auto slot_c, int d, v4i (&rd)[2 * (FM + FN)]) {
+    constexpr int P = decltype(slot_c)::value;
+    constexpr int b = P / kPerBase, o = (P % kPerBase) * Cfg::kSlotBytes;
+    const bool isA = d < 2 * FM;
+    const int f = isA ? d >> 1 : (d - 2 * FM) >> 1;
+    if (isA) rd[d] = rd16(((d & 1) ? bah[b] : bal[b]) + o + f * 32 * Cfg::kBK);
+    else rd[d] = rd16(((d & 1) ? bbh[b] : bbl[b]) + o + f * 32 * Cfg::kBK);
+  };
+
+  // ---- prologue ----
+  if (MODE == kRowwise) {
+    dword_rows_ab<Cfg>(reinterpret_cast<const uint8_t*>(op.ra), 4, op.a_rows,
+                       reinterpret_cast<const uint8_t*>(op.rb), 4, op.b_rows, 0,
+                       lds + Cfg::kRowScaleOff, wave, lane);
+  }
+  copy(0, std::integral_constant<int, 0>{});
+  copy(1, std::integral_constant<int, 1>{});
+  copy(2, std::integral_constant<int, 2>{});
+  copy(3, std::integral_constant<int, 3>{});
+  FP8GEMM_WAIT_VM_LGKM0(kWaitPrologue);
+  __builtin_amdgcn_s_barrier();
+  {
+    v4i rd[2 * (FM + FN)];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c0 = 4 * kk + h, c1 = c0 + 2;
-      bool z0 = false, z1 = false;
-      if (KTAIL) {
-        z0 = k0 + 16 * c0 >= op.K;
-        z1 = k0 + 16 * c1 >= op.K;
-      }
-      v8i af[FM], bf[FN];
+    for (int d = 0; d < 2 * (FM + FN); ++d) read_frag(std::integral_constant<int, 0>{}, d, rd);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint8_t* rowp = sA + arow[i] * Cfg::kBK;
-        const int sw = arow[i] & 7;
-        v4i lo = *reinterpret_cast<const v4i*>(rowp + 16 * (c0 ^ sw));
-        v4i hi = *reinterpret_cast<const v4i*>(rowp + 16 * (c1 ^ sw));
-        if (KTAIL) {
-          if (z0) lo = v4i{};
-          if (z1) hi = v4i{};
-        }
-        af[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+    for (int i = 0; i < FM; ++i) af0[i] = __builtin_shufflevector(rd[2 * i], rd[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint8_t* rowp = sB + brow[j] * Cfg::kBK;
-        const int sw = brow[j] & 7;
-        v4i lo = *reinterpret_cast<const v4i*>(rowp + 16 * (c0 ^ sw));
-        v4i hi = *reinterpret_cast<const v4i*>(rowp + 16 * (c1 ^ sw));
-        if (KTAIL) {
-          if (z0) lo = v4i{};
-          if (z1) hi = v4i{};
-        }
-        bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+    for (int j = 0; j < FN; ++j)
+      bf0[j] = __builtin_shufflevector(rd[2 * FM + 2 * j], rd[2 * FM + 2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    if (kMx) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          if (MODE == kMx32) {
-            const int scb = (int)(sb_cur[j] >> (16 * kk));
-            const int sca = (int)(sa_cur[i] >> (16 * kk));
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                bf[j], af[i], acc[i][j], 0, 0, 0, scb, 0, sca);
-          } else {
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                bf[j], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
-          }
-        }
+      for (int e = 0; e < 2 * (FM + FN); ++e) read_codes(0, ca[0], cb[0], e);
     }
   }
+
+  // ---- one sub-tile t = 4u + P ----
+  constexpr int kMfma = FM * FN;
+  constexpr int kReads = 2 * (FM + FN);
+  constexpr int kReadSpan = (kMfma * FP8GEMM_READ_SPAN + 7) / 8 > 0 ? (kMfma * FP8GEMM_READ_SPAN + 7) / 8 : 1;
+  auto step = [&](int t, auto slot_c, v8i (&fa)[FM], v8i (&fb)[FN], v8i (&na)[FM], v8i (&nb)[FN]) {
+    constexpr int P = decltype(slot_c)::value;
+    constexpr bool odd = P & 1;
+    constexpr int Z = P >> 1, PAR = P & 1;        // code set and parity used here
+    constexpr int kVmem = Cfg::kTileLoads + ((kMx && !odd) ? Cfg::kScaleLoads : 0);
+    constexpr int kDs = kReads + ((kMx && odd) ? 2 * (FM + FN) : 0);
+    __builtin_amdgcn_sched_barrier(0);
+    FP8GEMM_WAIT_VM_LGKM0(kWait);                 // own copies of sub-tile t+1 landed
+    __builtin_amdgcn_s_barrier();                 // ... everyone's; slot P is free
+    __builtin_amdgcn_sched_barrier(0);
+    const int sc = (t + S) < nsub ? t + S : nsub - 1;
+    v4i rd[kReads];
+#pragma unroll
+    for (int q = 0; q < kMfma; ++q) {
+      const int i = q / FN, j = q % FN;
+      if (kMx) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fb[j], fa[i], acc[i][j], 0, 0, 0, (int)cb[Z][PAR][j], 0, (int)ca[Z][PAR][i]);
+      } else {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0,
+                                                                    0, 0, 0, 0, 0);
+      }
+      // copy instructions of sub-tile t+4, spread evenly
+#pragma unroll
+      for (int v = q * kVmem / kMfma; v < (q + 1) * kVmem / kMfma; ++v) {
+        if (v < Cfg::kTileLoads) {
+          buffer_dma16(rs, cdst + P * Cfg::kSlotBytes + v * 1024, voff,
+                         (blk0 + v) * 16 * ld + sc * Cfg::kBK);
+        } else if (kMx) {
+          int ci = wave * Cfg::kScaleLoads + (v - Cfg::kTileLoads);
+          ci = ci < Cfg::kScaleInsts ? ci : Cfg::kScaleInsts - 1;
+          const bool isA = ci < Cfg::BM / 64;
+          const int li = isA ? ci : ci - Cfg::BM / 64;
+          buffer_dma4(isA ? rcA : rcB, lds + Cfg::kScaleOff + Z * Cfg::kScaleSlotBytes + ci * 256,
+                        cvoff, li * 64 * nblk + 4 * (sc >> 1));
+        }
+      }
+      // LDS reads of sub-tile t+1 (slot P+1) and, on odd sub-tiles, the next K
+      // tile's codes, spread over the first kReadSpan MFMAs
+      if (q < kReadSpan) {
+#pragma unroll
+        for (int d = q * kDs / kReadSpan; d < (q + 1) * kDs / kReadSpan; ++d) {
+          if (d < kReads) {
+            read_frag(std::integral_constant<int, (P + 1) % S>{}, d, rd);
+          } else if (kMx) {
+            // next K tile sits in scale slot ((P + 1) >> 1) & 1 and goes to set Z ^ 1
+            read_codes(((P + 1) >> 1) & 1, ca[Z ^ 1], cb[Z ^ 1], d - kReads);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) na[i] = __builtin_shufflevector(rd[2 * i], rd[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      nb[j] = __builtin_shufflevector(rd[2 * FM + 2 * j], rd[2 * FM + 2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  int t = 0;
+  for (; t + 4 <= nsub; t += 4) {
+    step(t, std::integral_constant<int, 0>{}, af0, bf0, af1, bf1);
+    step(t + 1, std::integral_constant<int, 1>{}, af1, bf1, af0, bf0);
+    step(t + 2, std::integral_constant<int, 2>{}, af0, bf0, af1, bf1);
+    step(t + 3, std::integral_constant<int, 3>{}, af1, bf1, af0, bf0);
+  }
+  if (t < nsub) {                                  // nsub % 4 == 2
+    step(t, std::integral_constant<int, 0>{}, af0, bf0, af1, bf1);
+    step(t + 1, std::integral_constant<int, 1>{}, af1, bf1, af0, bf0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0);     // no copy may still target LDS
+  __builtin_amdgcn_s_barrier();      // every wave is done with the ring
 }
 
-// Scale, round and store a tile.  m0/n0: global coordinates of the tile origin;
-// rows at or past m_end / columns at or past N are not stored.  Output row m
-// lives at C + m * ldc.
+// Scale, round and store a tile through LDS.  m0/n0: global coordinates of the
+// tile origin; rows at or past m_end and columns at or past N are not stored.
+// Output row m lives at C + m * ldc (ldc * sizeof(OutT) a multiple of 16 and C
+// 16-byte aligned).  The LDS ring must be idle (mainloop() ends with a barrier);
+// row-wise scales are read from the LDS copy mainloop() made.
 template <class Cfg, int MODE, typename OutT>
-__device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN], OutT* C,
-                                         int64_t ldc, int m0, int m_end, int n0, int N,
-                                         float tensor_scale, const float* row_sa,
-                                         const float* col_sb) {
+__device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN], uint8_t* lds,
+                                         OutT* C, int64_t ldc, int m0, int m_end, int n0, int N,
+                                         float tensor_scale) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
+  constexpr int kChunksPerRow = Cfg::WN * 2 / 16;        // 16-byte chunks of a staged row
+  constexpr int kRowsPerInst = 64 / kChunksPerRow;
+  static_assert(sizeof(OutT) == 2, "16-bit outputs");
+  static_assert(64 % kChunksPerRow == 0, "whole rows per store instruction");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
   const int h = lane >> 5;
+  uint8_t* stage = lds + wave * 32 * Cfg::kStagePitch;
+  const float* rsc = reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * Cfg::WM + i * 32 + (lane & 31);
-    if (m >= m_end) continue;
+    const int r = lane & 31;                             // staged row of this lane
     float fa = 1.0f;
     if (MODE == kTensor) fa = tensor_scale;
-    if (MODE == kRowwise) fa = row_sa[m];
-    OutT* crow = C + (int64_t)m * ldc;
+    if (MODE == kRowwise) fa = rsc[wm * Cfg::WM + i * 32 + r];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * Cfg::WN + j * 32 + 8 * g + 4 * h;
+        const int c = j * 32 + 8 * g + 4 * h;             // staged column of value 0
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * fa;
         if (MODE == kRowwise) {
+          const v4f fb = *reinterpret_cast<const v4f*>(rsc + Cfg::BM + wn * Cfg::WN + c);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] *= (n + e < N) ? col_sb[n + e] : 0.0f;
+          for (int e = 0; e < 4; ++e) v[e] *= fb[e];
         }
-        if (n + 3 < N) {
-          *reinterpret_cast<uint2*>(crow + n) = pack4<OutT>(v[0], v[1], v[2], v[3]);
-        } else {
+        *reinterpret_cast<uint2*>(stage + r * Cfg::kStagePitch + c * 2) =
+            pack4<OutT>(v[0], v[1], v[2], v[3]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0): staged rows written
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) crow[n + e] = to_out<OutT>(v[e]);
+    for (int q = 0; q < 32 / kRowsPerInst; ++q) {
+      const int rr = q * kRowsPerInst + lane / kChunksPerRow;
+      const int ch = lane % kChunksPerRow;
+      const v4i val = *reinterpret_cast<const v4i*>(stage + rr * Cfg::kStagePitch + ch * 16);
+      const int m = m0 + wm * Cfg::WM + i * 32 + rr;
+      const int n = n0 + wn * Cfg::WN + ch * 8;
+      if (m < m_end) {
+        OutT* dst = C + (int64_t)m * ldc + n;
+        if (n + 8 <= N) {
+          *reinterpret_cast<v4i*>(dst) = val;
+        } else {
+          OutT o[8];
+          __builtin_memcpy(o, &val, 16);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n + e < N) dst[e] = o[e];
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);                  // reads done before the next block
   }
+}
+
+// One output tile: the interior mainloop when the tile qualifies, else the
+// general (clamped) one, then the epilogue.  Each branch has its own accumulators
+// and epilogue so no accumulator copies join the two paths.
+template <class Cfg, int MODE, typename OutT, bool KALIGNED>
+__device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, OutT* C,
+                                          int64_t ldc, int m0, int m_end, int n0, int N,
+                                          float tensor_scale) {
+  if constexpr (KALIGNED && Cfg::kSlots == 4) {
+    if (interior_tile<Cfg>(op)) {
+      v16f acc[Cfg::kFragM][Cfg::kFragN];
+      mainloop_interior<Cfg, MODE>(op, lds, acc);
+      epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
+      return;
+    }
+  }
+  v16f acc[Cfg::kFragM][Cfg::kFragN];
+  mainloop<Cfg, MODE, KALIGNED>(op, lds, acc);
+  epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
 }
 
 }  // namespace fp8gemm

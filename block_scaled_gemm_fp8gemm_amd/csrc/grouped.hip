@@ -29,7 +29,8 @@ namespace {
 constexpr int kMaxGroups = 1024;
 
 template <class Cfg, int MODE, typename OutT, bool KALIGNED>
-__global__ __launch_bounds__(Cfg::kThreads) void grouped_kernel(GroupedProblem p, int tiles_n) {
+__global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void grouped_kernel(GroupedProblem p,
+                                                                                 int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::kLdsBytes];
   __shared__ int tile_start[kMaxGroups + 1];
   __shared__ int row_begin[kMaxGroups];
@@ -82,26 +83,35 @@ __global__ __launch_bounds__(Cfg::kThreads) void grouped_kernel(GroupedProblem p
     op.ldb = p.ldb;
     op.b_rows = p.N - n0;
     op.K = p.K;
+    op.sa = op.sb = nullptr;
+    op.ra = op.rb = nullptr;
     if (MODE == kMx32) {
       const int nblk = p.K / 32;
       op.sa = static_cast<const uint8_t*>(p.scale_a) + (int64_t)m0 * nblk;
       op.sb = static_cast<const uint8_t*>(p.scale_b) + ((int64_t)g * p.N + n0) * nblk;
-    } else {
-      op.sa = op.sb = nullptr;
+    }
+    if (MODE == kRowwise) {
+      op.ra = fsa + m0;
+      op.rb = fsb + (int64_t)g * p.N + n0;
     }
 
-    __syncthreads();  // the previous tile's last LDS reads are done
-    v16f acc[Cfg::kFragM][Cfg::kFragN];
-    mainloop<Cfg, MODE, KALIGNED>(op, lds, acc);
-
+    __syncthreads();  // the previous tile's epilogue is done with LDS
     const float ts = (MODE == kTensor) ? fsa[0] * fsb[g] : 1.0f;
-    const float* col_sb = (MODE == kRowwise) ? fsb + (int64_t)g * p.N : nullptr;
-    epilogue<Cfg, MODE, OutT>(acc, static_cast<OutT*>(p.C), p.ldc, m0, m_end, n0, p.N, ts, fsa,
-                              col_sb);
+    gemm_tile<Cfg, MODE, OutT, KALIGNED>(op, lds, static_cast<OutT*>(p.C), p.ldc, m0, m_end, n0,
+                                         p.N, ts);
   }
 }
 
-using Big = TileCfg<256, 256, 128, 128>;
+#ifndef FP8GEMM_BIG_CFG
+#define FP8GEMM_BIG_CFG 0
+#endif
+#if FP8GEMM_BIG_CFG == 0
+using Big = TileCfg<256, 256, 128, 128, 4, 1>;
+#else
+using Big = TileCfg<256, 128, 128, 64, 3, 2>;
+#endif
+// MX with K % 128 != 0 reads its codes into registers: the large tile would spill
+using Mid = TileCfg<128, 128, 64, 64, 4, 2>;
 
 template <class Cfg, int MODE, typename OutT>
 hipError_t launch_cfg(const GroupedProblem& p, hipStream_t stream) {
@@ -114,9 +124,10 @@ hipError_t launch_cfg(const GroupedProblem& p, hipStream_t stream) {
   const int tiles_n = (p.N + Cfg::BN - 1) / Cfg::BN;
   // never more workgroups than the largest possible tile count
   const int64_t max_tiles = (int64_t)((p.total_m + Cfg::BM - 1) / Cfg::BM + p.groups) * tiles_n;
-  const int grid = (int)(max_tiles < cus ? max_tiles : cus);
+  const int64_t slots = (int64_t)cus * Cfg::kWgPerCu;
+  const int grid = (int)(max_tiles < slots ? max_tiles : slots);
   if (grid <= 0) return hipSuccess;
-  if (p.K % Cfg::kBK == 0)
+  if (p.K % 128 == 0)
     hipLaunchKernelGGL((grouped_kernel<Cfg, MODE, OutT, true>), dim3(grid), dim3(Cfg::kThreads), 0,
                        stream, p, tiles_n);
   else
@@ -133,10 +144,12 @@ hipError_t launch_grouped_gemm(const GroupedProblem& p, int mode, int out, hipSt
   if (out == kF16) {
     if (mode == kTensor) return launch_cfg<Big, kTensor, _Float16>(p, stream);
     if (mode == kRowwise) return launch_cfg<Big, kRowwise, _Float16>(p, stream);
+    if (p.K % 128 != 0) return launch_cfg<Mid, kMx32, _Float16>(p, stream);
     return launch_cfg<Big, kMx32, _Float16>(p, stream);
   }
   if (mode == kTensor) return launch_cfg<Big, kTensor, __bf16>(p, stream);
   if (mode == kRowwise) return launch_cfg<Big, kRowwise, __bf16>(p, stream);
+  if (p.K % 128 != 0) return launch_cfg<Mid, kMx32, __bf16>(p, stream);
   return launch_cfg<Big, kMx32, __bf16>(p, stream);
 }
 
