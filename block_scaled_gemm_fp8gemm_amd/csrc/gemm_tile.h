@@ -79,7 +79,11 @@ struct TileCfg {
   static constexpr int kRowScaleBytes = (BM + BN) * 4;        // row-wise: fp32 per row / column
   static constexpr int kScaleOff = kSlots * kSlotBytes;
   static constexpr int kRowScaleOff = kScaleOff + kScaleSlots * kScaleSlotBytes;
-  static constexpr int kLdsBytes = kRowScaleOff + kRowScaleBytes;
+  // interior path, MX: two buffers of 16 code bytes (512 K) per row after the ring
+  static constexpr int kCodeBytes = 2 * (BM + BN) * 16;
+  static constexpr int kLdsBytes = kRowScaleOff + kRowScaleBytes > kScaleOff + kCodeBytes
+                                       ? kRowScaleOff + kRowScaleBytes
+                                       : kScaleOff + kCodeBytes;
   // copies per sub-tile and wavefront: 1 KiB (16 rows of 64 bytes) per instruction
   static constexpr int kTileLoads = (BM + BN) * kBK / 1024 / kWaves;
   // dword copies (MX codes per 128 K, row-wise scales) per wavefront: one dword per
@@ -496,20 +500,30 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
 }
 
 // ---------------------------------------------------------------------------
-// Interior tiles: the same ring, waits and barriers as mainloop(), with no
-// vector-ALU work inside the K loop.  On gfx950 every VALU instruction that the
-// single wavefront of a SIMD issues between its MFMAs delays the next MFMA, so
-// all per-sub-tile addressing is moved to scalar registers and instruction
-// offsets:
-//   * copies go through buffer descriptors of the tile's A / B rows: the lane
-//     offset (row within the 16-row block, swizzled chunk) is the same for every
-//     instruction and sub-tile, the row block and K offset are a scalar soffset;
-//   * the loop is unrolled over the 4-slot ring, so the slot of every LDS read is
-//     a constant folded into the ds_read offset field;
-//   * MX codes are read from LDS as single bytes (the one of this lane's 32-K
-//     block), so the MFMA takes them without a shift.
-// Conditions: every row of the tile is valid, K % 128 == 0, and the byte span of
-// a tile's rows fits a 32-bit buffer offset.
+// Interior tiles.  Two changes against mainloop(), both about the copy stream,
+// which bounds this kernel on gfx950:
+//   * Whole cache lines.  A copy instruction that reads 64 bytes from each of 16
+//     rows costs as many memory requests as one reading 128 bytes from each of
+//     them; measured on MI355X, 64-byte row pieces stream at about 14 TB/s and
+//     128-byte pieces at about 25 TB/s into LDS.  The ring therefore holds two
+//     128-K tiles of (BM + BN) rows x 128 bytes (the same 2 x 64 KiB for
+//     256 x 256), each tile is consumed as two 64-K MFMA steps, and the copies
+//     of K tile u + 2 go out while K tile u + 1 is consumed.
+//     LDS rows are 128 bytes; 16-byte chunk c of row r sits at chunk
+//     c ^ ((r >> 1) & 7), which spreads the 16 rows of a fragment read over all
+//     64 banks.
+//   * MX codes are fetched 16 bytes (512 K) per row at a time instead of 4 bytes
+//     per 128 K: each code copy touches one cache line per row, so this cuts its
+//     requests by four.
+// No vector-ALU work is left inside the K loop (each VALU instruction between
+// the MFMAs of the single wavefront of a SIMD delays the next MFMA): copies go
+// through buffer descriptors of the tile's rows with a loop-invariant lane
+// offset and a scalar offset; LDS reads use per-lane base registers with the
+// slot, K half and fragment folded into the instruction offset (the loop is
+// unrolled over the ring); MX codes are read as single bytes, the form the MFMA
+// takes.
+// Conditions: every row of the tile valid; K % 128 == 0 (MX: K % 512 == 0); the
+// byte span of a tile's rows fits a 32-bit buffer offset.
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
@@ -524,165 +538,172 @@ __device__ __forceinline__ void buffer_dma16(__amdgpu_buffer_rsrc_t rs, uint8_t*
                                            voff, soff, 0, 0);
 }
 
-__device__ __forceinline__ void buffer_dma4(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int voff,
-                                            int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 4,
-                                           voff, soff, 0, 0);
-}
-
 // An opaque copy of v: the compiler cannot fold constants through it, so an LDS
-// base stays in one register and the slot offsets stay in the ds_read offset field.
+// base stays in one register and the constant parts stay in the offset field.
 __device__ __forceinline__ int opaque(int v) {
   asm("" : "+v"(v));
   return v;
 }
 
 // Whether a tile takes the interior path (uniform over the workgroup).
-template <class Cfg>
+template <class Cfg, int MODE>
 __device__ __forceinline__ bool interior_tile(const TileOperands& op) {
-  return op.a_rows >= Cfg::BM && op.b_rows >= Cfg::BN && op.K % 128 == 0 &&
+  return op.a_rows >= Cfg::BM && op.b_rows >= Cfg::BN &&
+         op.K % (MODE == kMx32 ? 512 : 128) == 0 &&
          (int64_t)Cfg::BM * op.lda + op.K < ((int64_t)1 << 31) &&
          (int64_t)Cfg::BN * op.ldb + op.K < ((int64_t)1 << 31);
 }
 
 #ifndef FP8GEMM_READ_SPAN
-#define FP8GEMM_READ_SPAN 8    // eighths of a sub-tile's MFMAs over which its reads are spread
+#define FP8GEMM_READ_SPAN 4    // eighths of a step's MFMAs over which its LDS reads are spread
+#endif
+#ifndef FP8GEMM_COPY_SPAN
+#define FP8GEMM_COPY_SPAN 8    // eighths of a step's MFMAs over which its copies are spread
 #endif
 
 template <class Cfg, int MODE>
 __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_t* lds,
                                                   v16f (&acc)[Cfg::kFragM][Cfg::kFragN]) {
-  constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN, S = Cfg::kSlots;
+  constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   constexpr bool kMx = MODE == kMx32;
-  constexpr int nA = Cfg::BM / 16;               // 16-row copy blocks of A
-  static_assert(S == 4, "the loop is unrolled over a 4-slot ring");
-  static_assert(nA % Cfg::kTileLoads == 0, "each wave copies rows of one operand only");
-  constexpr int kLoadsOdd = Cfg::kTileLoads;
-  constexpr int kLoadsEven = Cfg::kTileLoads + (kMx ? Cfg::kScaleLoads : 0);
-  // in flight at a sub-tile's barrier: the copies of the next two sub-tiles but one
-  constexpr int kWait = kLoadsOdd + kLoadsEven;
-  constexpr int kWaitPrologue = 2 * kLoadsOdd + kLoadsEven;
-  static_assert(kWaitPrologue < 64, "vmcnt range");
-  // LDS slots reachable from one base register through the 16-bit offset field
-  constexpr int kMaxImm = (FM > FN ? FM - 1 : FN - 1) * 32 * Cfg::kBK;
-  constexpr int kPerBase = (3 * Cfg::kSlotBytes + kMaxImm < 65536)   ? 4
-                           : (Cfg::kSlotBytes + kMaxImm < 65536)     ? 2
-                                                                     : 1;
-  constexpr int kBases = S / kPerBase;
+  constexpr int kRowB = 128;                          // bytes per LDS row (one K tile)
+  constexpr int kTile = (Cfg::BM + Cfg::BN) * kRowB;  // one ring slot
+  constexpr int nA = Cfg::BM / 8;                     // 8-row copy blocks of A
+  constexpr int kLoads = kTile / 1024 / Cfg::kWaves;  // tile copies per wave and K tile
+  constexpr int kCodeInsts = (Cfg::BM + Cfg::BN) / 64;
+  constexpr int kCodeLoads = (kCodeInsts + Cfg::kWaves - 1) / Cfg::kWaves;
+  constexpr int kCodeBuf = (Cfg::BM + Cfg::BN) * 16;  // 16 code bytes per row
+  constexpr int kCodeOff = 2 * kTile;
+  static_assert(2 * kTile <= Cfg::kScaleOff, "ring fits");
+  static_assert(kCodeOff + 2 * kCodeBuf <= Cfg::kLdsBytes, "code buffers fit");
+  static_assert(kTile % (1024 * Cfg::kWaves) == 0, "equal copy share per wave");
+  static_assert(nA % kLoads == 0, "each wave copies rows of one operand only");
+  static_assert(kLoads % 2 == 0, "copy blocks of both swizzle phases per wave");
+  static_assert(kLoads < 64, "vmcnt range");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
   const int h = lane >> 5;
-  const int nsub = op.K / Cfg::kBK;              // even
+  const int nk = op.K / kRowB;                     // K tiles
+  const int nsub = 2 * nk;                         // 64-K MFMA steps
   const int nblk = op.K / 32;
+  const int ncode = nblk / 16;                     // 16-byte code groups per row
 
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
-  // ---- copy side (scalar except one lane offset) ----
-  const int g0 = wave * Cfg::kTileLoads;         // first 16-row block of this wave
+  // ---- copy side: scalar except two lane offsets ----
+  const int g0 = wave * kLoads;                   // first 8-row block of this wave
   const bool cpA = g0 < nA;
   const int blk0 = cpA ? g0 : g0 - nA;
   const int ld = cpA ? (int)op.lda : (int)op.ldb;
   const __amdgpu_buffer_rsrc_t rs =
       cpA ? buffer_rsrc(op.A, (uint32_t)((Cfg::BM - 1) * op.lda + op.K))
           : buffer_rsrc(op.B, (uint32_t)((Cfg::BN - 1) * op.ldb + op.K));
-  const int sub = lane >> 2;
-  const int voff = sub * ld + 16 * ((lane & 3) ^ ((sub >> 2) & 3));
+  // lane -> row (lane >> 3) of an 8-row block, LDS chunk lane & 7, global chunk
+  // (lane & 7) ^ ((row >> 1) & 7); the swizzle of even and odd blocks differs
+  const int crow = lane >> 3;
+  const int voff0 = crow * ld + 16 * ((lane & 7) ^ ((crow >> 1) & 7));
+  const int voff1 = crow * ld + 16 * ((lane & 7) ^ (((crow + 8) >> 1) & 7));
   uint8_t* const cdst = lds + g0 * 1024;
-  // MX codes: one dword (four 32-K blocks) per row and 128 K; 64 rows per instruction
   const __amdgpu_buffer_rsrc_t rcA = buffer_rsrc(op.sa, (uint32_t)(Cfg::BM * nblk));
   const __amdgpu_buffer_rsrc_t rcB = buffer_rsrc(op.sb, (uint32_t)(Cfg::BN * nblk));
   const int cvoff = lane * nblk;
-  auto copy = [&](int s, auto slot_c) {          // sub-tile s (clamped) into ring slot P
-    constexpr int P = decltype(slot_c)::value;
-    const int sc = s < nsub ? s : nsub - 1;      // past the end: harmless re-fetch
-#pragma unroll
-    for (int j = 0; j < Cfg::kTileLoads; ++j)
-      buffer_dma16(rs, cdst + P * Cfg::kSlotBytes + j * 1024, voff,
-                     (blk0 + j) * 16 * ld + sc * Cfg::kBK);
-    if (kMx && (P & 1) == 0) {
-#pragma unroll
-      for (int jj = 0; jj < Cfg::kScaleLoads; ++jj) {
-        int i = wave * Cfg::kScaleLoads + jj;
-        i = i < Cfg::kScaleInsts ? i : Cfg::kScaleInsts - 1;
-        const bool isA = i < Cfg::BM / 64;
-        const int li = isA ? i : i - Cfg::BM / 64;
-        buffer_dma4(isA ? rcA : rcB,
-                      lds + Cfg::kScaleOff + ((P >> 1) & 1) * Cfg::kScaleSlotBytes + i * 256, cvoff,
-                      li * 64 * nblk + 4 * (sc >> 1));
-      }
-    }
+
+  auto tile_copy = [&](int j, int slot, int kt) {       // j-th copy of K tile kt
+    buffer_dma16(rs, cdst + slot * kTile + j * 1024, (j & 1) ? voff1 : voff0,
+                 (blk0 + j) * 8 * ld + kt * kRowB);
+  };
+  auto code_copy = [&](int jj, int buf, int grp) {      // jj-th code copy of group grp
+    int ci = wave * kCodeLoads + jj;
+    ci = ci < kCodeInsts ? ci : kCodeInsts - 1;
+    const bool isA = ci < Cfg::BM / 64;
+    const int li = isA ? ci : ci - Cfg::BM / 64;
+    buffer_dma16(isA ? rcA : rcB, lds + kCodeOff + buf * kCodeBuf + ci * 1024, cvoff,
+                 li * 64 * nblk + 16 * grp);
   };
 
   // ---- read side: per-lane LDS bases, constant offsets ----
-  const int swz = (lane >> 2) & 3;
-  const int ra = (wm * Cfg::WM + (lane & 31)) * Cfg::kBK;
-  const int rb = (Cfg::BM + wn * Cfg::WN + (lane & 31)) * Cfg::kBK;
-  const int clo = 16 * (h ^ swz), chi = 16 * ((h + 2) ^ swz);
-  int bal[kBases], bah[kBases], bbl[kBases], bbh[kBases];
+  // fragment row r = wave base + 32 i + lane % 32; logical chunk 4p + 2c + h
+  // (K half p, chunk pair c) sits at (4p + 2c + h) ^ ((r >> 1) & 7)
+  const int rsw = ((lane & 31) >> 1) & 7;
+  const int ra = (wm * Cfg::WM + (lane & 31)) * kRowB;
+  const int rb = (Cfg::BM + wn * Cfg::WN + (lane & 31)) * kRowB;
+  int ba[2][2][2], bb[2][2][2];                        // [slot][half][chunk pair]
 #pragma unroll
-  for (int b = 0; b < kBases; ++b) {
-    const int o = b * kPerBase * Cfg::kSlotBytes;
-    bal[b] = opaque(ra + clo + o);
-    bah[b] = opaque(ra + chi + o);
-    bbl[b] = opaque(rb + clo + o);
-    bbh[b] = opaque(rb + chi + o);
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int ch = 16 * ((4 * p + 2 * c + h) ^ rsw);
+        ba[s][p][c] = opaque(s * kTile + ra + ch);
+        bb[s][p][c] = opaque(s * kTile + rb + ch);
+      }
+  // MX codes: byte 4 (u % 4) + 2 p + h of the row's 16-byte group u / 4; the
+  // group of the current K tile is in buffer `cur`, the next one in `nxt`
+  int cur_a = 0, cur_b = 0, nxt_a = 0, nxt_b = 0;
+  int cbuf = 0;                                        // buffer index of the current group
+  if (kMx) {
+    cur_a = opaque(kCodeOff + (wm * Cfg::WM + (lane & 31)) * 16 + h);
+    cur_b = opaque(kCodeOff + (Cfg::BM + wn * Cfg::WN + (lane & 31)) * 16 + h);
+    nxt_a = opaque(cur_a + kCodeBuf);
+    nxt_b = opaque(cur_b + kCodeBuf);
   }
-  const int csa = opaque(Cfg::kScaleOff + (wm * Cfg::WM + (lane & 31)) * 4 + h);
-  const int csb = opaque(Cfg::kScaleOff + (Cfg::BM + wn * Cfg::WN + (lane & 31)) * 4 + h);
-  auto rd16 = [&](int addr) { return *reinterpret_cast<const v4i*>(lds + addr); };
-  auto rd8 = [&](int addr) { return (uint32_t)lds[addr]; };
 
-  // codes[set][parity][fragment]: set = K tile parity, parity = sub-tile in K tile
-  uint32_t ca[2][2][FM], cb[2][2][FN];
+  auto rd16 = [&](int addr) { return *reinterpret_cast<const v4i*>(lds + addr); };
+  // the d-th 16-byte read of a step's fragments (slot s, half p)
+  auto read_frag = [&](auto s_c, auto p_c, int d, v4i (&rd)[2 * (FM + FN)]) {
+    constexpr int s = decltype(s_c)::value, p = decltype(p_c)::value;
+    const int c = d & 1;
+    if (d < 2 * FM) rd[d] = rd16(ba[s][p][c] + (d >> 1) * 32 * kRowB);
+    else rd[d] = rd16(bb[s][p][c] + ((d - 2 * FM) >> 1) * 32 * kRowB);
+  };
+  uint32_t ca[2][FM], cb[2][FN];                       // codes: [register set][fragment]
 #pragma unroll
-  for (int z = 0; z < 2; ++z)
+  for (int z = 0; z < 2; ++z) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int i = 0; i < FM; ++i) ca[z][i] = 0;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) ca[z][p][i] = 0;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) cb[z][p][j] = 0;
-    }
-  // codes of the K tile resident in scale slot z into set zz
-  auto read_codes = [&](int z, uint32_t (&a)[2][FM], uint32_t (&b)[2][FN], int e) {
-    // e-th of the 2 * (FM + FN) byte reads
-    const int p = e / (FM + FN), f = e % (FM + FN);
-    const int off = z * Cfg::kScaleSlotBytes + 2 * p;
-    if (f < FM) a[p][f] = rd8(csa + off + f * 128);
-    else b[p][f - FM] = rd8(csb + off + (f - FM) * 128);
+    for (int j = 0; j < FN; ++j) cb[z][j] = 0;
+  }
+  // the e-th code byte read of a step: K tile u with u % 4 == q, half p
+  auto read_code = [&](int base_a, int base_b, int q, int p, int e, uint32_t (&a)[FM],
+                       uint32_t (&b)[FN]) {
+    const int off = 4 * q + 2 * p;
+    if (e < FM) a[e] = lds[base_a + off + e * 32 * 16];
+    else b[e - FM] = lds[base_b + off + (e - FM) * 32 * 16];
   };
 
   v8i af0[FM], bf0[FN], af1[FM], bf1[FN];
-  auto read_frag = [&](auto slot_c, int d, v4i (&rd)[2 * (FM + FN)]) {
-    constexpr int P = decltype(slot_c)::value;
-    constexpr int b = P / kPerBase, o = (P % kPerBase) * Cfg::kSlotBytes;
-    const bool isA = d < 2 * FM;
-    const int f = isA ? d >> 1 : (d - 2 * FM) >> 1;
-    if (isA) rd[d] = rd16(((d & 1) ? bah[b] : bal[b]) + o + f * 32 * Cfg::kBK);
-    else rd[d] = rd16(((d & 1) ? bbh[b] : bbl[b]) + o + f * 32 * Cfg::kBK);
-  };
 
-  // ---- prologue ----
+  // ---- prologue: K tiles 0 and 1 (and code group 0) in flight; wait for tile 0 ----
   if (MODE == kRowwise) {
     dword_rows_ab<Cfg>(reinterpret_cast<const uint8_t*>(op.ra), 4, op.a_rows,
                        reinterpret_cast<const uint8_t*>(op.rb), 4, op.b_rows, 0,
                        lds + Cfg::kRowScaleOff, wave, lane);
   }
-  copy(0, std::integral_constant<int, 0>{});
-  copy(1, std::integral_constant<int, 1>{});
-  copy(2, std::integral_constant<int, 2>{});
-  copy(3, std::integral_constant<int, 3>{});
-  FP8GEMM_WAIT_VM_LGKM0(kWaitPrologue);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) tile_copy(j, 0, 0);
+  if (kMx) {
+#pragma unroll
+    for (int jj = 0; jj < kCodeLoads; ++jj) code_copy(jj, 0, 0);
+  }
+  {
+    const int k1 = nk > 1 ? 1 : 0;                    // one K tile: harmless re-fetch
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) tile_copy(j, 1, k1);
+  }
+  FP8GEMM_WAIT_VM_LGKM0(kLoads);
   __builtin_amdgcn_s_barrier();
   {
     v4i rd[2 * (FM + FN)];
 #pragma unroll
-    for (int d = 0; d < 2 * (FM + FN); ++d) read_frag(std::integral_constant<int, 0>{}, d, rd);
+    for (int d = 0; d < 2 * (FM + FN); ++d)
+      read_frag(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, d, rd);
 #pragma unroll
     for (int i = 0; i < FM; ++i) af0[i] = __builtin_shufflevector(rd[2 * i], rd[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
@@ -690,61 +711,66 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
       bf0[j] = __builtin_shufflevector(rd[2 * FM + 2 * j], rd[2 * FM + 2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
     if (kMx) {
 #pragma unroll
-      for (int e = 0; e < 2 * (FM + FN); ++e) read_codes(0, ca[0], cb[0], e);
+      for (int e = 0; e < FM + FN; ++e) read_code(cur_a, cur_b, 0, 0, e, ca[0], cb[0]);
     }
   }
 
-  // ---- one sub-tile t = 4u + P ----
+  // ---- one 64-K step t = (unroll base) + T: K tile u = t / 2, half p = T & 1 ----
   constexpr int kMfma = FM * FN;
   constexpr int kReads = 2 * (FM + FN);
   constexpr int kReadSpan = (kMfma * FP8GEMM_READ_SPAN + 7) / 8 > 0 ? (kMfma * FP8GEMM_READ_SPAN + 7) / 8 : 1;
-  auto step = [&](int t, auto slot_c, v8i (&fa)[FM], v8i (&fb)[FN], v8i (&na)[FM], v8i (&nb)[FN]) {
-    constexpr int P = decltype(slot_c)::value;
-    constexpr bool odd = P & 1;
-    constexpr int Z = P >> 1, PAR = P & 1;        // code set and parity used here
-    constexpr int kVmem = Cfg::kTileLoads + ((kMx && !odd) ? Cfg::kScaleLoads : 0);
-    constexpr int kDs = kReads + ((kMx && odd) ? 2 * (FM + FN) : 0);
+  constexpr int kCopySpan = (kMfma * FP8GEMM_COPY_SPAN + 7) / 8 > 0 ? (kMfma * FP8GEMM_COPY_SPAN + 7) / 8 : 1;
+  auto step = [&](int t, auto T_c, v8i (&fa)[FM], v8i (&fb)[FN], v8i (&na)[FM], v8i (&nb)[FN]) {
+    constexpr int T = decltype(T_c)::value;
+    constexpr int p = T & 1, q = (T >> 1) & 3, slot = (T >> 1) & 1;
+    constexpr int Z = T & 1;                     // code register set used by this step
+    // what step t + 1 reads: same K tile, other half; or the next K tile
+    constexpr int np = p ^ 1, nslot = p ? slot ^ 1 : slot, nq = p ? (q + 1) & 3 : q;
+    constexpr bool kCodeStep = kMx && p == 1 && q == 0;   // code group copy rides along
+    constexpr int kVmem = p ? kLoads + (kCodeStep ? kCodeLoads : 0) : 0;
+    constexpr int kDs = kReads + (kMx ? FM + FN : 0);
+    const int u = t >> 1;
     __builtin_amdgcn_sched_barrier(0);
-    FP8GEMM_WAIT_VM_LGKM0(kWait);                 // own copies of sub-tile t+1 landed
-    __builtin_amdgcn_s_barrier();                 // ... everyone's; slot P is free
+    if (p) {
+      // copies of K tile u + 1 (and code group) landed for every wave; slot of
+      // K tile u free (its last fragments were read in the previous step)
+      FP8GEMM_WAIT_VM_LGKM0(0);
+      __builtin_amdgcn_s_barrier();
+    } else {
+      __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): fragments in registers
+    }
     __builtin_amdgcn_sched_barrier(0);
-    const int sc = (t + S) < nsub ? t + S : nsub - 1;
+    const int kc = (u + 2) < nk ? u + 2 : nk - 1;    // past the end: harmless re-fetch
+    const int grp = (u >> 2) + 1 < ncode ? (u >> 2) + 1 : ncode - 1;
+    // code bytes of step t + 1 live in the group of K tile (t + 1) / 2
+    constexpr bool kNextGroup = p && q == 3;
     v4i rd[kReads];
 #pragma unroll
-    for (int q = 0; q < kMfma; ++q) {
-      const int i = q / FN, j = q % FN;
+    for (int m = 0; m < kMfma; ++m) {
+      const int i = m / FN, j = m % FN;
       if (kMx) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fb[j], fa[i], acc[i][j], 0, 0, 0, (int)cb[Z][PAR][j], 0, (int)ca[Z][PAR][i]);
+            fb[j], fa[i], acc[i][j], 0, 0, 0, (int)cb[Z][j], 0, (int)ca[Z][i]);
       } else {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0,
                                                                     0, 0, 0, 0, 0);
       }
-      // copy instructions of sub-tile t+4, spread evenly
+      if (m < kCopySpan) {
 #pragma unroll
-      for (int v = q * kVmem / kMfma; v < (q + 1) * kVmem / kMfma; ++v) {
-        if (v < Cfg::kTileLoads) {
-          buffer_dma16(rs, cdst + P * Cfg::kSlotBytes + v * 1024, voff,
-                         (blk0 + v) * 16 * ld + sc * Cfg::kBK);
-        } else if (kMx) {
-          int ci = wave * Cfg::kScaleLoads + (v - Cfg::kTileLoads);
-          ci = ci < Cfg::kScaleInsts ? ci : Cfg::kScaleInsts - 1;
-          const bool isA = ci < Cfg::BM / 64;
-          const int li = isA ? ci : ci - Cfg::BM / 64;
-          buffer_dma4(isA ? rcA : rcB, lds + Cfg::kScaleOff + Z * Cfg::kScaleSlotBytes + ci * 256,
-                        cvoff, li * 64 * nblk + 4 * (sc >> 1));
+        for (int v = m * kVmem / kCopySpan; v < (m + 1) * kVmem / kCopySpan; ++v) {
+          if (v < kLoads) tile_copy(v, slot, kc);
+          else if (kCodeStep) code_copy(v - kLoads, cbuf ^ 1, grp);
         }
       }
-      // LDS reads of sub-tile t+1 (slot P+1) and, on odd sub-tiles, the next K
-      // tile's codes, spread over the first kReadSpan MFMAs
-      if (q < kReadSpan) {
+      if (m < kReadSpan) {
 #pragma unroll
-        for (int d = q * kDs / kReadSpan; d < (q + 1) * kDs / kReadSpan; ++d) {
+        for (int d = m * kDs / kReadSpan; d < (m + 1) * kDs / kReadSpan; ++d) {
           if (d < kReads) {
-            read_frag(std::integral_constant<int, (P + 1) % S>{}, d, rd);
+            read_frag(std::integral_constant<int, nslot>{}, std::integral_constant<int, np>{}, d,
+                      rd);
           } else if (kMx) {
-            // next K tile sits in scale slot ((P + 1) >> 1) & 1 and goes to set Z ^ 1
-            read_codes(((P + 1) >> 1) & 1, ca[Z ^ 1], cb[Z ^ 1], d - kReads);
+            read_code(kNextGroup ? nxt_a : cur_a, kNextGroup ? nxt_b : cur_b, nq, np, d - kReads,
+                      ca[Z ^ 1], cb[Z ^ 1]);
           }
         }
       }
@@ -755,18 +781,39 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
 #pragma unroll
     for (int j = 0; j < FN; ++j)
       nb[j] = __builtin_shufflevector(rd[2 * FM + 2 * j], rd[2 * FM + 2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    if (kMx && kNextGroup) {                      // the next group is current from step t + 1
+      cbuf ^= 1;
+      const int ta = cur_a, tb = cur_b;
+      cur_a = nxt_a;
+      cur_b = nxt_b;
+      nxt_a = ta;
+      nxt_b = tb;
+    }
   };
 
   int t = 0;
-  for (; t + 4 <= nsub; t += 4) {
-    step(t, std::integral_constant<int, 0>{}, af0, bf0, af1, bf1);
-    step(t + 1, std::integral_constant<int, 1>{}, af1, bf1, af0, bf0);
-    step(t + 2, std::integral_constant<int, 2>{}, af0, bf0, af1, bf1);
-    step(t + 3, std::integral_constant<int, 3>{}, af1, bf1, af0, bf0);
-  }
-  if (t < nsub) {                                  // nsub % 4 == 2
-    step(t, std::integral_constant<int, 0>{}, af0, bf0, af1, bf1);
-    step(t + 1, std::integral_constant<int, 1>{}, af1, bf1, af0, bf0);
+  if constexpr (kMx) {                             // nsub % 8 == 0
+    for (; t < nsub; t += 8) {
+      step(t, std::integral_constant<int, 0>{}, af0, bf0, af1, bf1);
+      step(t + 1, std::integral_constant<int, 1>{}, af1, bf1, af0, bf0);
+      step(t + 2, std::integral_constant<int, 2>{}, af0, bf0, af1, bf1);
+      step(t + 3, std::integral_constant<int, 3>{}, af1, bf1, af0, bf0);
+      step(t + 4, std::integral_constant<int, 4>{}, af0, bf0, af1, bf1);
+      step(t + 5, std::integral_constant<int, 5>{}, af1, bf1, af0, bf0);
+      step(t + 6, std::integral_constant<int, 6>{}, af0, bf0, af1, bf1);
+      step(t + 7, std::integral_constant<int, 7>{}, af1, bf1, af0, bf0);
+    }
+  } else {                                         // nsub % 2 == 0
+    for (; t + 4 <= nsub; t += 4) {
+      step(t, std::integral_constant<int, 0>{}, af0, bf0, af1, bf1);
+      step(t + 1, std::integral_constant<int, 1>{}, af1, bf1, af0, bf0);
+      step(t + 2, std::integral_constant<int, 2>{}, af0, bf0, af1, bf1);
+      step(t + 3, std::integral_constant<int, 3>{}, af1, bf1, af0, bf0);
+    }
+    if (t < nsub) {
+      step(t, std::integral_constant<int, 0>{}, af0, bf0, af1, bf1);
+      step(t + 1, std::integral_constant<int, 1>{}, af1, bf1, af0, bf0);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0);     // no copy may still target LDS
@@ -849,7 +896,7 @@ __device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, 
                                           int64_t ldc, int m0, int m_end, int n0, int N,
                                           float tensor_scale) {
   if constexpr (KALIGNED && Cfg::kSlots == 4) {
-    if (interior_tile<Cfg>(op)) {
+    if (interior_tile<Cfg, MODE>(op)) {
       v16f acc[Cfg::kFragM][Cfg::kFragN];
       mainloop_interior<Cfg, MODE>(op, lds, acc);
       epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);

@@ -60,6 +60,36 @@ def test_gemm_big_tiles(mode, shape):
     assert_within_bound(C, Cr, Ar, "bf16", f"big {mode} {shape}")
 
 
+def _slice_scales(s, idx, mode):
+    return s if mode == "tensor" else s[idx]
+
+
+@pytest.mark.parametrize("mode,shape", [
+    ("mx32", (4096, 4096, 512)),      # large tiles, one 512-K group of MX codes
+    ("mx32", (4096, 4096, 1536)),     # three code groups, loop over 4 K tiles at a time
+    ("tensor", (4096, 4352, 384)),    # odd number of 128-K tiles: loop tail
+    ("rowwise", (4096, 4096, 640)),
+    ("mx32", (1024, 1024, 512)),      # small-tile kernel
+    ("rowwise", (1024, 768, 384)),
+])
+def test_gemm_interior_sampled(mode, shape):
+    """Full-tile shapes on the interior mainloop; the oracle checks sampled 128 x 128 blocks."""
+    M, N, K = shape
+    qa, sa, qb, sb = _oracle_operands(M, N, K, mode, seed=M + N + K, dist="mx_block")
+    announce("gemm interior", mode, shape)
+    C = _run_gpu(qa, sa, qb, sb, mode, "bf16")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(K)
+    blocks = [(0, 0), (M - 128, N - 128)] + [
+        (int(r) * 128, int(c) * 128) for r, c in rng.integers(0, [M // 128, N // 128], size=(6, 2))]
+    for r0, c0 in blocks:
+        ri, ci = np.arange(r0, r0 + 128), np.arange(c0, c0 + 128)
+        Cr, Ar = O.gemm_reference(qa[ri], _slice_scales(sa, ri, mode), qb[ci],
+                                  _slice_scales(sb, ci, mode), mode)
+        assert_within_bound(to_host(C[r0:r0 + 128, c0:c0 + 128]), Cr, Ar, "bf16",
+                            f"interior {mode} {shape} block {(r0, c0)}")
+
+
 def test_gemm_k16_tail_with_canaries():
     """K = 16 (one partial chunk pair) and guard bands around C must stay untouched."""
     M, N, K = 70, 90, 16
