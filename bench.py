@@ -68,6 +68,63 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+COPY_CAL_BYTES = 1 << 30          # plain device copy used to calibrate the byte counters
+
+
+def copy_calibration(dev):
+    """A plain device-to-device copy of COPY_CAL_BYTES, three times, for the counter
+    runs: FETCH_SIZE / WRITE_SIZE of its dispatches give the scale between the
+    counters and true bytes."""
+    import torch
+    src = torch.ones(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 copies of {COPY_CAL_BYTES} bytes")
+
+
+def _counter_means(csv_path, counter):
+    """Per-kernel mean of one rocprofv3 counter (KiB for FETCH_SIZE / WRITE_SIZE)."""
+    import csv
+    import collections
+    vals = collections.defaultdict(list)
+    with open(csv_path) as fh:
+        for row in csv.DictReader(fh):
+            if row.get("Counter_Name") != counter:
+                continue
+            vals[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: str):
+    """Write profiles/gemm_<workload>_traffic.json from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE) of `bench.py --copy-calibration`."""
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    gemm_name = [k for k in fetch if "gemm_kernel" in k or "grouped_kernel" in k]
+    copy_name = [k for k in fetch if "copy" in k.lower() and "gemm" not in k]
+    if len(gemm_name) != 1 or len(copy_name) != 1:
+        raise SystemExit(f"expected one GEMM and one copy kernel, got {gemm_name} / {copy_name}")
+    g, c = gemm_name[0], copy_name[0]
+    fetch_scale = COPY_CAL_BYTES / (fetch[c] * 1024.0)
+    write_scale = COPY_CAL_BYTES / (write[c] * 1024.0)
+    fetch_b = fetch[g] * 1024.0 * fetch_scale
+    write_b = write[g] * 1024.0 * write_scale
+    rec = {"workload": workload, "kernel": g, "kernel_source_digest": kernel_source_digest(),
+           "fetch_kib_per_launch_raw": fetch[g], "write_kib_per_launch_raw": write[g],
+           "copy_kernel": c, "copy_bytes": COPY_CAL_BYTES,
+           "copy_fetch_kib_raw": fetch[c], "copy_write_kib_raw": write[c],
+           "fetch_scale": fetch_scale, "write_scale": write_scale,
+           "hbm_fetch_bytes_per_launch": round(fetch_b), "hbm_write_bytes_per_launch": round(write_b),
+           "hbm_bytes_per_launch": round(fetch_b + write_b), "command": command}
+    out = os.path.join(ROOT, "profiles", f"gemm_{workload}_traffic.json")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def gemm_bytes(w) -> int:
     """Algorithmic bytes of one GEMM launch: A + B codes, scales, C."""
     mb = w.M * w.K + (w.groups or 1) * w.N * w.K
@@ -121,7 +178,18 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of A / columns of B in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/gemm_<workload>_traffic.json from two rocprofv3 --pmc "
+                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE); no GPU work")
+    ap.add_argument("--traffic-command", default="",
+                    help="the profiling command, recorded in the traffic summary")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        summarize_traffic(args.workload, *args.summarize_traffic, command=args.traffic_command)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
@@ -252,6 +320,10 @@ def main():
                            "gbs": round(quant_bytes_b / (qb_ms * 1e-3) / 1e9, 1)},
         },
     }
+    if args.copy_calibration:
+        del Ad, Bd
+        copy_calibration(dev)
+        Ad = Bd = None
     if not args.no_cpu_baseline:
         del Ad, Bd
         log("timing the CPU oracle on a bounded sample ...")
