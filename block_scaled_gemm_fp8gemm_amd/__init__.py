@@ -22,6 +22,7 @@ import os
 import re
 
 __all__ = [
+    "gemm_workspace",
     "Fp8GemmError", "SCALE_MODES", "OUT_DTYPES", "library_path", "load_library",
     "fp8gemm_quantize_workspace_size", "fp8gemm_quantize", "fp8gemm_workspace_size",
     "fp8gemm_run", "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run",
@@ -172,6 +173,25 @@ def _require_cuda(t, name, dtype=None, dim=None):
         raise ValueError(f"{name} must have unit stride in its last dimension")
 
 
+_WORKSPACES = {}
+
+
+def gemm_workspace(device, nbytes: int):
+    """A zero-filled device workspace of at least `nbytes`, cached per device.
+
+    The split-K GEMM keeps per-tile arrival counters in its workspace; they must
+    be zero before the first call and every call leaves them zero, so one buffer
+    serves all calls on a device that do not run concurrently.
+    """
+    torch = _torch()
+    key = torch.device(device)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=key)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def _ptr(t) -> int:
     return t.data_ptr() if t is not None else 0
 
@@ -221,7 +241,7 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
     m = SCALE_MODES[mode]
     need = fp8gemm_workspace_size(M, N, K, m)
     if need and workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=qa.device)
+        workspace = gemm_workspace(qa.device, need)
     fp8gemm_run(M, N, K, _ptr(qa), qa.stride(0), _ptr(qb), qb.stride(0), m, _ptr(sa), _ptr(sb),
                 _ptr(out), out.stride(0), OUT_DTYPES[out_dtype],
                 _ptr(workspace) if need else 0, workspace.numel() if need else 0,

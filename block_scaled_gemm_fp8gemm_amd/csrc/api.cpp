@@ -93,11 +93,8 @@ fp8gemm_status fp8gemm_quantize(const float* x, int64_t rows, int64_t k, int64_t
 }
 
 size_t fp8gemm_workspace_size(int64_t M, int64_t N, int64_t K, int mode) {
-  (void)M;
-  (void)N;
-  (void)K;
-  (void)mode;
-  return 0;
+  if (!valid_mode(mode) || M <= 0 || N <= 0 || K <= 0) return 0;
+  return fp8gemm::gemm_workspace_bytes(M, N, K, mode);
 }
 
 fp8gemm_status fp8gemm_run(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
@@ -112,6 +109,7 @@ fp8gemm_status fp8gemm_run(int64_t M, int64_t N, int64_t K, const uint8_t* A, in
   if (st != FP8GEMM_SUCCESS) return st;
   const size_t need = fp8gemm_workspace_size(M, N, K, mode);
   if (need > 0 && (!workspace || workspace_bytes < need)) return FP8GEMM_ERROR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return FP8GEMM_ERROR_MISALIGNED;
 
   fp8gemm::GemmProblem p;
   p.M = (int)M;
@@ -125,6 +123,7 @@ fp8gemm_status fp8gemm_run(int64_t M, int64_t N, int64_t K, const uint8_t* A, in
   p.scale_b = scale_b;
   p.C = C;
   p.ldc = ldc;
+  p.workspace = need > 0 ? workspace : nullptr;
   return from_hip(fp8gemm::launch_gemm(p, mode, out_dtype, static_cast<hipStream_t>(stream)));
 }
 

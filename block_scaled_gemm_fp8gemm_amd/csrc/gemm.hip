@@ -1,4 +1,5 @@
-// Dense scaled FP8 GEMM kernels for gfx950: one C tile per workgroup.
+// Dense scaled FP8 GEMM kernels for gfx950: one C tile per workgroup, and a
+// split-K kernel for shapes with too few output tiles to fill the GPU.
 //
 // Tile order.  "Hopper/Blackwell architecture features" §12.7.1 reorders program
 // ids in groups of GROUP_M tile rows so that concurrently running tiles share A
@@ -33,6 +34,7 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void gemm_kernel(G
   op.ldb = p.ldb;
   op.b_rows = p.N - n0;
   op.K = p.K;
+  op.sld = p.K / 32;
   const float* fsa = static_cast<const float*>(p.scale_a);
   const float* fsb = static_cast<const float*>(p.scale_b);
   op.sa = op.sb = nullptr;
@@ -89,17 +91,211 @@ hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
   return launch_cfg<Mid, MODE, OutT>(p, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Split-K.  The decode-like shape M = 128, N = K = 4096 of "Hopper/Blackwell
+// architecture features" §12.2.4 is bound by streaming B (16 MiB) from HBM, yet
+// it has only 32 output tiles of 128 x 128.  Here the output is cut into
+// 128 x 64 tiles and K into `splits` slices, so that tiles x splits >= 256
+// workgroups each stream an equal share of B.  Each workgroup runs the mainloop
+// over its slice (4-deep ring of 128-K tiles: a slice has few K tiles and its
+// copies come from HBM), stores its fp32 partial tile in the workspace and
+// counts its arrival on the tile's counter.  The last to arrive sums the
+// partials of slices 0, 1, ..., splits-1 in that order (so the result does not
+// depend on arrival order), resets the counter to zero for the next call and
+// runs the epilogue.
+// ---------------------------------------------------------------------------
+using SplitCfg = TileCfg<128, 64, 64, 32, 8, 1>;
+constexpr int kSplitTargetWgs = 256;       // one workgroup per CU of an MI355X
+
+struct SplitPlan {
+  int splits = 1, tiles_m = 0, tiles_n = 0;
+};
+
+SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int mode) {
+  SplitPlan plan;
+  const int64_t mid_tiles = ((M + Mid::BM - 1) / Mid::BM) * ((N + Mid::BN - 1) / Mid::BN);
+  if (mid_tiles >= 128 || K < 1024) return plan;
+  const int64_t tm = (M + SplitCfg::BM - 1) / SplitCfg::BM;
+  const int64_t tn = (N + SplitCfg::BN - 1) / SplitCfg::BN;
+  const int64_t gran = mode == kMx32 ? 512 : 128;    // K slices stay on the interior path
+  int best = 1;
+  for (int s = 2; s <= 16; s *= 2) {
+    if (K % (s * gran) != 0 || K / s < 512) break;
+    best = s;
+    if (tm * tn * s >= kSplitTargetWgs) break;
+  }
+  if (best == 1) return plan;
+  plan.splits = best;
+  plan.tiles_m = (int)tm;
+  plan.tiles_n = (int)tn;
+  return plan;
+}
+
+constexpr int64_t kPartialFloats = SplitCfg::BM * SplitCfg::BN;
+
+__host__ __device__ constexpr int64_t counter_bytes(int64_t tiles) {
+  return (tiles * 4 + 255) / 256 * 256;
+}
+
+template <class Cfg, int MODE, typename OutT>
+__global__ __launch_bounds__(Cfg::kThreads, 1) void splitk_kernel(GemmProblem p, int tiles_m,
+                                                                    int splits) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::kLdsBytes];
+  __shared__ int s_last;
+  constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
+  const int tile = blockIdx.x / splits, ks = blockIdx.x % splits;
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+  const int kslice = p.K / splits, k0 = ks * kslice;
+
+  TileOperands op;
+  op.A = p.A + (int64_t)m0 * p.lda + k0;
+  op.lda = p.lda;
+  op.a_rows = p.M - m0;
+  op.B = p.B + (int64_t)n0 * p.ldb + k0;
+  op.ldb = p.ldb;
+  op.b_rows = p.N - n0;
+  op.K = kslice;
+  op.sld = p.K / 32;
+  const float* fsa = static_cast<const float*>(p.scale_a);
+  const float* fsb = static_cast<const float*>(p.scale_b);
+  op.sa = op.sb = nullptr;
+  op.ra = op.rb = nullptr;
+  if (MODE == kMx32) {
+    op.sa = static_cast<const uint8_t*>(p.scale_a) + (int64_t)m0 * op.sld + k0 / 32;
+    op.sb = static_cast<const uint8_t*>(p.scale_b) + (int64_t)n0 * op.sld + k0 / 32;
+  }
+  if (MODE == kRowwise) {
+    op.ra = fsa + m0;
+    op.rb = fsb + n0;
+  }
+
+  v16f acc[FM][FN];
+  if (interior_tile<Cfg, MODE>(op)) mainloop_interior<Cfg, MODE, 4>(op, lds, acc);
+  else mainloop<Cfg, MODE, true>(op, lds, acc);
+
+  // partial tile: float4 r of thread x at [slice][tile][r][x] (coalesced per r)
+  const int tiles = tiles_m * (int)((p.N + Cfg::BN - 1) / Cfg::BN);
+  int* counters = static_cast<int*>(p.workspace);
+  v4f* partials = reinterpret_cast<v4f*>(static_cast<uint8_t*>(p.workspace) + counter_bytes(tiles));
+  constexpr int kVec = FM * FN * 4;
+  auto part = [&](int slice) {
+    return partials + ((int64_t)tile * splits + slice) * kVec * Cfg::kThreads + threadIdx.x;
+  };
+  // Partials travel as relaxed agent-scope atomics (8 bytes each): on gfx950 they
+  // are written through to, and read back from, the memory level shared by all
+  // XCDs, so ordering only needs the stores to have completed before the arrival
+  // is counted.  (An agent-scope release/acquire fence pair would write back and
+  // invalidate the whole L2 of the XCD instead, which cost more than the GEMM.)
+  {
+    uint64_t* mine = reinterpret_cast<uint64_t*>(part(ks));
+#pragma unroll
+    for (int r = 0; r < kVec; ++r) {
+      const v16f& a = acc[(r >> 2) / FN][(r >> 2) % FN];
+      const int g = r & 3;
+      const float2 lo{a[4 * g], a[4 * g + 1]}, hi{a[4 * g + 2], a[4 * g + 3]};
+      uint64_t* d = mine + 2 * r * Cfg::kThreads;
+      __hip_atomic_store(d, __builtin_bit_cast(uint64_t, lo), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(d + 1, __builtin_bit_cast(uint64_t, hi), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);                       // this thread's partial stored
+  __syncthreads();                                     // ... and every thread's
+  if (threadIdx.x == 0) {
+    const int prev =
+        __hip_atomic_fetch_add(&counters[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == splits - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0)                                // ready for the next call
+    __hip_atomic_store(&counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // sum the slices in order 0, 1, ..., splits - 1 (own slice from registers);
+  // the loads of up to four slices are issued together
+  constexpr int kBatch = 4;
+  v16f sum[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) sum[i][j] = v16f{};
+  for (int s0 = 0; s0 < splits; s0 += kBatch) {
+    v4f v[kBatch][kVec];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int slice = s0 + b;
+      if (slice < splits && slice != ks) {
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(part(slice));
+#pragma unroll
+        for (int r = 0; r < kVec; ++r) {
+          const uint64_t* d = src + 2 * r * Cfg::kThreads;
+          const float2 lo = __builtin_bit_cast(
+              float2, __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          const float2 hi = __builtin_bit_cast(
+              float2, __hip_atomic_load(d + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          v[b][r] = v4f{lo.x, lo.y, hi.x, hi.y};
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int slice = s0 + b;
+      if (slice >= splits) break;
+      if (slice == ks) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) sum[i][j] += acc[i][j];
+      } else {
+#pragma unroll
+        for (int r = 0; r < kVec; ++r) {
+          v16f& d = sum[(r >> 2) / FN][(r >> 2) % FN];
+          const int g = r & 3;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) d[4 * g + e] += v[b][r][e];
+        }
+      }
+    }
+  }
+  const float ts = (MODE == kTensor) ? fsa[0] * fsb[0] : 1.0f;
+  epilogue<Cfg, MODE, OutT>(sum, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N, ts);
+}
+
+template <int MODE, typename OutT>
+hipError_t launch_split(const GemmProblem& p, const SplitPlan& plan, hipStream_t stream) {
+  const int grid = plan.tiles_m * plan.tiles_n * plan.splits;
+  hipLaunchKernelGGL((splitk_kernel<SplitCfg, MODE, OutT>), dim3(grid), dim3(SplitCfg::kThreads), 0,
+                     stream, p, plan.tiles_m, plan.splits);
+  return hipGetLastError();
+}
+
+template <int MODE, typename OutT>
+hipError_t launch_any(const GemmProblem& p, hipStream_t stream) {
+  const SplitPlan plan = plan_split(p.M, p.N, p.K, MODE);
+  if (plan.splits > 1) return launch_split<MODE, OutT>(p, plan, stream);
+  return launch_mode<MODE, OutT>(p, stream);
+}
+
 }  // namespace
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int mode) {
+  const SplitPlan plan = plan_split(M, N, K, mode);
+  if (plan.splits <= 1) return 0;
+  const int64_t tiles = (int64_t)plan.tiles_m * plan.tiles_n;
+  return (size_t)(counter_bytes(tiles) + tiles * plan.splits * kPartialFloats * 4);
+}
 
 hipError_t launch_gemm(const GemmProblem& p, int mode, int out, hipStream_t stream) {
   if (out == kF16) {
-    if (mode == kTensor) return launch_mode<kTensor, _Float16>(p, stream);
-    if (mode == kRowwise) return launch_mode<kRowwise, _Float16>(p, stream);
-    return launch_mode<kMx32, _Float16>(p, stream);
+    if (mode == kTensor) return launch_any<kTensor, _Float16>(p, stream);
+    if (mode == kRowwise) return launch_any<kRowwise, _Float16>(p, stream);
+    return launch_any<kMx32, _Float16>(p, stream);
   }
-  if (mode == kTensor) return launch_mode<kTensor, __bf16>(p, stream);
-  if (mode == kRowwise) return launch_mode<kRowwise, __bf16>(p, stream);
-  return launch_mode<kMx32, __bf16>(p, stream);
+  if (mode == kTensor) return launch_any<kTensor, __bf16>(p, stream);
+  if (mode == kRowwise) return launch_any<kRowwise, __bf16>(p, stream);
+  return launch_any<kMx32, __bf16>(p, stream);
 }
 
 }  // namespace fp8gemm

@@ -75,7 +75,9 @@ struct TileCfg {
   static constexpr int kFragM = WM / 32, kFragN = WN / 32;
   static constexpr int kSlotBytes = (BM + BN) * kBK;
   static constexpr int kScaleSlotBytes = (BM + BN) * 4;       // MX: 4 codes per row per 128 K
-  static constexpr int kScaleSlots = 2;
+  // MX codes of a 128-K tile are copied with its first sub-tile, kSlots sub-tiles
+  // ahead, and read until its last one: kSlots / 2 K tiles are live at once
+  static constexpr int kScaleSlots = kSlots / 2 > 2 ? kSlots / 2 : 2;
   static constexpr int kRowScaleBytes = (BM + BN) * 4;        // row-wise: fp32 per row / column
   static constexpr int kScaleOff = kSlots * kSlotBytes;
   static constexpr int kRowScaleOff = kScaleOff + kScaleSlots * kScaleSlotBytes;
@@ -114,7 +116,8 @@ struct TileOperands {
   const uint8_t* sb;    // MX: E8M0 codes of B's first tile row
   const float* ra;      // row-wise: fp32 scale of A's first tile row
   const float* rb;      // row-wise: fp32 scale of B's first tile row
-  int K;
+  int K;                // K extent of this tile's product (a split's slice under split-K)
+  int sld;              // MX: bytes between the codes of consecutive rows
 };
 
 __device__ __forceinline__ void lds_dma16(const uint8_t* g, uint8_t* lds) {
@@ -361,9 +364,9 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
     const int sc = s < nvalid ? s : nvalid - 1;  // past the end: harmless re-fetch
     copy_subtile<Cfg, KTAIL>(op, slot_ptr(s), sc, wave, lane);
     if (kMxLds && (s & 1) == 0) {
-      dword_rows_ab<Cfg>(op.sa, nblk, op.a_rows, op.sb, nblk, op.b_rows, 4 * (sc >> 1),
-                         lds + Cfg::kScaleOff + ((s >> 1) & 1) * Cfg::kScaleSlotBytes, wave,
-                         lane);
+      uint8_t* sslot = lds + Cfg::kScaleOff + ((s >> 1) % Cfg::kScaleSlots) * Cfg::kScaleSlotBytes;
+      dword_rows_ab<Cfg>(op.sa, op.sld, op.a_rows, op.sb, op.sld, op.b_rows, 4 * (sc >> 1), sslot,
+                         wave, lane);
     }
   };
 
@@ -379,7 +382,7 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
   // words of K tile kt (resident in scale slot kt & 1)
   auto read_lds_codes = [&](int kt, uint32_t (&a)[FM], uint32_t (&b)[FN]) {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(lds + Cfg::kScaleOff +
-                                                          (kt & 1) * Cfg::kScaleSlotBytes);
+                                                          (kt % Cfg::kScaleSlots) * Cfg::kScaleSlotBytes);
 #pragma unroll
     for (int i = 0; i < FM; ++i) a[i] = w[arow[i]] >> (8 * h);
 #pragma unroll
@@ -391,12 +394,12 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = arow[i] < op.a_rows ? arow[i] : op.a_rows - 1;
-      a[i] = blk < nblk ? op.sa[(int64_t)r * nblk + blk] : 127u;
+      a[i] = blk < nblk ? op.sa[(int64_t)r * op.sld + blk] : 127u;
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int r = brow[j] < op.b_rows ? brow[j] : op.b_rows - 1;
-      b[j] = blk < nblk ? op.sb[(int64_t)r * nblk + blk] : 127u;
+      b[j] = blk < nblk ? op.sb[(int64_t)r * op.sld + blk] : 127u;
     }
   };
 
@@ -438,11 +441,11 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
     const int sn = t + S;                              // sub-tile to copy
     const int sc = sn < nvalid ? sn : nvalid - 1;      // past the end: harmless re-fetch
     uint8_t* cslot = slot_ptr(sn);
-    uint8_t* sslot = lds + Cfg::kScaleOff + ((sn >> 1) & 1) * Cfg::kScaleSlotBytes;
+    uint8_t* sslot = lds + Cfg::kScaleOff + ((sn >> 1) % Cfg::kScaleSlots) * Cfg::kScaleSlotBytes;
     const uint8_t* rslot = slot_ptr(t + 1);
     const int rk0 = (t + 1) * Cfg::kBK;
     const uint32_t* wsc = reinterpret_cast<const uint32_t*>(
-        lds + Cfg::kScaleOff + (((t + 1) >> 1) & 1) * Cfg::kScaleSlotBytes);
+        lds + Cfg::kScaleOff + (((t + 1) >> 1) % Cfg::kScaleSlots) * Cfg::kScaleSlotBytes);
     v4i rd[kReads];
 #pragma unroll
     for (int q = 0; q < kMfma; ++q) {
@@ -461,7 +464,7 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
         if (v < Cfg::kTileLoads) {
           copy_one<Cfg, KTAIL>(op, cslot, sc, v, wave, lane);
         } else if (kMxLds) {
-          dword_one<Cfg>(op.sa, nblk, op.a_rows, op.sb, nblk, op.b_rows, 4 * (sc >> 1), sslot,
+          dword_one<Cfg>(op.sa, op.sld, op.a_rows, op.sb, op.sld, op.b_rows, 4 * (sc >> 1), sslot,
                          v - Cfg::kTileLoads, wave, lane);
         }
       }
@@ -561,7 +564,9 @@ __device__ __forceinline__ bool interior_tile(const TileOperands& op) {
 #define FP8GEMM_COPY_SPAN 8    // eighths of a step's MFMAs over which its copies are spread
 #endif
 
-template <class Cfg, int MODE>
+// NS: ring depth in 128-K tiles (2 for the 256 x 256 tile, 4 for the split-K
+// tile, whose K slices are short and whose copies need more latency hiding).
+template <class Cfg, int MODE, int NS = 2>
 __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_t* lds,
                                                   v16f (&acc)[Cfg::kFragM][Cfg::kFragN]) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
@@ -573,20 +578,25 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   constexpr int kCodeInsts = (Cfg::BM + Cfg::BN) / 64;
   constexpr int kCodeLoads = (kCodeInsts + Cfg::kWaves - 1) / Cfg::kWaves;
   constexpr int kCodeBuf = (Cfg::BM + Cfg::BN) * 16;  // 16 code bytes per row
-  constexpr int kCodeOff = 2 * kTile;
-  static_assert(2 * kTile <= Cfg::kScaleOff, "ring fits");
+  constexpr int kCodeOff = NS * kTile;
+  constexpr bool kUniformOperand = nA % kLoads == 0;  // a wave copies rows of one operand
+  static_assert(NS == 2 || NS == 4, "ring of 2 or 4 K tiles");
+  static_assert(NS * kTile <= Cfg::kScaleOff, "ring fits");
   static_assert(kCodeOff + 2 * kCodeBuf <= Cfg::kLdsBytes, "code buffers fit");
   static_assert(kTile % (1024 * Cfg::kWaves) == 0, "equal copy share per wave");
-  static_assert(nA % kLoads == 0, "each wave copies rows of one operand only");
   static_assert(kLoads % 2 == 0, "copy blocks of both swizzle phases per wave");
-  static_assert(kLoads < 64, "vmcnt range");
+  static_assert((NS - 1) * kLoads + kCodeLoads < 64, "vmcnt range");
+  // ring slots reachable from one base register through the 16-bit offset field
+  constexpr int kMaxFrag = ((FM > FN ? FM : FN) - 1) * 32 * kRowB;
+  constexpr int kPerBase = (NS >= 4 && 3 * kTile + kMaxFrag < 65536) ? 4
+                           : (NS >= 2 && kTile + kMaxFrag < 65536) ? 2 : 1;
+  constexpr int kBases = NS / kPerBase;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
   const int h = lane >> 5;
   const int nk = op.K / kRowB;                     // K tiles
-  const int nsub = 2 * nk;                         // 64-K MFMA steps
   const int nblk = op.K / 32;
   const int ncode = nblk / 16;                     // 16-byte code groups per row
 
@@ -595,27 +605,42 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
-  // ---- copy side: scalar except two lane offsets ----
-  const int g0 = wave * kLoads;                   // first 8-row block of this wave
-  const bool cpA = g0 < nA;
-  const int blk0 = cpA ? g0 : g0 - nA;
-  const int ld = cpA ? (int)op.lda : (int)op.ldb;
-  const __amdgpu_buffer_rsrc_t rs =
-      cpA ? buffer_rsrc(op.A, (uint32_t)((Cfg::BM - 1) * op.lda + op.K))
-          : buffer_rsrc(op.B, (uint32_t)((Cfg::BN - 1) * op.ldb + op.K));
-  // lane -> row (lane >> 3) of an 8-row block, LDS chunk lane & 7, global chunk
-  // (lane & 7) ^ ((row >> 1) & 7); the swizzle of even and odd blocks differs
+  // ---- copy side ----
+  // copy instruction g of a K tile covers rows 8g .. 8g+7 of [A; B]: lane -> row
+  // (lane >> 3) of the block, LDS chunk lane & 7, global chunk (lane & 7) ^
+  // ((row >> 1) & 7); the swizzle of even and odd blocks differs
+  const int g0 = wave * kLoads;                   // first block of this wave
+  const __amdgpu_buffer_rsrc_t rsA = buffer_rsrc(op.A, (uint32_t)((Cfg::BM - 1) * op.lda + op.K));
+  const __amdgpu_buffer_rsrc_t rsB = buffer_rsrc(op.B, (uint32_t)((Cfg::BN - 1) * op.ldb + op.K));
+  const int lda = (int)op.lda, ldb = (int)op.ldb;
   const int crow = lane >> 3;
-  const int voff0 = crow * ld + 16 * ((lane & 7) ^ ((crow >> 1) & 7));
-  const int voff1 = crow * ld + 16 * ((lane & 7) ^ (((crow + 8) >> 1) & 7));
+  const int sw0 = 16 * ((lane & 7) ^ ((crow >> 1) & 7));
+  const int sw1 = 16 * ((lane & 7) ^ (((crow + 8) >> 1) & 7));
+  // per-instruction lane offsets (loop invariant)
+  int voff[kLoads];
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const bool isA = g0 + j < nA;
+    voff[j] = crow * (isA ? lda : ldb) + ((j & 1) ? sw1 : sw0);
+  }
   uint8_t* const cdst = lds + g0 * 1024;
-  const __amdgpu_buffer_rsrc_t rcA = buffer_rsrc(op.sa, (uint32_t)(Cfg::BM * nblk));
-  const __amdgpu_buffer_rsrc_t rcB = buffer_rsrc(op.sb, (uint32_t)(Cfg::BN * nblk));
-  const int cvoff = lane * nblk;
+  const __amdgpu_buffer_rsrc_t rcA =
+      buffer_rsrc(op.sa, (uint32_t)((Cfg::BM - 1) * op.sld + nblk));
+  const __amdgpu_buffer_rsrc_t rcB =
+      buffer_rsrc(op.sb, (uint32_t)((Cfg::BN - 1) * op.sld + nblk));
+  const int cvoff = lane * op.sld;
 
   auto tile_copy = [&](int j, int slot, int kt) {       // j-th copy of K tile kt
-    buffer_dma16(rs, cdst + slot * kTile + j * 1024, (j & 1) ? voff1 : voff0,
-                 (blk0 + j) * 8 * ld + kt * kRowB);
+    const int g = g0 + j;                               // wave-uniform
+    if (kUniformOperand) {
+      const bool isA = g0 < nA;
+      buffer_dma16(isA ? rsA : rsB, cdst + slot * kTile + j * 1024, voff[j],
+                   (isA ? g : g - nA) * 8 * (isA ? lda : ldb) + kt * kRowB);
+    } else {
+      const bool isA = g < nA;
+      buffer_dma16(isA ? rsA : rsB, cdst + slot * kTile + j * 1024, voff[j],
+                   (isA ? g : g - nA) * 8 * (isA ? lda : ldb) + kt * kRowB);
+    }
   };
   auto code_copy = [&](int jj, int buf, int grp) {      // jj-th code copy of group grp
     int ci = wave * kCodeLoads + jj;
@@ -623,7 +648,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
     const bool isA = ci < Cfg::BM / 64;
     const int li = isA ? ci : ci - Cfg::BM / 64;
     buffer_dma16(isA ? rcA : rcB, lds + kCodeOff + buf * kCodeBuf + ci * 1024, cvoff,
-                 li * 64 * nblk + 16 * grp);
+                 li * 64 * op.sld + 16 * grp);
   };
 
   // ---- read side: per-lane LDS bases, constant offsets ----
@@ -632,16 +657,16 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   const int rsw = ((lane & 31) >> 1) & 7;
   const int ra = (wm * Cfg::WM + (lane & 31)) * kRowB;
   const int rb = (Cfg::BM + wn * Cfg::WN + (lane & 31)) * kRowB;
-  int ba[2][2][2], bb[2][2][2];                        // [slot][half][chunk pair]
+  int ba[kBases][2][2], bb[kBases][2][2];              // [base][half][chunk pair]
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < kBases; ++s)
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int ch = 16 * ((4 * p + 2 * c + h) ^ rsw);
-        ba[s][p][c] = opaque(s * kTile + ra + ch);
-        bb[s][p][c] = opaque(s * kTile + rb + ch);
+        ba[s][p][c] = opaque(s * kPerBase * kTile + ra + ch);
+        bb[s][p][c] = opaque(s * kPerBase * kTile + rb + ch);
       }
   // MX codes: byte 4 (u % 4) + 2 p + h of the row's 16-byte group u / 4; the
   // group of the current K tile is in buffer `cur`, the next one in `nxt`
@@ -655,12 +680,13 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   }
 
   auto rd16 = [&](int addr) { return *reinterpret_cast<const v4i*>(lds + addr); };
-  // the d-th 16-byte read of a step's fragments (slot s, half p)
+  // the d-th 16-byte read of a step's fragments (ring slot s, half p)
   auto read_frag = [&](auto s_c, auto p_c, int d, v4i (&rd)[2 * (FM + FN)]) {
     constexpr int s = decltype(s_c)::value, p = decltype(p_c)::value;
+    constexpr int b = s / kPerBase, o = (s % kPerBase) * kTile;
     const int c = d & 1;
-    if (d < 2 * FM) rd[d] = rd16(ba[s][p][c] + (d >> 1) * 32 * kRowB);
-    else rd[d] = rd16(bb[s][p][c] + ((d - 2 * FM) >> 1) * 32 * kRowB);
+    if (d < 2 * FM) rd[d] = rd16(ba[b][p][c] + o + (d >> 1) * 32 * kRowB);
+    else rd[d] = rd16(bb[b][p][c] + o + ((d - 2 * FM) >> 1) * 32 * kRowB);
   };
   uint32_t ca[2][FM], cb[2][FN];                       // codes: [register set][fragment]
 #pragma unroll
@@ -680,7 +706,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
 
   v8i af0[FM], bf0[FN], af1[FM], bf1[FN];
 
-  // ---- prologue: K tiles 0 and 1 (and code group 0) in flight; wait for tile 0 ----
+  // ---- prologue: K tiles 0 .. NS-1 (and code group 0) in flight; wait for tile 0 ----
   if (MODE == kRowwise) {
     dword_rows_ab<Cfg>(reinterpret_cast<const uint8_t*>(op.ra), 4, op.a_rows,
                        reinterpret_cast<const uint8_t*>(op.rb), 4, op.b_rows, 0,
@@ -692,12 +718,13 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
 #pragma unroll
     for (int jj = 0; jj < kCodeLoads; ++jj) code_copy(jj, 0, 0);
   }
-  {
-    const int k1 = nk > 1 ? 1 : 0;                    // one K tile: harmless re-fetch
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) tile_copy(j, 1, k1);
+  for (int s = 1; s < NS; ++s) {
+    const int ks = s < nk ? s : nk - 1;               // short K: harmless re-fetch
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) tile_copy(j, s, ks);
   }
-  FP8GEMM_WAIT_VM_LGKM0(kLoads);
+  FP8GEMM_WAIT_VM_LGKM0((NS - 1) * kLoads);
   __builtin_amdgcn_s_barrier();
   {
     v4i rd[2 * (FM + FN)];
@@ -715,32 +742,36 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
     }
   }
 
-  // ---- one 64-K step t = (unroll base) + T: K tile u = t / 2, half p = T & 1 ----
+  // ---- one 64-K step t: K tile u = t / 2, half p; T = t mod (unrolled steps) ----
   constexpr int kMfma = FM * FN;
   constexpr int kReads = 2 * (FM + FN);
   constexpr int kReadSpan = (kMfma * FP8GEMM_READ_SPAN + 7) / 8 > 0 ? (kMfma * FP8GEMM_READ_SPAN + 7) / 8 : 1;
   constexpr int kCopySpan = (kMfma * FP8GEMM_COPY_SPAN + 7) / 8 > 0 ? (kMfma * FP8GEMM_COPY_SPAN + 7) / 8 : 1;
   auto step = [&](int t, auto T_c, v8i (&fa)[FM], v8i (&fb)[FN], v8i (&na)[FM], v8i (&nb)[FN]) {
     constexpr int T = decltype(T_c)::value;
-    constexpr int p = T & 1, q = (T >> 1) & 3, slot = (T >> 1) & 1;
+    constexpr int p = T & 1, ku = T >> 1;        // half, K tile within the unrolled body
+    constexpr int q = ku & 3, slot = ku % NS;
     constexpr int Z = T & 1;                     // code register set used by this step
     // what step t + 1 reads: same K tile, other half; or the next K tile
-    constexpr int np = p ^ 1, nslot = p ? slot ^ 1 : slot, nq = p ? (q + 1) & 3 : q;
+    constexpr int np = p ^ 1, nslot = p ? (ku + 1) % NS : slot, nq = p ? (q + 1) & 3 : q;
     constexpr bool kCodeStep = kMx && p == 1 && q == 0;   // code group copy rides along
     constexpr int kVmem = p ? kLoads + (kCodeStep ? kCodeLoads : 0) : 0;
     constexpr int kDs = kReads + (kMx ? FM + FN : 0);
+    // copies allowed in flight once K tile u + 1 has landed: those of K tiles
+    // u + 2 .. u + NS - 1 and a code group issued after K tile u + 1's copies
+    constexpr int kWaitOdd = (NS - 2) * kLoads + ((kMx && q >= 1 && q + 1 <= NS) ? kCodeLoads : 0);
     const int u = t >> 1;
     __builtin_amdgcn_sched_barrier(0);
     if (p) {
-      // copies of K tile u + 1 (and code group) landed for every wave; slot of
-      // K tile u free (its last fragments were read in the previous step)
-      FP8GEMM_WAIT_VM_LGKM0(0);
+      // copies of K tile u + 1 landed for every wave; slot of K tile u free (its
+      // last fragments were read in the previous step)
+      FP8GEMM_WAIT_VM_LGKM0(kWaitOdd);
       __builtin_amdgcn_s_barrier();
     } else {
       __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0): fragments in registers
     }
     __builtin_amdgcn_sched_barrier(0);
-    const int kc = (u + 2) < nk ? u + 2 : nk - 1;    // past the end: harmless re-fetch
+    const int kc = (u + NS) < nk ? u + NS : nk - 1;  // past the end: harmless re-fetch
     const int grp = (u >> 2) + 1 < ncode ? (u >> 2) + 1 : ncode - 1;
     // code bytes of step t + 1 live in the group of K tile (t + 1) / 2
     constexpr bool kNextGroup = p && q == 3;
@@ -790,29 +821,47 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
       nxt_b = tb;
     }
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  using I6 = std::integral_constant<int, 6>;
+  using I7 = std::integral_constant<int, 7>;
 
-  int t = 0;
-  if constexpr (kMx) {                             // nsub % 8 == 0
-    for (; t < nsub; t += 8) {
-      step(t, std::integral_constant<int, 0>{}, af0, bf0, af1, bf1);
-      step(t + 1, std::integral_constant<int, 1>{}, af1, bf1, af0, bf0);
-      step(t + 2, std::integral_constant<int, 2>{}, af0, bf0, af1, bf1);
-      step(t + 3, std::integral_constant<int, 3>{}, af1, bf1, af0, bf0);
-      step(t + 4, std::integral_constant<int, 4>{}, af0, bf0, af1, bf1);
-      step(t + 5, std::integral_constant<int, 5>{}, af1, bf1, af0, bf0);
-      step(t + 6, std::integral_constant<int, 6>{}, af0, bf0, af1, bf1);
-      step(t + 7, std::integral_constant<int, 7>{}, af1, bf1, af0, bf0);
+  // unrolled over 4 K tiles (MX code groups, 4-deep ring) or over the 2-deep ring
+  constexpr int kUnrollK = (kMx || NS == 4) ? 4 : 2;
+  int u = 0;
+  for (; u + kUnrollK <= nk; u += kUnrollK) {
+    const int t = 2 * u;
+    step(t, I0{}, af0, bf0, af1, bf1);
+    step(t + 1, I1{}, af1, bf1, af0, bf0);
+    step(t + 2, I2{}, af0, bf0, af1, bf1);
+    step(t + 3, I3{}, af1, bf1, af0, bf0);
+    if constexpr (kUnrollK == 4) {
+      step(t + 4, I4{}, af0, bf0, af1, bf1);
+      step(t + 5, I5{}, af1, bf1, af0, bf0);
+      step(t + 6, I6{}, af0, bf0, af1, bf1);
+      step(t + 7, I7{}, af1, bf1, af0, bf0);
     }
-  } else {                                         // nsub % 2 == 0
-    for (; t + 4 <= nsub; t += 4) {
-      step(t, std::integral_constant<int, 0>{}, af0, bf0, af1, bf1);
-      step(t + 1, std::integral_constant<int, 1>{}, af1, bf1, af0, bf0);
-      step(t + 2, std::integral_constant<int, 2>{}, af0, bf0, af1, bf1);
-      step(t + 3, std::integral_constant<int, 3>{}, af1, bf1, af0, bf0);
+  }
+  // remaining K tiles (never for MX, where K % 512 == 0)
+  if constexpr (!kMx) {
+    const int t = 2 * u;
+    if (u < nk) {
+      step(t, I0{}, af0, bf0, af1, bf1);
+      step(t + 1, I1{}, af1, bf1, af0, bf0);
     }
-    if (t < nsub) {
-      step(t, std::integral_constant<int, 0>{}, af0, bf0, af1, bf1);
-      step(t + 1, std::integral_constant<int, 1>{}, af1, bf1, af0, bf0);
+    if constexpr (kUnrollK == 4) {
+      if (u + 1 < nk) {
+        step(t + 2, I2{}, af0, bf0, af1, bf1);
+        step(t + 3, I3{}, af1, bf1, af0, bf0);
+      }
+      if (u + 2 < nk) {
+        step(t + 4, I4{}, af0, bf0, af1, bf1);
+        step(t + 5, I5{}, af1, bf1, af0, bf0);
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);

@@ -83,6 +83,7 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void grouped_kerne
     op.ldb = p.ldb;
     op.b_rows = p.N - n0;
     op.K = p.K;
+    op.sld = p.K / 32;
     op.sa = op.sb = nullptr;
     op.ra = op.rb = nullptr;
     if (MODE == kMx32) {

@@ -30,7 +30,14 @@ struct GemmProblem {
   const void* scale_b;
   void* C;
   int64_t ldc;
+  void* workspace;      // split-K partials and tile counters (gemm_workspace_bytes)
 };
+
+// Device workspace a dense GEMM of this shape needs (0: none).  Shapes with too
+// few output tiles to fill the GPU are split along K; the workspace then holds
+// the fp32 partial tiles and one arrival counter per output tile.  The counters
+// must be zero before the first call and every call leaves them zero.
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int mode);
 
 hipError_t launch_gemm(const GemmProblem& p, int mode, int out, hipStream_t stream);
 

@@ -50,7 +50,15 @@ def test_workspace_queries(lib):
     assert F.fp8gemm_quantize_workspace_size(4096, 4096, 0) > 0
     assert F.fp8gemm_quantize_workspace_size(4096, 4096, 1) == 0
     assert F.fp8gemm_quantize_workspace_size(4096, 4096, 2) == 0
-    assert F.fp8gemm_workspace_size(4096, 4096, 4096, 2) >= 0
+    # large shapes fill the GPU with output tiles: no workspace
+    assert F.fp8gemm_workspace_size(4096, 4096, 4096, 1) == 0
+    assert F.fp8gemm_workspace_size(8192, 8192, 8192, 2) == 0
+    # the decode-like M = 128 shape is split along K: partials + counters
+    for mode in (0, 1, 2):
+        need = F.fp8gemm_workspace_size(128, 4096, 4096, mode)
+        assert need >= 128 * 4096 * 4 * 2, (mode, need)
+    assert F.fp8gemm_workspace_size(128, 4096, 256, 0) == 0      # K too short to split
+    assert F.fp8gemm_workspace_size(128, 4096, 4096, 7) == 0     # bad mode
     assert F.fp8gemm_grouped_workspace_size(8, 16384, 14336, 4096, 1) >= 0
 
 
@@ -107,6 +115,17 @@ def test_run_validation(lib):
     assert _run(lib, ldc=68) == MISALIGNED
     assert _run(lib, sa=P3 + 1) == MISALIGNED
     assert _run(lib, M=1 << 31) == NOT_SUPPORTED
+
+
+def test_run_split_workspace_validation(lib):
+    """Split-K shapes need the queried workspace, 16-byte aligned; checked before any launch."""
+    M, N, K = 128, 4096, 4096
+    need = F.fp8gemm_workspace_size(M, N, K, 0)
+    assert need > 0
+    args = (M, N, K, P, K, P2, K, 0, P3, P3 + 64, P3 + 4096, N, 1)
+    assert lib.fp8gemm_run(*args, 0, 0, None) == WORKSPACE
+    assert lib.fp8gemm_run(*args, P3 + (1 << 20), need - 1, None) == WORKSPACE
+    assert lib.fp8gemm_run(*args, P3 + (1 << 20) + 8, need, None) == MISALIGNED
 
 
 def _grouped(lib, G=8, total_m=256, N=64, K=128, A=P, lda=128, off=P3 + 8192, B=P2, ldb=128,

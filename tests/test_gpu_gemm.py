@@ -90,6 +90,42 @@ def test_gemm_interior_sampled(mode, shape):
                             f"interior {mode} {shape} block {(r0, c0)}")
 
 
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", [(128, 4096, 4096), (100, 1000, 2048), (256, 640, 4096),
+                                   (128, 4096, 1024)])
+def test_gemm_splitk(mode, shape):
+    """Shapes with few output tiles run split along K (ragged M / N included)."""
+    M, N, K = shape
+    assert F.fp8gemm_workspace_size(M, N, K, F.SCALE_MODES[mode]) > 0, "shape is not split"
+    qa, sa, qb, sb = _oracle_operands(M, N, K, mode, seed=M + 5 * N + K, dist="mx_block")
+    announce("gemm split-K", mode, shape)
+    C = to_host(_run_gpu(qa, sa, qb, sb, mode, "bf16"))
+    Cr, Ar = O.gemm_reference(qa, sa, qb, sb, mode)
+    assert_within_bound(C, Cr, Ar, "bf16", f"split-K {mode} {shape}")
+
+
+def test_gemm_splitk_repeat_and_interleave():
+    """The per-tile counters reset themselves: repeated and interleaved calls on one
+    workspace give bit-identical results (the partials are summed in slice order)."""
+    ops1 = _oracle_operands(128, 4096, 4096, "tensor", seed=21)
+    ops2 = _oracle_operands(100, 1000, 2048, "rowwise", seed=22)
+    announce("gemm split-K repeat")
+    d1 = [to_dev(ops1[0], 16), scale_to_dev(ops1[1], "tensor"), to_dev(ops1[2], 16),
+          scale_to_dev(ops1[3], "tensor")]
+    d2 = [to_dev(ops2[0], 16), scale_to_dev(ops2[1], "rowwise"), to_dev(ops2[2], 16),
+          scale_to_dev(ops2[3], "rowwise")]
+    first1 = F.gemm(*d1, "tensor", "bf16")
+    first2 = F.gemm(*d2, "rowwise", "bf16")
+    for _ in range(3):
+        again1 = F.gemm(*d1, "tensor", "bf16")
+        again2 = F.gemm(*d2, "rowwise", "bf16")
+        torch.cuda.synchronize()
+        assert torch.equal(first1, again1)
+        assert torch.equal(first2, again2)
+    Cr, Ar = O.gemm_reference(*ops1, "tensor")
+    assert_within_bound(to_host(first1), Cr, Ar, "bf16", "split-K repeat")
+
+
 def test_gemm_k16_tail_with_canaries():
     """K = 16 (one partial chunk pair) and guard bands around C must stay untouched."""
     M, N, K = 70, 90, 16
