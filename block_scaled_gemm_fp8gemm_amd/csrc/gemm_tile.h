@@ -49,6 +49,9 @@
 #include "device_utils.h"
 #include "launch.h"
 
+#ifndef FP8GEMM_DIRECT_EPILOGUE
+#define FP8GEMM_DIRECT_EPILOGUE 1
+#endif
 #ifndef FP8GEMM_SCHED
 #define FP8GEMM_SCHED 1
 #endif
@@ -937,6 +940,60 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFr
   }
 }
 
+// Epilogue of a full tile straight from registers.  After the MFMAs a lane holds,
+// for each 32 x 32 block and group g of four accumulators, four consecutive
+// output columns 8g + 4h .. 8g + 4h + 3 (h = lane / 32) of row lane % 32.  One
+// V_PERMLANE32_SWAP per packed dword exchanges group 2k + 1 of the low half-wave
+// with group 2k of the high half, after which every lane owns eight consecutive
+// columns (16 bytes) of its row: C is written with 16-byte stores and no LDS
+// staging, so the epilogue costs a few hundred instructions and no waits.
+template <class Cfg, int MODE, typename OutT>
+__device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                                const uint8_t* lds, OutT* C, int64_t ldc, int m0,
+                                                int n0, float tensor_scale) {
+  constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
+  static_assert(sizeof(OutT) == 2, "16-bit outputs");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
+  const int h = lane >> 5;
+  const float* rsc = reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = wm * Cfg::WM + i * 32 + (lane & 31);   // tile row of this lane
+    float fa = 1.0f;
+    if (MODE == kTensor) fa = tensor_scale;
+    if (MODE == kRowwise) fa = rsc[r];
+    OutT* crow = C + (int64_t)(m0 + r) * ldc + n0 + wn * Cfg::WN;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        uint2 w[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int g = 2 * k + q;
+          const int c = j * 32 + 8 * g + 4 * h;           // wave-local column of value 0
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * fa;
+          if (MODE == kRowwise) {
+            const v4f fb = *reinterpret_cast<const v4f*>(rsc + Cfg::BM + wn * Cfg::WN + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] *= fb[e];
+          }
+          w[q] = pack4<OutT>(v[0], v[1], v[2], v[3]);
+        }
+        // low half keeps group 2k and takes the high half's; high half keeps 2k + 1
+        const auto sx = __builtin_amdgcn_permlane32_swap(w[0].x, w[1].x, false, false);
+        const auto sy = __builtin_amdgcn_permlane32_swap(w[0].y, w[1].y, false, false);
+        const v4i out{(int)sx[0], (int)sy[0], (int)sx[1], (int)sy[1]};
+        *reinterpret_cast<v4i*>(crow + j * 32 + 16 * k + 8 * h) = out;
+      }
+    }
+  }
+}
+
 // One output tile: the interior mainloop when the tile qualifies, else the
 // general (clamped) one, then the epilogue.  Each branch has its own accumulators
 // and epilogue so no accumulator copies join the two paths.
@@ -948,7 +1005,11 @@ __device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, 
     if (interior_tile<Cfg, MODE>(op)) {
       v16f acc[Cfg::kFragM][Cfg::kFragN];
       mainloop_interior<Cfg, MODE>(op, lds, acc);
+#if FP8GEMM_DIRECT_EPILOGUE
+      epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, n0, tensor_scale);
+#else
       epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
+#endif
       return;
     }
   }
