@@ -53,6 +53,73 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void gemm_kernel(G
                                        ts);
 }
 
+// Operands of the tiles of one persistent workgroup: tile i of the list is the
+// tile at position slot + i * stride of the grouped order, where the slot of a
+// workgroup is XCD-aware (the workgroups of one XCD hold consecutive slots), so
+// in every round each XCD works on a contiguous stretch of the grouped order.
+template <class Cfg, int MODE>
+struct DenseTiles {
+  GemmProblem p;
+  int tiles_m, tiles_n, slot, stride;
+  __device__ void coords(int i, int& m0, int& n0) const {
+    int tm, tn;
+    grouped_tile(slot + i * stride, tiles_m, tiles_n, kGroupM, &tm, &tn);
+    m0 = tm * Cfg::BM;
+    n0 = tn * Cfg::BN;
+  }
+  __device__ TileOperands op(int i) const {
+    int m0, n0;
+    coords(i, m0, n0);
+    TileOperands op;
+    op.A = p.A + (int64_t)m0 * p.lda;
+    op.lda = p.lda;
+    op.a_rows = p.M - m0;
+    op.B = p.B + (int64_t)n0 * p.ldb;
+    op.ldb = p.ldb;
+    op.b_rows = p.N - n0;
+    op.K = p.K;
+    op.sld = p.K / 32;
+    op.sa = op.sb = nullptr;
+    op.ra = op.rb = nullptr;
+    if (MODE == kMx32) {
+      op.sa = static_cast<const uint8_t*>(p.scale_a) + (int64_t)m0 * op.sld;
+      op.sb = static_cast<const uint8_t*>(p.scale_b) + (int64_t)n0 * op.sld;
+    }
+    if (MODE == kRowwise) {
+      op.ra = static_cast<const float*>(p.scale_a) + m0;
+      op.rb = static_cast<const float*>(p.scale_b) + n0;
+    }
+    return op;
+  }
+};
+
+// Persistent form for shapes whose tiles are all interior: one workgroup per CU
+// walks its tiles as one copy stream (the next tile's first K tiles are fetched
+// while the current one finishes, its epilogue runs while they land).
+template <class Cfg, int MODE, typename OutT>
+__global__ __launch_bounds__(Cfg::kThreads, 1) void gemm_persistent_kernel(GemmProblem p,
+                                                                           int tiles_m,
+                                                                           int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::kLdsBytes];
+  const int total = tiles_m * tiles_n;
+  DenseTiles<Cfg, MODE> src{p, tiles_m, tiles_n, xcd_linear(blockIdx.x, gridDim.x),
+                            (int)gridDim.x};
+  const int count = (total - src.slot + src.stride - 1) / src.stride;
+  const float* fsa = static_cast<const float*>(p.scale_a);
+  const float* fsb = static_cast<const float*>(p.scale_b);
+  const float ts = (MODE == kTensor) ? fsa[0] * fsb[0] : 1.0f;
+  OutT* C = static_cast<OutT*>(p.C);
+  auto epi = [&](const v16f (&acc)[Cfg::kFragM][Cfg::kFragN], int i, int rbuf)
+                 __attribute__((always_inline)) {
+    int m0, n0;
+    src.coords(i, m0, n0);
+    epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, p.ldc, m0, n0, ts, rbuf);
+  };
+  // epilogue_direct issues two 16-byte stores per 32 x 32 block and lane
+  if (count > 0)
+    stream_interior<Cfg, MODE, 2 * Cfg::kFragM * Cfg::kFragN>(src, 0, count, lds, epi);
+}
+
 template <class Cfg, int MODE, typename OutT>
 hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   const int tiles_m = (p.M + Cfg::BM - 1) / Cfg::BM;
@@ -80,6 +147,39 @@ using Big = TileCfg<256, 128, 128, 64, 3, 2>;
 #endif
 using Mid = TileCfg<128, 128, 64, 64, 4, 2>;
 
+#ifndef FP8GEMM_PERSISTENT
+#define FP8GEMM_PERSISTENT 0
+#endif
+
+int device_cus() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+  }
+  return cus;
+}
+
+// Every tile of the shape is an interior tile (the persistent stream's condition).
+template <class Cfg>
+bool all_interior(const GemmProblem& p) {
+  return p.M % Cfg::BM == 0 && p.N % Cfg::BN == 0 && p.K % 512 == 0 &&
+         (int64_t)Cfg::BM * p.lda + p.K < ((int64_t)1 << 31) &&
+         (int64_t)Cfg::BN * p.ldb + p.K < ((int64_t)1 << 31);
+}
+
+template <class Cfg, int MODE, typename OutT>
+hipError_t launch_persistent(const GemmProblem& p, hipStream_t stream) {
+  const int tiles_m = p.M / Cfg::BM, tiles_n = p.N / Cfg::BN;
+  const int total = tiles_m * tiles_n;
+  const int cus = device_cus();
+  const int grid = total < cus ? total : cus;
+  hipLaunchKernelGGL((gemm_persistent_kernel<Cfg, MODE, OutT>), dim3(grid), dim3(Cfg::kThreads), 0,
+                     stream, p, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
 template <int MODE, typename OutT>
 hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
   // Large tiles when they still give at least one tile per CU; otherwise smaller
@@ -87,7 +187,10 @@ hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
   const int64_t big_tiles = (int64_t)((p.M + Big::BM - 1) / Big::BM) * ((p.N + Big::BN - 1) / Big::BN);
   // MX with K % 128 != 0 reads its codes into registers: the large tile would spill
   const bool mx_ragged = MODE == kMx32 && p.K % 128 != 0;
-  if (big_tiles >= 256 * Big::kWgPerCu && !mx_ragged) return launch_cfg<Big, MODE, OutT>(p, stream);
+  if (big_tiles >= 256 * Big::kWgPerCu && !mx_ragged) {
+    if (FP8GEMM_PERSISTENT && all_interior<Big>(p)) return launch_persistent<Big, MODE, OutT>(p, stream);
+    return launch_cfg<Big, MODE, OutT>(p, stream);
+  }
   return launch_cfg<Mid, MODE, OutT>(p, stream);
 }
 

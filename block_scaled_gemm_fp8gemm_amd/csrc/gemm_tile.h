@@ -81,7 +81,8 @@ struct TileCfg {
   // MX codes of a 128-K tile are copied with its first sub-tile, kSlots sub-tiles
   // ahead, and read until its last one: kSlots / 2 K tiles are live at once
   static constexpr int kScaleSlots = kSlots / 2 > 2 ? kSlots / 2 : 2;
-  static constexpr int kRowScaleBytes = (BM + BN) * 4;        // row-wise: fp32 per row / column
+  // row-wise: fp32 per row / column, two buffers (persistent kernels alternate)
+  static constexpr int kRowScaleBytes = 2 * (BM + BN) * 4;
   static constexpr int kScaleOff = kSlots * kSlotBytes;
   static constexpr int kRowScaleOff = kScaleOff + kScaleSlots * kScaleSlotBytes;
   // interior path, MX: two buffers of 16 code bytes (512 K) per row after the ring
@@ -872,6 +873,346 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   __builtin_amdgcn_s_barrier();      // every wave is done with the ring
 }
 
+// ---------------------------------------------------------------------------
+// A run of interior tiles as one copy stream (persistent kernels).  Tiles
+// first .. last-1 of a workgroup's list (src.op(i)) share lda, ldb and K; their
+// 128-K tiles are consumed back to back, so the copies of the next tile's first
+// K tiles (and its first MX code group) go out while the current tile's last K
+// tiles are consumed, and the register fragments of its first step are read
+// during the current tile's last step.  Each tile's epilogue (epi(acc, i, buf),
+// buf = row-scale buffer) then runs while those copies are in flight, instead of
+// a new workgroup starting cold.  Row-wise scales of tile i are copied into LDS
+// buffer i % 2 during its K loop.
+// Conditions: every tile interior (interior_tile), K % 512 == 0.
+// ---------------------------------------------------------------------------
+template <class Cfg, int MODE, int kEpiStores, class Src, class Epi>
+__device__ __forceinline__ void stream_interior(const Src& src, int first, int last,
+                                                uint8_t* lds, Epi&& epi) {
+  static constexpr int NS = 2;
+  static constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
+  static constexpr bool kMx = MODE == kMx32;
+  static constexpr bool kRow = MODE == kRowwise;
+  static constexpr int kRowB = 128;
+  static constexpr int kTile = (Cfg::BM + Cfg::BN) * kRowB;
+  static constexpr int nA = Cfg::BM / 8;
+  static constexpr int kLoads = kTile / 1024 / Cfg::kWaves;
+  static constexpr int kCodeInsts = (Cfg::BM + Cfg::BN) / 64;           // also row-scale copies
+  static constexpr int kCodeLoads = (kCodeInsts + Cfg::kWaves - 1) / Cfg::kWaves;
+  static constexpr int kCodeBuf = (Cfg::BM + Cfg::BN) * 16;
+  static constexpr int kCodeOff = NS * kTile;
+  static constexpr int kRowScaleBuf = (Cfg::BM + Cfg::BN) * 4;
+  static constexpr bool kUniformOperand = nA % kLoads == 0;
+  static constexpr bool kSide = kMx || kRow;                              // side copies every 512 K
+  static constexpr int kSideLoads = kSide ? kCodeLoads : 0;
+  static_assert(NS * kTile <= Cfg::kScaleOff, "ring fits");
+  static_assert(kCodeOff + 2 * kCodeBuf <= Cfg::kLdsBytes, "code buffers fit");
+  static_assert(Cfg::kRowScaleOff + 2 * kRowScaleBuf <= Cfg::kLdsBytes, "row-scale buffers fit");
+  static_assert(kTile % (1024 * Cfg::kWaves) == 0, "equal copy share per wave");
+  static_assert(kLoads % 2 == 0, "copy blocks of both swizzle phases per wave");
+  static constexpr int kMaxFrag = ((FM > FN ? FM : FN) - 1) * 32 * kRowB;
+  static constexpr int kPerBase = (kTile + kMaxFrag < 65536) ? 2 : 1;
+  static constexpr int kBases = NS / kPerBase;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
+  const int h = lane >> 5;
+  const TileOperands op0 = src.op(first);
+  const int nk = op0.K / kRowB;                    // K tiles per output tile (% 4 == 0)
+  const int nblk = op0.K / 32;
+  const int ncode = nblk / 16;
+  const int lda = (int)op0.lda, ldb = (int)op0.ldb, sld = op0.sld;
+
+  // base addresses of a tile's A rows, B rows, A codes / row scales and B codes /
+  // column scales (scalar values; buffer descriptors are formed where used).
+  // Everything below passes them as separate scalars: a struct argument to the
+  // helper lambdas kept whole frames in scratch memory.
+  auto side_a = [](const TileOperands& op) __attribute__((always_inline)) {
+    return kMx ? static_cast<const void*>(op.sa) : static_cast<const void*>(op.ra);
+  };
+  auto side_b = [](const TileOperands& op) __attribute__((always_inline)) {
+    return kMx ? static_cast<const void*>(op.sb) : static_cast<const void*>(op.rb);
+  };
+  const uint32_t bytes_a = (uint32_t)((Cfg::BM - 1) * op0.lda + op0.K);
+  const uint32_t bytes_b = (uint32_t)((Cfg::BN - 1) * op0.ldb + op0.K);
+  const uint32_t bytes_sa = kMx ? (uint32_t)((Cfg::BM - 1) * op0.sld + nblk) : Cfg::BM * 4;
+  const uint32_t bytes_sb = kMx ? (uint32_t)((Cfg::BN - 1) * op0.sld + nblk) : Cfg::BN * 4;
+
+  // ---- copy side ----
+  const int g0 = wave * kLoads;
+  const int crow = lane >> 3;
+  const int sw0 = 16 * ((lane & 7) ^ ((crow >> 1) & 7));
+  const int sw1 = 16 * ((lane & 7) ^ (((crow + 8) >> 1) & 7));
+  int voff[kLoads];
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const bool isA = g0 + j < nA;
+    voff[j] = crow * (isA ? lda : ldb) + ((j & 1) ? sw1 : sw0);
+  }
+  uint8_t* const cdst = lds + g0 * 1024;
+  const int cvoff = kMx ? lane * sld : lane * 4;
+
+  // (selects below are on values: a select between two members of one object
+  // would select addresses and force the object into scratch memory)
+  auto tile_copy = [&](const void* pa, const void* pb, int j, int slot, int kt)
+                       __attribute__((always_inline)) {
+    const int g = g0 + j;
+    const bool isA = kUniformOperand ? (g0 < nA) : (g < nA);
+    buffer_dma16(buffer_rsrc(isA ? pa : pb, isA ? bytes_a : bytes_b),
+                 cdst + slot * kTile + j * 1024, voff[j],
+                 (isA ? g : g - nA) * 8 * (isA ? lda : ldb) + kt * kRowB);
+  };
+  // jj-th side copy: MX code group grp into code buffer buf, or row scales into
+  // row-scale buffer buf
+  auto side_copy = [&](const void* psa, const void* psb, int jj, int buf, int grp)
+                       __attribute__((always_inline)) {
+    int ci = wave * kCodeLoads + jj;
+    ci = ci < kCodeInsts ? ci : kCodeInsts - 1;
+    const bool isA = ci < Cfg::BM / 64;
+    const int li = isA ? ci : ci - Cfg::BM / 64;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(isA ? psa : psb, isA ? bytes_sa : bytes_sb);
+    if (kMx) {
+      buffer_dma16(rs, lds + kCodeOff + buf * kCodeBuf + ci * 1024, cvoff,
+                   li * 64 * sld + 16 * grp);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs,
+          (__attribute__((address_space(3))) void*)(lds + Cfg::kRowScaleOff + buf * kRowScaleBuf +
+                                                    ci * 256),
+          4, cvoff, li * 64 * 4, 0, 0);
+    }
+  };
+
+  // ---- read side ----
+  const int rsw = ((lane & 31) >> 1) & 7;
+  const int ra = (wm * Cfg::WM + (lane & 31)) * kRowB;
+  const int rb = (Cfg::BM + wn * Cfg::WN + (lane & 31)) * kRowB;
+  int ba[kBases][2][2], bb[kBases][2][2];
+#pragma unroll
+  for (int s = 0; s < kBases; ++s)
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int ch = 16 * ((4 * p + 2 * c + h) ^ rsw);
+        ba[s][p][c] = opaque(s * kPerBase * kTile + ra + ch);
+        bb[s][p][c] = opaque(s * kPerBase * kTile + rb + ch);
+      }
+  int cur_a = 0, cur_b = 0, nxt_a = 0, nxt_b = 0;
+  int cbuf = 0;
+  if (kMx) {
+    cur_a = opaque(kCodeOff + (wm * Cfg::WM + (lane & 31)) * 16 + h);
+    cur_b = opaque(kCodeOff + (Cfg::BM + wn * Cfg::WN + (lane & 31)) * 16 + h);
+    nxt_a = opaque(cur_a + kCodeBuf);
+    nxt_b = opaque(cur_b + kCodeBuf);
+  }
+  auto rd16 = [&](int addr) __attribute__((always_inline)) { return *reinterpret_cast<const v4i*>(lds + addr); };
+  auto read_frag = [&](auto s_c, auto p_c, int d, v4i (&rd)[2 * (FM + FN)]) __attribute__((always_inline)) {
+    constexpr int s = decltype(s_c)::value, p = decltype(p_c)::value;
+    constexpr int b = s / kPerBase, o = (s % kPerBase) * kTile;
+    const int c = d & 1;
+    if (d < 2 * FM) rd[d] = rd16(ba[b][p][c] + o + (d >> 1) * 32 * kRowB);
+    else rd[d] = rd16(bb[b][p][c] + o + ((d - 2 * FM) >> 1) * 32 * kRowB);
+  };
+  uint32_t ca[2][FM], cb[2][FN];
+#pragma unroll
+  for (int z = 0; z < 2; ++z) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) ca[z][i] = 0;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) cb[z][j] = 0;
+  }
+  auto read_code = [&](int base_a, int base_b, int q, int p, int e, uint32_t (&a)[FM],
+                       uint32_t (&b)[FN]) __attribute__((always_inline)) {
+    const int off = 4 * q + 2 * p;
+    if (e < FM) a[e] = lds[base_a + off + e * 32 * 16];
+    else b[e - FM] = lds[base_b + off + (e - FM) * 32 * 16];
+  };
+
+  v8i af0[FM], bf0[FN], af1[FM], bf1[FN];
+  v16f acc[FM][FN];
+
+  // ---- stream prologue: K tiles 0, 1 of the first tile (and its code group 0) ----
+  // current (c) and next (n) tile of the stream
+  const void *ca_ = op0.A, *cb_ = op0.B, *csa = side_a(op0), *csb = side_b(op0);
+  const void *na_ = ca_, *nb_ = cb_, *nsa = csa, *nsb = csb;
+  if (first + 1 < last) {
+    const TileOperands o1 = src.op(first + 1);
+    na_ = o1.A;
+    nb_ = o1.B;
+    nsa = side_a(o1);
+    nsb = side_b(o1);
+  }
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) tile_copy(ca_, cb_, j, 0, 0);
+  if (kMx) {
+#pragma unroll
+    for (int jj = 0; jj < kCodeLoads; ++jj) side_copy(csa, csb, jj, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) tile_copy(ca_, cb_, j, 1, 1);
+  FP8GEMM_WAIT_VM_LGKM0(kLoads);
+  __builtin_amdgcn_s_barrier();
+  {
+    v4i rd[2 * (FM + FN)];
+#pragma unroll
+    for (int d = 0; d < 2 * (FM + FN); ++d)
+      read_frag(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, d, rd);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af0[i] = __builtin_shufflevector(rd[2 * i], rd[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      bf0[j] = __builtin_shufflevector(rd[2 * FM + 2 * j], rd[2 * FM + 2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    if (kMx) {
+#pragma unroll
+      for (int e = 0; e < FM + FN; ++e) read_code(cur_a, cur_b, 0, 0, e, ca[0], cb[0]);
+    }
+  }
+
+  static constexpr int kMfma = FM * FN;
+  static constexpr int kReads = 2 * (FM + FN);
+  static constexpr int kReadSpan = (kMfma * FP8GEMM_READ_SPAN + 7) / 8 > 0 ? (kMfma * FP8GEMM_READ_SPAN + 7) / 8 : 1;
+  static constexpr int kCopySpan = (kMfma * FP8GEMM_COPY_SPAN + 7) / 8 > 0 ? (kMfma * FP8GEMM_COPY_SPAN + 7) / 8 : 1;
+  int rbuf = 0;                                    // row-scale buffer of the current tile
+  bool has_next = first + 1 < last;
+  bool fresh = true;                               // no epilogue stores in flight yet
+  // one 64-K step of the current tile: K tile u = t / 2, T = t % 8
+  auto step = [&](int t, auto T_c, v8i (&fa)[FM], v8i (&fb)[FN], v8i (&na)[FM], v8i (&nb)[FN]) __attribute__((always_inline)) {
+    constexpr int T = decltype(T_c)::value;
+    constexpr int p = T & 1, ku = T >> 1;
+    constexpr int q = ku & 3, slot = ku % NS;
+    constexpr int Z = T & 1;
+    constexpr int np = p ^ 1, nslot = p ? (ku + 1) % NS : slot, nq = p ? (q + 1) & 3 : q;
+    constexpr bool kSideStep = kSide && p == 1 && q == 0;
+    constexpr int kVmem = p ? kLoads + (kSideStep ? kSideLoads : 0) : 0;
+    constexpr int kDs = kReads + (kMx ? FM + FN : 0);
+    // in flight once K tile u + 1 has landed: a side copy issued after it (q == 1)
+    constexpr int kWaitOdd = (kSide && q == 1) ? kSideLoads : 0;
+    const int u = t >> 1;
+    __builtin_amdgcn_sched_barrier(0);
+    if (p) {
+      // first odd step after an epilogue: its C stores were issued after the
+      // copies of this K tile and may stay in flight (vmcnt retires in order)
+      if (T == 1 && u == 0 && !fresh) FP8GEMM_WAIT_VM_LGKM0(kWaitOdd + kEpiStores);
+      else FP8GEMM_WAIT_VM_LGKM0(kWaitOdd);
+      __builtin_amdgcn_s_barrier();
+    } else {
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // copy target: K tile u + 2 of this tile, else of the next tile, else a
+    // harmless re-fetch of this tile's last K tile
+    const int k2 = u + NS;
+    const bool to_next = k2 >= nk;
+    const bool tn = to_next && has_next;
+    const void* ta = tn ? na_ : ca_;
+    const void* tb = tn ? nb_ : cb_;
+    const int kt = to_next ? (has_next ? k2 - nk : nk - 1) : k2;
+    const int g1 = (u >> 2) + 1;                   // MX code group of K tile u + 4
+    const bool g_next = g1 >= ncode;
+    const bool gn = g_next && has_next;
+    const void* gsa = gn ? nsa : csa;
+    const void* gsb = gn ? nsb : csb;
+    const int grp = g_next ? (has_next ? 0 : ncode - 1) : g1;
+    constexpr bool kNextGroup = p && q == 3;
+    v4i rd[kReads];
+#pragma unroll
+    for (int m = 0; m < kMfma; ++m) {
+      const int i = m / FN, j = m % FN;
+      if (kMx) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fb[j], fa[i], acc[i][j], 0, 0, 0, (int)cb[Z][j], 0, (int)ca[Z][i]);
+      } else {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0,
+                                                                    0, 0, 0, 0, 0);
+      }
+      if (m < kCopySpan) {
+#pragma unroll
+        for (int v = m * kVmem / kCopySpan; v < (m + 1) * kVmem / kCopySpan; ++v) {
+          if (v < kLoads) tile_copy(ta, tb, v, slot, kt);
+          else if (kMx && kSideStep) side_copy(gsa, gsb, v - kLoads, cbuf ^ 1, grp);
+          else if (kRow && kSideStep) side_copy(csa, csb, v - kLoads, rbuf, 0);
+        }
+      }
+      if (m < kReadSpan) {
+#pragma unroll
+        for (int d = m * kDs / kReadSpan; d < (m + 1) * kDs / kReadSpan; ++d) {
+          if (d < kReads) {
+            read_frag(std::integral_constant<int, nslot>{}, std::integral_constant<int, np>{}, d,
+                      rd);
+          } else if (kMx) {
+            read_code(kNextGroup ? nxt_a : cur_a, kNextGroup ? nxt_b : cur_b, nq, np, d - kReads,
+                      ca[Z ^ 1], cb[Z ^ 1]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) na[i] = __builtin_shufflevector(rd[2 * i], rd[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      nb[j] = __builtin_shufflevector(rd[2 * FM + 2 * j], rd[2 * FM + 2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    if (kMx && kNextGroup) {
+      cbuf ^= 1;
+      const int ta = cur_a, tb = cur_b;
+      cur_a = nxt_a;
+      cur_b = nxt_b;
+      nxt_a = ta;
+      nxt_b = tb;
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  using I6 = std::integral_constant<int, 6>;
+  using I7 = std::integral_constant<int, 7>;
+
+  for (int tile = first; tile < last; ++tile) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
+    for (int u = 0; u < nk; u += 4) {
+      const int t = 2 * u;
+      step(t, I0{}, af0, bf0, af1, bf1);
+      step(t + 1, I1{}, af1, bf1, af0, bf0);
+      step(t + 2, I2{}, af0, bf0, af1, bf1);
+      step(t + 3, I3{}, af1, bf1, af0, bf0);
+      step(t + 4, I4{}, af0, bf0, af1, bf1);
+      step(t + 5, I5{}, af1, bf1, af0, bf0);
+      step(t + 6, I6{}, af0, bf0, af1, bf1);
+      step(t + 7, I7{}, af1, bf1, af0, bf0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    epi(acc, tile, rbuf);
+    __builtin_amdgcn_sched_barrier(0);
+    fresh = false;
+    // advance: the next tile becomes current
+    rbuf ^= 1;
+    if (has_next) {
+      ca_ = na_;
+      cb_ = nb_;
+      csa = nsa;
+      csb = nsb;
+      has_next = tile + 2 < last;
+      if (has_next) {
+        const TileOperands o2 = src.op(tile + 2);
+        na_ = o2.A;
+        nb_ = o2.B;
+        nsa = side_a(o2);
+        nsb = side_b(o2);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0);     // no copy may still target LDS
+  __builtin_amdgcn_s_barrier();      // every wave is done with the ring
+}
+
 // Scale, round and store a tile through LDS.  m0/n0: global coordinates of the
 // tile origin; rows at or past m_end and columns at or past N are not stored.
 // Output row m lives at C + m * ldc (ldc * sizeof(OutT) a multiple of 16 and C
@@ -950,14 +1291,15 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFr
 template <class Cfg, int MODE, typename OutT>
 __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                 const uint8_t* lds, OutT* C, int64_t ldc, int m0,
-                                                int n0, float tensor_scale) {
+                                                int n0, float tensor_scale, int rbuf = 0) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   static_assert(sizeof(OutT) == 2, "16-bit outputs");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
   const int h = lane >> 5;
-  const float* rsc = reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff);
+  const float* rsc =
+      reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff + rbuf * (Cfg::BM + Cfg::BN) * 4);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int r = wm * Cfg::WM + i * 32 + (lane & 31);   // tile row of this lane

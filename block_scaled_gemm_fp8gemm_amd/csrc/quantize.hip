@@ -9,12 +9,13 @@
 //   MX (32)    : per 32-element K block, E8M0 code = clamp(floor(log2 amax) - 8 + 127,
 //                0, 254) (127 if amax = 0), q = RNE_sat(x * 2^(127 - code))
 //
-// All kernels are HBM-streaming: 16 consecutive fp32 (four 16-byte loads) per
-// thread and unit of work, one 16-byte store of codes, reductions by wavefront
-// shuffles and LDS.  The division is IEEE binary32 (correctly rounded), as the
-// codes must be bit-exact.  Per-tensor scaling takes two passes (partial maxima,
-// then quantise) because the scale depends on the whole tensor; the other modes
-// read each element once.
+// All kernels are HBM-streaming.  The unit of work is 1024 consecutive values of
+// a row, taken by one wavefront so that every load and store instruction covers
+// one contiguous KiB (see load_unit); maxima are reduced with wavefront shuffles
+// and LDS.  The division is IEEE binary32 (correctly rounded), as the codes must
+// be bit-exact.  Per-tensor scaling takes two passes (partial maxima, then
+// quantise) because the scale depends on the whole tensor; the other modes read
+// each element once.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,51 +26,54 @@ namespace fp8gemm {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-struct Vec16 {
+// A unit is 1024 consecutive values of one row, handled by one wavefront: lane l
+// holds the float4s at columns 256 j + 4 l (j = 0..3), so each of the four loads
+// (and each of the four code stores) covers one contiguous KiB across the
+// wavefront and every cache line is fetched by a single instruction.  Columns at
+// or past k are neither read nor written (and count as zero for the maxima).
+struct Unit {
   f4 v[4];
 };
 
-__device__ __forceinline__ Vec16 load16(const float* p) {
-  const f4* p4 = reinterpret_cast<const f4*>(p);
-  Vec16 r;
+__device__ __forceinline__ Unit load_unit(const float* row, int col0, int k, int lane) {
+  Unit u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.v[i] = __builtin_nontemporal_load(p4 + i);
-  return r;
-}
-
-__device__ __forceinline__ float absmax16(const Vec16& x) {
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(x.v[i].x), fabsf(x.v[i].y)),
-                       fmaxf(fabsf(x.v[i].z), fabsf(x.v[i].w))));
+  for (int j = 0; j < 4; ++j) {
+    const int c = col0 + 256 * j + 4 * lane;
+    u.v[j] = c < k ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(row + c)) : f4{};
   }
-  return m;
+  return u;
 }
 
-// Quotient by s (binary32 division), then encode: 16 codes in a uint4.
-__device__ __forceinline__ uint4 encode16_div(const Vec16& x, float s) {
-  uint32_t w[4];
+__device__ __forceinline__ void store_codes(uint8_t* qrow, int col0, int k, int lane,
+                                            const uint32_t (&w)[4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = encode4_e4m3(x.v[i].x / s, x.v[i].y / s, x.v[i].z / s, x.v[i].w / s);
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  for (int j = 0; j < 4; ++j) {
+    const int c = col0 + 256 * j + 4 * lane;
+    if (c < k) *reinterpret_cast<uint32_t*>(qrow + c) = w[j];
+  }
 }
 
-// Exact power-of-two scaling by 2^e, then encode.
-__device__ __forceinline__ uint4 encode16_ldexp(const Vec16& x, int e) {
-  uint32_t w[4];
+__device__ __forceinline__ float absmax4(f4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+__device__ __forceinline__ float absmax_unit(const Unit& u) {
+  return fmaxf(fmaxf(absmax4(u.v[0]), absmax4(u.v[1])), fmaxf(absmax4(u.v[2]), absmax4(u.v[3])));
+}
+
+// Quotient by s (binary32 division), then encode.
+__device__ __forceinline__ void encode_unit_div(const Unit& u, float s, uint32_t (&w)[4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = encode4_e4m3(ldexpf(x.v[i].x, e), ldexpf(x.v[i].y, e), ldexpf(x.v[i].z, e),
-                        ldexpf(x.v[i].w, e));
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  for (int j = 0; j < 4; ++j)
+    w[j] = encode4_e4m3(u.v[j].x / s, u.v[j].y / s, u.v[j].z / s, u.v[j].w / s);
 }
 
-// Block-wide max of one value per thread (kThreads threads).
+// Block-wide max of one value per thread.
 __device__ __forceinline__ float block_max(float v, float* lds) {
   v = wave_max(v);
   const int wave = threadIdx.x >> 6;
@@ -77,23 +81,29 @@ __device__ __forceinline__ float block_max(float v, float* lds) {
   __syncthreads();
   float r = lds[0];
 #pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, lds[i]);
+  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, lds[i]);
   __syncthreads();
   return r;
 }
 
 // ---- per-tensor: pass 1, one partial maximum per workgroup -------------------
-__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const float* __restrict__ x,
-                                                                uint32_t units_per_row,
-                                                                uint32_t units, int64_t ldx,
+// Units are dealt to wavefronts in turn, two per wavefront and iteration.
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const float* __restrict__ x, int k,
+                                                                int upr, int units,
+                                                                int64_t ldx,
                                                                 float* __restrict__ partials) {
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[kWaves];
+  const int lane = threadIdx.x & 63;
+  const int w0 = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int nw = gridDim.x * kWaves;
   float m = 0.0f;
-  const uint32_t stride = gridDim.x * kThreads;
-  for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < units; u += stride) {
-    const uint32_t r = u / units_per_row;
-    const uint32_t c = u - r * units_per_row;
-    m = fmaxf(m, absmax16(load16(x + (int64_t)r * ldx + 16 * c)));
+  for (int u = w0; u < units; u += 2 * nw) {
+    const int u2 = u + nw;
+    const int r = u / upr, r2 = u2 / upr;
+    const Unit a = load_unit(x + (int64_t)r * ldx, (u - r * upr) * 1024, k, lane);
+    Unit b{};
+    if (u2 < units) b = load_unit(x + (int64_t)r2 * ldx, (u2 - r2 * upr) * 1024, k, lane);
+    m = fmaxf(m, fmaxf(absmax_unit(a), absmax_unit(b)));
   }
   m = block_max(m, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
@@ -101,116 +111,134 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const float* __r
 
 // ---- per-tensor: pass 2, scale from the partial maxima, then encode ----------
 __global__ __launch_bounds__(kThreads) void quant_tensor_kernel(
-    const float* __restrict__ x, uint32_t units_per_row, uint32_t units, int64_t ldx,
+    const float* __restrict__ x, int k, int upr, int units, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, const float* __restrict__ partials, int nparts,
     float* __restrict__ scale_out) {
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[kWaves];
   float m = 0.0f;
   for (int i = threadIdx.x; i < nparts; i += kThreads) m = fmaxf(m, partials[i]);
   const float amax = block_max(m, red);
   const float s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
   if (blockIdx.x == 0 && threadIdx.x == 0) scale_out[0] = s;
-  const uint32_t stride = gridDim.x * kThreads;
-  for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < units; u += stride) {
-    const uint32_t r = u / units_per_row;
-    const uint32_t c = u - r * units_per_row;
-    const Vec16 v = load16(x + (int64_t)r * ldx + 16 * c);
-    *reinterpret_cast<uint4*>(q + (int64_t)r * ldq + 16 * c) = encode16_div(v, s);
+  const int lane = threadIdx.x & 63;
+  const int w0 = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int nw = gridDim.x * kWaves;
+  for (int u = w0; u < units; u += 2 * nw) {
+    const int u2 = u + nw;
+    const int r = u / upr, r2 = u2 / upr;
+    const int c0 = (u - r * upr) * 1024, c2 = (u2 - r2 * upr) * 1024;
+    const Unit a = load_unit(x + (int64_t)r * ldx, c0, k, lane);
+    Unit b{};
+    if (u2 < units) b = load_unit(x + (int64_t)r2 * ldx, c2, k, lane);
+    uint32_t w[4];
+    encode_unit_div(a, s, w);
+    store_codes(q + (int64_t)r * ldq, c0, k, lane, w);
+    if (u2 < units) {
+      encode_unit_div(b, s, w);
+      store_codes(q + (int64_t)r2 * ldq, c2, k, lane, w);
+    }
   }
 }
 
-// ---- row-wise: one lane group of T threads per row, U units cached per thread --
-template <int T, int U>
+// ---- row-wise: one workgroup per row, the row cached in registers -------------
+// Wave w holds units w, w + 4, ... (up to U of them); rows longer than 4 U units
+// take the two-pass kernel below.
+template <int U>
 __global__ __launch_bounds__(kThreads) void quant_row_kernel(const float* __restrict__ x, int rows,
-                                                             int units_per_row, int64_t ldx,
+                                                             int k, int upr, int64_t ldx,
                                                              uint8_t* __restrict__ q, int64_t ldq,
                                                              float* __restrict__ scales) {
-  static_assert(T == 64 || T == 128 || T == 256, "row group is 1, 2 or 4 wavefronts");
-  constexpr int kRowsPerBlock = kThreads / T;
-  constexpr int kWavesPerRow = T / 64;
-  __shared__ float red[kThreads / 64];
-  const int g = threadIdx.x / T;  // row slot in this block
-  const int t = threadIdx.x % T;
-  for (int row0 = blockIdx.x * kRowsPerBlock; row0 < rows; row0 += gridDim.x * kRowsPerBlock) {
-    const int r = row0 + g;
-    const bool live = r < rows;
-    const float* xr = x + (int64_t)(live ? r : 0) * ldx;
-    Vec16 v[U];
+  __shared__ float red[kWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+    const float* xr = x + (int64_t)r * ldx;
+    Unit v[U];
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int c = t + j * T;
-      if (live && c < units_per_row) {
-        v[j] = load16(xr + 16 * c);
-        m = fmaxf(m, absmax16(v[j]));
-      }
+      const int u = wave + j * kWaves;
+      v[j] = u < upr ? load_unit(xr, u * 1024, k, lane) : Unit{};
+      m = fmaxf(m, absmax_unit(v[j]));
     }
-    m = wave_max(m);
-    if (kWavesPerRow > 1) {
-      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-      __syncthreads();
-      m = red[g * kWavesPerRow];
-#pragma unroll
-      for (int i = 1; i < kWavesPerRow; ++i) m = fmaxf(m, red[g * kWavesPerRow + i]);
-      __syncthreads();
-    }
+    m = block_max(m, red);
     const float s = (m == 0.0f) ? 1.0f : m / kE4M3Max;
-    if (live && t == 0) scales[r] = s;
-    uint8_t* qr = q + (int64_t)(live ? r : 0) * ldq;
+    if (threadIdx.x == 0) scales[r] = s;
+    uint8_t* qr = q + (int64_t)r * ldq;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int c = t + j * T;
-      if (live && c < units_per_row)
-        *reinterpret_cast<uint4*>(qr + 16 * c) = encode16_div(v[j], s);
+      const int u = wave + j * kWaves;
+      if (u < upr) {
+        uint32_t w[4];
+        encode_unit_div(v[j], s, w);
+        store_codes(qr, u * 1024, k, lane, w);
+      }
     }
   }
 }
 
 // ---- row-wise, long rows: two passes over the row (the second mostly from cache)
 __global__ __launch_bounds__(kThreads) void quant_row_long_kernel(
-    const float* __restrict__ x, int rows, int units_per_row, int64_t ldx,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales) {
-  __shared__ float red[kThreads / 64];
+    const float* __restrict__ x, int rows, int k, int upr, int64_t ldx, uint8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scales) {
+  __shared__ float red[kWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   for (int r = blockIdx.x; r < rows; r += gridDim.x) {
     const float* xr = x + (int64_t)r * ldx;
     float m = 0.0f;
-    for (int c = threadIdx.x; c < units_per_row; c += kThreads) m = fmaxf(m, absmax16(load16(xr + 16 * c)));
+    for (int u = wave; u < upr; u += kWaves) m = fmaxf(m, absmax_unit(load_unit(xr, u * 1024, k, lane)));
     m = block_max(m, red);
     const float s = (m == 0.0f) ? 1.0f : m / kE4M3Max;
     if (threadIdx.x == 0) scales[r] = s;
     uint8_t* qr = q + (int64_t)r * ldq;
-    for (int c = threadIdx.x; c < units_per_row; c += kThreads)
-      *reinterpret_cast<uint4*>(qr + 16 * c) = encode16_div(load16(xr + 16 * c), s);
+    for (int u = wave; u < upr; u += kWaves) {
+      uint32_t w[4];
+      encode_unit_div(load_unit(xr, u * 1024, k, lane), s, w);
+      store_codes(qr, u * 1024, k, lane, w);
+    }
   }
 }
 
-// ---- MX: two lanes per 32-element block, 16 elements each ----------------------
-__global__ __launch_bounds__(kThreads) void quant_mx_kernel(const float* __restrict__ x,
-                                                            uint32_t blocks_per_row,
-                                                            uint32_t blocks, int64_t ldx,
+// ---- MX: a 32-element block is one float4 of 8 consecutive lanes ---------------
+// Block maxima by xor-shuffles inside each group of 8 lanes; the first lane of a
+// group writes the block's E8M0 code.
+__device__ __forceinline__ void mx_unit(const Unit& u, uint8_t* qrow, uint8_t* crow, int col0,
+                                        int k, int lane) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float m = absmax4(u.v[j]);
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    m = fmaxf(m, __shfl_xor(m, 4, 64));
+    const uint32_t code = mx_code_from_amax(m);
+    const int e = 127 - (int)code;
+    w[j] = encode4_e4m3(ldexpf(u.v[j].x, e), ldexpf(u.v[j].y, e), ldexpf(u.v[j].z, e),
+                        ldexpf(u.v[j].w, e));
+    const int c = col0 + 256 * j + 4 * lane;
+    if ((lane & 7) == 0 && c < k) crow[c >> 5] = (uint8_t)code;
+  }
+  store_codes(qrow, col0, k, lane, w);
+}
+
+__global__ __launch_bounds__(kThreads) void quant_mx_kernel(const float* __restrict__ x, int k,
+                                                            int upr, int units, int64_t ldx,
                                                             uint8_t* __restrict__ q, int64_t ldq,
                                                             uint8_t* __restrict__ codes) {
-  const uint32_t stride = gridDim.x * (kThreads / 2);
-  const int half = threadIdx.x & 1;
-  // every lane runs the same number of iterations so the pair shuffle is always matched
-  for (uint32_t b0 = blockIdx.x * (kThreads / 2); b0 < blocks; b0 += stride) {
-    const uint32_t bi = b0 + (threadIdx.x >> 1);
-    const bool live = bi < blocks;
-    const uint32_t r = live ? bi / blocks_per_row : 0;
-    const uint32_t c = live ? bi - r * blocks_per_row : 0;
-    Vec16 v;
-    float m = 0.0f;
-    if (live) {
-      v = load16(x + (int64_t)r * ldx + 32 * c + 16 * half);
-      m = absmax16(v);
-    }
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    const uint32_t code = mx_code_from_amax(m);
-    if (live) {
-      *reinterpret_cast<uint4*>(q + (int64_t)r * ldq + 32 * c + 16 * half) =
-          encode16_ldexp(v, 127 - (int)code);
-      if (half == 0) codes[(int64_t)r * blocks_per_row + c] = (uint8_t)code;
-    }
+  const int lane = threadIdx.x & 63;
+  const int w0 = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int nw = gridDim.x * kWaves;
+  const int bpr = k / 32;
+  for (int u = w0; u < units; u += 2 * nw) {
+    const int u2 = u + nw;
+    const int r = u / upr, r2 = u2 / upr;
+    const int c0 = (u - r * upr) * 1024, c2 = (u2 - r2 * upr) * 1024;
+    const Unit a = load_unit(x + (int64_t)r * ldx, c0, k, lane);
+    Unit b{};
+    if (u2 < units) b = load_unit(x + (int64_t)r2 * ldx, c2, k, lane);
+    mx_unit(a, q + (int64_t)r * ldq, codes + (int64_t)r * bpr, c0, k, lane);
+    if (u2 < units) mx_unit(b, q + (int64_t)r2 * ldq, codes + (int64_t)r2 * bpr, c2, k, lane);
   }
 }
 
@@ -225,52 +253,47 @@ int grid_for(uint64_t work_items, int per_block, int cap) {
 
 hipError_t launch_quantize_tensor(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
                                   int64_t ldq, float* scale, float* partials, hipStream_t stream) {
-  const uint32_t upr = (uint32_t)(k / 16);
-  const uint32_t units = (uint32_t)(rows * upr);
-  const int grid = grid_for(units, kThreads, kQuantPartials);
-  hipLaunchKernelGGL(amax_partial_kernel, dim3(grid), dim3(kThreads), 0, stream, x, upr, units,
-                     ldx, partials);
+  const int upr = (int)((k + 1023) / 1024);
+  const int units = (int)(rows * upr);
+  // two units per wavefront and iteration
+  const int grid = grid_for((uint64_t)units, 2 * kWaves, kQuantPartials);
+  hipLaunchKernelGGL(amax_partial_kernel, dim3(grid), dim3(kThreads), 0, stream, x, (int)k, upr,
+                     units, ldx, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int grid2 = grid_for(units, kThreads, 4096);
-  hipLaunchKernelGGL(quant_tensor_kernel, dim3(grid2), dim3(kThreads), 0, stream, x, upr, units,
-                     ldx, q, ldq, partials, grid, scale);
+  const int grid2 = grid_for((uint64_t)units, 2 * kWaves, 8192);
+  hipLaunchKernelGGL(quant_tensor_kernel, dim3(grid2), dim3(kThreads), 0, stream, x, (int)k, upr,
+                     units, ldx, q, ldq, partials, grid, scale);
   return hipGetLastError();
-}
-
-template <int T, int U>
-static void launch_row(const float* x, int rows, int upr, int64_t ldx, uint8_t* q, int64_t ldq,
-                       float* scales, hipStream_t stream) {
-  const int rows_per_block = kThreads / T;
-  const int grid = grid_for((uint64_t)rows, rows_per_block, 65535);
-  hipLaunchKernelGGL((quant_row_kernel<T, U>), dim3(grid), dim3(kThreads), 0, stream, x, rows, upr,
-                     ldx, q, ldq, scales);
 }
 
 hipError_t launch_quantize_rowwise(const float* x, int64_t rows, int64_t k, int64_t ldx,
                                    uint8_t* q, int64_t ldq, float* scales, hipStream_t stream) {
-  const int upr = (int)(k / 16);
+  const int upr = (int)((k + 1023) / 1024);
   const int r = (int)rows;
-  if (upr <= 64) launch_row<64, 1>(x, r, upr, ldx, q, ldq, scales, stream);
-  else if (upr <= 128) launch_row<128, 1>(x, r, upr, ldx, q, ldq, scales, stream);
-  else if (upr <= 256) launch_row<256, 1>(x, r, upr, ldx, q, ldq, scales, stream);
-  else if (upr <= 512) launch_row<256, 2>(x, r, upr, ldx, q, ldq, scales, stream);
-  else if (upr <= 1024) launch_row<256, 4>(x, r, upr, ldx, q, ldq, scales, stream);
-  else {
-    const int grid = grid_for((uint64_t)rows, 1, 65535);
-    hipLaunchKernelGGL(quant_row_long_kernel, dim3(grid), dim3(kThreads), 0, stream, x, r, upr,
-                       ldx, q, ldq, scales);
-  }
+  const int grid = grid_for((uint64_t)rows, 1, 65535);
+  if (upr <= kWaves)
+    hipLaunchKernelGGL((quant_row_kernel<1>), dim3(grid), dim3(kThreads), 0, stream, x, r, (int)k,
+                       upr, ldx, q, ldq, scales);
+  else if (upr <= 2 * kWaves)
+    hipLaunchKernelGGL((quant_row_kernel<2>), dim3(grid), dim3(kThreads), 0, stream, x, r, (int)k,
+                       upr, ldx, q, ldq, scales);
+  else if (upr <= 4 * kWaves)
+    hipLaunchKernelGGL((quant_row_kernel<4>), dim3(grid), dim3(kThreads), 0, stream, x, r, (int)k,
+                       upr, ldx, q, ldq, scales);
+  else
+    hipLaunchKernelGGL(quant_row_long_kernel, dim3(grid), dim3(kThreads), 0, stream, x, r, (int)k,
+                       upr, ldx, q, ldq, scales);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
                               int64_t ldq, uint8_t* codes, hipStream_t stream) {
-  const uint32_t bpr = (uint32_t)(k / 32);
-  const uint32_t blocks = (uint32_t)(rows * bpr);
-  const int grid = grid_for(blocks, kThreads / 2, 8192);
-  hipLaunchKernelGGL(quant_mx_kernel, dim3(grid), dim3(kThreads), 0, stream, x, bpr, blocks, ldx,
-                     q, ldq, codes);
+  const int upr = (int)((k + 1023) / 1024);
+  const int units = (int)(rows * upr);
+  const int grid = grid_for((uint64_t)units, 2 * kWaves, 8192);
+  hipLaunchKernelGGL(quant_mx_kernel, dim3(grid), dim3(kThreads), 0, stream, x, (int)k, upr, units,
+                     ldx, q, ldq, codes);
   return hipGetLastError();
 }
 

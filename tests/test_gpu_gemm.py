@@ -71,6 +71,10 @@ def _slice_scales(s, idx, mode):
     ("rowwise", (4096, 4096, 640)),
     ("mx32", (1024, 1024, 512)),      # small-tile kernel
     ("rowwise", (1024, 768, 384)),
+    # more tiles than CUs: persistent workgroups walk several tiles each
+    ("tensor", (8192, 4096, 1024)),
+    ("rowwise", (8192, 8192, 512)),
+    ("mx32", (6144, 8192, 1024)),
 ])
 def test_gemm_interior_sampled(mode, shape):
     """Full-tile shapes on the interior mainloop; the oracle checks sampled 128 x 128 blocks."""
