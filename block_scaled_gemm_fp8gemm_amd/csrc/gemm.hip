@@ -188,7 +188,10 @@ hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
   // MX with K % 128 != 0 reads its codes into registers: the large tile would spill
   const bool mx_ragged = MODE == kMx32 && p.K % 128 != 0;
   if (big_tiles >= 256 * Big::kWgPerCu && !mx_ragged) {
-    if (FP8GEMM_PERSISTENT && all_interior<Big>(p)) return launch_persistent<Big, MODE, OutT>(p, stream);
+    // persistent streams pay off from about eight tiles per CU on (measured)
+    const bool many = big_tiles >= 8 * 256;
+    if ((FP8GEMM_PERSISTENT || many) && all_interior<Big>(p))
+      return launch_persistent<Big, MODE, OutT>(p, stream);
     return launch_cfg<Big, MODE, OutT>(p, stream);
   }
   return launch_cfg<Mid, MODE, OutT>(p, stream);
@@ -243,8 +246,11 @@ __host__ __device__ constexpr int64_t counter_bytes(int64_t tiles) {
 template <class Cfg, int MODE, typename OutT>
 __global__ __launch_bounds__(Cfg::kThreads, 1) void splitk_kernel(GemmProblem p, int tiles_m,
                                                                     int splits) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::kLdsBytes];
-  __shared__ int s_last;
+  // the arrival flag lives in the same LDS object as the ring: a second LDS
+  // variable makes the compiler wait for every ring copy before every LDS read
+  constexpr int kFlagOff = (Cfg::kLdsBytes + 15) / 16 * 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kFlagOff + 16];
+  int& s_last = *reinterpret_cast<int*>(lds + kFlagOff);
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   const int tile = blockIdx.x / splits, ks = blockIdx.x % splits;
   const int tm = tile % tiles_m, tn = tile / tiles_m;

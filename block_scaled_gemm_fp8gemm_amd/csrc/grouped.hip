@@ -9,11 +9,16 @@
 //   * the grid is one workgroup per CU; expert row offsets stay on the device and
 //     every workgroup derives the per-expert tile counts ceil(m_g/BM)*ceil(N/BN)
 //     and their prefix sums in LDS, so the host never synchronizes;
-//   * tiles are numbered expert by expert, tile rows fastest, so the tiles
-//     running at the same time share the same expert weight columns; the slot of
-//     a workgroup inside each round of the persistent loop is remapped so one XCD
-//     runs a contiguous run of tiles and reads each weight tile into its own L2
-//     once (the MI355X counterpart of sharing expert weights by multicast);
+//   * tiles are numbered expert by expert and, inside an expert, in the same
+//     grouped order as the dense GEMM (groups of a few tile rows, column-major
+//     inside a group); the slot of a workgroup inside each round of the
+//     persistent loop is remapped so one XCD runs a contiguous run of tiles, and
+//     the ~32 tiles resident on an XCD cover a few tile rows by several tile
+//     columns of one expert: both the activation rows and the expert weight
+//     columns they read are shared in that XCD's L2 (the MI355X counterpart of
+//     sharing expert weights by multicast).  Walking all tile rows of one column
+//     first instead shares the weights but makes each XCD stream ~1 MB of
+//     distinct activations per 128-deep K step, which measured 2.3x slower;
 //   * each tile uses the dense mainloop and epilogue, with rows past the expert's
 //     end clamped on load and masked on store (ragged experts, empty experts).
 #include <hip/hip_runtime.h>
@@ -28,13 +33,78 @@ namespace {
 
 constexpr int kMaxGroups = 1024;
 
+// The tiles of one persistent workgroup: list entry i is tile slot + i * stride
+// of the expert-major order (expert by expert, grouped order inside an expert).
+template <class Cfg, int MODE>
+struct GroupedTiles {
+  GroupedProblem p;
+  const int* tile_start;   // LDS: first tile of each expert, prefix sums
+  const int* row_begin;    // LDS: clamped expert row ranges
+  const int* row_end;
+  int tiles_n, slot, stride;
+
+  struct Where {
+    int g, m0, m_end, n0;
+  };
+  __device__ Where where(int i) const {
+    const int t = slot + i * stride;
+    int lo = 0, hi = p.groups - 1;          // expert of tile t: last g with tile_start[g] <= t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile_start[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    // the values come from LDS, so the compiler cannot see that they are the same
+    // in every lane; they are, and keeping them in scalar registers keeps every
+    // address derived from them (buffer descriptors included) scalar
+    Where w;
+    w.g = __builtin_amdgcn_readfirstlane(lo);
+    const int local = t - __builtin_amdgcn_readfirstlane(tile_start[w.g]);
+    const int rb = __builtin_amdgcn_readfirstlane(row_begin[w.g]);
+    w.m_end = __builtin_amdgcn_readfirstlane(row_end[w.g]);
+    const int tiles_m_g = (w.m_end - rb + Cfg::BM - 1) / Cfg::BM;
+    int tm, tn;
+    grouped_tile(local, tiles_m_g, tiles_n, kGroupM, &tm, &tn);
+    w.m0 = rb + tm * Cfg::BM;
+    w.n0 = tn * Cfg::BN;
+    return w;
+  }
+  __device__ TileOperands op_at(const Where& w) const {
+    TileOperands op;
+    op.A = p.A + (int64_t)w.m0 * p.lda;
+    op.lda = p.lda;
+    op.a_rows = w.m_end - w.m0;
+    op.B = p.B + (int64_t)w.g * p.stride_b + (int64_t)w.n0 * p.ldb;
+    op.ldb = p.ldb;
+    op.b_rows = p.N - w.n0;
+    op.K = p.K;
+    op.sld = p.K / 32;
+    op.sa = op.sb = nullptr;
+    op.ra = op.rb = nullptr;
+    if (MODE == kMx32) {
+      op.sa = static_cast<const uint8_t*>(p.scale_a) + (int64_t)w.m0 * op.sld;
+      op.sb = static_cast<const uint8_t*>(p.scale_b) + ((int64_t)w.g * p.N + w.n0) * op.sld;
+    }
+    if (MODE == kRowwise) {
+      op.ra = static_cast<const float*>(p.scale_a) + w.m0;
+      op.rb = static_cast<const float*>(p.scale_b) + (int64_t)w.g * p.N + w.n0;
+    }
+    return op;
+  }
+  __device__ TileOperands op(int i) const { return op_at(where(i)); }
+};
+
 template <class Cfg, int MODE, typename OutT, bool KALIGNED>
 __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void grouped_kernel(GroupedProblem p,
                                                                                  int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[Cfg::kLdsBytes];
-  __shared__ int tile_start[kMaxGroups + 1];
-  __shared__ int row_begin[kMaxGroups];
-  __shared__ int row_end[kMaxGroups];
+  // One LDS object holds the tile ring and the expert tables: with several LDS
+  // variables the compiler no longer proves that fragment reads and the ring's
+  // DMA writes are independent and waits for every copy before every read.
+  constexpr int kTableOff = (Cfg::kLdsBytes + 15) / 16 * 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kTableOff + (3 * kMaxGroups + 1) * 4];
+  int* tile_start = reinterpret_cast<int*>(lds + kTableOff);
+  int* row_begin = tile_start + kMaxGroups + 1;
+  int* row_end = row_begin + kMaxGroups;
 
   if (threadIdx.x == 0) {
     // Offsets are clamped into [0, total_m] so no row outside A or C is touched
@@ -52,54 +122,41 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void grouped_kerne
     }
   }
   __syncthreads();
-  const int total = tile_start[p.groups];
-  const int slot = xcd_linear(blockIdx.x, gridDim.x);
+  const int total = __builtin_amdgcn_readfirstlane(tile_start[p.groups]);
+  const GroupedTiles<Cfg, MODE> src{p, tile_start, row_begin, row_end, tiles_n,
+                                    xcd_linear(blockIdx.x, gridDim.x), (int)gridDim.x};
+  const int count = total > src.slot ? (total - src.slot + src.stride - 1) / src.stride : 0;
   const float* fsa = static_cast<const float*>(p.scale_a);
   const float* fsb = static_cast<const float*>(p.scale_b);
+  OutT* C = static_cast<OutT*>(p.C);
+  // full tiles with K % 512 == 0 run as copy streams (one per run of such tiles);
+  // tiles cut by an expert's last row take the general path
+  constexpr bool kStream = KALIGNED && Cfg::kSlots == 4;
+  auto streamable = [&](int i) __attribute__((always_inline)) {
+    return kStream && p.K % 512 == 0 && interior_tile<Cfg, MODE>(src.op(i));
+  };
+  auto epi = [&](const v16f (&acc)[Cfg::kFragM][Cfg::kFragN], int i, int rbuf)
+                 __attribute__((always_inline)) {
+    const auto w = src.where(i);
+    const float ts = (MODE == kTensor) ? fsa[0] * fsb[w.g] : 1.0f;
+    epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, p.ldc, w.m0, w.n0, ts, rbuf);
+  };
 
-  for (int t = slot; t < total; t += gridDim.x) {
-    // expert of tile t: last g with tile_start[g] <= t
-    int lo = 0, hi = p.groups - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (tile_start[mid] <= t) lo = mid;
-      else hi = mid - 1;
-    }
-    const int g = lo;
-    const int local = t - tile_start[g];
-    const int rows_g = row_end[g] - row_begin[g];
-    const int tiles_m_g = (rows_g + Cfg::BM - 1) / Cfg::BM;
-    const int tm = local % tiles_m_g, tn = local / tiles_m_g;
-    const int m0 = row_begin[g] + tm * Cfg::BM;
-    const int m_end = row_end[g];
-    const int n0 = tn * Cfg::BN;
-
-    TileOperands op;
-    op.A = p.A + (int64_t)m0 * p.lda;
-    op.lda = p.lda;
-    op.a_rows = m_end - m0;
-    const uint8_t* Bg = p.B + (int64_t)g * p.stride_b;
-    op.B = Bg + (int64_t)n0 * p.ldb;
-    op.ldb = p.ldb;
-    op.b_rows = p.N - n0;
-    op.K = p.K;
-    op.sld = p.K / 32;
-    op.sa = op.sb = nullptr;
-    op.ra = op.rb = nullptr;
-    if (MODE == kMx32) {
-      const int nblk = p.K / 32;
-      op.sa = static_cast<const uint8_t*>(p.scale_a) + (int64_t)m0 * nblk;
-      op.sb = static_cast<const uint8_t*>(p.scale_b) + ((int64_t)g * p.N + n0) * nblk;
-    }
-    if (MODE == kRowwise) {
-      op.ra = fsa + m0;
-      op.rb = fsb + (int64_t)g * p.N + n0;
-    }
-
+  int i = 0;
+  while (i < count) {
     __syncthreads();  // the previous tile's epilogue is done with LDS
-    const float ts = (MODE == kTensor) ? fsa[0] * fsb[g] : 1.0f;
-    gemm_tile<Cfg, MODE, OutT, KALIGNED>(op, lds, static_cast<OutT*>(p.C), p.ldc, m0, m_end, n0,
-                                         p.N, ts);
+    if (streamable(i)) {
+      int j = i + 1;
+      while (j < count && streamable(j)) ++j;
+      stream_interior<Cfg, MODE, 2 * Cfg::kFragM * Cfg::kFragN>(src, i, j, lds, epi);
+      i = j;
+    } else {
+      const auto w = src.where(i);
+      const float ts = (MODE == kTensor) ? fsa[0] * fsb[w.g] : 1.0f;
+      gemm_tile<Cfg, MODE, OutT, KALIGNED>(src.op_at(w), lds, C, p.ldc, w.m0, w.m_end, w.n0, p.N,
+                                           ts);
+      ++i;
+    }
   }
 }
 
