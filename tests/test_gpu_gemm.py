@@ -96,7 +96,7 @@ def test_gemm_interior_sampled(mode, shape):
 
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("shape", [(128, 4096, 4096), (100, 1000, 2048), (256, 640, 4096),
-                                   (128, 4096, 1024)])
+                                   (128, 4096, 1024), (200, 1024, 1024)])
 def test_gemm_splitk(mode, shape):
     """Shapes with few output tiles run split along K (ragged M / N included)."""
     M, N, K = shape
@@ -106,6 +106,23 @@ def test_gemm_splitk(mode, shape):
     C = to_host(_run_gpu(qa, sa, qb, sb, mode, "bf16"))
     Cr, Ar = O.gemm_reference(qa, sa, qb, sb, mode)
     assert_within_bound(C, Cr, Ar, "bf16", f"split-K {mode} {shape}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("out,shape", [
+    ("f16", (1, 2048, 1024)),         # one row of A
+    ("bf16", (17, 2056, 4160)),       # ragged M, N % 16 = 8, K % 128 = 64
+    ("f16", (64, 8200, 1056)),        # K % 128 = 32
+    ("bf16", (100, 2048, 384)),       # three 128-K tiles
+])
+def test_gemm_few_rows(mode, out, shape):
+    """Few rows of A against many columns (decode-like), ragged in every dimension."""
+    M, N, K = shape
+    qa, sa, qb, sb = _oracle_operands(M, N, K, mode, seed=7 * M + N + K, dist="mx_block")
+    announce("gemm few rows", mode, out, shape)
+    C = to_host(_run_gpu(qa, sa, qb, sb, mode, out))
+    Cr, Ar = O.gemm_reference(qa, sa, qb, sb, mode)
+    assert_within_bound(C, Cr, Ar, out, f"few rows {mode}/{out}/{shape}")
 
 
 def test_gemm_splitk_repeat_and_interleave():
