@@ -231,6 +231,8 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int mode) {
     if (tm * tn * s >= kSplitTargetWgs) break;
   }
   if (best == 1) return plan;
+  // the partials are addressed with 32-bit buffer offsets
+  if (tm * tn * best * SplitCfg::BM * SplitCfg::BN * 4 >= ((int64_t)1 << 31)) return plan;
   plan.splits = best;
   plan.tiles_m = (int)tm;
   plan.tiles_n = (int)tn;
@@ -283,31 +285,30 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void splitk_kernel(GemmProblem p,
   if (interior_tile<Cfg, MODE>(op)) mainloop_interior<Cfg, MODE, 4>(op, lds, acc);
   else mainloop<Cfg, MODE, true>(op, lds, acc);
 
-  // partial tile: float4 r of thread x at [slice][tile][r][x] (coalesced per r)
+  // partial tile: float4 r of thread x at [tile][slice][r][x] (coalesced per r)
   const int tiles = tiles_m * (int)((p.N + Cfg::BN - 1) / Cfg::BN);
   int* counters = static_cast<int*>(p.workspace);
-  v4f* partials = reinterpret_cast<v4f*>(static_cast<uint8_t*>(p.workspace) + counter_bytes(tiles));
   constexpr int kVec = FM * FN * 4;
-  auto part = [&](int slice) {
-    return partials + ((int64_t)tile * splits + slice) * kVec * Cfg::kThreads + threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rp =
+      buffer_rsrc(static_cast<uint8_t*>(p.workspace) + counter_bytes(tiles),
+                  (uint32_t)((int64_t)tiles * splits * kVec * Cfg::kThreads * 16));
+  auto poff = [&](int slice, int r) {
+    return ((((tile * splits + slice) * kVec) + r) * Cfg::kThreads + (int)threadIdx.x) * 16;
   };
-  // Partials travel as relaxed agent-scope atomics (8 bytes each): on gfx950 they
-  // are written through to, and read back from, the memory level shared by all
-  // XCDs, so ordering only needs the stores to have completed before the arrival
-  // is counted.  (An agent-scope release/acquire fence pair would write back and
-  // invalidate the whole L2 of the XCD instead, which cost more than the GEMM.)
+  // Partials travel as 16-byte buffer accesses with the SC1 cache policy, the
+  // policy of relaxed agent-scope atomics on gfx950: stores are written through
+  // to, and loads read from, the memory level shared by all XCDs, so ordering
+  // only needs the stores to have completed before the arrival is counted.  (An
+  // agent-scope release/acquire fence pair would write back and invalidate the
+  // whole L2 of the XCD instead, which cost more than the GEMM.)
+  constexpr int kSc1 = 16;
   {
-    uint64_t* mine = reinterpret_cast<uint64_t*>(part(ks));
 #pragma unroll
     for (int r = 0; r < kVec; ++r) {
       const v16f& a = acc[(r >> 2) / FN][(r >> 2) % FN];
       const int g = r & 3;
-      const float2 lo{a[4 * g], a[4 * g + 1]}, hi{a[4 * g + 2], a[4 * g + 3]};
-      uint64_t* d = mine + 2 * r * Cfg::kThreads;
-      __hip_atomic_store(d, __builtin_bit_cast(uint64_t, lo), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(d + 1, __builtin_bit_cast(uint64_t, hi), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      const v4f v{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rp, poff(ks, r), 0, kSc1);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);                       // this thread's partial stored
@@ -336,16 +337,10 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void splitk_kernel(GemmProblem p,
     for (int b = 0; b < kBatch; ++b) {
       const int slice = s0 + b;
       if (slice < splits && slice != ks) {
-        const uint64_t* src = reinterpret_cast<const uint64_t*>(part(slice));
 #pragma unroll
-        for (int r = 0; r < kVec; ++r) {
-          const uint64_t* d = src + 2 * r * Cfg::kThreads;
-          const float2 lo = __builtin_bit_cast(
-              float2, __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-          const float2 hi = __builtin_bit_cast(
-              float2, __hip_atomic_load(d + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-          v[b][r] = v4f{lo.x, lo.y, hi.x, hi.y};
-        }
+        for (int r = 0; r < kVec; ++r)
+          v[b][r] = __builtin_bit_cast(
+              v4f, __builtin_amdgcn_raw_buffer_load_b128(rp, poff(slice, r), 0, kSc1));
       }
     }
 #pragma unroll

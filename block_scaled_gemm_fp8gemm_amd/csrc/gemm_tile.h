@@ -61,6 +61,7 @@ namespace fp8gemm {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 // BM x BN output tile, WM x WN per wavefront, SLOTS-deep LDS ring, and the number
