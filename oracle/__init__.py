@@ -3,7 +3,8 @@
 A plain, slow, float64 reference of what the GPU path computes: e4m3fn and E8M0
 decoding by table, round-to-nearest-even encoding by table search, per-tensor,
 row-wise and 32-element microscaled quantisation, the scaled GEMM with its
-error bound, and the grouped (mixture-of-experts) form.
+error bound, the fused bias-and-activation epilogue, and the grouped
+(mixture-of-experts) form.
 
 Only ``tests/``, the smoke check in ``__graft_entry__`` and the CPU-baseline
 leg of ``bench.py`` may import this package.  The library under
@@ -16,8 +17,8 @@ paragraph), the dtype ``torch.float8_e4m3fn`` (the Cutlass-named Triton FP8
 post, parameter list, precision settings) and MXFP8 micro-scaling
 ("Hopper/Blackwell architecture features" §12.6.1, hardware table).  The bit
 layouts therefore follow the public standards those names refer to: the OCP
-8-bit floating point specification (OFP8, E4M3 with no infinities, one NaN
-pattern per sign, max 448) and the OCP Microscaling (MX) formats
+8-bit floating point specification (OFP8: E4M3 with no infinities, one NaN
+pattern per sign, max 448; E5M2 with IEEE-like infinities and NaNs, max 57344) and the OCP Microscaling (MX) formats
 specification v1.0 (E8M0 shared scale, 32-element blocks, scale exponent =
 floor(log2(amax)) - emax of the element format).
 
@@ -26,15 +27,19 @@ against exhaustive enumeration, exact rational arithmetic, integer-exact
 products, closed forms or the specifications' tabulated points
 (``tests/golden/``).  No function is "parity unpinned".
 """
-from .formats import (E4M3_DECODE, E4M3_MAX, E8M0_DECODE, decode_e4m3, decode_e8m0,
-                      encode_e4m3)
+from .formats import (E4M3_DECODE, E4M3_MAX, E5M2_DECODE, E5M2_MAX, E8M0_DECODE, FORMATS,
+                      decode, decode_e4m3, decode_e5m2, decode_e8m0, encode, encode_e4m3,
+                      encode_e5m2)
 from .quant import quantize, quantize_mx, quantize_rowwise, quantize_tensor
-from .gemm import (dequantize, gemm_reference, grouped_reference, output_ulp, tolerance,
+from .gemm import (ACT_LIPSCHITZ, activation, dequantize, epilogue_reference,
+                   epilogue_tolerance, gemm_reference, grouped_reference, output_ulp, tolerance,
                    within_bound, round_to_output)
 
 __all__ = [
-    "E4M3_DECODE", "E4M3_MAX", "E8M0_DECODE", "decode_e4m3", "decode_e8m0", "encode_e4m3",
+    "E4M3_DECODE", "E4M3_MAX", "E5M2_DECODE", "E5M2_MAX", "E8M0_DECODE", "FORMATS", "decode",
+    "decode_e4m3", "decode_e5m2", "decode_e8m0", "encode", "encode_e4m3", "encode_e5m2",
     "quantize", "quantize_mx", "quantize_rowwise", "quantize_tensor",
     "dequantize", "gemm_reference", "grouped_reference", "output_ulp", "tolerance",
-    "within_bound", "round_to_output",
+    "within_bound", "round_to_output", "ACT_LIPSCHITZ", "activation", "epilogue_reference",
+    "epilogue_tolerance",
 ]

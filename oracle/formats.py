@@ -1,4 +1,4 @@
-"""e4m3fn and E8M0 codes: decode tables and the round-to-nearest-even encoder.
+"""e4m3fn, e5m2 and E8M0 codes: decode tables and the round-to-nearest-even encoders.
 
 TEST INFRASTRUCTURE (see the package docstring).
 
@@ -9,6 +9,12 @@ layout below is the OCP OFP8 one: 1 sign bit, 4 exponent bits with bias 7,
 3 mantissa bits, subnormals when the exponent field is 0, and S.1111.111 as
 the only NaN (no infinities), so the largest finite magnitude is
 1.75 * 2^8 = 448.
+
+E5M2 is the second FP8 format the JAX/Triton Blackwell FP8 GEMM post names
+(its second paragraph contrasts the two).  The OCP OFP8 layout: 1 sign bit,
+5 exponent bits with bias 15, 2 mantissa bits, subnormals when the exponent
+field is 0, and the IEEE-like specials S.11111.00 = infinity and S.11111.xx
+(xx != 0) = NaN, so the largest finite magnitude is 1.75 * 2^15 = 57344.
 
 E8M0 is the MX shared-scale format ("Hopper/Blackwell architecture features"
 §12.6.1 names MXFP8): an 8-bit biased exponent, value 2^(code-127), with 0xFF
@@ -22,6 +28,8 @@ import numpy as np
 
 E4M3_MAX = 448.0
 E4M3_NAN_CODE = 0x7F
+E5M2_MAX = 57344.0
+E5M2_NAN_CODE = 0x7F
 
 
 def _e4m3_value(code: int) -> float:
@@ -38,20 +46,42 @@ def _e4m3_value(code: int) -> float:
     return -mag if s else mag
 
 
+def _e5m2_value(code: int) -> float:
+    """Value of one e5m2 code from its bit fields (OFP8 E5M2 definition)."""
+    s = (code >> 7) & 1
+    e = (code >> 2) & 0x1F
+    m = code & 0x3
+    if e == 0x1F:
+        mag = math.inf if m == 0 else math.nan
+    elif e == 0:
+        mag = math.ldexp(m, -16)            # subnormal: 0.m * 2^(1-15) = m * 2^-16
+    else:
+        mag = math.ldexp(4 + m, e - 15 - 2)  # normal: 1.m * 2^(e-15) = (4+m) * 2^(e-17)
+    return -mag if s else mag
+
+
 def _e8m0_value(code: int) -> float:
     return math.nan if code == 0xFF else math.ldexp(1.0, code - 127)
 
 
 E4M3_DECODE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
+E5M2_DECODE = np.array([_e5m2_value(c) for c in range(256)], dtype=np.float64)
 E8M0_DECODE = np.array([_e8m0_value(c) for c in range(256)], dtype=np.float64)
 
-# Non-negative finite magnitudes, indexed by code 0x00..0x7E (strictly increasing).
+# Non-negative finite magnitudes, indexed by code (strictly increasing):
+# e4m3fn 0x00..0x7E, e5m2 0x00..0x7B.
 _POS_MAGS = E4M3_DECODE[:0x7F].copy()
+_POS_MAGS_E5M2 = E5M2_DECODE[:0x7C].copy()
 
 
 def decode_e4m3(q: np.ndarray) -> np.ndarray:
     """float64 values of uint8 e4m3fn codes (exact)."""
     return E4M3_DECODE[np.asarray(q, dtype=np.uint8)]
+
+
+def decode_e5m2(q: np.ndarray) -> np.ndarray:
+    """float64 values of uint8 e5m2 codes (exact)."""
+    return E5M2_DECODE[np.asarray(q, dtype=np.uint8)]
 
 
 def decode_e8m0(c: np.ndarray) -> np.ndarray:
@@ -83,3 +113,51 @@ def encode_e4m3(v: np.ndarray) -> np.ndarray:
     code = np.where(a >= E4M3_MAX, np.uint8(0x7E), code)
     code = np.where(np.isnan(a), np.uint8(E4M3_NAN_CODE), code)
     return (code | sign).astype(np.uint8)
+
+
+def _encode_by_table(v: np.ndarray, mags: np.ndarray, fmax: float, nan_code: int) -> np.ndarray:
+    """Nearest code among the non-negative finite magnitudes `mags` (code = index),
+    ties to the even code, saturating at fmax, sign copied from v."""
+    v = np.asarray(v)
+    a = np.abs(v).astype(np.float64)
+    sign = np.signbit(v).astype(np.uint8) << 7
+    top = len(mags) - 1
+    lo = np.searchsorted(mags, a, side="right") - 1
+    lo = np.clip(lo, 0, top)
+    hi = np.minimum(lo + 1, top)
+    d_lo = a - mags[lo]
+    d_hi = mags[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (lo % 2 == 1))
+    code = np.where(take_hi, hi, lo).astype(np.uint8)
+    code = np.where(a >= fmax, np.uint8(top), code)
+    code = np.where(np.isnan(a), np.uint8(nan_code), code)
+    return (code | sign).astype(np.uint8)
+
+
+def encode_e5m2(v: np.ndarray) -> np.ndarray:
+    """Nearest e5m2 code to each value, ties to the even code, saturating.
+
+    The same definition as ``encode_e4m3`` over the 124 non-negative finite e5m2
+    magnitudes: magnitudes at or above 57344 (infinity included) saturate to
+    57344 (code 0x7B) -- the quantisers scale into range, and a saturating
+    conversion never produces the format's infinity; NaN gives 0x7F | sign.
+    """
+    return _encode_by_table(v, _POS_MAGS_E5M2, E5M2_MAX, E5M2_NAN_CODE)
+
+
+# Element formats by name: decode, encode, largest finite magnitude and the
+# exponent of that magnitude (emax, used by the MX scale rule).
+FORMATS = {
+    "e4m3": {"decode": decode_e4m3, "encode": encode_e4m3, "max": E4M3_MAX, "emax": 8},
+    "e5m2": {"decode": decode_e5m2, "encode": encode_e5m2, "max": E5M2_MAX, "emax": 15},
+}
+
+
+def decode(q: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
+    """float64 values of codes of element format `fmt`."""
+    return FORMATS[fmt]["decode"](q)
+
+
+def encode(v: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
+    """Round-to-nearest-even saturating encoding onto element format `fmt`."""
+    return FORMATS[fmt]["encode"](v)

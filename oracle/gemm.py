@@ -15,13 +15,18 @@ Blackwell FP8 GEMM post's kernel pseudocode; ``acc.to(tl.bfloat16)`` in
 "Hopper/Blackwell architecture features" §12.7.1/§12.7.2), so the result is
 delivered in fp16 or bf16 after fp32 accumulation.
 
+Either operand may hold e4m3fn or e5m2 codes (the JAX/Triton Blackwell FP8
+GEMM post names both formats; mixed E4M3 x E5M2 products are the usual
+gradient GEMM).
+
 This reference evaluates the sum in float64.  Every decoded e4m3 value is
 i * 2^j with |i| <= 15 and -9 <= j <= 5, so for per-tensor and row-wise scaling
-the inner sum sum_k decode*decode is an integer multiple of 2^-18 below 2^50
-units and float64 holds it exactly in any summation order; only the final
-multiplication by the scales rounds.  For MX each term carries a power-of-two
-block factor, which float64 also represents exactly; only the sum across blocks
-rounds (relative error near 1e-15 of sum |a*b|).
+of two e4m3 operands the inner sum sum_k decode*decode is an integer multiple of
+2^-18 below 2^50 units and float64 holds it exactly in any summation order; only
+the final multiplication by the scales rounds.  e5m2 values span 2^-16 to
+57344, so sums with an e5m2 operand, like MX sums (each term carries a
+power-of-two block factor), may round in float64: relative error near 1e-15 of
+sum |a*b|, far inside the acceptance bound.
 
 Acceptance bound (read from the target statement of this GEMM):
     |C - C_ref| <= 1e-3 * sum_k |dq_a[m,k] * dq_b[n,k]| + ulp_out(|C_ref|)
@@ -32,7 +37,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import decode_e4m3, decode_e8m0
+from .formats import decode, decode_e8m0
 from .quant import MX_BLOCK
 
 _OUT_FORMATS = {
@@ -42,9 +47,9 @@ _OUT_FORMATS = {
 }
 
 
-def dequantize(q: np.ndarray, scale, mode: str) -> np.ndarray:
-    """float64 values represented by codes q [R,K] and their scales."""
-    v = decode_e4m3(q)
+def dequantize(q: np.ndarray, scale, mode: str, fmt: str = "e4m3") -> np.ndarray:
+    """float64 values represented by codes q [R,K] (element format fmt) and their scales."""
+    v = decode(q, fmt)
     if mode == "tensor":
         return v * float(np.asarray(scale, dtype=np.float32))
     if mode == "rowwise":
@@ -60,23 +65,25 @@ def _select(x, idx):
     return x if idx is None else x[np.asarray(idx)]
 
 
-def gemm_reference(qa, sa, qb, sb, mode: str, rows=None, cols=None):
+def gemm_reference(qa, sa, qb, sb, mode: str, rows=None, cols=None, fmt_a: str = "e4m3",
+                   fmt_b: str = "e4m3"):
     """(C_ref, abs_ref) in float64 for the selected rows of A and columns of C.
 
-    qa: uint8 [M,K]; qb: uint8 [N,K] (column-major B).  Scales: "tensor" ->
-    float32 scalars; "rowwise" -> float32 [M] and [N]; "mx32" -> uint8 E8M0
-    [M,K/32] and [N,K/32].  ``rows``/``cols`` pick a sub-block (default all).
+    qa: uint8 [M,K]; qb: uint8 [N,K] (column-major B); fmt_a / fmt_b: their
+    element formats ("e4m3" or "e5m2").  Scales: "tensor" -> float32 scalars;
+    "rowwise" -> float32 [M] and [N]; "mx32" -> uint8 E8M0 [M,K/32] and
+    [N,K/32].  ``rows``/``cols`` pick a sub-block (default all).
     """
     qa_s = _select(qa, rows)
     qb_s = _select(qb, cols)
     if mode == "tensor":
-        da, db = decode_e4m3(qa_s), decode_e4m3(qb_s)
+        da, db = decode(qa_s, fmt_a), decode(qb_s, fmt_b)
         f = float(np.float32(sa)) * float(np.float32(sb))
-        inner = da @ db.T                        # exact: multiples of 2^-18 below 2^50 units
+        inner = da @ db.T                        # e4m3 x e4m3: exact (see above)
         absin = np.abs(da) @ np.abs(db).T
         return inner * f, absin * abs(f)
     if mode == "rowwise":
-        da, db = decode_e4m3(qa_s), decode_e4m3(qb_s)
+        da, db = decode(qa_s, fmt_a), decode(qb_s, fmt_b)
         fa = _select(np.asarray(sa, np.float32), rows).astype(np.float64)
         fb = _select(np.asarray(sb, np.float32), cols).astype(np.float64)
         inner = da @ db.T
@@ -84,8 +91,8 @@ def gemm_reference(qa, sa, qb, sb, mode: str, rows=None, cols=None):
         outer = fa[:, None] * fb[None, :]
         return inner * outer, absin * np.abs(outer)
     if mode == "mx32":
-        da = dequantize(qa_s, _select(sa, rows), "mx32")
-        db = dequantize(qb_s, _select(sb, cols), "mx32")
+        da = dequantize(qa_s, _select(sa, rows), "mx32", fmt_a)
+        db = dequantize(qb_s, _select(sb, cols), "mx32", fmt_b)
         return da @ db.T, np.abs(da) @ np.abs(db).T
     raise ValueError(f"unknown scale mode {mode!r}")
 
@@ -119,6 +126,59 @@ def grouped_reference(qa, sa, offsets, qb, sb, mode: str, rows=None, cols=None):
         C[sel] = c
         A[sel] = a
     return C, A
+
+
+# ---- fused epilogue: bias and activation ------------------------------------
+# The Cutlass-named Triton FP8 post fuses a Cutlass bias_add_relu epilogue into
+# the GEMM to save a round trip of C through memory.  Read here as
+#     C[m,n] = act(y[m,n] + bias[n]),  y the scaled GEMM above,
+# with act one of ReLU (the post's), or the exact (erf) GELU and SiLU, the other
+# activations a GEMM epilogue commonly fuses.
+
+# Lipschitz bounds of the activations: sup |act'| (GELU: 1.1289 at y = sqrt(2);
+# SiLU: 1.0998 at y = 2.3994)
+ACT_LIPSCHITZ = {"none": 1.0, "relu": 1.0, "gelu": 1.129, "silu": 1.1}
+
+
+def activation(y: np.ndarray, act: str) -> np.ndarray:
+    """The activation in float64: identity, max(y, 0), y * (1 + erf(y / sqrt 2)) / 2
+    or y / (1 + exp(-y))."""
+    y = np.asarray(y, dtype=np.float64)
+    if act == "none":
+        return y
+    if act == "relu":
+        return np.maximum(y, 0.0)
+    if act == "gelu":
+        from scipy.special import erf
+        return 0.5 * y * (1.0 + erf(y / np.sqrt(2.0)))
+    if act == "silu":
+        with np.errstate(over="ignore"):
+            return y / (1.0 + np.exp(-y))
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def epilogue_reference(C_ref, abs_ref, bias, act: str, cols=None):
+    """(out_ref, y_ref) of the fused epilogue: y = C_ref + bias[n] (float64, bias
+    float32 [N] or None), out = act(y).  ``cols`` selects the bias entries of the
+    columns C_ref holds (default all)."""
+    y = np.asarray(C_ref, dtype=np.float64)
+    if bias is not None:
+        b = np.asarray(bias, dtype=np.float32).astype(np.float64)
+        y = y + (b if cols is None else b[np.asarray(cols)])[None, :]
+    return activation(y, act), y
+
+
+def epilogue_tolerance(out_ref, y_ref, abs_ref, act: str, out: str) -> np.ndarray:
+    """Bound for the fused epilogue, from the arithmetic: the GEMM part
+    1e-3 * sum|a*b|, plus the fp32 rounding of the scaled value and of the bias
+    add (2^-22 |y|), both through the activation's Lipschitz bound L; plus the
+    activation's own fp32 evaluation (2^-20 (|act(y)| + |y|), covering the
+    cancellation in 1 + erf for large negative y); plus one output ulp."""
+    L = ACT_LIPSCHITZ[act]
+    y = np.abs(np.asarray(y_ref, np.float64))
+    o = np.abs(np.asarray(out_ref, np.float64))
+    return (L * (1e-3 * np.asarray(abs_ref, np.float64) + 2.0 ** -22 * y)
+            + 2.0 ** -20 * (o + y) + output_ulp(out_ref, out))
 
 
 def output_ulp(x: np.ndarray, out: str) -> np.ndarray:

@@ -1,4 +1,4 @@
-"""fp32 -> e4m3fn quantisation with per-tensor, row-wise and 32-element MX scales.
+"""fp32 -> e4m3fn / e5m2 quantisation with per-tensor, row-wise and 32-element MX scales.
 
 TEST INFRASTRUCTURE (see the package docstring).
 
@@ -20,6 +20,10 @@ scale rule open; the readings taken here are:
   Each element becomes ``encode(x * 2^-e)``; the product is a power-of-two
   scaling, exact in float64, and values in (448, 512) saturate.
 
+The same rules quantise to e5m2 (the JAX/Triton Blackwell FP8 GEMM post's
+second FP8 format) with its largest magnitude 57344 in place of 448 and its
+largest exponent 15 in place of 8 (the OCP MX rule for MXFP8 E5M2 elements).
+
 Inputs are rows x K float32 arrays with K contiguous; a column-major B is
 passed as its N x K transpose, so "row" always means the outer index.
 """
@@ -27,47 +31,50 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import E4M3_MAX, encode_e4m3
+from .formats import FORMATS
 
 MX_BLOCK = 32
 E4M3_EMAX = 8          # floor(log2(448))
+E5M2_EMAX = 15         # floor(log2(57344))
 
 
-def _scale_from_amax(amax: np.ndarray) -> np.ndarray:
-    """fl32(amax / 448) elementwise, 1.0 where amax is zero (binary32 division)."""
+def _scale_from_amax(amax: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
+    """fl32(amax / fmax) elementwise (fmax = 448 or 57344), 1.0 where amax is zero
+    (binary32 division)."""
     amax = np.asarray(amax, dtype=np.float32)
-    s = amax / np.float32(E4M3_MAX)
+    s = amax / np.float32(FORMATS[fmt]["max"])
     return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
 
 
-def quantize_tensor(x: np.ndarray):
+def quantize_tensor(x: np.ndarray, fmt: str = "e4m3"):
     """Per-tensor scale: returns (q uint8 [R,K], s float32 scalar array shape ())."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(x)) if x.size else np.float32(0)
-    s = _scale_from_amax(amax)
-    q = encode_e4m3(x / s)          # float32 / float32: binary32 division
+    s = _scale_from_amax(amax, fmt)
+    q = FORMATS[fmt]["encode"](x / s)          # float32 / float32: binary32 division
     return q, np.asarray(s, dtype=np.float32).reshape(())
 
 
-def quantize_rowwise(x: np.ndarray):
+def quantize_rowwise(x: np.ndarray, fmt: str = "e4m3"):
     """One scale per row (reduction over K): returns (q uint8 [R,K], s float32 [R])."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
-    s = _scale_from_amax(amax)
-    q = encode_e4m3(x / s[:, None])
+    s = _scale_from_amax(amax, fmt)
+    q = FORMATS[fmt]["encode"](x / s[:, None])
     return q, s
 
 
-def mx_scale_code(amax: np.ndarray) -> np.ndarray:
-    """E8M0 code of the shared exponent for each block maximum (OCP MX v1.0 rule)."""
+def mx_scale_code(amax: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
+    """E8M0 code of the shared exponent for each block maximum (OCP MX v1.0 rule):
+    clamp(floor(log2 amax) - emax + 127, 0, 254), 127 for an all-zero block."""
     amax = np.asarray(amax, dtype=np.float32).astype(np.float64)
     _, ex = np.frexp(amax)                  # amax = f * 2^ex, f in [0.5, 1): floor(log2) = ex-1
-    e = (ex.astype(np.int64) - 1) - E4M3_EMAX
+    e = (ex.astype(np.int64) - 1) - FORMATS[fmt]["emax"]
     code = np.clip(e + 127, 0, 254)
     return np.where(amax == 0, 127, code).astype(np.uint8)
 
 
-def quantize_mx(x: np.ndarray):
+def quantize_mx(x: np.ndarray, fmt: str = "e4m3"):
     """32-element K blocks: returns (q uint8 [R,K], e8m0 codes uint8 [R, K/32])."""
     x = np.asarray(x, dtype=np.float32)
     R, K = x.shape
@@ -75,19 +82,19 @@ def quantize_mx(x: np.ndarray):
         raise ValueError("MX quantisation needs K to be a multiple of 32")
     blocks = x.reshape(R, K // MX_BLOCK, MX_BLOCK)
     amax = np.max(np.abs(blocks), axis=2) if K else np.zeros((R, 0), np.float32)
-    codes = mx_scale_code(amax)
+    codes = mx_scale_code(amax, fmt)
     e = codes.astype(np.int64) - 127
     scaled = np.ldexp(blocks.astype(np.float64), -e[:, :, None])   # exact power-of-two scaling
-    q = encode_e4m3(scaled).reshape(R, K)
+    q = FORMATS[fmt]["encode"](scaled).reshape(R, K)
     return q, codes
 
 
-def quantize(x: np.ndarray, mode: str):
-    """Dispatch on mode name: "tensor" | "rowwise" | "mx32"."""
+def quantize(x: np.ndarray, mode: str, fmt: str = "e4m3"):
+    """Dispatch on mode name: "tensor" | "rowwise" | "mx32"; fmt "e4m3" | "e5m2"."""
     if mode == "tensor":
-        return quantize_tensor(x)
+        return quantize_tensor(x, fmt)
     if mode == "rowwise":
-        return quantize_rowwise(x)
+        return quantize_rowwise(x, fmt)
     if mode == "mx32":
-        return quantize_mx(x)
+        return quantize_mx(x, fmt)
     raise ValueError(f"unknown scale mode {mode!r}")

@@ -31,11 +31,21 @@ def _rand_codes(rng, shape):
     return c
 
 
-def _exact_value(code):
-    return Fraction(O.E4M3_DECODE[int(code)])  # table values are exact dyadic rationals
+def _exact_value(code, fmt="e4m3"):
+    table = O.E4M3_DECODE if fmt == "e4m3" else O.E5M2_DECODE
+    return Fraction(table[int(code)])  # table values are exact dyadic rationals
 
 
-def _exact_gemm(qa, sa, qb, sb, mode):
+def _rand_codes_fmt(rng, shape, fmt):
+    if fmt == "e4m3":
+        return _rand_codes(rng, shape)
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    bad = (c & 0x7C) == 0x7C                 # e5m2 infinities and NaNs
+    c[bad] &= 0xF3
+    return c
+
+
+def _exact_gemm(qa, sa, qb, sb, mode, fmt_a="e4m3", fmt_b="e4m3"):
     M, K = qa.shape
     N = qb.shape[0]
     C = np.empty((M, N), dtype=object)
@@ -52,7 +62,7 @@ def _exact_gemm(qa, sa, qb, sb, mode):
                 else:
                     fa = Fraction(2) ** (int(sa[m, k // 32]) - 127)
                     fb = Fraction(2) ** (int(sb[n, k // 32]) - 127)
-                t = fa * _exact_value(qa[m, k]) * fb * _exact_value(qb[n, k])
+                t = fa * _exact_value(qa[m, k], fmt_a) * fb * _exact_value(qb[n, k], fmt_b)
                 acc += t
                 aab += abs(t)
             C[m, n] = acc
@@ -249,3 +259,116 @@ def test_tolerance_rejects_planted_errors():
     assert not np.all(O.within_bound(Cdrop, C, A, "bf16"))
     assert not np.all(O.within_bound(C.T, C, A, "bf16"))
     assert not np.all(O.within_bound(-C, C, A, "bf16"))
+
+
+
+@pytest.mark.parametrize("mode", ["tensor", "rowwise", "mx32"])
+@pytest.mark.parametrize("fmts", [("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")])
+def test_bruteforce_exact_rationals_e5m2(mode, fmts):
+    """e5m2 and mixed-format operands against exact rationals (4x4x64)."""
+    M, N, K = 4, 4, 64
+    fa_, fb_ = fmts
+    rng = np.random.default_rng([7, ["tensor", "rowwise", "mx32"].index(mode), len(fa_ + fb_),
+                                 fa_ == "e4m3"])
+    qa, qb = _rand_codes_fmt(rng, (M, K), fa_), _rand_codes_fmt(rng, (N, K), fb_)
+    if mode == "tensor":
+        sa, sb = np.float32(0.37), np.float32(1.9e-3)
+    elif mode == "rowwise":
+        sa = rng.uniform(0.01, 3, M).astype(np.float32)
+        sb = rng.uniform(0.01, 3, N).astype(np.float32)
+    else:
+        sa = rng.integers(100, 150, size=(M, K // 32)).astype(np.uint8)
+        sb = rng.integers(100, 150, size=(N, K // 32)).astype(np.uint8)
+    C, A = O.gemm_reference(qa, sa, qb, sb, mode, fmt_a=fa_, fmt_b=fb_)
+    Ce, Ae = _exact_gemm(qa, sa, qb, sb, mode, fa_, fb_)
+    for m in range(M):
+        for n in range(N):
+            # float64 sums of terms spanning ~75 binades: K roundings at most
+            assert abs(Fraction(C[m, n]) - Ce[m, n]) <= Fraction(2) ** -46 * Ae[m, n]
+            assert abs(Fraction(A[m, n]) - Ae[m, n]) <= Fraction(2) ** -46 * Ae[m, n]
+
+
+def test_e5m2_operand_swaps_formats_consistently():
+    """Transposition symmetry: C(A:e4m3, B:e5m2) = C(B:e5m2, A:e4m3)^T."""
+    rng = np.random.default_rng(31)
+    qa, qb = _rand_codes_fmt(rng, (6, 96), "e4m3"), _rand_codes_fmt(rng, (5, 96), "e5m2")
+    sa = rng.uniform(0.1, 2, 6).astype(np.float32)
+    sb = rng.uniform(0.1, 2, 5).astype(np.float32)
+    C1, A1 = O.gemm_reference(qa, sa, qb, sb, "rowwise", fmt_a="e4m3", fmt_b="e5m2")
+    C2, A2 = O.gemm_reference(qb, sb, qa, sa, "rowwise", fmt_a="e5m2", fmt_b="e4m3")
+    assert np.allclose(C1, C2.T, rtol=1e-14, atol=0) and np.allclose(A1, A2.T, rtol=1e-14)
+    # and the wrong format assignment gives a different answer (the pin can see it)
+    C3, _ = O.gemm_reference(qa, sa, qb, sb, "rowwise", fmt_a="e4m3", fmt_b="e4m3")
+    assert not np.allclose(C1, C3)
+
+
+# ---- fused epilogue -----------------------------------------------------------
+
+def test_activation_closed_forms():
+    y = np.array([-2.0, -1.0, 0.0, 1.0, 2.0])
+    assert np.array_equal(O.activation(y, "none"), y)
+    assert np.array_equal(O.activation(y, "relu"), [0, 0, 0, 1, 2])
+    # GELU(y) = y * Phi(y): Phi(1) = 0.8413447460685429, Phi(2) = 0.9772498680518208
+    g = O.activation(y, "gelu")
+    assert abs(g[3] - 0.8413447460685429) < 1e-15 and abs(g[4] - 2 * 0.9772498680518208) < 1e-15
+    assert abs(g[1] + 0.15865525393145707) < 1e-15 and g[2] == 0
+    # SiLU(1) = 1 / (1 + e^-1)
+    s = O.activation(y, "silu")
+    assert abs(s[3] - 1 / (1 + np.exp(-1.0))) < 1e-15 and s[2] == 0
+    # odd-part identities: act(y) - act(-y) = y for GELU and SiLU
+    x = np.linspace(-30, 30, 2001)
+    for act in ("gelu", "silu", "relu"):
+        assert np.allclose(O.activation(x, act) - O.activation(-x, act), x, rtol=0, atol=1e-12)
+    # large negative inputs go to (signed) zero, large positive ones to y
+    assert O.activation(np.array([-800.0]), "silu")[0] == 0.0
+    assert O.activation(np.array([-40.0]), "gelu")[0] == 0.0
+    assert O.activation(np.array([40.0]), "gelu")[0] == 40.0
+
+
+def test_activation_lipschitz_bounds():
+    x = np.linspace(-20, 20, 400001)
+    for act, L in O.ACT_LIPSCHITZ.items():
+        d = np.abs(np.diff(O.activation(x, act)) / np.diff(x))
+        assert d.max() <= L, (act, d.max())
+        if act in ("gelu", "silu"):
+            assert d.max() > L - 0.002, (act, d.max())       # and the bound is tight
+
+
+def test_epilogue_reference_bias_and_identity():
+    rng = np.random.default_rng(41)
+    qa, qb = _rand_codes(rng, (8, 64)), _rand_codes(rng, (12, 64))
+    sa = rng.uniform(0.1, 1, 8).astype(np.float32)
+    sb = rng.uniform(0.1, 1, 12).astype(np.float32)
+    C, A = O.gemm_reference(qa, sa, qb, sb, "rowwise")
+    out, y = O.epilogue_reference(C, A, None, "none")
+    assert np.array_equal(out, C) and np.array_equal(y, C)
+    bias = rng.standard_normal(12).astype(np.float32)
+    out, y = O.epilogue_reference(C, A, bias, "none")
+    assert np.array_equal(out, C + bias.astype(np.float64)[None, :])
+    out, y = O.epilogue_reference(C, A, bias, "relu")
+    assert np.array_equal(out, np.maximum(C + bias.astype(np.float64)[None, :], 0))
+    # a column selection picks the matching bias entries
+    cols = np.array([3, 7, 11])
+    Cs, As = O.gemm_reference(qa, sa, qb, sb, "rowwise", cols=cols)
+    outs, _ = O.epilogue_reference(Cs, As, bias, "gelu", cols=cols)
+    full, _ = O.epilogue_reference(C, A, bias, "gelu")
+    assert np.array_equal(outs, full[:, cols])
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu", "silu"])
+def test_epilogue_tolerance_rejects_planted_mistakes(act):
+    """The bound accepts the correctly rounded result and rejects a dropped bias,
+    a wrong activation and a bias applied to the wrong column."""
+    rng = np.random.default_rng(["relu", "gelu", "silu"].index(act) + 50)
+    qa, qb = _rand_codes(rng, (16, 128)), _rand_codes(rng, (24, 128))
+    sa, sb = np.float32(0.02), np.float32(0.03)
+    C, A = O.gemm_reference(qa, sa, qb, sb, "tensor")
+    bias = (rng.standard_normal(24) * np.abs(C).mean()).astype(np.float32)
+    out, y = O.epilogue_reference(C, A, bias, act)
+    tol = O.epilogue_tolerance(out, y, A, act, "bf16")
+    good = O.round_to_output(out, "bf16")
+    assert np.all(np.abs(good - out) <= tol)
+    for bad in (O.activation(C, act),                                   # bias dropped
+                O.activation(y, "none" if act != "relu" else "silu"),   # wrong activation
+                O.activation(C + bias[::-1].astype(np.float64), act)):   # bias columns reversed
+        assert np.any(np.abs(O.round_to_output(bad, "bf16") - out) > tol)

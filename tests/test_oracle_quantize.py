@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 from oracle import quant as Q
+from oracle import formats as F
 from oracle.formats import decode_e4m3
 from workloads import block_scaled_normal, normal, with_outliers
 
@@ -134,7 +135,7 @@ def test_mx_subnormal_and_extreme_exponents():
     q, c = Q.quantize_mx(x)
     assert c[0, 0] == 0 and c[0, 1] == 127 + 127 - 8 and c[0, 2] == 0
     # 1e-40 * 2^127 ~ 0.017 -> nearest e4m3 code
-    assert q[0, 0] == Q.encode_e4m3(np.ldexp(np.float64(np.float32(1e-40)), 127))
+    assert q[0, 0] == F.encode_e4m3(np.ldexp(np.float64(np.float32(1e-40)), 127))
 
 
 def test_quantize_rejects_bad_mx_k():
@@ -148,4 +149,69 @@ def test_division_is_binary32():
     x = normal(rng, 1, 4096)
     q, s = Q.quantize_tensor(x)
     fl32 = (x / s).astype(np.float32)
-    assert np.array_equal(q, Q.encode_e4m3(fl32))
+    assert np.array_equal(q, F.encode_e4m3(fl32))
+
+
+# ---- e5m2 elements ------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_e5m2_max_element_maps_to_57344(seed):
+    rng = np.random.default_rng(seed)
+    x = with_outliers(rng, 64, 96)
+    q, s = Q.quantize_tensor(x, "e5m2")
+    assert float(s) == float(np.float32(np.max(np.abs(x))) / np.float32(57344.0))
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert q[i] == (0xFB if x[i] < 0 else 0x7B)
+    qr, sr = Q.quantize_rowwise(x, "e5m2")
+    j = np.argmax(np.abs(x), axis=1)
+    for r in range(x.shape[0]):
+        assert qr[r, j[r]] == (0xFB if x[r, j[r]] < 0 else 0x7B)
+    assert np.all(np.abs(F.decode_e5m2(qr)) <= 57344)
+    assert np.all(np.isfinite(F.decode_e5m2(qr)))
+
+
+def test_e5m2_mx_block_max_range_and_code():
+    rng = np.random.default_rng(4)
+    x = block_scaled_normal(rng, 16, 256)
+    q, codes = Q.quantize_mx(x, "e5m2")
+    blocks = np.abs(x).reshape(16, 8, 32)
+    amax = blocks.max(axis=2)
+    # shared exponent e = floor(log2 amax) - 15: 2^(e+15) <= amax < 2^(e+16)
+    e = codes.astype(np.int64) - 127
+    assert np.all(np.ldexp(1.0, e + 15) <= amax) and np.all(amax < np.ldexp(1.0, e + 16))
+    arg = blocks.argmax(axis=2)
+    qmax = np.abs(F.decode_e5m2(q.reshape(16, 8, 32)))[np.arange(16)[:, None],
+                                                       np.arange(8)[None, :], arg]
+    assert np.all((qmax >= 32768) & (qmax <= 57344))
+    # the e5m2 code is the e4m3 code lowered by the difference of the largest exponents
+    _, c4 = Q.quantize_mx(x, "e4m3")
+    assert np.array_equal(codes.astype(int), c4.astype(int) - 7)
+
+
+@pytest.mark.parametrize("j", [-9, 2, 13])
+def test_e5m2_scale_linearity(j):
+    rng = np.random.default_rng(12)
+    x = block_scaled_normal(rng, 8, 128)
+    y = np.ldexp(x, j).astype(np.float32)
+    for mode in ("tensor", "rowwise"):
+        q1, s1 = Q.quantize(x, mode, "e5m2")
+        q2, s2 = Q.quantize(y, mode, "e5m2")
+        assert np.array_equal(q1, q2)
+        assert np.array_equal(np.asarray(s2), np.ldexp(np.asarray(s1), j).astype(np.float32))
+    q1, c1 = Q.quantize_mx(x, "e5m2")
+    q2, c2 = Q.quantize_mx(y, "e5m2")
+    assert np.array_equal(q1, q2) and np.array_equal(c2.astype(int), c1.astype(int) + j)
+
+
+def test_e5m2_encoding_is_coarser_rounding_of_the_same_value():
+    # e5m2 keeps 2 mantissa bits: its code for a value equals the e4m3 code's value
+    # rounded again only where no double-rounding tie occurs; check the simple
+    # consequence that both lie within half an e5m2 ulp of the scaled input
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((32, 64)).astype(np.float32)
+    q, s = Q.quantize_tensor(x, "e5m2")
+    v = x.astype(np.float64) / float(s)
+    got = F.decode_e5m2(q)
+    _, ex = np.frexp(np.maximum(np.abs(v), 2.0 ** -14))
+    half_ulp = np.ldexp(1.0, ex - 1 - 2 - 1)          # 2^(floor(log2|v|) - 2) / 2
+    assert np.all(np.abs(got - v) <= half_ulp * (1 + 1e-12))
