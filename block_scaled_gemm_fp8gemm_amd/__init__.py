@@ -23,9 +23,10 @@ import re
 
 __all__ = [
     "gemm_workspace",
-    "Fp8GemmError", "SCALE_MODES", "OUT_DTYPES", "library_path", "load_library",
-    "fp8gemm_quantize_workspace_size", "fp8gemm_quantize", "fp8gemm_workspace_size",
-    "fp8gemm_run", "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run",
+    "Fp8GemmError", "SCALE_MODES", "OUT_DTYPES", "FORMATS", "ACTIVATIONS", "library_path",
+    "load_library", "fp8gemm_quantize_workspace_size", "fp8gemm_quantize",
+    "fp8gemm_quantize_ex", "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex",
+    "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run",
     "fp8gemm_status_string", "fp8gemm_version", "quantize", "gemm", "grouped_gemm",
     "exported_symbols",
 ]
@@ -35,6 +36,8 @@ _HEADER = os.path.join(os.path.dirname(_PKG), "include", "fp8gemm.h")
 
 SCALE_MODES = {"tensor": 0, "rowwise": 1, "mx32": 2}
 OUT_DTYPES = {"f16": 0, "bf16": 1}
+FORMATS = {"e4m3": 0, "e5m2": 1}
+ACTIVATIONS = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
 
 _STATUS_NAMES = {
     0: "FP8GEMM_SUCCESS", 1: "FP8GEMM_ERROR_INVALID_VALUE", 2: "FP8GEMM_ERROR_MISALIGNED",
@@ -62,9 +65,12 @@ _i64, _i32, _sz, _p, _int = (ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ct
 _SIGNATURES = {
     "fp8gemm_quantize_workspace_size": (_sz, [_i64, _i64, _int]),
     "fp8gemm_quantize": (_int, [_p, _i64, _i64, _i64, _int, _p, _i64, _p, _p, _sz, _p]),
+    "fp8gemm_quantize_ex": (_int, [_p, _i64, _i64, _i64, _int, _int, _p, _i64, _p, _p, _sz, _p]),
     "fp8gemm_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "fp8gemm_run": (_int, [_i64, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _p, _p, _i64, _int,
                            _p, _sz, _p]),
+    "fp8gemm_run_ex": (_int, [_i64, _i64, _i64, _p, _i64, _int, _p, _i64, _int, _int, _p, _p, _p,
+                              _int, _p, _i64, _int, _p, _sz, _p]),
     "fp8gemm_grouped_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _int]),
     "fp8gemm_grouped_run": (_int, [_i32, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _i64, _int,
                                    _p, _p, _p, _i64, _int, _p, _sz, _p]),
@@ -117,6 +123,13 @@ def fp8gemm_quantize(x: int, rows: int, k: int, ldx: int, mode: int, q: int, ldq
         x, rows, k, ldx, mode, q, ldq, scales, workspace, workspace_bytes, stream))
 
 
+def fp8gemm_quantize_ex(x: int, rows: int, k: int, ldx: int, mode: int, fmt: int, q: int,
+                        ldq: int, scales: int, workspace: int, workspace_bytes: int,
+                        stream: int) -> None:
+    _check("fp8gemm_quantize_ex", load_library().fp8gemm_quantize_ex(
+        x, rows, k, ldx, mode, fmt, q, ldq, scales, workspace, workspace_bytes, stream))
+
+
 def fp8gemm_workspace_size(M: int, N: int, K: int, mode: int) -> int:
     return load_library().fp8gemm_workspace_size(M, N, K, mode)
 
@@ -127,6 +140,15 @@ def fp8gemm_run(M: int, N: int, K: int, A: int, lda: int, B: int, ldb: int, mode
     _check("fp8gemm_run", load_library().fp8gemm_run(
         M, N, K, A, lda, B, ldb, mode, scale_a, scale_b, C, ldc, out_dtype, workspace,
         workspace_bytes, stream))
+
+
+def fp8gemm_run_ex(M: int, N: int, K: int, A: int, lda: int, a_format: int, B: int, ldb: int,
+                   b_format: int, mode: int, scale_a: int, scale_b: int, bias: int,
+                   activation: int, C: int, ldc: int, out_dtype: int, workspace: int,
+                   workspace_bytes: int, stream: int) -> None:
+    _check("fp8gemm_run_ex", load_library().fp8gemm_run_ex(
+        M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias, activation, C,
+        ldc, out_dtype, workspace, workspace_bytes, stream))
 
 
 def fp8gemm_grouped_workspace_size(num_groups: int, total_m: int, N: int, K: int,
@@ -196,10 +218,12 @@ def _ptr(t) -> int:
     return t.data_ptr() if t is not None else 0
 
 
-def quantize(x, mode: str = "tensor", out=None, scales=None, workspace=None):
+def quantize(x, mode: str = "tensor", out=None, scales=None, workspace=None,
+             fmt: str = "e4m3"):
     """fp32 [R, K] CUDA tensor -> (codes uint8 [R, K], scales).
 
-    scales: float32 [1] (tensor), float32 [R] (rowwise) or uint8 [R, K/32] (mx32).
+    scales: float32 [1] (tensor), float32 [R] (rowwise) or uint8 [R, K/32] (mx32);
+    fmt: element format of the codes, "e4m3" or "e5m2".
     """
     torch = _torch()
     _require_cuda(x, "x", torch.float32, 2)
@@ -218,15 +242,20 @@ def quantize(x, mode: str = "tensor", out=None, scales=None, workspace=None):
     need = fp8gemm_quantize_workspace_size(R, K, m)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    fp8gemm_quantize(_ptr(x), R, K, x.stride(0), m, _ptr(out), out.stride(0), _ptr(scales),
-                     _ptr(workspace) if need else 0, workspace.numel() if need else 0,
-                     _stream_handle(x.device))
+    fp8gemm_quantize_ex(_ptr(x), R, K, x.stride(0), m, FORMATS[fmt], _ptr(out), out.stride(0),
+                        _ptr(scales), _ptr(workspace) if need else 0,
+                        workspace.numel() if need else 0, _stream_handle(x.device))
     return out, scales
 
 
 def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None,
-         workspace=None):
-    """C [M, N] = dq(qa [M, K]) @ dq(qb [N, K])^T, returned as fp16 / bf16."""
+         workspace=None, fmt_a: str = "e4m3", fmt_b: str = "e4m3", bias=None,
+         activation: str = "none"):
+    """C [M, N] = act(dq(qa [M, K]) @ dq(qb [N, K])^T + bias), returned as fp16 / bf16.
+
+    fmt_a / fmt_b: element formats of the codes ("e4m3" or "e5m2"); bias: float32
+    [N] CUDA tensor or None; activation: "none", "relu", "gelu" or "silu".
+    """
     torch = _torch()
     _require_cuda(qa, "qa", torch.uint8, 2)
     _require_cuda(qb, "qb", torch.uint8, 2)
@@ -242,10 +271,15 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
     need = fp8gemm_workspace_size(M, N, K, m)
     if need and workspace is None:
         workspace = gemm_workspace(qa.device, need)
-    fp8gemm_run(M, N, K, _ptr(qa), qa.stride(0), _ptr(qb), qb.stride(0), m, _ptr(sa), _ptr(sb),
-                _ptr(out), out.stride(0), OUT_DTYPES[out_dtype],
-                _ptr(workspace) if need else 0, workspace.numel() if need else 0,
-                _stream_handle(qa.device))
+    if bias is not None:
+        _require_cuda(bias, "bias", torch.float32, 1)
+        if bias.numel() != N:
+            raise ValueError("bias must have N elements")
+    fp8gemm_run_ex(M, N, K, _ptr(qa), qa.stride(0), FORMATS[fmt_a], _ptr(qb), qb.stride(0),
+                   FORMATS[fmt_b], m, _ptr(sa), _ptr(sb), _ptr(bias), ACTIVATIONS[activation],
+                   _ptr(out), out.stride(0), OUT_DTYPES[out_dtype],
+                   _ptr(workspace) if need else 0, workspace.numel() if need else 0,
+                   _stream_handle(qa.device))
     return out
 
 

@@ -19,6 +19,10 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8gemm.so")
 
 SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "grouped.hip"]
+# gemm.hip is compiled once more per pair of operand formats other than e4m3 x e4m3
+FORMAT_UNITS = [("gemm.hip", ("FP8GEMM_FMT_A=1", "FP8GEMM_FMT_B=1"), ".e5m2_e5m2"),
+                ("gemm.hip", ("FP8GEMM_FMT_A=0", "FP8GEMM_FMT_B=1"), ".e4m3_e5m2"),
+                ("gemm.hip", ("FP8GEMM_FMT_A=1", "FP8GEMM_FMT_B=0"), ".e5m2_e4m3")]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -56,8 +60,10 @@ def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
     tag = "" if not defines else "." + "_".join(d.replace("=", "") for d in defines)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(hipcc, s, defines, tag), SOURCES))
+    units = [(s, tuple(defines), tag) for s in SOURCES]
+    units += [(s, tuple(defines) + d, tag + t) for s, d, t in FORMAT_UNITS]
+    with cf.ThreadPoolExecutor(max_workers=min(len(units), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda u: _compile(hipcc, *u), units))
     tmp = out + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

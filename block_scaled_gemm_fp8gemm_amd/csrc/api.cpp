@@ -26,6 +26,11 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool valid_mode(int mode) { return mode == kTensor || mode == kRowwise || mode == kMx32; }
 bool valid_out(int out) { return out == FP8GEMM_OUT_F16 || out == FP8GEMM_OUT_BF16; }
+bool valid_format(int f) { return f == FP8GEMM_FORMAT_E4M3 || f == FP8GEMM_FORMAT_E5M2; }
+bool valid_act(int a) {
+  return a == FP8GEMM_ACT_NONE || a == FP8GEMM_ACT_RELU || a == FP8GEMM_ACT_GELU ||
+         a == FP8GEMM_ACT_SILU;
+}
 
 fp8gemm_status from_hip(hipError_t e) {
   return e == hipSuccess ? FP8GEMM_SUCCESS : FP8GEMM_ERROR_LAUNCH;
@@ -64,7 +69,15 @@ size_t fp8gemm_quantize_workspace_size(int64_t rows, int64_t k, int mode) {
 fp8gemm_status fp8gemm_quantize(const float* x, int64_t rows, int64_t k, int64_t ldx, int mode,
                                 uint8_t* q, int64_t ldq, void* scales, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  if (!valid_mode(mode) || rows < 0 || k <= 0) return FP8GEMM_ERROR_INVALID_VALUE;
+  return fp8gemm_quantize_ex(x, rows, k, ldx, mode, FP8GEMM_FORMAT_E4M3, q, ldq, scales, workspace,
+                             workspace_bytes, stream);
+}
+
+fp8gemm_status fp8gemm_quantize_ex(const float* x, int64_t rows, int64_t k, int64_t ldx, int mode,
+                                   int format, uint8_t* q, int64_t ldq, void* scales,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_mode(mode) || !valid_format(format) || rows < 0 || k <= 0)
+    return FP8GEMM_ERROR_INVALID_VALUE;
   if (rows == 0) return FP8GEMM_SUCCESS;
   if (!x || !q || !scales) return FP8GEMM_ERROR_INVALID_VALUE;
   if (ldx < k || ldq < k) return FP8GEMM_ERROR_INVALID_VALUE;
@@ -84,12 +97,12 @@ fp8gemm_status fp8gemm_quantize(const float* x, int64_t rows, int64_t k, int64_t
   if (mode == kTensor)
     return from_hip(fp8gemm::launch_quantize_tensor(x, rows, k, ldx, q, ldq,
                                                     static_cast<float*>(scales),
-                                                    static_cast<float*>(workspace), s));
+                                                    static_cast<float*>(workspace), format, s));
   if (mode == kRowwise)
     return from_hip(fp8gemm::launch_quantize_rowwise(x, rows, k, ldx, q, ldq,
-                                                     static_cast<float*>(scales), s));
-  return from_hip(
-      fp8gemm::launch_quantize_mx(x, rows, k, ldx, q, ldq, static_cast<uint8_t*>(scales), s));
+                                                     static_cast<float*>(scales), format, s));
+  return from_hip(fp8gemm::launch_quantize_mx(x, rows, k, ldx, q, ldq,
+                                              static_cast<uint8_t*>(scales), format, s));
 }
 
 size_t fp8gemm_workspace_size(int64_t M, int64_t N, int64_t K, int mode) {
@@ -101,7 +114,18 @@ fp8gemm_status fp8gemm_run(int64_t M, int64_t N, int64_t K, const uint8_t* A, in
                            const uint8_t* B, int64_t ldb, int mode, const void* scale_a,
                            const void* scale_b, void* C, int64_t ldc, int out_dtype,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  if (!valid_mode(mode) || !valid_out(out_dtype) || M < 0 || N < 0 || K <= 0)
+  return fp8gemm_run_ex(M, N, K, A, lda, FP8GEMM_FORMAT_E4M3, B, ldb, FP8GEMM_FORMAT_E4M3, mode,
+                        scale_a, scale_b, nullptr, FP8GEMM_ACT_NONE, C, ldc, out_dtype, workspace,
+                        workspace_bytes, stream);
+}
+
+fp8gemm_status fp8gemm_run_ex(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                              int a_format, const uint8_t* B, int64_t ldb, int b_format, int mode,
+                              const void* scale_a, const void* scale_b, const float* bias,
+                              int activation, void* C, int64_t ldc, int out_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_mode(mode) || !valid_out(out_dtype) || !valid_format(a_format) ||
+      !valid_format(b_format) || !valid_act(activation) || M < 0 || N < 0 || K <= 0)
     return FP8GEMM_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return FP8GEMM_SUCCESS;
   fp8gemm_status st =
@@ -123,8 +147,18 @@ fp8gemm_status fp8gemm_run(int64_t M, int64_t N, int64_t K, const uint8_t* A, in
   p.scale_b = scale_b;
   p.C = C;
   p.ldc = ldc;
+  if (bias && !aligned(bias, 4)) return FP8GEMM_ERROR_MISALIGNED;
   p.workspace = need > 0 ? workspace : nullptr;
-  return from_hip(fp8gemm::launch_gemm(p, mode, out_dtype, static_cast<hipStream_t>(stream)));
+  p.bias = bias;
+  p.act = activation;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a_format == FP8GEMM_FORMAT_E5M2 && b_format == FP8GEMM_FORMAT_E5M2)
+    return from_hip(fp8gemm::launch_gemm_e5m2_e5m2(p, mode, out_dtype, s));
+  if (a_format == FP8GEMM_FORMAT_E5M2)
+    return from_hip(fp8gemm::launch_gemm_e5m2_e4m3(p, mode, out_dtype, s));
+  if (b_format == FP8GEMM_FORMAT_E5M2)
+    return from_hip(fp8gemm::launch_gemm_e4m3_e5m2(p, mode, out_dtype, s));
+  return from_hip(fp8gemm::launch_gemm(p, mode, out_dtype, s));
 }
 
 size_t fp8gemm_grouped_workspace_size(int32_t num_groups, int64_t total_m, int64_t N, int64_t K,

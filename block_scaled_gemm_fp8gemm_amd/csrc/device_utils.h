@@ -7,15 +7,23 @@
 //   * gfx950's v_cvt_pk_fp8_f32 rounds to nearest even onto OCP e4m3fn, including
 //     subnormals and ties, but turns magnitudes above 464 into NaN, so every value
 //     is clamped to [-448, 448] first (448 is what round-then-saturate gives).
+//   * e5m2 (the post's second FP8 format; OCP OFP8 E5M2) has infinities; its
+//     largest finite magnitude is 57344.  v_cvt_pk_bf8_f32 converts onto it, and
+//     values are clamped to [-57344, 57344] first, so the quantisers saturate
+//     instead of producing infinity.
 //   * E8M0 code c encodes 2^(c-127).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace fp8gemm {
 
 constexpr float kE4M3Max = 448.0f;
+constexpr float kE5M2Max = 57344.0f;
+
 
 __device__ __forceinline__ float clamp448(float v) {
   return fminf(fmaxf(v, -kE4M3Max), kE4M3Max);
@@ -29,13 +37,34 @@ __device__ __forceinline__ uint32_t encode4_e4m3(float a, float b, float c, floa
   return (uint32_t)w;
 }
 
+// Four fp32 values -> four e5m2 codes packed little-endian into 32 bits (round to
+// nearest even, saturating at 57344, sign of zero kept).
+__device__ __forceinline__ uint32_t encode4_e5m2(float a, float b, float c, float d) {
+  auto clamp = [](float v) { return fminf(fmaxf(v, -kE5M2Max), kE5M2Max); };
+  int w = __builtin_amdgcn_cvt_pk_bf8_f32(clamp(a), clamp(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_bf8_f32(clamp(c), clamp(d), w, true);
+  return (uint32_t)w;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
+  return FMT == kE5M2 ? encode4_e5m2(a, b, c, d) : encode4_e4m3(a, b, c, d);
+}
+
+template <int FMT>
+constexpr float elem_max() {
+  return FMT == kE5M2 ? kE5M2Max : kE4M3Max;
+}
+
 // E8M0 code of a 32-element block from its largest magnitude: floor(log2 amax)
-// read from the binary32 exponent field, minus 8 (the largest e4m3 exponent),
-// biased by 127 and clamped to [0, 254]; an all-zero block gets 127.
+// read from the binary32 exponent field, minus the element format's largest
+// exponent (8 for e4m3, 15 for e5m2), biased by 127 and clamped to [0, 254]; an
+// all-zero block gets 127.
+template <int FMT = kE4M3>
 __device__ __forceinline__ uint32_t mx_code_from_amax(float amax) {
   if (amax == 0.0f) return 127u;
   int ef = (int)(__float_as_uint(amax) >> 23);  // amax >= 0: no sign bit
-  int code = ef - 8;
+  int code = ef - (FMT == kE5M2 ? 15 : 8);
   return (uint32_t)(code < 0 ? 0 : code);
 }
 

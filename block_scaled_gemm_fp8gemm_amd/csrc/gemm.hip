@@ -17,7 +17,7 @@
 namespace fp8gemm {
 namespace {
 
-template <class Cfg, int MODE, typename OutT, bool KALIGNED>
+template <class Cfg, int MODE, typename OutT, bool KALIGNED, bool FUSED>
 __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void gemm_kernel(GemmProblem p,
                                                                               int tiles_m,
                                                               int tiles_n) {
@@ -49,8 +49,8 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void gemm_kernel(G
   }
 
   const float ts = (MODE == kTensor) ? fsa[0] * fsb[0] : 1.0f;
-  gemm_tile<Cfg, MODE, OutT, KALIGNED>(op, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N,
-                                       ts);
+  gemm_tile<Cfg, MODE, OutT, KALIGNED, FUSED>(op, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M,
+                                              n0, p.N, ts, p.bias, p.act);
 }
 
 // Operands of the tiles of one persistent workgroup: tile i of the list is the
@@ -96,7 +96,7 @@ struct DenseTiles {
 // Persistent form for shapes whose tiles are all interior: one workgroup per CU
 // walks its tiles as one copy stream (the next tile's first K tiles are fetched
 // while the current one finishes, its epilogue runs while they land).
-template <class Cfg, int MODE, typename OutT>
+template <class Cfg, int MODE, typename OutT, bool FUSED>
 __global__ __launch_bounds__(Cfg::kThreads, 1) void gemm_persistent_kernel(GemmProblem p,
                                                                            int tiles_m,
                                                                            int tiles_n) {
@@ -113,24 +113,24 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void gemm_persistent_kernel(GemmP
                  __attribute__((always_inline)) {
     int m0, n0;
     src.coords(i, m0, n0);
-    epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, p.ldc, m0, n0, ts, rbuf);
+    epilogue_direct<Cfg, MODE, OutT, FUSED>(acc, lds, C, p.ldc, m0, n0, ts, rbuf, p.bias, p.act);
   };
   // epilogue_direct issues two 16-byte stores per 32 x 32 block and lane
   if (count > 0)
     stream_interior<Cfg, MODE, 2 * Cfg::kFragM * Cfg::kFragN>(src, 0, count, lds, epi);
 }
 
-template <class Cfg, int MODE, typename OutT>
+template <class Cfg, int MODE, typename OutT, bool FUSED>
 hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   const int tiles_m = (p.M + Cfg::BM - 1) / Cfg::BM;
   const int tiles_n = (p.N + Cfg::BN - 1) / Cfg::BN;
   const int grid = tiles_m * tiles_n;
   if (p.K % 128 == 0)
-    hipLaunchKernelGGL((gemm_kernel<Cfg, MODE, OutT, true>), dim3(grid), dim3(Cfg::kThreads), 0,
-                       stream, p, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_kernel<Cfg, MODE, OutT, true, FUSED>), dim3(grid),
+                       dim3(Cfg::kThreads), 0, stream, p, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL((gemm_kernel<Cfg, MODE, OutT, false>), dim3(grid), dim3(Cfg::kThreads), 0,
-                       stream, p, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_kernel<Cfg, MODE, OutT, false, FUSED>), dim3(grid),
+                       dim3(Cfg::kThreads), 0, stream, p, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -169,18 +169,18 @@ bool all_interior(const GemmProblem& p) {
          (int64_t)Cfg::BN * p.ldb + p.K < ((int64_t)1 << 31);
 }
 
-template <class Cfg, int MODE, typename OutT>
+template <class Cfg, int MODE, typename OutT, bool FUSED>
 hipError_t launch_persistent(const GemmProblem& p, hipStream_t stream) {
   const int tiles_m = p.M / Cfg::BM, tiles_n = p.N / Cfg::BN;
   const int total = tiles_m * tiles_n;
   const int cus = device_cus();
   const int grid = total < cus ? total : cus;
-  hipLaunchKernelGGL((gemm_persistent_kernel<Cfg, MODE, OutT>), dim3(grid), dim3(Cfg::kThreads), 0,
-                     stream, p, tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_persistent_kernel<Cfg, MODE, OutT, FUSED>), dim3(grid),
+                     dim3(Cfg::kThreads), 0, stream, p, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-template <int MODE, typename OutT>
+template <int MODE, typename OutT, bool FUSED>
 hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
   // Large tiles when they still give at least one tile per CU; otherwise smaller
   // tiles for more parallelism.
@@ -191,10 +191,10 @@ hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
     // persistent streams pay off from about eight tiles per CU on (measured)
     const bool many = big_tiles >= 8 * 256;
     if ((FP8GEMM_PERSISTENT || many) && all_interior<Big>(p))
-      return launch_persistent<Big, MODE, OutT>(p, stream);
-    return launch_cfg<Big, MODE, OutT>(p, stream);
+      return launch_persistent<Big, MODE, OutT, FUSED>(p, stream);
+    return launch_cfg<Big, MODE, OutT, FUSED>(p, stream);
   }
-  return launch_cfg<Mid, MODE, OutT>(p, stream);
+  return launch_cfg<Mid, MODE, OutT, FUSED>(p, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -245,7 +245,7 @@ __host__ __device__ constexpr int64_t counter_bytes(int64_t tiles) {
   return (tiles * 4 + 255) / 256 * 256;
 }
 
-template <class Cfg, int MODE, typename OutT>
+template <class Cfg, int MODE, typename OutT, bool FUSED>
 __global__ __launch_bounds__(Cfg::kThreads, 1) void splitk_kernel(GemmProblem p, int tiles_m,
                                                                     int splits) {
   // the arrival flag lives in the same LDS object as the ring: a second LDS
@@ -364,34 +364,54 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void splitk_kernel(GemmProblem p,
     }
   }
   const float ts = (MODE == kTensor) ? fsa[0] * fsb[0] : 1.0f;
-  epilogue<Cfg, MODE, OutT>(sum, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N, ts);
+  epilogue<Cfg, MODE, OutT, FUSED>(sum, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N,
+                                   ts, p.bias, p.act);
 }
 
-template <int MODE, typename OutT>
+template <int MODE, typename OutT, bool FUSED>
 hipError_t launch_split(const GemmProblem& p, const SplitPlan& plan, hipStream_t stream) {
   const int grid = plan.tiles_m * plan.tiles_n * plan.splits;
-  hipLaunchKernelGGL((splitk_kernel<SplitCfg, MODE, OutT>), dim3(grid), dim3(SplitCfg::kThreads), 0,
-                     stream, p, plan.tiles_m, plan.splits);
+  hipLaunchKernelGGL((splitk_kernel<SplitCfg, MODE, OutT, FUSED>), dim3(grid),
+                     dim3(SplitCfg::kThreads), 0, stream, p, plan.tiles_m, plan.splits);
   return hipGetLastError();
 }
 
+template <int MODE, typename OutT, bool FUSED>
+hipError_t launch_plan(const GemmProblem& p, hipStream_t stream) {
+  const SplitPlan plan = plan_split(p.M, p.N, p.K, MODE);
+  if (plan.splits > 1) return launch_split<MODE, OutT, FUSED>(p, plan, stream);
+  return launch_mode<MODE, OutT, FUSED>(p, stream);
+}
+
+// kernels with the fused bias / activation epilogue only when it is asked for
 template <int MODE, typename OutT>
 hipError_t launch_any(const GemmProblem& p, hipStream_t stream) {
-  const SplitPlan plan = plan_split(p.M, p.N, p.K, MODE);
-  if (plan.splits > 1) return launch_split<MODE, OutT>(p, plan, stream);
-  return launch_mode<MODE, OutT>(p, stream);
+  if (p.bias != nullptr || p.act != kActNone) return launch_plan<MODE, OutT, true>(p, stream);
+  return launch_plan<MODE, OutT, false>(p, stream);
 }
 
 }  // namespace
 
+// This file is compiled once per pair of operand formats (FP8GEMM_FMT_A/B); the
+// e4m3 x e4m3 build also defines the workspace query (the plan does not depend
+// on the formats).
+#if FP8GEMM_FMT_A == 0 && FP8GEMM_FMT_B == 0
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int mode) {
   const SplitPlan plan = plan_split(M, N, K, mode);
   if (plan.splits <= 1) return 0;
   const int64_t tiles = (int64_t)plan.tiles_m * plan.tiles_n;
   return (size_t)(counter_bytes(tiles) + tiles * plan.splits * kPartialFloats * 4);
 }
+#define FP8GEMM_LAUNCH_NAME launch_gemm
+#elif FP8GEMM_FMT_A == 1 && FP8GEMM_FMT_B == 1
+#define FP8GEMM_LAUNCH_NAME launch_gemm_e5m2_e5m2
+#elif FP8GEMM_FMT_A == 0 && FP8GEMM_FMT_B == 1
+#define FP8GEMM_LAUNCH_NAME launch_gemm_e4m3_e5m2
+#elif FP8GEMM_FMT_A == 1 && FP8GEMM_FMT_B == 0
+#define FP8GEMM_LAUNCH_NAME launch_gemm_e5m2_e4m3
+#endif
 
-hipError_t launch_gemm(const GemmProblem& p, int mode, int out, hipStream_t stream) {
+hipError_t FP8GEMM_LAUNCH_NAME(const GemmProblem& p, int mode, int out, hipStream_t stream) {
   if (out == kF16) {
     if (mode == kTensor) return launch_any<kTensor, _Float16>(p, stream);
     if (mode == kRowwise) return launch_any<kRowwise, _Float16>(p, stream);

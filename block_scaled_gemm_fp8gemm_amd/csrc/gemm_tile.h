@@ -49,6 +49,18 @@
 #include "device_utils.h"
 #include "launch.h"
 
+// Element formats of the A and B codes, fixed per translation unit: the library
+// compiles the GEMM once per format pair, and the inline namespace keeps the
+// instances of these header templates apart.
+#ifndef FP8GEMM_FMT_A
+#define FP8GEMM_FMT_A 0
+#endif
+#ifndef FP8GEMM_FMT_B
+#define FP8GEMM_FMT_B 0
+#endif
+#define FP8GEMM_FMT_NS_(a, b) fmt_##a##b
+#define FP8GEMM_FMT_NS(a, b) FP8GEMM_FMT_NS_(a, b)
+
 #ifndef FP8GEMM_DIRECT_EPILOGUE
 #define FP8GEMM_DIRECT_EPILOGUE 1
 #endif
@@ -57,6 +69,10 @@
 #endif
 
 namespace fp8gemm {
+inline namespace FP8GEMM_FMT_NS(FP8GEMM_FMT_A, FP8GEMM_FMT_B) {
+
+// operand-format fields of the F8F6F4 MFMA (B is its first operand)
+constexpr int kFmtA = FP8GEMM_FMT_A, kFmtB = FP8GEMM_FMT_B;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -292,10 +308,10 @@ __device__ __forceinline__ void mfma_subtile(v16f (&acc)[Cfg::kFragM][Cfg::kFrag
     for (int j = 0; j < Cfg::kFragN; ++j) {
       if (MODE == kMx32) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            bf[j], af[i], acc[i][j], 0, 0, 0, (int)sb[j], 0, (int)sa[i]);
+            bf[j], af[i], acc[i][j], kFmtB, kFmtA, 0, (int)sb[j], 0, (int)sa[i]);
       } else {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], 0,
-                                                                    0, 0, 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], kFmtB,
+                                                                    kFmtA, 0, 0, 0, 0);
       }
     }
 }
@@ -458,11 +474,11 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
       if (MODE == kMx32) {
         const uint32_t sa = (kMxLds && odd) ? sa_cur[i] >> 16 : sa_cur[i];
         const uint32_t sb = (kMxLds && odd) ? sb_cur[j] >> 16 : sb_cur[j];
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0,
-                                                                    0, (int)sb, 0, (int)sa);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fb[j], fa[i], acc[i][j], kFmtB, kFmtA, 0, (int)sb, 0, (int)sa);
       } else {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0,
-                                                                    0, 0, 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], kFmtB,
+                                                                    kFmtA, 0, 0, 0, 0);
       }
 #pragma unroll
       for (int v = q * kVmem / kMfma; v < (q + 1) * kVmem / kMfma; ++v) {
@@ -786,10 +802,10 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
       const int i = m / FN, j = m % FN;
       if (kMx) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fb[j], fa[i], acc[i][j], 0, 0, 0, (int)cb[Z][j], 0, (int)ca[Z][i]);
+            fb[j], fa[i], acc[i][j], kFmtB, kFmtA, 0, (int)cb[Z][j], 0, (int)ca[Z][i]);
       } else {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0,
-                                                                    0, 0, 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], kFmtB,
+                                                                    kFmtA, 0, 0, 0, 0);
       }
       if (m < kCopySpan) {
 #pragma unroll
@@ -1122,10 +1138,10 @@ __device__ __forceinline__ void stream_interior(const Src& src, int first, int l
       const int i = m / FN, j = m % FN;
       if (kMx) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fb[j], fa[i], acc[i][j], 0, 0, 0, (int)cb[Z][j], 0, (int)ca[Z][i]);
+            fb[j], fa[i], acc[i][j], kFmtB, kFmtA, 0, (int)cb[Z][j], 0, (int)ca[Z][i]);
       } else {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0,
-                                                                    0, 0, 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], kFmtB,
+                                                                    kFmtA, 0, 0, 0, 0);
       }
       if (m < kCopySpan) {
 #pragma unroll
@@ -1219,10 +1235,40 @@ __device__ __forceinline__ void stream_interior(const Src& src, int first, int l
 // Output row m lives at C + m * ldc (ldc * sizeof(OutT) a multiple of 16 and C
 // 16-byte aligned).  The LDS ring must be idle (mainloop() ends with a barrier);
 // row-wise scales are read from the LDS copy mainloop() made.
-template <class Cfg, int MODE, typename OutT>
+// Fused epilogue operations after the scales: bias[n] added, then an activation
+// (the Cutlass-named Triton FP8 post fuses a bias_add_relu epilogue to save the
+// round trip of C; GELU, erf form, and SiLU are the other common choices).
+__device__ __forceinline__ float activate(float v, int act) {
+  if (act == kActRelu) return fmaxf(v, 0.0f);
+  if (act == kActGelu) return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+  if (act == kActSilu) return v / (1.0f + expf(-v));
+  return v;
+}
+
+// bias (may be null) and act are uniform over the launch; n is the output column
+// of v[0] and v[e] belongs to column n + e (columns at or past N are never
+// stored, their bias reads stay inside the array).  Kernels are instantiated
+// with and without these operations (FUSED): the activations' math inlined
+// into every output group makes the epilogue many times larger, and the plain
+// GEMM measured 10-20 % slower when it merely carried that code.
+template <bool FUSED>
+__device__ __forceinline__ void fused_ops(float (&v)[4], const float* bias, int act, int n, int N) {
+  if constexpr (!FUSED) return;
+  if (bias != nullptr) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += bias[n + e < N ? n + e : N - 1];
+  }
+  if (act != kActNone) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = activate(v[e], act);
+  }
+}
+
+template <class Cfg, int MODE, typename OutT, bool FUSED = false>
 __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN], uint8_t* lds,
                                          OutT* C, int64_t ldc, int m0, int m_end, int n0, int N,
-                                         float tensor_scale) {
+                                         float tensor_scale, const float* bias = nullptr,
+                                         int act = kActNone) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   constexpr int kChunksPerRow = Cfg::WN * 2 / 16;        // 16-byte chunks of a staged row
   constexpr int kRowsPerInst = 64 / kChunksPerRow;
@@ -1253,6 +1299,7 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFr
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] *= fb[e];
         }
+        fused_ops<FUSED>(v, bias, act, n0 + wn * Cfg::WN + c, N);
         *reinterpret_cast<uint2*>(stage + r * Cfg::kStagePitch + c * 2) =
             pack4<OutT>(v[0], v[1], v[2], v[3]);
       }
@@ -1289,10 +1336,11 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFr
 // with group 2k of the high half, after which every lane owns eight consecutive
 // columns (16 bytes) of its row: C is written with 16-byte stores and no LDS
 // staging, so the epilogue costs a few hundred instructions and no waits.
-template <class Cfg, int MODE, typename OutT>
+template <class Cfg, int MODE, typename OutT, bool FUSED = false>
 __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                 const uint8_t* lds, OutT* C, int64_t ldc, int m0,
-                                                int n0, float tensor_scale, int rbuf = 0) {
+                                                int n0, float tensor_scale, int rbuf = 0,
+                                                const float* bias = nullptr, int act = kActNone) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   static_assert(sizeof(OutT) == 2, "16-bit outputs");
   const int lane = threadIdx.x & 63;
@@ -1325,6 +1373,7 @@ __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][C
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] *= fb[e];
           }
+          fused_ops<FUSED>(v, bias, act, n0 + wn * Cfg::WN + c, n0 + Cfg::BN);
           w[q] = pack4<OutT>(v[0], v[1], v[2], v[3]);
         }
         // low half keeps group 2k and takes the high half's; high half keeps 2k + 1
@@ -1340,25 +1389,29 @@ __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][C
 // One output tile: the interior mainloop when the tile qualifies, else the
 // general (clamped) one, then the epilogue.  Each branch has its own accumulators
 // and epilogue so no accumulator copies join the two paths.
-template <class Cfg, int MODE, typename OutT, bool KALIGNED>
+template <class Cfg, int MODE, typename OutT, bool KALIGNED, bool FUSED = false>
 __device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, OutT* C,
                                           int64_t ldc, int m0, int m_end, int n0, int N,
-                                          float tensor_scale) {
+                                          float tensor_scale, const float* bias = nullptr,
+                                          int act = kActNone) {
   if constexpr (KALIGNED && Cfg::kSlots == 4) {
     if (interior_tile<Cfg, MODE>(op)) {
       v16f acc[Cfg::kFragM][Cfg::kFragN];
       mainloop_interior<Cfg, MODE>(op, lds, acc);
 #if FP8GEMM_DIRECT_EPILOGUE
-      epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, n0, tensor_scale);
+      epilogue_direct<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, n0, tensor_scale, 0, bias,
+                                              act);
 #else
-      epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
+      epilogue<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias,
+                                       act);
 #endif
       return;
     }
   }
   v16f acc[Cfg::kFragM][Cfg::kFragN];
   mainloop<Cfg, MODE, KALIGNED>(op, lds, acc);
-  epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
+  epilogue<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act);
 }
 
+}  // inline namespace
 }  // namespace fp8gemm

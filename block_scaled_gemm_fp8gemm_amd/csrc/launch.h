@@ -10,15 +10,23 @@ namespace fp8gemm {
 // Per-tensor quantisation keeps one partial maximum per workgroup of its first pass.
 constexpr int kQuantPartials = 1024;
 
+// fmt: element format of the codes (kE4M3 or kE5M2, device_utils.h).
 hipError_t launch_quantize_tensor(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
-                                  int64_t ldq, float* scale, float* partials, hipStream_t stream);
+                                  int64_t ldq, float* scale, float* partials, int fmt,
+                                  hipStream_t stream);
 hipError_t launch_quantize_rowwise(const float* x, int64_t rows, int64_t k, int64_t ldx,
-                                   uint8_t* q, int64_t ldq, float* scales, hipStream_t stream);
+                                   uint8_t* q, int64_t ldq, float* scales, int fmt,
+                                   hipStream_t stream);
 hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
-                              int64_t ldq, uint8_t* codes, hipStream_t stream);
+                              int64_t ldq, uint8_t* codes, int fmt, hipStream_t stream);
 
 enum ScaleMode : int { kTensor = 0, kRowwise = 1, kMx32 = 2 };
 enum OutType : int { kF16 = 0, kBF16 = 1 };
+// Element formats of the codes; the values are the operand-format fields of the
+// F8F6F4 MFMA for the two FP8 formats.
+enum ElemFormat : int { kE4M3 = 0, kE5M2 = 1 };
+// Activation of the fused epilogue (applied after the scales and the bias).
+enum Activation : int { kActNone = 0, kActRelu = 1, kActGelu = 2, kActSilu = 3 };
 
 struct GemmProblem {
   int M, N, K;
@@ -31,6 +39,8 @@ struct GemmProblem {
   void* C;
   int64_t ldc;
   void* workspace;      // split-K partials and tile counters (gemm_workspace_bytes)
+  const float* bias;    // fused epilogue: fp32 [N] added after the scales, or null
+  int act;              // fused epilogue: Activation applied last
 };
 
 // Device workspace a dense GEMM of this shape needs (0: none).  Shapes with too
@@ -40,6 +50,10 @@ struct GemmProblem {
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int mode);
 
 hipError_t launch_gemm(const GemmProblem& p, int mode, int out, hipStream_t stream);
+// The same GEMM for e5m2 operands (A format first, then B).
+hipError_t launch_gemm_e5m2_e5m2(const GemmProblem& p, int mode, int out, hipStream_t stream);
+hipError_t launch_gemm_e4m3_e5m2(const GemmProblem& p, int mode, int out, hipStream_t stream);
+hipError_t launch_gemm_e5m2_e4m3(const GemmProblem& p, int mode, int out, hipStream_t stream);
 
 struct GroupedProblem {
   int groups;

@@ -1,4 +1,5 @@
-// fp32 -> e4m3fn quantisation kernels for gfx950 (scale computation and encoding).
+// fp32 -> e4m3fn / e5m2 quantisation kernels for gfx950 (scale computation and
+// encoding).
 //
 // What is computed (the E4M3 operands with per-block scale factors of the
 // JAX/Triton Blackwell FP8 GEMM post, the row-wise FP8 GEMM of "Hopper/Blackwell
@@ -8,6 +9,8 @@
 //   row-wise   : the same with one amax per row (reduction along K)
 //   MX (32)    : per 32-element K block, E8M0 code = clamp(floor(log2 amax) - 8 + 127,
 //                0, 254) (127 if amax = 0), q = RNE_sat(x * 2^(127 - code))
+// and the same with 57344 and 15 in place of 448 and 8 for e5m2 codes (the post's
+// second FP8 format).
 //
 // All kernels are HBM-streaming.  The unit of work is 1024 consecutive values of
 // a row, taken by one wavefront so that every load and store instruction covers
@@ -67,10 +70,11 @@ __device__ __forceinline__ float absmax_unit(const Unit& u) {
 }
 
 // Quotient by s (binary32 division), then encode.
+template <int FMT>
 __device__ __forceinline__ void encode_unit_div(const Unit& u, float s, uint32_t (&w)[4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    w[j] = encode4_e4m3(u.v[j].x / s, u.v[j].y / s, u.v[j].z / s, u.v[j].w / s);
+    w[j] = encode4<FMT>(u.v[j].x / s, u.v[j].y / s, u.v[j].z / s, u.v[j].w / s);
 }
 
 // Block-wide max of one value per thread.
@@ -110,6 +114,7 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const float* __r
 }
 
 // ---- per-tensor: pass 2, scale from the partial maxima, then encode ----------
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void quant_tensor_kernel(
     const float* __restrict__ x, int k, int upr, int units, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, const float* __restrict__ partials, int nparts,
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void quant_tensor_kernel(
   float m = 0.0f;
   for (int i = threadIdx.x; i < nparts; i += kThreads) m = fmaxf(m, partials[i]);
   const float amax = block_max(m, red);
-  const float s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
+  const float s = (amax == 0.0f) ? 1.0f : amax / elem_max<FMT>();
   if (blockIdx.x == 0 && threadIdx.x == 0) scale_out[0] = s;
   const int lane = threadIdx.x & 63;
   const int w0 = blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -131,10 +136,10 @@ __global__ __launch_bounds__(kThreads) void quant_tensor_kernel(
     Unit b{};
     if (u2 < units) b = load_unit(x + (int64_t)r2 * ldx, c2, k, lane);
     uint32_t w[4];
-    encode_unit_div(a, s, w);
+    encode_unit_div<FMT>(a, s, w);
     store_codes(q + (int64_t)r * ldq, c0, k, lane, w);
     if (u2 < units) {
-      encode_unit_div(b, s, w);
+      encode_unit_div<FMT>(b, s, w);
       store_codes(q + (int64_t)r2 * ldq, c2, k, lane, w);
     }
   }
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void quant_tensor_kernel(
 // ---- row-wise: one workgroup per row, the row cached in registers -------------
 // Wave w holds units w, w + 4, ... (up to U of them); rows longer than 4 U units
 // take the two-pass kernel below.
-template <int U>
+template <int U, int FMT>
 __global__ __launch_bounds__(kThreads) void quant_row_kernel(const float* __restrict__ x, int rows,
                                                              int k, int upr, int64_t ldx,
                                                              uint8_t* __restrict__ q, int64_t ldq,
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const float* __rest
       m = fmaxf(m, absmax_unit(v[j]));
     }
     m = block_max(m, red);
-    const float s = (m == 0.0f) ? 1.0f : m / kE4M3Max;
+    const float s = (m == 0.0f) ? 1.0f : m / elem_max<FMT>();
     if (threadIdx.x == 0) scales[r] = s;
     uint8_t* qr = q + (int64_t)r * ldq;
 #pragma unroll
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const float* __rest
       const int u = wave + j * kWaves;
       if (u < upr) {
         uint32_t w[4];
-        encode_unit_div(v[j], s, w);
+        encode_unit_div<FMT>(v[j], s, w);
         store_codes(qr, u * 1024, k, lane, w);
       }
     }
@@ -178,6 +183,7 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(const float* __rest
 }
 
 // ---- row-wise, long rows: two passes over the row (the second mostly from cache)
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void quant_row_long_kernel(
     const float* __restrict__ x, int rows, int k, int upr, int64_t ldx, uint8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scales) {
@@ -189,12 +195,12 @@ __global__ __launch_bounds__(kThreads) void quant_row_long_kernel(
     float m = 0.0f;
     for (int u = wave; u < upr; u += kWaves) m = fmaxf(m, absmax_unit(load_unit(xr, u * 1024, k, lane)));
     m = block_max(m, red);
-    const float s = (m == 0.0f) ? 1.0f : m / kE4M3Max;
+    const float s = (m == 0.0f) ? 1.0f : m / elem_max<FMT>();
     if (threadIdx.x == 0) scales[r] = s;
     uint8_t* qr = q + (int64_t)r * ldq;
     for (int u = wave; u < upr; u += kWaves) {
       uint32_t w[4];
-      encode_unit_div(load_unit(xr, u * 1024, k, lane), s, w);
+      encode_unit_div<FMT>(load_unit(xr, u * 1024, k, lane), s, w);
       store_codes(qr, u * 1024, k, lane, w);
     }
   }
@@ -203,6 +209,7 @@ __global__ __launch_bounds__(kThreads) void quant_row_long_kernel(
 // ---- MX: a 32-element block is one float4 of 8 consecutive lanes ---------------
 // Block maxima by xor-shuffles inside each group of 8 lanes; the first lane of a
 // group writes the block's E8M0 code.
+template <int FMT>
 __device__ __forceinline__ void mx_unit(const Unit& u, uint8_t* qrow, uint8_t* crow, int col0,
                                         int k, int lane) {
   uint32_t w[4];
@@ -212,9 +219,9 @@ __device__ __forceinline__ void mx_unit(const Unit& u, uint8_t* qrow, uint8_t* c
     m = fmaxf(m, __shfl_xor(m, 1, 64));
     m = fmaxf(m, __shfl_xor(m, 2, 64));
     m = fmaxf(m, __shfl_xor(m, 4, 64));
-    const uint32_t code = mx_code_from_amax(m);
+    const uint32_t code = mx_code_from_amax<FMT>(m);
     const int e = 127 - (int)code;
-    w[j] = encode4_e4m3(ldexpf(u.v[j].x, e), ldexpf(u.v[j].y, e), ldexpf(u.v[j].z, e),
+    w[j] = encode4<FMT>(ldexpf(u.v[j].x, e), ldexpf(u.v[j].y, e), ldexpf(u.v[j].z, e),
                         ldexpf(u.v[j].w, e));
     const int c = col0 + 256 * j + 4 * lane;
     if ((lane & 7) == 0 && c < k) crow[c >> 5] = (uint8_t)code;
@@ -222,6 +229,7 @@ __device__ __forceinline__ void mx_unit(const Unit& u, uint8_t* qrow, uint8_t* c
   store_codes(qrow, col0, k, lane, w);
 }
 
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const float* __restrict__ x, int k,
                                                             int upr, int units, int64_t ldx,
                                                             uint8_t* __restrict__ q, int64_t ldq,
@@ -237,8 +245,8 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const float* __restr
     const Unit a = load_unit(x + (int64_t)r * ldx, c0, k, lane);
     Unit b{};
     if (u2 < units) b = load_unit(x + (int64_t)r2 * ldx, c2, k, lane);
-    mx_unit(a, q + (int64_t)r * ldq, codes + (int64_t)r * bpr, c0, k, lane);
-    if (u2 < units) mx_unit(b, q + (int64_t)r2 * ldq, codes + (int64_t)r2 * bpr, c2, k, lane);
+    mx_unit<FMT>(a, q + (int64_t)r * ldq, codes + (int64_t)r * bpr, c0, k, lane);
+    if (u2 < units) mx_unit<FMT>(b, q + (int64_t)r2 * ldq, codes + (int64_t)r2 * bpr, c2, k, lane);
   }
 }
 
@@ -249,10 +257,9 @@ int grid_for(uint64_t work_items, int per_block, int cap) {
   return (int)g;
 }
 
-}  // namespace
-
-hipError_t launch_quantize_tensor(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
-                                  int64_t ldq, float* scale, float* partials, hipStream_t stream) {
+template <int FMT>
+hipError_t quantize_tensor_fmt(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
+                               int64_t ldq, float* scale, float* partials, hipStream_t stream) {
   const int upr = (int)((k + 1023) / 1024);
   const int units = (int)(rows * upr);
   // two units per wavefront and iteration
@@ -262,39 +269,64 @@ hipError_t launch_quantize_tensor(const float* x, int64_t rows, int64_t k, int64
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int grid2 = grid_for((uint64_t)units, 2 * kWaves, 8192);
-  hipLaunchKernelGGL(quant_tensor_kernel, dim3(grid2), dim3(kThreads), 0, stream, x, (int)k, upr,
-                     units, ldx, q, ldq, partials, grid, scale);
+  hipLaunchKernelGGL((quant_tensor_kernel<FMT>), dim3(grid2), dim3(kThreads), 0, stream, x,
+                     (int)k, upr, units, ldx, q, ldq, partials, grid, scale);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_rowwise(const float* x, int64_t rows, int64_t k, int64_t ldx,
-                                   uint8_t* q, int64_t ldq, float* scales, hipStream_t stream) {
+template <int FMT>
+hipError_t quantize_rowwise_fmt(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
+                                int64_t ldq, float* scales, hipStream_t stream) {
   const int upr = (int)((k + 1023) / 1024);
   const int r = (int)rows;
   const int grid = grid_for((uint64_t)rows, 1, 65535);
   if (upr <= kWaves)
-    hipLaunchKernelGGL((quant_row_kernel<1>), dim3(grid), dim3(kThreads), 0, stream, x, r, (int)k,
-                       upr, ldx, q, ldq, scales);
+    hipLaunchKernelGGL((quant_row_kernel<1, FMT>), dim3(grid), dim3(kThreads), 0, stream, x, r,
+                       (int)k, upr, ldx, q, ldq, scales);
   else if (upr <= 2 * kWaves)
-    hipLaunchKernelGGL((quant_row_kernel<2>), dim3(grid), dim3(kThreads), 0, stream, x, r, (int)k,
-                       upr, ldx, q, ldq, scales);
+    hipLaunchKernelGGL((quant_row_kernel<2, FMT>), dim3(grid), dim3(kThreads), 0, stream, x, r,
+                       (int)k, upr, ldx, q, ldq, scales);
   else if (upr <= 4 * kWaves)
-    hipLaunchKernelGGL((quant_row_kernel<4>), dim3(grid), dim3(kThreads), 0, stream, x, r, (int)k,
-                       upr, ldx, q, ldq, scales);
+    hipLaunchKernelGGL((quant_row_kernel<4, FMT>), dim3(grid), dim3(kThreads), 0, stream, x, r,
+                       (int)k, upr, ldx, q, ldq, scales);
   else
-    hipLaunchKernelGGL(quant_row_long_kernel, dim3(grid), dim3(kThreads), 0, stream, x, r, (int)k,
-                       upr, ldx, q, ldq, scales);
+    hipLaunchKernelGGL((quant_row_long_kernel<FMT>), dim3(grid), dim3(kThreads), 0, stream, x, r,
+                       (int)k, upr, ldx, q, ldq, scales);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
-                              int64_t ldq, uint8_t* codes, hipStream_t stream) {
+template <int FMT>
+hipError_t quantize_mx_fmt(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
+                           int64_t ldq, uint8_t* codes, hipStream_t stream) {
   const int upr = (int)((k + 1023) / 1024);
   const int units = (int)(rows * upr);
   const int grid = grid_for((uint64_t)units, 2 * kWaves, 8192);
-  hipLaunchKernelGGL(quant_mx_kernel, dim3(grid), dim3(kThreads), 0, stream, x, (int)k, upr, units,
-                     ldx, q, ldq, codes);
+  hipLaunchKernelGGL((quant_mx_kernel<FMT>), dim3(grid), dim3(kThreads), 0, stream, x, (int)k,
+                     upr, units, ldx, q, ldq, codes);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_tensor(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
+                                  int64_t ldq, float* scale, float* partials, int fmt,
+                                  hipStream_t stream) {
+  if (fmt == kE5M2)
+    return quantize_tensor_fmt<kE5M2>(x, rows, k, ldx, q, ldq, scale, partials, stream);
+  return quantize_tensor_fmt<kE4M3>(x, rows, k, ldx, q, ldq, scale, partials, stream);
+}
+
+hipError_t launch_quantize_rowwise(const float* x, int64_t rows, int64_t k, int64_t ldx,
+                                   uint8_t* q, int64_t ldq, float* scales, int fmt,
+                                   hipStream_t stream) {
+  if (fmt == kE5M2) return quantize_rowwise_fmt<kE5M2>(x, rows, k, ldx, q, ldq, scales, stream);
+  return quantize_rowwise_fmt<kE4M3>(x, rows, k, ldx, q, ldq, scales, stream);
+}
+
+hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
+                              int64_t ldq, uint8_t* codes, int fmt, hipStream_t stream) {
+  if (fmt == kE5M2) return quantize_mx_fmt<kE5M2>(x, rows, k, ldx, q, ldq, codes, stream);
+  return quantize_mx_fmt<kE4M3>(x, rows, k, ldx, q, ldq, codes, stream);
 }
 
 }  // namespace fp8gemm

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FP8GEMM_VERSION 100 /* 1.0.0 */
+#define FP8GEMM_VERSION 110 /* 1.1.0: e5m2 operands and fused epilogues */
 
 typedef enum fp8gemm_status {
   FP8GEMM_SUCCESS = 0,
@@ -65,6 +65,22 @@ typedef enum fp8gemm_out_dtype {
   FP8GEMM_OUT_F16 = 0, /* IEEE binary16, round to nearest even */
   FP8GEMM_OUT_BF16 = 1 /* bfloat16, round to nearest even      */
 } fp8gemm_out_dtype;
+
+/* Element format of operand codes (the JAX/Triton Blackwell FP8 GEMM post names
+   both FP8 formats, E4M3 and E5M2, in its second paragraph). */
+typedef enum fp8gemm_format {
+  FP8GEMM_FORMAT_E4M3 = 0, /* OCP e4m3fn: bias 7, no infinity, max 448 (the default)      */
+  FP8GEMM_FORMAT_E5M2 = 1  /* OCP e5m2: bias 15, infinities and NaNs, max 57344           */
+} fp8gemm_format;
+
+/* Activation of the fused epilogue (the Cutlass-named Triton FP8 post fuses a
+   bias_add_relu epilogue to save a round trip of C through memory). */
+typedef enum fp8gemm_activation {
+  FP8GEMM_ACT_NONE = 0,
+  FP8GEMM_ACT_RELU = 1, /* max(y, 0)                              */
+  FP8GEMM_ACT_GELU = 2, /* y * (1 + erf(y / sqrt(2))) / 2          */
+  FP8GEMM_ACT_SILU = 3  /* y / (1 + exp(-y))                       */
+} fp8gemm_activation;
 
 /* ------------------------------------------------------------------------- */
 /* Quantisation: fp32 -> e4m3fn codes + scales.                                */
@@ -96,6 +112,15 @@ fp8gemm_status fp8gemm_quantize(const float* x, int64_t rows, int64_t k, int64_t
                                 uint8_t* q, int64_t ldq, void* scales, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* The same for either element format (fp8gemm_format): with FP8GEMM_FORMAT_E5M2
+   the rules above use 57344 in place of 448 (s = fl32(amax/57344), saturation
+   to +-57344, never infinity) and 15 in place of 8 (MX32: e = floor(log2 amax)
+   - 15).  fp8gemm_quantize is this call with FP8GEMM_FORMAT_E4M3.  Errors as
+   above; an unknown format is INVALID_VALUE. */
+fp8gemm_status fp8gemm_quantize_ex(const float* x, int64_t rows, int64_t k, int64_t ldx, int mode,
+                                   int format, uint8_t* q, int64_t ldq, void* scales,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* Dense scaled GEMM: C[m,n] = cast( sum_k dq_a(m,k) * dq_b(k,n) ).             */
 /*                                                                           */
@@ -118,6 +143,30 @@ fp8gemm_status fp8gemm_run(int64_t M, int64_t N, int64_t K, const uint8_t* A, in
                            const uint8_t* B, int64_t ldb, int mode, const void* scale_a,
                            const void* scale_b, void* C, int64_t ldc, int out_dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Dense scaled GEMM with operand formats and a fused epilogue:                */
+/*   y[m,n] = sum_k dq_a(m,k) * dq_b(k,n)  (as fp8gemm_run),                   */
+/*   C[m,n] = cast( act( y[m,n] + bias[n] ) ).                                 */
+/* a_format, b_format: fp8gemm_format of the A and B codes (any pair: e5m2 x   */
+/*          e5m2 or mixed e4m3 x e5m2, the gradient-GEMM pairing).              */
+/* bias   : device float[N], 4-byte aligned, or NULL (no bias).               */
+/* activation: fp8gemm_activation, applied in fp32 after the scales and bias.   */
+/* The scale modes, layouts, workspace and errors are those of fp8gemm_run      */
+/* (the workspace size does not depend on formats or epilogue); an unknown      */
+/* format or activation is INVALID_VALUE.  fp8gemm_run is this call with e4m3   */
+/* operands, no bias and FP8GEMM_ACT_NONE.                                     */
+/* Accuracy: |C - act(y_ref + bias)| <= L * (1e-3 * sum_k|dq_a*dq_b|           */
+/*   + 2^-22 |y_ref + bias|) + 2^-20 (|act| + |y_ref + bias|) + 1 output ulp,   */
+/*   with L the activation's Lipschitz bound (1 for none/ReLU, 1.13 for GELU,  */
+/*   1.1 for SiLU) and the 2^-22 and 2^-20 terms the fp32 rounding of the       */
+/*   scaled value, the bias add and the activation's math functions.            */
+/* ------------------------------------------------------------------------- */
+fp8gemm_status fp8gemm_run_ex(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                              int a_format, const uint8_t* B, int64_t ldb, int b_format, int mode,
+                              const void* scale_a, const void* scale_b, const float* bias,
+                              int activation, void* C, int64_t ldc, int out_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Grouped (mixture-of-experts) GEMM, the grouped form in the MoE paragraph of   */

@@ -29,16 +29,17 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = F.exported_symbols()
     assert set(names) == {
-        "fp8gemm_quantize_workspace_size", "fp8gemm_quantize", "fp8gemm_workspace_size",
-        "fp8gemm_run", "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run",
-        "fp8gemm_status_string", "fp8gemm_version"}
+        "fp8gemm_quantize_workspace_size", "fp8gemm_quantize", "fp8gemm_quantize_ex",
+        "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex",
+        "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run", "fp8gemm_status_string",
+        "fp8gemm_version"}
     raw = ctypes.CDLL(F.library_path())
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert F.fp8gemm_version() == 100
+    assert F.fp8gemm_version() == 110
     for code, name in [(0, "FP8GEMM_SUCCESS"), (1, "FP8GEMM_ERROR_INVALID_VALUE"),
                        (2, "FP8GEMM_ERROR_MISALIGNED"), (3, "FP8GEMM_ERROR_NOT_SUPPORTED"),
                        (4, "FP8GEMM_ERROR_WORKSPACE"), (5, "FP8GEMM_ERROR_LAUNCH"),
@@ -115,6 +116,33 @@ def test_run_validation(lib):
     assert _run(lib, ldc=68) == MISALIGNED
     assert _run(lib, sa=P3 + 1) == MISALIGNED
     assert _run(lib, M=1 << 31) == NOT_SUPPORTED
+
+
+def _run_ex(lib, M=64, N=64, K=128, A=P, lda=128, fa=0, B=P2, ldb=128, fb=0, mode=1, sa=P3,
+            sb=P3 + 256, bias=0, act=0, C=P3 + 4096, ldc=64, out=1):
+    return lib.fp8gemm_run_ex(M, N, K, A, lda, fa, B, ldb, fb, mode, sa, sb, bias, act, C, ldc,
+                              out, 0, 0, None)
+
+
+def test_extended_entry_points_validation(lib):
+    """Formats and the fused epilogue are validated before any HIP call."""
+    assert _run_ex(lib, M=0) == SUCCESS
+    assert _run_ex(lib, M=0, fa=1, fb=1, bias=P, act=3) == SUCCESS
+    assert _run_ex(lib, fa=2) == INVALID
+    assert _run_ex(lib, fb=-1) == INVALID
+    assert _run_ex(lib, act=4) == INVALID
+    assert _run_ex(lib, act=-1) == INVALID
+    assert _run_ex(lib, bias=P + 2) == MISALIGNED
+    assert _run_ex(lib, fa=1, K=112, lda=112, ldb=112, mode=2) == NOT_SUPPORTED
+    assert _run_ex(lib, A=0) == INVALID
+    q = lambda **kw: lib.fp8gemm_quantize_ex(kw.get("x", P), 64, kw.get("k", 256), 256,
+                                             kw.get("mode", 1), kw.get("fmt", 0), P2, 256, P3, 0,
+                                             0, None)
+    assert q(fmt=2) == INVALID
+    assert q(fmt=-1) == INVALID
+    assert q(fmt=1, x=0) == INVALID
+    assert q(fmt=1, k=48, mode=2) == NOT_SUPPORTED
+    assert q(fmt=1, mode=0) == WORKSPACE
 
 
 def test_run_split_workspace_validation(lib):
