@@ -96,7 +96,7 @@ struct DenseTiles {
 // Persistent form for shapes whose tiles are all interior: one workgroup per CU
 // walks its tiles as one copy stream (the next tile's first K tiles are fetched
 // while the current one finishes, its epilogue runs while they land).
-template <class Cfg, int MODE, typename OutT, bool FUSED>
+template <class Cfg, int MODE, typename OutT>
 __global__ __launch_bounds__(Cfg::kThreads, 1) void gemm_persistent_kernel(GemmProblem p,
                                                                            int tiles_m,
                                                                            int tiles_n) {
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void gemm_persistent_kernel(GemmP
                  __attribute__((always_inline)) {
     int m0, n0;
     src.coords(i, m0, n0);
-    epilogue_direct<Cfg, MODE, OutT, FUSED>(acc, lds, C, p.ldc, m0, n0, ts, rbuf, p.bias, p.act);
+    epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, p.ldc, m0, n0, ts, rbuf);
   };
   // epilogue_direct issues two 16-byte stores per 32 x 32 block and lane
   if (count > 0)
@@ -169,14 +169,14 @@ bool all_interior(const GemmProblem& p) {
          (int64_t)Cfg::BN * p.ldb + p.K < ((int64_t)1 << 31);
 }
 
-template <class Cfg, int MODE, typename OutT, bool FUSED>
+template <class Cfg, int MODE, typename OutT>
 hipError_t launch_persistent(const GemmProblem& p, hipStream_t stream) {
   const int tiles_m = p.M / Cfg::BM, tiles_n = p.N / Cfg::BN;
   const int total = tiles_m * tiles_n;
   const int cus = device_cus();
   const int grid = total < cus ? total : cus;
-  hipLaunchKernelGGL((gemm_persistent_kernel<Cfg, MODE, OutT, FUSED>), dim3(grid),
-                     dim3(Cfg::kThreads), 0, stream, p, tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_persistent_kernel<Cfg, MODE, OutT>), dim3(grid), dim3(Cfg::kThreads), 0,
+                     stream, p, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -190,8 +190,9 @@ hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
   if (big_tiles >= 256 * Big::kWgPerCu && !mx_ragged) {
     // persistent streams pay off from about eight tiles per CU on (measured)
     const bool many = big_tiles >= 8 * 256;
-    if ((FP8GEMM_PERSISTENT || many) && all_interior<Big>(p))
-      return launch_persistent<Big, MODE, OutT, FUSED>(p, stream);
+    // (the fused epilogue stages through the ring, so it never runs in a stream)
+    if ((FP8GEMM_PERSISTENT || many) && !FUSED && all_interior<Big>(p))
+      return launch_persistent<Big, MODE, OutT>(p, stream);
     return launch_cfg<Big, MODE, OutT, FUSED>(p, stream);
   }
   return launch_cfg<Mid, MODE, OutT, FUSED>(p, stream);
@@ -364,8 +365,11 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void splitk_kernel(GemmProblem p,
     }
   }
   const float ts = (MODE == kTensor) ? fsa[0] * fsb[0] : 1.0f;
-  epilogue<Cfg, MODE, OutT, FUSED>(sum, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N,
-                                   ts, p.bias, p.act);
+  if constexpr (FUSED)
+    epilogue_fused<Cfg, MODE, OutT>(sum, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N, ts,
+                                    p.bias, p.act);
+  else
+    epilogue<Cfg, MODE, OutT>(sum, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N, ts);
 }
 
 template <int MODE, typename OutT, bool FUSED>

@@ -1245,30 +1245,10 @@ __device__ __forceinline__ float activate(float v, int act) {
   return v;
 }
 
-// bias (may be null) and act are uniform over the launch; n is the output column
-// of v[0] and v[e] belongs to column n + e (columns at or past N are never
-// stored, their bias reads stay inside the array).  Kernels are instantiated
-// with and without these operations (FUSED): the activations' math inlined
-// into every output group makes the epilogue many times larger, and the plain
-// GEMM measured 10-20 % slower when it merely carried that code.
-template <bool FUSED>
-__device__ __forceinline__ void fused_ops(float (&v)[4], const float* bias, int act, int n, int N) {
-  if constexpr (!FUSED) return;
-  if (bias != nullptr) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] += bias[n + e < N ? n + e : N - 1];
-  }
-  if (act != kActNone) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = activate(v[e], act);
-  }
-}
-
-template <class Cfg, int MODE, typename OutT, bool FUSED = false>
+template <class Cfg, int MODE, typename OutT>
 __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN], uint8_t* lds,
                                          OutT* C, int64_t ldc, int m0, int m_end, int n0, int N,
-                                         float tensor_scale, const float* bias = nullptr,
-                                         int act = kActNone) {
+                                         float tensor_scale) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   constexpr int kChunksPerRow = Cfg::WN * 2 / 16;        // 16-byte chunks of a staged row
   constexpr int kRowsPerInst = 64 / kChunksPerRow;
@@ -1299,7 +1279,6 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFr
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] *= fb[e];
         }
-        fused_ops<FUSED>(v, bias, act, n0 + wn * Cfg::WN + c, N);
         *reinterpret_cast<uint2*>(stage + r * Cfg::kStagePitch + c * 2) =
             pack4<OutT>(v[0], v[1], v[2], v[3]);
       }
@@ -1336,11 +1315,10 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFr
 // with group 2k of the high half, after which every lane owns eight consecutive
 // columns (16 bytes) of its row: C is written with 16-byte stores and no LDS
 // staging, so the epilogue costs a few hundred instructions and no waits.
-template <class Cfg, int MODE, typename OutT, bool FUSED = false>
+template <class Cfg, int MODE, typename OutT>
 __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                 const uint8_t* lds, OutT* C, int64_t ldc, int m0,
-                                                int n0, float tensor_scale, int rbuf = 0,
-                                                const float* bias = nullptr, int act = kActNone) {
+                                                int n0, float tensor_scale, int rbuf = 0) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   static_assert(sizeof(OutT) == 2, "16-bit outputs");
   const int lane = threadIdx.x & 63;
@@ -1373,7 +1351,6 @@ __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][C
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] *= fb[e];
           }
-          fused_ops<FUSED>(v, bias, act, n0 + wn * Cfg::WN + c, n0 + Cfg::BN);
           w[q] = pack4<OutT>(v[0], v[1], v[2], v[3]);
         }
         // low half keeps group 2k and takes the high half's; high half keeps 2k + 1
@@ -1383,6 +1360,88 @@ __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][C
         *reinterpret_cast<v4i*>(crow + j * 32 + 16 * k + 8 * h) = out;
       }
     }
+  }
+}
+
+// Fused epilogue (bias, activation).  The scaled fp32 tile goes through LDS, one
+// block of 32 rows per wavefront at a time, and the bias, the activation, the
+// cast and the stores run in a loop over 16-byte pieces: four copies of the
+// activation's math instead of one per accumulator register.  (Inlining
+// it into the register epilogues made those kernels many times larger and the
+// fused GEMM slower than a separate pass over C; kernels without a fused
+// epilogue are separate instances and carry none of this code.)  Needs the ring
+// free: it runs after the mainloop's final barrier, never inside a copy stream.
+template <class Cfg, int MODE, typename OutT>
+__device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                               uint8_t* lds, OutT* C, int64_t ldc, int m0,
+                                               int m_end, int n0, int N, float tensor_scale,
+                                               const float* bias, int act) {
+  constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
+  constexpr int kPitch = Cfg::WN + 4;                    // staged fp32 row (+16 bytes)
+  constexpr int kPiecesPerRow = Cfg::WN / 4;
+  constexpr int kIters = 32 * kPiecesPerRow / 64;
+  static_assert(Cfg::kWaves * 32 * kPitch * 4 <= Cfg::kSlots * Cfg::kSlotBytes,
+                "fp32 staging fits in the ring");
+  static_assert((32 * kPiecesPerRow) % 64 == 0, "whole store instructions");
+  static_assert(64 % kPiecesPerRow == 0, "a lane keeps its columns over the store loop");
+  static_assert(sizeof(OutT) == 2, "16-bit outputs");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
+  const int h = lane >> 5;
+  float* stage = reinterpret_cast<float*>(lds) + wave * 32 * kPitch;
+  // the store loop hands each lane the same four columns every time: their bias
+  // is loaded once, before any wait on the staged rows
+  const int cc = (lane % kPiecesPerRow) * 4;            // wave-local column of the lane
+  const int n = n0 + wn * Cfg::WN + cc;
+  float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (bias != nullptr) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bv[e] = n + e < N ? bias[n + e] : 0.0f;
+  }
+  const float* rsc = reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = lane & 31;
+    float fa = 1.0f;
+    if (MODE == kTensor) fa = tensor_scale;
+    if (MODE == kRowwise) fa = rsc[wm * Cfg::WM + i * 32 + r];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = j * 32 + 8 * g + 4 * h;
+        v4f v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * fa;
+        if (MODE == kRowwise) {
+          const v4f fb = *reinterpret_cast<const v4f*>(rsc + Cfg::BM + wn * Cfg::WN + c);
+          v *= fb;
+        }
+        *reinterpret_cast<v4f*>(stage + r * kPitch + c) = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0): staged rows written
+    // unrolled by 4: the LDS reads of four pieces are in flight together
+#pragma unroll 4
+    for (int it = 0; it < kIters; ++it) {
+      const int rr = (it * 64 + lane) / kPiecesPerRow;
+      const v4f val = *reinterpret_cast<const v4f*>(stage + rr * kPitch + cc);
+      const int m = m0 + wm * Cfg::WM + i * 32 + rr;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = activate(val[e] + bv[e], act);
+      if (m < m_end) {
+        OutT* dst = C + (int64_t)m * ldc + n;
+        if (n + 4 <= N) {
+          *reinterpret_cast<uint2*>(dst) = pack4<OutT>(v[0], v[1], v[2], v[3]);
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) dst[e] = to_out<OutT>(v[e]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);                  // reads done before the next block
   }
 }
 
@@ -1398,19 +1457,25 @@ __device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, 
     if (interior_tile<Cfg, MODE>(op)) {
       v16f acc[Cfg::kFragM][Cfg::kFragN];
       mainloop_interior<Cfg, MODE>(op, lds, acc);
+      if constexpr (FUSED) {
+        epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias,
+                                        act);
+      } else {
 #if FP8GEMM_DIRECT_EPILOGUE
-      epilogue_direct<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, n0, tensor_scale, 0, bias,
-                                              act);
+        epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, n0, tensor_scale);
 #else
-      epilogue<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias,
-                                       act);
+        epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
 #endif
+      }
       return;
     }
   }
   v16f acc[Cfg::kFragM][Cfg::kFragN];
   mainloop<Cfg, MODE, KALIGNED>(op, lds, acc);
-  epilogue<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act);
+  if constexpr (FUSED)
+    epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act);
+  else
+    epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
 }
 
 }  // inline namespace
