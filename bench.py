@@ -192,8 +192,8 @@ def cpu_baseline(w, rows: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--formats", default="e4m3,e4m3", metavar="A,B",
                     help="element formats of the A and B codes (e4m3 or e5m2; dense only)")
@@ -316,7 +316,9 @@ def main():
 
     qa_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
     qb_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
-    gemm_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    gemm_each = sorted(e[2].elapsed_time(e[3]) for e in events)
+    gemm_ms = sum(gemm_each) / args.steps
+    gemm_med, gemm_min = gemm_each[len(gemm_each) // 2], gemm_each[0]
     ms_per_step = elapsed * 1e3 / args.steps
     flops = w.flops
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -354,6 +356,29 @@ def main():
                 "operand_sets": nsets, "note": "back-to-back launches over distinct operand copies"}
         del qbs, qas
         log(f"cold-cache GEMM: {cold}")
+        # context: a plain device read (torch sum over int64 words) of the same
+        # number of bytes from HBM, rotated over distinct buffers, and of 1 GiB
+        def read_rate(nbytes, sets, reps):
+            bufs = [torch.ones(nbytes // 8, dtype=torch.int64, device=dev) for _ in range(sets)]
+            for b in bufs:
+                b.sum()
+            torch.cuda.synchronize()
+            r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            r0.record()
+            for _ in range(reps):
+                for b in bufs:
+                    b.sum()
+            r1.record()
+            torch.cuda.synchronize()
+            ms = r0.elapsed_time(r1) / (reps * sets)
+            del bufs
+            return {"bytes": nbytes, "ms": round(ms, 5), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        gb = gemm_bytes(w) // 8 * 8
+        cold["hbm_read_context"] = {
+            "kernel": "torch sum over int64 words (a plain device read)",
+            "same_bytes": read_rate(gb, max(2, -(-(512 << 20) // gb)), 4),
+            "one_gib": read_rate(1 << 30, 2, 3)}
+        log(f"plain read context: {cold['hbm_read_context']}")
     gemm_gbs = gemm_bytes(w) / (gemm_ms * 1e-3) / 1e9
     # the committed counter summaries are of the default e4m3 GEMM without epilogue
     default_variant = args.formats == "e4m3,e4m3" and not use_bias
@@ -386,7 +411,8 @@ def main():
                    "step": "quantize A + quantize B + GEMM"},
         "roofline": roofline,
         "kernels": {
-            "gemm": {"ms": round(gemm_ms, 5), "tflops": round(achieved, 1),
+            "gemm": {"ms": round(gemm_ms, 5), "ms_median": round(gemm_med, 5),
+                     "ms_min": round(gemm_min, 5), "tflops": round(achieved, 1),
                      "gbs_algorithmic": round(gemm_gbs, 1)},
             "quantize_a": {"ms": round(qa_ms, 4),
                            "gbs": round(quant_bytes_a / (qa_ms * 1e-3) / 1e9, 1)},
