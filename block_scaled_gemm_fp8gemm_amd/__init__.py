@@ -26,6 +26,7 @@ __all__ = [
     "Fp8GemmError", "SCALE_MODES", "OUT_DTYPES", "FORMATS", "ACTIVATIONS", "library_path",
     "load_library", "fp8gemm_quantize_workspace_size", "fp8gemm_quantize",
     "fp8gemm_quantize_ex", "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex",
+    "fp8gemm_workspace_size_kn", "fp8gemm_run_kn",
     "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run",
     "fp8gemm_status_string", "fp8gemm_version", "quantize", "gemm", "grouped_gemm",
     "exported_symbols",
@@ -70,6 +71,9 @@ _SIGNATURES = {
     "fp8gemm_run": (_int, [_i64, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _p, _p, _i64, _int,
                            _p, _sz, _p]),
     "fp8gemm_run_ex": (_int, [_i64, _i64, _i64, _p, _i64, _int, _p, _i64, _int, _int, _p, _p, _p,
+                              _int, _p, _i64, _int, _p, _sz, _p]),
+    "fp8gemm_workspace_size_kn": (_sz, [_i64, _i64, _i64, _int]),
+    "fp8gemm_run_kn": (_int, [_i64, _i64, _i64, _p, _i64, _int, _p, _i64, _int, _int, _p, _p, _p,
                               _int, _p, _i64, _int, _p, _sz, _p]),
     "fp8gemm_grouped_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _int]),
     "fp8gemm_grouped_run": (_int, [_i32, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _i64, _int,
@@ -147,6 +151,19 @@ def fp8gemm_run_ex(M: int, N: int, K: int, A: int, lda: int, a_format: int, B: i
                    activation: int, C: int, ldc: int, out_dtype: int, workspace: int,
                    workspace_bytes: int, stream: int) -> None:
     _check("fp8gemm_run_ex", load_library().fp8gemm_run_ex(
+        M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias, activation, C,
+        ldc, out_dtype, workspace, workspace_bytes, stream))
+
+
+def fp8gemm_workspace_size_kn(M: int, N: int, K: int, mode: int) -> int:
+    return load_library().fp8gemm_workspace_size_kn(M, N, K, mode)
+
+
+def fp8gemm_run_kn(M: int, N: int, K: int, A: int, lda: int, a_format: int, B: int, ldb: int,
+                   b_format: int, mode: int, scale_a: int, scale_b: int, bias: int,
+                   activation: int, C: int, ldc: int, out_dtype: int, workspace: int,
+                   workspace_bytes: int, stream: int) -> None:
+    _check("fp8gemm_run_kn", load_library().fp8gemm_run_kn(
         M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias, activation, C,
         ldc, out_dtype, workspace, workspace_bytes, stream))
 
@@ -250,17 +267,22 @@ def quantize(x, mode: str = "tensor", out=None, scales=None, workspace=None,
 
 def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None,
          workspace=None, fmt_a: str = "e4m3", fmt_b: str = "e4m3", bias=None,
-         activation: str = "none"):
-    """C [M, N] = act(dq(qa [M, K]) @ dq(qb [N, K])^T + bias), returned as fp16 / bf16.
+         activation: str = "none", b_layout: str = "nk"):
+    """C [M, N] = act(dq(qa [M, K]) @ dq(qb) + bias), returned as fp16 / bf16.
 
-    fmt_a / fmt_b: element formats of the codes ("e4m3" or "e5m2"); bias: float32
-    [N] CUDA tensor or None; activation: "none", "relu", "gelu" or "silu".
+    qb is [N, K] (K contiguous, b_layout "nk") or [K, N] (N contiguous, "kn"; its
+    MX codes sb then [K/32, N]); fmt_a / fmt_b: element formats of the codes
+    ("e4m3" or "e5m2"); bias: float32 [N] CUDA tensor or None; activation: "none",
+    "relu", "gelu" or "silu".
     """
     torch = _torch()
     _require_cuda(qa, "qa", torch.uint8, 2)
     _require_cuda(qb, "qb", torch.uint8, 2)
     M, K = qa.shape
-    N, Kb = qb.shape
+    if b_layout == "kn":
+        Kb, N = qb.shape
+    else:
+        N, Kb = qb.shape
     if K != Kb:
         raise ValueError("qa and qb must share K")
     tdt = torch.float16 if out_dtype == "f16" else torch.bfloat16
@@ -268,14 +290,16 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
         ldc = (N + 7) // 8 * 8
         out = torch.empty((M, ldc), dtype=tdt, device=qa.device)[:, :N]
     m = SCALE_MODES[mode]
-    need = fp8gemm_workspace_size(M, N, K, m)
+    kn = b_layout == "kn"
+    need = (fp8gemm_workspace_size_kn if kn else fp8gemm_workspace_size)(M, N, K, m)
     if need and workspace is None:
         workspace = gemm_workspace(qa.device, need)
     if bias is not None:
         _require_cuda(bias, "bias", torch.float32, 1)
         if bias.numel() != N:
             raise ValueError("bias must have N elements")
-    fp8gemm_run_ex(M, N, K, _ptr(qa), qa.stride(0), FORMATS[fmt_a], _ptr(qb), qb.stride(0),
+    (fp8gemm_run_kn if kn else fp8gemm_run_ex)(
+                   M, N, K, _ptr(qa), qa.stride(0), FORMATS[fmt_a], _ptr(qb), qb.stride(0),
                    FORMATS[fmt_b], m, _ptr(sa), _ptr(sb), _ptr(bias), ACTIVATIONS[activation],
                    _ptr(out), out.stride(0), OUT_DTYPES[out_dtype],
                    _ptr(workspace) if need else 0, workspace.numel() if need else 0,

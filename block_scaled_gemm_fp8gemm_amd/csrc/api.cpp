@@ -161,6 +161,69 @@ fp8gemm_status fp8gemm_run_ex(int64_t M, int64_t N, int64_t K, const uint8_t* A,
   return from_hip(fp8gemm::launch_gemm(p, mode, out_dtype, s));
 }
 
+// Row-major B: the workspace holds the K-contiguous copy of B ([N][K] bytes), for
+// MX its codes ([N][K/32]), each rounded up to 256 bytes, then the GEMM's own
+// workspace.
+namespace {
+constexpr int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+int64_t kn_b_bytes(int64_t N, int64_t K) { return round256(N * K); }
+int64_t kn_code_bytes(int64_t N, int64_t K, int mode) {
+  return mode == kMx32 ? round256(N * (K / 32)) : 0;
+}
+}  // namespace
+
+size_t fp8gemm_workspace_size_kn(int64_t M, int64_t N, int64_t K, int mode) {
+  if (!valid_mode(mode) || M <= 0 || N <= 0 || K <= 0) return 0;
+  return (size_t)(kn_b_bytes(N, K) + kn_code_bytes(N, K, mode)) +
+         fp8gemm_workspace_size(M, N, K, mode);
+}
+
+fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                              int a_format, const uint8_t* B, int64_t ldb, int b_format, int mode,
+                              const void* scale_a, const void* scale_b, const float* bias,
+                              int activation, void* C, int64_t ldc, int out_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_mode(mode) || !valid_out(out_dtype) || !valid_format(a_format) ||
+      !valid_format(b_format) || !valid_act(activation) || M < 0 || N < 0 || K <= 0)
+    return FP8GEMM_ERROR_INVALID_VALUE;
+  if (M == 0 || N == 0) return FP8GEMM_SUCCESS;
+  if (!B || !scale_b) return FP8GEMM_ERROR_INVALID_VALUE;
+  if (ldb < N) return FP8GEMM_ERROR_INVALID_VALUE;
+  if (N > kMaxDim || K > kMaxDim || ldb > kMaxDim) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if (K % 16 != 0 || (mode == kMx32 && K % 32 != 0)) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  // one transpose workgroup per 64 x 64 tile: keep the grid below 2^31
+  if (((K + 63) / 64) * ((N + 63) / 64) > kMaxDim) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if (!aligned(B, 16) || ldb % 16 != 0) return FP8GEMM_ERROR_MISALIGNED;
+  const size_t need = fp8gemm_workspace_size_kn(M, N, K, mode);
+  if (!workspace || workspace_bytes < need) return FP8GEMM_ERROR_WORKSPACE;
+  if (!aligned(workspace, 16)) return FP8GEMM_ERROR_MISALIGNED;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* bt = ws;
+  uint8_t* codes_t = ws + kn_b_bytes(N, K);
+  uint8_t* ws_gemm = codes_t + kn_code_bytes(N, K, mode);
+  const size_t gemm_bytes = workspace_bytes - (size_t)(ws_gemm - ws);
+  // the GEMM's checks run first, on the transposed operands, so a call they
+  // reject enqueues nothing
+  const int64_t ldbt = K;                     // K % 16 == 0: 16-byte rows
+  fp8gemm_status st = check_gemm_common(M, N, K, A, lda, bt, ldbt, mode, scale_a,
+                                        mode == kMx32 ? codes_t : scale_b, C, ldc, out_dtype);
+  if (st != FP8GEMM_SUCCESS) return st;
+  if (bias && !aligned(bias, 4)) return FP8GEMM_ERROR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = fp8gemm::launch_transpose_u8(B, ldb, bt, ldbt, K, N, s);
+  if (e != hipSuccess) return FP8GEMM_ERROR_LAUNCH;
+  const void* sb = scale_b;
+  if (mode == kMx32) {
+    e = fp8gemm::launch_transpose_u8(static_cast<const uint8_t*>(scale_b), N, codes_t, K / 32,
+                                     K / 32, N, s);
+    if (e != hipSuccess) return FP8GEMM_ERROR_LAUNCH;
+    sb = codes_t;
+  }
+  return fp8gemm_run_ex(M, N, K, A, lda, a_format, bt, ldbt, b_format, mode, scale_a, sb, bias,
+                        activation, C, ldc, out_dtype, gemm_bytes ? ws_gemm : nullptr, gemm_bytes,
+                        stream);
+}
+
 size_t fp8gemm_grouped_workspace_size(int32_t num_groups, int64_t total_m, int64_t N, int64_t K,
                                       int mode) {
   (void)num_groups;

@@ -69,6 +69,11 @@ struct GroupedProblem {
   int64_t ldc;
 };
 
+// out[c][r] = in[r][c] for a rows x cols byte matrix (row pitches ldi >= cols and
+// ldo >= rows bytes): the row-major B operand and its MX codes made K-contiguous.
+hipError_t launch_transpose_u8(const uint8_t* in, int64_t ldi, uint8_t* out, int64_t ldo,
+                               int64_t rows, int64_t cols, hipStream_t stream);
+
 hipError_t launch_grouped_gemm(const GroupedProblem& p, int mode, int out, hipStream_t stream);
 
 }  // namespace fp8gemm

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FP8GEMM_VERSION 110 /* 1.1.0: e5m2 operands and fused epilogues */
+#define FP8GEMM_VERSION 120 /* 1.2.0: e5m2 operands, fused epilogues, row-major B */
 
 typedef enum fp8gemm_status {
   FP8GEMM_SUCCESS = 0,
@@ -163,6 +163,28 @@ fp8gemm_status fp8gemm_run(int64_t M, int64_t N, int64_t K, const uint8_t* A, in
 /*   scaled value, the bias add and the activation's math functions.            */
 /* ------------------------------------------------------------------------- */
 fp8gemm_status fp8gemm_run_ex(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                              int a_format, const uint8_t* B, int64_t ldb, int b_format, int mode,
+                              const void* scale_a, const void* scale_b, const float* bias,
+                              int activation, void* C, int64_t ldc, int out_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Dense scaled GEMM with B in row-major [K,N] layout (N contiguous), the layout */
+/* of the pages' Triton listings ("Hopper/Blackwell architecture features"      */
+/* §12.7.1/§12.7.2 advance b_ptr by BLOCK_K * stride_bk).                        */
+/*   B      : element (k,n) at B[k*ldb+n]; ldb >= N, a multiple of 16; 16-byte   */
+/*            aligned.                                                           */
+/*   scale_b: TENSOR float[1]; ROWWISE float[N]; MX32 uint8 [K/32][N] (row-major, */
+/*            N codes per row).                                                 */
+/* Everything else (A, C, formats, scale_a, bias, activation, accuracy, errors) */
+/* as fp8gemm_run_ex.  The call first copies B and its MX codes into the        */
+/* K-contiguous layout in the workspace (one HBM pass over B), then runs the    */
+/* GEMM: workspace is fp8gemm_workspace_size_kn() bytes, 16-byte aligned,       */
+/* zero-filled before its first use (never NULL: the copy lives there).         */
+/* ------------------------------------------------------------------------- */
+size_t fp8gemm_workspace_size_kn(int64_t M, int64_t N, int64_t K, int mode);
+
+fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                               int a_format, const uint8_t* B, int64_t ldb, int b_format, int mode,
                               const void* scale_a, const void* scale_b, const float* bias,
                               int activation, void* C, int64_t ldc, int out_dtype,

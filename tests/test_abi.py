@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol(lib):
     names = F.exported_symbols()
     assert set(names) == {
         "fp8gemm_quantize_workspace_size", "fp8gemm_quantize", "fp8gemm_quantize_ex",
-        "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex",
+        "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex", "fp8gemm_workspace_size_kn",
+        "fp8gemm_run_kn",
         "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run", "fp8gemm_status_string",
         "fp8gemm_version"}
     raw = ctypes.CDLL(F.library_path())
@@ -39,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert F.fp8gemm_version() == 110
+    assert F.fp8gemm_version() == 120
     for code, name in [(0, "FP8GEMM_SUCCESS"), (1, "FP8GEMM_ERROR_INVALID_VALUE"),
                        (2, "FP8GEMM_ERROR_MISALIGNED"), (3, "FP8GEMM_ERROR_NOT_SUPPORTED"),
                        (4, "FP8GEMM_ERROR_WORKSPACE"), (5, "FP8GEMM_ERROR_LAUNCH"),
@@ -143,6 +144,26 @@ def test_extended_entry_points_validation(lib):
     assert q(fmt=1, x=0) == INVALID
     assert q(fmt=1, k=48, mode=2) == NOT_SUPPORTED
     assert q(fmt=1, mode=0) == WORKSPACE
+
+
+def test_row_major_b_validation(lib):
+    """fp8gemm_run_kn: validated before any HIP call; the workspace holds B's copy."""
+    need = F.fp8gemm_workspace_size_kn(64, 64, 128, 1)
+    assert need >= 64 * 128
+    assert F.fp8gemm_workspace_size_kn(64, 64, 128, 2) >= need + 64 * 4     # + MX codes
+    assert F.fp8gemm_workspace_size_kn(64, 64, 128, 9) == 0
+    def run(B=P2, ldb=64, ws=P3 + (1 << 20), wsb=need, K=128, mode=1, **kw):
+        return lib.fp8gemm_run_kn(kw.get("M", 64), 64, K, P, 128, 0, B, ldb, 0, mode, P3,
+                                  P3 + 256, 0, 0, P3 + 4096, 64, 1, ws, wsb, None)
+    assert run(M=0) == SUCCESS
+    assert run(B=0) == INVALID
+    assert run(ldb=32) == INVALID                                 # ldb < N
+    assert run(ldb=72) == MISALIGNED
+    assert run(B=P2 + 8) == MISALIGNED
+    assert run(ws=0) == WORKSPACE
+    assert run(wsb=need - 16) == WORKSPACE
+    assert run(ws=P3 + (1 << 20) + 8) == MISALIGNED
+    assert run(K=120) == NOT_SUPPORTED
 
 
 def test_run_split_workspace_validation(lib):
