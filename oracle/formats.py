@@ -1,4 +1,4 @@
-"""e4m3fn, e5m2 and E8M0 codes: decode tables and the round-to-nearest-even encoders.
+"""e4m3fn, e5m2, e2m1 and E8M0 codes: decode tables and the round-to-nearest-even encoders.
 
 TEST INFRASTRUCTURE (see the package docstring).
 
@@ -15,6 +15,15 @@ E5M2 is the second FP8 format the JAX/Triton Blackwell FP8 GEMM post names
 5 exponent bits with bias 15, 2 mantissa bits, subnormals when the exponent
 field is 0, and the IEEE-like specials S.11111.00 = infinity and S.11111.xx
 (xx != 0) = NaN, so the largest finite magnitude is 1.75 * 2^15 = 57344.
+
+E2M1 (FP4) is the 4-bit element format of MXFP4, one of the narrow formats
+"Hopper/Blackwell architecture features" §12.6.1 lists for the new tensor
+cores (FP4 / FP6 next to FP8, with micro-scaling); §12.6.4 lists FP4 GEMMs as
+experimental.  The OCP MX v1.0 layout: 1 sign bit, 2 exponent bits with bias
+1, 1 mantissa bit, a subnormal when the exponent field is 0, no infinity and
+no NaN, so the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.  A code here is the
+4-bit pattern S.EE.M in the low bits of a byte (sign = bit 3); two codes share
+a byte when packed (see ``pack_fp4``).
 
 E8M0 is the MX shared-scale format ("Hopper/Blackwell architecture features"
 §12.6.1 names MXFP8): an 8-bit biased exponent, value 2^(code-127), with 0xFF
@@ -60,18 +69,33 @@ def _e5m2_value(code: int) -> float:
     return -mag if s else mag
 
 
+def _e2m1_value(code: int) -> float:
+    """Value of one 4-bit e2m1 code from its bit fields (OCP MX FP4 definition)."""
+    s = (code >> 3) & 1
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        mag = math.ldexp(m, -1)             # subnormal: 0.m * 2^(1-1) = m * 2^-1
+    else:
+        mag = math.ldexp(2 + m, e - 1 - 1)  # normal: 1.m * 2^(e-1) = (2+m) * 2^(e-2)
+    return -mag if s else mag
+
+
 def _e8m0_value(code: int) -> float:
     return math.nan if code == 0xFF else math.ldexp(1.0, code - 127)
 
 
 E4M3_DECODE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
 E5M2_DECODE = np.array([_e5m2_value(c) for c in range(256)], dtype=np.float64)
+E2M1_MAX = 6.0
+E2M1_DECODE = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
 E8M0_DECODE = np.array([_e8m0_value(c) for c in range(256)], dtype=np.float64)
 
 # Non-negative finite magnitudes, indexed by code (strictly increasing):
 # e4m3fn 0x00..0x7E, e5m2 0x00..0x7B.
 _POS_MAGS = E4M3_DECODE[:0x7F].copy()
 _POS_MAGS_E5M2 = E5M2_DECODE[:0x7C].copy()
+_POS_MAGS_E2M1 = E2M1_DECODE[:0x8].copy()          # e2m1 0x0..0x7
 
 
 def decode_e4m3(q: np.ndarray) -> np.ndarray:
@@ -115,12 +139,14 @@ def encode_e4m3(v: np.ndarray) -> np.ndarray:
     return (code | sign).astype(np.uint8)
 
 
-def _encode_by_table(v: np.ndarray, mags: np.ndarray, fmax: float, nan_code: int) -> np.ndarray:
+def _encode_by_table(v: np.ndarray, mags: np.ndarray, fmax: float, nan_code: int,
+                     sign_bit: int = 7) -> np.ndarray:
     """Nearest code among the non-negative finite magnitudes `mags` (code = index),
-    ties to the even code, saturating at fmax, sign copied from v."""
+    ties to the even code, saturating at fmax, sign copied from v into bit
+    `sign_bit`."""
     v = np.asarray(v)
     a = np.abs(v).astype(np.float64)
-    sign = np.signbit(v).astype(np.uint8) << 7
+    sign = np.signbit(v).astype(np.uint8) << sign_bit
     top = len(mags) - 1
     lo = np.searchsorted(mags, a, side="right") - 1
     lo = np.clip(lo, 0, top)
@@ -145,11 +171,47 @@ def encode_e5m2(v: np.ndarray) -> np.ndarray:
     return _encode_by_table(v, _POS_MAGS_E5M2, E5M2_MAX, E5M2_NAN_CODE)
 
 
+def decode_e2m1(q: np.ndarray) -> np.ndarray:
+    """float64 values of 4-bit e2m1 codes held one per uint8 (exact)."""
+    return E2M1_DECODE[np.asarray(q, dtype=np.uint8) & 0xF]
+
+
+def encode_e2m1(v: np.ndarray) -> np.ndarray:
+    """Nearest e2m1 code to each value (one 4-bit code per uint8), ties to the
+    even code, saturating.
+
+    The definition of ``encode_e4m3`` over the 8 non-negative e2m1 magnitudes
+    0, 0.5, 1, 1.5, 2, 3, 4, 6: magnitudes at or above 6 saturate to 6 (code
+    0x7), the sign goes to bit 3 (so -0.0 and small negatives give 0x8).  The
+    format has no NaN; NaN inputs are out of contract (they give 0x7 | sign).
+    """
+    return _encode_by_table(v, _POS_MAGS_E2M1, E2M1_MAX, 0x7, sign_bit=3)
+
+
+def pack_fp4(codes: np.ndarray) -> np.ndarray:
+    """Two 4-bit codes per byte along the last axis: element 2i in bits 0-3 and
+    element 2i+1 in bits 4-7 (the first element in the low nibble)."""
+    c = np.asarray(codes, dtype=np.uint8) & 0xF
+    if c.shape[-1] % 2:
+        raise ValueError("an even number of 4-bit codes per row is needed")
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_fp4(packed: np.ndarray) -> np.ndarray:
+    """Inverse of ``pack_fp4``: one 4-bit code per uint8, twice as many columns."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
 # Element formats by name: decode, encode, largest finite magnitude and the
 # exponent of that magnitude (emax, used by the MX scale rule).
 FORMATS = {
     "e4m3": {"decode": decode_e4m3, "encode": encode_e4m3, "max": E4M3_MAX, "emax": 8},
     "e5m2": {"decode": decode_e5m2, "encode": encode_e5m2, "max": E5M2_MAX, "emax": 15},
+    "e2m1": {"decode": decode_e2m1, "encode": encode_e2m1, "max": E2M1_MAX, "emax": 2},
 }
 
 

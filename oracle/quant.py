@@ -24,6 +24,12 @@ The same rules quantise to e5m2 (the JAX/Triton Blackwell FP8 GEMM post's
 second FP8 format) with its largest magnitude 57344 in place of 448 and its
 largest exponent 15 in place of 8 (the OCP MX rule for MXFP8 E5M2 elements).
 
+MXFP4 (the FP4 micro-scaled format "Hopper/Blackwell architecture features"
+§12.6.1 lists) takes the MX rule with e2m1 elements: largest magnitude 6, whose
+exponent is 2, so e = floor(log2 amax) - 2; values in (6, 8) saturate to 6.
+Its codes are returned one per uint8 (``formats.pack_fp4`` gives the packed
+two-per-byte layout); per-tensor and row-wise FP4 are not defined here.
+
 Inputs are rows x K float32 arrays with K contiguous; a column-major B is
 passed as its N x K transpose, so "row" always means the outer index.
 """
@@ -36,6 +42,7 @@ from .formats import FORMATS
 MX_BLOCK = 32
 E4M3_EMAX = 8          # floor(log2(448))
 E5M2_EMAX = 15         # floor(log2(57344))
+E2M1_EMAX = 2          # floor(log2(6))
 
 
 def _scale_from_amax(amax: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
@@ -90,7 +97,10 @@ def quantize_mx(x: np.ndarray, fmt: str = "e4m3"):
 
 
 def quantize(x: np.ndarray, mode: str, fmt: str = "e4m3"):
-    """Dispatch on mode name: "tensor" | "rowwise" | "mx32"; fmt "e4m3" | "e5m2"."""
+    """Dispatch on mode name: "tensor" | "rowwise" | "mx32"; fmt "e4m3" | "e5m2",
+    or "e2m1" with "mx32" only."""
+    if fmt == "e2m1" and mode != "mx32":
+        raise ValueError("e2m1 elements are defined with MX block scales only")
     if mode == "tensor":
         return quantize_tensor(x, fmt)
     if mode == "rowwise":
