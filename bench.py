@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 from workloads import WORKLOADS, dense_inputs, grouped_inputs  # noqa: E402
 
 PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 MFMA peak (no sparsity)
+PEAK_FP4_TFLOPS = 10100.0         # MI355X dense FP4 (MXFP4) MFMA peak
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
 DEFAULT_WORKLOAD = "mx8192"
 # the pages' own figures, measured on other hardware: context, not targets
@@ -145,9 +146,10 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: st
     print(json.dumps(rec, indent=1))
 
 
-def gemm_bytes(w) -> int:
-    """Algorithmic bytes of one GEMM launch: A + B codes, scales, C."""
-    mb = w.M * w.K + (w.groups or 1) * w.N * w.K
+def gemm_bytes(w, code_bytes: float = 1.0) -> int:
+    """Algorithmic bytes of one GEMM launch: A + B codes (code_bytes per element:
+    1, or 0.5 for FP4), scales, C."""
+    mb = int((w.M * w.K + (w.groups or 1) * w.N * w.K) * code_bytes)
     if w.mode == "mx32":
         mb += (w.M + (w.groups or 1) * w.N) * (w.K // 32)
     elif w.mode == "rowwise":
@@ -157,9 +159,10 @@ def gemm_bytes(w) -> int:
     return mb + 2 * w.M * w.N
 
 
-def cpu_baseline(w, rows: int):
-    """Oracle on a bounded sample: quantise `rows` rows of A and of B, then the
-    float64 GEMM reference of that rows x rows x K block (value and sum|a*b|)."""
+def cpu_baseline(w, rows: int, fmt: str = "e4m3"):
+    """Oracle on a bounded sample: quantise `rows` rows of A and of B (element
+    format fmt), then the float64 GEMM reference of that rows x rows x K block
+    (value and sum|a*b|)."""
     import numpy as np
     import oracle as O
     from oracle import quant as Q
@@ -176,17 +179,15 @@ def cpu_baseline(w, rows: int):
         Bs = B[:rows]
     As = A[:rows]
     t0 = time.perf_counter()
-    qa, sa = Q.quantize(As, w.mode)
-    qb, sb = Q.quantize(Bs, w.mode)
-    if w.mode == "tensor":   # the sample's own scales; the work is the same
-        pass
-    O.gemm_reference(qa, sa, qb, sb, w.mode)
+    qa, sa = Q.quantize(As, w.mode, fmt)
+    qb, sb = Q.quantize(Bs, w.mode, fmt)
+    O.gemm_reference(qa, sa, qb, sb, w.mode, fmt_a=fmt, fmt_b=fmt)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * rows * w.K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{rows} rows of A and {rows} columns of B (K={w.K}): quantise both, "
-                      f"float64 GEMM reference with sum|a*b|; {dt:.2f} s"}
+            "sample": f"{rows} rows of A and {rows} columns of B (K={w.K}, {fmt}): quantise "
+                      f"both, float64 GEMM reference with sum|a*b|; {dt:.2f} s"}
 
 
 def main():
@@ -196,7 +197,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--formats", default="e4m3,e4m3", metavar="A,B",
-                    help="element formats of the A and B codes (e4m3 or e5m2; dense only)")
+                    help="element formats of the A and B codes (e4m3 or e5m2, or e2m1,e2m1 for "
+                         "MXFP4 with the mx32 workload; dense only)")
     ap.add_argument("--epilogue", default="none", choices=["none", "bias", "bias+relu",
                                                            "bias+gelu", "bias+silu"],
                     help="fused epilogue of the GEMM (dense only)")
@@ -230,6 +232,12 @@ def main():
     use_bias = args.epilogue != "none"
     if w.groups and (args.formats != "e4m3,e4m3" or use_bias):
         raise SystemExit("--formats and --epilogue apply to the dense workloads")
+    fp4 = "e2m1" in (fmt_a, fmt_b)
+    if fp4 and (fmt_a != fmt_b or w.mode != "mx32"):
+        raise SystemExit("e2m1 (MXFP4) runs as e2m1,e2m1 on an mx32 workload")
+    kq = w.K // 2 if fp4 else w.K            # code bytes per row
+    peak = PEAK_FP4_TFLOPS if fp4 else PEAK_FP8_TFLOPS
+    code_bytes = 0.5 if fp4 else 1.0
     dev = torch.device("cuda:0")
     F.load_library()
     log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} mode={w.mode} out={w.out} groups={w.groups}")
@@ -251,8 +259,8 @@ def main():
     rows_b = Bd.shape[0]
 
     # ---- outputs and workspaces allocated once ---------------------------------
-    qa = torch.empty((w.M, w.K), dtype=torch.uint8, device=dev)
-    qb = torch.empty((rows_b, w.K), dtype=torch.uint8, device=dev)
+    qa = torch.empty((w.M, kq), dtype=torch.uint8, device=dev)
+    qb = torch.empty((rows_b, kq), dtype=torch.uint8, device=dev)
     if w.mode == "tensor":
         sa = torch.empty(1, dtype=torch.float32, device=dev)
         sb = torch.empty(1, dtype=torch.float32, device=dev)
@@ -323,8 +331,9 @@ def main():
     flops = w.flops
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (gemm_ms * 1e-3) / 1e12
-    quant_bytes_a = w.M * w.K * 5 + (w.M * w.K // 32 if w.mode == "mx32" else 4 * w.M)
-    quant_bytes_b = rows_b * w.K * 5 + (rows_b * w.K // 32 if w.mode == "mx32" else 4 * rows_b)
+    quant_bytes_a = w.M * w.K * 4 + w.M * kq + (w.M * w.K // 32 if w.mode == "mx32" else 4 * w.M)
+    quant_bytes_b = rows_b * w.K * 4 + rows_b * kq + (rows_b * w.K // 32 if w.mode == "mx32"
+                                                      else 4 * rows_b)
     if w.mode == "tensor":  # the amax pass reads the input once more
         quant_bytes_a += w.M * w.K * 4
         quant_bytes_b += rows_b * w.K * 4
@@ -332,10 +341,11 @@ def main():
     # HBM-bound shapes (arithmetic intensity below the MFMA/HBM ridge): the roofline
     # is bytes over time; a cold-cache rate is measured as well, cycling the GEMM
     # over enough distinct operand copies (>= 512 MiB) that none is cache resident
-    hbm_bound = flops / gemm_bytes(w) < PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    gbytes = gemm_bytes(w, code_bytes)
+    hbm_bound = flops / gbytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     cold = None
-    if hbm_bound and not w.groups and rows_b * w.K >= (4 << 20):
-        nsets = max(2, -(-(512 << 20) // (rows_b * w.K)))
+    if hbm_bound and not w.groups and rows_b * kq >= (4 << 20):
+        nsets = max(2, -(-(512 << 20) // (rows_b * kq)))
         qbs = [qb.clone() for _ in range(nsets)]
         qas = [qa.clone() for _ in range(nsets)]
         for i in range(nsets):
@@ -352,7 +362,7 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         cold_ms = e0.elapsed_time(e1) / (reps * nsets)
-        cold = {"ms": round(cold_ms, 5), "gbs_algorithmic": round(gemm_bytes(w) / (cold_ms * 1e-3) / 1e9, 1),
+        cold = {"ms": round(cold_ms, 5), "gbs_algorithmic": round(gbytes / (cold_ms * 1e-3) / 1e9, 1),
                 "operand_sets": nsets, "note": "back-to-back launches over distinct operand copies"}
         del qbs, qas
         log(f"cold-cache GEMM: {cold}")
@@ -373,13 +383,13 @@ def main():
             ms = r0.elapsed_time(r1) / (reps * sets)
             del bufs
             return {"bytes": nbytes, "ms": round(ms, 5), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
-        gb = gemm_bytes(w) // 8 * 8
+        gb = gbytes // 8 * 8
         cold["hbm_read_context"] = {
             "kernel": "torch sum over int64 words (a plain device read)",
             "same_bytes": read_rate(gb, max(2, -(-(512 << 20) // gb)), 4),
             "one_gib": read_rate(1 << 30, 2, 3)}
         log(f"plain read context: {cold['hbm_read_context']}")
-    gemm_gbs = gemm_bytes(w) / (gemm_ms * 1e-3) / 1e9
+    gemm_gbs = gbytes / (gemm_ms * 1e-3) / 1e9
     # the committed counter summaries are of the default e4m3 GEMM without epilogue
     default_variant = args.formats == "e4m3,e4m3" and not use_bias
     traffic = measured_traffic(w.name) if default_variant else None
@@ -388,8 +398,8 @@ def main():
                     "unit": "GB/s", "frac": round(gemm_gbs / PEAK_HBM_GBS, 4),
                     "traffic": traffic}
     else:
-        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                     "traffic": traffic}
 
     result = {
@@ -403,7 +413,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3",
+        "dtype": fmt_a if fmt_a == fmt_b else f"{fmt_a}x{fmt_b}",
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "scale": w.mode,
                    "out": w.out, "groups": w.groups, "formats": [fmt_a, fmt_b],
@@ -430,7 +440,7 @@ def main():
     if not args.no_cpu_baseline:
         del Ad, Bd
         log("timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_rows, fmt_a if fmt_a == fmt_b else "e4m3")
     print(json.dumps(result), flush=True)
 
 

@@ -37,7 +37,7 @@ _HEADER = os.path.join(os.path.dirname(_PKG), "include", "fp8gemm.h")
 
 SCALE_MODES = {"tensor": 0, "rowwise": 1, "mx32": 2}
 OUT_DTYPES = {"f16": 0, "bf16": 1}
-FORMATS = {"e4m3": 0, "e5m2": 1}
+FORMATS = {"e4m3": 0, "e5m2": 1, "e2m1": 4}   # e2m1: FP4, two codes per byte, MX only
 ACTIVATIONS = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
 
 _STATUS_NAMES = {
@@ -240,15 +240,17 @@ def quantize(x, mode: str = "tensor", out=None, scales=None, workspace=None,
     """fp32 [R, K] CUDA tensor -> (codes uint8 [R, K], scales).
 
     scales: float32 [1] (tensor), float32 [R] (rowwise) or uint8 [R, K/32] (mx32);
-    fmt: element format of the codes, "e4m3" or "e5m2".
+    fmt: element format of the codes, "e4m3", "e5m2" or "e2m1" (FP4 with mx32:
+    codes packed two per byte, uint8 [R, K/2]).
     """
     torch = _torch()
     _require_cuda(x, "x", torch.float32, 2)
     m = SCALE_MODES[mode]
     R, K = x.shape
     if out is None:
-        ldq = (K + 15) // 16 * 16
-        out = torch.empty((R, ldq), dtype=torch.uint8, device=x.device)[:, :K]
+        kb = K // 2 if fmt == "e2m1" else K
+        ldq = (kb + 15) // 16 * 16
+        out = torch.empty((R, ldq), dtype=torch.uint8, device=x.device)[:, :kb]
     if scales is None:
         if mode == "tensor":
             scales = torch.empty(1, dtype=torch.float32, device=x.device)
@@ -272,8 +274,9 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
 
     qb is [N, K] (K contiguous, b_layout "nk") or [K, N] (N contiguous, "kn"; its
     MX codes sb then [K/32, N]); fmt_a / fmt_b: element formats of the codes
-    ("e4m3" or "e5m2"); bias: float32 [N] CUDA tensor or None; activation: "none",
-    "relu", "gelu" or "silu".
+    ("e4m3" or "e5m2"; or "e2m1" for both, FP4 packed two per byte so that qa is
+    [M, K/2] and qb [N, K/2], mode "mx32"); bias: float32 [N] CUDA tensor or None;
+    activation: "none", "relu", "gelu" or "silu".
     """
     torch = _torch()
     _require_cuda(qa, "qa", torch.uint8, 2)
@@ -283,6 +286,9 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
         Kb, N = qb.shape
     else:
         N, Kb = qb.shape
+    fp4 = "e2m1" in (fmt_a, fmt_b)
+    if fp4:                                   # packed codes: K counts elements
+        K, Kb = 2 * K, 2 * Kb
     if K != Kb:
         raise ValueError("qa and qb must share K")
     tdt = torch.float16 if out_dtype == "f16" else torch.bfloat16
@@ -291,7 +297,7 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
         out = torch.empty((M, ldc), dtype=tdt, device=qa.device)[:, :N]
     m = SCALE_MODES[mode]
     kn = b_layout == "kn"
-    need = (fp8gemm_workspace_size_kn if kn else fp8gemm_workspace_size)(M, N, K, m)
+    need = 0 if fp4 else (fp8gemm_workspace_size_kn if kn else fp8gemm_workspace_size)(M, N, K, m)
     if need and workspace is None:
         workspace = gemm_workspace(qa.device, need)
     if bias is not None:

@@ -26,7 +26,9 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool valid_mode(int mode) { return mode == kTensor || mode == kRowwise || mode == kMx32; }
 bool valid_out(int out) { return out == FP8GEMM_OUT_F16 || out == FP8GEMM_OUT_BF16; }
-bool valid_format(int f) { return f == FP8GEMM_FORMAT_E4M3 || f == FP8GEMM_FORMAT_E5M2; }
+bool valid_format(int f) {
+  return f == FP8GEMM_FORMAT_E4M3 || f == FP8GEMM_FORMAT_E5M2 || f == FP8GEMM_FORMAT_E2M1;
+}
 bool valid_act(int a) {
   return a == FP8GEMM_ACT_NONE || a == FP8GEMM_ACT_RELU || a == FP8GEMM_ACT_GELU ||
          a == FP8GEMM_ACT_SILU;
@@ -36,16 +38,18 @@ fp8gemm_status from_hip(hipError_t e) {
   return e == hipSuccess ? FP8GEMM_SUCCESS : FP8GEMM_ERROR_LAUNCH;
 }
 
-// Checks shared by the dense and grouped GEMM (M is the number of A rows).
+// Checks shared by the dense and grouped GEMM (M is the number of A rows; per_byte
+// is the number of codes per operand byte: 1, or 2 for FP4).
 fp8gemm_status check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                                  const uint8_t* B, int64_t ldb, int mode, const void* scale_a,
-                                 const void* scale_b, const void* C, int64_t ldc, int out) {
+                                 const void* scale_b, const void* C, int64_t ldc, int out,
+                                 int per_byte = 1) {
   if (!A || !B || !C || !scale_a || !scale_b) return FP8GEMM_ERROR_INVALID_VALUE;
-  if (lda < K || ldb < K || ldc < N) return FP8GEMM_ERROR_INVALID_VALUE;
+  if (lda * per_byte < K || ldb * per_byte < K || ldc < N) return FP8GEMM_ERROR_INVALID_VALUE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim || lda > kMaxDim || ldb > kMaxDim ||
       ldc > kMaxDim)
     return FP8GEMM_ERROR_NOT_SUPPORTED;
-  if (K % 16 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if (K % (16 * per_byte) != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (mode == kMx32 && K % 32 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
   // the grid is one workgroup per 128 x 128 tile at most: keep it below 2^31
   if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return FP8GEMM_ERROR_NOT_SUPPORTED;
@@ -78,9 +82,11 @@ fp8gemm_status fp8gemm_quantize_ex(const float* x, int64_t rows, int64_t k, int6
                                    void* workspace, size_t workspace_bytes, void* stream) {
   if (!valid_mode(mode) || !valid_format(format) || rows < 0 || k <= 0)
     return FP8GEMM_ERROR_INVALID_VALUE;
+  const bool fp4 = format == FP8GEMM_FORMAT_E2M1;
+  if (fp4 && mode != kMx32) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (rows == 0) return FP8GEMM_SUCCESS;
   if (!x || !q || !scales) return FP8GEMM_ERROR_INVALID_VALUE;
-  if (ldx < k || ldq < k) return FP8GEMM_ERROR_INVALID_VALUE;
+  if (ldx < k || ldq * (fp4 ? 2 : 1) < k) return FP8GEMM_ERROR_INVALID_VALUE;
   if (k % 16 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (mode == kMx32 && k % 32 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
   // 32-bit unit indexing inside the kernels: at most 2^32 - 1 elements per call
@@ -127,18 +133,21 @@ fp8gemm_status fp8gemm_run_ex(int64_t M, int64_t N, int64_t K, const uint8_t* A,
   if (!valid_mode(mode) || !valid_out(out_dtype) || !valid_format(a_format) ||
       !valid_format(b_format) || !valid_act(activation) || M < 0 || N < 0 || K <= 0)
     return FP8GEMM_ERROR_INVALID_VALUE;
+  // FP4 pairs with FP4 only, and only with MX block scales
+  const bool fp4 = a_format == FP8GEMM_FORMAT_E2M1 || b_format == FP8GEMM_FORMAT_E2M1;
+  if (fp4 && (a_format != b_format || mode != kMx32)) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (M == 0 || N == 0) return FP8GEMM_SUCCESS;
-  fp8gemm_status st =
-      check_gemm_common(M, N, K, A, lda, B, ldb, mode, scale_a, scale_b, C, ldc, out_dtype);
+  fp8gemm_status st = check_gemm_common(M, N, K, A, lda, B, ldb, mode, scale_a, scale_b, C, ldc,
+                                        out_dtype, fp4 ? 2 : 1);
   if (st != FP8GEMM_SUCCESS) return st;
-  const size_t need = fp8gemm_workspace_size(M, N, K, mode);
+  const size_t need = fp4 ? 0 : fp8gemm_workspace_size(M, N, K, mode);
   if (need > 0 && (!workspace || workspace_bytes < need)) return FP8GEMM_ERROR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return FP8GEMM_ERROR_MISALIGNED;
 
   fp8gemm::GemmProblem p;
   p.M = (int)M;
   p.N = (int)N;
-  p.K = (int)K;
+  p.K = (int)(fp4 ? K / 2 : K);        // FP4: the kernels walk K in bytes
   p.A = A;
   p.lda = lda;
   p.B = B;
@@ -152,6 +161,7 @@ fp8gemm_status fp8gemm_run_ex(int64_t M, int64_t N, int64_t K, const uint8_t* A,
   p.bias = bias;
   p.act = activation;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fp4) return from_hip(fp8gemm::launch_gemm_e2m1_e2m1(p, mode, out_dtype, s));
   if (a_format == FP8GEMM_FORMAT_E5M2 && b_format == FP8GEMM_FORMAT_E5M2)
     return from_hip(fp8gemm::launch_gemm_e5m2_e5m2(p, mode, out_dtype, s));
   if (a_format == FP8GEMM_FORMAT_E5M2)
@@ -186,6 +196,8 @@ fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A,
   if (!valid_mode(mode) || !valid_out(out_dtype) || !valid_format(a_format) ||
       !valid_format(b_format) || !valid_act(activation) || M < 0 || N < 0 || K <= 0)
     return FP8GEMM_ERROR_INVALID_VALUE;
+  if (a_format == FP8GEMM_FORMAT_E2M1 || b_format == FP8GEMM_FORMAT_E2M1)
+    return FP8GEMM_ERROR_NOT_SUPPORTED;          // no transposing copy of packed FP4
   if (M == 0 || N == 0) return FP8GEMM_SUCCESS;
   if (!B || !scale_b) return FP8GEMM_ERROR_INVALID_VALUE;
   if (ldb < N) return FP8GEMM_ERROR_INVALID_VALUE;

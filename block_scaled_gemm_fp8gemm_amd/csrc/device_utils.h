@@ -11,6 +11,9 @@
 //     largest finite magnitude is 57344.  v_cvt_pk_bf8_f32 converts onto it, and
 //     values are clamped to [-57344, 57344] first, so the quantisers saturate
 //     instead of producing infinity.
+//   * e2m1 (FP4, the MXFP4 element; OCP MX v1.0) has magnitudes 0, 0.5, 1, 1.5, 2,
+//     3, 4, 6 and no infinity or NaN; it is encoded here in software (round to a
+//     multiple of the binade's spacing with v_rndne, saturating at 6).
 //   * E8M0 code c encodes 2^(c-127).
 #pragma once
 
@@ -46,6 +49,25 @@ __device__ __forceinline__ uint32_t encode4_e5m2(float a, float b, float c, floa
   return (uint32_t)w;
 }
 
+// One fp32 value -> e2m1 code (bits 0-3): round to nearest even onto the grid of
+// spacing 0.5 below 2, 1 below 4 and 2 above (a power-of-two scaling and rintf,
+// both exact), saturating at 6; the sign goes to bit 3, so -0 gives 0x8.
+__device__ __forceinline__ uint32_t encode_e2m1(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 0x8u;
+  const float a = fabsf(v);
+  const float inv = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);   // 1 / spacing
+  const float r = fminf(rintf(a * inv) / inv, 6.0f);
+  // 0, .5, 1, 1.5 -> 0..3;  2, 3 -> 4, 5;  4 -> 6;  6 -> 7
+  const uint32_t mag = r < 2.0f ? (uint32_t)(r * 2.0f)
+                                : (r < 4.0f ? (uint32_t)r + 2u : (r < 6.0f ? 6u : 7u));
+  return sign | mag;
+}
+
+// Four fp32 values -> four e2m1 codes in 16 bits, the first in bits 0-3.
+__device__ __forceinline__ uint32_t encode4_e2m1(float a, float b, float c, float d) {
+  return encode_e2m1(a) | (encode_e2m1(b) << 4) | (encode_e2m1(c) << 8) | (encode_e2m1(d) << 12);
+}
+
 template <int FMT>
 __device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
   return FMT == kE5M2 ? encode4_e5m2(a, b, c, d) : encode4_e4m3(a, b, c, d);
@@ -58,13 +80,13 @@ constexpr float elem_max() {
 
 // E8M0 code of a 32-element block from its largest magnitude: floor(log2 amax)
 // read from the binary32 exponent field, minus the element format's largest
-// exponent (8 for e4m3, 15 for e5m2), biased by 127 and clamped to [0, 254]; an
+// exponent (8 for e4m3, 15 for e5m2, 2 for e2m1), biased by 127 and clamped to [0, 254]; an
 // all-zero block gets 127.
 template <int FMT = kE4M3>
 __device__ __forceinline__ uint32_t mx_code_from_amax(float amax) {
   if (amax == 0.0f) return 127u;
   int ef = (int)(__float_as_uint(amax) >> 23);  // amax >= 0: no sign bit
-  int code = ef - (FMT == kE5M2 ? 15 : 8);
+  int code = ef - (FMT == kE5M2 ? 15 : FMT == kE2M1 ? 2 : 8);
   return (uint32_t)(code < 0 ? 0 : code);
 }
 

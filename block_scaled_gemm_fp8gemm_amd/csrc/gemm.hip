@@ -34,14 +34,14 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void gemm_kernel(G
   op.ldb = p.ldb;
   op.b_rows = p.N - n0;
   op.K = p.K;
-  op.sld = p.K / 32;
+  op.sld = p.K / kBlkBytes;
   const float* fsa = static_cast<const float*>(p.scale_a);
   const float* fsb = static_cast<const float*>(p.scale_b);
   op.sa = op.sb = nullptr;
   op.ra = op.rb = nullptr;
   if (MODE == kMx32) {
-    op.sa = static_cast<const uint8_t*>(p.scale_a) + (int64_t)m0 * (p.K / 32);
-    op.sb = static_cast<const uint8_t*>(p.scale_b) + (int64_t)n0 * (p.K / 32);
+    op.sa = static_cast<const uint8_t*>(p.scale_a) + (int64_t)m0 * op.sld;
+    op.sb = static_cast<const uint8_t*>(p.scale_b) + (int64_t)n0 * op.sld;
   }
   if (MODE == kRowwise) {
     op.ra = fsa + m0;
@@ -78,7 +78,7 @@ struct DenseTiles {
     op.ldb = p.ldb;
     op.b_rows = p.N - n0;
     op.K = p.K;
-    op.sld = p.K / 32;
+    op.sld = p.K / kBlkBytes;
     op.sa = op.sb = nullptr;
     op.ra = op.rb = nullptr;
     if (MODE == kMx32) {
@@ -180,6 +180,19 @@ hipError_t launch_persistent(const GemmProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// FP4 operands (K counted in bytes): the large tile only when every tile is an
+// interior one (its edge tiles would read their codes into registers and spill),
+// and one tile per workgroup (no persistent stream).
+template <int MODE, typename OutT, bool FUSED>
+hipError_t launch_mode_f4(const GemmProblem& p, hipStream_t stream) {
+  const int64_t big_tiles = (int64_t)((p.M + Big::BM - 1) / Big::BM) * ((p.N + Big::BN - 1) / Big::BN);
+  const bool interior = p.M % Big::BM == 0 && p.N % Big::BN == 0 && p.K % (16 * kBlkBytes) == 0 &&
+                        (int64_t)Big::BM * p.lda + p.K < ((int64_t)1 << 31) &&
+                        (int64_t)Big::BN * p.ldb + p.K < ((int64_t)1 << 31);
+  if (big_tiles >= 256 * Big::kWgPerCu && interior) return launch_cfg<Big, MODE, OutT, FUSED>(p, stream);
+  return launch_cfg<Mid, MODE, OutT, FUSED>(p, stream);
+}
+
 template <int MODE, typename OutT, bool FUSED>
 hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
   // Large tiles when they still give at least one tile per CU; otherwise smaller
@@ -268,14 +281,14 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void splitk_kernel(GemmProblem p,
   op.ldb = p.ldb;
   op.b_rows = p.N - n0;
   op.K = kslice;
-  op.sld = p.K / 32;
+  op.sld = p.K / kBlkBytes;
   const float* fsa = static_cast<const float*>(p.scale_a);
   const float* fsb = static_cast<const float*>(p.scale_b);
   op.sa = op.sb = nullptr;
   op.ra = op.rb = nullptr;
   if (MODE == kMx32) {
-    op.sa = static_cast<const uint8_t*>(p.scale_a) + (int64_t)m0 * op.sld + k0 / 32;
-    op.sb = static_cast<const uint8_t*>(p.scale_b) + (int64_t)n0 * op.sld + k0 / 32;
+    op.sa = static_cast<const uint8_t*>(p.scale_a) + (int64_t)m0 * op.sld + k0 / kBlkBytes;
+    op.sb = static_cast<const uint8_t*>(p.scale_b) + (int64_t)n0 * op.sld + k0 / kBlkBytes;
   }
   if (MODE == kRowwise) {
     op.ra = fsa + m0;
@@ -382,9 +395,13 @@ hipError_t launch_split(const GemmProblem& p, const SplitPlan& plan, hipStream_t
 
 template <int MODE, typename OutT, bool FUSED>
 hipError_t launch_plan(const GemmProblem& p, hipStream_t stream) {
-  const SplitPlan plan = plan_split(p.M, p.N, p.K, MODE);
-  if (plan.splits > 1) return launch_split<MODE, OutT, FUSED>(p, plan, stream);
-  return launch_mode<MODE, OutT, FUSED>(p, stream);
+  if constexpr (kF4) {
+    return launch_mode_f4<MODE, OutT, FUSED>(p, stream);      // no split-K for FP4
+  } else {
+    const SplitPlan plan = plan_split(p.M, p.N, p.K, MODE);
+    if (plan.splits > 1) return launch_split<MODE, OutT, FUSED>(p, plan, stream);
+    return launch_mode<MODE, OutT, FUSED>(p, stream);
+  }
 }
 
 // kernels with the fused bias / activation epilogue only when it is asked for
@@ -413,9 +430,17 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int mode) {
 #define FP8GEMM_LAUNCH_NAME launch_gemm_e4m3_e5m2
 #elif FP8GEMM_FMT_A == 1 && FP8GEMM_FMT_B == 0
 #define FP8GEMM_LAUNCH_NAME launch_gemm_e5m2_e4m3
+#elif FP8GEMM_FMT_A == 4 && FP8GEMM_FMT_B == 4
+#define FP8GEMM_LAUNCH_NAME launch_gemm_e2m1_e2m1
 #endif
 
 hipError_t FP8GEMM_LAUNCH_NAME(const GemmProblem& p, int mode, int out, hipStream_t stream) {
+#if FP8GEMM_FMT_A == 4
+  // MXFP4: E8M0 block scales only; K, lda and ldb count bytes (two codes each)
+  if (mode != kMx32) return hipErrorInvalidValue;
+  if (out == kF16) return launch_any<kMx32, _Float16>(p, stream);
+  return launch_any<kMx32, __bf16>(p, stream);
+#else
   if (out == kF16) {
     if (mode == kTensor) return launch_any<kTensor, _Float16>(p, stream);
     if (mode == kRowwise) return launch_any<kRowwise, _Float16>(p, stream);
@@ -424,6 +449,7 @@ hipError_t FP8GEMM_LAUNCH_NAME(const GemmProblem& p, int mode, int out, hipStrea
   if (mode == kTensor) return launch_any<kTensor, __bf16>(p, stream);
   if (mode == kRowwise) return launch_any<kRowwise, __bf16>(p, stream);
   return launch_any<kMx32, __bf16>(p, stream);
+#endif
 }
 
 }  // namespace fp8gemm

@@ -73,12 +73,30 @@ inline namespace FP8GEMM_FMT_NS(FP8GEMM_FMT_A, FP8GEMM_FMT_B) {
 
 // operand-format fields of the F8F6F4 MFMA (B is its first operand)
 constexpr int kFmtA = FP8GEMM_FMT_A, kFmtB = FP8GEMM_FMT_B;
+// FP4 (e2m1, format field 4) operands: two codes per byte, so one 64-byte K
+// sub-tile holds 128 K elements and feeds two MFMAs of 64 K.  The instruction
+// takes 16 bytes per lane for FP4 (32 elements of row lane % 32 from 32-K block
+// lane / 32, low nibble first; probed on gfx950), so the two 16-byte chunks a
+// lane reads for an FP8 fragment are exactly the operands of those two MFMAs,
+// and an E8M0 block covers 16 bytes instead of 32.  Only FP4 x FP4 is built.
+constexpr bool kF4 = kFmtA == 4;
+static_assert((kFmtA == 4) == (kFmtB == 4), "FP4 operands pair with FP4 operands only");
+constexpr int kBlkBytes = kF4 ? 16 : 32;     // bytes of one 32-element MX block
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+
+// The 16-byte halves of an FP8 fragment as FP4 operands (the instruction reads
+// the first four registers of an FP4 operand, so no copies are made).
+__device__ __forceinline__ v8i lo16(const v8i& v) {
+  return __builtin_shufflevector(v, v, 0, 1, 2, 3, 0, 1, 2, 3);
+}
+__device__ __forceinline__ v8i hi16(const v8i& v) {
+  return __builtin_shufflevector(v, v, 4, 5, 6, 7, 4, 5, 6, 7);
+}
 
 // BM x BN output tile, WM x WN per wavefront, SLOTS-deep LDS ring, and the number
 // of workgroups meant to share a CU (their waves then share each SIMD, so one
@@ -342,11 +360,13 @@ __device__ __forceinline__ void sched_subtile() {
 // The loop runs an even number of sub-tiles (K tails are zero-filled) and copies
 // past the end re-fetch the last sub-tile, so counts per sub-tile are constant.
 // With K % 128 != 0 the MX codes are read with byte loads and every wait drains
-// all copies (a rarely used, simpler path).
+// all copies (a rarely used, simpler path).  FP4 operands always take that path
+// here (KALIGNED = false): their interior tiles run mainloop_interior.
 template <class Cfg, int MODE, bool KALIGNED>
 __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
                                          v16f (&acc)[Cfg::kFragM][Cfg::kFragN]) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
+  static_assert(!(kF4 && KALIGNED), "FP4 edge tiles read their codes into registers");
   constexpr bool KTAIL = !KALIGNED;
   constexpr bool kMxLds = (MODE == kMx32) && KALIGNED;
   constexpr bool kMxReg = (MODE == kMx32) && !KALIGNED;
@@ -367,7 +387,7 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
   const int h = lane >> 5;
   const int nsub = ((op.K + 127) / 128) * 2;     // even number of 64-K sub-tiles
   const int nvalid = (op.K + Cfg::kBK - 1) / Cfg::kBK;
-  const int nblk = op.K / 32;
+  const int nblk = op.K / kBlkBytes;
 
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -409,18 +429,22 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
 #pragma unroll
     for (int j = 0; j < FN; ++j) b[j] = w[Cfg::BM + brow[j]] >> (8 * h);
   };
-  // codes of sub-tile s straight from global memory (K % 128 != 0): block 2s + h
+  // codes of sub-tile s straight from global memory (K % 128 != 0): block 2s + h.
+  // FP4: blocks 4s + h (first MFMA, bits 0-7) and 4s + 2 + h (second, bits 16-23)
   auto load_reg_codes = [&](int s, uint32_t (&a)[FM], uint32_t (&b)[FN]) {
-    const int blk = 2 * s + h;
+    const int blk = (kF4 ? 4 : 2) * s + h;
+    auto code = [&](const uint8_t* base, int b) { return b < nblk ? (uint32_t)base[b] : 127u; };
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = arow[i] < op.a_rows ? arow[i] : op.a_rows - 1;
-      a[i] = blk < nblk ? op.sa[(int64_t)r * op.sld + blk] : 127u;
+      const uint8_t* row = op.sa + (int64_t)r * op.sld;
+      a[i] = kF4 ? code(row, blk) | (code(row, blk + 2) << 16) : code(row, blk);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int r = brow[j] < op.b_rows ? brow[j] : op.b_rows - 1;
-      b[j] = blk < nblk ? op.sb[(int64_t)r * op.sld + blk] : 127u;
+      const uint8_t* row = op.sb + (int64_t)r * op.sld;
+      b[j] = kF4 ? code(row, blk) | (code(row, blk + 2) << 16) : code(row, blk);
     }
   };
 
@@ -471,7 +495,14 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
 #pragma unroll
     for (int q = 0; q < kMfma; ++q) {
       const int i = q / FN, j = q % FN;
-      if (MODE == kMx32) {
+      if (kF4) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            lo16(fb[j]), lo16(fa[i]), acc[i][j], kFmtB, kFmtA, 0, (int)sb_cur[j], 0,
+            (int)sa_cur[i]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            hi16(fb[j]), hi16(fa[i]), acc[i][j], kFmtB, kFmtA, 0, (int)(sb_cur[j] >> 16), 0,
+            (int)(sa_cur[i] >> 16));
+      } else if (MODE == kMx32) {
         const uint32_t sa = (kMxLds && odd) ? sa_cur[i] >> 16 : sa_cur[i];
         const uint32_t sb = (kMxLds && odd) ? sb_cur[j] >> 16 : sb_cur[j];
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -546,8 +577,12 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
 // slot, K half and fragment folded into the instruction offset (the loop is
 // unrolled over the ring); MX codes are read as single bytes, the form the MFMA
 // takes.
-// Conditions: every row of the tile valid; K % 128 == 0 (MX: K % 512 == 0); the
-// byte span of a tile's rows fits a 32-bit buffer offset.
+// Conditions: every row of the tile valid; K % 128 == 0 (MX: a whole 16-byte code
+// group per row, K % 512 == 0, FP4 K % 256 == 0 bytes); the byte span of a tile's
+// rows fits a 32-bit buffer offset.
+// FP4: a 64-K step of the description below is a 64-byte step of 128 K elements,
+// two MFMAs per fragment pair, each with its own code byte; a code group then
+// covers two K tiles instead of four.
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
@@ -573,7 +608,7 @@ __device__ __forceinline__ int opaque(int v) {
 template <class Cfg, int MODE>
 __device__ __forceinline__ bool interior_tile(const TileOperands& op) {
   return op.a_rows >= Cfg::BM && op.b_rows >= Cfg::BN &&
-         op.K % (MODE == kMx32 ? 512 : 128) == 0 &&
+         op.K % (MODE == kMx32 ? 16 * kBlkBytes : 128) == 0 &&
          (int64_t)Cfg::BM * op.lda + op.K < ((int64_t)1 << 31) &&
          (int64_t)Cfg::BN * op.ldb + op.K < ((int64_t)1 << 31);
 }
@@ -618,8 +653,10 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
   const int h = lane >> 5;
   const int nk = op.K / kRowB;                     // K tiles
-  const int nblk = op.K / 32;
+  const int nblk = op.K / kBlkBytes;
   const int ncode = nblk / 16;                     // 16-byte code groups per row
+  constexpr int kGroupTiles = 16 * kBlkBytes / kRowB;   // K tiles per code group (4, FP4 2)
+  constexpr int kCodes = kF4 ? 2 : 1;              // code bytes per fragment and step
 
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -689,7 +726,8 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
         ba[s][p][c] = opaque(s * kPerBase * kTile + ra + ch);
         bb[s][p][c] = opaque(s * kPerBase * kTile + rb + ch);
       }
-  // MX codes: byte 4 (u % 4) + 2 p + h of the row's 16-byte group u / 4; the
+  // MX codes: byte 4 (u % 4) + 2 p + h of the row's 16-byte group u / 4 (FP4:
+  // bytes 8 (u % 2) + 4 p + 2 c + h of group u / 2, c = the step's MFMA); the
   // group of the current K tile is in buffer `cur`, the next one in `nxt`
   int cur_a = 0, cur_b = 0, nxt_a = 0, nxt_b = 0;
   int cbuf = 0;                                        // buffer index of the current group
@@ -709,20 +747,23 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
     if (d < 2 * FM) rd[d] = rd16(ba[b][p][c] + o + (d >> 1) * 32 * kRowB);
     else rd[d] = rd16(bb[b][p][c] + o + ((d - 2 * FM) >> 1) * 32 * kRowB);
   };
-  uint32_t ca[2][FM], cb[2][FN];                       // codes: [register set][fragment]
+  uint32_t ca[2][kCodes][FM], cb[2][kCodes][FN];      // codes: [register set][MFMA][fragment]
 #pragma unroll
-  for (int z = 0; z < 2; ++z) {
+  for (int z = 0; z < 2; ++z)
 #pragma unroll
-    for (int i = 0; i < FM; ++i) ca[z][i] = 0;
+    for (int c = 0; c < kCodes; ++c) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) cb[z][j] = 0;
-  }
-  // the e-th code byte read of a step: K tile u with u % 4 == q, half p
-  auto read_code = [&](int base_a, int base_b, int q, int p, int e, uint32_t (&a)[FM],
-                       uint32_t (&b)[FN]) {
-    const int off = 4 * q + 2 * p;
-    if (e < FM) a[e] = lds[base_a + off + e * 32 * 16];
-    else b[e - FM] = lds[base_b + off + (e - FM) * 32 * 16];
+      for (int i = 0; i < FM; ++i) ca[z][c][i] = 0;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) cb[z][c][j] = 0;
+    }
+  // the e-th code byte read of a step: K tile u with u % kGroupTiles == q, half p
+  auto read_code = [&](int base_a, int base_b, int q, int p, int e,
+                       uint32_t (&a)[kCodes][FM], uint32_t (&b)[kCodes][FN]) {
+    const int c = e / (FM + FN), f = e % (FM + FN);
+    const int off = kF4 ? 8 * q + 4 * p + 2 * c : 4 * q + 2 * p;
+    if (f < FM) a[c][f] = lds[base_a + off + f * 32 * 16];
+    else b[c][f - FM] = lds[base_b + off + (f - FM) * 32 * 16];
   };
 
   v8i af0[FM], bf0[FN], af1[FM], bf1[FN];
@@ -759,7 +800,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
       bf0[j] = __builtin_shufflevector(rd[2 * FM + 2 * j], rd[2 * FM + 2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
     if (kMx) {
 #pragma unroll
-      for (int e = 0; e < FM + FN; ++e) read_code(cur_a, cur_b, 0, 0, e, ca[0], cb[0]);
+      for (int e = 0; e < kCodes * (FM + FN); ++e) read_code(cur_a, cur_b, 0, 0, e, ca[0], cb[0]);
     }
   }
 
@@ -771,16 +812,21 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   auto step = [&](int t, auto T_c, v8i (&fa)[FM], v8i (&fb)[FN], v8i (&na)[FM], v8i (&nb)[FN]) {
     constexpr int T = decltype(T_c)::value;
     constexpr int p = T & 1, ku = T >> 1;        // half, K tile within the unrolled body
-    constexpr int q = ku & 3, slot = ku % NS;
+    constexpr int q = ku % kGroupTiles, slot = ku % NS;
     constexpr int Z = T & 1;                     // code register set used by this step
     // what step t + 1 reads: same K tile, other half; or the next K tile
-    constexpr int np = p ^ 1, nslot = p ? (ku + 1) % NS : slot, nq = p ? (q + 1) & 3 : q;
+    constexpr int np = p ^ 1, nslot = p ? (ku + 1) % NS : slot;
+    constexpr int nq = p ? (q + 1) % kGroupTiles : q;
     constexpr bool kCodeStep = kMx && p == 1 && q == 0;   // code group copy rides along
     constexpr int kVmem = p ? kLoads + (kCodeStep ? kCodeLoads : 0) : 0;
-    constexpr int kDs = kReads + (kMx ? FM + FN : 0);
+    constexpr int kDs = kReads + (kMx ? kCodes * (FM + FN) : 0);
+    // code bytes of step t + 1 live in the group of K tile (t + 1) / 2
+    constexpr bool kNextGroup = p && q == kGroupTiles - 1;
     // copies allowed in flight once K tile u + 1 has landed: those of K tiles
-    // u + 2 .. u + NS - 1 and a code group issued after K tile u + 1's copies
-    constexpr int kWaitOdd = (NS - 2) * kLoads + ((kMx && q >= 1 && q + 1 <= NS) ? kCodeLoads : 0);
+    // u + 2 .. u + NS - 1 and a code group issued after K tile u + 1's copies,
+    // unless this step reads that group (its last K tile)
+    constexpr int kWaitOdd =
+        (NS - 2) * kLoads + ((kMx && q >= 1 && q + 1 <= NS && !kNextGroup) ? kCodeLoads : 0);
     const int u = t >> 1;
     __builtin_amdgcn_sched_barrier(0);
     if (p) {
@@ -793,16 +839,21 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
     }
     __builtin_amdgcn_sched_barrier(0);
     const int kc = (u + NS) < nk ? u + NS : nk - 1;  // past the end: harmless re-fetch
-    const int grp = (u >> 2) + 1 < ncode ? (u >> 2) + 1 : ncode - 1;
-    // code bytes of step t + 1 live in the group of K tile (t + 1) / 2
-    constexpr bool kNextGroup = p && q == 3;
+    const int grp = u / kGroupTiles + 1 < ncode ? u / kGroupTiles + 1 : ncode - 1;
     v4i rd[kReads];
 #pragma unroll
     for (int m = 0; m < kMfma; ++m) {
       const int i = m / FN, j = m % FN;
-      if (kMx) {
+      if (kF4) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fb[j], fa[i], acc[i][j], kFmtB, kFmtA, 0, (int)cb[Z][j], 0, (int)ca[Z][i]);
+            lo16(fb[j]), lo16(fa[i]), acc[i][j], kFmtB, kFmtA, 0, (int)cb[Z][0][j], 0,
+            (int)ca[Z][0][i]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            hi16(fb[j]), hi16(fa[i]), acc[i][j], kFmtB, kFmtA, 0, (int)cb[Z][kCodes - 1][j], 0,
+            (int)ca[Z][kCodes - 1][i]);
+      } else if (kMx) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fb[j], fa[i], acc[i][j], kFmtB, kFmtA, 0, (int)cb[Z][0][j], 0, (int)ca[Z][0][i]);
       } else {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], kFmtB,
                                                                     kFmtA, 0, 0, 0, 0);
@@ -851,8 +902,10 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   using I6 = std::integral_constant<int, 6>;
   using I7 = std::integral_constant<int, 7>;
 
-  // unrolled over 4 K tiles (MX code groups, 4-deep ring) or over the 2-deep ring
-  constexpr int kUnrollK = (kMx || NS == 4) ? 4 : 2;
+  // unrolled over 4 K tiles (4-deep ring), an MX code group (4 K tiles, FP4 2)
+  // or the 2-deep ring
+  constexpr int kUnrollK = NS == 4 ? 4 : kMx ? kGroupTiles : 2;
+  static_assert(!kMx || kUnrollK % kGroupTiles == 0, "whole code groups per unrolled body");
   int u = 0;
   for (; u + kUnrollK <= nk; u += kUnrollK) {
     const int t = 2 * u;
@@ -867,7 +920,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
       step(t + 7, I7{}, af1, bf1, af0, bf0);
     }
   }
-  // remaining K tiles (never for MX, where K % 512 == 0)
+  // remaining K tiles (never for MX, whose K is a whole number of code groups)
   if constexpr (!kMx) {
     const int t = 2 * u;
     if (u < nk) {
@@ -906,6 +959,7 @@ template <class Cfg, int MODE, int kEpiStores, class Src, class Epi>
 __device__ __forceinline__ void stream_interior(const Src& src, int first, int last,
                                                 uint8_t* lds, Epi&& epi) {
   static constexpr int NS = 2;
+  static_assert(!kF4, "FP4 GEMMs run one tile per workgroup");
   static constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   static constexpr bool kMx = MODE == kMx32;
   static constexpr bool kRow = MODE == kRowwise;
@@ -1471,7 +1525,7 @@ __device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, 
     }
   }
   v16f acc[Cfg::kFragM][Cfg::kFragN];
-  mainloop<Cfg, MODE, KALIGNED>(op, lds, acc);
+  mainloop<Cfg, MODE, KALIGNED && !kF4>(op, lds, acc);
   if constexpr (FUSED)
     epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act);
   else

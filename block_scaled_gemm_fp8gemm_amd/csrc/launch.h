@@ -23,8 +23,8 @@ hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t k, int64_t l
 enum ScaleMode : int { kTensor = 0, kRowwise = 1, kMx32 = 2 };
 enum OutType : int { kF16 = 0, kBF16 = 1 };
 // Element formats of the codes; the values are the operand-format fields of the
-// F8F6F4 MFMA for the two FP8 formats.
-enum ElemFormat : int { kE4M3 = 0, kE5M2 = 1 };
+// F8F6F4 MFMA (e2m1 = FP4, two codes per byte, MX scales only).
+enum ElemFormat : int { kE4M3 = 0, kE5M2 = 1, kE2M1 = 4 };
 // Activation of the fused epilogue (applied after the scales and the bias).
 enum Activation : int { kActNone = 0, kActRelu = 1, kActGelu = 2, kActSilu = 3 };
 
@@ -54,6 +54,9 @@ hipError_t launch_gemm(const GemmProblem& p, int mode, int out, hipStream_t stre
 hipError_t launch_gemm_e5m2_e5m2(const GemmProblem& p, int mode, int out, hipStream_t stream);
 hipError_t launch_gemm_e4m3_e5m2(const GemmProblem& p, int mode, int out, hipStream_t stream);
 hipError_t launch_gemm_e5m2_e4m3(const GemmProblem& p, int mode, int out, hipStream_t stream);
+// MXFP4 x MXFP4 (mode kMx32 only): K, lda and ldb of the problem count bytes
+// (two e2m1 codes each), the E8M0 codes stay one per 32 elements.
+hipError_t launch_gemm_e2m1_e2m1(const GemmProblem& p, int mode, int out, hipStream_t stream);
 
 struct GroupedProblem {
   int groups;

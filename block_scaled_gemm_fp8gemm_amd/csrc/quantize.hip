@@ -10,7 +10,8 @@
 //   MX (32)    : per 32-element K block, E8M0 code = clamp(floor(log2 amax) - 8 + 127,
 //                0, 254) (127 if amax = 0), q = RNE_sat(x * 2^(127 - code))
 // and the same with 57344 and 15 in place of 448 and 8 for e5m2 codes (the post's
-// second FP8 format).
+// second FP8 format); MX only, 6 and 2 for e2m1 (FP4, two codes per byte, the
+// first in the low nibble: the MXFP4 format of the architecture page's §12.6.1).
 //
 // All kernels are HBM-streaming.  The unit of work is 1024 consecutive values of
 // a row, taken by one wavefront so that every load and store instruction covers
@@ -221,12 +222,19 @@ __device__ __forceinline__ void mx_unit(const Unit& u, uint8_t* qrow, uint8_t* c
     m = fmaxf(m, __shfl_xor(m, 4, 64));
     const uint32_t code = mx_code_from_amax<FMT>(m);
     const int e = 127 - (int)code;
-    w[j] = encode4<FMT>(ldexpf(u.v[j].x, e), ldexpf(u.v[j].y, e), ldexpf(u.v[j].z, e),
-                        ldexpf(u.v[j].w, e));
+    const float x0 = ldexpf(u.v[j].x, e), x1 = ldexpf(u.v[j].y, e);
+    const float x2 = ldexpf(u.v[j].z, e), x3 = ldexpf(u.v[j].w, e);
     const int c = col0 + 256 * j + 4 * lane;
+    if constexpr (FMT == kE2M1) {
+      // two codes per byte: columns c .. c+3 are bytes c/2, c/2 + 1 (128 contiguous
+      // bytes per instruction across the wavefront)
+      if (c < k) *reinterpret_cast<uint16_t*>(qrow + (c >> 1)) = (uint16_t)encode4_e2m1(x0, x1, x2, x3);
+    } else {
+      w[j] = encode4<FMT>(x0, x1, x2, x3);
+    }
     if ((lane & 7) == 0 && c < k) crow[c >> 5] = (uint8_t)code;
   }
-  store_codes(qrow, col0, k, lane, w);
+  if constexpr (FMT != kE2M1) store_codes(qrow, col0, k, lane, w);
 }
 
 template <int FMT>
@@ -326,6 +334,7 @@ hipError_t launch_quantize_rowwise(const float* x, int64_t rows, int64_t k, int6
 hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
                               int64_t ldq, uint8_t* codes, int fmt, hipStream_t stream) {
   if (fmt == kE5M2) return quantize_mx_fmt<kE5M2>(x, rows, k, ldx, q, ldq, codes, stream);
+  if (fmt == kE2M1) return quantize_mx_fmt<kE2M1>(x, rows, k, ldx, q, ldq, codes, stream);
   return quantize_mx_fmt<kE4M3>(x, rows, k, ldx, q, ldq, codes, stream);
 }
 

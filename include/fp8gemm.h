@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FP8GEMM_VERSION 120 /* 1.2.0: e5m2 operands, fused epilogues, row-major B */
+#define FP8GEMM_VERSION 130 /* 1.3.0: e5m2 operands, fused epilogues, row-major B, MXFP4 */
 
 typedef enum fp8gemm_status {
   FP8GEMM_SUCCESS = 0,
@@ -70,7 +70,12 @@ typedef enum fp8gemm_out_dtype {
    both FP8 formats, E4M3 and E5M2, in its second paragraph). */
 typedef enum fp8gemm_format {
   FP8GEMM_FORMAT_E4M3 = 0, /* OCP e4m3fn: bias 7, no infinity, max 448 (the default)      */
-  FP8GEMM_FORMAT_E5M2 = 1  /* OCP e5m2: bias 15, infinities and NaNs, max 57344           */
+  FP8GEMM_FORMAT_E5M2 = 1, /* OCP e5m2: bias 15, infinities and NaNs, max 57344           */
+  /* FP4, the MXFP4 element ("Hopper/Blackwell architecture features" §12.6.1 lists FP4
+     next to FP8 with micro-scaling): OCP MX e2m1, bias 1, magnitudes 0, .5, 1, 1.5, 2,
+     3, 4, 6, no infinity or NaN.  Two codes per byte, element 2i in bits 0-3 and
+     element 2i+1 in bits 4-7 (sign = bit 3 of a code).  MX32 scales only. */
+  FP8GEMM_FORMAT_E2M1 = 4
 } fp8gemm_format;
 
 /* Activation of the fused epilogue (the Cutlass-named Triton FP8 post fuses a
@@ -115,8 +120,12 @@ fp8gemm_status fp8gemm_quantize(const float* x, int64_t rows, int64_t k, int64_t
 /* The same for either element format (fp8gemm_format): with FP8GEMM_FORMAT_E5M2
    the rules above use 57344 in place of 448 (s = fl32(amax/57344), saturation
    to +-57344, never infinity) and 15 in place of 8 (MX32: e = floor(log2 amax)
-   - 15).  fp8gemm_quantize is this call with FP8GEMM_FORMAT_E4M3.  Errors as
-   above; an unknown format is INVALID_VALUE. */
+   - 15).  With FP8GEMM_FORMAT_E2M1 (MX32 only, else NOT_SUPPORTED) they use 6
+   and 2 (e = floor(log2 amax) - 2, q = RNE_sat(x * 2^-e) onto e2m1, saturating
+   at +-6) and q holds two codes per byte: element (r,i) in byte q[r*ldq + i/2],
+   low nibble for even i; ldq >= k/2 bytes, a multiple of 16.
+   fp8gemm_quantize is this call with FP8GEMM_FORMAT_E4M3.  Errors as above; an
+   unknown format is INVALID_VALUE. */
 fp8gemm_status fp8gemm_quantize_ex(const float* x, int64_t rows, int64_t k, int64_t ldx, int mode,
                                    int format, uint8_t* q, int64_t ldq, void* scales,
                                    void* workspace, size_t workspace_bytes, void* stream);
@@ -148,8 +157,13 @@ fp8gemm_status fp8gemm_run(int64_t M, int64_t N, int64_t K, const uint8_t* A, in
 /* Dense scaled GEMM with operand formats and a fused epilogue:                */
 /*   y[m,n] = sum_k dq_a(m,k) * dq_b(k,n)  (as fp8gemm_run),                   */
 /*   C[m,n] = cast( act( y[m,n] + bias[n] ) ).                                 */
-/* a_format, b_format: fp8gemm_format of the A and B codes (any pair: e5m2 x   */
-/*          e5m2 or mixed e4m3 x e5m2, the gradient-GEMM pairing).              */
+/* a_format, b_format: fp8gemm_format of the A and B codes (any pair of e4m3   */
+/*          and e5m2: e5m2 x e5m2 or mixed e4m3 x e5m2, the gradient-GEMM       */
+/*          pairing), or E2M1 for both (MXFP4 x MXFP4: mode MX32 only, else     */
+/*          NOT_SUPPORTED; A holds two codes per byte, element (m,k) in byte    */
+/*          A[m*lda + k/2], likewise B[n*ldb + k/2]; lda, ldb >= K/2 bytes;     */
+/*          K % 32 == 0; scales uint8 [M][K/32] and [N][K/32]; no workspace,    */
+/*          NULL allowed).                                                      */
 /* bias   : device float[N], 4-byte aligned, or NULL (no bias).               */
 /* activation: fp8gemm_activation, applied in fp32 after the scales and bias.   */
 /* The scale modes, layouts, workspace and errors are those of fp8gemm_run      */
@@ -177,7 +191,8 @@ fp8gemm_status fp8gemm_run_ex(int64_t M, int64_t N, int64_t K, const uint8_t* A,
 /*   scale_b: TENSOR float[1]; ROWWISE float[N]; MX32 uint8 [K/32][N] (row-major, */
 /*            N codes per row).                                                 */
 /* Everything else (A, C, formats, scale_a, bias, activation, accuracy, errors) */
-/* as fp8gemm_run_ex.  The call first copies B and its MX codes into the        */
+/* as fp8gemm_run_ex; E2M1 operands are NOT_SUPPORTED here.  The call first    */
+/* copies B and its MX codes into the                                           */
 /* K-contiguous layout in the workspace (one HBM pass over B), then runs the    */
 /* GEMM: workspace is fp8gemm_workspace_size_kn() bytes, 16-byte aligned,       */
 /* zero-filled before its first use (never NULL: the copy lives there).         */

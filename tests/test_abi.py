@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert F.fp8gemm_version() == 120
+    assert F.fp8gemm_version() == 130
     for code, name in [(0, "FP8GEMM_SUCCESS"), (1, "FP8GEMM_ERROR_INVALID_VALUE"),
                        (2, "FP8GEMM_ERROR_MISALIGNED"), (3, "FP8GEMM_ERROR_NOT_SUPPORTED"),
                        (4, "FP8GEMM_ERROR_WORKSPACE"), (5, "FP8GEMM_ERROR_LAUNCH"),
@@ -144,6 +144,32 @@ def test_extended_entry_points_validation(lib):
     assert q(fmt=1, x=0) == INVALID
     assert q(fmt=1, k=48, mode=2) == NOT_SUPPORTED
     assert q(fmt=1, mode=0) == WORKSPACE
+
+
+def test_fp4_validation(lib):
+    """MXFP4 operands: MX scales only, FP4 x FP4 only, K counted in elements with
+    two codes per byte; all checked before any HIP call."""
+    run = lambda **kw: _run_ex(lib, **{"fa": 4, "fb": 4, "mode": 2, "K": 256, "lda": 128,
+                                       "ldb": 128, **kw})
+    assert run(M=0) == SUCCESS
+    assert run(mode=1) == NOT_SUPPORTED                # row-wise FP4
+    assert run(mode=0) == NOT_SUPPORTED                # per-tensor FP4
+    assert run(fb=0) == NOT_SUPPORTED                  # FP4 x e4m3
+    assert run(fa=1) == NOT_SUPPORTED                  # e5m2 x FP4
+    assert run(lda=112) == INVALID                     # lda < K/2 bytes
+    assert run(K=240, lda=128, ldb=128) == NOT_SUPPORTED   # K % 32
+    assert run(lda=136) == MISALIGNED
+    assert _run_ex(lib, fa=3) == INVALID               # FP6 formats are not offered
+    q = lambda **kw: lib.fp8gemm_quantize_ex(P, 64, kw.get("k", 256), 256, kw.get("mode", 2), 4,
+                                             P2, kw.get("ldq", 128), P3, 0, 0, None)
+    assert q(mode=1) == NOT_SUPPORTED
+    assert q(mode=0) == NOT_SUPPORTED
+    assert q(ldq=112) == INVALID                       # ldq < k/2 bytes
+    assert q(ldq=136) == MISALIGNED
+    assert q(k=48) == NOT_SUPPORTED                    # MX: k % 32
+    need = F.fp8gemm_workspace_size_kn(64, 64, 128, 2)
+    assert lib.fp8gemm_run_kn(64, 64, 128, P, 64, 4, P2, 64, 4, 2, P3, P3 + 256, 0, 0,
+                              P3 + 4096, 64, 1, P3 + (1 << 20), need, None) == NOT_SUPPORTED
 
 
 def test_row_major_b_validation(lib):
