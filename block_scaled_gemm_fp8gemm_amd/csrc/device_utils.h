@@ -50,16 +50,19 @@ __device__ __forceinline__ uint32_t encode4_e5m2(float a, float b, float c, floa
 }
 
 // One fp32 value -> e2m1 code (bits 0-3): round to nearest even onto the grid of
-// spacing 0.5 below 2, 1 below 4 and 2 above (a power-of-two scaling and rintf,
-// both exact), saturating at 6; the sign goes to bit 3, so -0 gives 0x8.
+// spacing 0.5 below 2, 1 below 4 and 2 above (multiplications by powers of two
+// and rintf, all exact), saturating at 6; the sign goes to bit 3, so -0 gives
+// 0x8.  The code of the rounded magnitude r: 2r for r < 1 (0 or 0.5); else the
+// exponent field plus one, doubled, with the top mantissa bit as the last bit.
 __device__ __forceinline__ uint32_t encode_e2m1(float v) {
   const uint32_t sign = (__float_as_uint(v) >> 28) & 0x8u;
   const float a = fabsf(v);
-  const float inv = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);   // 1 / spacing
-  const float r = fminf(rintf(a * inv) / inv, 6.0f);
-  // 0, .5, 1, 1.5 -> 0..3;  2, 3 -> 4, 5;  4 -> 6;  6 -> 7
-  const uint32_t mag = r < 2.0f ? (uint32_t)(r * 2.0f)
-                                : (r < 4.0f ? (uint32_t)r + 2u : (r < 6.0f ? 6u : 7u));
+  const float up = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);   // 1 / spacing
+  const float dn = a < 2.0f ? 0.5f : (a < 4.0f ? 1.0f : 2.0f);   // spacing
+  const float r = fminf(rintf(a * up) * dn, 6.0f);
+  const uint32_t b = __float_as_uint(r);
+  const uint32_t mag = r < 1.0f ? (uint32_t)(r * 2.0f)
+                                : ((((b >> 23) - 126u) << 1) | ((b >> 22) & 1u));
   return sign | mag;
 }
 

@@ -67,6 +67,9 @@
 #ifndef FP8GEMM_SCHED
 #define FP8GEMM_SCHED 1
 #endif
+#ifndef FP8GEMM_F4_UNROLL
+#define FP8GEMM_F4_UNROLL 1    // FP4 interior loop: code groups per unrolled body (1 or 2)
+#endif
 
 namespace fp8gemm {
 inline namespace FP8GEMM_FMT_NS(FP8GEMM_FMT_A, FP8GEMM_FMT_B) {
@@ -904,8 +907,9 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
 
   // unrolled over 4 K tiles (4-deep ring), an MX code group (4 K tiles, FP4 2)
   // or the 2-deep ring
-  constexpr int kUnrollK = NS == 4 ? 4 : kMx ? kGroupTiles : 2;
+  constexpr int kUnrollK = NS == 4 ? 4 : kMx ? kGroupTiles * (kF4 ? FP8GEMM_F4_UNROLL : 1) : 2;
   static_assert(!kMx || kUnrollK % kGroupTiles == 0, "whole code groups per unrolled body");
+  static_assert(kUnrollK == 2 || kUnrollK == 4, "the body below unrolls 2 or 4 K tiles");
   int u = 0;
   for (; u + kUnrollK <= nk; u += kUnrollK) {
     const int t = 2 * u;
@@ -920,7 +924,18 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
       step(t + 7, I7{}, af1, bf1, af0, bf0);
     }
   }
-  // remaining K tiles (never for MX, whose K is a whole number of code groups)
+  // remaining K tiles: for MX one code group (FP4 with two groups per body);
+  // otherwise any K tiles left
+  if constexpr (kMx && kUnrollK > kGroupTiles) {
+    static_assert(2 * kGroupTiles == kUnrollK, "one group left at most");
+    const int t = 2 * u;
+    if (u < nk) {
+      step(t, I0{}, af0, bf0, af1, bf1);
+      step(t + 1, I1{}, af1, bf1, af0, bf0);
+      step(t + 2, I2{}, af0, bf0, af1, bf1);
+      step(t + 3, I3{}, af1, bf1, af0, bf0);
+    }
+  }
   if constexpr (!kMx) {
     const int t = 2 * u;
     if (u < nk) {

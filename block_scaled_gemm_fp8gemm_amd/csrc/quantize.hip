@@ -224,17 +224,30 @@ __device__ __forceinline__ void mx_unit(const Unit& u, uint8_t* qrow, uint8_t* c
     const int e = 127 - (int)code;
     const float x0 = ldexpf(u.v[j].x, e), x1 = ldexpf(u.v[j].y, e);
     const float x2 = ldexpf(u.v[j].z, e), x3 = ldexpf(u.v[j].w, e);
+    w[j] = FMT == kE2M1 ? encode4_e2m1(x0, x1, x2, x3) : encode4<FMT>(x0, x1, x2, x3);
     const int c = col0 + 256 * j + 4 * lane;
-    if constexpr (FMT == kE2M1) {
-      // two codes per byte: columns c .. c+3 are bytes c/2, c/2 + 1 (128 contiguous
-      // bytes per instruction across the wavefront)
-      if (c < k) *reinterpret_cast<uint16_t*>(qrow + (c >> 1)) = (uint16_t)encode4_e2m1(x0, x1, x2, x3);
-    } else {
-      w[j] = encode4<FMT>(x0, x1, x2, x3);
-    }
     if ((lane & 7) == 0 && c < k) crow[c >> 5] = (uint8_t)code;
   }
-  if constexpr (FMT != kE2M1) store_codes(qrow, col0, k, lane, w);
+  if constexpr (FMT == kE2M1) {
+    // Two codes per byte: lane l holds the 16 bits of bytes 128 j + 2 l and + 1.
+    // Lanes 2i and 2i + 1 swap halves so that the even lane stores the word at
+    // 128 j + 4 i for j = 0, 2 and the odd lane the one for j = 1, 3: two 4-byte
+    // stores per lane, each instruction covering two 128-byte runs.
+    const bool odd = lane & 1;
+    const int pair = lane >> 1;
+#pragma unroll
+    for (int jp = 0; jp < 4; jp += 2) {
+      const uint32_t keep = odd ? w[jp + 1] : w[jp];
+      const uint32_t give = odd ? w[jp] : w[jp + 1];
+      const uint32_t got = (uint32_t)__shfl_xor((int)give, 1, 64);
+      const uint32_t word = odd ? (got | (keep << 16)) : (keep | (got << 16));
+      const int j = jp + (odd ? 1 : 0);
+      const int c = col0 + 256 * j + 8 * pair;          // first of the word's 8 columns
+      if (c < k) *reinterpret_cast<uint32_t*>(qrow + (c >> 1)) = word;
+    }
+  } else {
+    store_codes(qrow, col0, k, lane, w);
+  }
 }
 
 template <int FMT>
