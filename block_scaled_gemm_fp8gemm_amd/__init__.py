@@ -72,6 +72,8 @@ _SIGNATURES = {
                            _p, _sz, _p]),
     "fp8gemm_run_ex": (_int, [_i64, _i64, _i64, _p, _i64, _int, _p, _i64, _int, _int, _p, _p, _p,
                               _int, _p, _i64, _int, _p, _sz, _p]),
+    "fp8gemm_run_mxout": (_int, [_i64, _i64, _i64, _p, _i64, _int, _p, _i64, _int, _int, _p, _p,
+                                 _p, _int, _p, _i64, _p, _i64, _p, _sz, _p]),
     "fp8gemm_workspace_size_kn": (_sz, [_i64, _i64, _i64, _int]),
     "fp8gemm_run_kn": (_int, [_i64, _i64, _i64, _p, _i64, _int, _p, _i64, _int, _int, _p, _p, _p,
                               _int, _p, _i64, _int, _p, _sz, _p]),
@@ -153,6 +155,15 @@ def fp8gemm_run_ex(M: int, N: int, K: int, A: int, lda: int, a_format: int, B: i
     _check("fp8gemm_run_ex", load_library().fp8gemm_run_ex(
         M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias, activation, C,
         ldc, out_dtype, workspace, workspace_bytes, stream))
+
+
+def fp8gemm_run_mxout(M: int, N: int, K: int, A: int, lda: int, a_format: int, B: int, ldb: int,
+                      b_format: int, mode: int, scale_a: int, scale_b: int, bias: int,
+                      activation: int, C: int, ldc: int, c_scales: int, ldcs: int,
+                      workspace: int, workspace_bytes: int, stream: int) -> None:
+    _check("fp8gemm_run_mxout", load_library().fp8gemm_run_mxout(
+        M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias, activation, C,
+        ldc, c_scales, ldcs, workspace, workspace_bytes, stream))
 
 
 def fp8gemm_workspace_size_kn(M: int, N: int, K: int, mode: int) -> int:
@@ -311,6 +322,45 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
                    _ptr(workspace) if need else 0, workspace.numel() if need else 0,
                    _stream_handle(qa.device))
     return out
+
+
+def gemm_mxout(qa, sa, qb, sb, mode: str = "tensor", out=None, out_scales=None,
+               workspace=None, fmt_a: str = "e4m3", fmt_b: str = "e4m3", bias=None,
+               activation: str = "none"):
+    """(codes uint8 [M, N], E8M0 uint8 [M, N/32]): y = act(dq(qa) @ dq(qb) + bias)
+    quantised for the next layer, e4m3 with one E8M0 scale per 32 columns (the
+    MX rule of ``quantize``); N must be a multiple of 32.  Operands as ``gemm``
+    (qb [N, K], K contiguous)."""
+    torch = _torch()
+    _require_cuda(qa, "qa", torch.uint8, 2)
+    _require_cuda(qb, "qb", torch.uint8, 2)
+    M, K = qa.shape
+    N, Kb = qb.shape
+    fp4 = "e2m1" in (fmt_a, fmt_b)
+    if fp4:
+        K, Kb = 2 * K, 2 * Kb
+    if K != Kb:
+        raise ValueError("qa and qb must share K")
+    if out is None:
+        ldc = (N + 15) // 16 * 16
+        out = torch.empty((M, ldc), dtype=torch.uint8, device=qa.device)[:, :N]
+    if out_scales is None:
+        out_scales = torch.empty((M, N // 32), dtype=torch.uint8, device=qa.device)
+    m = SCALE_MODES[mode]
+    need = 0 if fp4 else fp8gemm_workspace_size(M, N, K, m)
+    if need and workspace is None:
+        workspace = gemm_workspace(qa.device, need)
+    if bias is not None:
+        _require_cuda(bias, "bias", torch.float32, 1)
+        if bias.numel() != N:
+            raise ValueError("bias must have N elements")
+    fp8gemm_run_mxout(M, N, K, _ptr(qa), qa.stride(0), FORMATS[fmt_a], _ptr(qb), qb.stride(0),
+                      FORMATS[fmt_b], m, _ptr(sa), _ptr(sb), _ptr(bias), ACTIVATIONS[activation],
+                      _ptr(out), out.stride(0), _ptr(out_scales),
+                      out_scales.stride(0) if out_scales.dim() == 2 else max(N // 32, 1),
+                      _ptr(workspace) if need else 0, workspace.numel() if need else 0,
+                      _stream_handle(qa.device))
+    return out, out_scales
 
 
 def grouped_gemm(qa, sa, offsets, qb, sb, mode: str = "rowwise", out_dtype: str = "bf16",

@@ -125,18 +125,31 @@ fp8gemm_status fp8gemm_run(int64_t M, int64_t N, int64_t K, const uint8_t* A, in
                         workspace_bytes, stream);
 }
 
-fp8gemm_status fp8gemm_run_ex(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
-                              int a_format, const uint8_t* B, int64_t ldb, int b_format, int mode,
-                              const void* scale_a, const void* scale_b, const float* bias,
-                              int activation, void* C, int64_t ldc, int out_dtype,
-                              void* workspace, size_t workspace_bytes, void* stream) {
-  if (!valid_mode(mode) || !valid_out(out_dtype) || !valid_format(a_format) ||
+}  // extern "C"
+
+namespace {
+
+// The dense GEMM behind fp8gemm_run_ex (16-bit outputs) and fp8gemm_run_mxout
+// (out_dtype kE4M3Mx: e4m3 codes to C, E8M0 codes to cs).
+fp8gemm_status run_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                         int a_format, const uint8_t* B, int64_t ldb, int b_format, int mode,
+                         const void* scale_a, const void* scale_b, const float* bias,
+                         int activation, void* C, int64_t ldc, int out_dtype, uint8_t* cs,
+                         int64_t ldcs, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool qout = out_dtype == fp8gemm::kE4M3Mx;
+  if (!valid_mode(mode) || !(valid_out(out_dtype) || qout) || !valid_format(a_format) ||
       !valid_format(b_format) || !valid_act(activation) || M < 0 || N < 0 || K <= 0)
     return FP8GEMM_ERROR_INVALID_VALUE;
   // FP4 pairs with FP4 only, and only with MX block scales
   const bool fp4 = a_format == FP8GEMM_FORMAT_E2M1 || b_format == FP8GEMM_FORMAT_E2M1;
   if (fp4 && (a_format != b_format || mode != kMx32)) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (M == 0 || N == 0) return FP8GEMM_SUCCESS;
+  if (qout) {
+    if (!cs || ldcs < N / 32) return FP8GEMM_ERROR_INVALID_VALUE;
+    if (N % 32 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
+    if (ldcs > kMaxDim) return FP8GEMM_ERROR_NOT_SUPPORTED;
+    if (ldc % 16 != 0) return FP8GEMM_ERROR_MISALIGNED;      // byte rows of codes
+  }
   fp8gemm_status st = check_gemm_common(M, N, K, A, lda, B, ldb, mode, scale_a, scale_b, C, ldc,
                                         out_dtype, fp4 ? 2 : 1);
   if (st != FP8GEMM_SUCCESS) return st;
@@ -160,6 +173,8 @@ fp8gemm_status fp8gemm_run_ex(int64_t M, int64_t N, int64_t K, const uint8_t* A,
   p.workspace = need > 0 ? workspace : nullptr;
   p.bias = bias;
   p.act = activation;
+  p.cs = cs;
+  p.ldcs = ldcs;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fp4) return from_hip(fp8gemm::launch_gemm_e2m1_e2m1(p, mode, out_dtype, s));
   if (a_format == FP8GEMM_FORMAT_E5M2 && b_format == FP8GEMM_FORMAT_E5M2)
@@ -169,6 +184,31 @@ fp8gemm_status fp8gemm_run_ex(int64_t M, int64_t N, int64_t K, const uint8_t* A,
   if (b_format == FP8GEMM_FORMAT_E5M2)
     return from_hip(fp8gemm::launch_gemm_e4m3_e5m2(p, mode, out_dtype, s));
   return from_hip(fp8gemm::launch_gemm(p, mode, out_dtype, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8gemm_status fp8gemm_run_ex(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                              int a_format, const uint8_t* B, int64_t ldb, int b_format, int mode,
+                              const void* scale_a, const void* scale_b, const float* bias,
+                              int activation, void* C, int64_t ldc, int out_dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_out(out_dtype)) return FP8GEMM_ERROR_INVALID_VALUE;
+  return run_dense(M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias,
+                   activation, C, ldc, out_dtype, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+fp8gemm_status fp8gemm_run_mxout(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                 int a_format, const uint8_t* B, int64_t ldb, int b_format,
+                                 int mode, const void* scale_a, const void* scale_b,
+                                 const float* bias, int activation, uint8_t* C, int64_t ldc,
+                                 uint8_t* c_scales, int64_t ldcs, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return run_dense(M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias,
+                   activation, C, ldc, fp8gemm::kE4M3Mx, c_scales, ldcs, workspace,
+                   workspace_bytes, stream);
 }
 
 // Row-major B: the workspace holds the K-contiguous copy of B ([N][K] bytes), for

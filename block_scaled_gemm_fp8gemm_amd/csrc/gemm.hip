@@ -50,7 +50,7 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void gemm_kernel(G
 
   const float ts = (MODE == kTensor) ? fsa[0] * fsb[0] : 1.0f;
   gemm_tile<Cfg, MODE, OutT, KALIGNED, FUSED>(op, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M,
-                                              n0, p.N, ts, p.bias, p.act);
+                                              n0, p.N, ts, p.bias, p.act, p.cs, p.ldcs);
 }
 
 // Operands of the tiles of one persistent workgroup: tile i of the list is the
@@ -204,8 +204,10 @@ hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
     // persistent streams pay off from about eight tiles per CU on (measured)
     const bool many = big_tiles >= 8 * 256;
     // (the fused epilogue stages through the ring, so it never runs in a stream)
-    if ((FP8GEMM_PERSISTENT || many) && !FUSED && all_interior<Big>(p))
-      return launch_persistent<Big, MODE, OutT>(p, stream);
+    if constexpr (!FUSED) {
+      if ((FP8GEMM_PERSISTENT || many) && all_interior<Big>(p))
+        return launch_persistent<Big, MODE, OutT>(p, stream);
+    }
     return launch_cfg<Big, MODE, OutT, FUSED>(p, stream);
   }
   return launch_cfg<Mid, MODE, OutT, FUSED>(p, stream);
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void splitk_kernel(GemmProblem p,
   const float ts = (MODE == kTensor) ? fsa[0] * fsb[0] : 1.0f;
   if constexpr (FUSED)
     epilogue_fused<Cfg, MODE, OutT>(sum, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N, ts,
-                                    p.bias, p.act);
+                                    p.bias, p.act, p.cs, p.ldcs);
   else
     epilogue<Cfg, MODE, OutT>(sum, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N, ts);
 }
@@ -404,11 +406,16 @@ hipError_t launch_plan(const GemmProblem& p, hipStream_t stream) {
   }
 }
 
-// kernels with the fused bias / activation epilogue only when it is asked for
+// kernels with the fused bias / activation epilogue only when it is asked for;
+// the e4m3 + MX-scale output (OutT = uint8_t) always runs the fused epilogue
 template <int MODE, typename OutT>
 hipError_t launch_any(const GemmProblem& p, hipStream_t stream) {
-  if (p.bias != nullptr || p.act != kActNone) return launch_plan<MODE, OutT, true>(p, stream);
-  return launch_plan<MODE, OutT, false>(p, stream);
+  if constexpr (std::is_same<OutT, uint8_t>::value) {
+    return launch_plan<MODE, OutT, true>(p, stream);
+  } else {
+    if (p.bias != nullptr || p.act != kActNone) return launch_plan<MODE, OutT, true>(p, stream);
+    return launch_plan<MODE, OutT, false>(p, stream);
+  }
 }
 
 }  // namespace
@@ -439,8 +446,14 @@ hipError_t FP8GEMM_LAUNCH_NAME(const GemmProblem& p, int mode, int out, hipStrea
   // MXFP4: E8M0 block scales only; K, lda and ldb count bytes (two codes each)
   if (mode != kMx32) return hipErrorInvalidValue;
   if (out == kF16) return launch_any<kMx32, _Float16>(p, stream);
+  if (out == kE4M3Mx) return launch_any<kMx32, uint8_t>(p, stream);
   return launch_any<kMx32, __bf16>(p, stream);
 #else
+  if (out == kE4M3Mx) {
+    if (mode == kTensor) return launch_any<kTensor, uint8_t>(p, stream);
+    if (mode == kRowwise) return launch_any<kRowwise, uint8_t>(p, stream);
+    return launch_any<kMx32, uint8_t>(p, stream);
+  }
   if (out == kF16) {
     if (mode == kTensor) return launch_any<kTensor, _Float16>(p, stream);
     if (mode == kRowwise) return launch_any<kRowwise, _Float16>(p, stream);

@@ -1440,11 +1440,18 @@ __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][C
 // fused GEMM slower than a separate pass over C; kernels without a fused
 // epilogue are separate instances and carry none of this code.)  Needs the ring
 // free: it runs after the mainloop's final barrier, never inside a copy stream.
+// With OutT = uint8_t the output is quantised again for the next layer: e4m3
+// codes with one E8M0 code per 32 consecutive columns of a row (the MX rule of
+// the quantisers), written to cs[m * ldcs + n / 32]; N % 32 == 0.  The 32
+// columns of a block are the four-column pieces of 8 consecutive lanes, so the
+// block maximum takes three xor-shuffles.
 template <class Cfg, int MODE, typename OutT>
 __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                uint8_t* lds, OutT* C, int64_t ldc, int m0,
                                                int m_end, int n0, int N, float tensor_scale,
-                                               const float* bias, int act) {
+                                               const float* bias, int act,
+                                               uint8_t* cs = nullptr, int64_t ldcs = 0) {
+  constexpr bool kQ = std::is_same<OutT, uint8_t>::value;
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   constexpr int kPitch = Cfg::WN + 4;                    // staged fp32 row (+16 bytes)
   constexpr int kPiecesPerRow = Cfg::WN / 4;
@@ -1453,7 +1460,8 @@ __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cf
                 "fp32 staging fits in the ring");
   static_assert((32 * kPiecesPerRow) % 64 == 0, "whole store instructions");
   static_assert(64 % kPiecesPerRow == 0, "a lane keeps its columns over the store loop");
-  static_assert(sizeof(OutT) == 2, "16-bit outputs");
+  static_assert(sizeof(OutT) == 2 || kQ, "16-bit outputs or e4m3 codes");
+  static_assert(!kQ || kPiecesPerRow % 8 == 0, "32-column blocks inside one lane group");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
@@ -1500,7 +1508,20 @@ __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cf
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = activate(val[e] + bv[e], act);
-      if (m < m_end) {
+      if constexpr (kQ) {
+        float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        a = fmaxf(a, __shfl_xor(a, 1, 64));
+        a = fmaxf(a, __shfl_xor(a, 2, 64));
+        a = fmaxf(a, __shfl_xor(a, 4, 64));
+        const uint32_t code = mx_code_from_amax<kE4M3>(a);
+        const int e = 127 - (int)code;
+        const uint32_t w = encode4_e4m3(ldexpf(v[0], e), ldexpf(v[1], e), ldexpf(v[2], e),
+                                        ldexpf(v[3], e));
+        if (m < m_end && n < N) {           // N % 32 == 0: a block is all in or all out
+          *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(C) + (int64_t)m * ldc + n) = w;
+          if ((lane & 7) == 0) cs[(int64_t)m * ldcs + (n >> 5)] = (uint8_t)code;
+        }
+      } else if (m < m_end) {
         OutT* dst = C + (int64_t)m * ldc + n;
         if (n + 4 <= N) {
           *reinterpret_cast<uint2*>(dst) = pack4<OutT>(v[0], v[1], v[2], v[3]);
@@ -1521,14 +1542,15 @@ template <class Cfg, int MODE, typename OutT, bool KALIGNED, bool FUSED = false>
 __device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, OutT* C,
                                           int64_t ldc, int m0, int m_end, int n0, int N,
                                           float tensor_scale, const float* bias = nullptr,
-                                          int act = kActNone) {
+                                          int act = kActNone, uint8_t* cs = nullptr,
+                                          int64_t ldcs = 0) {
   if constexpr (KALIGNED && Cfg::kSlots == 4) {
     if (interior_tile<Cfg, MODE>(op)) {
       v16f acc[Cfg::kFragM][Cfg::kFragN];
       mainloop_interior<Cfg, MODE>(op, lds, acc);
       if constexpr (FUSED) {
         epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias,
-                                        act);
+                                        act, cs, ldcs);
       } else {
 #if FP8GEMM_DIRECT_EPILOGUE
         epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, n0, tensor_scale);
@@ -1542,7 +1564,8 @@ __device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, 
   v16f acc[Cfg::kFragM][Cfg::kFragN];
   mainloop<Cfg, MODE, KALIGNED && !kF4>(op, lds, acc);
   if constexpr (FUSED)
-    epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act);
+    epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act,
+                                    cs, ldcs);
   else
     epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
 }

@@ -21,7 +21,9 @@ hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t k, int64_t l
                               int64_t ldq, uint8_t* codes, int fmt, hipStream_t stream);
 
 enum ScaleMode : int { kTensor = 0, kRowwise = 1, kMx32 = 2 };
-enum OutType : int { kF16 = 0, kBF16 = 1 };
+// kE4M3Mx: e4m3 codes with an E8M0 scale per 32 columns of each row (the fused
+// epilogue quantises the output for the next layer; codes to C, scales to cs).
+enum OutType : int { kF16 = 0, kBF16 = 1, kE4M3Mx = 2 };
 // Element formats of the codes; the values are the operand-format fields of the
 // F8F6F4 MFMA (e2m1 = FP4, two codes per byte, MX scales only).
 enum ElemFormat : int { kE4M3 = 0, kE5M2 = 1, kE2M1 = 4 };
@@ -41,6 +43,8 @@ struct GemmProblem {
   void* workspace;      // split-K partials and tile counters (gemm_workspace_bytes)
   const float* bias;    // fused epilogue: fp32 [N] added after the scales, or null
   int act;              // fused epilogue: Activation applied last
+  uint8_t* cs = nullptr;  // kE4M3Mx: E8M0 codes of C, cs[m * ldcs + n / 32]
+  int64_t ldcs = 0;
 };
 
 // Device workspace a dense GEMM of this shape needs (0: none).  Shapes with too

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FP8GEMM_VERSION 130 /* 1.3.0: e5m2 operands, fused epilogues, row-major B, MXFP4 */
+#define FP8GEMM_VERSION 140 /* 1.4.0: e5m2, fused epilogues, row-major B, MXFP4, MX output */
 
 typedef enum fp8gemm_status {
   FP8GEMM_SUCCESS = 0,
@@ -181,6 +181,34 @@ fp8gemm_status fp8gemm_run_ex(int64_t M, int64_t N, int64_t K, const uint8_t* A,
                               const void* scale_a, const void* scale_b, const float* bias,
                               int activation, void* C, int64_t ldc, int out_dtype,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Dense scaled GEMM whose output is quantised again for the next layer: the    */
+/* fused epilogue of fp8gemm_run_ex computes y = act(scaled GEMM + bias) in     */
+/* fp32 and writes it as e4m3 codes with one E8M0 scale per 32 consecutive      */
+/* columns of each row (the MX32 rule of fp8gemm_quantize: e = floor(log2 amax) */
+/* - 8, code = clamp(e + 127, 0, 254), q = RNE_sat(y * 2^-e)).  The Cutlass-    */
+/* named Triton FP8 post fuses epilogues to save a round trip of C through      */
+/* memory; this one also saves the quantisation pass of the next FP8 GEMM.      */
+/*   C       : device uint8 e4m3 codes, element (m,n) at C[m*ldc+n]; ldc >= N,  */
+/*             a multiple of 16; 16-byte aligned.                               */
+/*   c_scales: device uint8 E8M0 codes, block (m, n/32) at c_scales[m*ldcs +    */
+/*             n/32]; ldcs >= N/32.                                             */
+/*   N must be a multiple of 32 (else NOT_SUPPORTED).                           */
+/* A, B, formats, mode, scales, bias, activation, workspace and errors as       */
+/* fp8gemm_run_ex.  Accuracy: each output dequantises (code value times its    */
+/* block's 2^e) to within the fp8gemm_run_ex bound of act(y_ref + bias) plus    */
+/* half an e4m3 spacing at its magnitude and block exponent (and the saturation */
+/* of block maxima in [448, 512) * 2^e to 448 * 2^e); a block exponent may      */
+/* differ by one from the exact result's when its maximum lies within that      */
+/* bound of a power of two.                                                     */
+/* ------------------------------------------------------------------------- */
+fp8gemm_status fp8gemm_run_mxout(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                 int a_format, const uint8_t* B, int64_t ldb, int b_format,
+                                 int mode, const void* scale_a, const void* scale_b,
+                                 const float* bias, int activation, uint8_t* C, int64_t ldc,
+                                 uint8_t* c_scales, int64_t ldcs, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Dense scaled GEMM with B in row-major [K,N] layout (N contiguous), the layout */

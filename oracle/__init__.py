@@ -34,8 +34,8 @@ from .formats import (E2M1_DECODE, E2M1_MAX, E4M3_DECODE, E4M3_MAX, E5M2_DECODE,
                       unpack_fp4)
 from .quant import quantize, quantize_mx, quantize_rowwise, quantize_tensor
 from .gemm import (ACT_LIPSCHITZ, activation, dequantize, epilogue_reference,
-                   epilogue_tolerance, gemm_reference, grouped_reference, output_ulp, tolerance,
-                   within_bound, round_to_output)
+                   epilogue_tolerance, gemm_reference, grouped_reference, mx_output_reference,
+                   mx_output_within_bound, output_ulp, tolerance, within_bound, round_to_output)
 
 __all__ = [
     "E2M1_DECODE", "E2M1_MAX", "decode_e2m1", "encode_e2m1", "pack_fp4", "unpack_fp4",
@@ -44,5 +44,5 @@ __all__ = [
     "quantize", "quantize_mx", "quantize_rowwise", "quantize_tensor",
     "dequantize", "gemm_reference", "grouped_reference", "output_ulp", "tolerance",
     "within_bound", "round_to_output", "ACT_LIPSCHITZ", "activation", "epilogue_reference",
-    "epilogue_tolerance",
+    "epilogue_tolerance", "mx_output_reference", "mx_output_within_bound",
 ]

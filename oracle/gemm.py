@@ -212,3 +212,55 @@ def round_to_output(x: np.ndarray, out: str) -> np.ndarray:
     q = output_ulp(x, out)
     r = np.rint(x / q) * q                    # x / q is exact (power of two); rint is RNE
     return np.where(np.abs(r) > fmax, np.copysign(np.inf, x), r)
+
+
+# ---- output quantised for the next layer (e4m3 + E8M0 per 32 columns) --------
+# The fused epilogue may write its result as MX codes, the form the next FP8
+# GEMM consumes (the Cutlass-named Triton FP8 post fuses epilogues to save a
+# round trip of C).  Reading: y = act(C + bias) is quantised per row in blocks
+# of 32 consecutive columns with the MX rule of ``quant.quantize_mx``.
+
+def mx_output_reference(out_ref: np.ndarray):
+    """(codes uint8 [M,N], E8M0 uint8 [M,N/32]): the MX e4m3 quantisation of the
+    binary32 rounding of the exact epilogue output."""
+    from .quant import quantize_mx
+    return quantize_mx(np.asarray(out_ref, np.float64).astype(np.float32), "e4m3")
+
+
+def _e4m3_half_spacing(x: np.ndarray) -> np.ndarray:
+    """Half the e4m3 spacing at scaled magnitudes x (2^-10 in the subnormal range)."""
+    x = np.abs(np.asarray(x, np.float64))
+    _, ex = np.frexp(np.maximum(x, 2.0 ** -6))
+    return np.ldexp(1.0, (ex.astype(np.int64) - 1) - 3 - 1)
+
+
+def mx_output_within_bound(q, codes, out_ref, tol_y) -> np.ndarray:
+    """Which outputs of an MX-quantised result (q [M,N] e4m3 codes, codes [M,N/32]
+    E8M0) are acceptable against the exact output out_ref with tolerance tol_y.
+
+    The dequantised value decode(q) * 2^e must lie within tol_y plus half an e4m3
+    spacing (at the block exponent e and the magnitude |out_ref| + tol_y) of
+    out_ref, or, for a block maximum in [448, 512) * 2^e, at most the saturation
+    distance beyond 448 * 2^e; the block exponent may differ by one from that of
+    the exact block maximum only where that maximum lies within its tolerance of
+    a power of two."""
+    from .formats import decode_e4m3
+    from .quant import mx_scale_code
+    y = np.asarray(out_ref, np.float64)
+    t = np.asarray(tol_y, np.float64) * np.ones_like(y)
+    M, N = y.shape
+    e = np.repeat(np.asarray(codes, np.int64) - 127, 32, axis=1)          # [M, N]
+    dq = decode_e4m3(q) * np.ldexp(1.0, e)
+    scaled = (np.abs(y) + t) * np.ldexp(1.0, -e)
+    allow = t + _e4m3_half_spacing(scaled) * np.ldexp(1.0, e)
+    sat = np.maximum(np.abs(y) + t - 448.0 * np.ldexp(1.0, e), 0.0)
+    ok = np.abs(dq - y) <= allow + sat
+    # block exponents: exact unless the block maximum's band crosses a power of two
+    blk = np.abs(y).reshape(M, N // 32, 32)
+    tb = t.reshape(M, N // 32, 32)
+    amax = blk.max(axis=2)
+    lo = mx_scale_code(np.maximum(blk - tb, 0).max(axis=2).astype(np.float32)).astype(np.int64)
+    hi = mx_scale_code((blk + tb).max(axis=2).astype(np.float32)).astype(np.int64)
+    c = np.asarray(codes, np.int64)
+    ok_code = (c >= np.minimum(lo, mx_scale_code(amax.astype(np.float32)))) & (c <= hi)
+    return ok & np.repeat(ok_code, 32, axis=1)

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {
         "fp8gemm_quantize_workspace_size", "fp8gemm_quantize", "fp8gemm_quantize_ex",
         "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex", "fp8gemm_workspace_size_kn",
-        "fp8gemm_run_kn",
+        "fp8gemm_run_kn", "fp8gemm_run_mxout",
         "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run", "fp8gemm_status_string",
         "fp8gemm_version"}
     raw = ctypes.CDLL(F.library_path())
@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert F.fp8gemm_version() == 130
+    assert F.fp8gemm_version() == 140
     for code, name in [(0, "FP8GEMM_SUCCESS"), (1, "FP8GEMM_ERROR_INVALID_VALUE"),
                        (2, "FP8GEMM_ERROR_MISALIGNED"), (3, "FP8GEMM_ERROR_NOT_SUPPORTED"),
                        (4, "FP8GEMM_ERROR_WORKSPACE"), (5, "FP8GEMM_ERROR_LAUNCH"),
@@ -170,6 +170,22 @@ def test_fp4_validation(lib):
     need = F.fp8gemm_workspace_size_kn(64, 64, 128, 2)
     assert lib.fp8gemm_run_kn(64, 64, 128, P, 64, 4, P2, 64, 4, 2, P3, P3 + 256, 0, 0,
                               P3 + 4096, 64, 1, P3 + (1 << 20), need, None) == NOT_SUPPORTED
+
+
+def test_mxout_validation(lib):
+    """fp8gemm_run_mxout: e4m3 codes plus E8M0 per 32 columns; checked before any HIP call."""
+    def run(N=64, C=P3 + 4096, ldc=64, cs=P3 + 65536, ldcs=2, **kw):
+        return lib.fp8gemm_run_mxout(kw.get("M", 64), N, 128, P, 128, kw.get("fa", 0), P2, 128,
+                                     kw.get("fb", 0), kw.get("mode", 1), P3, P3 + 256, 0, 0, C,
+                                     ldc, cs, ldcs, 0, 0, None)
+    assert run(M=0) == SUCCESS
+    assert run(cs=0) == INVALID
+    assert run(ldcs=1) == INVALID                 # ldcs < N/32
+    assert run(N=48, ldc=48) == NOT_SUPPORTED     # N % 32
+    assert run(ldc=72) == MISALIGNED              # byte rows of codes: ldc % 16
+    assert run(ldc=32) == INVALID                 # ldc < N
+    assert run(C=P3 + 4100) == MISALIGNED
+    assert run(mode=7) == INVALID
 
 
 def test_row_major_b_validation(lib):
