@@ -159,6 +159,11 @@ def gemm_bytes(w, code_bytes: float = 1.0) -> int:
     return mb + 2 * w.M * w.N
 
 
+def gemm_bytes_mxout(w, code_bytes: float = 1.0) -> int:
+    """The same with the output as e4m3 codes plus one E8M0 code per 32 columns."""
+    return gemm_bytes(w, code_bytes) - 2 * w.M * w.N + w.M * w.N + w.M * (w.N // 32)
+
+
 def cpu_baseline(w, rows: int, fmt: str = "e4m3"):
     """Oracle on a bounded sample: quantise `rows` rows of A and of B (element
     format fmt), then the float64 GEMM reference of that rows x rows x K block
@@ -200,8 +205,13 @@ def main():
                     help="element formats of the A and B codes (e4m3 or e5m2, or e2m1,e2m1 for "
                          "MXFP4 with the mx32 workload; dense only)")
     ap.add_argument("--epilogue", default="none", choices=["none", "bias", "bias+relu",
-                                                           "bias+gelu", "bias+silu"],
-                    help="fused epilogue of the GEMM (dense only)")
+                                                           "bias+gelu", "bias+silu", "mxout"],
+                    help="fused epilogue of the GEMM (dense only); mxout: the output quantised "
+                         "for the next layer (e4m3 + E8M0 per 32 columns)")
+    ap.add_argument("--b-layout", default="nk", choices=["nk", "kn"],
+                    help="kn: B row-major [K, N] (fp8gemm_run_kn, its transposing copy timed "
+                         "with the GEMM); B is then quantised once before timing (resident "
+                         "weights) and a step is quantise A + GEMM")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of A / columns of B in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -229,8 +239,12 @@ def main():
     w = WORKLOADS[args.workload]
     fmt_a, fmt_b = args.formats.split(",")
     act = args.epilogue.split("+")[1] if "+" in args.epilogue else "none"
-    use_bias = args.epilogue != "none"
-    if w.groups and (args.formats != "e4m3,e4m3" or use_bias):
+    mxout = args.epilogue == "mxout"
+    kn = args.b_layout == "kn"
+    if kn and (w.groups or mxout):
+        raise SystemExit("--b-layout kn applies to the dense workloads with a 16-bit output")
+    use_bias = args.epilogue not in ("none", "mxout")
+    if w.groups and (args.formats != "e4m3,e4m3" or use_bias or mxout):
         raise SystemExit("--formats and --epilogue apply to the dense workloads")
     fp4 = "e2m1" in (fmt_a, fmt_b)
     if fp4 and (fmt_a != fmt_b or w.mode != "mx32"):
@@ -278,6 +292,9 @@ def main():
         ws_b = torch.empty_like(ws_a)
     tdt = torch.bfloat16 if w.out == "bf16" else torch.float16
     C = torch.empty((w.M, w.N), dtype=tdt, device=dev)
+    if mxout:
+        Cq = torch.empty((w.M, w.N), dtype=torch.uint8, device=dev)
+        Cs = torch.empty((w.M, w.N // 32), dtype=torch.uint8, device=dev)
     bias = None
     if use_bias:
         import numpy as np
@@ -291,6 +308,11 @@ def main():
             F.grouped_gemm(qa, sa, offsets, qb.view(w.groups, w.N, w.K),
                            sb.view(w.groups, -1) if w.mode == "mx32" else sb.view(w.groups, w.N),
                            w.mode, w.out, out=C)
+        elif kn:
+            F.gemm(qa, sa, qb_kn, sb_kn, w.mode, w.out, out=C, fmt_a=fmt_a, fmt_b=fmt_b,
+                   bias=bias, activation=act, b_layout="kn")
+        elif mxout:
+            F.gemm_mxout(qa, sa, qb, sb, w.mode, out=Cq, out_scales=Cs, fmt_a=fmt_a, fmt_b=fmt_b)
         else:
             F.gemm(qa, sa, qb, sb, w.mode, w.out, out=C, fmt_a=fmt_a, fmt_b=fmt_b, bias=bias,
                    activation=act)
@@ -301,13 +323,19 @@ def main():
         F.quantize(Ad, w.mode, out=qa, scales=sa, workspace=ws_a, fmt=fmt_a)
         if ev is not None:
             ev[1].record()
-        F.quantize(Bd, w.mode, out=qb, scales=sb, workspace=ws_b, fmt=fmt_b)
+        if not kn:
+            F.quantize(Bd, w.mode, out=qb, scales=sb, workspace=ws_b, fmt=fmt_b)
         if ev is not None:
             ev[2].record()
         run_gemm()
         if ev is not None:
             ev[3].record()
 
+    if kn:   # resident row-major weights: quantised and laid out once, before timing
+        F.quantize(Bd, w.mode, out=qb, scales=sb, workspace=ws_b, fmt=fmt_b)
+        qb_kn = qb.t().contiguous()
+        sb_kn = sb.t().contiguous() if w.mode == "mx32" else sb
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -341,10 +369,10 @@ def main():
     # HBM-bound shapes (arithmetic intensity below the MFMA/HBM ridge): the roofline
     # is bytes over time; a cold-cache rate is measured as well, cycling the GEMM
     # over enough distinct operand copies (>= 512 MiB) that none is cache resident
-    gbytes = gemm_bytes(w, code_bytes)
+    gbytes = (gemm_bytes_mxout if mxout else gemm_bytes)(w, code_bytes)
     hbm_bound = flops / gbytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     cold = None
-    if hbm_bound and not w.groups and rows_b * kq >= (4 << 20):
+    if hbm_bound and not w.groups and not mxout and rows_b * kq >= (4 << 20):
         nsets = max(2, -(-(512 << 20) // (rows_b * kq)))
         qbs = [qb.clone() for _ in range(nsets)]
         qas = [qa.clone() for _ in range(nsets)]
@@ -391,7 +419,7 @@ def main():
         log(f"plain read context: {cold['hbm_read_context']}")
     gemm_gbs = gbytes / (gemm_ms * 1e-3) / 1e9
     # the committed counter summaries are of the default e4m3 GEMM without epilogue
-    default_variant = args.formats == "e4m3,e4m3" and not use_bias
+    default_variant = args.formats == "e4m3,e4m3" and args.epilogue == "none" and not kn
     traffic = measured_traffic(w.name) if default_variant else None
     if hbm_bound:
         roofline = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS,
@@ -417,8 +445,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "scale": w.mode,
                    "out": w.out, "groups": w.groups, "formats": [fmt_a, fmt_b],
-                   "epilogue": args.epilogue,
-                   "step": "quantize A + quantize B + GEMM"},
+                   "epilogue": args.epilogue, "b_layout": args.b_layout,
+                   "step": "quantize A + GEMM (row-major B resident, transposing copy inside "
+                           "the GEMM call)" if kn else "quantize A + quantize B + GEMM"},
         "roofline": roofline,
         "kernels": {
             "gemm": {"ms": round(gemm_ms, 5), "ms_median": round(gemm_med, 5),
@@ -426,8 +455,8 @@ def main():
                      "gbs_algorithmic": round(gemm_gbs, 1)},
             "quantize_a": {"ms": round(qa_ms, 4),
                            "gbs": round(quant_bytes_a / (qa_ms * 1e-3) / 1e9, 1)},
-            "quantize_b": {"ms": round(qb_ms, 4),
-                           "gbs": round(quant_bytes_b / (qb_ms * 1e-3) / 1e9, 1)},
+            "quantize_b": None if kn else {"ms": round(qb_ms, 4),
+                                           "gbs": round(quant_bytes_b / (qb_ms * 1e-3) / 1e9, 1)},
         },
     }
     if cold is not None:
