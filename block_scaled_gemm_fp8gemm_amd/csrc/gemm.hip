@@ -204,7 +204,7 @@ hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
     // persistent streams pay off from about eight tiles per CU on (measured)
     const bool many = big_tiles >= 8 * 256;
     // (the fused epilogue stages through the ring, so it never runs in a stream)
-    if constexpr (!FUSED) {
+    if constexpr (!FUSED && !std::is_same<OutT, uint8_t>::value) {
       if ((FP8GEMM_PERSISTENT || many) && all_interior<Big>(p))
         return launch_persistent<Big, MODE, OutT>(p, stream);
     }
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void splitk_kernel(GemmProblem p,
     }
   }
   const float ts = (MODE == kTensor) ? fsa[0] * fsb[0] : 1.0f;
-  if constexpr (FUSED)
+  if constexpr (FUSED || std::is_same<OutT, uint8_t>::value)
     epilogue_fused<Cfg, MODE, OutT>(sum, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N, ts,
                                     p.bias, p.act, p.cs, p.ldcs);
   else
@@ -406,16 +406,13 @@ hipError_t launch_plan(const GemmProblem& p, hipStream_t stream) {
   }
 }
 
-// kernels with the fused bias / activation epilogue only when it is asked for;
-// the e4m3 + MX-scale output (OutT = uint8_t) always runs the fused epilogue
+// kernels with the fused bias / activation epilogue only when it is asked for
+// (the e4m3 + MX-scale output, OutT = uint8_t, quantises interior tiles without
+// one straight from registers and the other tiles in the fused epilogue's loop)
 template <int MODE, typename OutT>
 hipError_t launch_any(const GemmProblem& p, hipStream_t stream) {
-  if constexpr (std::is_same<OutT, uint8_t>::value) {
-    return launch_plan<MODE, OutT, true>(p, stream);
-  } else {
-    if (p.bias != nullptr || p.act != kActNone) return launch_plan<MODE, OutT, true>(p, stream);
-    return launch_plan<MODE, OutT, false>(p, stream);
-  }
+  if (p.bias != nullptr || p.act != kActNone) return launch_plan<MODE, OutT, true>(p, stream);
+  return launch_plan<MODE, OutT, false>(p, stream);
 }
 
 }  // namespace

@@ -1432,6 +1432,74 @@ __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][C
   }
 }
 
+// The output quantised for the next layer, straight from registers (interior
+// tiles without bias or activation): e4m3 codes with one E8M0 code per 32
+// consecutive columns of a row, by the quantisers' MX rule.  A 32 x 32 block j
+// of row r is one MX block, held by lanes r (columns 8g .. 8g + 3) and r + 32
+// (8g + 4 .. 8g + 7): the block maximum is the lane's 16 values and one swap
+// with its partner (v_permlane32_swap); after encoding, a second swap of the
+// 4-byte groups leaves each lane two 8-byte runs of its row (columns 16k + 8h ..
+// 16k + 8h + 7).  Needs N % 32 == 0 (every interior tile is whole).
+template <class Cfg, int MODE>
+__device__ __forceinline__ void epilogue_direct_q(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                                  const uint8_t* lds, uint8_t* C, int64_t ldc,
+                                                  int m0, int n0, float tensor_scale,
+                                                  uint8_t* cs, int64_t ldcs) {
+  constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
+  const int h = lane >> 5;
+  const float* rsc = reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = wm * Cfg::WM + i * 32 + (lane & 31);   // tile row of this lane
+    float fa = 1.0f;
+    if (MODE == kTensor) fa = tensor_scale;
+    if (MODE == kRowwise) fa = rsc[r];
+    uint8_t* crow = C + (int64_t)(m0 + r) * ldc + n0 + wn * Cfg::WN;
+    uint8_t* srow = cs + (int64_t)(m0 + r) * ldcs + ((n0 + wn * Cfg::WN) >> 5);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      float v[16];
+      float a = 0.0f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = j * 32 + 8 * g + 4 * h;             // wave-local column of value 0
+        v4f fb{1.0f, 1.0f, 1.0f, 1.0f};
+        if (MODE == kRowwise) fb = *reinterpret_cast<const v4f*>(rsc + Cfg::BM + wn * Cfg::WN + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[4 * g + e] = acc[i][j][4 * g + e] * fa;
+          if (MODE == kRowwise) v[4 * g + e] *= fb[e];
+          a = fmaxf(a, fabsf(v[4 * g + e]));
+        }
+      }
+      const auto am = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a),
+                                                       false, false);
+      // one of the pair is this lane's own maximum, the other its partner's
+      a = fmaxf(__uint_as_float(am[0]), __uint_as_float(am[1]));
+      const uint32_t code = mx_code_from_amax<kE4M3>(a);
+      const int e = 127 - (int)code;
+      uint32_t w[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        w[g] = encode4_e4m3(ldexpf(v[4 * g], e), ldexpf(v[4 * g + 1], e), ldexpf(v[4 * g + 2], e),
+                            ldexpf(v[4 * g + 3], e));
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        // low half keeps group 2k and takes the high half's; high half keeps 2k + 1
+        const auto sw = __builtin_amdgcn_permlane32_swap(w[2 * k], w[2 * k + 1], false, false);
+        uint2 out;
+        out.x = sw[0];
+        out.y = sw[1];
+        *reinterpret_cast<uint2*>(crow + j * 32 + 16 * k + 8 * h) = out;
+      }
+      if (h == 0) srow[j] = (uint8_t)code;
+    }
+  }
+}
+
 // Fused epilogue (bias, activation).  The scaled fp32 tile goes through LDS, one
 // block of 32 rows per wavefront at a time, and the bias, the activation, the
 // cast and the stores run in a loop over 16-byte pieces: four copies of the
@@ -1551,6 +1619,8 @@ __device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, 
       if constexpr (FUSED) {
         epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias,
                                         act, cs, ldcs);
+      } else if constexpr (std::is_same<OutT, uint8_t>::value) {
+        epilogue_direct_q<Cfg, MODE>(acc, lds, C, ldc, m0, n0, tensor_scale, cs, ldcs);
       } else {
 #if FP8GEMM_DIRECT_EPILOGUE
         epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, n0, tensor_scale);
@@ -1563,7 +1633,7 @@ __device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, 
   }
   v16f acc[Cfg::kFragM][Cfg::kFragN];
   mainloop<Cfg, MODE, KALIGNED && !kF4>(op, lds, acc);
-  if constexpr (FUSED)
+  if constexpr (FUSED || std::is_same<OutT, uint8_t>::value)
     epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act,
                                     cs, ldcs);
   else
