@@ -1377,6 +1377,64 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFr
   }
 }
 
+// Bias (and ReLU) epilogue of a full tile from registers, the layout of
+// epilogue_direct below.  Each wave first copies the bias of its WN columns into
+// a wave-private stretch of the (free) ring, then reads four columns at a time
+// like the row-wise column scales (bias == nullptr: zeros).
+template <class Cfg, int MODE, typename OutT>
+__device__ __forceinline__ void epilogue_direct_bias(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                                     uint8_t* lds, OutT* C, int64_t ldc,
+                                                     int m0, int n0, float tensor_scale,
+                                                     const float* bias, bool relu) {
+  constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
+  const int h = lane >> 5;
+  const float* rsc = reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff);
+  const int nw = n0 + wn * Cfg::WN;                      // first column of this wave
+  static_assert(Cfg::kWaves * Cfg::WN * 4 <= Cfg::kSlots * Cfg::kSlotBytes, "bias fits the ring");
+  float* bl = reinterpret_cast<float*>(lds) + wave * Cfg::WN;
+#pragma unroll
+  for (int c = lane; c < Cfg::WN; c += 64) bl[c] = bias != nullptr ? bias[nw + c] : 0.0f;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * Cfg::WM + i * 32 + (lane & 31);
+      float fa = 1.0f;
+      if (MODE == kTensor) fa = tensor_scale;
+      if (MODE == kRowwise) fa = rsc[r];
+      OutT* crow = C + (int64_t)(m0 + r) * ldc + nw;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        uint2 w[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int g = 2 * k + q;
+          const int c = j * 32 + 8 * g + 4 * h;
+          v4f fb{1.0f, 1.0f, 1.0f, 1.0f};
+          if (MODE == kRowwise) fb = *reinterpret_cast<const v4f*>(rsc + Cfg::BM + wn * Cfg::WN + c);
+          const v4f bv = *reinterpret_cast<const v4f*>(bl + c);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = acc[i][j][4 * g + e] * fa;
+            if (MODE == kRowwise) v[e] *= fb[e];
+            v[e] += bv[e];
+            if (relu) v[e] = fmaxf(v[e], 0.0f);
+          }
+          w[q] = pack4<OutT>(v[0], v[1], v[2], v[3]);
+        }
+        const auto sx = __builtin_amdgcn_permlane32_swap(w[0].x, w[1].x, false, false);
+        const auto sy = __builtin_amdgcn_permlane32_swap(w[0].y, w[1].y, false, false);
+        const v4i out{(int)sx[0], (int)sy[0], (int)sx[1], (int)sy[1]};
+        *reinterpret_cast<v4i*>(crow + j * 32 + 16 * k + 8 * h) = out;
+      }
+    }
+  }
+}
+
 // Epilogue of a full tile straight from registers.  After the MFMAs a lane holds,
 // for each 32 x 32 block and group g of four accumulators, four consecutive
 // output columns 8g + 4h .. 8g + 4h + 3 (h = lane / 32) of row lane % 32.  One
@@ -1384,12 +1442,20 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFr
 // with group 2k of the high half, after which every lane owns eight consecutive
 // columns (16 bytes) of its row: C is written with 16-byte stores and no LDS
 // staging, so the epilogue costs a few hundred instructions and no waits.
-template <class Cfg, int MODE, typename OutT>
+// BIAS (fused kernels, interior tiles, no activation or ReLU): the bias of the
+// lane's 16 columns of block j is loaded once per j and added after the scales,
+// then ReLU when `relu`; the heavier activations take the staged loop below.
+template <class Cfg, int MODE, typename OutT, bool BIAS = false>
 __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
-                                                const uint8_t* lds, OutT* C, int64_t ldc, int m0,
-                                                int n0, float tensor_scale, int rbuf = 0) {
+                                                uint8_t* lds, OutT* C, int64_t ldc, int m0,
+                                                int n0, float tensor_scale, int rbuf = 0,
+                                                const float* bias = nullptr, bool relu = false) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   static_assert(sizeof(OutT) == 2, "16-bit outputs");
+  if constexpr (BIAS) {
+    epilogue_direct_bias<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, n0, tensor_scale, bias, relu);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
@@ -1616,7 +1682,14 @@ __device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, 
     if (interior_tile<Cfg, MODE>(op)) {
       v16f acc[Cfg::kFragM][Cfg::kFragN];
       mainloop_interior<Cfg, MODE>(op, lds, acc);
-      if constexpr (FUSED) {
+      if constexpr (FUSED && !std::is_same<OutT, uint8_t>::value) {
+        if (act == kActNone || act == kActRelu)
+          epilogue_direct<Cfg, MODE, OutT, true>(acc, lds, C, ldc, m0, n0, tensor_scale, 0, bias,
+                                                 act == kActRelu);
+        else
+          epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias,
+                                          act, cs, ldcs);
+      } else if constexpr (FUSED) {
         epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias,
                                         act, cs, ldcs);
       } else if constexpr (std::is_same<OutT, uint8_t>::value) {
