@@ -308,7 +308,7 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
         out = torch.empty((M, ldc), dtype=tdt, device=qa.device)[:, :N]
     m = SCALE_MODES[mode]
     kn = b_layout == "kn"
-    need = 0 if fp4 else (fp8gemm_workspace_size_kn if kn else fp8gemm_workspace_size)(M, N, K, m)
+    need = (fp8gemm_workspace_size_kn if kn else fp8gemm_workspace_size)(M, N, K, m)
     if need and workspace is None:
         workspace = gemm_workspace(qa.device, need)
     if bias is not None:
@@ -347,7 +347,7 @@ def gemm_mxout(qa, sa, qb, sb, mode: str = "tensor", out=None, out_scales=None,
     if out_scales is None:
         out_scales = torch.empty((M, N // 32), dtype=torch.uint8, device=qa.device)
     m = SCALE_MODES[mode]
-    need = 0 if fp4 else fp8gemm_workspace_size(M, N, K, m)
+    need = fp8gemm_workspace_size(M, N, K, m)
     if need and workspace is None:
         workspace = gemm_workspace(qa.device, need)
     if bias is not None:

@@ -153,7 +153,9 @@ fp8gemm_status run_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int6
   fp8gemm_status st = check_gemm_common(M, N, K, A, lda, B, ldb, mode, scale_a, scale_b, C, ldc,
                                         out_dtype, fp4 ? 2 : 1);
   if (st != FP8GEMM_SUCCESS) return st;
-  const size_t need = fp4 ? 0 : fp8gemm_workspace_size(M, N, K, mode);
+  // FP4 shapes split along K at most as often as FP8 ones of the same element
+  // count, so the query (K in elements) covers them too
+  const size_t need = fp8gemm_workspace_size(M, N, K, mode);
   if (need > 0 && (!workspace || workspace_bytes < need)) return FP8GEMM_ERROR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return FP8GEMM_ERROR_MISALIGNED;
 

@@ -239,7 +239,10 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int mode) {
   if (mid_tiles >= 128 || K < 1024) return plan;
   const int64_t tm = (M + SplitCfg::BM - 1) / SplitCfg::BM;
   const int64_t tn = (N + SplitCfg::BN - 1) / SplitCfg::BN;
-  const int64_t gran = mode == kMx32 ? 512 : 128;    // K slices stay on the interior path
+  // K slices stay on the interior path: whole MX code groups (512 bytes of K, FP4
+  // 256: K counts bytes there, and an FP4 plan never splits more than the FP8
+  // plan of the same element count, so the workspace query covers both)
+  const int64_t gran = mode == kMx32 ? 16 * kBlkBytes : 128;
   int best = 1;
   for (int s = 2; s <= 16; s *= 2) {
     if (K % (s * gran) != 0 || K / s < 512) break;
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void splitk_kernel(GemmProblem p,
 
   v16f acc[FM][FN];
   if (interior_tile<Cfg, MODE>(op)) mainloop_interior<Cfg, MODE, 4>(op, lds, acc);
-  else mainloop<Cfg, MODE, true>(op, lds, acc);
+  else mainloop<Cfg, MODE, !kF4>(op, lds, acc);
 
   // partial tile: float4 r of thread x at [tile][slice][r][x] (coalesced per r)
   const int tiles = tiles_m * (int)((p.N + Cfg::BN - 1) / Cfg::BN);
@@ -397,13 +400,10 @@ hipError_t launch_split(const GemmProblem& p, const SplitPlan& plan, hipStream_t
 
 template <int MODE, typename OutT, bool FUSED>
 hipError_t launch_plan(const GemmProblem& p, hipStream_t stream) {
-  if constexpr (kF4) {
-    return launch_mode_f4<MODE, OutT, FUSED>(p, stream);      // no split-K for FP4
-  } else {
-    const SplitPlan plan = plan_split(p.M, p.N, p.K, MODE);
-    if (plan.splits > 1) return launch_split<MODE, OutT, FUSED>(p, plan, stream);
-    return launch_mode<MODE, OutT, FUSED>(p, stream);
-  }
+  const SplitPlan plan = plan_split(p.M, p.N, p.K, MODE);
+  if (plan.splits > 1) return launch_split<MODE, OutT, FUSED>(p, plan, stream);
+  if constexpr (kF4) return launch_mode_f4<MODE, OutT, FUSED>(p, stream);
+  else return launch_mode<MODE, OutT, FUSED>(p, stream);
 }
 
 // kernels with the fused bias / activation epilogue only when it is asked for

@@ -826,10 +826,14 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
     // code bytes of step t + 1 live in the group of K tile (t + 1) / 2
     constexpr bool kNextGroup = p && q == kGroupTiles - 1;
     // copies allowed in flight once K tile u + 1 has landed: those of K tiles
-    // u + 2 .. u + NS - 1 and a code group issued after K tile u + 1's copies,
-    // unless this step reads that group (its last K tile)
+    // u + 2 .. u + NS - 1 and a code group issued after K tile u + 1's copies.
+    // On the last K tile of a group this step also reads the next group, whose
+    // copy went out in K tile u - q right after that tile's copies of K tile
+    // u - q + NS: then only the tile copies of the q - 1 K tiles since may remain.
+    constexpr int kAfterTile = (NS - 2) * kLoads + ((kMx && q >= 1 && q + 1 <= NS) ? kCodeLoads : 0);
+    constexpr int kAfterCode = (q - 1) * kLoads;
     constexpr int kWaitOdd =
-        (NS - 2) * kLoads + ((kMx && q >= 1 && q + 1 <= NS && !kNextGroup) ? kCodeLoads : 0);
+        (kNextGroup && kAfterCode < kAfterTile) ? kAfterCode : kAfterTile;
     const int u = t >> 1;
     __builtin_amdgcn_sched_barrier(0);
     if (p) {

@@ -162,8 +162,8 @@ fp8gemm_status fp8gemm_run(int64_t M, int64_t N, int64_t K, const uint8_t* A, in
 /*          pairing), or E2M1 for both (MXFP4 x MXFP4: mode MX32 only, else     */
 /*          NOT_SUPPORTED; A holds two codes per byte, element (m,k) in byte    */
 /*          A[m*lda + k/2], likewise B[n*ldb + k/2]; lda, ldb >= K/2 bytes;     */
-/*          K % 32 == 0; scales uint8 [M][K/32] and [N][K/32]; no workspace,    */
-/*          NULL allowed).                                                      */
+/*          K % 32 == 0; scales uint8 [M][K/32] and [N][K/32]; the workspace    */
+/*          of fp8gemm_workspace_size(M, N, K, MX32), K in elements).           */
 /* bias   : device float[N], 4-byte aligned, or NULL (no bias).               */
 /* activation: fp8gemm_activation, applied in fp32 after the scales and bias.   */
 /* The scale modes, layouts, workspace and errors are those of fp8gemm_run      */

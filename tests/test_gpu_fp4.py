@@ -108,23 +108,27 @@ def test_gemm_fp4_small(out, shape):
     _assert(C, Cr, Ar, out, f"e2m1 {out} {shape}")
 
 
-@pytest.mark.parametrize("shape", [(512, 512, 1024), (4096, 4096, 1024), (4096, 4096, 1536)])
+@pytest.mark.parametrize("shape", [(512, 512, 1024), (4096, 4096, 1024), (4096, 4096, 1536),
+                                   (128, 4096, 4096), (96, 1000, 6144)])
 def test_gemm_fp4_interior(shape):
     """Full tiles: 128 x 128 tiles (16 tiles) and 256 x 256 tiles (256 tiles), K a
-    whole number of code groups, in two and in three groups."""
+    whole number of code groups, in two and in three groups; and split-K shapes
+    with few output tiles (decode-like M = 128, and ragged M and N with three
+    code groups per K slice)."""
     M, N, K = shape
     qa, sa, qb, sb = _operands(M, N, K, seed=N + K)
     announce("gemm e2m1 interior", shape)
     C = _run(qa, sa, qb, sb)
     torch.cuda.synchronize()
     rng = np.random.default_rng(K)
-    blocks = [(0, 0), (M - 128, N - 128)] + [
-        (int(r) * 128, int(c) * 128) for r, c in rng.integers(0, [M // 128, N // 128], (3, 2))]
+    bm, bn = min(128, M), 128
+    blocks = [(0, 0), (M - bm, N - bn)] + [
+        (int(r) * bm, int(c) * bn) for r, c in rng.integers(0, [M // bm, N // bn], (3, 2))]
     for r0, c0 in blocks:
-        ri, ci = np.arange(r0, r0 + 128), np.arange(c0, c0 + 128)
+        ri, ci = np.arange(r0, r0 + bm), np.arange(c0, c0 + bn)
         Cr, Ar = O.gemm_reference(qa, sa, qb, sb, "mx32", rows=ri, cols=ci, fmt_a="e2m1",
                                   fmt_b="e2m1")
-        _assert(to_host(C[r0:r0 + 128, c0:c0 + 128]), Cr, Ar, "bf16",
+        _assert(to_host(C[r0:r0 + bm, c0:c0 + bn]), Cr, Ar, "bf16",
                 f"e2m1 {shape} block {(r0, c0)}")
 
 
