@@ -394,26 +394,29 @@ def main():
                 "operand_sets": nsets, "note": "back-to-back launches over distinct operand copies"}
         del qbs, qas
         log(f"cold-cache GEMM: {cold}")
-        # context: a plain device read (torch sum over int64 words) of the same
-        # number of bytes from HBM, rotated over distinct buffers, and of 1 GiB
+        # context: a plain device read of the same number of bytes from HBM,
+        # rotated over distinct buffers, and of 1 GiB: torch row sums over 16 KiB
+        # rows of int64 words (one workgroup per row, no cross-workgroup reduction)
         def read_rate(nbytes, sets, reps):
-            bufs = [torch.ones(nbytes // 8, dtype=torch.int64, device=dev) for _ in range(sets)]
+            rows = nbytes // 16384
+            bufs = [torch.ones((rows, 2048), dtype=torch.int64, device=dev) for _ in range(sets)]
             for b in bufs:
-                b.sum()
+                b.sum(dim=1)
             torch.cuda.synchronize()
             r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             r0.record()
             for _ in range(reps):
                 for b in bufs:
-                    b.sum()
+                    b.sum(dim=1)
             r1.record()
             torch.cuda.synchronize()
             ms = r0.elapsed_time(r1) / (reps * sets)
             del bufs
-            return {"bytes": nbytes, "ms": round(ms, 5), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            nb = rows * 16384
+            return {"bytes": nb, "ms": round(ms, 5), "gbs": round(nb / (ms * 1e-3) / 1e9, 1)}
         gb = gbytes // 8 * 8
         cold["hbm_read_context"] = {
-            "kernel": "torch sum over int64 words (a plain device read)",
+            "kernel": "torch row sums over 16 KiB rows of int64 words (a plain device read)",
             "same_bytes": read_rate(gb, max(2, -(-(512 << 20) // gb)), 4),
             "one_gib": read_rate(1 << 30, 2, 3)}
         log(f"plain read context: {cold['hbm_read_context']}")

@@ -225,3 +225,17 @@ def test_workload_mx8192_sampled_tiles():
     corners = [(0, 0), (0, w.N - 128), (w.M - 128, 0), (w.M - 128, w.N - 128)]
     rand = [(int(r) * 128, int(c) * 128) for r, c in rng.integers(0, w.M // 128, size=(12, 2))]
     _end_to_end("mx8192", tiles=corners + rand)
+
+
+def test_gemm_splitk_growing_tile_count():
+    """Split shapes with more output tiles after fewer, on the one workspace the
+    binding keeps: a later call's tile counters never lie where an earlier call
+    left partial tiles (the counters have a fixed place)."""
+    shapes = [(128, 2048, 4096), (128, 8192, 4096), (64, 8192, 2048), (128, 2048, 4096)]
+    for i, (M, N, K) in enumerate(shapes):
+        assert F.fp8gemm_workspace_size(M, N, K, F.SCALE_MODES["rowwise"]) > 0, "not split"
+        qa, sa, qb, sb = _oracle_operands(M, N, K, "rowwise", seed=40 + i, dist="mx_block")
+        announce("gemm split-K growing", (M, N, K))
+        C = to_host(_run_gpu(qa, sa, qb, sb, "rowwise", "bf16"))
+        Cr, Ar = O.gemm_reference(qa, sa, qb, sb, "rowwise")
+        assert_within_bound(C, Cr, Ar, "bf16", f"split-K after other shapes {(M, N, K)}")
