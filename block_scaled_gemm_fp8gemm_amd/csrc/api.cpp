@@ -213,11 +213,17 @@ fp8gemm_status fp8gemm_run_mxout(int64_t M, int64_t N, int64_t K, const uint8_t*
                    workspace_bytes, stream);
 }
 
-// Row-major B: the workspace holds the K-contiguous copy of B ([N][K] bytes), for
-// MX its codes ([N][K/32]), each rounded up to 256 bytes, then the GEMM's own
-// workspace.
+// Row-major B: the workspace starts with the GEMM's own workspace (at least the
+// split-K counter head, so the counters keep their fixed place and a workspace
+// shared with fp8gemm_run calls never has them overwritten), then the
+// K-contiguous copy of B ([N][K] bytes) and, for MX, its codes ([N][K/32]), each
+// rounded up to 256 bytes.
 namespace {
 constexpr int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+int64_t kn_head_bytes(int64_t M, int64_t N, int64_t K, int mode) {
+  const int64_t g = (int64_t)fp8gemm_workspace_size(M, N, K, mode);
+  return round256(g > fp8gemm::kSplitCounterBytes ? g : fp8gemm::kSplitCounterBytes);
+}
 int64_t kn_b_bytes(int64_t N, int64_t K) { return round256(N * K); }
 int64_t kn_code_bytes(int64_t N, int64_t K, int mode) {
   return mode == kMx32 ? round256(N * (K / 32)) : 0;
@@ -226,8 +232,7 @@ int64_t kn_code_bytes(int64_t N, int64_t K, int mode) {
 
 size_t fp8gemm_workspace_size_kn(int64_t M, int64_t N, int64_t K, int mode) {
   if (!valid_mode(mode) || M <= 0 || N <= 0 || K <= 0) return 0;
-  return (size_t)(kn_b_bytes(N, K) + kn_code_bytes(N, K, mode)) +
-         fp8gemm_workspace_size(M, N, K, mode);
+  return (size_t)(kn_head_bytes(M, N, K, mode) + kn_b_bytes(N, K) + kn_code_bytes(N, K, mode));
 }
 
 fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
@@ -252,10 +257,10 @@ fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A,
   if (!workspace || workspace_bytes < need) return FP8GEMM_ERROR_WORKSPACE;
   if (!aligned(workspace, 16)) return FP8GEMM_ERROR_MISALIGNED;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint8_t* bt = ws;
-  uint8_t* codes_t = ws + kn_b_bytes(N, K);
-  uint8_t* ws_gemm = codes_t + kn_code_bytes(N, K, mode);
-  const size_t gemm_bytes = workspace_bytes - (size_t)(ws_gemm - ws);
+  uint8_t* ws_gemm = ws;
+  uint8_t* bt = ws + kn_head_bytes(M, N, K, mode);
+  uint8_t* codes_t = bt + kn_b_bytes(N, K);
+  const size_t gemm_bytes = fp8gemm_workspace_size(M, N, K, mode);
   // the GEMM's checks run first, on the transposed operands, so a call they
   // reject enqueues nothing
   const int64_t ldbt = K;                     // K % 16 == 0: 16-byte rows

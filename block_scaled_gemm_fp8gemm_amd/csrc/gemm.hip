@@ -250,8 +250,8 @@ constexpr int kSplitTargetWgs = 512;       // two workgroups per CU
 // 128, so fewer than kMaxSplitTiles split tiles, and a later call of another
 // shape on the same workspace never finds partial tiles of an earlier call where
 // its counters are (every call leaves the counters it used at zero).
-constexpr int64_t kMaxSplitTiles = 1024;
-constexpr int64_t kCounterBytes = kMaxSplitTiles * 4;
+constexpr int64_t kMaxSplitTiles = kSplitCounterBytes / 4;
+constexpr int64_t kCounterBytes = kSplitCounterBytes;
 static_assert(128 * 128 * 128 / (SplitCfg::BM * SplitCfg::BN) <= kMaxSplitTiles,
               "counters for every split plan");
 

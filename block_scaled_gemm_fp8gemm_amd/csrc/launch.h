@@ -47,6 +47,10 @@ struct GemmProblem {
   int64_t ldcs = 0;
 };
 
+// The split-K arrival counters: the first kSplitCounterBytes of a GEMM workspace,
+// whatever the shape (every call leaves the counters it used at zero).
+constexpr int64_t kSplitCounterBytes = 4096;
+
 // Device workspace a dense GEMM of this shape needs (0: none).  Shapes with too
 // few output tiles to fill the GPU are split along K; the workspace then holds
 // the fp32 partial tiles and one arrival counter per output tile.  The counters

@@ -142,8 +142,10 @@ fp8gemm_status fp8gemm_quantize_ex(const float* x, int64_t rows, int64_t k, int6
 /* M, N >= 0 (either 0: SUCCESS, nothing enqueued).  K > 0, multiple of 16     */
 /* (32 for MX32).  lda, ldb >= K and multiples of 16; ldc >= N with ldc*2 a     */
 /* multiple of 16; A, B, C 16-byte aligned; scale arrays 4-byte aligned.        */
-/* workspace: fp8gemm_workspace_size() bytes (may be 0 -> NULL allowed); it must */
-/* be zero-filled before its first use and is left zero-filled by every call.   */
+/* workspace: fp8gemm_workspace_size() bytes (may be 0 -> NULL allowed).  Its    */
+/* first 4 KiB hold split-K arrival counters: zero-fill the workspace before    */
+/* its first use; every call leaves the counters at zero (the rest is scratch), */
+/* so one workspace serves calls of every shape, including fp8gemm_run_kn.      */
 /* Accuracy: |C - C_ref| <= 1e-3 * sum_k|dq_a*dq_b| + 1 ulp of the output type. */
 /* ------------------------------------------------------------------------- */
 size_t fp8gemm_workspace_size(int64_t M, int64_t N, int64_t K, int mode);
@@ -223,7 +225,9 @@ fp8gemm_status fp8gemm_run_mxout(int64_t M, int64_t N, int64_t K, const uint8_t*
 /* copies B and its MX codes into the                                           */
 /* K-contiguous layout in the workspace (one HBM pass over B), then runs the    */
 /* GEMM: workspace is fp8gemm_workspace_size_kn() bytes, 16-byte aligned,       */
-/* zero-filled before its first use (never NULL: the copy lives there).         */
+/* zero-filled before its first use (never NULL: the copy lives there).  Its    */
+/* first 4 KiB are the counters of fp8gemm_run (left at zero); the copies come  */
+/* after the GEMM's own workspace, so the two entry points may share one.       */
 /* ------------------------------------------------------------------------- */
 size_t fp8gemm_workspace_size_kn(int64_t M, int64_t N, int64_t K, int mode);
 

@@ -75,3 +75,20 @@ def test_gemm_row_major_b_e5m2_fused():
     o_ref, y_ref = O.epilogue_reference(Cr, Ar, bias, "relu")
     tol = O.epilogue_tolerance(o_ref, y_ref, Ar, "relu", "bf16")
     assert np.all(np.abs(C - o_ref) <= tol)
+
+
+def test_row_major_b_shares_the_workspace_with_split_k():
+    """Row-major-B calls and K-contiguous split-K calls of different shapes share the
+    binding's one workspace: the copies of B never land on the split-K counters."""
+    seq = [("nk", (128, 4096, 4096)), ("kn", (128, 8192, 2048)), ("nk", (128, 8192, 2048)),
+           ("kn", (300, 260, 512)), ("nk", (64, 2048, 4096)), ("kn", (128, 4096, 4096))]
+    for i, (layout, (M, N, K)) in enumerate(seq):
+        qa, sa, qb, sb = _operands(M, N, K, "rowwise", seed=60 + i)
+        announce("gemm shared workspace", layout, (M, N, K))
+        if layout == "kn":
+            C = to_host(_run_kn(qa, sa, qb, sb, "rowwise"))
+        else:
+            C = to_host(F.gemm(to_dev(qa, 16), scale_to_dev(sa, "rowwise"), to_dev(qb, 16),
+                               scale_to_dev(sb, "rowwise"), "rowwise", "bf16"))
+        Cr, Ar = O.gemm_reference(qa, sa, qb, sb, "rowwise")
+        assert_within_bound(C, Cr, Ar, "bf16", f"shared workspace {layout} {(M, N, K)}")
