@@ -156,3 +156,27 @@ def test_quantize_then_gemm_fp4():
     qbr, sbr = Q.quantize_mx(B, "e2m1")
     Cr, Ar = O.gemm_reference(qar, sar, qbr, sbr, "mx32", fmt_a="e2m1", fmt_b="e2m1")
     _assert(C, Cr, Ar, "bf16", "quantize + gemm e2m1")
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 32), (1, 33, 64), (65, 1, 96), (2, 64, 32)])
+def test_gemm_fp4_degenerate(shape):
+    """Single rows / columns and the smallest K (one 32-element block, 16 bytes)."""
+    M, N, K = shape
+    qa, sa, qb, sb = _operands(M, N, K, seed=M * 31 + N + K)
+    announce("gemm e2m1 degenerate", shape)
+    C = to_host(_run(qa, sa, qb, sb))
+    Cr, Ar = O.gemm_reference(qa, sa, qb, sb, "mx32", fmt_a="e2m1", fmt_b="e2m1")
+    _assert(C, Cr, Ar, "bf16", f"e2m1 degenerate {shape}")
+
+
+def test_quantize_fp4_block_maxima_at_binade_edges():
+    """Block maxima at 4 * 2^j, 6 * 2^j and just below 8 * 2^j (the top of the binade
+    the shared exponent maps to [4, 8)), and just below 4 * 2^j (one exponent less)."""
+    rows = []
+    for j in (-10, -1, 0, 3, 20):
+        for top in (4.0, 6.0, np.nextafter(np.float32(8.0), np.float32(0)),
+                    np.nextafter(np.float32(4.0), np.float32(0))):
+            row = np.linspace(-top, top, 32).astype(np.float32) * np.float32(2.0 ** j)
+            rows.append(row)
+    x = np.stack(rows).astype(np.float32)
+    _check_quant(x, "binade edges")

@@ -102,3 +102,15 @@ def test_mxout_feeds_the_next_gemm():
     Cr, Ar = O.gemm_reference(q, c, q2, s2, "mx32")          # from the GPU's own layer-1 codes
     ok = O.within_bound(to_host(C2), Cr, Ar, "bf16")
     assert ok.all(), f"{int((~ok).sum())} outputs of the second GEMM outside the bound"
+
+
+@pytest.mark.parametrize("shape,fmt", [((1, 32, 64), "e4m3"), ((2, 64, 32), "e5m2"),
+                                       ((130, 96, 160), "e5m2")])
+def test_mxout_degenerate_and_e5m2(shape, fmt):
+    """One 32-column block, a single row, the smallest K, and e5m2 operands."""
+    M, N, K = shape
+    mode = "mx32"
+    qa, sa, qb, sb = _operands(M, N, K, mode, fmt, seed=M + 7 * N + K)
+    announce("gemm mxout degenerate", fmt, shape)
+    q, c = _run(qa, sa, qb, sb, mode, fmt)
+    _check(qa, sa, qb, sb, mode, fmt, q=q, c=c, what=f"mxout {fmt} {shape}")
