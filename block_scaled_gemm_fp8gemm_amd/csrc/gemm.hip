@@ -227,10 +227,12 @@ hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
 // runs the epilogue.
 // ---------------------------------------------------------------------------
 // FP8GEMM_SPLIT_CFG (tuning switch): 1 (default) 64 x 64 tiles, one workgroup per
-// CU; 0 128 x 64 tiles; 2 64 x 64 tiles, two workgroups per CU.  For M = 128,
-// N = K = 4096 the 64 x 64 tiles split K in two instead of four and halve the
-// fp32 partials exchanged (8 -> 4 MiB written): 14.9 -> 13.5 us (measured; the
-// two-per-CU form 14.3 us).
+// CU; 0 128 x 64 tiles; 2 64 x 64 tiles, two workgroups per CU; 3 64 x 64 tiles
+// with an eight-deep ring of 128-K tiles.  For M = 128, N = K = 4096 the 64 x 64
+// tiles split K in two instead of four and halve the fp32 partials exchanged
+// (8 -> 4 MiB written): 14.9 -> 13.5 us (measured; two per CU 14.3 us; the
+// eight-deep ring 14.8 against 14.2 us on another box, so the copy stream of a
+// slice is not bound by the bytes in flight).
 #ifndef FP8GEMM_SPLIT_CFG
 #define FP8GEMM_SPLIT_CFG 1
 #endif
@@ -239,6 +241,9 @@ using SplitCfg = TileCfg<128, 64, 64, 32, 8, 1>;
 constexpr int kSplitTargetWgs = 256;       // one workgroup per CU of an MI355X
 #elif FP8GEMM_SPLIT_CFG == 1
 using SplitCfg = TileCfg<64, 64, 32, 32, 8, 1>;
+constexpr int kSplitTargetWgs = 256;
+#elif FP8GEMM_SPLIT_CFG == 3
+using SplitCfg = TileCfg<64, 64, 32, 32, 16, 1>;
 constexpr int kSplitTargetWgs = 256;
 #else
 using SplitCfg = TileCfg<64, 64, 32, 32, 8, 2>;
@@ -285,6 +290,8 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int mode) {
 }
 
 constexpr int64_t kPartialFloats = SplitCfg::BM * SplitCfg::BN;
+// ring depth of the split-K mainloop in 128-K tiles: as deep as the LDS allows
+constexpr int kSplitRing = SplitCfg::kSlots >= 16 ? 8 : 4;
 
 __host__ __device__ constexpr int64_t counter_bytes(int64_t tiles) {
   return (void)tiles, kCounterBytes;
@@ -327,7 +334,7 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void splitk_kernel
   }
 
   v16f acc[FM][FN];
-  if (interior_tile<Cfg, MODE>(op)) mainloop_interior<Cfg, MODE, 4>(op, lds, acc);
+  if (interior_tile<Cfg, MODE>(op)) mainloop_interior<Cfg, MODE, kSplitRing>(op, lds, acc);
   else mainloop<Cfg, MODE, !kF4>(op, lds, acc);
 
   // partial tile: float4 r of thread x at [tile][slice][r][x] (coalesced per r)

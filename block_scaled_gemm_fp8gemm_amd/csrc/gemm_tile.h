@@ -607,6 +607,18 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. E - 1.
+template <int B, int E>
+struct Unroll {
+  template <class F>
+  static __device__ __forceinline__ void run(F&& f) {
+    if constexpr (B < E) {
+      f(std::integral_constant<int, B>{});
+      Unroll<B + 1, E>::run(f);
+    }
+  }
+};
+
 // Whether a tile takes the interior path (uniform over the workgroup).
 template <class Cfg, int MODE>
 __device__ __forceinline__ bool interior_tile(const TileOperands& op) {
@@ -623,8 +635,9 @@ __device__ __forceinline__ bool interior_tile(const TileOperands& op) {
 #define FP8GEMM_COPY_SPAN 8    // eighths of a step's MFMAs over which its copies are spread
 #endif
 
-// NS: ring depth in 128-K tiles (2 for the 256 x 256 tile, 4 for the split-K
-// tile, whose K slices are short and whose copies need more latency hiding).
+// NS: ring depth in 128-K tiles (2 for the 256 x 256 tile; 4 or 8 for the split-K
+// tiles, whose K slices are short and whose copies come from HBM: a slice streams
+// at about the ring's bytes per HBM latency).
 template <class Cfg, int MODE, int NS = 2>
 __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_t* lds,
                                                   v16f (&acc)[Cfg::kFragM][Cfg::kFragN]) {
@@ -639,7 +652,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   constexpr int kCodeBuf = (Cfg::BM + Cfg::BN) * 16;  // 16 code bytes per row
   constexpr int kCodeOff = NS * kTile;
   constexpr bool kUniformOperand = nA % kLoads == 0;  // a wave copies rows of one operand
-  static_assert(NS == 2 || NS == 4, "ring of 2 or 4 K tiles");
+  static_assert(NS == 2 || NS == 4 || NS == 8, "ring of 2, 4 or 8 K tiles");
   static_assert(NS * kTile <= Cfg::kScaleOff, "ring fits");
   static_assert(kCodeOff + 2 * kCodeBuf <= Cfg::kLdsBytes, "code buffers fit");
   static_assert(kTile % (1024 * Cfg::kWaves) == 0, "equal copy share per wave");
@@ -911,10 +924,34 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
 
   // unrolled over 4 K tiles (4-deep ring), an MX code group (4 K tiles, FP4 2)
   // or the 2-deep ring
-  constexpr int kUnrollK = NS == 4 ? 4 : kMx ? kGroupTiles * (kF4 ? FP8GEMM_F4_UNROLL : 1) : 2;
+  constexpr int kUnrollK = NS >= 4 ? NS : kMx ? kGroupTiles * (kF4 ? FP8GEMM_F4_UNROLL : 1) : 2;
   static_assert(!kMx || kUnrollK % kGroupTiles == 0, "whole code groups per unrolled body");
-  static_assert(kUnrollK == 2 || kUnrollK == 4, "the body below unrolls 2 or 4 K tiles");
+  static_assert(kUnrollK == 2 || kUnrollK == 4 || kUnrollK == 8, "2, 4 or 8 K tiles per body");
   int u = 0;
+  if constexpr (kUnrollK == 8) {
+    // the eight-deep ring: sixteen steps per body, then whole K tiles (MX: whole
+    // code groups) one by one
+    for (; u + kUnrollK <= nk; u += kUnrollK) {
+      const int t = 2 * u;
+      Unroll<0, kUnrollK>::run([&](auto k_c) __attribute__((always_inline)) {
+        constexpr int k = decltype(k_c)::value;
+        step(t + 2 * k, std::integral_constant<int, 2 * k>{}, af0, bf0, af1, bf1);
+        step(t + 2 * k + 1, std::integral_constant<int, 2 * k + 1>{}, af1, bf1, af0, bf0);
+      });
+    }
+    const int t = 2 * u;
+    constexpr int kG = kMx ? kGroupTiles : 1;
+    Unroll<0, kUnrollK / kG - 1>::run([&](auto g_c) __attribute__((always_inline)) {
+      constexpr int g = decltype(g_c)::value;
+      if (u + g * kG < nk) {
+        Unroll<g * kG, (g + 1) * kG>::run([&](auto k_c) __attribute__((always_inline)) {
+          constexpr int k = decltype(k_c)::value;
+          step(t + 2 * k, std::integral_constant<int, 2 * k>{}, af0, bf0, af1, bf1);
+          step(t + 2 * k + 1, std::integral_constant<int, 2 * k + 1>{}, af1, bf1, af0, bf0);
+        });
+      }
+    });
+  } else {
   for (; u + kUnrollK <= nk; u += kUnrollK) {
     const int t = 2 * u;
     step(t, I0{}, af0, bf0, af1, bf1);
@@ -956,6 +993,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
         step(t + 5, I5{}, af1, bf1, af0, bf0);
       }
     }
+  }
   }
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0);     // no copy may still target LDS
