@@ -134,17 +134,10 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Large-problem tile.  FP8GEMM_BIG_CFG selects it (tuning switch):
-//   0: 256 x 256, 4 wavefronts of 128 x 128, one workgroup per CU, 4-slot ring
-//   1: 256 x 128, 4 wavefronts of 128 x 64, two workgroups per CU, 3-slot ring
-#ifndef FP8GEMM_BIG_CFG
-#define FP8GEMM_BIG_CFG 0
-#endif
-#if FP8GEMM_BIG_CFG == 0
+// Large-problem tile: 256 x 256, 4 wavefronts of 128 x 128, one workgroup per CU,
+// 4-slot ring (the interior path's two 128-K slots plus code buffers need its
+// 144 KiB of LDS).
 using Big = TileCfg<256, 256, 128, 128, 4, 1>;
-#else
-using Big = TileCfg<256, 128, 128, 64, 3, 2>;
-#endif
 using Mid = TileCfg<128, 128, 64, 64, 4, 2>;
 
 #ifndef FP8GEMM_PERSISTENT
