@@ -160,14 +160,8 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void grouped_kerne
   }
 }
 
-#ifndef FP8GEMM_BIG_CFG
-#define FP8GEMM_BIG_CFG 0
-#endif
-#if FP8GEMM_BIG_CFG == 0
+// the dense GEMM's large tile: 256 x 256, 4 wavefronts of 128 x 128, one per CU
 using Big = TileCfg<256, 256, 128, 128, 4, 1>;
-#else
-using Big = TileCfg<256, 128, 128, 64, 3, 2>;
-#endif
 // MX with K % 128 != 0 reads its codes into registers: the large tile would spill
 using Mid = TileCfg<128, 128, 64, 64, 4, 2>;
 
