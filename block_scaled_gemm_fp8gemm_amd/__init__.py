@@ -80,6 +80,8 @@ _SIGNATURES = {
     "fp8gemm_grouped_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _int]),
     "fp8gemm_grouped_run": (_int, [_i32, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _i64, _int,
                                    _p, _p, _p, _i64, _int, _p, _sz, _p]),
+    "fp8gemm_grouped_run_ex": (_int, [_i32, _i64, _i64, _i64, _p, _i64, _int, _p, _p, _i64, _int,
+                                      _i64, _int, _p, _p, _p, _i64, _int, _p, _sz, _p]),
     "fp8gemm_status_string": (ctypes.c_char_p, [_int]),
     "fp8gemm_version": (_int, []),
 }
@@ -191,6 +193,16 @@ def fp8gemm_grouped_run(num_groups: int, total_m: int, N: int, K: int, A: int, l
     _check("fp8gemm_grouped_run", load_library().fp8gemm_grouped_run(
         num_groups, total_m, N, K, A, lda, offsets, B, ldb, stride_b, mode, scale_a, scale_b, C,
         ldc, out_dtype, workspace, workspace_bytes, stream))
+
+
+def fp8gemm_grouped_run_ex(num_groups: int, total_m: int, N: int, K: int, A: int, lda: int,
+                           a_format: int, offsets: int, B: int, ldb: int, b_format: int,
+                           stride_b: int, mode: int, scale_a: int, scale_b: int, C: int, ldc: int,
+                           out_dtype: int, workspace: int, workspace_bytes: int,
+                           stream: int) -> None:
+    _check("fp8gemm_grouped_run_ex", load_library().fp8gemm_grouped_run_ex(
+        num_groups, total_m, N, K, A, lda, a_format, offsets, B, ldb, b_format, stride_b, mode,
+        scale_a, scale_b, C, ldc, out_dtype, workspace, workspace_bytes, stream))
 
 
 def fp8gemm_status_string(status: int) -> str:
@@ -364,14 +376,19 @@ def gemm_mxout(qa, sa, qb, sb, mode: str = "tensor", out=None, out_scales=None,
 
 
 def grouped_gemm(qa, sa, offsets, qb, sb, mode: str = "rowwise", out_dtype: str = "bf16",
-                 out=None, workspace=None):
-    """Grouped GEMM: rows [offsets[g], offsets[g+1]) of qa use expert qb[g] ([G, N, K])."""
+                 out=None, workspace=None, fmt: str = "e4m3"):
+    """Grouped GEMM: rows [offsets[g], offsets[g+1]) of qa use expert qb[g] ([G, N, K]).
+
+    fmt: "e4m3", or "e2m1" (MXFP4 activations and experts, mode "mx32", codes
+    packed two per byte: qa [total_m, K/2], qb [G, N, K/2])."""
     torch = _torch()
     _require_cuda(qa, "qa", torch.uint8, 2)
     _require_cuda(qb, "qb", torch.uint8, 3)
     _require_cuda(offsets, "offsets", torch.int32, 1)
     total_m, K = qa.shape
     G, N, Kb = qb.shape
+    if fmt == "e2m1":
+        K, Kb = 2 * K, 2 * Kb
     if K != Kb or offsets.numel() != G + 1:
         raise ValueError("shape mismatch between qa, qb and offsets")
     tdt = torch.float16 if out_dtype == "f16" else torch.bfloat16
@@ -382,8 +399,9 @@ def grouped_gemm(qa, sa, offsets, qb, sb, mode: str = "rowwise", out_dtype: str 
     need = fp8gemm_grouped_workspace_size(G, total_m, N, K, m)
     if need and workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=qa.device)
-    fp8gemm_grouped_run(G, total_m, N, K, _ptr(qa), qa.stride(0), _ptr(offsets), _ptr(qb),
-                        qb.stride(1), qb.stride(0), m, _ptr(sa), _ptr(sb), _ptr(out),
-                        out.stride(0), OUT_DTYPES[out_dtype], _ptr(workspace) if need else 0,
-                        workspace.numel() if need else 0, _stream_handle(qa.device))
+    fp8gemm_grouped_run_ex(G, total_m, N, K, _ptr(qa), qa.stride(0), FORMATS[fmt], _ptr(offsets),
+                           _ptr(qb), qb.stride(1), FORMATS[fmt], qb.stride(0), m, _ptr(sa),
+                           _ptr(sb), _ptr(out), out.stride(0), OUT_DTYPES[out_dtype],
+                           _ptr(workspace) if need else 0, workspace.numel() if need else 0,
+                           _stream_handle(qa.device))
     return out

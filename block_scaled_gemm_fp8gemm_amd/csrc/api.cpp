@@ -299,14 +299,31 @@ fp8gemm_status fp8gemm_grouped_run(int32_t num_groups, int64_t total_m, int64_t 
                                    const void* scale_a, const void* scale_b, void* C,
                                    int64_t ldc, int out_dtype, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  if (!valid_mode(mode) || !valid_out(out_dtype) || num_groups < 1 || total_m < 0 || N < 0 ||
-      K <= 0)
+  return fp8gemm_grouped_run_ex(num_groups, total_m, N, K, A, lda, FP8GEMM_FORMAT_E4M3, offsets,
+                                B, ldb, FP8GEMM_FORMAT_E4M3, stride_b, mode, scale_a, scale_b, C,
+                                ldc, out_dtype, workspace, workspace_bytes, stream);
+}
+
+fp8gemm_status fp8gemm_grouped_run_ex(int32_t num_groups, int64_t total_m, int64_t N, int64_t K,
+                                      const uint8_t* A, int64_t lda, int a_format,
+                                      const int32_t* offsets, const uint8_t* B, int64_t ldb,
+                                      int b_format, int64_t stride_b, int mode,
+                                      const void* scale_a, const void* scale_b, void* C,
+                                      int64_t ldc, int out_dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (!valid_mode(mode) || !valid_out(out_dtype) || !valid_format(a_format) ||
+      !valid_format(b_format) || num_groups < 1 || total_m < 0 || N < 0 || K <= 0)
     return FP8GEMM_ERROR_INVALID_VALUE;
+  // e4m3 experts, or MXFP4 activations and experts
+  const bool fp4 = a_format == FP8GEMM_FORMAT_E2M1 && b_format == FP8GEMM_FORMAT_E2M1;
+  if (!fp4 && (a_format != FP8GEMM_FORMAT_E4M3 || b_format != FP8GEMM_FORMAT_E4M3))
+    return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if (fp4 && mode != kMx32) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (num_groups > kMaxGroups) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (total_m == 0 || N == 0) return FP8GEMM_SUCCESS;
   if (!offsets) return FP8GEMM_ERROR_INVALID_VALUE;
   fp8gemm_status st = check_gemm_common(total_m, N, K, A, lda, B, ldb, mode, scale_a, scale_b, C,
-                                        ldc, out_dtype);
+                                        ldc, out_dtype, fp4 ? 2 : 1);
   if (st != FP8GEMM_SUCCESS) return st;
   if (stride_b < N * ldb) return FP8GEMM_ERROR_INVALID_VALUE;
   if (stride_b % 16 != 0) return FP8GEMM_ERROR_MISALIGNED;
@@ -318,7 +335,7 @@ fp8gemm_status fp8gemm_grouped_run(int32_t num_groups, int64_t total_m, int64_t 
   p.groups = num_groups;
   p.total_m = (int)total_m;
   p.N = (int)N;
-  p.K = (int)K;
+  p.K = (int)(fp4 ? K / 2 : K);        // FP4: the kernels walk K in bytes
   p.A = A;
   p.lda = lda;
   p.offsets = offsets;
@@ -329,8 +346,9 @@ fp8gemm_status fp8gemm_grouped_run(int32_t num_groups, int64_t total_m, int64_t 
   p.scale_b = scale_b;
   p.C = C;
   p.ldc = ldc;
-  return from_hip(
-      fp8gemm::launch_grouped_gemm(p, mode, out_dtype, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fp4) return from_hip(fp8gemm::launch_grouped_gemm_e2m1_e2m1(p, mode, out_dtype, s));
+  return from_hip(fp8gemm::launch_grouped_gemm(p, mode, out_dtype, s));
 }
 
 const char* fp8gemm_status_string(int status) {

@@ -78,7 +78,7 @@ struct GroupedTiles {
     op.ldb = p.ldb;
     op.b_rows = p.N - w.n0;
     op.K = p.K;
-    op.sld = p.K / 32;
+    op.sld = p.K / kBlkBytes;
     op.sa = op.sb = nullptr;
     op.ra = op.rb = nullptr;
     if (MODE == kMx32) {
@@ -130,8 +130,8 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void grouped_kerne
   const float* fsb = static_cast<const float*>(p.scale_b);
   OutT* C = static_cast<OutT*>(p.C);
   // full tiles with K % 512 == 0 run as copy streams (one per run of such tiles);
-  // tiles cut by an expert's last row take the general path
-  constexpr bool kStream = KALIGNED && Cfg::kSlots == 4;
+  // tiles cut by an expert's last row take the general path (FP4: every tile)
+  constexpr bool kStream = KALIGNED && Cfg::kSlots == 4 && !kF4;
   auto streamable = [&](int i) __attribute__((always_inline)) {
     return kStream && p.K % 512 == 0 && interior_tile<Cfg, MODE>(src.op(i));
   };
@@ -145,12 +145,17 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void grouped_kerne
   int i = 0;
   while (i < count) {
     __syncthreads();  // the previous tile's epilogue is done with LDS
-    if (streamable(i)) {
-      int j = i + 1;
-      while (j < count && streamable(j)) ++j;
-      stream_interior<Cfg, MODE, 2 * Cfg::kFragM * Cfg::kFragN>(src, i, j, lds, epi);
-      i = j;
-    } else {
+    bool streamed = false;
+    if constexpr (kStream) {
+      if (streamable(i)) {
+        int j = i + 1;
+        while (j < count && streamable(j)) ++j;
+        stream_interior<Cfg, MODE, 2 * Cfg::kFragM * Cfg::kFragN>(src, i, j, lds, epi);
+        i = j;
+        streamed = true;
+      }
+    }
+    if (!streamed) {
       const auto w = src.where(i);
       const float ts = (MODE == kTensor) ? fsa[0] * fsb[w.g] : 1.0f;
       gemm_tile<Cfg, MODE, OutT, KALIGNED>(src.op_at(w), lds, C, p.ldc, w.m0, w.m_end, w.n0, p.N,
@@ -190,6 +195,16 @@ hipError_t launch_cfg(const GroupedProblem& p, hipStream_t stream) {
 
 }  // namespace
 
+#if FP8GEMM_FMT_A == 4 && FP8GEMM_FMT_B == 4
+// MXFP4 experts (K, lda, ldb and stride_b in bytes): 128 x 128 tiles, whose edge
+// tiles read their codes into registers without spilling.
+hipError_t launch_grouped_gemm_e2m1_e2m1(const GroupedProblem& p, int mode, int out,
+                                         hipStream_t stream) {
+  if (mode != kMx32) return hipErrorInvalidValue;
+  if (out == kF16) return launch_cfg<Mid, kMx32, _Float16>(p, stream);
+  return launch_cfg<Mid, kMx32, __bf16>(p, stream);
+}
+#else
 int grouped_max_groups() { return kMaxGroups; }
 
 hipError_t launch_grouped_gemm(const GroupedProblem& p, int mode, int out, hipStream_t stream) {
@@ -204,5 +219,6 @@ hipError_t launch_grouped_gemm(const GroupedProblem& p, int mode, int out, hipSt
   if (p.K % 128 != 0) return launch_cfg<Mid, kMx32, __bf16>(p, stream);
   return launch_cfg<Big, kMx32, __bf16>(p, stream);
 }
+#endif
 
 }  // namespace fp8gemm

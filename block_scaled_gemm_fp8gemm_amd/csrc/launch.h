@@ -86,5 +86,8 @@ hipError_t launch_transpose_u8(const uint8_t* in, int64_t ldi, uint8_t* out, int
                                int64_t rows, int64_t cols, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const GroupedProblem& p, int mode, int out, hipStream_t stream);
+// MXFP4 experts (mode kMx32 only; K, lda, ldb and stride_b count bytes).
+hipError_t launch_grouped_gemm_e2m1_e2m1(const GroupedProblem& p, int mode, int out,
+                                         hipStream_t stream);
 
 }  // namespace fp8gemm

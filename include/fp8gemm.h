@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FP8GEMM_VERSION 140 /* 1.4.0: e5m2, fused epilogues, row-major B, MXFP4, MX output */
+#define FP8GEMM_VERSION 150 /* 1.5.0: e5m2, fused epilogues, row-major B, MXFP4 (dense, grouped), MX output */
 
 typedef enum fp8gemm_status {
   FP8GEMM_SUCCESS = 0,
@@ -262,6 +262,20 @@ fp8gemm_status fp8gemm_grouped_run(int32_t num_groups, int64_t total_m, int64_t 
                                    const void* scale_a, const void* scale_b, void* C,
                                    int64_t ldc, int out_dtype, void* workspace,
                                    size_t workspace_bytes, void* stream);
+
+/* The same with operand formats: a_format and b_format both FP8GEMM_FORMAT_E4M3
+   (fp8gemm_grouped_run), or both FP8GEMM_FORMAT_E2M1 with MX32 scales (MXFP4
+   activations and experts; A holds two codes per byte, element (m,k) in byte
+   A[m*lda + k/2], expert g's element (k,n) in byte B[g*stride_b + n*ldb + k/2];
+   lda, ldb >= K/2 bytes; K % 32 == 0; E8M0 codes as above).  Other pairings are
+   NOT_SUPPORTED. */
+fp8gemm_status fp8gemm_grouped_run_ex(int32_t num_groups, int64_t total_m, int64_t N, int64_t K,
+                                      const uint8_t* A, int64_t lda, int a_format,
+                                      const int32_t* offsets, const uint8_t* B, int64_t ldb,
+                                      int b_format, int64_t stride_b, int mode,
+                                      const void* scale_a, const void* scale_b, void* C,
+                                      int64_t ldc, int out_dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fp8gemm_status_string(int status);

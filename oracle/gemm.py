@@ -97,7 +97,8 @@ def gemm_reference(qa, sa, qb, sb, mode: str, rows=None, cols=None, fmt_a: str =
     raise ValueError(f"unknown scale mode {mode!r}")
 
 
-def grouped_reference(qa, sa, offsets, qb, sb, mode: str, rows=None, cols=None):
+def grouped_reference(qa, sa, offsets, qb, sb, mode: str, rows=None, cols=None,
+                      fmt: str = "e4m3"):
     """Grouped GEMM reference: rows [offsets[g], offsets[g+1]) of A use expert g.
 
     qa: uint8 [total_m, K] sorted by expert; offsets: int [G+1] with
@@ -119,10 +120,11 @@ def grouped_reference(qa, sa, offsets, qb, sb, mode: str, rows=None, cols=None):
             continue
         r = rows[sel]
         if mode == "tensor":
-            c, a = gemm_reference(qa[r], sa, qb[g], np.asarray(sb)[g], mode, cols=cols)
+            c, a = gemm_reference(qa[r], sa, qb[g], np.asarray(sb)[g], mode, cols=cols,
+                                  fmt_a=fmt, fmt_b=fmt)
         else:
             c, a = gemm_reference(qa[r], np.asarray(sa)[r], qb[g], np.asarray(sb)[g], mode,
-                                  cols=cols)
+                                  cols=cols, fmt_a=fmt, fmt_b=fmt)
         C[sel] = c
         A[sel] = a
     return C, A

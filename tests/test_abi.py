@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol(lib):
         "fp8gemm_quantize_workspace_size", "fp8gemm_quantize", "fp8gemm_quantize_ex",
         "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex", "fp8gemm_workspace_size_kn",
         "fp8gemm_run_kn", "fp8gemm_run_mxout",
-        "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run", "fp8gemm_status_string",
+        "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run", "fp8gemm_grouped_run_ex",
+        "fp8gemm_status_string",
         "fp8gemm_version"}
     raw = ctypes.CDLL(F.library_path())
     for n in names:
@@ -40,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert F.fp8gemm_version() == 140
+    assert F.fp8gemm_version() == 150
     for code, name in [(0, "FP8GEMM_SUCCESS"), (1, "FP8GEMM_ERROR_INVALID_VALUE"),
                        (2, "FP8GEMM_ERROR_MISALIGNED"), (3, "FP8GEMM_ERROR_NOT_SUPPORTED"),
                        (4, "FP8GEMM_ERROR_WORKSPACE"), (5, "FP8GEMM_ERROR_LAUNCH"),
@@ -170,6 +171,21 @@ def test_fp4_validation(lib):
     need = F.fp8gemm_workspace_size_kn(64, 64, 128, 2)
     assert lib.fp8gemm_run_kn(64, 64, 128, P, 64, 4, P2, 64, 4, 2, P3, P3 + 256, 0, 0,
                               P3 + 4096, 64, 1, P3 + (1 << 20), need, None) == NOT_SUPPORTED
+
+
+def test_grouped_fp4_validation(lib):
+    """fp8gemm_grouped_run_ex: e4m3 experts or MXFP4 activations and experts only."""
+    def run(fa=4, fb=4, mode=2, K=256, lda=128, ldb=128, stride_b=64 * 128, **kw):
+        return lib.fp8gemm_grouped_run_ex(2, kw.get("total_m", 64), 64, K, P, lda, fa, P3, P2, ldb,
+                                          fb, stride_b, mode, P3 + 256, P3 + 512, P3 + 4096, 64, 1,
+                                          0, 0, None)
+    assert run(total_m=0) == SUCCESS
+    assert run(mode=1) == NOT_SUPPORTED                  # FP4 needs MX scales
+    assert run(fb=0) == NOT_SUPPORTED                    # FP4 x e4m3
+    assert run(fa=1, fb=1, lda=256, ldb=256, stride_b=64 * 256) == NOT_SUPPORTED   # e5m2 experts
+    assert run(lda=112) == INVALID                       # lda < K/2 bytes
+    assert run(stride_b=64 * 128 - 16) == INVALID        # experts overlap
+    assert run(fa=7) == INVALID
 
 
 def test_mxout_validation(lib):

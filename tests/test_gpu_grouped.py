@@ -110,3 +110,26 @@ def test_workload_grouped_moe():
     Cr, Ar = O.grouped_reference(qa, sa, off, qw, sw, w.mode, rows=rows)
     Cg = to_host(C[torch.from_numpy(rows).to(DEV)])
     assert_within_bound(Cg, Cr, Ar, w.out, "grouped_moe sampled rows")
+
+
+@pytest.mark.parametrize("counts,N,K", [([5, 0, 300, 77], 200, 192), ([0, 0, 513], 64, 128),
+                                        ([1, 1, 1, 1, 1, 1], 300, 64), ([256, 256], 512, 512),
+                                        ([130, 0, 260], 256, 1056)])
+def test_grouped_fp4(counts, N, K):
+    """MXFP4 activations and experts (two e2m1 codes per byte): ragged and empty
+    experts, experts shorter than a tile, whole code groups and a K tail."""
+    rng = np.random.default_rng(3 * sum(counts) + N + K)
+    counts = np.array(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = normal(rng, int(off[-1]), K)
+    W = np.stack([normal(rng, N, K, 0.02) for _ in counts])
+    qa, sa = Q.quantize(x, "mx32", "e2m1")
+    qs, ss = zip(*[Q.quantize(W[g], "mx32", "e2m1") for g in range(len(counts))])
+    qw, sw = np.stack(qs), np.stack(ss)
+    announce("grouped e2m1", counts.tolist(), N, K)
+    C = F.grouped_gemm(to_dev(O.pack_fp4(qa), 16), scale_to_dev(sa, "mx32"),
+                       torch.from_numpy(off).to(DEV), _dev3(O.pack_fp4(qw)),
+                       torch.from_numpy(np.ascontiguousarray(sw)).to(DEV), "mx32", "bf16",
+                       fmt="e2m1")
+    Cr, Ar = O.grouped_reference(qa, sa, off, qw, sw, "mx32", fmt="e2m1")
+    assert_within_bound(to_host(C), Cr, Ar, "bf16", f"grouped e2m1 {counts.tolist()}")
