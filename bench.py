@@ -19,6 +19,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -244,9 +245,12 @@ def main():
     if kn and (w.groups or mxout):
         raise SystemExit("--b-layout kn applies to the dense workloads with a 16-bit output")
     use_bias = args.epilogue not in ("none", "mxout")
-    if w.groups and (args.formats != "e4m3,e4m3" or use_bias or mxout):
-        raise SystemExit("--formats and --epilogue apply to the dense workloads")
     fp4 = "e2m1" in (fmt_a, fmt_b)
+    if w.groups and ((args.formats != "e4m3,e4m3" and not fp4) or use_bias or mxout):
+        raise SystemExit("--epilogue applies to the dense workloads; the grouped one takes "
+                         "--formats e2m1,e2m1 only")
+    if fp4 and w.groups:       # MXFP4 experts: the same shapes and inputs with MX scales
+        w = dataclasses.replace(w, mode="mx32")
     if fp4 and (fmt_a != fmt_b or w.mode != "mx32"):
         raise SystemExit("e2m1 (MXFP4) runs as e2m1,e2m1 on an mx32 workload")
     kq = w.K // 2 if fp4 else w.K            # code bytes per row
@@ -305,9 +309,9 @@ def main():
         if w.groups:
             if w.mode == "tensor":
                 raise SystemExit("grouped per-tensor benchmarking is not configured")
-            F.grouped_gemm(qa, sa, offsets, qb.view(w.groups, w.N, w.K),
+            F.grouped_gemm(qa, sa, offsets, qb.view(w.groups, w.N, kq),
                            sb.view(w.groups, -1) if w.mode == "mx32" else sb.view(w.groups, w.N),
-                           w.mode, w.out, out=C)
+                           w.mode, w.out, out=C, fmt=fmt_a)
         elif kn:
             F.gemm(qa, sa, qb_kn, sb_kn, w.mode, w.out, out=C, fmt_a=fmt_a, fmt_b=fmt_b,
                    bias=bias, activation=act, b_layout="kn")

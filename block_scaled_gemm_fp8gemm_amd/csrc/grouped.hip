@@ -196,13 +196,18 @@ hipError_t launch_cfg(const GroupedProblem& p, hipStream_t stream) {
 }  // namespace
 
 #if FP8GEMM_FMT_A == 4 && FP8GEMM_FMT_B == 4
-// MXFP4 experts (K, lda, ldb and stride_b in bytes): 128 x 128 tiles, whose edge
-// tiles read their codes into registers without spilling.
+// MXFP4 experts (K, lda, ldb and stride_b in bytes): the large tile, one tile at
+// a time (full tiles take the interior mainloop, tiles cut by an expert's last
+// row read their codes into registers); a K tail takes 128 x 128 tiles.
 hipError_t launch_grouped_gemm_e2m1_e2m1(const GroupedProblem& p, int mode, int out,
                                          hipStream_t stream) {
   if (mode != kMx32) return hipErrorInvalidValue;
-  if (out == kF16) return launch_cfg<Mid, kMx32, _Float16>(p, stream);
-  return launch_cfg<Mid, kMx32, __bf16>(p, stream);
+  if (out == kF16) {
+    if (p.K % 128 != 0) return launch_cfg<Mid, kMx32, _Float16>(p, stream);
+    return launch_cfg<Big, kMx32, _Float16>(p, stream);
+  }
+  if (p.K % 128 != 0) return launch_cfg<Mid, kMx32, __bf16>(p, stream);
+  return launch_cfg<Big, kMx32, __bf16>(p, stream);
 }
 #else
 int grouped_max_groups() { return kMaxGroups; }

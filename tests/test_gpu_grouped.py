@@ -114,10 +114,11 @@ def test_workload_grouped_moe():
 
 @pytest.mark.parametrize("counts,N,K", [([5, 0, 300, 77], 200, 192), ([0, 0, 513], 64, 128),
                                         ([1, 1, 1, 1, 1, 1], 300, 64), ([256, 256], 512, 512),
-                                        ([130, 0, 260], 256, 1056)])
+                                        ([130, 0, 260], 256, 1056), ([130, 0, 300, 7], 512, 1024)])
 def test_grouped_fp4(counts, N, K):
     """MXFP4 activations and experts (two e2m1 codes per byte): ragged and empty
-    experts, experts shorter than a tile, whole code groups and a K tail."""
+    experts, experts shorter than a tile, whole code groups and a K tail, on both
+    tile sizes (K a multiple of 256: the 256 x 256 tile with cut tiles)."""
     rng = np.random.default_rng(3 * sum(counts) + N + K)
     counts = np.array(counts)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
