@@ -81,7 +81,12 @@ constexpr int kFmtA = FP8GEMM_FMT_A, kFmtB = FP8GEMM_FMT_B;
 // takes 16 bytes per lane for FP4 (32 elements of row lane % 32 from 32-K block
 // lane / 32, low nibble first; probed on gfx950), so the two 16-byte chunks a
 // lane reads for an FP8 fragment are exactly the operands of those two MFMAs,
-// and an E8M0 block covers 16 bytes instead of 32.  Only FP4 x FP4 is built.
+// and an E8M0 block covers 16 bytes instead of 32.  A lane takes chunks 2h and
+// 2h + 1 of a 64-byte step (h = lane / 32): the first MFMA then covers blocks
+// 4s and 4s + 2, the second 4s + 1 and 4s + 3 (the order of K inside an MFMA
+// does not matter), and the two code bytes a lane needs, 4s + 2h and 4s + 2h + 1,
+// are adjacent: one 16-bit read, byte 0 for the first MFMA and byte 1 (op_sel 1,
+// probed) for the second.  Only FP4 x FP4 is built.
 constexpr bool kF4 = kFmtA == 4;
 static_assert((kFmtA == 4) == (kFmtB == 4), "FP4 operands pair with FP4 operands only");
 constexpr int kBlkBytes = kF4 ? 16 : 32;     // bytes of one 32-element MX block
@@ -270,7 +275,7 @@ __device__ __forceinline__ v4i read_one(const uint8_t* slot, int r, int k0, int 
   const bool isA = r < 2 * Cfg::kFragM;
   const int idx = isA ? r >> 1 : (r - 2 * Cfg::kFragM) >> 1;
   const int row = isA ? arow[idx] : Cfg::BM + brow[idx];
-  const int c = h + 2 * (r & 1);
+  const int c = kF4 ? 2 * h + (r & 1) : h + 2 * (r & 1);
   v4i v = *reinterpret_cast<const v4i*>(slot + row * Cfg::kBK + 16 * (c ^ lds_swz(row)));
   if (KTAIL && k0 + 16 * c >= K) v = v4i{};
   return v;
@@ -282,7 +287,7 @@ __device__ __forceinline__ void read_frags(const uint8_t* slot, int k0, int K,
                                            const int (&arow)[Cfg::kFragM],
                                            const int (&brow)[Cfg::kFragN], int h,
                                            v8i (&af)[Cfg::kFragM], v8i (&bf)[Cfg::kFragN]) {
-  const int c0 = h, c1 = h + 2;
+  const int c0 = kF4 ? 2 * h : h, c1 = kF4 ? 2 * h + 1 : h + 2;
   bool z0 = false, z1 = false;
   if (KTAIL) {
     z0 = k0 + 16 * c0 >= K;
@@ -435,19 +440,19 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
   // codes of sub-tile s straight from global memory (K % 128 != 0): block 2s + h.
   // FP4: blocks 4s + h (first MFMA, bits 0-7) and 4s + 2 + h (second, bits 16-23)
   auto load_reg_codes = [&](int s, uint32_t (&a)[FM], uint32_t (&b)[FN]) {
-    const int blk = (kF4 ? 4 : 2) * s + h;
+    const int blk = kF4 ? 4 * s + 2 * h : 2 * s + h;
     auto code = [&](const uint8_t* base, int b) { return b < nblk ? (uint32_t)base[b] : 127u; };
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = arow[i] < op.a_rows ? arow[i] : op.a_rows - 1;
       const uint8_t* row = op.sa + (int64_t)r * op.sld;
-      a[i] = kF4 ? code(row, blk) | (code(row, blk + 2) << 16) : code(row, blk);
+      a[i] = kF4 ? code(row, blk) | (code(row, blk + 1) << 8) : code(row, blk);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int r = brow[j] < op.b_rows ? brow[j] : op.b_rows - 1;
       const uint8_t* row = op.sb + (int64_t)r * op.sld;
-      b[j] = kF4 ? code(row, blk) | (code(row, blk + 2) << 16) : code(row, blk);
+      b[j] = kF4 ? code(row, blk) | (code(row, blk + 1) << 8) : code(row, blk);
     }
   };
 
@@ -503,8 +508,8 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
             lo16(fb[j]), lo16(fa[i]), acc[i][j], kFmtB, kFmtA, 0, (int)sb_cur[j], 0,
             (int)sa_cur[i]);
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            hi16(fb[j]), hi16(fa[i]), acc[i][j], kFmtB, kFmtA, 0, (int)(sb_cur[j] >> 16), 0,
-            (int)(sa_cur[i] >> 16));
+            hi16(fb[j]), hi16(fa[i]), acc[i][j], kFmtB, kFmtA, 1, (int)sb_cur[j], 1,
+            (int)sa_cur[i]);
       } else if (MODE == kMx32) {
         const uint32_t sa = (kMxLds && odd) ? sa_cur[i] >> 16 : sa_cur[i];
         const uint32_t sb = (kMxLds && odd) ? sb_cur[j] >> 16 : sb_cur[j];
@@ -672,7 +677,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   const int nblk = op.K / kBlkBytes;
   const int ncode = nblk / 16;                     // 16-byte code groups per row
   constexpr int kGroupTiles = 16 * kBlkBytes / kRowB;   // K tiles per code group (4, FP4 2)
-  constexpr int kCodes = kF4 ? 2 : 1;              // code bytes per fragment and step
+  constexpr int kCodes = 1;                        // code reads per fragment and step
 
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -738,18 +743,18 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
     for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const int ch = 16 * ((4 * p + 2 * c + h) ^ rsw);
+        const int ch = 16 * ((kF4 ? 4 * p + 2 * h + c : 4 * p + 2 * c + h) ^ rsw);
         ba[s][p][c] = opaque(s * kPerBase * kTile + ra + ch);
         bb[s][p][c] = opaque(s * kPerBase * kTile + rb + ch);
       }
   // MX codes: byte 4 (u % 4) + 2 p + h of the row's 16-byte group u / 4 (FP4:
-  // bytes 8 (u % 2) + 4 p + 2 c + h of group u / 2, c = the step's MFMA); the
+  // bytes 8 (u % 2) + 4 p + 2 h + c of group u / 2, c = the step's MFMA); the
   // group of the current K tile is in buffer `cur`, the next one in `nxt`
   int cur_a = 0, cur_b = 0, nxt_a = 0, nxt_b = 0;
   int cbuf = 0;                                        // buffer index of the current group
   if (kMx) {
-    cur_a = opaque(kCodeOff + (wm * Cfg::WM + (lane & 31)) * 16 + h);
-    cur_b = opaque(kCodeOff + (Cfg::BM + wn * Cfg::WN + (lane & 31)) * 16 + h);
+    cur_a = opaque(kCodeOff + (wm * Cfg::WM + (lane & 31)) * 16 + (kF4 ? 2 * h : h));
+    cur_b = opaque(kCodeOff + (Cfg::BM + wn * Cfg::WN + (lane & 31)) * 16 + (kF4 ? 2 * h : h));
     nxt_a = opaque(cur_a + kCodeBuf);
     nxt_b = opaque(cur_b + kCodeBuf);
   }
@@ -777,9 +782,15 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   auto read_code = [&](int base_a, int base_b, int q, int p, int e,
                        uint32_t (&a)[kCodes][FM], uint32_t (&b)[kCodes][FN]) {
     const int c = e / (FM + FN), f = e % (FM + FN);
-    const int off = kF4 ? 8 * q + 4 * p + 2 * c : 4 * q + 2 * p;
-    if (f < FM) a[c][f] = lds[base_a + off + f * 32 * 16];
-    else b[c][f - FM] = lds[base_b + off + (f - FM) * 32 * 16];
+    if constexpr (kF4) {           // the two adjacent code bytes of the step's MFMAs
+      const int off = 8 * q + 4 * p;
+      if (f < FM) a[c][f] = *reinterpret_cast<const uint16_t*>(lds + base_a + off + f * 32 * 16);
+      else b[c][f - FM] = *reinterpret_cast<const uint16_t*>(lds + base_b + off + (f - FM) * 32 * 16);
+    } else {
+      const int off = 4 * q + 2 * p;
+      if (f < FM) a[c][f] = lds[base_a + off + f * 32 * 16];
+      else b[c][f - FM] = lds[base_b + off + (f - FM) * 32 * 16];
+    }
   };
 
   v8i af0[FM], bf0[FN], af1[FM], bf1[FN];
@@ -869,8 +880,8 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
             lo16(fb[j]), lo16(fa[i]), acc[i][j], kFmtB, kFmtA, 0, (int)cb[Z][0][j], 0,
             (int)ca[Z][0][i]);
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            hi16(fb[j]), hi16(fa[i]), acc[i][j], kFmtB, kFmtA, 0, (int)cb[Z][kCodes - 1][j], 0,
-            (int)ca[Z][kCodes - 1][i]);
+            hi16(fb[j]), hi16(fa[i]), acc[i][j], kFmtB, kFmtA, 1, (int)cb[Z][0][j], 1,
+            (int)ca[Z][0][i]);
       } else if (kMx) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             fb[j], fa[i], acc[i][j], kFmtB, kFmtA, 0, (int)cb[Z][0][j], 0, (int)ca[Z][0][i]);
