@@ -28,6 +28,7 @@ __all__ = [
     "fp8gemm_quantize_ex", "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex",
     "fp8gemm_workspace_size_kn", "fp8gemm_run_kn",
     "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run",
+    "fp8gemm_run_path", "PATHS",
     "fp8gemm_status_string", "fp8gemm_version", "quantize", "gemm", "grouped_gemm",
     "exported_symbols",
 ]
@@ -39,6 +40,9 @@ SCALE_MODES = {"tensor": 0, "rowwise": 1, "mx32": 2}
 OUT_DTYPES = {"f16": 0, "bf16": 1}
 FORMATS = {"e4m3": 0, "e5m2": 1, "e2m1": 4}   # e2m1: FP4, two codes per byte, MX only
 ACTIVATIONS = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
+
+# kernel paths of a dense GEMM (fp8gemm_run_path)
+PATHS = {0: "none", 1: "splitk", 2: "tile128", 3: "tile256", 4: "persistent"}
 
 _STATUS_NAMES = {
     0: "FP8GEMM_SUCCESS", 1: "FP8GEMM_ERROR_INVALID_VALUE", 2: "FP8GEMM_ERROR_MISALIGNED",
@@ -82,6 +86,7 @@ _SIGNATURES = {
                                    _p, _p, _p, _i64, _int, _p, _sz, _p]),
     "fp8gemm_grouped_run_ex": (_int, [_i32, _i64, _i64, _i64, _p, _i64, _int, _p, _p, _i64, _int,
                                       _i64, _int, _p, _p, _p, _i64, _int, _p, _sz, _p]),
+    "fp8gemm_run_path": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int, _int, _int]),
     "fp8gemm_status_string": (ctypes.c_char_p, [_int]),
     "fp8gemm_version": (_int, []),
 }
@@ -205,6 +210,13 @@ def fp8gemm_grouped_run_ex(num_groups: int, total_m: int, N: int, K: int, A: int
         scale_a, scale_b, C, ldc, out_dtype, workspace, workspace_bytes, stream))
 
 
+def fp8gemm_run_path(M: int, N: int, K: int, lda: int, ldb: int, a_format: int, b_format: int,
+                     mode: int, fused: int) -> str:
+    """Name of the kernel path a dense GEMM call of this shape takes (see PATHS)."""
+    return PATHS[load_library().fp8gemm_run_path(M, N, K, lda, ldb, a_format, b_format, mode,
+                                                 fused)]
+
+
 def fp8gemm_status_string(status: int) -> str:
     return load_library().fp8gemm_status_string(status).decode()
 
@@ -239,17 +251,23 @@ _WORKSPACES = {}
 
 
 def gemm_workspace(device, nbytes: int):
-    """A zero-filled device workspace of at least `nbytes`, cached per device.
+    """A zero-filled device workspace of at least `nbytes`, cached per (device,
+    current stream).
 
-    The split-K GEMM keeps per-tile arrival counters in its workspace; they must
-    be zero before the first call and every call leaves them zero, so one buffer
-    serves all calls on a device that do not run concurrently.
+    The split-K GEMM keeps per-tile arrival counters and fp32 partial tiles at
+    fixed places of its workspace: the counters must be zero before the first
+    call and every call leaves them zero, so one buffer serves every call that
+    cannot run concurrently with another one on it, i.e. the calls of one stream.
+    Calls on different streams get different buffers.  Each buffer is allocated
+    (and zero-filled) on its own stream, so PyTorch's caching allocator reuses a
+    replaced, smaller buffer only after the work already queued on that stream.
     """
     torch = _torch()
-    key = torch.device(device)
+    dev = torch.device(device)
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=key)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         _WORKSPACES[key] = ws
     return ws
 

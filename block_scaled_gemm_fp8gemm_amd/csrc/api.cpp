@@ -10,8 +10,30 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/fp8gemm.h"
 #include "launch.h"
+#include "plan.h"
+
+namespace fp8gemm {
+
+// One cached CU count per device (0 = not queried yet).  Concurrent first calls
+// may both query; they store the same value.
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+}  // namespace fp8gemm
 
 namespace {
 
@@ -349,6 +371,16 @@ fp8gemm_status fp8gemm_grouped_run_ex(int32_t num_groups, int64_t total_m, int64
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fp4) return from_hip(fp8gemm::launch_grouped_gemm_e2m1_e2m1(p, mode, out_dtype, s));
   return from_hip(fp8gemm::launch_grouped_gemm(p, mode, out_dtype, s));
+}
+
+int fp8gemm_run_path(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int a_format,
+                     int b_format, int mode, int fused) {
+  if (!valid_mode(mode) || !valid_format(a_format) || !valid_format(b_format) || M < 0 || N < 0 ||
+      K <= 0 || lda < 0 || ldb < 0)
+    return FP8GEMM_PATH_NONE;
+  const bool fp4 = a_format == FP8GEMM_FORMAT_E2M1 || b_format == FP8GEMM_FORMAT_E2M1;
+  if (fp4 && (a_format != b_format || mode != kMx32)) return FP8GEMM_PATH_NONE;
+  return fp8gemm::choose_path(M, N, fp4 ? K / 2 : K, lda, ldb, mode, fp4, fused != 0);
 }
 
 const char* fp8gemm_status_string(int status) {

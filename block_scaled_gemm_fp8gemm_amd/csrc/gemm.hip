@@ -12,6 +12,7 @@
 
 #include "gemm_tile.h"
 #include "launch.h"
+#include "plan.h"
 #include "tile_order.h"
 
 namespace fp8gemm {
@@ -134,76 +135,23 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Large-problem tile: 256 x 256, 4 wavefronts of 128 x 128, one workgroup per CU,
-// 4-slot ring (the interior path's two 128-K slots plus code buffers need its
-// 144 KiB of LDS).
+// Large-problem tile: 256 x 256, 4 wavefronts of 128 x 128, one workgroup per CU
+// (the interior path's two 128-K ring slots plus code buffers need its 144 KiB of
+// LDS); mid-size tile: 128 x 128, 4 wavefronts of 64 x 64, two workgroups per CU.
 using Big = TileCfg<256, 256, 128, 128, 4, 1>;
 using Mid = TileCfg<128, 128, 64, 64, 4, 2>;
-
-#ifndef FP8GEMM_PERSISTENT
-#define FP8GEMM_PERSISTENT 0
-#endif
-
-int device_cus() {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-  }
-  return cus;
-}
-
-// Every tile of the shape is an interior tile (the persistent stream's condition).
-template <class Cfg>
-bool all_interior(const GemmProblem& p) {
-  return p.M % Cfg::BM == 0 && p.N % Cfg::BN == 0 && p.K % 512 == 0 &&
-         (int64_t)Cfg::BM * p.lda + p.K < ((int64_t)1 << 31) &&
-         (int64_t)Cfg::BN * p.ldb + p.K < ((int64_t)1 << 31);
-}
+static_assert(Big::BM == kBigTile && Big::BN == kBigTile && Big::kWgPerCu == 1, "plan.h tiles");
+static_assert(Mid::BM == kMidTile && Mid::BN == kMidTile, "plan.h tiles");
 
 template <class Cfg, int MODE, typename OutT>
 hipError_t launch_persistent(const GemmProblem& p, hipStream_t stream) {
   const int tiles_m = p.M / Cfg::BM, tiles_n = p.N / Cfg::BN;
   const int total = tiles_m * tiles_n;
-  const int cus = device_cus();
+  const int cus = device_cu_count();
   const int grid = total < cus ? total : cus;
   hipLaunchKernelGGL((gemm_persistent_kernel<Cfg, MODE, OutT>), dim3(grid), dim3(Cfg::kThreads), 0,
                      stream, p, tiles_m, tiles_n);
   return hipGetLastError();
-}
-
-// FP4 operands (K counted in bytes): the large tile only when every tile is an
-// interior one (its edge tiles would read their codes into registers and spill),
-// and one tile per workgroup (no persistent stream).
-template <int MODE, typename OutT, bool FUSED>
-hipError_t launch_mode_f4(const GemmProblem& p, hipStream_t stream) {
-  const int64_t big_tiles = (int64_t)((p.M + Big::BM - 1) / Big::BM) * ((p.N + Big::BN - 1) / Big::BN);
-  const bool interior = p.M % Big::BM == 0 && p.N % Big::BN == 0 && p.K % (16 * kBlkBytes) == 0 &&
-                        (int64_t)Big::BM * p.lda + p.K < ((int64_t)1 << 31) &&
-                        (int64_t)Big::BN * p.ldb + p.K < ((int64_t)1 << 31);
-  if (big_tiles >= 256 * Big::kWgPerCu && interior) return launch_cfg<Big, MODE, OutT, FUSED>(p, stream);
-  return launch_cfg<Mid, MODE, OutT, FUSED>(p, stream);
-}
-
-template <int MODE, typename OutT, bool FUSED>
-hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
-  // Large tiles when they still give at least one tile per CU; otherwise smaller
-  // tiles for more parallelism.
-  const int64_t big_tiles = (int64_t)((p.M + Big::BM - 1) / Big::BM) * ((p.N + Big::BN - 1) / Big::BN);
-  // MX with K % 128 != 0 reads its codes into registers: the large tile would spill
-  const bool mx_ragged = MODE == kMx32 && p.K % 128 != 0;
-  if (big_tiles >= 256 * Big::kWgPerCu && !mx_ragged) {
-    // persistent streams pay off from about eight tiles per CU on (measured)
-    const bool many = big_tiles >= 8 * 256;
-    // (the fused epilogue stages through the ring, so it never runs in a stream)
-    if constexpr (!FUSED && !std::is_same<OutT, uint8_t>::value) {
-      if ((FP8GEMM_PERSISTENT || many) && all_interior<Big>(p))
-        return launch_persistent<Big, MODE, OutT>(p, stream);
-    }
-    return launch_cfg<Big, MODE, OutT, FUSED>(p, stream);
-  }
-  return launch_cfg<Mid, MODE, OutT, FUSED>(p, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -219,76 +167,18 @@ hipError_t launch_mode(const GemmProblem& p, hipStream_t stream) {
 // depend on arrival order), resets the counter to zero for the next call and
 // runs the epilogue.
 // ---------------------------------------------------------------------------
-// FP8GEMM_SPLIT_CFG (tuning switch): 1 (default) 64 x 64 tiles, one workgroup per
-// CU; 0 128 x 64 tiles; 2 64 x 64 tiles, two workgroups per CU; 3 64 x 64 tiles
-// with an eight-deep ring of 128-K tiles.  For M = 128, N = K = 4096 the 64 x 64
-// tiles split K in two instead of four and halve the fp32 partials exchanged
-// (8 -> 4 MiB written): 14.9 -> 13.5 us (measured; two per CU 14.3 us; the
-// eight-deep ring 14.8 against 14.2 us on another box, so the copy stream of a
-// slice is not bound by the bytes in flight).
-#ifndef FP8GEMM_SPLIT_CFG
-#define FP8GEMM_SPLIT_CFG 1
-#endif
-#if FP8GEMM_SPLIT_CFG == 0
-using SplitCfg = TileCfg<128, 64, 64, 32, 8, 1>;
-constexpr int kSplitTargetWgs = 256;       // one workgroup per CU of an MI355X
-#elif FP8GEMM_SPLIT_CFG == 1
+// 64 x 64 split tiles, 4 wavefronts of 32 x 32, one workgroup per CU.  For M =
+// 128, N = K = 4096 the 64 x 64 tiles split K in two instead of four and halve
+// the fp32 partials exchanged against 128 x 64 tiles (8 -> 4 MiB written):
+// 14.9 -> 13.5 us (measured; two workgroups per CU 14.3 us, an eight-deep ring
+// 4 % slower, so the copy stream of a slice is not bound by the bytes in flight).
 using SplitCfg = TileCfg<64, 64, 32, 32, 8, 1>;
-constexpr int kSplitTargetWgs = 256;
-#elif FP8GEMM_SPLIT_CFG == 3
-using SplitCfg = TileCfg<64, 64, 32, 32, 16, 1>;
-constexpr int kSplitTargetWgs = 256;
-#else
-using SplitCfg = TileCfg<64, 64, 32, 32, 8, 2>;
-constexpr int kSplitTargetWgs = 512;       // two workgroups per CU
-#endif
-
-// The arrival counters sit at a fixed place, the first kCounterBytes of the
-// workspace, whatever the shape: split shapes have fewer than 128 tiles of 128 x
-// 128, so fewer than kMaxSplitTiles split tiles, and a later call of another
-// shape on the same workspace never finds partial tiles of an earlier call where
-// its counters are (every call leaves the counters it used at zero).
-constexpr int64_t kMaxSplitTiles = kSplitCounterBytes / 4;
-constexpr int64_t kCounterBytes = kSplitCounterBytes;
+static_assert(SplitCfg::BM == kSplitTile && SplitCfg::BN == kSplitTile, "plan.h tiles");
 static_assert(128 * 128 * 128 / (SplitCfg::BM * SplitCfg::BN) <= kMaxSplitTiles,
               "counters for every split plan");
 
-struct SplitPlan {
-  int splits = 1, tiles_m = 0, tiles_n = 0;
-};
-
-SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int mode) {
-  SplitPlan plan;
-  const int64_t mid_tiles = ((M + Mid::BM - 1) / Mid::BM) * ((N + Mid::BN - 1) / Mid::BN);
-  if (mid_tiles >= 128 || K < 1024) return plan;
-  const int64_t tm = (M + SplitCfg::BM - 1) / SplitCfg::BM;
-  const int64_t tn = (N + SplitCfg::BN - 1) / SplitCfg::BN;
-  // K slices stay on the interior path: whole MX code groups (512 bytes of K, FP4
-  // 256: K counts bytes there, and an FP4 plan never splits more than the FP8
-  // plan of the same element count, so the workspace query covers both)
-  const int64_t gran = mode == kMx32 ? 16 * kBlkBytes : 128;
-  int best = 1;
-  for (int s = 2; s <= 16; s *= 2) {
-    if (K % (s * gran) != 0 || K / s < 512) break;
-    best = s;
-    if (tm * tn * s >= kSplitTargetWgs) break;
-  }
-  if (best == 1 || tm * tn > kMaxSplitTiles) return plan;
-  // the partials are addressed with 32-bit buffer offsets
-  if (tm * tn * best * SplitCfg::BM * SplitCfg::BN * 4 >= ((int64_t)1 << 31)) return plan;
-  plan.splits = best;
-  plan.tiles_m = (int)tm;
-  plan.tiles_n = (int)tn;
-  return plan;
-}
-
-constexpr int64_t kPartialFloats = SplitCfg::BM * SplitCfg::BN;
-// ring depth of the split-K mainloop in 128-K tiles: as deep as the LDS allows
-constexpr int kSplitRing = SplitCfg::kSlots >= 16 ? 8 : 4;
-
-__host__ __device__ constexpr int64_t counter_bytes(int64_t tiles) {
-  return (void)tiles, kCounterBytes;
-}
+// ring depth of the split-K mainloop in 128-K tiles
+constexpr int kSplitRing = 4;
 
 template <class Cfg, int MODE, typename OutT, bool FUSED>
 __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void splitk_kernel(GemmProblem p, int tiles_m,
@@ -335,7 +225,7 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void splitk_kernel
   int* counters = static_cast<int*>(p.workspace);
   constexpr int kVec = FM * FN * 4;
   const __amdgpu_buffer_rsrc_t rp =
-      buffer_rsrc(static_cast<uint8_t*>(p.workspace) + counter_bytes(tiles),
+      buffer_rsrc(static_cast<uint8_t*>(p.workspace) + kSplitCounterBytes,
                   (uint32_t)((int64_t)tiles * splits * kVec * Cfg::kThreads * 16));
   auto poff = [&](int slice, int r) {
     return ((((tile * splits + slice) * kVec) + r) * Cfg::kThreads + (int)threadIdx.x) * 16;
@@ -426,10 +316,22 @@ hipError_t launch_split(const GemmProblem& p, const SplitPlan& plan, hipStream_t
 
 template <int MODE, typename OutT, bool FUSED>
 hipError_t launch_plan(const GemmProblem& p, hipStream_t stream) {
-  const SplitPlan plan = plan_split(p.M, p.N, p.K, MODE);
-  if (plan.splits > 1) return launch_split<MODE, OutT, FUSED>(p, plan, stream);
-  if constexpr (kF4) return launch_mode_f4<MODE, OutT, FUSED>(p, stream);
-  else return launch_mode<MODE, OutT, FUSED>(p, stream);
+  constexpr bool kNoStream = FUSED || std::is_same<OutT, uint8_t>::value;
+  switch (choose_path(p.M, p.N, p.K, p.lda, p.ldb, MODE, kF4, kNoStream)) {
+    case kPathSplitK:
+      return launch_split<MODE, OutT, FUSED>(p, plan_split(p.M, p.N, p.K, MODE, kBlkBytes),
+                                             stream);
+    case kPathPersistent:
+      // (the fused epilogue stages through the ring, so it never runs in a stream)
+      if constexpr (!kNoStream && !kF4) return launch_persistent<Big, MODE, OutT>(p, stream);
+      return hipErrorInvalidValue;
+    case kPathTile256:
+      return launch_cfg<Big, MODE, OutT, FUSED>(p, stream);
+    case kPathTile128:
+      return launch_cfg<Mid, MODE, OutT, FUSED>(p, stream);
+    default:
+      return hipSuccess;
+  }
 }
 
 // kernels with the fused bias / activation epilogue only when it is asked for
@@ -448,10 +350,7 @@ hipError_t launch_any(const GemmProblem& p, hipStream_t stream) {
 // on the formats).
 #if FP8GEMM_FMT_A == 0 && FP8GEMM_FMT_B == 0
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int mode) {
-  const SplitPlan plan = plan_split(M, N, K, mode);
-  if (plan.splits <= 1) return 0;
-  const int64_t tiles = (int64_t)plan.tiles_m * plan.tiles_n;
-  return (size_t)(counter_bytes(tiles) + tiles * plan.splits * kPartialFloats * 4);
+  return (size_t)split_workspace_bytes(plan_split(M, N, K, mode, 32));
 }
 #define FP8GEMM_LAUNCH_NAME launch_gemm
 #elif FP8GEMM_FMT_A == 1 && FP8GEMM_FMT_B == 1

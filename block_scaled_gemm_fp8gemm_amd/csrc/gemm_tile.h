@@ -438,7 +438,8 @@ __device__ __forceinline__ void mainloop(const TileOperands& op, uint8_t* lds,
     for (int j = 0; j < FN; ++j) b[j] = w[Cfg::BM + brow[j]] >> (8 * h);
   };
   // codes of sub-tile s straight from global memory (K % 128 != 0): block 2s + h.
-  // FP4: blocks 4s + h (first MFMA, bits 0-7) and 4s + 2 + h (second, bits 16-23)
+  // FP4: blocks 4s + 2h (first MFMA, bits 0-7) and 4s + 2h + 1 (second MFMA, bits
+  // 8-15, which it reads through op_sel 1)
   auto load_reg_codes = [&](int s, uint32_t (&a)[FM], uint32_t (&b)[FN]) {
     const int blk = kF4 ? 4 * s + 2 * h : 2 * s + h;
     auto code = [&](const uint8_t* base, int b) { return b < nblk ? (uint32_t)base[b] : 127u; };
@@ -732,7 +733,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
 
   // ---- read side: per-lane LDS bases, constant offsets ----
   // fragment row r = wave base + 32 i + lane % 32; logical chunk 4p + 2c + h
-  // (K half p, chunk pair c) sits at (4p + 2c + h) ^ ((r >> 1) & 7)
+  // (K half p, chunk pair c; FP4 4p + 2h + c) sits at (chunk) ^ ((r >> 1) & 7)
   const int rsw = ((lane & 31) >> 1) & 7;
   const int ra = (wm * Cfg::WM + (lane & 31)) * kRowB;
   const int rb = (Cfg::BM + wn * Cfg::WN + (lane & 31)) * kRowB;

@@ -172,12 +172,7 @@ using Mid = TileCfg<128, 128, 64, 64, 4, 2>;
 
 template <class Cfg, int MODE, typename OutT>
 hipError_t launch_cfg(const GroupedProblem& p, hipStream_t stream) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-  }
+  const int cus = device_cu_count();
   const int tiles_n = (p.N + Cfg::BN - 1) / Cfg::BN;
   // never more workgroups than the largest possible tile count
   const int64_t max_tiles = (int64_t)((p.total_m + Cfg::BM - 1) / Cfg::BM + p.groups) * tiles_n;

@@ -7,6 +7,10 @@
 
 namespace fp8gemm {
 
+// Compute units of the current device, queried once per device and cached (256
+// on an MI355X; the persistent kernels launch one workgroup per CU).
+int device_cu_count();
+
 // Per-tensor quantisation keeps one partial maximum per workgroup of its first pass.
 constexpr int kQuantPartials = 1024;
 

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FP8GEMM_VERSION 150 /* 1.5.0: e5m2, fused epilogues, row-major B, MXFP4 (dense, grouped), MX output */
+#define FP8GEMM_VERSION 160 /* 1.6.0: e5m2, fused epilogues, row-major B, MXFP4 (dense, grouped), MX output, path query */
 
 typedef enum fp8gemm_status {
   FP8GEMM_SUCCESS = 0,
@@ -145,7 +145,10 @@ fp8gemm_status fp8gemm_quantize_ex(const float* x, int64_t rows, int64_t k, int6
 /* workspace: fp8gemm_workspace_size() bytes (may be 0 -> NULL allowed).  Its    */
 /* first 4 KiB hold split-K arrival counters: zero-fill the workspace before    */
 /* its first use; every call leaves the counters at zero (the rest is scratch), */
-/* so one workspace serves calls of every shape, including fp8gemm_run_kn.      */
+/* so one workspace serves calls of every shape, including fp8gemm_run_kn, as   */
+/* long as they run one after another.  Calls that may run concurrently (on     */
+/* different streams) need separate workspaces: the counters and the partial    */
+/* tiles sit at fixed places, so two overlapping calls on one workspace race.   */
 /* Accuracy: |C - C_ref| <= 1e-3 * sum_k|dq_a*dq_b| + 1 ulp of the output type. */
 /* ------------------------------------------------------------------------- */
 size_t fp8gemm_workspace_size(int64_t M, int64_t N, int64_t K, int mode);
@@ -276,6 +279,34 @@ fp8gemm_status fp8gemm_grouped_run_ex(int32_t num_groups, int64_t total_m, int64
                                       const void* scale_a, const void* scale_b, void* C,
                                       int64_t ldc, int out_dtype, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Which kernel a dense GEMM call of this shape runs (no HIP call, no launch):   */
+/* the tiling and persistence choices of "Hopper/Blackwell architecture          */
+/* features" §12.7 (tile size per shape, persistent kernels in §12.7.3) and the  */
+/* split along K for shapes with too few output tiles (the M = 128 shape of       */
+/* §12.2.4).  The arguments are those of fp8gemm_run_ex / fp8gemm_run_mxout: K   */
+/* in elements, lda / ldb in bytes; fused is nonzero when a bias or activation  */
+/* is fused or the output is quantised (fp8gemm_run_mxout).                      */
+/*   FP8GEMM_PATH_NONE       : nothing is launched (M or N is 0) or the formats   */
+/*                             or mode are invalid or not offered together.      */
+/*   FP8GEMM_PATH_SPLITK     : few output tiles: 64 x 64 tiles, K split over     */
+/*                             workgroups, fp32 partials in the workspace.       */
+/*   FP8GEMM_PATH_TILE128    : 128 x 128 tiles, one per workgroup.               */
+/*   FP8GEMM_PATH_TILE256    : 256 x 256 tiles, one per workgroup.               */
+/*   FP8GEMM_PATH_PERSISTENT : 256 x 256 tiles, one workgroup per compute unit   */
+/*                             walking its tiles as one copy stream.             */
+/* ------------------------------------------------------------------------- */
+typedef enum fp8gemm_path {
+  FP8GEMM_PATH_NONE = 0,
+  FP8GEMM_PATH_SPLITK = 1,
+  FP8GEMM_PATH_TILE128 = 2,
+  FP8GEMM_PATH_TILE256 = 3,
+  FP8GEMM_PATH_PERSISTENT = 4
+} fp8gemm_path;
+
+int fp8gemm_run_path(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int a_format,
+                     int b_format, int mode, int fused);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fp8gemm_status_string(int status);

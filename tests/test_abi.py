@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
         "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex", "fp8gemm_workspace_size_kn",
         "fp8gemm_run_kn", "fp8gemm_run_mxout",
         "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run", "fp8gemm_grouped_run_ex",
-        "fp8gemm_status_string",
+        "fp8gemm_run_path", "fp8gemm_status_string",
         "fp8gemm_version"}
     raw = ctypes.CDLL(F.library_path())
     for n in names:
@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert F.fp8gemm_version() == 150
+    assert F.fp8gemm_version() == 160
     for code, name in [(0, "FP8GEMM_SUCCESS"), (1, "FP8GEMM_ERROR_INVALID_VALUE"),
                        (2, "FP8GEMM_ERROR_MISALIGNED"), (3, "FP8GEMM_ERROR_NOT_SUPPORTED"),
                        (4, "FP8GEMM_ERROR_WORKSPACE"), (5, "FP8GEMM_ERROR_LAUNCH"),
@@ -63,6 +63,36 @@ def test_workspace_queries(lib):
     assert F.fp8gemm_workspace_size(128, 4096, 256, 0) == 0      # K too short to split
     assert F.fp8gemm_workspace_size(128, 4096, 4096, 7) == 0     # bad mode
     assert F.fp8gemm_grouped_workspace_size(8, 16384, 14336, 4096, 1) >= 0
+
+
+@pytest.mark.parametrize("shape,ld,fmt,mode,fused,path", [
+    ((0, 4096, 4096), None, "e4m3", "tensor", 0, "none"),
+    ((128, 4096, 4096), None, "e4m3", "tensor", 0, "splitk"),       # the decode-like shape
+    ((128, 4096, 4096), None, "e4m3", "mx32", 1, "splitk"),
+    ((128, 4096, 256), None, "e4m3", "tensor", 0, "tile128"),       # K too short to split
+    ((1024, 1024, 512), None, "e4m3", "mx32", 0, "tile128"),
+    ((4096, 4096, 4096), None, "e4m3", "rowwise", 0, "tile256"),    # 256 tiles: one per CU
+    ((8192, 8192, 8192), None, "e4m3", "mx32", 0, "tile256"),       # 1024 tiles
+    ((16384, 8192, 512), None, "e4m3", "tensor", 0, "persistent"),  # 2048 tiles, all interior
+    ((8192, 16384, 1024), None, "e4m3", "mx32", 0, "persistent"),
+    ((16384, 8192, 512), None, "e5m2", "rowwise", 0, "persistent"),
+    ((16384, 8192, 512), None, "e4m3", "tensor", 1, "tile256"),     # fused: never streamed
+    ((16384, 8192, 384), None, "e4m3", "tensor", 0, "tile256"),     # K % 512 != 0
+    ((16384, 8320, 512), None, "e4m3", "tensor", 0, "tile256"),     # N cut: edge tiles
+    ((4096, 4096, 4160), None, "e4m3", "mx32", 0, "tile128"),       # MX K tail: codes in registers
+    ((8192, 8192, 8192), None, "e2m1", "mx32", 0, "tile256"),       # FP4: never persistent
+    ((16384, 8192, 1024), None, "e2m1", "mx32", 0, "tile256"),
+    ((4000, 4096, 8192), None, "e2m1", "mx32", 0, "tile128"),
+    ((128, 4096, 4096), None, "e2m1", "mx32", 0, "splitk"),
+    ((128, 4096, 4096), None, "e2m1", "tensor", 0, "none"),        # FP4 takes MX scales only
+])
+def test_run_path_rules(lib, shape, ld, fmt, mode, fused, path):
+    """The kernel a dense GEMM shape dispatches to (the query runs the launch code's
+    own planner)."""
+    M, N, K = shape
+    kb = K // 2 if fmt == "e2m1" else K
+    f = F.FORMATS[fmt]
+    assert F.fp8gemm_run_path(M, N, K, kb, kb, f, f, F.SCALE_MODES[mode], fused) == path
 
 
 def _quant(lib, x=P, rows=64, k=256, ldx=256, mode=1, q=P2, ldq=256, scales=P3, ws=0, wsb=0):

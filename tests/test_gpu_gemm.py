@@ -71,7 +71,7 @@ def _slice_scales(s, idx, mode):
     ("rowwise", (4096, 4096, 640)),
     ("mx32", (1024, 1024, 512)),      # small-tile kernel
     ("rowwise", (1024, 768, 384)),
-    # more tiles than CUs: persistent workgroups walk several tiles each
+    # 512 - 1024 tiles of 256 x 256: one tile per workgroup, several waves of workgroups
     ("tensor", (8192, 4096, 1024)),
     ("rowwise", (8192, 8192, 512)),
     ("mx32", (6144, 8192, 1024)),
@@ -92,6 +92,50 @@ def test_gemm_interior_sampled(mode, shape):
                                   _slice_scales(sb, ci, mode), mode)
         assert_within_bound(to_host(C[r0:r0 + 128, c0:c0 + 128]), Cr, Ar, "bf16",
                             f"interior {mode} {shape} block {(r0, c0)}")
+
+
+def _grouped_tile(linear, tiles_m, tiles_n, group_m=4):
+    """Position in the grouped tile order -> (tile row, tile column): groups of
+    group_m tile rows, column-major inside a group (the order the kernels use)."""
+    per_group = group_m * tiles_n
+    gid = linear // per_group
+    first_m = gid * group_m
+    rows = min(tiles_m - first_m, group_m)
+    in_group = linear - gid * per_group
+    return first_m + in_group % rows, in_group // rows
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("out", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [(16384, 8192, 512), (8192, 16384, 1024)])
+def test_gemm_persistent_sampled(mode, out, shape):
+    """Shapes with >= 2048 tiles of 256 x 256, all interior, take the persistent
+    kernel: one workgroup per CU walks tiles slot, slot + 256, ... of the grouped
+    order as one copy stream.  The oracle checks 128 x 128 blocks of the first and
+    the last tile of several workgroups' lists (both diagonal quadrants of each),
+    the first and the last tile of the matrix."""
+    M, N, K = shape
+    assert F.fp8gemm_run_path(M, N, K, K, K, 0, 0, F.SCALE_MODES[mode], 0) == "persistent"
+    qa, sa, qb, sb = _oracle_operands(M, N, K, mode, seed=M // 7 + N + K, dist="mx_block")
+    announce("gemm persistent", mode, out, shape)
+    C = _run_gpu(qa, sa, qb, sb, mode, out)
+    torch.cuda.synchronize()
+    tiles_m, tiles_n = M // 256, N // 256
+    total, grid = tiles_m * tiles_n, 256            # one workgroup per CU of an MI355X
+    positions = {0, total - 1}
+    for slot in (0, 37, 128, 200, 255):
+        count = (total - slot + grid - 1) // grid
+        positions |= {slot, slot + (count - 1) * grid}
+    blocks = set()
+    for pos in sorted(positions):
+        tm, tn = _grouped_tile(pos, tiles_m, tiles_n)
+        blocks |= {(tm * 256, tn * 256), (tm * 256 + 128, tn * 256 + 128)}
+    for r0, c0 in sorted(blocks):
+        ri, ci = np.arange(r0, r0 + 128), np.arange(c0, c0 + 128)
+        Cr, Ar = O.gemm_reference(qa[ri], _slice_scales(sa, ri, mode), qb[ci],
+                                  _slice_scales(sb, ci, mode), mode)
+        assert_within_bound(to_host(C[r0:r0 + 128, c0:c0 + 128]), Cr, Ar, out,
+                            f"persistent {mode}/{out} {shape} block {(r0, c0)}")
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -145,6 +189,35 @@ def test_gemm_splitk_repeat_and_interleave():
         assert torch.equal(first2, again2)
     Cr, Ar = O.gemm_reference(*ops1, "tensor")
     assert_within_bound(to_host(first1), Cr, Ar, "bf16", "split-K repeat")
+
+
+def test_gemm_splitk_two_streams():
+    """Split-K GEMMs queued on two streams at once: the binding gives each stream
+    its own workspace (counters and partial tiles), so neither corrupts the other."""
+    ops1 = _oracle_operands(128, 4096, 4096, "tensor", seed=31)
+    ops2 = _oracle_operands(128, 2048, 4096, "rowwise", seed=32)
+    announce("gemm split-K on two streams")
+    d1 = [to_dev(ops1[0], 16), scale_to_dev(ops1[1], "tensor"), to_dev(ops1[2], 16),
+          scale_to_dev(ops1[3], "tensor")]
+    d2 = [to_dev(ops2[0], 16), scale_to_dev(ops2[1], "rowwise"), to_dev(ops2[2], 16),
+          scale_to_dev(ops2[3], "rowwise")]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()        # default priority
+    outs1, outs2 = [], []
+    for _ in range(6):
+        with torch.cuda.stream(s1):
+            outs1.append(F.gemm(*d1, "tensor", "bf16"))
+        with torch.cuda.stream(s2):
+            outs2.append(F.gemm(*d2, "rowwise", "bf16"))
+    torch.cuda.synchronize()
+    for c in outs1[1:]:
+        assert torch.equal(c, outs1[0])
+    for c in outs2[1:]:
+        assert torch.equal(c, outs2[0])
+    Cr, Ar = O.gemm_reference(*ops1, "tensor")
+    assert_within_bound(to_host(outs1[0]), Cr, Ar, "bf16", "split-K stream 1")
+    Cr, Ar = O.gemm_reference(*ops2, "rowwise")
+    assert_within_bound(to_host(outs2[-1]), Cr, Ar, "bf16", "split-K stream 2")
 
 
 def test_gemm_k16_tail_with_canaries():

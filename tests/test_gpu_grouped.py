@@ -40,9 +40,11 @@ def _dev3(q):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("out", ["bf16", "f16"])
 @pytest.mark.parametrize("counts,N,K", [([5, 0, 300, 77], 200, 192), ([0, 0, 513], 64, 128),
-                                        ([1, 1, 1, 1, 1, 1], 300, 64), ([256, 256], 512, 256)])
-def test_grouped_small(mode, counts, N, K):
+                                        ([1, 1, 1, 1, 1, 1], 300, 64), ([256, 256], 512, 256),
+                                        ([300, 0, 1200, 500], 768, 1024)])
+def test_grouped_small(mode, out, counts, N, K):
     rng = np.random.default_rng(sum(counts) + N + K)
     counts = np.array(counts)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
@@ -50,11 +52,11 @@ def test_grouped_small(mode, counts, N, K):
     W = np.stack([normal(rng, N, K, 0.02) for _ in counts])
     qa, sa = Q.quantize(x, mode)
     qw, sw = _quant_experts(W, mode)
-    announce("grouped", mode, counts.tolist(), N, K)
+    announce("grouped", mode, out, counts.tolist(), N, K)
     C = F.grouped_gemm(to_dev(qa, 16), scale_to_dev(sa, mode), torch.from_numpy(off).to(DEV),
-                       _dev3(qw), torch.from_numpy(np.ascontiguousarray(sw)).to(DEV), mode, "bf16")
+                       _dev3(qw), torch.from_numpy(np.ascontiguousarray(sw)).to(DEV), mode, out)
     Cr, Ar = O.grouped_reference(qa, sa, off, qw, sw, mode)
-    assert_within_bound(to_host(C), Cr, Ar, "bf16", f"grouped {mode} {counts.tolist()}")
+    assert_within_bound(to_host(C), Cr, Ar, out, f"grouped {mode}/{out} {counts.tolist()}")
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -112,10 +114,11 @@ def test_workload_grouped_moe():
     assert_within_bound(Cg, Cr, Ar, w.out, "grouped_moe sampled rows")
 
 
+@pytest.mark.parametrize("out", ["bf16", "f16"])
 @pytest.mark.parametrize("counts,N,K", [([5, 0, 300, 77], 200, 192), ([0, 0, 513], 64, 128),
                                         ([1, 1, 1, 1, 1, 1], 300, 64), ([256, 256], 512, 512),
                                         ([130, 0, 260], 256, 1056), ([130, 0, 300, 7], 512, 1024)])
-def test_grouped_fp4(counts, N, K):
+def test_grouped_fp4(out, counts, N, K):
     """MXFP4 activations and experts (two e2m1 codes per byte): ragged and empty
     experts, experts shorter than a tile, whole code groups and a K tail, on both
     tile sizes (K a multiple of 256: the 256 x 256 tile with cut tiles)."""
@@ -127,10 +130,10 @@ def test_grouped_fp4(counts, N, K):
     qa, sa = Q.quantize(x, "mx32", "e2m1")
     qs, ss = zip(*[Q.quantize(W[g], "mx32", "e2m1") for g in range(len(counts))])
     qw, sw = np.stack(qs), np.stack(ss)
-    announce("grouped e2m1", counts.tolist(), N, K)
+    announce("grouped e2m1", out, counts.tolist(), N, K)
     C = F.grouped_gemm(to_dev(O.pack_fp4(qa), 16), scale_to_dev(sa, "mx32"),
                        torch.from_numpy(off).to(DEV), _dev3(O.pack_fp4(qw)),
-                       torch.from_numpy(np.ascontiguousarray(sw)).to(DEV), "mx32", "bf16",
+                       torch.from_numpy(np.ascontiguousarray(sw)).to(DEV), "mx32", out,
                        fmt="e2m1")
     Cr, Ar = O.grouped_reference(qa, sa, off, qw, sw, "mx32", fmt="e2m1")
-    assert_within_bound(to_host(C), Cr, Ar, "bf16", f"grouped e2m1 {counts.tolist()}")
+    assert_within_bound(to_host(C), Cr, Ar, out, f"grouped e2m1/{out} {counts.tolist()}")
