@@ -28,7 +28,7 @@ __all__ = [
     "fp8gemm_quantize_ex", "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex",
     "fp8gemm_workspace_size_kn", "fp8gemm_run_kn",
     "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run",
-    "fp8gemm_run_path", "PATHS",
+    "fp8gemm_run_path", "PATHS", "fp8gemm_run_noalloc", "NOALLOC_SCRATCH_BYTES",
     "fp8gemm_status_string", "fp8gemm_version", "quantize", "gemm", "grouped_gemm",
     "exported_symbols",
 ]
@@ -40,6 +40,9 @@ SCALE_MODES = {"tensor": 0, "rowwise": 1, "mx32": 2}
 OUT_DTYPES = {"f16": 0, "bf16": 1}
 FORMATS = {"e4m3": 0, "e5m2": 1, "e2m1": 4}   # e2m1: FP4, two codes per byte, MX only
 ACTIVATIONS = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
+
+# FP8GEMM_NOALLOC_SCRATCH_BYTES: the static scratch of fp8gemm_run_noalloc
+NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024 + 4096
 
 # kernel paths of a dense GEMM (fp8gemm_run_path)
 PATHS = {0: "none", 1: "splitk", 2: "tile128", 3: "tile256", 4: "persistent"}
@@ -87,6 +90,8 @@ _SIGNATURES = {
     "fp8gemm_grouped_run_ex": (_int, [_i32, _i64, _i64, _i64, _p, _i64, _int, _p, _p, _i64, _int,
                                       _i64, _int, _p, _p, _p, _i64, _int, _p, _sz, _p]),
     "fp8gemm_run_path": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int, _int, _int]),
+    "fp8gemm_run_noalloc": (_int, [_i64, _i64, _i64, _p, _i64, _int, _p, _i64, _int, _int, _p, _p,
+                                   _p, _int, _p, _i64, _int, _p]),
     "fp8gemm_status_string": (ctypes.c_char_p, [_int]),
     "fp8gemm_version": (_int, []),
 }
@@ -208,6 +213,14 @@ def fp8gemm_grouped_run_ex(num_groups: int, total_m: int, N: int, K: int, A: int
     _check("fp8gemm_grouped_run_ex", load_library().fp8gemm_grouped_run_ex(
         num_groups, total_m, N, K, A, lda, a_format, offsets, B, ldb, b_format, stride_b, mode,
         scale_a, scale_b, C, ldc, out_dtype, workspace, workspace_bytes, stream))
+
+
+def fp8gemm_run_noalloc(M: int, N: int, K: int, A: int, lda: int, a_format: int, B: int,
+                        ldb: int, b_format: int, mode: int, scale_a: int, scale_b: int, bias: int,
+                        activation: int, C: int, ldc: int, out_dtype: int, stream: int) -> None:
+    _check("fp8gemm_run_noalloc", load_library().fp8gemm_run_noalloc(
+        M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias, activation, C,
+        ldc, out_dtype, stream))
 
 
 def fp8gemm_run_path(M: int, N: int, K: int, lda: int, ldb: int, a_format: int, b_format: int,

@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/fp8gemm.h"
 #include "launch.h"
@@ -157,7 +158,8 @@ fp8gemm_status run_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int6
                          int a_format, const uint8_t* B, int64_t ldb, int b_format, int mode,
                          const void* scale_a, const void* scale_b, const float* bias,
                          int activation, void* C, int64_t ldc, int out_dtype, uint8_t* cs,
-                         int64_t ldcs, void* workspace, size_t workspace_bytes, void* stream) {
+                         int64_t ldcs, void* workspace, size_t workspace_bytes, void* stream,
+                         bool dry_run = false) {
   const bool qout = out_dtype == fp8gemm::kE4M3Mx;
   if (!valid_mode(mode) || !(valid_out(out_dtype) || qout) || !valid_format(a_format) ||
       !valid_format(b_format) || !valid_act(activation) || M < 0 || N < 0 || K <= 0)
@@ -175,6 +177,8 @@ fp8gemm_status run_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int6
   fp8gemm_status st = check_gemm_common(M, N, K, A, lda, B, ldb, mode, scale_a, scale_b, C, ldc,
                                         out_dtype, fp4 ? 2 : 1);
   if (st != FP8GEMM_SUCCESS) return st;
+  if (bias && !aligned(bias, 4)) return FP8GEMM_ERROR_MISALIGNED;
+  if (dry_run) return FP8GEMM_SUCCESS;              // every check but the workspace's passed
   // FP4 shapes split along K at most as often as FP8 ones of the same element
   // count, so the query (K in elements) covers them too
   const size_t need = fp8gemm_workspace_size(M, N, K, mode);
@@ -193,7 +197,6 @@ fp8gemm_status run_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int6
   p.scale_b = scale_b;
   p.C = C;
   p.ldc = ldc;
-  if (bias && !aligned(bias, 4)) return FP8GEMM_ERROR_MISALIGNED;
   p.workspace = need > 0 ? workspace : nullptr;
   p.bias = bias;
   p.act = activation;
@@ -233,6 +236,76 @@ fp8gemm_status fp8gemm_run_mxout(int64_t M, int64_t N, int64_t K, const uint8_t*
   return run_dense(M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias,
                    activation, C, ldc, fp8gemm::kE4M3Mx, c_scales, ldcs, workspace,
                    workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// fp8gemm_run_noalloc: fp8gemm_run_ex for callers that cannot allocate (code
+// under graph capture, serving loops that forbid allocation).  The split-K
+// counters and partial tiles live in `scratch`, a static device array of
+// FP8GEMM_NOALLOC_SCRATCH_BYTES that each device holds from the library's load
+// until the process ends.  Host code never uses the array's name as an address
+// (on the host it only names the symbol): the first call on a device, with that
+// device current, looks its device address up with hipGetSymbolAddress, keeps
+// it for the device and zeroes the counter head with a fill kernel on the
+// caller's stream; from then on every call leaves the counters at zero.  The
+// kernels get that address as their workspace, as fp8gemm_run_ex's kernels get
+// the caller's workspace.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[FP8GEMM_NOALLOC_SCRATCH_BYTES];
+
+__global__ void zero_words(int* p, int n) {
+  for (int i = (int)threadIdx.x; i < n; i += (int)blockDim.x) p[i] = 0;
+}
+
+// Device address of `scratch` on the current device (nullptr on a HIP error).
+void* scratch_address(hipStream_t stream) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    hipLaunchKernelGGL(zero_words, dim3(1), dim3(256), 0, stream, static_cast<int*>(p),
+                       (int)(fp8gemm::kSplitCounterBytes / 4));
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8gemm_status fp8gemm_run_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                   int a_format, const uint8_t* B, int64_t ldb, int b_format,
+                                   int mode, const void* scale_a, const void* scale_b,
+                                   const float* bias, int activation, void* C, int64_t ldc,
+                                   int out_dtype, void* stream) {
+  if (!valid_out(out_dtype)) return FP8GEMM_ERROR_INVALID_VALUE;
+  // every argument check first, without a workspace and without any HIP call
+  fp8gemm_status st = run_dense(M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a,
+                                scale_b, bias, activation, C, ldc, out_dtype, nullptr, 0, nullptr,
+                                0, stream, /*dry_run=*/true);
+  if (st != FP8GEMM_SUCCESS || M == 0 || N == 0) return st;
+  const size_t need = fp8gemm_workspace_size(M, N, K, mode);
+  if (need > (size_t)FP8GEMM_NOALLOC_SCRATCH_BYTES) return FP8GEMM_ERROR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_address(s);
+    if (ws == nullptr) return FP8GEMM_ERROR_LAUNCH;
+  }
+  return run_dense(M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias,
+                   activation, C, ldc, out_dtype, nullptr, 0, ws,
+                   need > 0 ? (size_t)FP8GEMM_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 // Row-major B: the workspace starts with the GEMM's own workspace (at least the

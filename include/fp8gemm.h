@@ -281,6 +281,32 @@ fp8gemm_status fp8gemm_grouped_run_ex(int32_t num_groups, int64_t total_m, int64
                                       size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* fp8gemm_run_ex without a workspace, for callers that cannot allocate device  */
+/* memory (code under HIP graph capture, serving loops or harnesses that forbid */
+/* allocation).  The call allocates nothing: the split-K counters and partial   */
+/* tiles go to a static device array of FP8GEMM_NOALLOC_SCRATCH_BYTES that every */
+/* device the library runs on holds until the process ends.  The first call on */
+/* a device (with it current) looks the array's address up and zeroes its       */
+/* counters with a kernel on `stream`; every call leaves them at zero again.    */
+/* Arguments, results, accuracy and errors as fp8gemm_run_ex, except:           */
+/*   - a shape whose fp8gemm_workspace_size() exceeds                           */
+/*     FP8GEMM_NOALLOC_SCRATCH_BYTES returns FP8GEMM_ERROR_WORKSPACE, checked    */
+/*     before any HIP call (every shape with at most 512 split workgroups fits,  */
+/*     the M = 128, N = K = 4096 decode shape among them);                      */
+/*   - FP8GEMM_ERROR_LAUNCH also reports a failed look-up of the scratch.       */
+/* All calls on one device share its scratch, which keeps the last call's       */
+/* contents: calls that may overlap on one device (different streams or host    */
+/* threads) race and must be ordered by the caller.                             */
+/* ------------------------------------------------------------------------- */
+#define FP8GEMM_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024 + 4096)
+
+fp8gemm_status fp8gemm_run_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                   int a_format, const uint8_t* B, int64_t ldb, int b_format,
+                                   int mode, const void* scale_a, const void* scale_b,
+                                   const float* bias, int activation, void* C, int64_t ldc,
+                                   int out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* Which kernel a dense GEMM call of this shape runs (no HIP call, no launch):   */
 /* the tiling and persistence choices of "Hopper/Blackwell architecture          */
 /* features" §12.7 (tile size per shape, persistent kernels in §12.7.3) and the  */

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
         "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex", "fp8gemm_workspace_size_kn",
         "fp8gemm_run_kn", "fp8gemm_run_mxout",
         "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run", "fp8gemm_grouped_run_ex",
-        "fp8gemm_run_path", "fp8gemm_status_string",
+        "fp8gemm_run_path", "fp8gemm_run_noalloc", "fp8gemm_status_string",
         "fp8gemm_version"}
     raw = ctypes.CDLL(F.library_path())
     for n in names:
@@ -93,6 +93,31 @@ def test_run_path_rules(lib, shape, ld, fmt, mode, fused, path):
     kb = K // 2 if fmt == "e2m1" else K
     f = F.FORMATS[fmt]
     assert F.fp8gemm_run_path(M, N, K, kb, kb, f, f, F.SCALE_MODES[mode], fused) == path
+
+
+def _noalloc(lib, M=128, N=4096, K=4096, A=P, lda=4096, B=P2, ldb=4096, mode=0, sa=P3, sb=P3,
+             C=P, ldc=4096, out=1, afmt=0, bfmt=0, bias=0, act=0):
+    return lib.fp8gemm_run_noalloc(M, N, K, A, lda, afmt, B, ldb, bfmt, mode, sa, sb, bias, act, C,
+                                   ldc, out, None)
+
+
+def test_noalloc_validation(lib):
+    """Argument errors and a split too large for the static scratch are reported
+    before any HIP call (the fake addresses are never touched)."""
+    assert F.NOALLOC_SCRATCH_BYTES == 8 * 1024 * 1024 + 4096
+    assert _noalloc(lib, out=5) == INVALID
+    assert _noalloc(lib, mode=9) == INVALID
+    assert _noalloc(lib, A=0) == INVALID
+    assert _noalloc(lib, lda=100) == INVALID                  # lda < K
+    assert _noalloc(lib, K=4008) == NOT_SUPPORTED             # K % 16 != 0
+    assert _noalloc(lib, A=P + 8) == MISALIGNED
+    assert _noalloc(lib, bias=P + 2) == MISALIGNED
+    assert _noalloc(lib, afmt=4, bfmt=0, mode=2) == NOT_SUPPORTED
+    assert _noalloc(lib, M=0) == SUCCESS                      # nothing to do
+    # 504 split tiles x 2 K slices: 16.5 MB of partials, more than the scratch
+    M, N, K = 256, 8064, 4096
+    assert F.fp8gemm_workspace_size(M, N, K, 0) > F.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(lib, M=M, N=N, K=K, lda=K, ldb=K, ldc=N) == WORKSPACE
 
 
 def _quant(lib, x=P, rows=64, k=256, ldx=256, mode=1, q=P2, ldq=256, scales=P3, ws=0, wsb=0):
