@@ -350,7 +350,7 @@ hipError_t launch_any(const GemmProblem& p, hipStream_t stream) {
 // on the formats).
 #if FP8GEMM_FMT_A == 0 && FP8GEMM_FMT_B == 0
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int mode) {
-  return (size_t)split_workspace_bytes(plan_split(M, N, K, mode, 32));
+  return (size_t)gemm_workspace_need(M, N, K, mode);
 }
 #define FP8GEMM_LAUNCH_NAME launch_gemm
 #elif FP8GEMM_FMT_A == 1 && FP8GEMM_FMT_B == 1

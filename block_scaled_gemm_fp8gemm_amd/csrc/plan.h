@@ -76,6 +76,13 @@ inline int64_t split_workspace_bytes(const SplitPlan& plan) {
   return kSplitCounterBytes + tiles * plan.splits * kSplitTile * kSplitTile * 4;
 }
 
+// Workspace a dense GEMM needs (K in elements): the split-K plan of FP8
+// operands; FP4 shapes split along K at most as often as FP8 ones of the same
+// element count (their slices are whole 256-byte code groups), so this covers them.
+inline int64_t gemm_workspace_need(int64_t M, int64_t N, int64_t K, int mode) {
+  return split_workspace_bytes(plan_split(M, N, K, mode, 32));
+}
+
 // The byte span of a tile's rows fits the 32-bit offsets of a buffer descriptor.
 inline bool spans_fit(int64_t rows, int64_t ld, int64_t K) {
   return rows * ld + K < ((int64_t)1 << 31);

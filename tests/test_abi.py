@@ -69,6 +69,10 @@ def test_workspace_queries(lib):
     ((0, 4096, 4096), None, "e4m3", "tensor", 0, "none"),
     ((128, 4096, 4096), None, "e4m3", "tensor", 0, "splitk"),       # the decode-like shape
     ((128, 4096, 4096), None, "e4m3", "mx32", 1, "splitk"),
+    ((1, 8192, 1024), None, "e5m2", "rowwise", 0, "splitk"),
+    ((128, 4096, 4160), None, "e4m3", "tensor", 0, "tile128"),     # K % 256 != 0: no slices
+    ((256, 640, 4096), None, "e4m3", "rowwise", 0, "splitk"),
+    ((128, 16384, 4096), None, "e4m3", "tensor", 0, "tile128"),    # 128 tiles of 128 x 128
     ((128, 4096, 256), None, "e4m3", "tensor", 0, "tile128"),       # K too short to split
     ((1024, 1024, 512), None, "e4m3", "mx32", 0, "tile128"),
     ((4096, 4096, 4096), None, "e4m3", "rowwise", 0, "tile256"),    # 256 tiles: one per CU

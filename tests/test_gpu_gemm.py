@@ -169,6 +169,37 @@ def test_gemm_few_rows(mode, out, shape):
     assert_within_bound(C, Cr, Ar, out, f"few rows {mode}/{out}/{shape}")
 
 
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("out,shape", [
+    ("bf16", (128, 4096, 4096)),   # the decode-like shape
+    ("f16", (1, 2048, 1024)),      # one row; 512-K slices
+    ("bf16", (33, 1000, 2048)),    # ragged M and N
+    ("f16", (100, 12000, 1024)),   # N ragged
+    ("bf16", (64, 4100, 8192)),    # last tile 4 columns, K = 8192
+    ("bf16", (128, 4096, 8192)),
+    ("bf16", (128, 256, 1024)),    # few tiles
+])
+def test_gemm_decode_shapes(mode, out, shape):
+    """Few rows of A (M <= 128) against many columns of B, split along K where the
+    output tiles alone do not fill the GPU; the whole output, or all rows x
+    sampled 128-column blocks for the large shapes, against the oracle."""
+    M, N, K = shape
+    qa, sa, qb, sb = _oracle_operands(M, N, K, mode, seed=M + 3 * N + K, dist="mx_block")
+    path = F.fp8gemm_run_path(M, N, K, K, K, 0, 0, F.SCALE_MODES[mode], 0)
+    announce("gemm decode shape", mode, out, shape, path)
+    C = _run_gpu(qa, sa, qb, sb, mode, out)
+    torch.cuda.synchronize()
+    if N * K <= 4096 * 4096:
+        Cr, Ar = O.gemm_reference(qa, sa, qb, sb, mode)
+        assert_within_bound(to_host(C), Cr, Ar, out, f"decode {mode}/{out} {shape}")
+        return
+    for c0 in (0, N - 128, (N // 3) // 32 * 32):
+        ci = np.arange(c0, c0 + 128)
+        Cr, Ar = O.gemm_reference(qa, sa, qb[ci], _slice_scales(sb, ci, mode), mode)
+        assert_within_bound(to_host(C[:, c0:c0 + 128]), Cr, Ar, out,
+                            f"decode {mode}/{out} {shape} columns {c0}..")
+
+
 def test_gemm_splitk_repeat_and_interleave():
     """The per-tile counters reset themselves: repeated and interleaved calls on one
     workspace give bit-identical results (the partials are summed in slice order)."""

@@ -1,8 +1,8 @@
 """fp8gemm_run_noalloc (no workspace argument, a static device scratch) against
 fp8gemm_run_ex (the caller's workspace) and the oracle.
 
-Two calls in a row on split-K shapes (the path that needs scratch), the second
-with a smaller input, in every scale mode: the output must be bit-identical to
+Calls in a row on split-K shapes (the path that needs scratch), each smaller
+than the one before it, in every scale mode: the output must be bit-identical to
 fp8gemm_run_ex's (both run the same kernels) and within the GEMM bound of the
 oracle.  A shape without split-K runs without touching the scratch, and a shape
 whose split needs more than the scratch holds is rejected before any launch.
@@ -39,7 +39,8 @@ def _run_noalloc(M, N, K, d, mode, out, C):
 
 @pytest.mark.parametrize("mode", ["tensor", "rowwise", "mx32"])
 def test_noalloc_two_calls_match_run_ex(mode):
-    for i, (M, N, K) in enumerate([(128, 4096, 4096), (64, 2048, 2048)]):
+    for i, (M, N, K) in enumerate([(256, 640, 4096), (128, 4096, 4096), (64, 2048, 2048),
+                                   (100, 512, 2048)]):
         assert F.fp8gemm_run_path(M, N, K, K, K, 0, 0, F.SCALE_MODES[mode], 0) == "splitk"
         assert 0 < F.fp8gemm_workspace_size(M, N, K, F.SCALE_MODES[mode]) <= \
             F.NOALLOC_SCRATCH_BYTES
