@@ -21,17 +21,19 @@ layouts therefore follow the public standards those names refer to: the OCP
 pattern per sign, max 448; E5M2 with IEEE-like infinities and NaNs, max 57344) and the OCP Microscaling (MX) formats
 specification v1.0 (E8M0 shared scale, 32-element blocks, scale exponent =
 floor(log2(amax)) - emax of the element format; the FP4 E2M1 element of
-MXFP4, max 6, which §12.6.1 of the architecture page lists next to FP8).
+MXFP4, max 6, and the FP6 E2M3 / E3M2 elements of MXFP6, max 7.5 / 28, which
+§12.6.1 of the architecture page lists next to FP8).
 
 Parity pins.  Every function here is pinned by ``tests/test_oracle_*.py``
 against exhaustive enumeration, exact rational arithmetic, integer-exact
 products, closed forms or the specifications' tabulated points
 (``tests/golden/``).  No function is "parity unpinned".
 """
-from .formats import (E2M1_DECODE, E2M1_MAX, E4M3_DECODE, E4M3_MAX, E5M2_DECODE, E5M2_MAX,
-                      E8M0_DECODE, FORMATS, decode, decode_e2m1, decode_e4m3, decode_e5m2,
-                      decode_e8m0, encode, encode_e2m1, encode_e4m3, encode_e5m2, pack_fp4,
-                      unpack_fp4)
+from .formats import (E2M1_DECODE, E2M1_MAX, E2M3_DECODE, E2M3_MAX, E3M2_DECODE, E3M2_MAX,
+                      E4M3_DECODE, E4M3_MAX, E5M2_DECODE, E5M2_MAX, E8M0_DECODE, FORMATS,
+                      decode, decode_e2m1, decode_e2m3, decode_e3m2, decode_e4m3, decode_e5m2,
+                      decode_e8m0, encode, encode_e2m1, encode_e2m3, encode_e3m2, encode_e4m3,
+                      encode_e5m2, pack_fp4, pack_fp6, unpack_fp4, unpack_fp6)
 from .quant import quantize, quantize_mx, quantize_rowwise, quantize_tensor
 from .gemm import (ACT_LIPSCHITZ, activation, dequantize, epilogue_reference,
                    epilogue_tolerance, gemm_reference, grouped_reference, mx_output_reference,
@@ -39,6 +41,8 @@ from .gemm import (ACT_LIPSCHITZ, activation, dequantize, epilogue_reference,
 
 __all__ = [
     "E2M1_DECODE", "E2M1_MAX", "decode_e2m1", "encode_e2m1", "pack_fp4", "unpack_fp4",
+    "E2M3_DECODE", "E2M3_MAX", "E3M2_DECODE", "E3M2_MAX", "decode_e2m3", "decode_e3m2",
+    "encode_e2m3", "encode_e3m2", "pack_fp6", "unpack_fp6",
     "E4M3_DECODE", "E4M3_MAX", "E5M2_DECODE", "E5M2_MAX", "E8M0_DECODE", "FORMATS", "decode",
     "decode_e4m3", "decode_e5m2", "decode_e8m0", "encode", "encode_e4m3", "encode_e5m2",
     "quantize", "quantize_mx", "quantize_rowwise", "quantize_tensor",

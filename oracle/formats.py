@@ -1,4 +1,4 @@
-"""e4m3fn, e5m2, e2m1 and E8M0 codes: decode tables and the round-to-nearest-even encoders.
+"""e4m3fn, e5m2, e2m1, e2m3, e3m2 and E8M0 codes: decode tables and the round-to-nearest-even encoders.
 
 TEST INFRASTRUCTURE (see the package docstring).
 
@@ -24,6 +24,14 @@ experimental.  The OCP MX v1.0 layout: 1 sign bit, 2 exponent bits with bias
 no NaN, so the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.  A code here is the
 4-bit pattern S.EE.M in the low bits of a byte (sign = bit 3); two codes share
 a byte when packed (see ``pack_fp4``).
+
+E2M3 and E3M2 (FP6) are the 6-bit element formats of MXFP6, the other narrow
+format §12.6.1 lists next to FP4.  The OCP MX v1.0 layouts: 1 sign bit (bit 5),
+then 2 exponent bits with bias 1 and 3 mantissa bits (E2M3: subnormals m/8,
+normals (1 + m/8) 2^(e-1), largest 7.5), or 3 exponent bits with bias 3 and 2
+mantissa bits (E3M2: subnormals m/16, normals (1 + m/4) 2^(e-3), largest 28);
+no infinity and no NaN.  Packed, a row of codes is a little-endian bit string,
+element i in bits 6i .. 6i + 5 (four codes in three bytes, see ``pack_fp6``).
 
 E8M0 is the MX shared-scale format ("Hopper/Blackwell architecture features"
 §12.6.1 names MXFP8): an 8-bit biased exponent, value 2^(code-127), with 0xFF
@@ -81,6 +89,30 @@ def _e2m1_value(code: int) -> float:
     return -mag if s else mag
 
 
+def _e2m3_value(code: int) -> float:
+    """Value of one 6-bit e2m3 code from its bit fields (OCP MX FP6 E2M3 definition)."""
+    s = (code >> 5) & 1
+    e = (code >> 3) & 0x3
+    m = code & 0x7
+    if e == 0:
+        mag = math.ldexp(m, -3)             # subnormal: 0.m * 2^(1-1) = m * 2^-3
+    else:
+        mag = math.ldexp(8 + m, e - 1 - 3)  # normal: 1.m * 2^(e-1) = (8+m) * 2^(e-4)
+    return -mag if s else mag
+
+
+def _e3m2_value(code: int) -> float:
+    """Value of one 6-bit e3m2 code from its bit fields (OCP MX FP6 E3M2 definition)."""
+    s = (code >> 5) & 1
+    e = (code >> 2) & 0x7
+    m = code & 0x3
+    if e == 0:
+        mag = math.ldexp(m, -4)             # subnormal: 0.m * 2^(1-3) = m * 2^-4
+    else:
+        mag = math.ldexp(4 + m, e - 3 - 2)  # normal: 1.m * 2^(e-3) = (4+m) * 2^(e-5)
+    return -mag if s else mag
+
+
 def _e8m0_value(code: int) -> float:
     return math.nan if code == 0xFF else math.ldexp(1.0, code - 127)
 
@@ -89,6 +121,10 @@ E4M3_DECODE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
 E5M2_DECODE = np.array([_e5m2_value(c) for c in range(256)], dtype=np.float64)
 E2M1_MAX = 6.0
 E2M1_DECODE = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
+E2M3_MAX = 7.5
+E2M3_DECODE = np.array([_e2m3_value(c) for c in range(64)], dtype=np.float64)
+E3M2_MAX = 28.0
+E3M2_DECODE = np.array([_e3m2_value(c) for c in range(64)], dtype=np.float64)
 E8M0_DECODE = np.array([_e8m0_value(c) for c in range(256)], dtype=np.float64)
 
 # Non-negative finite magnitudes, indexed by code (strictly increasing):
@@ -96,6 +132,8 @@ E8M0_DECODE = np.array([_e8m0_value(c) for c in range(256)], dtype=np.float64)
 _POS_MAGS = E4M3_DECODE[:0x7F].copy()
 _POS_MAGS_E5M2 = E5M2_DECODE[:0x7C].copy()
 _POS_MAGS_E2M1 = E2M1_DECODE[:0x8].copy()          # e2m1 0x0..0x7
+_POS_MAGS_E2M3 = E2M3_DECODE[:0x20].copy()         # e2m3 0x00..0x1F
+_POS_MAGS_E3M2 = E3M2_DECODE[:0x20].copy()         # e3m2 0x00..0x1F
 
 
 def decode_e4m3(q: np.ndarray) -> np.ndarray:
@@ -206,12 +244,64 @@ def unpack_fp4(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+def decode_e2m3(q: np.ndarray) -> np.ndarray:
+    """float64 values of 6-bit e2m3 codes held one per uint8 (exact)."""
+    return E2M3_DECODE[np.asarray(q, dtype=np.uint8) & 0x3F]
+
+
+def decode_e3m2(q: np.ndarray) -> np.ndarray:
+    """float64 values of 6-bit e3m2 codes held one per uint8 (exact)."""
+    return E3M2_DECODE[np.asarray(q, dtype=np.uint8) & 0x3F]
+
+
+def encode_e2m3(v: np.ndarray) -> np.ndarray:
+    """Nearest e2m3 code to each value (one 6-bit code per uint8), ties to the
+    even code, saturating: the definition of ``encode_e4m3`` over the 32
+    non-negative e2m3 magnitudes; magnitudes at or above 7.5 give 7.5 (code
+    0x1F), the sign goes to bit 5.  No NaN exists (NaN inputs give 0x1F | sign)."""
+    return _encode_by_table(v, _POS_MAGS_E2M3, E2M3_MAX, 0x1F, sign_bit=5)
+
+
+def encode_e3m2(v: np.ndarray) -> np.ndarray:
+    """Nearest e3m2 code to each value (one 6-bit code per uint8), ties to the
+    even code, saturating at 28 (code 0x1F); sign in bit 5, as ``encode_e2m3``."""
+    return _encode_by_table(v, _POS_MAGS_E3M2, E3M2_MAX, 0x1F, sign_bit=5)
+
+
+def pack_fp6(codes: np.ndarray) -> np.ndarray:
+    """6-bit codes packed along the last axis as a little-endian bit string:
+    element i in bits 6i .. 6i + 5, so each group of four codes c0..c3 is the
+    24-bit word c0 | c1 << 6 | c2 << 12 | c3 << 18 stored in three bytes, low
+    byte first."""
+    c = np.asarray(codes, dtype=np.uint32) & 0x3F
+    if c.shape[-1] % 4:
+        raise ValueError("a multiple of four 6-bit codes per row is needed")
+    w = c[..., 0::4] | (c[..., 1::4] << 6) | (c[..., 2::4] << 12) | (c[..., 3::4] << 18)
+    out = np.empty(c.shape[:-1] + (3 * w.shape[-1],), dtype=np.uint8)
+    out[..., 0::3] = w & 0xFF
+    out[..., 1::3] = (w >> 8) & 0xFF
+    out[..., 2::3] = (w >> 16) & 0xFF
+    return out
+
+
+def unpack_fp6(packed: np.ndarray) -> np.ndarray:
+    """Inverse of ``pack_fp6``: one 6-bit code per uint8, 4/3 as many columns."""
+    p = np.asarray(packed, dtype=np.uint32)
+    w = p[..., 0::3] | (p[..., 1::3] << 8) | (p[..., 2::3] << 16)
+    out = np.empty(p.shape[:-1] + (4 * w.shape[-1],), dtype=np.uint8)
+    for j in range(4):
+        out[..., j::4] = (w >> (6 * j)) & 0x3F
+    return out
+
+
 # Element formats by name: decode, encode, largest finite magnitude and the
 # exponent of that magnitude (emax, used by the MX scale rule).
 FORMATS = {
     "e4m3": {"decode": decode_e4m3, "encode": encode_e4m3, "max": E4M3_MAX, "emax": 8},
     "e5m2": {"decode": decode_e5m2, "encode": encode_e5m2, "max": E5M2_MAX, "emax": 15},
     "e2m1": {"decode": decode_e2m1, "encode": encode_e2m1, "max": E2M1_MAX, "emax": 2},
+    "e2m3": {"decode": decode_e2m3, "encode": encode_e2m3, "max": E2M3_MAX, "emax": 2},
+    "e3m2": {"decode": decode_e3m2, "encode": encode_e3m2, "max": E3M2_MAX, "emax": 4},
 }
 
 

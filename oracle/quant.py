@@ -30,6 +30,12 @@ exponent is 2, so e = floor(log2 amax) - 2; values in (6, 8) saturate to 6.
 Its codes are returned one per uint8 (``formats.pack_fp4`` gives the packed
 two-per-byte layout); per-tensor and row-wise FP4 are not defined here.
 
+MXFP6 likewise takes the MX rule with e2m3 elements (largest 7.5, exponent 2:
+e = floor(log2 amax) - 2; values in (7.5, 8) saturate to 7.5) or e3m2 elements
+(largest 28, exponent 4: e = floor(log2 amax) - 4; values in (28, 32)
+saturate to 28).  Codes are returned one per uint8 (``formats.pack_fp6`` gives
+the packed layout, four codes in three bytes).
+
 Inputs are rows x K float32 arrays with K contiguous; a column-major B is
 passed as its N x K transpose, so "row" always means the outer index.
 """
@@ -43,6 +49,9 @@ MX_BLOCK = 32
 E4M3_EMAX = 8          # floor(log2(448))
 E5M2_EMAX = 15         # floor(log2(57344))
 E2M1_EMAX = 2          # floor(log2(6))
+E2M3_EMAX = 2          # floor(log2(7.5))
+E3M2_EMAX = 4          # floor(log2(28))
+MX_ONLY = ("e2m1", "e2m3", "e3m2")     # element formats defined with MX scales only
 
 
 def _scale_from_amax(amax: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
@@ -98,9 +107,9 @@ def quantize_mx(x: np.ndarray, fmt: str = "e4m3"):
 
 def quantize(x: np.ndarray, mode: str, fmt: str = "e4m3"):
     """Dispatch on mode name: "tensor" | "rowwise" | "mx32"; fmt "e4m3" | "e5m2",
-    or "e2m1" with "mx32" only."""
-    if fmt == "e2m1" and mode != "mx32":
-        raise ValueError("e2m1 elements are defined with MX block scales only")
+    or "e2m1" / "e2m3" / "e3m2" with "mx32" only."""
+    if fmt in MX_ONLY and mode != "mx32":
+        raise ValueError(f"{fmt} elements are defined with MX block scales only")
     if mode == "tensor":
         return quantize_tensor(x, fmt)
     if mode == "rowwise":
