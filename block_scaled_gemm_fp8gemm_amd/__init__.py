@@ -38,7 +38,10 @@ _HEADER = os.path.join(os.path.dirname(_PKG), "include", "fp8gemm.h")
 
 SCALE_MODES = {"tensor": 0, "rowwise": 1, "mx32": 2}
 OUT_DTYPES = {"f16": 0, "bf16": 1}
-FORMATS = {"e4m3": 0, "e5m2": 1, "e2m1": 4}   # e2m1: FP4, two codes per byte, MX only
+# e2m3 / e3m2: FP6, four codes in three bytes; e2m1: FP4, two codes per byte (MX only)
+FORMATS = {"e4m3": 0, "e5m2": 1, "e2m3": 2, "e3m2": 3, "e2m1": 4}
+# bits of one code
+CODE_BITS = {"e4m3": 8, "e5m2": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}
 ACTIVATIONS = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
 
 # FP8GEMM_NOALLOC_SCRATCH_BYTES: the static scratch of fp8gemm_run_noalloc
@@ -294,15 +297,16 @@ def quantize(x, mode: str = "tensor", out=None, scales=None, workspace=None,
     """fp32 [R, K] CUDA tensor -> (codes uint8 [R, K], scales).
 
     scales: float32 [1] (tensor), float32 [R] (rowwise) or uint8 [R, K/32] (mx32);
-    fmt: element format of the codes, "e4m3", "e5m2" or "e2m1" (FP4 with mx32:
-    codes packed two per byte, uint8 [R, K/2]).
+    fmt: element format of the codes, "e4m3", "e5m2", or with mx32 "e2m1" (FP4,
+    codes packed two per byte, uint8 [R, K/2]) or "e2m3" / "e3m2" (FP6, four codes
+    in three bytes, uint8 [R, 3K/4]).
     """
     torch = _torch()
     _require_cuda(x, "x", torch.float32, 2)
     m = SCALE_MODES[mode]
     R, K = x.shape
     if out is None:
-        kb = K // 2 if fmt == "e2m1" else K
+        kb = K * CODE_BITS[fmt] // 8                  # bytes of a row of codes
         ldq = (kb + 15) // 16 * 16
         out = torch.empty((R, ldq), dtype=torch.uint8, device=x.device)[:, :kb]
     if scales is None:
@@ -329,7 +333,9 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
     qb is [N, K] (K contiguous, b_layout "nk") or [K, N] (N contiguous, "kn"; its
     MX codes sb then [K/32, N]); fmt_a / fmt_b: element formats of the codes
     ("e4m3" or "e5m2"; or "e2m1" for both, FP4 packed two per byte so that qa is
-    [M, K/2] and qb [N, K/2], mode "mx32"); bias: float32 [N] CUDA tensor or None;
+    [M, K/2] and qb [N, K/2], mode "mx32"; or "e2m3" / "e3m2" for both, FP6 with
+    four codes in three bytes, [M, 3K/4] and [N, 3K/4], mode "mx32", K % 128 == 0);
+    bias: float32 [N] CUDA tensor or None;
     activation: "none", "relu", "gelu" or "silu".
     """
     torch = _torch()
@@ -340,9 +346,8 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
         Kb, N = qb.shape
     else:
         N, Kb = qb.shape
-    fp4 = "e2m1" in (fmt_a, fmt_b)
-    if fp4:                                   # packed codes: K counts elements
-        K, Kb = 2 * K, 2 * Kb
+    # packed codes: K counts elements
+    K, Kb = K * 8 // CODE_BITS[fmt_a], Kb * 8 // CODE_BITS[fmt_b]
     if K != Kb:
         raise ValueError("qa and qb must share K")
     tdt = torch.float16 if out_dtype == "f16" else torch.bfloat16
@@ -379,9 +384,7 @@ def gemm_mxout(qa, sa, qb, sb, mode: str = "tensor", out=None, out_scales=None,
     _require_cuda(qb, "qb", torch.uint8, 2)
     M, K = qa.shape
     N, Kb = qb.shape
-    fp4 = "e2m1" in (fmt_a, fmt_b)
-    if fp4:
-        K, Kb = 2 * K, 2 * Kb
+    K, Kb = K * 8 // CODE_BITS[fmt_a], Kb * 8 // CODE_BITS[fmt_b]
     if K != Kb:
         raise ValueError("qa and qb must share K")
     if out is None:

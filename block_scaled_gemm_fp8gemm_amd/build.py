@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8gemm.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "grouped.hip", "transpose.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "grouped.hip", "transpose.hip", "gemm_fp6.hip"]
 # gemm.hip is compiled once more per pair of operand formats other than e4m3 x e4m3,
 # grouped.hip once more for MXFP4 experts
 FORMAT_UNITS = [("gemm.hip", ("FP8GEMM_FMT_A=1", "FP8GEMM_FMT_B=1"), ".e5m2_e5m2"),

@@ -50,8 +50,12 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 bool valid_mode(int mode) { return mode == kTensor || mode == kRowwise || mode == kMx32; }
 bool valid_out(int out) { return out == FP8GEMM_OUT_F16 || out == FP8GEMM_OUT_BF16; }
 bool valid_format(int f) {
-  return f == FP8GEMM_FORMAT_E4M3 || f == FP8GEMM_FORMAT_E5M2 || f == FP8GEMM_FORMAT_E2M1;
+  return f == FP8GEMM_FORMAT_E4M3 || f == FP8GEMM_FORMAT_E5M2 || f == FP8GEMM_FORMAT_E2M3 ||
+         f == FP8GEMM_FORMAT_E3M2 || f == FP8GEMM_FORMAT_E2M1;
 }
+bool is_fp6(int f) { return f == FP8GEMM_FORMAT_E2M3 || f == FP8GEMM_FORMAT_E3M2; }
+// bits of one code of format f (packed formats share bytes)
+int code_bits(int f) { return f == FP8GEMM_FORMAT_E2M1 ? 4 : is_fp6(f) ? 6 : 8; }
 bool valid_act(int a) {
   return a == FP8GEMM_ACT_NONE || a == FP8GEMM_ACT_RELU || a == FP8GEMM_ACT_GELU ||
          a == FP8GEMM_ACT_SILU;
@@ -61,18 +65,19 @@ fp8gemm_status from_hip(hipError_t e) {
   return e == hipSuccess ? FP8GEMM_SUCCESS : FP8GEMM_ERROR_LAUNCH;
 }
 
-// Checks shared by the dense and grouped GEMM (M is the number of A rows; per_byte
-// is the number of codes per operand byte: 1, or 2 for FP4).
+// Checks shared by the dense and grouped GEMM (M is the number of A rows; bits is
+// the size of one operand code: 8, 6 for FP6 or 4 for FP4, so a row of K codes
+// takes K * bits / 8 bytes and K must keep rows of whole 16-byte chunks).
 fp8gemm_status check_gemm_common(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                                  const uint8_t* B, int64_t ldb, int mode, const void* scale_a,
                                  const void* scale_b, const void* C, int64_t ldc, int out,
-                                 int per_byte = 1) {
+                                 int bits = 8) {
   if (!A || !B || !C || !scale_a || !scale_b) return FP8GEMM_ERROR_INVALID_VALUE;
-  if (lda * per_byte < K || ldb * per_byte < K || ldc < N) return FP8GEMM_ERROR_INVALID_VALUE;
+  if (lda * 8 < K * bits || ldb * 8 < K * bits || ldc < N) return FP8GEMM_ERROR_INVALID_VALUE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim || lda > kMaxDim || ldb > kMaxDim ||
       ldc > kMaxDim)
     return FP8GEMM_ERROR_NOT_SUPPORTED;
-  if (K % (16 * per_byte) != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if ((K * bits) % 128 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (mode == kMx32 && K % 32 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
   // the grid is one workgroup per 128 x 128 tile at most: keep it below 2^31
   if (((M + 127) / 128) * ((N + 127) / 128) > kMaxDim) return FP8GEMM_ERROR_NOT_SUPPORTED;
@@ -105,11 +110,11 @@ fp8gemm_status fp8gemm_quantize_ex(const float* x, int64_t rows, int64_t k, int6
                                    void* workspace, size_t workspace_bytes, void* stream) {
   if (!valid_mode(mode) || !valid_format(format) || rows < 0 || k <= 0)
     return FP8GEMM_ERROR_INVALID_VALUE;
-  const bool fp4 = format == FP8GEMM_FORMAT_E2M1;
-  if (fp4 && mode != kMx32) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  const int bits = code_bits(format);
+  if (bits < 8 && mode != kMx32) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (rows == 0) return FP8GEMM_SUCCESS;
   if (!x || !q || !scales) return FP8GEMM_ERROR_INVALID_VALUE;
-  if (ldx < k || ldq * (fp4 ? 2 : 1) < k) return FP8GEMM_ERROR_INVALID_VALUE;
+  if (ldx < k || ldq * 8 < k * bits) return FP8GEMM_ERROR_INVALID_VALUE;
   if (k % 16 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (mode == kMx32 && k % 32 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
   // 32-bit unit indexing inside the kernels: at most 2^32 - 1 elements per call
@@ -164,9 +169,14 @@ fp8gemm_status run_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int6
   if (!valid_mode(mode) || !(valid_out(out_dtype) || qout) || !valid_format(a_format) ||
       !valid_format(b_format) || !valid_act(activation) || M < 0 || N < 0 || K <= 0)
     return FP8GEMM_ERROR_INVALID_VALUE;
-  // FP4 pairs with FP4 only, and only with MX block scales
+  // FP4 pairs with FP4 only, FP6 with FP6 (e2m3 / e3m2 in any pairing), both
+  // with MX block scales only; FP6 needs K % 128 == 0
   const bool fp4 = a_format == FP8GEMM_FORMAT_E2M1 || b_format == FP8GEMM_FORMAT_E2M1;
+  const bool fp6 = is_fp6(a_format) || is_fp6(b_format);
   if (fp4 && (a_format != b_format || mode != kMx32)) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if (fp6 && (!is_fp6(a_format) || !is_fp6(b_format) || mode != kMx32))
+    return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if (fp6 && K % 128 != 0) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (M == 0 || N == 0) return FP8GEMM_SUCCESS;
   if (qout) {
     if (!cs || ldcs < N / 32) return FP8GEMM_ERROR_INVALID_VALUE;
@@ -175,9 +185,13 @@ fp8gemm_status run_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int6
     if (ldc % 16 != 0) return FP8GEMM_ERROR_MISALIGNED;      // byte rows of codes
   }
   fp8gemm_status st = check_gemm_common(M, N, K, A, lda, B, ldb, mode, scale_a, scale_b, C, ldc,
-                                        out_dtype, fp4 ? 2 : 1);
+                                        out_dtype, fp4 ? 4 : fp6 ? 6 : 8);
   if (st != FP8GEMM_SUCCESS) return st;
   if (bias && !aligned(bias, 4)) return FP8GEMM_ERROR_MISALIGNED;
+  // FP6 tiles: 128 rows of A (and of B) addressed with 32-bit buffer offsets
+  if (fp6 && (127 * lda + K / 4 * 3 >= ((int64_t)1 << 31) ||
+              127 * ldb + K / 4 * 3 >= ((int64_t)1 << 31)))
+    return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (dry_run) return FP8GEMM_SUCCESS;              // every check but the workspace's passed
   // FP4 shapes split along K at most as often as FP8 ones of the same element
   // count, so the query (K in elements) covers them too
@@ -203,6 +217,11 @@ fp8gemm_status run_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int6
   p.cs = cs;
   p.ldcs = ldcs;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fp6) {
+    p.K = (int)K;                        // the FP6 kernel walks K in elements
+    p.workspace = nullptr;
+    return from_hip(fp8gemm::launch_gemm_fp6(p, a_format, b_format, out_dtype, s));
+  }
   if (fp4) return from_hip(fp8gemm::launch_gemm_e2m1_e2m1(p, mode, out_dtype, s));
   if (a_format == FP8GEMM_FORMAT_E5M2 && b_format == FP8GEMM_FORMAT_E5M2)
     return from_hip(fp8gemm::launch_gemm_e5m2_e5m2(p, mode, out_dtype, s));
@@ -338,8 +357,8 @@ fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A,
   if (!valid_mode(mode) || !valid_out(out_dtype) || !valid_format(a_format) ||
       !valid_format(b_format) || !valid_act(activation) || M < 0 || N < 0 || K <= 0)
     return FP8GEMM_ERROR_INVALID_VALUE;
-  if (a_format == FP8GEMM_FORMAT_E2M1 || b_format == FP8GEMM_FORMAT_E2M1)
-    return FP8GEMM_ERROR_NOT_SUPPORTED;          // no transposing copy of packed FP4
+  if (code_bits(a_format) < 8 || code_bits(b_format) < 8)
+    return FP8GEMM_ERROR_NOT_SUPPORTED;          // no transposing copy of packed FP4 / FP6
   if (M == 0 || N == 0) return FP8GEMM_SUCCESS;
   if (!B || !scale_b) return FP8GEMM_ERROR_INVALID_VALUE;
   if (ldb < N) return FP8GEMM_ERROR_INVALID_VALUE;
@@ -418,7 +437,7 @@ fp8gemm_status fp8gemm_grouped_run_ex(int32_t num_groups, int64_t total_m, int64
   if (total_m == 0 || N == 0) return FP8GEMM_SUCCESS;
   if (!offsets) return FP8GEMM_ERROR_INVALID_VALUE;
   fp8gemm_status st = check_gemm_common(total_m, N, K, A, lda, B, ldb, mode, scale_a, scale_b, C,
-                                        ldc, out_dtype, fp4 ? 2 : 1);
+                                        ldc, out_dtype, fp4 ? 4 : 8);
   if (st != FP8GEMM_SUCCESS) return st;
   if (stride_b < N * ldb) return FP8GEMM_ERROR_INVALID_VALUE;
   if (stride_b % 16 != 0) return FP8GEMM_ERROR_MISALIGNED;
@@ -453,6 +472,11 @@ int fp8gemm_run_path(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, 
     return FP8GEMM_PATH_NONE;
   const bool fp4 = a_format == FP8GEMM_FORMAT_E2M1 || b_format == FP8GEMM_FORMAT_E2M1;
   if (fp4 && (a_format != b_format || mode != kMx32)) return FP8GEMM_PATH_NONE;
+  const bool fp6 = is_fp6(a_format) || is_fp6(b_format);
+  if (fp6) {                                   // one FP6 kernel: 128 x 128 tiles
+    if (!is_fp6(a_format) || !is_fp6(b_format) || mode != kMx32) return FP8GEMM_PATH_NONE;
+    return M > 0 && N > 0 ? FP8GEMM_PATH_TILE128 : FP8GEMM_PATH_NONE;
+  }
   return fp8gemm::choose_path(M, N, fp4 ? K / 2 : K, lda, ldb, mode, fp4, fused != 0);
 }
 

@@ -14,6 +14,9 @@
 //   * e2m1 (FP4, the MXFP4 element; OCP MX v1.0) has magnitudes 0, 0.5, 1, 1.5, 2,
 //     3, 4, 6 and no infinity or NaN; it is encoded here in software (round to a
 //     multiple of the binade's spacing with v_rndne, saturating at 6).
+//   * e2m3 and e3m2 (FP6, the MXFP6 elements; OCP MX v1.0) have largest
+//     magnitudes 7.5 and 28 and no infinity or NaN; they are encoded in software
+//     like e2m1.
 //   * E8M0 code c encodes 2^(c-127).
 #pragma once
 
@@ -71,6 +74,44 @@ __device__ __forceinline__ uint32_t encode4_e2m1(float a, float b, float c, floa
   return encode_e2m1(a) | (encode_e2m1(b) << 4) | (encode_e2m1(c) << 8) | (encode_e2m1(d) << 12);
 }
 
+// One fp32 value -> FP6 code (bits 0-5): e2m3 (bias 1, 3 mantissa bits, largest
+// 7.5) or e3m2 (bias 3, 2 mantissa bits, largest 28), round to nearest even,
+// saturating; the sign goes to bit 5, so -0 gives 0x20.  The magnitude is
+// rounded to a multiple of its binade's spacing 2^(E - mantissa bits), E =
+// floor(log2 |v|) from the binary32 exponent, no smaller than the smallest
+// normal exponent 1 - bias (the subnormal spacing continues below it): a
+// multiplication by the power of two 1 / spacing, rintf, and the inverse
+// multiplication, all exact.  The code of the rounded magnitude r: r / spacing
+// below the smallest normal; else the exponent field (exponent + bias) and the
+// top mantissa bits of r.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode_fp6(float v) {
+  constexpr int kBias = FMT == kE2M3 ? 1 : 3;
+  constexpr int kMb = FMT == kE2M3 ? 3 : 2;
+  constexpr float kMax = FMT == kE2M3 ? 7.5f : 28.0f;
+  constexpr float kMinNormal = FMT == kE2M3 ? 1.0f : 0.25f;
+  constexpr float kSubScale = FMT == kE2M3 ? 8.0f : 16.0f;    // 1 / subnormal spacing
+  const uint32_t sign = (__float_as_uint(v) >> 26) & 0x20u;
+  const float a = fabsf(v);
+  int e = (int)(__float_as_uint(a) >> 23) - 127;
+  e = e < 1 - kBias ? 1 - kBias : e;                     // in [1 - bias, 128]
+  const float up = __uint_as_float((uint32_t)(127 + kMb - e) << 23);   // 1 / spacing
+  const float dn = __uint_as_float((uint32_t)(127 - kMb + e) << 23);   // spacing
+  const float r = fminf(rintf(a * up) * dn, kMax);
+  const uint32_t b = __float_as_uint(r);
+  const uint32_t mag = r < kMinNormal
+                           ? (uint32_t)(r * kSubScale)
+                           : ((((b >> 23) - 127u + kBias) << kMb) | ((b >> (23 - kMb)) & ((1u << kMb) - 1)));
+  return sign | mag;
+}
+
+// Four fp32 values -> four FP6 codes in the low 24 bits, the first in bits 0-5.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4_fp6(float a, float b, float c, float d) {
+  return encode_fp6<FMT>(a) | (encode_fp6<FMT>(b) << 6) | (encode_fp6<FMT>(c) << 12) |
+         (encode_fp6<FMT>(d) << 18);
+}
+
 template <int FMT>
 __device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
   return FMT == kE5M2 ? encode4_e5m2(a, b, c, d) : encode4_e4m3(a, b, c, d);
@@ -83,13 +124,14 @@ constexpr float elem_max() {
 
 // E8M0 code of a 32-element block from its largest magnitude: floor(log2 amax)
 // read from the binary32 exponent field, minus the element format's largest
-// exponent (8 for e4m3, 15 for e5m2, 2 for e2m1), biased by 127 and clamped to [0, 254]; an
+// exponent (8 for e4m3, 15 for e5m2, 2 for e2m1 and e2m3, 4 for e3m2), biased by
+// 127 and clamped to [0, 254]; an
 // all-zero block gets 127.
 template <int FMT = kE4M3>
 __device__ __forceinline__ uint32_t mx_code_from_amax(float amax) {
   if (amax == 0.0f) return 127u;
   int ef = (int)(__float_as_uint(amax) >> 23);  // amax >= 0: no sign bit
-  int code = ef - (FMT == kE5M2 ? 15 : FMT == kE2M1 ? 2 : 8);
+  int code = ef - (FMT == kE5M2 ? 15 : (FMT == kE2M1 || FMT == kE2M3) ? 2 : FMT == kE3M2 ? 4 : 8);
   return (uint32_t)(code < 0 ? 0 : code);
 }
 

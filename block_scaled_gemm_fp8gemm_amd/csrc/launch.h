@@ -29,8 +29,9 @@ enum ScaleMode : int { kTensor = 0, kRowwise = 1, kMx32 = 2 };
 // epilogue quantises the output for the next layer; codes to C, scales to cs).
 enum OutType : int { kF16 = 0, kBF16 = 1, kE4M3Mx = 2 };
 // Element formats of the codes; the values are the operand-format fields of the
-// F8F6F4 MFMA (e2m1 = FP4, two codes per byte, MX scales only).
-enum ElemFormat : int { kE4M3 = 0, kE5M2 = 1, kE2M1 = 4 };
+// F8F6F4 MFMA (e2m3 / e3m2 = FP6, four codes in three bytes; e2m1 = FP4, two
+// codes per byte; the narrow formats take MX scales only).
+enum ElemFormat : int { kE4M3 = 0, kE5M2 = 1, kE2M3 = 2, kE3M2 = 3, kE2M1 = 4 };
 // Activation of the fused epilogue (applied after the scales and the bias).
 enum Activation : int { kActNone = 0, kActRelu = 1, kActGelu = 2, kActSilu = 3 };
 
@@ -69,6 +70,10 @@ hipError_t launch_gemm_e5m2_e4m3(const GemmProblem& p, int mode, int out, hipStr
 // MXFP4 x MXFP4 (mode kMx32 only): K, lda and ldb of the problem count bytes
 // (two e2m1 codes each), the E8M0 codes stay one per 32 elements.
 hipError_t launch_gemm_e2m1_e2m1(const GemmProblem& p, int mode, int out, hipStream_t stream);
+// MXFP6 (e2m3 / e3m2 operands, MX scales): K counts elements (K % 128 == 0),
+// lda and ldb bytes (four codes in three bytes).
+hipError_t launch_gemm_fp6(const GemmProblem& p, int fmt_a, int fmt_b, int out,
+                           hipStream_t stream);
 
 struct GroupedProblem {
   int groups;

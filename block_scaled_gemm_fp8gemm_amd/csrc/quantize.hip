@@ -1,5 +1,5 @@
-// fp32 -> e4m3fn / e5m2 quantisation kernels for gfx950 (scale computation and
-// encoding).
+// fp32 -> e4m3fn / e5m2 / e2m3 / e3m2 / e2m1 quantisation kernels for gfx950
+// (scale computation and encoding).
 //
 // What is computed (the E4M3 operands with per-block scale factors of the
 // JAX/Triton Blackwell FP8 GEMM post, the row-wise FP8 GEMM of "Hopper/Blackwell
@@ -11,7 +11,9 @@
 //                0, 254) (127 if amax = 0), q = RNE_sat(x * 2^(127 - code))
 // and the same with 57344 and 15 in place of 448 and 8 for e5m2 codes (the post's
 // second FP8 format); MX only, 6 and 2 for e2m1 (FP4, two codes per byte, the
-// first in the low nibble: the MXFP4 format of the architecture page's §12.6.1).
+// first in the low nibble: the MXFP4 format of the architecture page's §12.6.1),
+// 7.5 and 2 for e2m3 and 28 and 4 for e3m2 (FP6, the MXFP6 elements of the same
+// table; four codes in three bytes, a little-endian 6-bit stream).
 //
 // All kernels are HBM-streaming.  The unit of work is 1024 consecutive values of
 // a row, taken by one wavefront so that every load and store instruction covers
@@ -224,11 +226,26 @@ __device__ __forceinline__ void mx_unit(const Unit& u, uint8_t* qrow, uint8_t* c
     const int e = 127 - (int)code;
     const float x0 = ldexpf(u.v[j].x, e), x1 = ldexpf(u.v[j].y, e);
     const float x2 = ldexpf(u.v[j].z, e), x3 = ldexpf(u.v[j].w, e);
-    w[j] = FMT == kE2M1 ? encode4_e2m1(x0, x1, x2, x3) : encode4<FMT>(x0, x1, x2, x3);
+    if constexpr (FMT == kE2M1) w[j] = encode4_e2m1(x0, x1, x2, x3);
+    else if constexpr (FMT == kE2M3 || FMT == kE3M2) w[j] = encode4_fp6<FMT>(x0, x1, x2, x3);
+    else w[j] = encode4<FMT>(x0, x1, x2, x3);
     const int c = col0 + 256 * j + 4 * lane;
     if ((lane & 7) == 0 && c < k) crow[c >> 5] = (uint8_t)code;
   }
-  if constexpr (FMT == kE2M1) {
+  if constexpr (FMT == kE2M3 || FMT == kE3M2) {
+    // Four codes in three bytes: the lane's float4 is 24 bits; lanes 4i .. 4i + 3
+    // (16 columns) make the 96-bit run at byte 192 j + 12 i, stored as three
+    // dwords by lanes 4i, 4i + 1, 4i + 2 (dword t = bits 32t .. 32t + 31: the
+    // lane's own 24 bits shifted down by 8t and the next lane's shifted up).
+    const int t = lane & 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t nxt = (uint32_t)__shfl_down((int)w[j], 1, 64);
+      const uint32_t word = (w[j] >> (8 * t)) | (t < 3 ? nxt << (24 - 8 * t) : 0u);
+      const int cg = col0 + 256 * j + 16 * (lane >> 2);   // first column of the run
+      if (t < 3 && cg < k) *reinterpret_cast<uint32_t*>(qrow + cg / 4 * 3 + 4 * t) = word;
+    }
+  } else if constexpr (FMT == kE2M1) {
     // Two codes per byte: lane l holds the 16 bits of bytes 128 j + 2 l and + 1.
     // Lanes 2i and 2i + 1 swap halves so that the even lane stores the word at
     // 128 j + 4 i for j = 0, 2 and the odd lane the one for j = 1, 3: two 4-byte
@@ -348,6 +365,8 @@ hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t k, int64_t l
                               int64_t ldq, uint8_t* codes, int fmt, hipStream_t stream) {
   if (fmt == kE5M2) return quantize_mx_fmt<kE5M2>(x, rows, k, ldx, q, ldq, codes, stream);
   if (fmt == kE2M1) return quantize_mx_fmt<kE2M1>(x, rows, k, ldx, q, ldq, codes, stream);
+  if (fmt == kE2M3) return quantize_mx_fmt<kE2M3>(x, rows, k, ldx, q, ldq, codes, stream);
+  if (fmt == kE3M2) return quantize_mx_fmt<kE3M2>(x, rows, k, ldx, q, ldq, codes, stream);
   return quantize_mx_fmt<kE4M3>(x, rows, k, ldx, q, ldq, codes, stream);
 }
 

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FP8GEMM_VERSION 160 /* 1.6.0: e5m2, fused epilogues, row-major B, MXFP4 (dense, grouped), MX output, path query */
+#define FP8GEMM_VERSION 170 /* 1.7.0: e5m2, fused epilogues, row-major B, MXFP4 (dense, grouped), MXFP6 (dense), MX output, path query, no-allocation GEMM */
 
 typedef enum fp8gemm_status {
   FP8GEMM_SUCCESS = 0,
@@ -71,6 +71,13 @@ typedef enum fp8gemm_out_dtype {
 typedef enum fp8gemm_format {
   FP8GEMM_FORMAT_E4M3 = 0, /* OCP e4m3fn: bias 7, no infinity, max 448 (the default)      */
   FP8GEMM_FORMAT_E5M2 = 1, /* OCP e5m2: bias 15, infinities and NaNs, max 57344           */
+  /* FP6, the MXFP6 elements (§12.6.1 of the same page lists FP6 with micro-scaling):
+     OCP MX e2m3 (bias 1, 3 mantissa bits, max 7.5) and e3m2 (bias 3, 2 mantissa bits,
+     max 28), no infinity or NaN, sign = bit 5 of a code.  Four codes in three bytes:
+     a row is a little-endian 6-bit stream, element i in bits 6i .. 6i+5 (element
+     (r,i) starts at bit 6i of the row's bytes).  MX32 scales only. */
+  FP8GEMM_FORMAT_E2M3 = 2,
+  FP8GEMM_FORMAT_E3M2 = 3,
   /* FP4, the MXFP4 element ("Hopper/Blackwell architecture features" §12.6.1 lists FP4
      next to FP8 with micro-scaling): OCP MX e2m1, bias 1, magnitudes 0, .5, 1, 1.5, 2,
      3, 4, 6, no infinity or NaN.  Two codes per byte, element 2i in bits 0-3 and
@@ -123,7 +130,10 @@ fp8gemm_status fp8gemm_quantize(const float* x, int64_t rows, int64_t k, int64_t
    - 15).  With FP8GEMM_FORMAT_E2M1 (MX32 only, else NOT_SUPPORTED) they use 6
    and 2 (e = floor(log2 amax) - 2, q = RNE_sat(x * 2^-e) onto e2m1, saturating
    at +-6) and q holds two codes per byte: element (r,i) in byte q[r*ldq + i/2],
-   low nibble for even i; ldq >= k/2 bytes, a multiple of 16.
+   low nibble for even i; ldq >= k/2 bytes, a multiple of 16.  With
+   FP8GEMM_FORMAT_E2M3 / E3M2 (MX32 only) they use 7.5 and 2 / 28 and 4 (e =
+   floor(log2 amax) - 2 or - 4, saturating at +-7.5 / +-28) and q holds a row of
+   k 6-bit codes in 3k/4 bytes (the stream above); ldq >= 3k/4, a multiple of 16.
    fp8gemm_quantize is this call with FP8GEMM_FORMAT_E4M3.  Errors as above; an
    unknown format is INVALID_VALUE. */
 fp8gemm_status fp8gemm_quantize_ex(const float* x, int64_t rows, int64_t k, int64_t ldx, int mode,
@@ -168,7 +178,10 @@ fp8gemm_status fp8gemm_run(int64_t M, int64_t N, int64_t K, const uint8_t* A, in
 /*          NOT_SUPPORTED; A holds two codes per byte, element (m,k) in byte    */
 /*          A[m*lda + k/2], likewise B[n*ldb + k/2]; lda, ldb >= K/2 bytes;     */
 /*          K % 32 == 0; scales uint8 [M][K/32] and [N][K/32]; the workspace    */
-/*          of fp8gemm_workspace_size(M, N, K, MX32), K in elements).           */
+/*          of fp8gemm_workspace_size(M, N, K, MX32), K in elements); or E2M3 /  */
+/*          E3M2 for both, in any pairing (MXFP6: MX32 only; A and B rows hold   */
+/*          K codes in 3K/4 bytes; lda, ldb >= 3K/4; K % 128 == 0, else         */
+/*          NOT_SUPPORTED; no workspace).                                       */
 /* bias   : device float[N], 4-byte aligned, or NULL (no bias).               */
 /* activation: fp8gemm_activation, applied in fp32 after the scales and bias.   */
 /* The scale modes, layouts, workspace and errors are those of fp8gemm_run      */
@@ -224,7 +237,8 @@ fp8gemm_status fp8gemm_run_mxout(int64_t M, int64_t N, int64_t K, const uint8_t*
 /*   scale_b: TENSOR float[1]; ROWWISE float[N]; MX32 uint8 [K/32][N] (row-major, */
 /*            N codes per row).                                                 */
 /* Everything else (A, C, formats, scale_a, bias, activation, accuracy, errors) */
-/* as fp8gemm_run_ex; E2M1 operands are NOT_SUPPORTED here.  The call first    */
+/* as fp8gemm_run_ex; E2M1 and FP6 operands are NOT_SUPPORTED here.  The call  */
+/* first                                                                      */
 /* copies B and its MX codes into the                                           */
 /* K-contiguous layout in the workspace (one HBM pass over B), then runs the    */
 /* GEMM: workspace is fp8gemm_workspace_size_kn() bytes, 16-byte aligned,       */

@@ -26,19 +26,21 @@ def fp8_chunk(lo, hi, top):
     return np.concatenate([x, np.full(pad, top, np.float32)])
 
 
-def fp4_chunk(lo, hi):
+def mx_chunk(lo, hi, top=6.0):
+    """Blocks of 32 whose first element is `top` (the format's largest value, so
+    the shared exponent is 0) and whose other 31 are the patterns lo .. hi - 1."""
     x = patterns(lo, hi)
     blocks = -(-len(x) // 31)
     blocks += (-blocks) % (COLS // 32)
     buf = np.zeros((blocks, 32), np.float32)
-    buf[:, 0] = 6.0
+    buf[:, 0] = top
     flat = buf[:, 1:].reshape(-1)
     flat[:len(x)] = x
     buf[:, 1:] = flat.reshape(blocks, 31)
     return buf.reshape(-1)
 
 
-def oracle_fp4(lo, hi):
-    return O.encode_e2m1(fp4_chunk(lo, hi))
+def oracle_mx(lo, hi, top, fmt):
+    return O.encode(mx_chunk(lo, hi, top), fmt)
 
 

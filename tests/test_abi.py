@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert F.fp8gemm_version() == 160
+    assert F.fp8gemm_version() == 170
     for code, name in [(0, "FP8GEMM_SUCCESS"), (1, "FP8GEMM_ERROR_INVALID_VALUE"),
                        (2, "FP8GEMM_ERROR_MISALIGNED"), (3, "FP8GEMM_ERROR_NOT_SUPPORTED"),
                        (4, "FP8GEMM_ERROR_WORKSPACE"), (5, "FP8GEMM_ERROR_LAUNCH"),
@@ -124,6 +124,26 @@ def test_noalloc_validation(lib):
     assert _noalloc(lib, M=M, N=N, K=K, lda=K, ldb=K, ldc=N) == WORKSPACE
 
 
+def test_fp6_validation(lib):
+    """FP6 (e2m3 / e3m2) takes MX scales, pairs with FP6 only, needs K % 128 == 0
+    and is not offered for row-major B or grouped; rows hold 3K/4 bytes."""
+    e2m3, e3m2, e4m3 = F.FORMATS["e2m3"], F.FORMATS["e3m2"], F.FORMATS["e4m3"]
+    assert _noalloc(lib, K=1024, lda=768, ldb=768, mode=2, afmt=e2m3, bfmt=e3m2, M=0) == SUCCESS
+    assert _noalloc(lib, K=1024, lda=768, ldb=768, mode=0, afmt=e2m3, bfmt=e2m3) == NOT_SUPPORTED
+    assert _noalloc(lib, K=1024, lda=768, ldb=768, mode=2, afmt=e2m3, bfmt=e4m3) == NOT_SUPPORTED
+    assert _noalloc(lib, K=1088, lda=816, ldb=816, mode=2, afmt=e2m3, bfmt=e2m3) == NOT_SUPPORTED
+    assert _noalloc(lib, K=1024, lda=752, ldb=768, mode=2, afmt=e2m3, bfmt=e2m3) == INVALID
+    assert F.fp8gemm_run_path(512, 512, 1024, 768, 768, e2m3, e3m2, 2, 0) == "tile128"
+    assert F.fp8gemm_run_path(512, 512, 1024, 768, 768, e2m3, e4m3, 2, 0) == "none"
+    assert lib.fp8gemm_run_kn(64, 64, 1024, P, 768, e2m3, P2, 64, e2m3, 2, P3, P3, 0, 0, P,
+                              64, 1, P, 1 << 20, None) == NOT_SUPPORTED
+    assert lib.fp8gemm_grouped_run_ex(2, 64, 64, 1024, P, 768, e2m3, P2, P3, 768, e2m3,
+                                      64 * 768, 2, P3, P3, P, 64, 1, 0, 0, None) == NOT_SUPPORTED
+    # quantiser: MX only; q rows of 3k/4 bytes
+    assert lib.fp8gemm_quantize_ex(P, 4, 64, 64, 1, e3m2, P2, 48, P3, 0, 0, None) == NOT_SUPPORTED
+    assert lib.fp8gemm_quantize_ex(P, 4, 64, 64, 2, e3m2, P2, 32, P3, 0, 0, None) == INVALID
+
+
 def _quant(lib, x=P, rows=64, k=256, ldx=256, mode=1, q=P2, ldq=256, scales=P3, ws=0, wsb=0):
     return lib.fp8gemm_quantize(x, rows, k, ldx, mode, q, ldq, scales, ws, wsb, None)
 
@@ -189,7 +209,8 @@ def test_extended_entry_points_validation(lib):
     """Formats and the fused epilogue are validated before any HIP call."""
     assert _run_ex(lib, M=0) == SUCCESS
     assert _run_ex(lib, M=0, fa=1, fb=1, bias=P, act=3) == SUCCESS
-    assert _run_ex(lib, fa=2) == INVALID
+    assert _run_ex(lib, fa=5) == INVALID
+    assert _run_ex(lib, fa=2) == NOT_SUPPORTED      # e2m3 codes with e4m3 B: no such pairing
     assert _run_ex(lib, fb=-1) == INVALID
     assert _run_ex(lib, act=4) == INVALID
     assert _run_ex(lib, act=-1) == INVALID
@@ -199,7 +220,8 @@ def test_extended_entry_points_validation(lib):
     q = lambda **kw: lib.fp8gemm_quantize_ex(kw.get("x", P), 64, kw.get("k", 256), 256,
                                              kw.get("mode", 1), kw.get("fmt", 0), P2, 256, P3, 0,
                                              0, None)
-    assert q(fmt=2) == INVALID
+    assert q(fmt=5) == INVALID
+    assert q(fmt=2) == NOT_SUPPORTED                # e2m3 codes need block (MX) scaling
     assert q(fmt=-1) == INVALID
     assert q(fmt=1, x=0) == INVALID
     assert q(fmt=1, k=48, mode=2) == NOT_SUPPORTED
@@ -219,7 +241,8 @@ def test_fp4_validation(lib):
     assert run(lda=112) == INVALID                     # lda < K/2 bytes
     assert run(K=240, lda=128, ldb=128) == NOT_SUPPORTED   # K % 32
     assert run(lda=136) == MISALIGNED
-    assert _run_ex(lib, fa=3) == INVALID               # FP6 formats are not offered
+    assert _run_ex(lib, fa=3) == NOT_SUPPORTED         # e3m2 x e4m3: no such pairing
+    assert _run_ex(lib, fa=7) == INVALID               # no format 7
     q = lambda **kw: lib.fp8gemm_quantize_ex(P, 64, kw.get("k", 256), 256, kw.get("mode", 2), 4,
                                              P2, kw.get("ldq", 128), P3, 0, 0, None)
     assert q(mode=1) == NOT_SUPPORTED

@@ -7,8 +7,9 @@ through the GPU at scale 1 and is compared bit for bit with the oracle:
 
 * e4m3 / e5m2, per-tensor scaling: every chunk also holds the format's largest
   value (448, 57344), so amax / max = 1 and the codes are encode(x) itself;
-* e2m1 (MXFP4): every 32-element block starts with 6.0, so the block exponent is
-  floor(log2 6) - 2 = 0 (E8M0 code 127) and the codes are encode(x).
+* e2m1 (MXFP4), e2m3 / e3m2 (MXFP6): every 32-element block starts with the
+  format's largest value (6, 7.5, 28), so the block exponent is floor(log2 max)
+  - emax = 0 (E8M0 code 127) and the codes are encode(x).
 
 Negative inputs differ only in the sign bit, which both sides copy.  The oracle
 side runs in a pool of worker processes, a chunk ahead of the GPU.
@@ -22,8 +23,8 @@ import torch
 
 import block_scaled_gemm_fp8gemm_amd as F
 import oracle as O
-from exhaustive_inputs import (COLS, fp4_chunk as _fp4_chunk, fp8_chunk as _fp8_chunk,
-                               oracle_fp4 as _oracle_fp4, oracle_fp8 as _oracle_fp8)
+from exhaustive_inputs import (COLS, fp8_chunk as _fp8_chunk, mx_chunk as _mx_chunk,
+                               oracle_fp8 as _oracle_fp8, oracle_mx as _oracle_mx)
 
 from gpu_support import DEV, announce
 
@@ -67,23 +68,26 @@ def test_every_fp32_input_fp8(fmt, top):
             del xd, q
 
 
-def test_every_fp32_input_e2m1():
-    end = int(np.float32(6.0).view(np.uint32)) + 1
+@pytest.mark.parametrize("fmt,top", [("e2m1", 6.0), ("e2m3", 7.5), ("e3m2", 28.0)])
+def test_every_fp32_input_mx_narrow(fmt, top):
+    end = int(np.float32(top).view(np.uint32)) + 1
     step = CHUNK // 32 * 31
     starts = list(range(0, end, step))
+    unpack = O.unpack_fp4 if fmt == "e2m1" else O.unpack_fp6
     with _pool() as pool:
-        futs = {s: pool.submit(_oracle_fp4, s, min(s + step, end)) for s in starts[:WORKERS]}
+        futs = {s: pool.submit(_oracle_mx, s, min(s + step, end), top, fmt)
+                for s in starts[:WORKERS]}
         for n, s in enumerate(starts):
             e = min(s + step, end)
             if n + WORKERS < len(starts):
                 s2 = starts[n + WORKERS]
-                futs[s2] = pool.submit(_oracle_fp4, s2, min(s2 + step, end))
-            x = _fp4_chunk(s, e)
-            announce("exhaustive e2m1", f"patterns {s:#010x}..{e - 1:#010x}")
+                futs[s2] = pool.submit(_oracle_mx, s2, min(s2 + step, end), top, fmt)
+            x = _mx_chunk(s, e, top)
+            announce("exhaustive", fmt, f"patterns {s:#010x}..{e - 1:#010x}")
             xd = torch.from_numpy(x).to(DEV).view(-1, COLS)
-            q, codes = F.quantize(xd, "mx32", fmt="e2m1")
-            assert np.all(codes.cpu().numpy() == 127), "block exponent of a block with maximum 6"
-            got = O.unpack_fp4(q.cpu().numpy()).reshape(-1)
+            q, codes = F.quantize(xd, "mx32", fmt=fmt)
+            assert np.all(codes.cpu().numpy() == 127), "block exponent of a block with the maximum"
+            got = unpack(q.cpu().numpy()).reshape(-1)
             want = futs.pop(s).result()
             assert np.array_equal(got, want), _first_mismatch(got, want, x)
             del xd, q
