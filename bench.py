@@ -33,6 +33,7 @@ from workloads import WORKLOADS, dense_inputs, grouped_inputs  # noqa: E402
 
 PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 MFMA peak (no sparsity)
 PEAK_FP4_TFLOPS = 10100.0         # MI355X dense FP4 (MXFP4) MFMA peak
+PEAK_FP6_TFLOPS = 10100.0         # MI355X dense FP6 (MXFP6) MFMA peak
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
 DEFAULT_WORKLOAD = "mx8192"
 # the pages' own figures, measured on other hardware: context, not targets
@@ -149,7 +150,7 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, command: st
 
 def gemm_bytes(w, code_bytes: float = 1.0) -> int:
     """Algorithmic bytes of one GEMM launch: A + B codes (code_bytes per element:
-    1, or 0.5 for FP4), scales, C."""
+    1, 0.75 for FP6 or 0.5 for FP4), scales, C."""
     mb = int((w.M * w.K + (w.groups or 1) * w.N * w.K) * code_bytes)
     if w.mode == "mx32":
         mb += (w.M + (w.groups or 1) * w.N) * (w.K // 32)
@@ -223,8 +224,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--formats", default="e4m3,e4m3", metavar="A,B",
-                    help="element formats of the A and B codes (e4m3 or e5m2, or e2m1,e2m1 for "
-                         "MXFP4 with the mx32 workload; dense only)")
+                    help="element formats of the A and B codes (e4m3 or e5m2; e2m1,e2m1 for "
+                         "MXFP4; e2m3 or e3m2 in any pairing for MXFP6, dense mx32 workloads "
+                         "with K % 128 == 0)")
     ap.add_argument("--epilogue", default="none", choices=["none", "bias", "bias+relu",
                                                            "bias+gelu", "bias+silu", "mxout"],
                     help="fused epilogue of the GEMM (dense only); mxout: the output quantised "
@@ -273,9 +275,14 @@ def main():
         w = dataclasses.replace(w, mode="mx32")
     if fp4 and (fmt_a != fmt_b or w.mode != "mx32"):
         raise SystemExit("e2m1 (MXFP4) runs as e2m1,e2m1 on an mx32 workload")
-    kq = w.K // 2 if fp4 else w.K            # code bytes per row
-    peak = PEAK_FP4_TFLOPS if fp4 else PEAK_FP8_TFLOPS
-    code_bytes = 0.5 if fp4 else 1.0
+    fp6_fmts = ("e2m3", "e3m2")
+    fp6 = fmt_a in fp6_fmts or fmt_b in fp6_fmts
+    if fp6 and (fmt_a not in fp6_fmts or fmt_b not in fp6_fmts or w.mode != "mx32" or w.groups
+                or kn or w.K % 128):
+        raise SystemExit("MXFP6 runs as e2m3 / e3m2 pairs on a dense mx32 workload, K % 128 == 0")
+    kq = w.K // 2 if fp4 else w.K * 3 // 4 if fp6 else w.K     # code bytes per row
+    peak = PEAK_FP4_TFLOPS if fp4 else PEAK_FP6_TFLOPS if fp6 else PEAK_FP8_TFLOPS
+    code_bytes = 0.5 if fp4 else 0.75 if fp6 else 1.0
     dev = torch.device("cuda:0")
     F.load_library()
     log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} mode={w.mode} out={w.out} groups={w.groups}")
