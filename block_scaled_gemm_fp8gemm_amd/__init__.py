@@ -18,6 +18,7 @@ e4m3fn bytes held in ``torch.uint8`` tensors.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import re
 
@@ -28,7 +29,7 @@ __all__ = [
     "fp8gemm_quantize_ex", "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex",
     "fp8gemm_workspace_size_kn", "fp8gemm_run_kn",
     "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run",
-    "fp8gemm_run_path", "PATHS", "fp8gemm_run_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "fp8gemm_run_path", "fp8gemm_run_kn_path", "PATHS", "fp8gemm_run_noalloc", "NOALLOC_SCRATCH_BYTES",
     "fp8gemm_status_string", "fp8gemm_version", "quantize", "gemm", "grouped_gemm",
     "exported_symbols",
 ]
@@ -93,6 +94,7 @@ _SIGNATURES = {
     "fp8gemm_grouped_run_ex": (_int, [_i32, _i64, _i64, _i64, _p, _i64, _int, _p, _p, _i64, _int,
                                       _i64, _int, _p, _p, _p, _i64, _int, _p, _sz, _p]),
     "fp8gemm_run_path": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int, _int, _int]),
+    "fp8gemm_run_kn_path": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int, _int]),
     "fp8gemm_run_noalloc": (_int, [_i64, _i64, _i64, _p, _i64, _int, _p, _i64, _int, _int, _p, _p,
                                    _p, _int, _p, _i64, _int, _p]),
     "fp8gemm_status_string": (ctypes.c_char_p, [_int]),
@@ -233,6 +235,13 @@ def fp8gemm_run_path(M: int, N: int, K: int, lda: int, ldb: int, a_format: int, 
                                                  fused)]
 
 
+def fp8gemm_run_kn_path(M: int, N: int, K: int, lda: int, ldb: int, a_format: int,
+                        b_format: int, mode: int) -> str:
+    """Kernel path of fp8gemm_run_kn's in-kernel form for this shape ("none": the
+    call makes B K-contiguous in the workspace first)."""
+    return PATHS[load_library().fp8gemm_run_kn_path(M, N, K, lda, ldb, a_format, b_format, mode)]
+
+
 def fp8gemm_status_string(status: int) -> str:
     return load_library().fp8gemm_status_string(status).decode()
 
@@ -325,6 +334,15 @@ def quantize(x, mode: str = "tensor", out=None, scales=None, workspace=None,
     return out, scales
 
 
+@functools.lru_cache(maxsize=256)
+def _gemm_workspace_need(M, N, K, lda, ldb, a_format, b_format, mode, kn):
+    """Workspace bytes of a dense GEMM call: row-major B read in the kernels needs
+    only the GEMM's own workspace, the transposing form also B's copy."""
+    if kn and fp8gemm_run_kn_path(M, N, K, lda, ldb, a_format, b_format, mode) == "none":
+        return fp8gemm_workspace_size_kn(M, N, K, mode)
+    return fp8gemm_workspace_size(M, N, K, mode)
+
+
 def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None,
          workspace=None, fmt_a: str = "e4m3", fmt_b: str = "e4m3", bias=None,
          activation: str = "none", b_layout: str = "nk"):
@@ -356,7 +374,8 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
         out = torch.empty((M, ldc), dtype=tdt, device=qa.device)[:, :N]
     m = SCALE_MODES[mode]
     kn = b_layout == "kn"
-    need = (fp8gemm_workspace_size_kn if kn else fp8gemm_workspace_size)(M, N, K, m)
+    need = _gemm_workspace_need(M, N, K, qa.stride(0), qb.stride(0), FORMATS[fmt_a],
+                                FORMATS[fmt_b], m, kn)
     if need and workspace is None:
         workspace = gemm_workspace(qa.device, need)
     if bias is not None:

@@ -19,12 +19,17 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8gemm.so")
 
 SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "grouped.hip", "transpose.hip", "gemm_fp6.hip"]
-# gemm.hip is compiled once more per pair of operand formats other than e4m3 x e4m3,
-# grouped.hip once more for MXFP4 experts
+# gemm.hip is compiled once more per pair of operand formats other than e4m3 x e4m3
+# and once per FP8 pair for row-major B (FP8GEMM_KN), grouped.hip once more for
+# MXFP4 experts
 FORMAT_UNITS = [("gemm.hip", ("FP8GEMM_FMT_A=1", "FP8GEMM_FMT_B=1"), ".e5m2_e5m2"),
                 ("gemm.hip", ("FP8GEMM_FMT_A=0", "FP8GEMM_FMT_B=1"), ".e4m3_e5m2"),
                 ("gemm.hip", ("FP8GEMM_FMT_A=1", "FP8GEMM_FMT_B=0"), ".e5m2_e4m3"),
                 ("gemm.hip", ("FP8GEMM_FMT_A=4", "FP8GEMM_FMT_B=4"), ".e2m1_e2m1"),
+                ("gemm.hip", ("FP8GEMM_KN=1",), ".kn"),
+                ("gemm.hip", ("FP8GEMM_KN=1", "FP8GEMM_FMT_A=1", "FP8GEMM_FMT_B=1"), ".kn_e5m2_e5m2"),
+                ("gemm.hip", ("FP8GEMM_KN=1", "FP8GEMM_FMT_A=0", "FP8GEMM_FMT_B=1"), ".kn_e4m3_e5m2"),
+                ("gemm.hip", ("FP8GEMM_KN=1", "FP8GEMM_FMT_A=1", "FP8GEMM_FMT_B=0"), ".kn_e5m2_e4m3"),
                 ("grouped.hip", ("FP8GEMM_FMT_A=4", "FP8GEMM_FMT_B=4"), ".e2m1_e2m1")]
 
 ARCH = "gfx950"

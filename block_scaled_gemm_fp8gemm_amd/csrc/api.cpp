@@ -342,6 +342,15 @@ int64_t kn_b_bytes(int64_t N, int64_t K) { return round256(N * K); }
 int64_t kn_code_bytes(int64_t N, int64_t K, int mode) {
   return mode == kMx32 ? round256(N * (K / 32)) : 0;
 }
+// Whether fp8gemm_run_kn reads the row-major B inside the GEMM kernels
+// (transposing LDS reads) instead of making it K-contiguous in the workspace
+// first: FP8 codes, MX code rows of whole 16-byte chunks, and a shape the
+// in-kernel form takes (K % 128 == 0, MX K % 512 == 0, 32-bit spans).
+bool kn_in_kernel(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int a_format,
+                  int b_format, int mode) {
+  return code_bits(a_format) == 8 && code_bits(b_format) == 8 && (mode != kMx32 || N % 16 == 0) &&
+         fp8gemm::choose_path_kn(M, N, K, lda, ldb, mode) != fp8gemm::kPathNone;
+}
 }  // namespace
 
 size_t fp8gemm_workspace_size_kn(int64_t M, int64_t N, int64_t K, int mode) {
@@ -367,6 +376,39 @@ fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A,
   // one transpose workgroup per 64 x 64 tile: keep the grid below 2^31
   if (((K + 63) / 64) * ((N + 63) / 64) > kMaxDim) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (!aligned(B, 16) || ldb % 16 != 0) return FP8GEMM_ERROR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kn_in_kernel(M, N, K, lda, ldb, a_format, b_format, mode)) {
+    // B's own checks passed above; K stands in for the pitch of a K-contiguous B
+    fp8gemm_status st = check_gemm_common(M, N, K, A, lda, B, K, mode, scale_a, scale_b, C, ldc,
+                                          out_dtype);
+    if (st != FP8GEMM_SUCCESS) return st;
+    if (bias && !aligned(bias, 4)) return FP8GEMM_ERROR_MISALIGNED;
+    const size_t need = fp8gemm_workspace_size(M, N, K, mode);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return FP8GEMM_ERROR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return FP8GEMM_ERROR_MISALIGNED;
+    fp8gemm::GemmProblem p;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.A = A;
+    p.lda = lda;
+    p.B = B;
+    p.ldb = ldb;
+    p.scale_a = scale_a;
+    p.scale_b = scale_b;
+    p.C = C;
+    p.ldc = ldc;
+    p.workspace = need > 0 ? workspace : nullptr;
+    p.bias = bias;
+    p.act = activation;
+    if (a_format == FP8GEMM_FORMAT_E5M2 && b_format == FP8GEMM_FORMAT_E5M2)
+      return from_hip(fp8gemm::launch_gemm_kn_e5m2_e5m2(p, mode, out_dtype, s));
+    if (a_format == FP8GEMM_FORMAT_E5M2)
+      return from_hip(fp8gemm::launch_gemm_kn_e5m2_e4m3(p, mode, out_dtype, s));
+    if (b_format == FP8GEMM_FORMAT_E5M2)
+      return from_hip(fp8gemm::launch_gemm_kn_e4m3_e5m2(p, mode, out_dtype, s));
+    return from_hip(fp8gemm::launch_gemm_kn(p, mode, out_dtype, s));
+  }
   const size_t need = fp8gemm_workspace_size_kn(M, N, K, mode);
   if (!workspace || workspace_bytes < need) return FP8GEMM_ERROR_WORKSPACE;
   if (!aligned(workspace, 16)) return FP8GEMM_ERROR_MISALIGNED;
@@ -382,7 +424,6 @@ fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A,
                                         mode == kMx32 ? codes_t : scale_b, C, ldc, out_dtype);
   if (st != FP8GEMM_SUCCESS) return st;
   if (bias && !aligned(bias, 4)) return FP8GEMM_ERROR_MISALIGNED;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = fp8gemm::launch_transpose_u8(B, ldb, bt, ldbt, K, N, s);
   if (e != hipSuccess) return FP8GEMM_ERROR_LAUNCH;
   const void* sb = scale_b;
@@ -478,6 +519,15 @@ int fp8gemm_run_path(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, 
     return M > 0 && N > 0 ? FP8GEMM_PATH_TILE128 : FP8GEMM_PATH_NONE;
   }
   return fp8gemm::choose_path(M, N, fp4 ? K / 2 : K, lda, ldb, mode, fp4, fused != 0);
+}
+
+int fp8gemm_run_kn_path(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                        int a_format, int b_format, int mode) {
+  if (!valid_mode(mode) || !valid_format(a_format) || !valid_format(b_format) || M <= 0 ||
+      N <= 0 || K <= 0 || lda < 0 || ldb < 0)
+    return FP8GEMM_PATH_NONE;
+  if (!kn_in_kernel(M, N, K, lda, ldb, a_format, b_format, mode)) return FP8GEMM_PATH_NONE;
+  return fp8gemm::choose_path_kn(M, N, K, lda, ldb, mode);
 }
 
 const char* fp8gemm_status_string(int status) {

@@ -15,8 +15,16 @@
 #include "plan.h"
 #include "tile_order.h"
 
+// FP8GEMM_KN=1 builds the kernels for row-major B ([K][N]): every tile runs the
+// interior mainloop in its transposing-read form (no persistent kernel).
+#ifndef FP8GEMM_KN
+#define FP8GEMM_KN 0
+#endif
+
 namespace fp8gemm {
 namespace {
+
+constexpr bool kKn = FP8GEMM_KN;
 
 template <class Cfg, int MODE, typename OutT, bool KALIGNED, bool FUSED>
 __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void gemm_kernel(GemmProblem p,
@@ -31,18 +39,19 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void gemm_kernel(G
   op.A = p.A + (int64_t)m0 * p.lda;
   op.lda = p.lda;
   op.a_rows = p.M - m0;
-  op.B = p.B + (int64_t)n0 * p.ldb;
+  op.B = kKn ? p.B + n0 : p.B + (int64_t)n0 * p.ldb;
   op.ldb = p.ldb;
   op.b_rows = p.N - n0;
   op.K = p.K;
   op.sld = p.K / kBlkBytes;
+  op.sldb = p.N;                         // row-major B: its codes are [K/32][N]
   const float* fsa = static_cast<const float*>(p.scale_a);
   const float* fsb = static_cast<const float*>(p.scale_b);
   op.sa = op.sb = nullptr;
   op.ra = op.rb = nullptr;
   if (MODE == kMx32) {
     op.sa = static_cast<const uint8_t*>(p.scale_a) + (int64_t)m0 * op.sld;
-    op.sb = static_cast<const uint8_t*>(p.scale_b) + (int64_t)n0 * op.sld;
+    op.sb = static_cast<const uint8_t*>(p.scale_b) + (kKn ? (int64_t)n0 : (int64_t)n0 * op.sld);
   }
   if (MODE == kRowwise) {
     op.ra = fsa + m0;
@@ -50,8 +59,12 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void gemm_kernel(G
   }
 
   const float ts = (MODE == kTensor) ? fsa[0] * fsb[0] : 1.0f;
-  gemm_tile<Cfg, MODE, OutT, KALIGNED, FUSED>(op, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M,
-                                              n0, p.N, ts, p.bias, p.act, p.cs, p.ldcs);
+  if constexpr (kKn)
+    gemm_tile_kn<Cfg, MODE, OutT, FUSED>(op, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0,
+                                         p.N, ts, p.bias, p.act, p.cs, p.ldcs);
+  else
+    gemm_tile<Cfg, MODE, OutT, KALIGNED, FUSED>(op, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M,
+                                                n0, p.N, ts, p.bias, p.act, p.cs, p.ldcs);
 }
 
 // Operands of the tiles of one persistent workgroup: tile i of the list is the
@@ -126,7 +139,10 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   const int tiles_m = (p.M + Cfg::BM - 1) / Cfg::BM;
   const int tiles_n = (p.N + Cfg::BN - 1) / Cfg::BN;
   const int grid = tiles_m * tiles_n;
-  if (p.K % 128 == 0)
+  if constexpr (kKn)   // K % 128 == 0 on this path
+    hipLaunchKernelGGL((gemm_kernel<Cfg, MODE, OutT, true, FUSED>), dim3(grid),
+                       dim3(Cfg::kThreads), 0, stream, p, tiles_m, tiles_n);
+  else if (p.K % 128 == 0)
     hipLaunchKernelGGL((gemm_kernel<Cfg, MODE, OutT, true, FUSED>), dim3(grid),
                        dim3(Cfg::kThreads), 0, stream, p, tiles_m, tiles_n);
   else
@@ -189,7 +205,11 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void splitk_kernel
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kFlagOff + 16];
   int& s_last = *reinterpret_cast<int*>(lds + kFlagOff);
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
-  const int tile = blockIdx.x / splits, ks = blockIdx.x % splits;
+  // XCD-aware: the workgroups of one XCD hold a contiguous run of (tile, slice)
+  // pairs, so the tile rows that share B columns (and, for row-major B, the
+  // neighbouring column tiles that share its 128-byte lines) meet in one L2
+  const int lin = xcd_linear(blockIdx.x, gridDim.x);
+  const int tile = lin / splits, ks = lin % splits;
   const int tm = tile % tiles_m, tn = tile / tiles_m;
   const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
   const int kslice = p.K / splits, k0 = ks * kslice;
@@ -198,18 +218,20 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void splitk_kernel
   op.A = p.A + (int64_t)m0 * p.lda + k0;
   op.lda = p.lda;
   op.a_rows = p.M - m0;
-  op.B = p.B + (int64_t)n0 * p.ldb + k0;
+  op.B = kKn ? p.B + (int64_t)k0 * p.ldb + n0 : p.B + (int64_t)n0 * p.ldb + k0;
   op.ldb = p.ldb;
   op.b_rows = p.N - n0;
   op.K = kslice;
   op.sld = p.K / kBlkBytes;
+  op.sldb = p.N;
   const float* fsa = static_cast<const float*>(p.scale_a);
   const float* fsb = static_cast<const float*>(p.scale_b);
   op.sa = op.sb = nullptr;
   op.ra = op.rb = nullptr;
   if (MODE == kMx32) {
     op.sa = static_cast<const uint8_t*>(p.scale_a) + (int64_t)m0 * op.sld + k0 / kBlkBytes;
-    op.sb = static_cast<const uint8_t*>(p.scale_b) + (int64_t)n0 * op.sld + k0 / kBlkBytes;
+    op.sb = static_cast<const uint8_t*>(p.scale_b) +
+            (kKn ? (int64_t)(k0 / 32) * p.N + n0 : (int64_t)n0 * op.sld + k0 / kBlkBytes);
   }
   if (MODE == kRowwise) {
     op.ra = fsa + m0;
@@ -217,7 +239,8 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void splitk_kernel
   }
 
   v16f acc[FM][FN];
-  if (interior_tile<Cfg, MODE>(op)) mainloop_interior<Cfg, MODE, kSplitRing>(op, lds, acc);
+  if constexpr (kKn) mainloop_interior<Cfg, MODE, kSplitRing, true>(op, lds, acc);
+  else if (interior_tile<Cfg, MODE>(op)) mainloop_interior<Cfg, MODE, kSplitRing>(op, lds, acc);
   else mainloop<Cfg, MODE, !kF4>(op, lds, acc);
 
   // partial tile: float4 r of thread x at [tile][slice][r][x] (coalesced per r)
@@ -317,13 +340,17 @@ hipError_t launch_split(const GemmProblem& p, const SplitPlan& plan, hipStream_t
 template <int MODE, typename OutT, bool FUSED>
 hipError_t launch_plan(const GemmProblem& p, hipStream_t stream) {
   constexpr bool kNoStream = FUSED || std::is_same<OutT, uint8_t>::value;
-  switch (choose_path(p.M, p.N, p.K, p.lda, p.ldb, MODE, kF4, kNoStream)) {
+  const GemmPath path = kKn ? choose_path_kn(p.M, p.N, p.K, p.lda, p.ldb, MODE)
+                            : choose_path(p.M, p.N, p.K, p.lda, p.ldb, MODE, kF4, kNoStream);
+  // row-major B outside the in-kernel form: the caller transposes B first
+  if (kKn && path == kPathNone && p.M > 0 && p.N > 0) return hipErrorInvalidValue;
+  switch (path) {
     case kPathSplitK:
       return launch_split<MODE, OutT, FUSED>(p, plan_split(p.M, p.N, p.K, MODE, kBlkBytes),
                                              stream);
     case kPathPersistent:
       // (the fused epilogue stages through the ring, so it never runs in a stream)
-      if constexpr (!kNoStream && !kF4) return launch_persistent<Big, MODE, OutT>(p, stream);
+      if constexpr (!kNoStream && !kF4 && !kKn) return launch_persistent<Big, MODE, OutT>(p, stream);
       return hipErrorInvalidValue;
     case kPathTile256:
       return launch_cfg<Big, MODE, OutT, FUSED>(p, stream);
@@ -348,7 +375,15 @@ hipError_t launch_any(const GemmProblem& p, hipStream_t stream) {
 // This file is compiled once per pair of operand formats (FP8GEMM_FMT_A/B); the
 // e4m3 x e4m3 build also defines the workspace query (the plan does not depend
 // on the formats).
-#if FP8GEMM_FMT_A == 0 && FP8GEMM_FMT_B == 0
+#if FP8GEMM_KN && FP8GEMM_FMT_A == 0 && FP8GEMM_FMT_B == 0
+#define FP8GEMM_LAUNCH_NAME launch_gemm_kn
+#elif FP8GEMM_KN && FP8GEMM_FMT_A == 1 && FP8GEMM_FMT_B == 1
+#define FP8GEMM_LAUNCH_NAME launch_gemm_kn_e5m2_e5m2
+#elif FP8GEMM_KN && FP8GEMM_FMT_A == 0 && FP8GEMM_FMT_B == 1
+#define FP8GEMM_LAUNCH_NAME launch_gemm_kn_e4m3_e5m2
+#elif FP8GEMM_KN && FP8GEMM_FMT_A == 1 && FP8GEMM_FMT_B == 0
+#define FP8GEMM_LAUNCH_NAME launch_gemm_kn_e5m2_e4m3
+#elif FP8GEMM_FMT_A == 0 && FP8GEMM_FMT_B == 0
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int mode) {
   return (size_t)gemm_workspace_need(M, N, K, mode);
 }

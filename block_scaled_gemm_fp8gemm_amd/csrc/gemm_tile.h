@@ -91,6 +91,7 @@ constexpr bool kF4 = kFmtA == 4;
 static_assert((kFmtA == 4) == (kFmtB == 4), "FP4 operands pair with FP4 operands only");
 constexpr int kBlkBytes = kF4 ? 16 : 32;     // bytes of one 32-element MX block
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -165,7 +166,22 @@ struct TileOperands {
   const float* rb;      // row-wise: fp32 scale of B's first tile row
   int K;                // K extent of this tile's product (a split's slice under split-K)
   int sld;              // MX: bytes between the codes of consecutive rows
+  // Row-major B ([K][N], N contiguous; the kn kernels): B is this tile's first
+  // column of K-row 0, ldb the bytes between K-rows, b_rows the valid columns;
+  // sb the tile's first column of the codes [K/32][N], sldb the bytes between
+  // their rows.
+  int sldb = 0;
 };
+
+// Row-major B in LDS: a 128-K tile is 128 K-rows of BN bytes; 16-byte chunk c of
+// K-row k sits at chunk c ^ kn_swz(k).  A transposing read takes 8 K-rows at one
+// 32-column fragment (two chunks, both halves): with this XOR the 32 lanes of a
+// half-wave hit 32 distinct bank pairs for BN = 64, 128 and 256 (rows of 64 B
+// share a 256-byte bank line four ways, rows of 128 B two ways).
+template <int BN>
+__device__ __forceinline__ int kn_swz(int k) {
+  return 2 * ((k / (256 / BN)) & (BN / 32 - 1));
+}
 
 __device__ __forceinline__ void lds_dma16(const uint8_t* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
@@ -606,6 +622,40 @@ __device__ __forceinline__ void buffer_dma16(__amdgpu_buffer_rsrc_t rs, uint8_t*
                                            voff, soff, 0, 0);
 }
 
+// The same copy issued from inline assembly, so that the compiler does not track
+// it.  The compiler makes every LDS read that it cannot tell apart from a pending
+// direct-to-LDS copy wait for all of them (s_waitcnt vmcnt(0)); it does so for
+// the transposing reads (ds_read_b64_tr_b8), which would serialise the copy ring.
+// Loops that issue their copies here keep their own explicit waits, which count
+// these copies like any other (they are ordinary vector-memory operations); the
+// instruction writes no VGPR.  rs: the four descriptor words (buffer_rsrc_words).
+typedef unsigned v4u_rs __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4u_rs buffer_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return v4u_rs{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+// lds_base: LDS byte address of the destination area (wave-uniform), lds_off its
+// offset; soff the scalar byte offset into the buffer.  The sums are formed at
+// the copy from values passed through an empty volatile asm (scalar_fresh), so
+// the compiler cannot hoist one SGPR per copy out of an unrolled loop.
+__device__ __forceinline__ uint32_t lds_address(const uint8_t* lds) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)lds);
+}
+template <class T>
+__device__ __forceinline__ T scalar_fresh(T v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+__device__ __forceinline__ void buffer_dma16_untracked(v4u_rs rs, uint32_t lds_base,
+                                                       uint32_t lds_off, int voff, int soff) {
+  const uint32_t m0 = scalar_fresh(lds_base) + lds_off;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+
 // An opaque copy of v: the compiler cannot fold constants through it, so an LDS
 // base stays in one register and the constant parts stay in the offset field.
 __device__ __forceinline__ int opaque(int v) {
@@ -644,7 +694,21 @@ __device__ __forceinline__ bool interior_tile(const TileOperands& op) {
 // NS: ring depth in 128-K tiles (2 for the 256 x 256 tile; 4 or 8 for the split-K
 // tiles, whose K slices are short and whose copies come from HBM: a slice streams
 // at about the ring's bytes per HBM latency).
-template <class Cfg, int MODE, int NS = 2>
+//
+// KN: B is row-major [K][N] (the layout of the pages' Triton listings, e.g.
+// "Hopper/Blackwell architecture features" §12.7.1, where the B pointer advances
+// by BLOCK_K * stride_bk).  Its K tile is copied as 128 K-rows of BN bytes (whole
+// lines, chunks XOR-swizzled by kn_swz) and each B fragment is assembled from
+// four transposing LDS reads (ds_read_b64_tr_b8; probed on gfx950: in each
+// 16-lane group, byte j of lane i comes from byte i % 8 of the 8 bytes addressed
+// by lane 2 j + i / 8).  Lanes 2 m and 2 m + 1 of a group address K-row kb + m at
+// the group's 16 columns, so lane i receives column i at K-rows kb .. kb + 7: the
+// eight K bytes of operand bytes 8 q .. 8 q + 7 (kb = 32 (q / 2) + 16 h + 8 (q % 2)
+// within the 64-K step).  MX codes of B come as [K/32][N] and sit in LDS as [16
+// blocks][BN] per group.  Tiles cut by M or N run here too: A rows past the edge
+// read as zero (the copy range ends at the last valid row) and B columns past N
+// hold whatever the copy finds there; neither is ever stored.
+template <class Cfg, int MODE, int NS = 2, bool KN = false>
 __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_t* lds,
                                                   v16f (&acc)[Cfg::kFragM][Cfg::kFragN]) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
@@ -664,8 +728,13 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   static_assert(kTile % (1024 * Cfg::kWaves) == 0, "equal copy share per wave");
   static_assert(kLoads % 2 == 0, "copy blocks of both swizzle phases per wave");
   static_assert((NS - 1) * kLoads + kCodeLoads < 64, "vmcnt range");
+  // KN: K-rows per B copy instruction, 16-byte chunks per K-row
+  constexpr int kKRows = 1024 / Cfg::BN, kChunks = Cfg::BN / 16;
+  static_assert(!KN || !kF4, "row-major B: one code per byte");
   // ring slots reachable from one base register through the 16-bit offset field
-  constexpr int kMaxFrag = ((FM > FN ? FM : FN) - 1) * 32 * kRowB;
+  // (KN: the B reads add up to 104 K-rows of BN bytes)
+  constexpr int kMaxFrag0 = ((FM > FN ? FM : FN) - 1) * 32 * kRowB;
+  constexpr int kMaxFrag = KN && 104 * Cfg::BN > kMaxFrag0 ? 104 * Cfg::BN : kMaxFrag0;
   constexpr int kPerBase = (NS >= 4 && 3 * kTile + kMaxFrag < 65536) ? 4
                            : (NS >= 2 && kTile + kMaxFrag < 65536) ? 2 : 1;
   constexpr int kBases = NS / kPerBase;
@@ -690,36 +759,84 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   // (lane >> 3) of the block, LDS chunk lane & 7, global chunk (lane & 7) ^
   // ((row >> 1) & 7); the swizzle of even and odd blocks differs
   const int g0 = wave * kLoads;                   // first block of this wave
-  const __amdgpu_buffer_rsrc_t rsA = buffer_rsrc(op.A, (uint32_t)((Cfg::BM - 1) * op.lda + op.K));
-  const __amdgpu_buffer_rsrc_t rsB = buffer_rsrc(op.B, (uint32_t)((Cfg::BN - 1) * op.ldb + op.K));
+  // valid rows (KN: B columns) of the tile: copies of rows past A's edge read zero
+  const int a_tile = op.a_rows < Cfg::BM ? op.a_rows : Cfg::BM;
+  const int b_tile = op.b_rows < Cfg::BN ? op.b_rows : Cfg::BN;
+  const uint32_t nrA = (uint32_t)((a_tile - 1) * op.lda + op.K);
+  const uint32_t nrB = KN ? (uint32_t)((op.K - 1) * op.ldb + b_tile)
+                          : (uint32_t)((Cfg::BN - 1) * op.ldb + op.K);
+  const __amdgpu_buffer_rsrc_t rsA = buffer_rsrc(op.A, nrA);
+  const __amdgpu_buffer_rsrc_t rsB = buffer_rsrc(op.B, nrB);
+  // KN: the copies go out untracked (see buffer_dma16_untracked)
+  const v4u_rs wsA = buffer_rsrc_words(op.A, nrA), wsB = buffer_rsrc_words(op.B, nrB);
   const int lda = (int)op.lda, ldb = (int)op.ldb;
   const int crow = lane >> 3;
   const int sw0 = 16 * ((lane & 7) ^ ((crow >> 1) & 7));
   const int sw1 = 16 * ((lane & 7) ^ (((crow + 8) >> 1) & 7));
-  // per-instruction lane offsets (loop invariant)
+  // per-instruction lane offsets (loop invariant); KN: B instruction g covers
+  // K-rows kKRows (g - nA) .. + kKRows - 1 (that first K-row goes in the scalar
+  // offset), lane -> K-row lane / kChunks, LDS chunk lane % kChunks, global chunk
+  // (lane % kChunks) ^ kn_swz(K-row); kn_swz has period 8 in the K-row and every
+  // wave's first B instruction starts at a multiple of 8 K-rows, so at most two
+  // distinct lane offsets remain
+  static_assert(!KN || ((kLoads * kKRows) % 8 == 0 && (nA * kKRows) % 8 == 0),
+                "B copy blocks start on the swizzle period");
   int voff[kLoads];
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) {
     const bool isA = g0 + j < nA;
-    voff[j] = crow * (isA ? lda : ldb) + ((j & 1) ? sw1 : sw0);
+    if (KN && !isA) {
+      const int kr = lane / kChunks;
+      voff[j] = kr * ldb + 16 * ((lane % kChunks) ^ kn_swz<Cfg::BN>(((j * kKRows) & 7) + kr));
+    } else {
+      voff[j] = crow * (isA ? lda : ldb) + ((j & 1) ? sw1 : sw0);
+    }
   }
   uint8_t* const cdst = lds + g0 * 1024;
-  const __amdgpu_buffer_rsrc_t rcA =
-      buffer_rsrc(op.sa, (uint32_t)((Cfg::BM - 1) * op.sld + nblk));
-  const __amdgpu_buffer_rsrc_t rcB =
-      buffer_rsrc(op.sb, (uint32_t)((Cfg::BN - 1) * op.sld + nblk));
+  const uint32_t lds_base = KN ? lds_address(lds) : 0u;
+  const uint32_t ncA = (uint32_t)((a_tile - 1) * op.sld + nblk);
+  const uint32_t ncB = KN ? (uint32_t)((nblk - 1) * op.sldb + b_tile)
+                          : (uint32_t)((Cfg::BN - 1) * op.sld + nblk);
+  const __amdgpu_buffer_rsrc_t rcA = buffer_rsrc(op.sa, ncA);
+  const __amdgpu_buffer_rsrc_t rcB = buffer_rsrc(op.sb, ncB);
+  const v4u_rs wcA = buffer_rsrc_words(op.sa, ncA), wcB = buffer_rsrc_words(op.sb, ncB);
   const int cvoff = lane * op.sld;
+  // KN: each wave copies rows of one operand (kUniformOperand), so its
+  // descriptor, lane offsets and the linear scalar offset of a copy, soff =
+  // g * t_row + kt * t_kt + t_base for copy block g of K tile kt, are set once.
+  static_assert(!KN || kUniformOperand, "KN: a wave copies rows of one operand");
+  const bool wave_a = g0 < nA;
+  const v4u_rs ws_t = wave_a ? wsA : wsB;
+  const int t_row = wave_a ? 8 * lda : kKRows * ldb;
+  const int t_kt = wave_a ? kRowB : kRowB * ldb;
+  const int t_base = wave_a ? 0 : -nA * kKRows * ldb;
+  // KN, MX: B code copy jj covers code rows (32-K blocks) kKRows li .. + kKRows - 1
+  // of the group, lane -> block lane / kChunks, 16 columns at 16 (lane % kChunks);
+  // A code copies as in the K-contiguous layout.  soff = grp * c_grp + c_base.
+  int cv[kCodeLoads], c_grp[kCodeLoads], c_base[kCodeLoads];
+  v4u_rs wc[kCodeLoads];
+#pragma unroll
+  for (int jj = 0; jj < kCodeLoads; ++jj) {
+    int ci = wave * kCodeLoads + jj;
+    ci = ci < kCodeInsts ? ci : kCodeInsts - 1;
+    const bool code_a = ci < Cfg::BM / 64;
+    const int li = code_a ? ci : ci - Cfg::BM / 64;
+    cv[jj] = code_a ? lane * op.sld
+                    : (li * kKRows + lane / kChunks) * op.sldb + 16 * (lane % kChunks);
+    c_grp[jj] = code_a ? 16 : 16 * op.sldb;
+    c_base[jj] = code_a ? li * 64 * op.sld : 0;
+    wc[jj] = code_a ? wcA : wcB;
+  }
 
   auto tile_copy = [&](int j, int slot, int kt) {       // j-th copy of K tile kt
     const int g = g0 + j;                               // wave-uniform
-    if (kUniformOperand) {
-      const bool isA = g0 < nA;
-      buffer_dma16(isA ? rsA : rsB, cdst + slot * kTile + j * 1024, voff[j],
-                   (isA ? g : g - nA) * 8 * (isA ? lda : ldb) + kt * kRowB);
+    const bool isA = kUniformOperand ? g0 < nA : g < nA;
+    if constexpr (KN) {
+      const int soff = g * scalar_fresh(t_row) + kt * scalar_fresh(t_kt) + t_base;
+      buffer_dma16_untracked(ws_t, lds_base, (uint32_t)(g * 1024 + slot * kTile), voff[j], soff);
     } else {
-      const bool isA = g < nA;
-      buffer_dma16(isA ? rsA : rsB, cdst + slot * kTile + j * 1024, voff[j],
-                   (isA ? g : g - nA) * 8 * (isA ? lda : ldb) + kt * kRowB);
+      const int soff = isA ? g * 8 * lda + kt * kRowB : (g - nA) * 8 * ldb + kt * kRowB;
+      buffer_dma16(isA ? rsA : rsB, cdst + slot * kTile + j * 1024, voff[j], soff);
     }
   };
   auto code_copy = [&](int jj, int buf, int grp) {      // jj-th code copy of group grp
@@ -727,8 +844,13 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
     ci = ci < kCodeInsts ? ci : kCodeInsts - 1;
     const bool isA = ci < Cfg::BM / 64;
     const int li = isA ? ci : ci - Cfg::BM / 64;
-    buffer_dma16(isA ? rcA : rcB, lds + kCodeOff + buf * kCodeBuf + ci * 1024, cvoff,
-                 li * 64 * op.sld + 16 * grp);
+    if constexpr (KN) {
+      buffer_dma16_untracked(wc[jj], lds_base, (uint32_t)(kCodeOff + buf * kCodeBuf + ci * 1024),
+                             cv[jj], grp * scalar_fresh(c_grp[jj]) + c_base[jj]);
+    } else {
+      buffer_dma16(isA ? rcA : rcB, lds + kCodeOff + buf * kCodeBuf + ci * 1024, cvoff,
+                   li * 64 * op.sld + 16 * grp);
+    }
   };
 
   // ---- read side: per-lane LDS bases, constant offsets ----
@@ -746,8 +868,25 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
       for (int c = 0; c < 2; ++c) {
         const int ch = 16 * ((kF4 ? 4 * p + 2 * h + c : 4 * p + 2 * c + h) ^ rsw);
         ba[s][p][c] = opaque(s * kPerBase * kTile + ra + ch);
-        bb[s][p][c] = opaque(s * kPerBase * kTile + rb + ch);
+        if (!KN) bb[s][p][c] = opaque(s * kPerBase * kTile + rb + ch);
       }
+  // KN: lane (16-lane group G, position w) addresses K-row kb + w / 2 at columns
+  // 32 j + 16 G + 8 (w % 2) of fragment j: chunk 2 j' + G, j' = this wave's
+  // fragment column / 32, at (2 j' + G) ^ kn_swz(w / 2) (kb % 8 == 0 leaves the
+  // swizzle to the lane); base per fragment, K offsets in the offset field
+  int bk[kBases][KN ? FN : 1];
+  if constexpr (KN) {
+    const int w = lane & 15, G = (lane >> 4) & 1;
+    const int swz = kn_swz<Cfg::BN>(w >> 1);
+#pragma unroll
+    for (int s = 0; s < kBases; ++s)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int c2 = (wn * Cfg::WN + 32 * j) / 16;      // even
+        bk[s][j] = opaque(s * kPerBase * kTile + Cfg::BM * kRowB + (16 * h + (w >> 1)) * Cfg::BN +
+                          16 * ((c2 ^ swz) + G) + 8 * (w & 1));
+      }
+  }
   // MX codes: byte 4 (u % 4) + 2 p + h of the row's 16-byte group u / 4 (FP4:
   // bytes 8 (u % 2) + 4 p + 2 h + c of group u / 2, c = the step's MFMA); the
   // group of the current K tile is in buffer `cur`, the next one in `nxt`
@@ -755,19 +894,55 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   int cbuf = 0;                                        // buffer index of the current group
   if (kMx) {
     cur_a = opaque(kCodeOff + (wm * Cfg::WM + (lane & 31)) * 16 + (kF4 ? 2 * h : h));
-    cur_b = opaque(kCodeOff + (Cfg::BM + wn * Cfg::WN + (lane & 31)) * 16 + (kF4 ? 2 * h : h));
+    cur_b = KN ? opaque(kCodeOff + Cfg::BM * 16 + h * Cfg::BN + wn * Cfg::WN + (lane & 31))
+               : opaque(kCodeOff + (Cfg::BM + wn * Cfg::WN + (lane & 31)) * 16 + (kF4 ? 2 * h : h));
     nxt_a = opaque(cur_a + kCodeBuf);
     nxt_b = opaque(cur_b + kCodeBuf);
   }
 
   auto rd16 = [&](int addr) { return *reinterpret_cast<const v4i*>(lds + addr); };
-  // the d-th 16-byte read of a step's fragments (ring slot s, half p)
-  auto read_frag = [&](auto s_c, auto p_c, int d, v4i (&rd)[2 * (FM + FN)]) {
+  auto rdtr = [&](int addr) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        reinterpret_cast<__attribute__((address_space(3))) v2i*>(
+            (__attribute__((address_space(3))) uint8_t*)(lds + addr)));
+  };
+  // a step's LDS reads: 16-byte reads of A (and of B), KN: four 8-byte
+  // transposing reads per B fragment
+  constexpr int kReadsA = 2 * FM, kReadsB = (KN ? 4 : 2) * FN;
+  struct Reads {
+    v4i rd[kReadsA + (KN ? 0 : kReadsB)];
+    v2i rt[KN ? kReadsB : 1];
+  };
+  // the d-th read of a step's fragments (ring slot s, half p)
+  auto read_frag = [&](auto s_c, auto p_c, int d, Reads& r) {
     constexpr int s = decltype(s_c)::value, p = decltype(p_c)::value;
     constexpr int b = s / kPerBase, o = (s % kPerBase) * kTile;
     const int c = d & 1;
-    if (d < 2 * FM) rd[d] = rd16(ba[b][p][c] + o + (d >> 1) * 32 * kRowB);
-    else rd[d] = rd16(bb[b][p][c] + o + ((d - 2 * FM) >> 1) * 32 * kRowB);
+    if (d < kReadsA) {
+      r.rd[d] = rd16(ba[b][p][c] + o + (d >> 1) * 32 * kRowB);
+    } else if constexpr (KN) {
+      const int e = d - kReadsA, q = e & 3;
+      r.rt[e] = rdtr(bk[b][e >> 2] + o + (64 * p + 32 * (q >> 1) + 8 * (q & 1)) * Cfg::BN);
+    } else {
+      r.rd[d] = rd16(bb[b][p][c] + o + ((d - kReadsA) >> 1) * 32 * kRowB);
+    }
+  };
+  // fragments from a step's reads
+  auto frags = [&](const Reads& r, v8i (&fa)[FM], v8i (&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[i] = __builtin_shufflevector(r.rd[2 * i], r.rd[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (KN) {
+        const v4i lo = __builtin_shufflevector(r.rt[4 * j], r.rt[4 * j + 1], 0, 1, 2, 3);
+        const v4i hi = __builtin_shufflevector(r.rt[4 * j + 2], r.rt[4 * j + 3], 0, 1, 2, 3);
+        fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {
+        fb[j] = __builtin_shufflevector(r.rd[kReadsA + 2 * j], r.rd[kReadsA + 2 * j + 1], 0, 1, 2,
+                                        3, 4, 5, 6, 7);
+      }
+    }
   };
   uint32_t ca[2][kCodes][FM], cb[2][kCodes][FN];      // codes: [register set][MFMA][fragment]
 #pragma unroll
@@ -790,6 +965,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
     } else {
       const int off = 4 * q + 2 * p;
       if (f < FM) a[c][f] = lds[base_a + off + f * 32 * 16];
+      else if (KN) b[c][f - FM] = lds[base_b + off * Cfg::BN + (f - FM) * 32];
       else b[c][f - FM] = lds[base_b + off + (f - FM) * 32 * 16];
     }
   };
@@ -817,15 +993,11 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   FP8GEMM_WAIT_VM_LGKM0((NS - 1) * kLoads);
   __builtin_amdgcn_s_barrier();
   {
-    v4i rd[2 * (FM + FN)];
+    Reads r0;
 #pragma unroll
-    for (int d = 0; d < 2 * (FM + FN); ++d)
-      read_frag(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, d, rd);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) af0[i] = __builtin_shufflevector(rd[2 * i], rd[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      bf0[j] = __builtin_shufflevector(rd[2 * FM + 2 * j], rd[2 * FM + 2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    for (int d = 0; d < kReadsA + kReadsB; ++d)
+      read_frag(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, d, r0);
+    frags(r0, af0, bf0);
     if (kMx) {
 #pragma unroll
       for (int e = 0; e < kCodes * (FM + FN); ++e) read_code(cur_a, cur_b, 0, 0, e, ca[0], cb[0]);
@@ -834,7 +1006,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
 
   // ---- one 64-K step t: K tile u = t / 2, half p; T = t mod (unrolled steps) ----
   constexpr int kMfma = FM * FN;
-  constexpr int kReads = 2 * (FM + FN);
+  constexpr int kReads = kReadsA + kReadsB;
   constexpr int kReadSpan = (kMfma * FP8GEMM_READ_SPAN + 7) / 8 > 0 ? (kMfma * FP8GEMM_READ_SPAN + 7) / 8 : 1;
   constexpr int kCopySpan = (kMfma * FP8GEMM_COPY_SPAN + 7) / 8 > 0 ? (kMfma * FP8GEMM_COPY_SPAN + 7) / 8 : 1;
   auto step = [&](int t, auto T_c, v8i (&fa)[FM], v8i (&fb)[FN], v8i (&na)[FM], v8i (&nb)[FN]) {
@@ -872,7 +1044,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
     __builtin_amdgcn_sched_barrier(0);
     const int kc = (u + NS) < nk ? u + NS : nk - 1;  // past the end: harmless re-fetch
     const int grp = u / kGroupTiles + 1 < ncode ? u / kGroupTiles + 1 : ncode - 1;
-    v4i rd[kReads];
+    Reads rd;
 #pragma unroll
     for (int m = 0; m < kMfma; ++m) {
       const int i = m / FN, j = m % FN;
@@ -911,11 +1083,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int i = 0; i < FM; ++i) na[i] = __builtin_shufflevector(rd[2 * i], rd[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      nb[j] = __builtin_shufflevector(rd[2 * FM + 2 * j], rd[2 * FM + 2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    frags(rd, na, nb);
     if (kMx && kNextGroup) {                      // the next group is current from step t + 1
       cbuf ^= 1;
       const int ta = cur_a, tb = cur_b;
@@ -1723,6 +1891,49 @@ __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cf
   }
 }
 
+// Epilogue of a full interior tile (every row and column valid): straight from
+// the accumulators where the output allows it.
+template <class Cfg, int MODE, typename OutT, bool FUSED>
+__device__ __forceinline__ void epilogue_full_tile(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                                   uint8_t* lds, OutT* C, int64_t ldc, int m0,
+                                                   int m_end, int n0, int N, float tensor_scale,
+                                                   const float* bias, int act, uint8_t* cs,
+                                                   int64_t ldcs) {
+  if constexpr (FUSED && !std::is_same<OutT, uint8_t>::value) {
+    if (act == kActNone || act == kActRelu)
+      epilogue_direct<Cfg, MODE, OutT, true>(acc, lds, C, ldc, m0, n0, tensor_scale, 0, bias,
+                                             act == kActRelu);
+    else
+      epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act,
+                                      cs, ldcs);
+  } else if constexpr (FUSED) {
+    epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act,
+                                    cs, ldcs);
+  } else if constexpr (std::is_same<OutT, uint8_t>::value) {
+    epilogue_direct_q<Cfg, MODE>(acc, lds, C, ldc, m0, n0, tensor_scale, cs, ldcs);
+  } else {
+#if FP8GEMM_DIRECT_EPILOGUE
+    epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, n0, tensor_scale);
+#else
+    epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
+#endif
+  }
+}
+
+// Epilogue of any tile (rows and columns past the edges are not stored).
+template <class Cfg, int MODE, typename OutT, bool FUSED>
+__device__ __forceinline__ void epilogue_any_tile(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                                  uint8_t* lds, OutT* C, int64_t ldc, int m0,
+                                                  int m_end, int n0, int N, float tensor_scale,
+                                                  const float* bias, int act, uint8_t* cs,
+                                                  int64_t ldcs) {
+  if constexpr (FUSED || std::is_same<OutT, uint8_t>::value)
+    epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act,
+                                    cs, ldcs);
+  else
+    epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
+}
+
 // One output tile: the interior mainloop when the tile qualifies, else the
 // general (clamped) one, then the epilogue.  Each branch has its own accumulators
 // and epilogue so no accumulator copies join the two paths.
@@ -1736,35 +1947,37 @@ __device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, 
     if (interior_tile<Cfg, MODE>(op)) {
       v16f acc[Cfg::kFragM][Cfg::kFragN];
       mainloop_interior<Cfg, MODE>(op, lds, acc);
-      if constexpr (FUSED && !std::is_same<OutT, uint8_t>::value) {
-        if (act == kActNone || act == kActRelu)
-          epilogue_direct<Cfg, MODE, OutT, true>(acc, lds, C, ldc, m0, n0, tensor_scale, 0, bias,
-                                                 act == kActRelu);
-        else
-          epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias,
-                                          act, cs, ldcs);
-      } else if constexpr (FUSED) {
-        epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias,
-                                        act, cs, ldcs);
-      } else if constexpr (std::is_same<OutT, uint8_t>::value) {
-        epilogue_direct_q<Cfg, MODE>(acc, lds, C, ldc, m0, n0, tensor_scale, cs, ldcs);
-      } else {
-#if FP8GEMM_DIRECT_EPILOGUE
-        epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, n0, tensor_scale);
-#else
-        epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
-#endif
-      }
+      epilogue_full_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale,
+                                                 bias, act, cs, ldcs);
       return;
     }
   }
   v16f acc[Cfg::kFragM][Cfg::kFragN];
   mainloop<Cfg, MODE, KALIGNED && !kF4>(op, lds, acc);
-  if constexpr (FUSED || std::is_same<OutT, uint8_t>::value)
-    epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act,
-                                    cs, ldcs);
-  else
-    epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
+  epilogue_any_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale,
+                                            bias, act, cs, ldcs);
+}
+
+// One output tile with row-major B ([K][N]): the interior mainloop in its KN
+// form for every tile (the caller guarantees K % 128 == 0, MX K % 512 == 0, and
+// 32-bit spans); tiles cut by M or N end in the general epilogue.
+template <class Cfg, int MODE, typename OutT, bool FUSED = false>
+__device__ __forceinline__ void gemm_tile_kn(const TileOperands& op, uint8_t* lds, OutT* C,
+                                             int64_t ldc, int m0, int m_end, int n0, int N,
+                                             float tensor_scale, const float* bias = nullptr,
+                                             int act = kActNone, uint8_t* cs = nullptr,
+                                             int64_t ldcs = 0) {
+  if (op.a_rows >= Cfg::BM && op.b_rows >= Cfg::BN) {
+    v16f acc[Cfg::kFragM][Cfg::kFragN];
+    mainloop_interior<Cfg, MODE, 2, true>(op, lds, acc);
+    epilogue_full_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale,
+                                               bias, act, cs, ldcs);
+    return;
+  }
+  v16f acc[Cfg::kFragM][Cfg::kFragN];
+  mainloop_interior<Cfg, MODE, 2, true>(op, lds, acc);
+  epilogue_any_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale,
+                                            bias, act, cs, ldcs);
 }
 
 }  // inline namespace

@@ -67,6 +67,13 @@ hipError_t launch_gemm(const GemmProblem& p, int mode, int out, hipStream_t stre
 hipError_t launch_gemm_e5m2_e5m2(const GemmProblem& p, int mode, int out, hipStream_t stream);
 hipError_t launch_gemm_e4m3_e5m2(const GemmProblem& p, int mode, int out, hipStream_t stream);
 hipError_t launch_gemm_e5m2_e4m3(const GemmProblem& p, int mode, int out, hipStream_t stream);
+// The same GEMMs with B row-major [K][N] (ldb: bytes between K-rows; MX codes of
+// B [K/32][N]) read by the kernels through transposing LDS reads; only for
+// shapes where choose_path_kn() finds a path (else hipErrorInvalidValue).
+hipError_t launch_gemm_kn(const GemmProblem& p, int mode, int out, hipStream_t stream);
+hipError_t launch_gemm_kn_e5m2_e5m2(const GemmProblem& p, int mode, int out, hipStream_t stream);
+hipError_t launch_gemm_kn_e4m3_e5m2(const GemmProblem& p, int mode, int out, hipStream_t stream);
+hipError_t launch_gemm_kn_e5m2_e4m3(const GemmProblem& p, int mode, int out, hipStream_t stream);
 // MXFP4 x MXFP4 (mode kMx32 only): K, lda and ldb of the problem count bytes
 // (two e2m1 codes each), the E8M0 codes stay one per 32 elements.
 hipError_t launch_gemm_e2m1_e2m1(const GemmProblem& p, int mode, int out, hipStream_t stream);

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FP8GEMM_VERSION 170 /* 1.7.0: e5m2, fused epilogues, row-major B, MXFP4 (dense, grouped), MXFP6 (dense), MX output, path query, no-allocation GEMM */
+#define FP8GEMM_VERSION 180 /* 1.8.0: e5m2, fused epilogues, row-major B read in-kernel, MXFP4 (dense, grouped), MXFP6 (dense), MX output, path queries, no-allocation GEMM */
 
 typedef enum fp8gemm_status {
   FP8GEMM_SUCCESS = 0,
@@ -237,14 +237,21 @@ fp8gemm_status fp8gemm_run_mxout(int64_t M, int64_t N, int64_t K, const uint8_t*
 /*   scale_b: TENSOR float[1]; ROWWISE float[N]; MX32 uint8 [K/32][N] (row-major, */
 /*            N codes per row).                                                 */
 /* Everything else (A, C, formats, scale_a, bias, activation, accuracy, errors) */
-/* as fp8gemm_run_ex; E2M1 and FP6 operands are NOT_SUPPORTED here.  The call  */
-/* first                                                                      */
-/* copies B and its MX codes into the                                           */
-/* K-contiguous layout in the workspace (one HBM pass over B), then runs the    */
-/* GEMM: workspace is fp8gemm_workspace_size_kn() bytes, 16-byte aligned,       */
-/* zero-filled before its first use (never NULL: the copy lives there).  Its    */
-/* first 4 KiB are the counters of fp8gemm_run (left at zero); the copies come  */
-/* after the GEMM's own workspace, so the two entry points may share one.       */
+/* as fp8gemm_run_ex; E2M1 and FP6 operands are NOT_SUPPORTED here.            */
+/* Two forms, chosen per call (fp8gemm_run_kn_path tells which):                 */
+/*   in-kernel : the GEMM kernels read B row-major and form the K-major MFMA     */
+/*               operand with transposing LDS reads (no extra pass over B).      */
+/*               Taken when K % 128 == 0 (MX: K % 512 == 0 and N % 16 == 0) and  */
+/*               the operand spans fit 32-bit offsets (K * ldb < 2^31 - 256).    */
+/*               Workspace: fp8gemm_workspace_size(M, N, K, mode) bytes (NULL    */
+/*               when that is 0).                                                */
+/*   transposing: otherwise the call first copies B and its MX codes into the   */
+/*               K-contiguous layout in the workspace (one HBM pass over B), then */
+/*               runs the GEMM.  Workspace never NULL: the copy lives there.     */
+/* fp8gemm_workspace_size_kn() bytes, 16-byte aligned and zero-filled before    */
+/* its first use, serve either form.  Its first 4 KiB are the counters of       */
+/* fp8gemm_run (left at zero); the copies come after the GEMM's own workspace,  */
+/* so the two entry points may share one.                                       */
 /* ------------------------------------------------------------------------- */
 size_t fp8gemm_workspace_size_kn(int64_t M, int64_t N, int64_t K, int mode);
 
@@ -347,6 +354,12 @@ typedef enum fp8gemm_path {
 
 int fp8gemm_run_path(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int a_format,
                      int b_format, int mode, int fused);
+
+/* The kernel path fp8gemm_run_kn takes in its in-kernel form (ldb: bytes      */
+/* between the K-rows of the row-major B), or FP8GEMM_PATH_NONE when the call   */
+/* makes B K-contiguous first (or would launch nothing).  Never PERSISTENT.     */
+int fp8gemm_run_kn_path(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                        int a_format, int b_format, int mode);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fp8gemm_status_string(int status);

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
         "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex", "fp8gemm_workspace_size_kn",
         "fp8gemm_run_kn", "fp8gemm_run_mxout",
         "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run", "fp8gemm_grouped_run_ex",
-        "fp8gemm_run_path", "fp8gemm_run_noalloc", "fp8gemm_status_string",
+        "fp8gemm_run_path", "fp8gemm_run_kn_path", "fp8gemm_run_noalloc", "fp8gemm_status_string",
         "fp8gemm_version"}
     raw = ctypes.CDLL(F.library_path())
     for n in names:
@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert F.fp8gemm_version() == 170
+    assert F.fp8gemm_version() == 180
     for code, name in [(0, "FP8GEMM_SUCCESS"), (1, "FP8GEMM_ERROR_INVALID_VALUE"),
                        (2, "FP8GEMM_ERROR_MISALIGNED"), (3, "FP8GEMM_ERROR_NOT_SUPPORTED"),
                        (4, "FP8GEMM_ERROR_WORKSPACE"), (5, "FP8GEMM_ERROR_LAUNCH"),
@@ -287,13 +287,15 @@ def test_mxout_validation(lib):
 
 
 def test_row_major_b_validation(lib):
-    """fp8gemm_run_kn: validated before any HIP call; the workspace holds B's copy."""
-    need = F.fp8gemm_workspace_size_kn(64, 64, 128, 1)
-    assert need >= 64 * 128
-    assert F.fp8gemm_workspace_size_kn(64, 64, 128, 2) >= need + 64 * 4     # + MX codes
-    assert F.fp8gemm_workspace_size_kn(64, 64, 128, 9) == 0
-    def run(B=P2, ldb=64, ws=P3 + (1 << 20), wsb=need, K=128, mode=1, **kw):
-        return lib.fp8gemm_run_kn(kw.get("M", 64), 64, K, P, 128, 0, B, ldb, 0, mode, P3,
+    """fp8gemm_run_kn, transposing form (K % 128 != 0): validated before any HIP
+    call; the workspace holds B's copy."""
+    need = F.fp8gemm_workspace_size_kn(64, 64, 144, 1)
+    assert need >= 64 * 144
+    assert F.fp8gemm_workspace_size_kn(64, 64, 144, 2) >= need + 64 * 4     # + MX codes
+    assert F.fp8gemm_workspace_size_kn(64, 64, 144, 9) == 0
+    assert F.fp8gemm_run_kn_path(64, 64, 144, 144, 64, 0, 0, 1) == "none"
+    def run(B=P2, ldb=64, ws=P3 + (1 << 20), wsb=need, K=144, mode=1, **kw):
+        return lib.fp8gemm_run_kn(kw.get("M", 64), 64, K, P, 144, 0, B, ldb, 0, mode, P3,
                                   P3 + 256, 0, 0, P3 + 4096, 64, 1, ws, wsb, None)
     assert run(M=0) == SUCCESS
     assert run(B=0) == INVALID
@@ -304,6 +306,56 @@ def test_row_major_b_validation(lib):
     assert run(wsb=need - 16) == WORKSPACE
     assert run(ws=P3 + (1 << 20) + 8) == MISALIGNED
     assert run(K=120) == NOT_SUPPORTED
+
+
+@pytest.mark.parametrize("shape,ld,fa,fb,mode,path", [
+    ((128, 4096, 4096), None, "e4m3", "e4m3", "tensor", "splitk"),
+    ((128, 4096, 4096), None, "e5m2", "e4m3", "mx32", "splitk"),
+    ((4096, 4096, 4096), None, "e4m3", "e4m3", "rowwise", "tile256"),
+    ((16384, 8192, 512), None, "e4m3", "e4m3", "tensor", "tile256"),     # never persistent
+    ((2048, 4096, 1024), None, "e4m3", "e5m2", "mx32", "tile128"),
+    ((300, 520, 384), None, "e5m2", "e5m2", "rowwise", "tile128"),         # edge tiles
+    ((2048, 4096, 4160), None, "e4m3", "e4m3", "tensor", "none"),          # K % 128
+    ((2048, 4096, 1152), None, "e4m3", "e4m3", "mx32", "none"),            # MX: K % 512
+    ((2048, 4112, 1024), None, "e4m3", "e4m3", "mx32", "tile128"),         # MX: N % 16 == 0
+    ((2048, 4100, 1024), (1024, 4112), "e4m3", "e4m3", "mx32", "none"),    # MX: N % 16
+    ((2048, 4100, 1024), (1024, 4112), "e4m3", "e4m3", "tensor", "tile128"),
+    ((256, 256, 1 << 19), (1 << 19, 8192), "e4m3", "e4m3", "tensor", "none"),  # K * ldb >= 2^31
+    ((128, 4096, 4096), None, "e2m1", "e2m1", "mx32", "none"),             # FP4: transposing form refused
+    ((0, 4096, 4096), None, "e4m3", "e4m3", "tensor", "none"),
+])
+def test_row_major_b_in_kernel_rules(lib, shape, ld, fa, fb, mode, path):
+    """Which shapes fp8gemm_run_kn serves with the transposing LDS reads (the query
+    runs the same planner as the call)."""
+    M, N, K = shape
+    lda, ldb = ld if ld else (K, N)
+    assert F.fp8gemm_run_kn_path(M, N, K, lda, ldb, F.FORMATS[fa], F.FORMATS[fb],
+                                 F.SCALE_MODES[mode]) == path
+
+
+def test_row_major_b_in_kernel_validation(lib):
+    """fp8gemm_run_kn, in-kernel form (K % 128 == 0): the dense GEMM's checks and
+    only the dense GEMM's workspace, all before any HIP call."""
+    M, N, K = 128, 4096, 4096                      # split-K: needs the dense workspace
+    need = F.fp8gemm_workspace_size(M, N, K, 0)
+    assert need > 0 and F.fp8gemm_workspace_size_kn(M, N, K, 0) > need
+    def run(A=P, lda=K, ldb=N, ws=P3 + (1 << 20), wsb=need, C=P3 + 4096, ldc=N, bias=0,
+            sb=P3 + 256, **kw):
+        return lib.fp8gemm_run_kn(kw.get("M", M), N, K, A, lda, 0, P2, ldb, 0, 0, P3, sb, bias,
+                                  0, C, ldc, 1, ws, wsb, None)
+    assert F.fp8gemm_run_kn_path(M, N, K, K, N, 0, 0, 0) == "splitk"
+    assert run(M=0) == SUCCESS
+    assert run(ws=0) == WORKSPACE
+    assert run(wsb=need - 16) == WORKSPACE
+    assert run(ws=P3 + (1 << 20) + 8) == MISALIGNED
+    assert run(A=0) == INVALID
+    assert run(lda=K - 16) == INVALID                  # lda < K
+    assert run(A=P + 8) == MISALIGNED
+    assert run(C=0) == INVALID
+    assert run(ldc=N - 8) == INVALID
+    assert run(C=P3 + 4100) == MISALIGNED
+    assert run(bias=P3 + 2) == MISALIGNED
+    assert run(sb=P3 + 258) == MISALIGNED
 
 
 def test_run_split_workspace_validation(lib):

@@ -1,9 +1,13 @@
 """GPU parity of the dense GEMM with B in row-major [K, N] layout (N contiguous).
 
 The oracle's B is [N, K]; the GPU gets its transpose (and, for MX, the transposed
-codes [K/32, N]) through fp8gemm_run_kn, on ragged shapes (edge path), full
-tiles (interior path, sampled blocks), a split-K shape and with e5m2 codes and a
-fused epilogue.
+codes [K/32, N]) through fp8gemm_run_kn.  Two forms: shapes with K % 128 == 0
+(MX: K % 512 == 0, N % 16 == 0) are read row-major by the GEMM kernels
+themselves (transposing LDS reads), the others are made K-contiguous first.
+Both are checked against the oracle on ragged shapes, full tiles (sampled
+blocks), split-K shapes, every e4m3 / e5m2 pairing and fused epilogues; the
+in-kernel form must also equal the K-contiguous GEMM bit for bit where the two
+run the same tile path (same products, same order).
 """
 import numpy as np
 import pytest
@@ -92,3 +96,109 @@ def test_row_major_b_shares_the_workspace_with_split_k():
                                scale_to_dev(sb, "rowwise"), "rowwise", "bf16"))
         Cr, Ar = O.gemm_reference(qa, sa, qb, sb, "rowwise")
         assert_within_bound(C, Cr, Ar, "bf16", f"shared workspace {layout} {(M, N, K)}")
+
+
+def _run_nk(qa, sa, qb, sb, mode, out="bf16", fb="e4m3", bias=None, act="none"):
+    bd = None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).to(DEV)
+    return F.gemm(to_dev(qa, 16), scale_to_dev(sa, mode), to_dev(qb, 16), scale_to_dev(sb, mode),
+                  mode, out, fmt_b=fb, bias=bd, activation=act)
+
+
+def _kn_path(M, N, K, mode, fb="e4m3"):
+    return F.fp8gemm_run_kn_path(M, N, K, (K + 15) // 16 * 16, (N + 15) // 16 * 16,
+                                 F.FORMATS["e4m3"], F.FORMATS[fb], F.SCALE_MODES[mode])
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("out,shape,path", [
+    ("bf16", (300, 528, 512), "tile128"),         # edge tiles in M and N
+    ("f16", (128, 256, 512), "tile128"),          # one row of full tiles
+    ("bf16", (300, 528, 1024), "splitk"),         # ragged split tiles
+    ("bf16", (100, 2000, 4096), "splitk"),
+    ("f16", (64, 1024, 8192), "splitk"),
+])
+def test_gemm_row_major_b_in_kernel(mode, out, shape, path):
+    M, N, K = shape
+    assert _kn_path(M, N, K, mode) == path
+    qa, sa, qb, sb = _operands(M, N, K, mode, seed=7 * M + N + K)
+    announce("gemm row-major B in-kernel", mode, out, shape, path)
+    C = to_host(_run_kn(qa, sa, qb, sb, mode, out))
+    Cr, Ar = O.gemm_reference(qa, sa, qb, sb, mode)
+    assert_within_bound(C, Cr, Ar, out, f"row-major B in-kernel {mode}/{out}/{shape}")
+    Cn = to_host(_run_nk(qa, sa, qb, sb, mode, out))
+    assert F.fp8gemm_run_path(M, N, K, (K + 15) // 16 * 16, (K + 15) // 16 * 16, 0, 0,
+                              F.SCALE_MODES[mode], 0) == path
+    diff = np.argwhere(C != Cn)
+    assert diff.size == 0, (f"in-kernel row-major B differs from the K-contiguous GEMM "
+                            f"({mode}, {shape}) at {len(diff)} outputs, first {tuple(diff[0])}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", [(4096, 4096, 512), (4352, 4160, 512)])
+def test_gemm_row_major_b_in_kernel_large_tile(mode, shape):
+    """256 x 256 tiles read row-major: all full tiles, and a grid cut by N (and
+    full in M); sampled 128 x 128 blocks, first, last and edge ones."""
+    M, N, K = shape
+    assert _kn_path(M, N, K, mode) == "tile256"
+    qa, sa, qb, sb = _operands(M, N, K, mode, seed=M + N)
+    announce("gemm row-major B in-kernel 256", mode, shape)
+    C = _run_kn(qa, sa, qb, sb, mode)
+    torch.cuda.synchronize()
+    for r0, c0 in ((0, 0), (M - 128, N - 128), (2048, 1024), (256 * 7, N - 64)):
+        ri = np.arange(r0, min(r0 + 128, M))
+        ci = np.arange(c0, min(c0 + 128, N))
+        Cr, Ar = O.gemm_reference(qa, sa, qb, sb, mode, rows=ri, cols=ci)
+        assert_within_bound(to_host(C[ri[0]:ri[-1] + 1, ci[0]:ci[-1] + 1]), Cr, Ar, "bf16",
+                            f"row-major B in-kernel 256 {mode} block {(r0, c0)}")
+
+
+@pytest.mark.parametrize("fa,fb", [("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")])
+@pytest.mark.parametrize("mode", MODES)
+def test_gemm_row_major_b_in_kernel_formats(fa, fb, mode):
+    M, N, K = 192, 400, 512
+    A, B = random_inputs(M, N, K, 31, "mx_block")
+    qa, sa = Q.quantize(A, mode, fa)
+    qb, sb = Q.quantize(B, mode, fb)
+    assert F.fp8gemm_run_kn_path(M, N, K, K, (N + 15) // 16 * 16, F.FORMATS[fa], F.FORMATS[fb],
+                                 F.SCALE_MODES[mode]) == "tile128"
+    announce("gemm row-major B in-kernel formats", fa, fb, mode)
+    qb_kn = to_dev(np.ascontiguousarray(qb.T), 16)
+    sb_d = (torch.from_numpy(np.ascontiguousarray(np.asarray(sb, np.uint8).T)).to(DEV)
+            if mode == "mx32" else scale_to_dev(sb, mode))
+    C = to_host(F.gemm(to_dev(qa, 16), scale_to_dev(sa, mode), qb_kn, sb_d, mode, "bf16",
+                       fmt_a=fa, fmt_b=fb, b_layout="kn"))
+    Cr, Ar = O.gemm_reference(qa, sa, qb, sb, mode, fmt_a=fa, fmt_b=fb)
+    assert_within_bound(C, Cr, Ar, "bf16", f"row-major B in-kernel {fa}x{fb} {mode}")
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu", "silu"])
+def test_gemm_row_major_b_in_kernel_fused(act):
+    M, N, K = 300, 528, 512
+    qa, sa, qb, sb = _operands(M, N, K, "mx32", seed=17)
+    bias = np.random.default_rng(18).standard_normal(N).astype(np.float32) * 2
+    assert _kn_path(M, N, K, "mx32") == "tile128"
+    announce("gemm row-major B in-kernel fused", act)
+    C = to_host(_run_kn(qa, sa, qb, sb, "mx32", bias=bias, act=act))
+    Cr, Ar = O.gemm_reference(qa, sa, qb, sb, "mx32")
+    o_ref, y_ref = O.epilogue_reference(Cr, Ar, bias, act)
+    tol = O.epilogue_tolerance(o_ref, y_ref, Ar, act, "bf16")
+    bad = np.argwhere(np.abs(C - o_ref) > tol)
+    assert bad.size == 0, f"{act}: {len(bad)} outside the bound, first {tuple(bad[0])}"
+
+
+def test_gemm_row_major_b_in_kernel_wide_pitch():
+    """B rows (K-rows) with a pitch well past N, and codes of MX rows of N."""
+    M, N, K = 256, 384, 512
+    for mode in MODES:
+        qa, sa, qb, sb = _operands(M, N, K, mode, seed=44)
+        buf = torch.zeros((K, N + 208), dtype=torch.uint8, device=DEV)
+        buf[:, :N] = torch.from_numpy(np.ascontiguousarray(qb.T)).to(DEV)
+        qb_kn = buf[:, :N]
+        assert F.fp8gemm_run_kn_path(M, N, K, K, N + 208, 0, 0, F.SCALE_MODES[mode]) == "tile128"
+        sb_d = (torch.from_numpy(np.ascontiguousarray(np.asarray(sb, np.uint8).T)).to(DEV)
+                if mode == "mx32" else scale_to_dev(sb, mode))
+        announce("gemm row-major B in-kernel wide pitch", mode)
+        C = to_host(F.gemm(to_dev(qa, 16), scale_to_dev(sa, mode), qb_kn, sb_d, mode, "bf16",
+                           b_layout="kn"))
+        Cr, Ar = O.gemm_reference(qa, sa, qb, sb, mode)
+        assert_within_bound(C, Cr, Ar, "bf16", f"row-major B wide pitch {mode}")
