@@ -1529,10 +1529,36 @@ __device__ __forceinline__ void stream_interior(const Src& src, int first, int l
 // Fused epilogue operations after the scales: bias[n] added, then an activation
 // (the Cutlass-named Triton FP8 post fuses a bias_add_relu epilogue to save the
 // round trip of C; GELU, erf form, and SiLU are the other common choices).
+// Activations of the fused epilogue in fp32, from the hardware reciprocal and
+// exp2 (v_rcp_f32, v_exp_f32; about an ulp each):
+//   GELU(v) = v Phi(v) = v (1 + erf(v / sqrt 2)) / 2, with erf(z), z >= 0, from
+//     the rational approximation 7.1.26 of Abramowitz and Stegun's Handbook of
+//     Mathematical Functions: erf(z) = 1 - t (a1 + t (a2 + ... + t a5)) e^(-z^2),
+//     t = 1 / (1 + p z), |error| <= 1.5e-7.  With q = (1 - erf(|v| / sqrt 2)) / 2,
+//     Phi(v) = 1 - q for v >= 0 and q for v < 0.
+//   SiLU(v) = v / (1 + e^-v).
+// About 16 and 5 vector instructions per value.
+__device__ __forceinline__ float gelu_f32(float v) {
+  // z = |v| / sqrt 2 folded into p (t = 1 / (1 + p |v| / sqrt 2)), the 1/2 of q
+  // into a1 .. a5, and e^(-z^2) = 2^(-v^2 log2(e) / 2)
+  constexpr double kP = 0.3275911, kA1 = 0.254829592, kA2 = -0.284496736;
+  constexpr double kA3 = 1.421413741, kA4 = -1.453152027, kA5 = 1.061405429;
+  constexpr float kPs = (float)(kP * 0.70710678118654752);
+  constexpr float kB1 = (float)(kA1 / 2), kB2 = (float)(kA2 / 2), kB3 = (float)(kA3 / 2);
+  constexpr float kB4 = (float)(kA4 / 2), kB5 = (float)(kA5 / 2);
+  constexpr float kE = (float)(-0.5 * 1.4426950408889634);
+  const float t = __builtin_amdgcn_rcpf(fmaf(kPs, fabsf(v), 1.0f));
+  const float hpoly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, kB5, kB4), kB3), kB2), kB1);
+  const float q = hpoly * __builtin_amdgcn_exp2f((v * v) * kE);
+  return v * (v >= 0.0f ? 1.0f - q : q);
+}
+__device__ __forceinline__ float silu_f32(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * 1.4426950408889634f));
+}
 __device__ __forceinline__ float activate(float v, int act) {
   if (act == kActRelu) return fmaxf(v, 0.0f);
-  if (act == kActGelu) return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
-  if (act == kActSilu) return v / (1.0f + expf(-v));
+  if (act == kActGelu) return gelu_f32(v);
+  if (act == kActSilu) return silu_f32(v);
   return v;
 }
 
@@ -1603,11 +1629,11 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFr
 // epilogue_direct below.  Each wave first copies the bias of its WN columns into
 // a wave-private stretch of the (free) ring, then reads four columns at a time
 // like the row-wise column scales (bias == nullptr: zeros).
-template <class Cfg, int MODE, typename OutT>
+template <class Cfg, int MODE, typename OutT, int ACT>
 __device__ __forceinline__ void epilogue_direct_bias(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                      uint8_t* lds, OutT* C, int64_t ldc,
                                                      int m0, int n0, float tensor_scale,
-                                                     const float* bias, bool relu) {
+                                                     const float* bias) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -1643,8 +1669,7 @@ __device__ __forceinline__ void epilogue_direct_bias(const v16f (&acc)[Cfg::kFra
           for (int e = 0; e < 4; ++e) {
             v[e] = acc[i][j][4 * g + e] * fa;
             if (MODE == kRowwise) v[e] *= fb[e];
-            v[e] += bv[e];
-            if (relu) v[e] = fmaxf(v[e], 0.0f);
+            v[e] = activate(v[e] + bv[e], ACT);
           }
           w[q] = pack4<OutT>(v[0], v[1], v[2], v[3]);
         }
@@ -1664,18 +1689,25 @@ __device__ __forceinline__ void epilogue_direct_bias(const v16f (&acc)[Cfg::kFra
 // with group 2k of the high half, after which every lane owns eight consecutive
 // columns (16 bytes) of its row: C is written with 16-byte stores and no LDS
 // staging, so the epilogue costs a few hundred instructions and no waits.
-// BIAS (fused kernels, interior tiles, no activation or ReLU): the bias of the
-// lane's 16 columns of block j is loaded once per j and added after the scales,
-// then ReLU when `relu`; the heavier activations take the staged loop below.
+// BIAS (fused kernels, interior tiles): the bias of the lane's 16 columns of
+// block j is loaded once per j and added after the scales, then the activation
+// `act` (one instance of the loop per activation, chosen once).
 template <class Cfg, int MODE, typename OutT, bool BIAS = false>
 __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                 uint8_t* lds, OutT* C, int64_t ldc, int m0,
                                                 int n0, float tensor_scale, int rbuf = 0,
-                                                const float* bias = nullptr, bool relu = false) {
+                                                const float* bias = nullptr, int act = kActNone) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   static_assert(sizeof(OutT) == 2, "16-bit outputs");
   if constexpr (BIAS) {
-    epilogue_direct_bias<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, n0, tensor_scale, bias, relu);
+    if (act == kActGelu)
+      epilogue_direct_bias<Cfg, MODE, OutT, kActGelu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias);
+    else if (act == kActSilu)
+      epilogue_direct_bias<Cfg, MODE, OutT, kActSilu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias);
+    else if (act == kActRelu)
+      epilogue_direct_bias<Cfg, MODE, OutT, kActRelu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias);
+    else
+      epilogue_direct_bias<Cfg, MODE, OutT, kActNone>(acc, lds, C, ldc, m0, n0, tensor_scale, bias);
     return;
   }
   const int lane = threadIdx.x & 63;
@@ -1900,12 +1932,7 @@ __device__ __forceinline__ void epilogue_full_tile(const v16f (&acc)[Cfg::kFragM
                                                    const float* bias, int act, uint8_t* cs,
                                                    int64_t ldcs) {
   if constexpr (FUSED && !std::is_same<OutT, uint8_t>::value) {
-    if (act == kActNone || act == kActRelu)
-      epilogue_direct<Cfg, MODE, OutT, true>(acc, lds, C, ldc, m0, n0, tensor_scale, 0, bias,
-                                             act == kActRelu);
-    else
-      epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act,
-                                      cs, ldcs);
+    epilogue_direct<Cfg, MODE, OutT, true>(acc, lds, C, ldc, m0, n0, tensor_scale, 0, bias, act);
   } else if constexpr (FUSED) {
     epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act,
                                     cs, ldcs);
