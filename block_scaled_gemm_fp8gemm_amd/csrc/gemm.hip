@@ -240,7 +240,7 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void splitk_kernel
 
   v16f acc[FM][FN];
   if constexpr (kKn) mainloop_interior<Cfg, MODE, kSplitRing, true>(op, lds, acc);
-  else if (interior_tile<Cfg, MODE>(op)) mainloop_interior<Cfg, MODE, kSplitRing>(op, lds, acc);
+  else if (interior_k<Cfg, MODE>(op)) mainloop_interior<Cfg, MODE, kSplitRing>(op, lds, acc);
   else mainloop<Cfg, MODE, !kF4>(op, lds, acc);
 
   // partial tile: float4 r of thread x at [tile][slice][r][x] (coalesced per r)

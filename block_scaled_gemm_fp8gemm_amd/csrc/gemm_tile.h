@@ -675,13 +675,21 @@ struct Unroll {
   }
 };
 
-// Whether a tile takes the interior path (uniform over the workgroup).
+// Whether a tile's K extent and spans suit the interior mainloop (whole 128-K
+// tiles, MX whole code groups, 32-bit buffer offsets); uniform over the
+// workgroup.  Rows past M or N are read as zero there, so tiles cut by the edges
+// qualify too (their epilogue masks the stores).
 template <class Cfg, int MODE>
-__device__ __forceinline__ bool interior_tile(const TileOperands& op) {
-  return op.a_rows >= Cfg::BM && op.b_rows >= Cfg::BN &&
-         op.K % (MODE == kMx32 ? 16 * kBlkBytes : 128) == 0 &&
+__device__ __forceinline__ bool interior_k(const TileOperands& op) {
+  return op.K % (MODE == kMx32 ? 16 * kBlkBytes : 128) == 0 &&
          (int64_t)Cfg::BM * op.lda + op.K < ((int64_t)1 << 31) &&
          (int64_t)Cfg::BN * op.ldb + op.K < ((int64_t)1 << 31);
+}
+// ... and the tile is whole (every row and column valid): the copy-stream and
+// register-direct epilogue paths.
+template <class Cfg, int MODE>
+__device__ __forceinline__ bool interior_tile(const TileOperands& op) {
+  return op.a_rows >= Cfg::BM && op.b_rows >= Cfg::BN && interior_k<Cfg, MODE>(op);
 }
 
 #ifndef FP8GEMM_READ_SPAN
@@ -759,12 +767,13 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   // (lane >> 3) of the block, LDS chunk lane & 7, global chunk (lane & 7) ^
   // ((row >> 1) & 7); the swizzle of even and odd blocks differs
   const int g0 = wave * kLoads;                   // first block of this wave
-  // valid rows (KN: B columns) of the tile: copies of rows past A's edge read zero
+  // valid rows (KN: B columns) of the tile: copies of rows past the edge of A
+  // (and of a K-contiguous B) read zero, so tiles cut by M or N run here too
   const int a_tile = op.a_rows < Cfg::BM ? op.a_rows : Cfg::BM;
   const int b_tile = op.b_rows < Cfg::BN ? op.b_rows : Cfg::BN;
   const uint32_t nrA = (uint32_t)((a_tile - 1) * op.lda + op.K);
   const uint32_t nrB = KN ? (uint32_t)((op.K - 1) * op.ldb + b_tile)
-                          : (uint32_t)((Cfg::BN - 1) * op.ldb + op.K);
+                          : (uint32_t)((b_tile - 1) * op.ldb + op.K);
   const __amdgpu_buffer_rsrc_t rsA = buffer_rsrc(op.A, nrA);
   const __amdgpu_buffer_rsrc_t rsB = buffer_rsrc(op.B, nrB);
   // KN: the copies go out untracked (see buffer_dma16_untracked)
@@ -796,7 +805,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   const uint32_t lds_base = KN ? lds_address(lds) : 0u;
   const uint32_t ncA = (uint32_t)((a_tile - 1) * op.sld + nblk);
   const uint32_t ncB = KN ? (uint32_t)((nblk - 1) * op.sldb + b_tile)
-                          : (uint32_t)((Cfg::BN - 1) * op.sld + nblk);
+                          : (uint32_t)((b_tile - 1) * op.sld + nblk);
   const __amdgpu_buffer_rsrc_t rcA = buffer_rsrc(op.sa, ncA);
   const __amdgpu_buffer_rsrc_t rcB = buffer_rsrc(op.sb, ncB);
   const v4u_rs wcA = buffer_rsrc_words(op.sa, ncA), wcB = buffer_rsrc_words(op.sb, ncB);
@@ -1963,19 +1972,26 @@ __device__ __forceinline__ void epilogue_any_tile(const v16f (&acc)[Cfg::kFragM]
 
 // One output tile: the interior mainloop when the tile qualifies, else the
 // general (clamped) one, then the epilogue.  Each branch has its own accumulators
-// and epilogue so no accumulator copies join the two paths.
-template <class Cfg, int MODE, typename OutT, bool KALIGNED, bool FUSED = false>
+// and epilogue so no accumulator copies join the two paths.  EDGE_INTERIOR: tiles
+// cut by M or N take the interior mainloop too (the grouped kernel keeps them on
+// the general one: its copy-stream path spills once the extra branch is there).
+template <class Cfg, int MODE, typename OutT, bool KALIGNED, bool FUSED = false,
+          bool EDGE_INTERIOR = true>
 __device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, OutT* C,
                                           int64_t ldc, int m0, int m_end, int n0, int N,
                                           float tensor_scale, const float* bias = nullptr,
                                           int act = kActNone, uint8_t* cs = nullptr,
                                           int64_t ldcs = 0) {
   if constexpr (KALIGNED && Cfg::kSlots == 4) {
-    if (interior_tile<Cfg, MODE>(op)) {
+    if (EDGE_INTERIOR ? interior_k<Cfg, MODE>(op) : interior_tile<Cfg, MODE>(op)) {
       v16f acc[Cfg::kFragM][Cfg::kFragN];
       mainloop_interior<Cfg, MODE>(op, lds, acc);
-      epilogue_full_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale,
-                                                 bias, act, cs, ldcs);
+      if (!EDGE_INTERIOR || (op.a_rows >= Cfg::BM && op.b_rows >= Cfg::BN))
+        epilogue_full_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N,
+                                                   tensor_scale, bias, act, cs, ldcs);
+      else                                        // a tile cut by M or N
+        epilogue_any_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N,
+                                                  tensor_scale, bias, act, cs, ldcs);
       return;
     }
   }
@@ -1994,17 +2010,14 @@ __device__ __forceinline__ void gemm_tile_kn(const TileOperands& op, uint8_t* ld
                                              float tensor_scale, const float* bias = nullptr,
                                              int act = kActNone, uint8_t* cs = nullptr,
                                              int64_t ldcs = 0) {
-  if (op.a_rows >= Cfg::BM && op.b_rows >= Cfg::BN) {
-    v16f acc[Cfg::kFragM][Cfg::kFragN];
-    mainloop_interior<Cfg, MODE, 2, true>(op, lds, acc);
-    epilogue_full_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale,
-                                               bias, act, cs, ldcs);
-    return;
-  }
   v16f acc[Cfg::kFragM][Cfg::kFragN];
   mainloop_interior<Cfg, MODE, 2, true>(op, lds, acc);
-  epilogue_any_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale,
-                                            bias, act, cs, ldcs);
+  if (op.a_rows >= Cfg::BM && op.b_rows >= Cfg::BN)
+    epilogue_full_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale,
+                                               bias, act, cs, ldcs);
+  else
+    epilogue_any_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale,
+                                              bias, act, cs, ldcs);
 }
 
 }  // inline namespace

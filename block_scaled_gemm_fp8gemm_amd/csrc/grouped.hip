@@ -158,8 +158,8 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void grouped_kerne
     if (!streamed) {
       const auto w = src.where(i);
       const float ts = (MODE == kTensor) ? fsa[0] * fsb[w.g] : 1.0f;
-      gemm_tile<Cfg, MODE, OutT, KALIGNED>(src.op_at(w), lds, C, p.ldc, w.m0, w.m_end, w.n0, p.N,
-                                           ts);
+      gemm_tile<Cfg, MODE, OutT, KALIGNED, false, false>(src.op_at(w), lds, C, p.ldc, w.m0,
+                                                         w.m_end, w.n0, p.N, ts);
       ++i;
     }
   }
