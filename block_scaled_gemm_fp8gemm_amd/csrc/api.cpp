@@ -514,9 +514,9 @@ int fp8gemm_run_path(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, 
   const bool fp4 = a_format == FP8GEMM_FORMAT_E2M1 || b_format == FP8GEMM_FORMAT_E2M1;
   if (fp4 && (a_format != b_format || mode != kMx32)) return FP8GEMM_PATH_NONE;
   const bool fp6 = is_fp6(a_format) || is_fp6(b_format);
-  if (fp6) {                                   // one FP6 kernel: 128 x 128 tiles
+  if (fp6) {
     if (!is_fp6(a_format) || !is_fp6(b_format) || mode != kMx32) return FP8GEMM_PATH_NONE;
-    return M > 0 && N > 0 ? FP8GEMM_PATH_TILE128 : FP8GEMM_PATH_NONE;
+    return fp8gemm::choose_path_fp6(M, N, K, lda, ldb);
   }
   return fp8gemm::choose_path(M, N, fp4 ? K / 2 : K, lda, ldb, mode, fp4, fused != 0);
 }

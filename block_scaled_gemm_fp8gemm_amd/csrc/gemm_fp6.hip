@@ -26,6 +26,7 @@
 
 #include "gemm_tile.h"
 #include "launch.h"
+#include "plan.h"
 #include "tile_order.h"
 
 namespace fp8gemm {
@@ -208,8 +209,273 @@ __global__ __launch_bounds__(256, 2) void fp6_kernel(GemmProblem p, int tiles_m,
     epilogue<Cfg, MODE, OutT>(acc, lds, C, p.ldc, m0, p.M, n0, p.N, 1.0f);
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles for shapes with a tile per CU: 4 wavefronts of 128 x 128, one
+// workgroup per CU.  A 64-K step of a 128 x 128 wavefront tile reads 8 fragments
+// for 16 MFMAs; the 128 x 128 tile above reads 4 for 4, and at two workgroups per
+// CU asks for more LDS bandwidth than there is.
+//   * K tiles of 96 bytes per row (128 codes, two MFMA steps), so no step
+//     straddles two tiles, in a three-slot ring: A plane (3 x 256 rows x 96 B),
+//     then B plane, then two buffers of 16 E8M0 codes per row: 160 KiB.  With the
+//     planes apart every slot is in reach of one base register per piece.
+//   * A K tile holds four 32-element blocks of 24 bytes.  Step 0 feeds lane h
+//     block 2 h, step 1 block 2 h + 1 (any order of K inside an MFMA sums the
+//     same, and a lane still holds one whole MX block with its own code).  A
+//     lane reads the two whole 16-byte chunks its block lies in (chunks 3 h,
+//     3 h + 1 for the even block, 3 h + 1, 3 h + 2 for the odd one) into eight
+//     registers like an FP8 fragment, and the MFMA takes registers 0-5 or 2-7:
+//     a third more LDS reads than the 24 bytes, but operands the register
+//     allocator places without copies.
+//   * Row stride 96 bytes puts rows r and r + 8 on the same banks; chunk c of
+//     row r is stored at (c + ((r >> 3) & 1)) mod 6, which makes the 16-byte
+//     reads of 16 rows conflict-free.
+//   * Copy instruction j of a wave covers flat chunks 64 j .. 64 j + 63 of its
+//     operand's 128 rows (row F / 6, position F % 6); instructions j and j + 3 are
+//     32 rows apart with the same pattern, so a lane has three offsets and the
+//     row offset goes in the scalar offset.
+//   * K tile u: step 0 reads step 1's fragments (same slot) during its MFMAs;
+//     step 1 waits for K tile u + 1, meets the other waves at the one barrier
+//     of the K tile, copies K tile u + 3 into the slot of K tile u (and, at the
+//     first K tile of a code group, the next group) and reads K tile u + 1.
+//   * Rows past M or N read as zero (the copy range ends at the last valid row).
+namespace big {
+
+using Cfg = TileCfg<256, 256, 128, 128, 4, 1>;
+constexpr int BM = 256, BN = 256;
+constexpr int kTileB = 96;                         // bytes per row and K tile
+constexpr int NS = 3;                              // ring slots
+constexpr int kSlot = BM * kTileB;                 // one operand's slot, 24 KiB
+constexpr int kPlane = NS * kSlot;                 // 72 KiB per operand
+constexpr int kCodeOff = 2 * kPlane;
+constexpr int kCodeBuf = (BM + BN) * 16;           // 16 codes (512 K) per row
+constexpr int kLdsBytes = kCodeOff + 2 * kCodeBuf;
+constexpr int kLoads = kSlot / 1024 / 2;           // copies per wave and K tile (2 waves per operand)
+constexpr int kCodeLoads = 2;                      // 16-byte code copies per wave and group
+constexpr int kGroupTiles = 4;                     // K tiles per code group
+constexpr int kBody = 12;                          // K tiles per unrolled body (3 slots x 4)
+static_assert(kLoads == 12 && kLoads % 3 == 0, "copy pattern repeats every 3 instructions");
+static_assert(kLdsBytes <= 160 * 1024, "one workgroup per CU");
+static_assert(Cfg::kWaves * 32 * Cfg::kStagePitch <= kCodeOff, "epilogue staging fits the ring");
+static_assert(Cfg::kSlots * Cfg::kSlotBytes <= kCodeOff, "fused epilogue staging fits the ring");
+static_assert((NS - 1) * kLoads + kCodeLoads < 64, "vmcnt range");
+
+template <int FA, int FB, int MODE, typename OutT, bool FUSED>
+__global__ __launch_bounds__(256, 1) void fp6_big_kernel(GemmProblem p, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, kGroupM, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
+  const int h = lane >> 5;
+  const int a_rows = p.M - m0 < BM ? p.M - m0 : BM;
+  const int b_rows = p.N - n0 < BN ? p.N - n0 : BN;
+  const int kbytes = p.K / 4 * 3;
+  const int nk = p.K / 128;                        // K tiles
+  const int nblk = p.K / 32, sld = nblk;
+  const int ngroups = (nk + kGroupTiles - 1) / kGroupTiles;
+
+  // ---- copy side: waves 0-1 copy A rows, 2-3 B rows (128 rows each) ----
+  const bool a_wave = wave < 2;
+  const int ld = (int)(a_wave ? p.lda : p.ldb);
+  const __amdgpu_buffer_rsrc_t rs = a_wave
+      ? buffer_rsrc(p.A + (int64_t)m0 * p.lda, (uint32_t)((a_rows - 1) * p.lda + kbytes))
+      : buffer_rsrc(p.B + (int64_t)n0 * p.ldb, (uint32_t)((b_rows - 1) * p.ldb + kbytes));
+  int voff[3];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const int f = ((wave & 1) * kLoads + q) * 64 + lane;     // flat chunk of the operand's slot
+    const int r = f / 6, cp = f % 6;
+    const int c = (cp + 6 - ((r >> 3) & 1)) % 6;              // global chunk held at position cp
+    voff[q] = r * ld + 16 * c;
+  }
+  uint8_t* const cdst = lds + (a_wave ? 0 : kPlane) + (wave & 1) * kLoads * 1024;
+  auto copy_tile = [&](int slot, int kt) __attribute__((always_inline)) {
+    kt = kt < nk ? kt : nk - 1;                    // past the end: harmless re-fetch
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j)
+      buffer_dma16(rs, cdst + slot * kSlot + j * 1024, voff[j % 3], (j / 3) * 32 * ld + kt * kTileB);
+  };
+  // codes: copy instruction ci = 2 wave + jj covers rows 64 ci .. 64 ci + 63 of
+  // [A; B] (16 bytes per row: lane = row)
+  const __amdgpu_buffer_rsrc_t rc = a_wave
+      ? buffer_rsrc(static_cast<const uint8_t*>(p.scale_a) + (int64_t)m0 * sld,
+                    (uint32_t)((a_rows - 1) * sld + nblk))
+      : buffer_rsrc(static_cast<const uint8_t*>(p.scale_b) + (int64_t)n0 * sld,
+                    (uint32_t)((b_rows - 1) * sld + nblk));
+  auto copy_codes = [&](int buf, int g) __attribute__((always_inline)) {
+    g = g < ngroups ? g : ngroups - 1;             // past the end: harmless re-fetch
+#pragma unroll
+    for (int jj = 0; jj < kCodeLoads; ++jj)
+      buffer_dma16(rc, lds + kCodeOff + buf * kCodeBuf + (2 * wave + jj) * 1024,
+                   (64 * (2 * (wave & 1) + jj) + lane) * sld, 16 * g);
+  };
+
+  // ---- read side: lane (row lane % 32, h = lane / 32); chunk c of the row at
+  // position (c + rot) mod 6, rot = (row >> 3) & 1 = (lane >> 3) & 1; step pp
+  // reads chunks 3 h + pp and 3 h + pp + 1 ----
+  const int rot = (lane >> 3) & 1;
+  auto pos = [&](int c) { return 16 * ((c + rot) % 6); };
+  int ba0[2], ba1[2], bb0[2], bb1[2];
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp) {
+    const int ra = (wm * Cfg::WM + (lane & 31)) * kTileB;
+    const int rb = kPlane + (wn * Cfg::WN + (lane & 31)) * kTileB;
+    ba0[pp] = opaque(ra + pos(3 * h + pp));
+    ba1[pp] = opaque(ra + pos(3 * h + pp + 1));
+    bb0[pp] = opaque(rb + pos(3 * h + pp));
+    bb1[pp] = opaque(rb + pos(3 * h + pp + 1));
+  }
+  auto rd16 = [&](int addr) __attribute__((always_inline)) {
+    return *reinterpret_cast<const v4i*>(lds + addr);
+  };
+  // a fragment: the two chunks in eight registers; the block is registers 0-5
+  // (step 0, even block) or 2-7 (step 1, odd block)
+  auto frag = [&](int a0, int a1, auto pp_c) __attribute__((always_inline)) {
+    const v8i v = __builtin_shufflevector(rd16(a0), rd16(a1), 0, 1, 2, 3, 4, 5, 6, 7);
+    if constexpr (decltype(pp_c)::value == 0)
+      return __builtin_shufflevector(v, v, 0, 1, 2, 3, 4, 5, -1, -1);
+    else
+      return __builtin_shufflevector(v, v, 2, 3, 4, 5, 6, 7, -1, -1);
+  };
+  // codes of (row, block b of the group): kCodeOff + buf * kCodeBuf + row * 16 + b;
+  // the lane's block of step pp in K tile q4 of the group is 4 q4 + 2 h + pp
+  int cur_a = opaque(kCodeOff + (wm * Cfg::WM + (lane & 31)) * 16 + 2 * h);
+  int cur_b = opaque(kCodeOff + (BM + wn * Cfg::WN + (lane & 31)) * 16 + 2 * h);
+  int nxt_a = opaque(cur_a + kCodeBuf), nxt_b = opaque(cur_b + kCodeBuf);
+
+  v16f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
+  v8i af[2][FM], bf[2][FN];
+  uint32_t sa[2][FM], sb[2][FN];
+
+  // fragments and codes of step pp of the K tile in ring slot s, K tile q4 of its
+  // code group, into register set z
+  // fragment f (A fragments, then B) of step pp of the K tile in ring slot s,
+  // K tile q4 of its code group, and its code
+  auto read_one = [&](int s, auto pp_c, int q4, int ca, int cb, int f, v8i (&fa)[FM],
+                      v8i (&fb)[FN], uint32_t (&xa)[FM], uint32_t (&xb)[FN])
+                      __attribute__((always_inline)) {
+    constexpr int pp = decltype(pp_c)::value;
+    if (f < FM) {
+      const int o = s * kSlot + f * 32 * kTileB;
+      fa[f] = frag(ba0[pp] + o, ba1[pp] + o, pp_c);
+      xa[f] = lds[ca + f * 32 * 16 + 4 * q4 + pp];
+    } else {
+      const int j = f - FM, o = s * kSlot + j * 32 * kTileB;
+      fb[j] = frag(bb0[pp] + o, bb1[pp] + o, pp_c);
+      xb[j] = lds[cb + j * 32 * 16 + 4 * q4 + pp];
+    }
+  };
+  auto read_step = [&](int s, auto pp_c, int q4, int ca, int cb, v8i (&fa)[FM], v8i (&fb)[FN],
+                       uint32_t (&xa)[FM], uint32_t (&xb)[FN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < FM + FN; ++f) read_one(s, pp_c, q4, ca, cb, f, fa, fb, xa, xb);
+  };
+  // the MFMAs of register set z, the reads of the next step (`next(f)`, one
+  // fragment before each of the first FM + FN MFMAs) interleaved in a fixed order
+  auto mfmas = [&](int z, auto&& next) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < FM * FN; ++m) {
+      const int i = m / FN, j = m % FN;
+      if (m < FM + FN) next(m);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          bf[z][j], af[z][i], acc[i][j], FB, FA, 0, (int)sb[z][j], 0, (int)sa[z][i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- prologue: code group 0 and K tiles 0 .. 2 in flight; wait for K tile 0 ----
+  copy_codes(0, 0);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) copy_tile(s, s);
+  FP8GEMM_WAIT_VM_LGKM0((NS - 1) * kLoads);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  read_step(0, std::integral_constant<int, 0>{}, 0, cur_a, cur_b, af[0], bf[0], sa[0], sb[0]);
+
+  // ---- K tile u (k = u mod 12 of the body: slot k mod 3, K tile k mod 4 of
+  // its code group) ----
+  auto ktile = [&](int u, auto k_c) __attribute__((always_inline)) {
+    constexpr int k = decltype(k_c)::value;
+    constexpr int slot = k % NS, q4 = k % kGroupTiles, nslot = (k + 1) % NS;
+    constexpr bool kNextGroup = q4 == kGroupTiles - 1;   // K tile u + 1 starts a group
+    // step 0: fragments of step 1 during the MFMAs of step 0
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xc07f);            // lgkmcnt(0): step 0's fragments in registers
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0, [&](int f) __attribute__((always_inline)) {
+      read_one(slot, std::integral_constant<int, 1>{}, q4, cur_a, cur_b, f, af[1], bf[1], sa[1],
+               sb[1]);
+    });
+    // step 1: K tile u + 1 landed for every wave; the slot of K tile u is free
+    // (copies issued after K tile u + 1's: K tile u + 2, and a code group when
+    // K tile u - 1 started one)
+    constexpr int kAfter = kLoads + (((k + kBody - 1) % kGroupTiles == 0) ? kCodeLoads : 0);
+    __builtin_amdgcn_sched_barrier(0);
+    FP8GEMM_WAIT_VM_LGKM0(kAfter);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (q4 == 0) copy_codes((u / kGroupTiles + 1) & 1, u / kGroupTiles + 1);
+    copy_tile(slot, u + NS);
+    // (after the last K tile these reads find a stale slot and are never used;
+    // a condition here would keep both register sets live across it)
+    mfmas(1, [&](int f) __attribute__((always_inline)) {
+      if constexpr (kNextGroup)
+        read_one(nslot, std::integral_constant<int, 0>{}, 0, nxt_a, nxt_b, f, af[0], bf[0],
+                 sa[0], sb[0]);
+      else
+        read_one(nslot, std::integral_constant<int, 0>{}, q4 + 1, cur_a, cur_b, f, af[0], bf[0],
+                 sa[0], sb[0]);
+    });
+    if constexpr (kNextGroup) {                    // the next group is current from K tile u + 1
+      const int ta = cur_a, tb = cur_b;
+      cur_a = nxt_a;
+      cur_b = nxt_b;
+      nxt_a = ta;
+      nxt_b = tb;
+    }
+  };
+  // whole bodies without branches (a branch between K tiles makes the compiler
+  // shuffle the fragment registers), then the K tiles left one by one
+  int u0 = 0;
+  for (; u0 + kBody <= nk; u0 += kBody) {
+    Unroll<0, kBody>::run([&](auto k_c) __attribute__((always_inline)) {
+      ktile(u0 + decltype(k_c)::value, k_c);
+    });
+  }
+  Unroll<0, kBody - 1>::run([&](auto k_c) __attribute__((always_inline)) {
+    constexpr int k = decltype(k_c)::value;
+    if (u0 + k < nk) ktile(u0 + k, k_c);
+  });
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0);                   // no copy may still target LDS
+  __builtin_amdgcn_s_barrier();
+
+  OutT* C = static_cast<OutT*>(p.C);
+  if (a_rows == BM && b_rows == BN)
+    epilogue_full_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, p.ldc, m0, p.M, n0, p.N, 1.0f, p.bias,
+                                               p.act, p.cs, p.ldcs);
+  else
+    epilogue_any_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, p.ldc, m0, p.M, n0, p.N, 1.0f, p.bias,
+                                              p.act, p.cs, p.ldcs);
+}
+
+}  // namespace big
+
 template <int FA, int FB, typename OutT, bool FUSED>
 hipError_t launch_typed(const GemmProblem& p, hipStream_t stream) {
+  if (choose_path_fp6(p.M, p.N, p.K, p.lda, p.ldb) == kPathTile256) {
+    const int tiles_m = (p.M + big::BM - 1) / big::BM, tiles_n = (p.N + big::BN - 1) / big::BN;
+    hipLaunchKernelGGL((big::fp6_big_kernel<FA, FB, kMx32, OutT, FUSED>),
+                       dim3(tiles_m * tiles_n), dim3(256), 0, stream, p, tiles_m, tiles_n);
+    return hipGetLastError();
+  }
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   hipLaunchKernelGGL((fp6_kernel<FA, FB, kMx32, OutT, FUSED>), dim3(tiles_m * tiles_n),
                      dim3(256), 0, stream, p, tiles_m, tiles_n);

@@ -130,4 +130,16 @@ inline GemmPath choose_path_kn(int64_t M, int64_t N, int64_t K, int64_t lda, int
   return big_tiles >= 256 ? kPathTile256 : kPathTile128;
 }
 
+// Path of the MXFP6 GEMM (K in elements, K % 128 == 0; lda, ldb in bytes): the
+// 256 x 256 tile once it gives a tile per CU and its 256-row spans fit 32-bit
+// offsets, else 128 x 128 tiles.
+inline GemmPath choose_path_fp6(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+  if (M <= 0 || N <= 0) return kPathNone;
+  const int64_t kb = K / 4 * 3;
+  const int64_t big_tiles = ((M + kBigTile - 1) / kBigTile) * ((N + kBigTile - 1) / kBigTile);
+  if (big_tiles >= 256 && spans_fit(kBigTile, lda, kb) && spans_fit(kBigTile, ldb, kb))
+    return kPathTile256;
+  return kPathTile128;
+}
+
 }  // namespace fp8gemm

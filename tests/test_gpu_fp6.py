@@ -159,3 +159,41 @@ def test_gemm_fp6_quantised_output():
     tol = O.tolerance(Cr, Ar, "bf16") - O.output_ulp(Cr, "bf16")
     ok = O.mx_output_within_bound(to_host(q), to_host(c), Cr, tol)
     assert ok.all(), f"{int((~ok).sum())} quantised outputs outside the bound"
+
+
+@pytest.mark.parametrize("fa,fb", [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2")])
+@pytest.mark.parametrize("shape", [(4096, 4096, 1024), (4100, 4160, 512)])
+def test_gemm_fp6_large_tile_sampled(fa, fb, shape):
+    """256 x 256 tiles (a tile per CU and more): full grid, and a grid cut by M
+    and N; sampled 128 x 128 blocks, first, last, inner and edge ones."""
+    M, N, K = shape
+    assert F.fp8gemm_run_path(M, N, K, K * 3 // 4, K * 3 // 4, F.FORMATS[fa], F.FORMATS[fb],
+                              2, 0) == "tile256"
+    qa, sa, qb, sb = _operands(M, N, K, fa, fb, seed=M + N + K)
+    announce("gemm fp6 256", fa, fb, shape)
+    C = _run(qa, sa, qb, sb, fa, fb)
+    torch.cuda.synchronize()
+    for r0, c0 in ((0, 0), (M - 128, N - 128), (1920, 2176), (256 * 15, N - 80), (M - 20, 384)):
+        ri = np.arange(r0, min(r0 + 128, M))
+        ci = np.arange(c0, min(c0 + 128, N))
+        Cr, Ar = O.gemm_reference(qa, sa, qb, sb, "mx32", rows=ri, cols=ci, fmt_a=fa, fmt_b=fb)
+        _assert(to_host(C[ri[0]:ri[-1] + 1, ci[0]:ci[-1] + 1]), Cr, Ar, "bf16",
+                f"{fa}x{fb} {shape} block {(r0, c0)}")
+
+
+@pytest.mark.parametrize("act", ["none", "gelu"])
+def test_gemm_fp6_large_tile_fused(act):
+    """The fused epilogue (bias, activation) and f16 output on 256 x 256 tiles,
+    over a whole output with cut tiles."""
+    M, N, K = 4128, 4096, 256
+    qa, sa, qb, sb = _operands(M, N, K, "e2m3", "e3m2", seed=21)
+    assert F.fp8gemm_run_path(M, N, K, K * 3 // 4, K * 3 // 4, F.FORMATS["e2m3"],
+                              F.FORMATS["e3m2"], 2, 1) == "tile256"
+    bias = np.random.default_rng(22).standard_normal(N).astype(np.float32)
+    announce("gemm fp6 256 fused", act)
+    C = to_host(_run(qa, sa, qb, sb, "e2m3", "e3m2", "f16", bias=bias, act=act))
+    rows = np.concatenate([np.arange(0, 64), np.arange(M - 96, M)])
+    cols = np.concatenate([np.arange(0, 64), np.arange(N - 64, N)])
+    Cr, Ar = O.gemm_reference(qa, sa, qb, sb, "mx32", rows=rows, cols=cols, fmt_a="e2m3",
+                              fmt_b="e3m2")
+    _assert(C[np.ix_(rows, cols)], Cr, Ar, "f16", f"fp6 256 {act}", bias=bias, act=act, cols=cols)
