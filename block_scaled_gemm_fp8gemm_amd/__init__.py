@@ -27,10 +27,12 @@ __all__ = [
     "Fp8GemmError", "SCALE_MODES", "OUT_DTYPES", "FORMATS", "ACTIVATIONS", "library_path",
     "load_library", "fp8gemm_quantize_workspace_size", "fp8gemm_quantize",
     "fp8gemm_quantize_ex", "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex",
+    "fp8gemm_run_mxout", "fp8gemm_qout_workspace_size", "fp8gemm_run_qout",
     "fp8gemm_workspace_size_kn", "fp8gemm_run_kn",
     "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run",
     "fp8gemm_run_path", "fp8gemm_run_kn_path", "PATHS", "fp8gemm_run_noalloc", "NOALLOC_SCRATCH_BYTES",
-    "fp8gemm_status_string", "fp8gemm_version", "quantize", "gemm", "grouped_gemm",
+    "fp8gemm_status_string", "fp8gemm_version", "quantize", "gemm", "gemm_mxout", "gemm_qout",
+    "grouped_gemm",
     "exported_symbols",
 ]
 
@@ -85,6 +87,9 @@ _SIGNATURES = {
                               _int, _p, _i64, _int, _p, _sz, _p]),
     "fp8gemm_run_mxout": (_int, [_i64, _i64, _i64, _p, _i64, _int, _p, _i64, _int, _int, _p, _p,
                                  _p, _int, _p, _i64, _p, _i64, _p, _sz, _p]),
+    "fp8gemm_qout_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
+    "fp8gemm_run_qout": (_int, [_i64, _i64, _i64, _p, _i64, _int, _p, _i64, _int, _int, _p, _p,
+                                _p, _int, _int, _int, _p, _i64, _p, _p, _sz, _p]),
     "fp8gemm_workspace_size_kn": (_sz, [_i64, _i64, _i64, _int]),
     "fp8gemm_run_kn": (_int, [_i64, _i64, _i64, _p, _i64, _int, _p, _i64, _int, _int, _p, _p, _p,
                               _int, _p, _i64, _int, _p, _sz, _p]),
@@ -181,6 +186,19 @@ def fp8gemm_run_mxout(M: int, N: int, K: int, A: int, lda: int, a_format: int, B
     _check("fp8gemm_run_mxout", load_library().fp8gemm_run_mxout(
         M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias, activation, C,
         ldc, c_scales, ldcs, workspace, workspace_bytes, stream))
+
+
+def fp8gemm_qout_workspace_size(M: int, N: int, K: int, mode: int) -> int:
+    return load_library().fp8gemm_qout_workspace_size(M, N, K, mode)
+
+
+def fp8gemm_run_qout(M: int, N: int, K: int, A: int, lda: int, a_format: int, B: int, ldb: int,
+                     b_format: int, mode: int, scale_a: int, scale_b: int, bias: int,
+                     activation: int, out_mode: int, c_format: int, C: int, ldc: int,
+                     c_scales: int, workspace: int, workspace_bytes: int, stream: int) -> None:
+    _check("fp8gemm_run_qout", load_library().fp8gemm_run_qout(
+        M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias, activation,
+        out_mode, c_format, C, ldc, c_scales, workspace, workspace_bytes, stream))
 
 
 def fp8gemm_workspace_size_kn(M: int, N: int, K: int, mode: int) -> int:
@@ -425,6 +443,46 @@ def gemm_mxout(qa, sa, qb, sb, mode: str = "tensor", out=None, out_scales=None,
                       out_scales.stride(0) if out_scales.dim() == 2 else max(N // 32, 1),
                       _ptr(workspace) if need else 0, workspace.numel() if need else 0,
                       _stream_handle(qa.device))
+    return out, out_scales
+
+
+def gemm_qout(qa, sa, qb, sb, mode: str = "tensor", out_mode: str = "rowwise",
+              out_fmt: str = "e4m3", out=None, out_scales=None, workspace=None,
+              fmt_a: str = "e4m3", fmt_b: str = "e4m3", bias=None, activation: str = "none"):
+    """(codes uint8 [M, N], scales float32 [M] or [1]): y = act(dq(qa) @ dq(qb) +
+    bias) quantised for the next layer with a fresh scale per row (out_mode
+    "rowwise") or for the whole output ("tensor"), by the rule of ``quantize``;
+    out_fmt "e4m3" or "e5m2"; N must be a multiple of 16.  Operands as ``gemm``
+    (qb [N, K], K contiguous).  The row scales are the scale_a of a row-wise GEMM
+    that takes the codes as its A operand."""
+    torch = _torch()
+    _require_cuda(qa, "qa", torch.uint8, 2)
+    _require_cuda(qb, "qb", torch.uint8, 2)
+    M, K = qa.shape
+    N, Kb = qb.shape
+    K, Kb = K * 8 // CODE_BITS[fmt_a], Kb * 8 // CODE_BITS[fmt_b]
+    if K != Kb:
+        raise ValueError("qa and qb must share K")
+    if out is None:
+        ldc = (N + 15) // 16 * 16
+        out = torch.empty((M, ldc), dtype=torch.uint8, device=qa.device)[:, :N]
+    om = SCALE_MODES[out_mode]
+    if out_scales is None:
+        out_scales = torch.empty(M if out_mode == "rowwise" else 1, dtype=torch.float32,
+                                 device=qa.device)
+    m = SCALE_MODES[mode]
+    need = fp8gemm_qout_workspace_size(M, N, K, m)
+    if need and workspace is None:
+        workspace = gemm_workspace(qa.device, need)
+    if bias is not None:
+        _require_cuda(bias, "bias", torch.float32, 1)
+        if bias.numel() != N:
+            raise ValueError("bias must have N elements")
+    fp8gemm_run_qout(M, N, K, _ptr(qa), qa.stride(0), FORMATS[fmt_a], _ptr(qb), qb.stride(0),
+                     FORMATS[fmt_b], m, _ptr(sa), _ptr(sb), _ptr(bias), ACTIVATIONS[activation],
+                     om, FORMATS[out_fmt], _ptr(out), out.stride(0), _ptr(out_scales),
+                     _ptr(workspace) if need else 0, workspace.numel() if need else 0,
+                     _stream_handle(qa.device))
     return out, out_scales
 
 

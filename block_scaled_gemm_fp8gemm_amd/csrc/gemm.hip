@@ -404,8 +404,18 @@ hipError_t FP8GEMM_LAUNCH_NAME(const GemmProblem& p, int mode, int out, hipStrea
   if (mode != kMx32) return hipErrorInvalidValue;
   if (out == kF16) return launch_any<kMx32, _Float16>(p, stream);
   if (out == kE4M3Mx) return launch_any<kMx32, uint8_t>(p, stream);
+  if (out == kF32Max) return launch_plan<kMx32, float, true>(p, stream);
   return launch_any<kMx32, __bf16>(p, stream);
 #else
+#if !FP8GEMM_KN
+  // the fp32 output with its maxima always takes the fused kernels (their
+  // epilogues carry the atomic maxima)
+  if (out == kF32Max) {
+    if (mode == kTensor) return launch_plan<kTensor, float, true>(p, stream);
+    if (mode == kRowwise) return launch_plan<kRowwise, float, true>(p, stream);
+    return launch_plan<kMx32, float, true>(p, stream);
+  }
+#endif
   if (out == kE4M3Mx) {
     if (mode == kTensor) return launch_any<kTensor, uint8_t>(p, stream);
     if (mode == kRowwise) return launch_any<kRowwise, uint8_t>(p, stream);

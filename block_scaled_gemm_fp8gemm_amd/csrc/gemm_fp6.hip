@@ -486,6 +486,7 @@ template <int FA, int FB>
 hipError_t launch_formats(const GemmProblem& p, int out, hipStream_t stream) {
   const bool fused = p.bias != nullptr || p.act != kActNone;
   if (out == kE4M3Mx) return launch_typed<FA, FB, uint8_t, true>(p, stream);
+  if (out == kF32Max) return launch_typed<FA, FB, float, true>(p, stream);
   if (out == kF16)
     return fused ? launch_typed<FA, FB, _Float16, true>(p, stream)
                  : launch_typed<FA, FB, _Float16, false>(p, stream);

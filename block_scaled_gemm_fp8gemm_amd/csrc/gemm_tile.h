@@ -1761,6 +1761,72 @@ __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][C
   }
 }
 
+// fp32 output of a full tile straight from registers, with the bias, the
+// activation ACT and the maxima of the staged epilogue's float output (cs as
+// uint32_t maxima; ldcs != 0: one per row, else one for the whole output).  A
+// lane stores each of its groups of four consecutive columns as one 16-byte
+// piece (lanes r and r + 32 together cover 32 bytes of row r per store, the
+// four groups of a block 128 bytes); its row maximum is its own values and its
+// partner lane's.  The bias is copied into a wave-private stretch of the free
+// ring first, as in epilogue_direct_bias.
+template <class Cfg, int MODE, int ACT>
+__device__ __forceinline__ void epilogue_direct_f32(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                                    uint8_t* lds, float* C, int64_t ldc, int m0,
+                                                    int n0, float tensor_scale, const float* bias,
+                                                    uint8_t* cs, int64_t ldcs) {
+  constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
+  const int h = lane >> 5;
+  const float* rsc = reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff);
+  const int nw = n0 + wn * Cfg::WN;                      // first column of this wave
+  static_assert(Cfg::kWaves * Cfg::WN * 4 <= Cfg::kSlots * Cfg::kSlotBytes, "bias fits the ring");
+  float* bl = reinterpret_cast<float*>(lds) + wave * Cfg::WN;
+#pragma unroll
+  for (int c = lane; c < Cfg::WN; c += 64) bl[c] = bias != nullptr ? bias[nw + c] : 0.0f;
+  uint32_t* amax = reinterpret_cast<uint32_t*>(cs);
+  float run = 0.0f;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = wm * Cfg::WM + i * 32 + (lane & 31);   // tile row of this lane
+    float fa = 1.0f;
+    if (MODE == kTensor) fa = tensor_scale;
+    if (MODE == kRowwise) fa = rsc[r];
+    float* crow = C + (int64_t)(m0 + r) * ldc + nw;
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = j * 32 + 8 * g + 4 * h;             // wave-local column of value 0
+        v4f fb{1.0f, 1.0f, 1.0f, 1.0f};
+        if (MODE == kRowwise) fb = *reinterpret_cast<const v4f*>(rsc + Cfg::BM + wn * Cfg::WN + c);
+        const v4f bv = *reinterpret_cast<const v4f*>(bl + c);
+        v4f v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = acc[i][j][4 * g + e] * fa;
+          if (MODE == kRowwise) x *= fb[e];
+          v[e] = activate(x + bv[e], ACT);
+          a = fmaxf(a, fabsf(v[e]));
+        }
+        *reinterpret_cast<v4f*>(crow + c) = v;
+      }
+    }
+    if (ldcs != 0) {
+      a = fmaxf(a, __shfl_xor(a, 32, 64));               // the other half of the row
+      if (h == 0 && a > 0.0f) atomicMax(amax + m0 + r, __float_as_uint(a));
+    } else {
+      run = fmaxf(run, a);
+    }
+  }
+  if (ldcs == 0) {
+    run = wave_max(run);
+    if (lane == 0 && run > 0.0f) atomicMax(amax, __float_as_uint(run));
+  }
+}
+
 // The output quantised for the next layer, straight from registers (interior
 // tiles without bias or activation): e4m3 codes with one E8M0 code per 32
 // consecutive columns of a row, by the quantisers' MX rule.  A 32 x 32 block j
@@ -1842,6 +1908,11 @@ __device__ __forceinline__ void epilogue_direct_q(const v16f (&acc)[Cfg::kFragM]
 // the quantisers), written to cs[m * ldcs + n / 32]; N % 32 == 0.  The 32
 // columns of a block are the four-column pieces of 8 consecutive lanes, so the
 // block maximum takes three xor-shuffles.
+// With OutT = float the fp32 result is stored as it is and its magnitudes are
+// folded into the maxima at cs (read as uint32_t: the bits of a non-negative
+// float order like the float): ldcs != 0, one maximum per row of C (the lanes
+// of a row reduce by xor-shuffles, then one atomic max per row and block of 32
+// rows); ldcs == 0, one maximum for the whole output (one atomic per wave).
 template <class Cfg, int MODE, typename OutT>
 __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                uint8_t* lds, OutT* C, int64_t ldc, int m0,
@@ -1849,6 +1920,7 @@ __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cf
                                                const float* bias, int act,
                                                uint8_t* cs = nullptr, int64_t ldcs = 0) {
   constexpr bool kQ = std::is_same<OutT, uint8_t>::value;
+  constexpr bool kF = std::is_same<OutT, float>::value;
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   constexpr int kPitch = Cfg::WN + 4;                    // staged fp32 row (+16 bytes)
   constexpr int kPiecesPerRow = Cfg::WN / 4;
@@ -1857,7 +1929,7 @@ __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cf
                 "fp32 staging fits in the ring");
   static_assert((32 * kPiecesPerRow) % 64 == 0, "whole store instructions");
   static_assert(64 % kPiecesPerRow == 0, "a lane keeps its columns over the store loop");
-  static_assert(sizeof(OutT) == 2 || kQ, "16-bit outputs or e4m3 codes");
+  static_assert(sizeof(OutT) == 2 || kQ || kF, "16-bit or fp32 outputs or e4m3 codes");
   static_assert(!kQ || kPiecesPerRow % 8 == 0, "32-column blocks inside one lane group");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -1874,6 +1946,8 @@ __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cf
     for (int e = 0; e < 4; ++e) bv[e] = n + e < N ? bias[n + e] : 0.0f;
   }
   const float* rsc = reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff);
+  uint32_t* amax = reinterpret_cast<uint32_t*>(cs);      // kF: the maxima
+  float run = 0.0f;                                      // kF, one maximum: this wave's
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int r = lane & 31;
@@ -1918,6 +1992,28 @@ __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cf
           *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(C) + (int64_t)m * ldc + n) = w;
           if ((lane & 7) == 0) cs[(int64_t)m * ldcs + (n >> 5)] = (uint8_t)code;
         }
+      } else if constexpr (kF) {
+        float a = 0.0f;
+        if (m < m_end) {
+          float* dst = reinterpret_cast<float*>(C) + (int64_t)m * ldc + n;
+          if (n + 4 <= N) {
+            *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};
+            a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+          } else {
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) {
+                dst[e] = v[e];
+                a = fmaxf(a, fabsf(v[e]));
+              }
+          }
+        }
+        if (ldcs != 0) {
+          a = group_max(a, kPiecesPerRow);               // the lanes of row m
+          if (lane % kPiecesPerRow == 0 && m < m_end && a > 0.0f)
+            atomicMax(amax + m, __float_as_uint(a));
+        } else {
+          run = fmaxf(run, a);
+        }
       } else if (m < m_end) {
         OutT* dst = C + (int64_t)m * ldc + n;
         if (n + 4 <= N) {
@@ -1930,6 +2026,12 @@ __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cf
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);                  // reads done before the next block
   }
+  if constexpr (kF) {
+    if (ldcs == 0) {
+      run = wave_max(run);
+      if (lane == 0 && run > 0.0f) atomicMax(amax, __float_as_uint(run));
+    }
+  }
 }
 
 // Epilogue of a full interior tile (every row and column valid): straight from
@@ -1940,7 +2042,20 @@ __device__ __forceinline__ void epilogue_full_tile(const v16f (&acc)[Cfg::kFragM
                                                    int m_end, int n0, int N, float tensor_scale,
                                                    const float* bias, int act, uint8_t* cs,
                                                    int64_t ldcs) {
-  if constexpr (FUSED && !std::is_same<OutT, uint8_t>::value) {
+  if constexpr (std::is_same<OutT, float>::value) {
+    if (act == kActGelu)
+      epilogue_direct_f32<Cfg, MODE, kActGelu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias, cs,
+                                               ldcs);
+    else if (act == kActSilu)
+      epilogue_direct_f32<Cfg, MODE, kActSilu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias, cs,
+                                               ldcs);
+    else if (act == kActRelu)
+      epilogue_direct_f32<Cfg, MODE, kActRelu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias, cs,
+                                               ldcs);
+    else
+      epilogue_direct_f32<Cfg, MODE, kActNone>(acc, lds, C, ldc, m0, n0, tensor_scale, bias, cs,
+                                               ldcs);
+  } else if constexpr (FUSED && !std::is_same<OutT, uint8_t>::value) {
     epilogue_direct<Cfg, MODE, OutT, true>(acc, lds, C, ldc, m0, n0, tensor_scale, 0, bias, act);
   } else if constexpr (FUSED) {
     epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act,
@@ -1963,7 +2078,7 @@ __device__ __forceinline__ void epilogue_any_tile(const v16f (&acc)[Cfg::kFragM]
                                                   int m_end, int n0, int N, float tensor_scale,
                                                   const float* bias, int act, uint8_t* cs,
                                                   int64_t ldcs) {
-  if constexpr (FUSED || std::is_same<OutT, uint8_t>::value)
+  if constexpr (FUSED || sizeof(OutT) != 2)
     epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act,
                                     cs, ldcs);
   else

@@ -288,6 +288,50 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const float* __restr
   }
 }
 
+// ---- the requantised GEMM output: maxima from the GEMM epilogue, then encode ---
+// The GEMM kernels stored y in fp32 and folded |y| into amax (per row or one for
+// the output; zeroed by zero_words_kernel before the GEMM); this pass derives
+// the scales by the per-tensor / row-wise rule above and encodes.  One
+// wavefront per row (rows dealt to wavefronts in turn), 1024 columns per step
+// as in load_unit.
+template <int FMT, bool PER_ROW>
+__global__ __launch_bounds__(kThreads) void requant_kernel(const float* __restrict__ y, int rows,
+                                                           int n, int64_t ldy,
+                                                           const uint32_t* __restrict__ amax,
+                                                           uint8_t* __restrict__ q, int64_t ldq,
+                                                           float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int w0 = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int nw = gridDim.x * kWaves;
+  float s = 1.0f;
+  if constexpr (!PER_ROW) {
+    const float m = __uint_as_float(amax[0]);
+    s = (m == 0.0f) ? 1.0f : m / elem_max<FMT>();
+    if (blockIdx.x == 0 && threadIdx.x == 0) scales[0] = s;
+  }
+  for (int r = w0; r < rows; r += nw) {
+    if constexpr (PER_ROW) {
+      const float m = __uint_as_float(amax[r]);
+      s = (m == 0.0f) ? 1.0f : m / elem_max<FMT>();
+      if (lane == 0) scales[r] = s;
+    }
+    const float* yr = y + (int64_t)r * ldy;
+    uint8_t* qr = q + (int64_t)r * ldq;
+    for (int c0 = 0; c0 < n; c0 += 1024) {
+      uint32_t w[4];
+      encode_unit_div<FMT>(load_unit(yr, c0, n, lane), s, w);
+      store_codes(qr, c0, n, lane, w);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void zero_words_kernel(uint32_t* __restrict__ p,
+                                                              int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * kThreads)
+    p[i] = 0u;
+}
+
 int grid_for(uint64_t work_items, int per_block, int cap) {
   uint64_t g = (work_items + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -344,6 +388,19 @@ hipError_t quantize_mx_fmt(const float* x, int64_t rows, int64_t k, int64_t ldx,
   return hipGetLastError();
 }
 
+template <int FMT>
+hipError_t requant_fmt(const float* y, int64_t rows, int64_t n, int64_t ldy, const uint32_t* amax,
+                       bool per_row, uint8_t* q, int64_t ldq, float* scales, hipStream_t stream) {
+  const int grid = grid_for((uint64_t)rows, kWaves, 16384);
+  if (per_row)
+    hipLaunchKernelGGL((requant_kernel<FMT, true>), dim3(grid), dim3(kThreads), 0, stream, y,
+                       (int)rows, (int)n, ldy, amax, q, ldq, scales);
+  else
+    hipLaunchKernelGGL((requant_kernel<FMT, false>), dim3(grid), dim3(kThreads), 0, stream, y,
+                       (int)rows, (int)n, ldy, amax, q, ldq, scales);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quantize_tensor(const float* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
@@ -368,6 +425,20 @@ hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t k, int64_t l
   if (fmt == kE2M3) return quantize_mx_fmt<kE2M3>(x, rows, k, ldx, q, ldq, codes, stream);
   if (fmt == kE3M2) return quantize_mx_fmt<kE3M2>(x, rows, k, ldx, q, ldq, codes, stream);
   return quantize_mx_fmt<kE4M3>(x, rows, k, ldx, q, ldq, codes, stream);
+}
+
+hipError_t launch_zero_words(uint32_t* p, int64_t count, hipStream_t stream) {
+  const int grid = grid_for((uint64_t)count, kThreads, 1024);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(grid), dim3(kThreads), 0, stream, p, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant(const float* y, int64_t rows, int64_t n, int64_t ldy,
+                          const uint32_t* amax, bool per_row, uint8_t* q, int64_t ldq,
+                          float* scales, int fmt, hipStream_t stream) {
+  if (fmt == kE5M2)
+    return requant_fmt<kE5M2>(y, rows, n, ldy, amax, per_row, q, ldq, scales, stream);
+  return requant_fmt<kE4M3>(y, rows, n, ldy, amax, per_row, q, ldq, scales, stream);
 }
 
 }  // namespace fp8gemm

@@ -3,8 +3,9 @@
 A plain, slow, float64 reference of what the GPU path computes: e4m3fn and E8M0
 decoding by table, round-to-nearest-even encoding by table search, per-tensor,
 row-wise and 32-element microscaled quantisation, the scaled GEMM with its
-error bound, the fused bias-and-activation epilogue, and the grouped
-(mixture-of-experts) form.
+error bound, the fused bias-and-activation epilogue, the output quantised for
+the next layer (MX blocks, or a fresh per-tensor / per-row scale), and the
+grouped (mixture-of-experts) form.
 
 Only ``tests/``, the smoke check in ``__graft_entry__`` and the CPU-baseline
 leg of ``bench.py`` may import this package.  The library under
@@ -37,7 +38,8 @@ from .formats import (E2M1_DECODE, E2M1_MAX, E2M3_DECODE, E2M3_MAX, E3M2_DECODE,
 from .quant import quantize, quantize_mx, quantize_rowwise, quantize_tensor
 from .gemm import (ACT_LIPSCHITZ, activation, dequantize, epilogue_reference,
                    epilogue_tolerance, gemm_reference, grouped_reference, mx_output_reference,
-                   mx_output_within_bound, output_ulp, tolerance, within_bound, round_to_output)
+                   mx_output_within_bound, output_ulp, scaled_output_reference,
+                   scaled_output_within_bound, tolerance, within_bound, round_to_output)
 
 __all__ = [
     "E2M1_DECODE", "E2M1_MAX", "decode_e2m1", "encode_e2m1", "pack_fp4", "unpack_fp4",
@@ -49,4 +51,5 @@ __all__ = [
     "dequantize", "gemm_reference", "grouped_reference", "output_ulp", "tolerance",
     "within_bound", "round_to_output", "ACT_LIPSCHITZ", "activation", "epilogue_reference",
     "epilogue_tolerance", "mx_output_reference", "mx_output_within_bound",
+    "scaled_output_reference", "scaled_output_within_bound",
 ]

@@ -266,3 +266,79 @@ def mx_output_within_bound(q, codes, out_ref, tol_y) -> np.ndarray:
     c = np.asarray(codes, np.int64)
     ok_code = (c >= np.minimum(lo, mx_scale_code(amax.astype(np.float32)))) & (c <= hi)
     return ok & np.repeat(ok_code, 32, axis=1)
+
+
+# ---- output quantised for the next layer with a fresh per-tensor / per-row scale
+# The same saving of a C round trip, with the output's scale chosen afresh from
+# y itself: one for the whole output or one per row (the scale_a of a row-wise
+# GEMM that takes the codes as its A operand).  Reading: y = act(C + bias) is
+# rounded to binary32 and quantised with the per-tensor or row-wise rule of
+# ``quant.quantize_tensor`` / ``quant.quantize_rowwise``.
+
+def scaled_output_reference(out_ref: np.ndarray, out_mode: str, fmt: str = "e4m3"):
+    """(codes uint8 [M,N], scales float32 [M] or ()): the row-wise ("rowwise") or
+    per-tensor ("tensor") quantisation of the binary32 rounding of the exact
+    epilogue output."""
+    from .quant import quantize_rowwise, quantize_tensor
+    y32 = np.asarray(out_ref, np.float64).astype(np.float32)
+    if out_mode == "rowwise":
+        return quantize_rowwise(y32, fmt)
+    if out_mode == "tensor":
+        return quantize_tensor(y32, fmt)
+    raise ValueError(f"unknown output scale mode {out_mode!r}")
+
+
+_SPACING = {"e4m3": (3, -6), "e5m2": (2, -14)}      # mantissa bits, smallest normal exponent
+
+
+def _half_spacing(x: np.ndarray, fmt: str) -> np.ndarray:
+    """Half the spacing of the format's values at magnitudes x (the subnormal
+    spacing below the smallest normal)."""
+    mbits, emin = _SPACING[fmt]
+    x = np.abs(np.asarray(x, np.float64))
+    _, ex = np.frexp(np.maximum(x, 2.0 ** emin))
+    return np.ldexp(1.0, (ex.astype(np.int64) - 1) - mbits - 1)
+
+
+def scaled_output_within_bound(q, scales, out_ref, tol_y, out_mode: str,
+                               fmt: str = "e4m3") -> np.ndarray:
+    """Which outputs of a result quantised with fresh scales (q [M,N] codes,
+    scales float [M] for "rowwise" or one value for "tensor") are acceptable
+    against the exact output out_ref with tolerance tol_y.
+
+    A computed y' lies within tol_y of out_ref, its maximum magnitude amax'
+    between those of |out_ref| - tol_y and |out_ref| + tol_y (over the row or the
+    whole output), so its scale fl32(amax' / max) lies between the scales of
+    those two bounds (binary32 rounding is monotone), or is 1 where the lower
+    bound is 0.  A code then dequantises (value times the scale s) to within
+    tol_y, half a spacing of the format at the scaled magnitude (|out_ref| +
+    tol_y) / s, the binary32 rounding of the quotient (2^-24 relative) and, for
+    values beyond max * s, the saturation distance, of out_ref.  The mask is
+    False for every output of a row (or of the output) whose scale is out of
+    range."""
+    from .formats import FORMATS
+    y = np.asarray(out_ref, np.float64)
+    t = np.asarray(tol_y, np.float64) * np.ones_like(y)
+    fmax = float(FORMATS[fmt]["max"])
+    a = np.abs(y)
+    lo_v = np.maximum(a - t, 0.0)
+    hi_v = a + t
+    if out_mode == "rowwise":
+        lo, hi = lo_v.max(axis=1), hi_v.max(axis=1)
+        s = np.asarray(scales, np.float64).reshape(-1)
+        sb = s[:, None] * np.ones_like(y)
+    elif out_mode == "tensor":
+        lo, hi = np.asarray(lo_v.max()), np.asarray(hi_v.max())
+        s = np.asarray(scales, np.float64).reshape(())
+        sb = s * np.ones_like(y)
+    else:
+        raise ValueError(f"unknown output scale mode {out_mode!r}")
+    s_lo = (lo.astype(np.float32) / np.float32(fmax)).astype(np.float64)
+    s_hi = (hi.astype(np.float32) / np.float32(fmax)).astype(np.float64)
+    ok_s = ((s >= s_lo) & (s <= s_hi) & (s > 0)) | ((lo == 0) & (s == 1.0))
+    dq = FORMATS[fmt]["decode"](np.asarray(q, np.uint8)) * sb
+    allow = (t + _half_spacing(hi_v / sb, fmt) * sb + 2.0 ** -24 * hi_v
+             + np.maximum(hi_v - fmax * sb, 0.0))
+    ok = np.abs(dq - y) <= allow
+    ok_s = ok_s[:, None] if out_mode == "rowwise" else ok_s
+    return ok & ok_s

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {
         "fp8gemm_quantize_workspace_size", "fp8gemm_quantize", "fp8gemm_quantize_ex",
         "fp8gemm_workspace_size", "fp8gemm_run", "fp8gemm_run_ex", "fp8gemm_workspace_size_kn",
-        "fp8gemm_run_kn", "fp8gemm_run_mxout",
+        "fp8gemm_run_kn", "fp8gemm_run_mxout", "fp8gemm_qout_workspace_size", "fp8gemm_run_qout",
         "fp8gemm_grouped_workspace_size", "fp8gemm_grouped_run", "fp8gemm_grouped_run_ex",
         "fp8gemm_run_path", "fp8gemm_run_kn_path", "fp8gemm_run_noalloc", "fp8gemm_status_string",
         "fp8gemm_version"}
@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert F.fp8gemm_version() == 180
+    assert F.fp8gemm_version() == 190
     for code, name in [(0, "FP8GEMM_SUCCESS"), (1, "FP8GEMM_ERROR_INVALID_VALUE"),
                        (2, "FP8GEMM_ERROR_MISALIGNED"), (3, "FP8GEMM_ERROR_NOT_SUPPORTED"),
                        (4, "FP8GEMM_ERROR_WORKSPACE"), (5, "FP8GEMM_ERROR_LAUNCH"),
@@ -284,6 +284,40 @@ def test_mxout_validation(lib):
     assert run(ldc=32) == INVALID                 # ldc < N
     assert run(C=P3 + 4100) == MISALIGNED
     assert run(mode=7) == INVALID
+
+
+def test_qout_validation(lib):
+    """fp8gemm_run_qout: codes with a fresh per-tensor / per-row scale; every check
+    runs before any HIP call (a failing one means nothing was enqueued)."""
+    M, N, K = 64, 64, 128
+    need = F.fp8gemm_qout_workspace_size(M, N, K, 1)
+
+    def run(N=N, C=P3 + 4096, ldc=64, cs=P3 + 65536, om=1, cf=0, ws=0x100000, wsb=need, **kw):
+        return lib.fp8gemm_run_qout(kw.get("M", M), N, K, P, 128, kw.get("fa", 0), P2, 128,
+                                    kw.get("fb", 0), kw.get("mode", 1), P3, P3 + 256, 0,
+                                    kw.get("act", 0), om, cf, C, ldc, cs, ws, wsb, None)
+    assert run(M=0) == SUCCESS and run(N=0, ldc=16) == SUCCESS
+    assert run(om=2) == INVALID                   # MX blocks: fp8gemm_run_mxout
+    assert run(om=5) == INVALID and run(cf=9) == INVALID
+    assert run(cf=4) == NOT_SUPPORTED             # FP4 codes out
+    assert run(cs=0) == INVALID
+    assert run(C=0) == INVALID
+    assert run(N=40, ldc=48) == NOT_SUPPORTED     # N % 16
+    assert run(ldc=72) == MISALIGNED              # byte rows of codes: ldc % 16
+    assert run(ldc=32) == INVALID                 # ldc < N
+    assert run(C=P3 + 4100) == MISALIGNED
+    assert run(cs=P3 + 65538) == MISALIGNED
+    assert run(ws=0) == WORKSPACE and run(wsb=need - 1) == WORKSPACE
+    assert run(ws=0x100008) == MISALIGNED
+    assert run(mode=7) == INVALID and run(act=9) == INVALID
+    assert run(fa=4) == NOT_SUPPORTED             # FP4 pairs with FP4 only
+    # the workspace: the GEMM's own (at least its counters), M maxima, M x N fp32
+    for shape, mode in [((64, 64, 128), 1), ((128, 4096, 4096), 2), ((8192, 8192, 8192), 0)]:
+        m, n, k = shape
+        q = F.fp8gemm_qout_workspace_size(m, n, k, mode)
+        g = max(F.fp8gemm_workspace_size(m, n, k, mode), 4096)
+        assert q >= g + 4 * m + 4 * m * n and q <= g + 4 * m + 4 * m * (n + 63) + 512
+    assert F.fp8gemm_qout_workspace_size(0, 64, 128, 1) == 0
 
 
 def test_row_major_b_validation(lib):
