@@ -166,6 +166,13 @@ def gemm_bytes_mxout(w, code_bytes: float = 1.0) -> int:
     return gemm_bytes(w, code_bytes) - 2 * w.M * w.N + w.M * w.N + w.M * (w.N // 32)
 
 
+def gemm_bytes_qout(w, code_bytes: float = 1.0) -> int:
+    """The same with the output as e4m3 codes plus fp32 scales (one per row; the
+    per-tensor case counts the same): the result's own bytes, not the fp32 y the
+    implementation writes and reads back between its two kernels."""
+    return gemm_bytes(w, code_bytes) - 2 * w.M * w.N + w.M * w.N + 4 * w.M
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -228,9 +235,12 @@ def main():
                          "MXFP4; e2m3 or e3m2 in any pairing for MXFP6, dense mx32 workloads "
                          "with K % 128 == 0)")
     ap.add_argument("--epilogue", default="none", choices=["none", "bias", "bias+relu",
-                                                           "bias+gelu", "bias+silu", "mxout"],
+                                                           "bias+gelu", "bias+silu", "mxout",
+                                                           "qrow", "qtensor"],
                     help="fused epilogue of the GEMM (dense only); mxout: the output quantised "
-                         "for the next layer (e4m3 + E8M0 per 32 columns)")
+                         "for the next layer (e4m3 + E8M0 per 32 columns); qrow / qtensor: "
+                         "quantised with a fresh fp32 scale per row / for the whole output "
+                         "(the timed GEMM then includes the requantising kernel)")
     ap.add_argument("--b-layout", default="nk", choices=["nk", "kn"],
                     help="kn: B row-major [K, N] (fp8gemm_run_kn, its transposing copy timed "
                          "with the GEMM); B is then quantised once before timing (resident "
@@ -263,12 +273,13 @@ def main():
     fmt_a, fmt_b = args.formats.split(",")
     act = args.epilogue.split("+")[1] if "+" in args.epilogue else "none"
     mxout = args.epilogue == "mxout"
+    qout = args.epilogue in ("qrow", "qtensor")
     kn = args.b_layout == "kn"
-    if kn and (w.groups or mxout):
+    if kn and (w.groups or mxout or qout):
         raise SystemExit("--b-layout kn applies to the dense workloads with a 16-bit output")
-    use_bias = args.epilogue not in ("none", "mxout")
+    use_bias = args.epilogue not in ("none", "mxout", "qrow", "qtensor")
     fp4 = "e2m1" in (fmt_a, fmt_b)
-    if w.groups and ((args.formats != "e4m3,e4m3" and not fp4) or use_bias or mxout):
+    if w.groups and ((args.formats != "e4m3,e4m3" and not fp4) or use_bias or mxout or qout):
         raise SystemExit("--epilogue applies to the dense workloads; the grouped one takes "
                          "--formats e2m1,e2m1 only")
     if fp4 and w.groups:       # MXFP4 experts: the same shapes and inputs with MX scales
@@ -326,6 +337,12 @@ def main():
     if mxout:
         Cq = torch.empty((w.M, w.N), dtype=torch.uint8, device=dev)
         Cs = torch.empty((w.M, w.N // 32), dtype=torch.uint8, device=dev)
+    if qout:
+        qmode = "rowwise" if args.epilogue == "qrow" else "tensor"
+        Cq = torch.empty((w.M, w.N), dtype=torch.uint8, device=dev)
+        Cs = torch.empty(w.M if qmode == "rowwise" else 1, dtype=torch.float32, device=dev)
+        ws_q = torch.zeros(F.fp8gemm_qout_workspace_size(w.M, w.N, w.K, mode_id),
+                           dtype=torch.uint8, device=dev)
     bias = None
     if use_bias:
         import numpy as np
@@ -344,6 +361,9 @@ def main():
                    bias=bias, activation=act, b_layout="kn")
         elif mxout:
             F.gemm_mxout(qa, sa, qb, sb, w.mode, out=Cq, out_scales=Cs, fmt_a=fmt_a, fmt_b=fmt_b)
+        elif qout:
+            F.gemm_qout(qa, sa, qb, sb, w.mode, qmode, out=Cq, out_scales=Cs, workspace=ws_q,
+                        fmt_a=fmt_a, fmt_b=fmt_b)
         else:
             F.gemm(qa, sa, qb, sb, w.mode, w.out, out=C, fmt_a=fmt_a, fmt_b=fmt_b, bias=bias,
                    activation=act)
@@ -400,10 +420,10 @@ def main():
     # HBM-bound shapes (arithmetic intensity below the MFMA/HBM ridge): the roofline
     # is bytes over time; a cold-cache rate is measured as well, cycling the GEMM
     # over enough distinct operand copies (>= 512 MiB) that none is cache resident
-    gbytes = (gemm_bytes_mxout if mxout else gemm_bytes)(w, code_bytes)
+    gbytes = (gemm_bytes_mxout if mxout else gemm_bytes_qout if qout else gemm_bytes)(w, code_bytes)
     hbm_bound = flops / gbytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     cold = None
-    if not w.groups and not mxout and not kn and rows_b * kq >= (4 << 20):
+    if not w.groups and not mxout and not qout and not kn and rows_b * kq >= (4 << 20):
         # >= 512 MiB of distinct operands (at least three sets): no launch finds
         # its operands in the 256 MB Infinity Cache
         nsets = max(3, -(-(512 << 20) // (rows_b * kq + w.M * kq)))
@@ -493,7 +513,10 @@ def main():
                    "out": w.out, "groups": w.groups, "formats": [fmt_a, fmt_b],
                    "epilogue": args.epilogue, "b_layout": args.b_layout,
                    "step": "quantize A + GEMM (row-major B resident, transposing copy inside "
-                           "the GEMM call)" if kn else "quantize A + quantize B + GEMM"},
+                           "the GEMM call)" if kn else
+                           "quantize A + quantize B + GEMM (zero the maxima, GEMM storing fp32 y "
+                           "with atomic maxima, requantise)" if qout else
+                           "quantize A + quantize B + GEMM"},
         "roofline": roofline,
         "kernels": {
             "gemm": {"ms": round(gemm_ms, 5), "ms_median": round(gemm_med, 5),

@@ -369,7 +369,7 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
     qb is [N, K] (K contiguous, b_layout "nk") or [K, N] (N contiguous, "kn"; its
     MX codes sb then [K/32, N]); fmt_a / fmt_b: element formats of the codes
     ("e4m3" or "e5m2"; or "e2m1" for both, FP4 packed two per byte so that qa is
-    [M, K/2] and qb [N, K/2], mode "mx32"; or "e2m3" / "e3m2" for both, FP6 with
+    [M, K/2] and qb [N, K/2] (or [K, N/2] with b_layout "kn", N even), mode "mx32"; or "e2m3" / "e3m2" for both, FP6 with
     four codes in three bytes, [M, 3K/4] and [N, 3K/4], mode "mx32", K % 128 == 0);
     bias: float32 [N] CUDA tensor or None;
     activation: "none", "relu", "gelu" or "silu".
@@ -378,12 +378,13 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
     _require_cuda(qa, "qa", torch.uint8, 2)
     _require_cuda(qb, "qb", torch.uint8, 2)
     M, K = qa.shape
-    if b_layout == "kn":
+    K = K * 8 // CODE_BITS[fmt_a]           # packed codes: K counts elements
+    if b_layout == "kn":                    # packed FP4 B: two codes per byte along N
         Kb, N = qb.shape
+        N = N * 8 // CODE_BITS[fmt_b]
     else:
         N, Kb = qb.shape
-    # packed codes: K counts elements
-    K, Kb = K * 8 // CODE_BITS[fmt_a], Kb * 8 // CODE_BITS[fmt_b]
+        Kb = Kb * 8 // CODE_BITS[fmt_b]
     if K != Kb:
         raise ValueError("qa and qb must share K")
     tdt = torch.float16 if out_dtype == "f16" else torch.bfloat16

@@ -436,11 +436,14 @@ fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A,
   if (!valid_mode(mode) || !valid_out(out_dtype) || !valid_format(a_format) ||
       !valid_format(b_format) || !valid_act(activation) || M < 0 || N < 0 || K <= 0)
     return FP8GEMM_ERROR_INVALID_VALUE;
-  if (code_bits(a_format) < 8 || code_bits(b_format) < 8)
-    return FP8GEMM_ERROR_NOT_SUPPORTED;          // no transposing copy of packed FP4 / FP6
+  // FP8 pairs, or FP4 with FP4 (MX only; row-major FP4 B packs two codes per byte
+  // along N); no FP6 here
+  const bool fp4 = a_format == FP8GEMM_FORMAT_E2M1 || b_format == FP8GEMM_FORMAT_E2M1;
+  if (fp4 && (a_format != b_format || mode != kMx32)) return FP8GEMM_ERROR_NOT_SUPPORTED;
+  if (is_fp6(a_format) || is_fp6(b_format)) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (M == 0 || N == 0) return FP8GEMM_SUCCESS;
   if (!B || !scale_b) return FP8GEMM_ERROR_INVALID_VALUE;
-  if (ldb < N) return FP8GEMM_ERROR_INVALID_VALUE;
+  if (fp4 ? ldb * 2 < N : ldb < N) return FP8GEMM_ERROR_INVALID_VALUE;
   if (N > kMaxDim || K > kMaxDim || ldb > kMaxDim) return FP8GEMM_ERROR_NOT_SUPPORTED;
   if (K % 16 != 0 || (mode == kMx32 && K % 32 != 0)) return FP8GEMM_ERROR_NOT_SUPPORTED;
   // one transpose workgroup per 64 x 64 tile: keep the grid below 2^31
@@ -489,12 +492,14 @@ fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A,
   const size_t gemm_bytes = fp8gemm_workspace_size(M, N, K, mode);
   // the GEMM's checks run first, on the transposed operands, so a call they
   // reject enqueues nothing
-  const int64_t ldbt = K;                     // K % 16 == 0: 16-byte rows
+  const int64_t ldbt = fp4 ? K / 2 : K;       // K % 16 == 0 (FP4: K % 32): 16-byte rows
   fp8gemm_status st = check_gemm_common(M, N, K, A, lda, bt, ldbt, mode, scale_a,
-                                        mode == kMx32 ? codes_t : scale_b, C, ldc, out_dtype);
+                                        mode == kMx32 ? codes_t : scale_b, C, ldc, out_dtype,
+                                        fp4 ? 4 : 8);
   if (st != FP8GEMM_SUCCESS) return st;
   if (bias && !aligned(bias, 4)) return FP8GEMM_ERROR_MISALIGNED;
-  hipError_t e = fp8gemm::launch_transpose_u8(B, ldb, bt, ldbt, K, N, s);
+  hipError_t e = fp4 ? fp8gemm::launch_transpose_u4(B, ldb, bt, ldbt, K, N, s)
+                     : fp8gemm::launch_transpose_u8(B, ldb, bt, ldbt, K, N, s);
   if (e != hipSuccess) return FP8GEMM_ERROR_LAUNCH;
   const void* sb = scale_b;
   if (mode == kMx32) {

@@ -116,6 +116,10 @@ hipError_t launch_zero_words(uint32_t* p, int64_t count, hipStream_t stream);
 // ldo >= rows bytes): the row-major B operand and its MX codes made K-contiguous.
 hipError_t launch_transpose_u8(const uint8_t* in, int64_t ldi, uint8_t* out, int64_t ldo,
                                int64_t rows, int64_t cols, hipStream_t stream);
+// The same for packed FP4 codes (two per byte along a row, low nibble first):
+// element (r, c) at in[r * ldi + c / 2] goes to out[c * ldo + r / 2]; rows even.
+hipError_t launch_transpose_u4(const uint8_t* in, int64_t ldi, uint8_t* out, int64_t ldo,
+                               int64_t rows, int64_t cols, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const GroupedProblem& p, int mode, int out, hipStream_t stream);
 // MXFP4 experts (mode kMx32 only; K, lda, ldb and stride_b count bytes).

@@ -7,7 +7,8 @@
 // A workgroup transposes a 64 x 64 byte tile through LDS: 256 threads read it as
 // 64 rows of four 16-byte pieces, and write the transposed tile the same way
 // (each thread gathers its 16 output bytes from one LDS column).  Tiles cut by the
-// matrix edge move byte by byte, guarded.
+// matrix edge move byte by byte, guarded.  Packed FP4 codes (two per byte) take a
+// nibble transpose with the same tile shape in elements.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -61,7 +62,60 @@ __global__ __launch_bounds__(256) void transpose_u8_kernel(const uint8_t* __rest
   }
 }
 
+// Nibble transpose of a packed FP4 matrix: in holds rows x cols 4-bit codes, two
+// per byte along a row (element (r, c) in byte in[r * ldi + c / 2], low nibble for
+// even c); out receives the cols x rows transpose packed the same way (element
+// (c, r) in byte out[c * ldo + r / 2]).  rows % 2 == 0, so every output byte takes
+// two whole input rows.  A workgroup moves a 64 x 64 element tile: 256 threads
+// read it as 64 rows of four 8-byte pieces into LDS, then each thread assembles 8
+// output bytes (16 consecutive input rows of one column) from one LDS column.
+__global__ __launch_bounds__(256) void transpose_u4_kernel(const uint8_t* __restrict__ in,
+                                                           int64_t ldi, uint8_t* __restrict__ out,
+                                                           int64_t ldo, int rows, int cols,
+                                                           int tiles_c) {
+  constexpr int kB = kT / 2;                        // bytes per tile row
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kT * (kB + 4)];
+  const int tr = blockIdx.x / tiles_c, tc = blockIdx.x % tiles_c;
+  const int r0 = tr * kT, c0 = tc * kT;             // elements
+  const int t = threadIdx.x;
+  const int lr = t >> 2, lb = (t & 3) * 8;          // tile row, first byte of the piece
+  const int cb = (cols + 1) / 2;                    // bytes of an input row
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = r0 + lr, b = c0 / 2 + lb + e;
+    tile[lr * (kB + 4) + lb + e] = (r < rows && b < cb) ? in[(int64_t)r * ldi + b] : 0;
+  }
+  __syncthreads();
+  // output row c0 + oc (an input column), bytes for input rows r0 + 16 q .. + 15
+  const int oc = t >> 2, q = t & 3;
+  const int c = c0 + oc;
+  const int shift = (oc & 1) * 4;
+  uint8_t ob[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int lr0 = 16 * q + 2 * e;
+    const uint8_t lo = (tile[lr0 * (kB + 4) + oc / 2] >> shift) & 0xF;
+    const uint8_t hi = (tile[(lr0 + 1) * (kB + 4) + oc / 2] >> shift) & 0xF;
+    ob[e] = (uint8_t)(lo | (hi << 4));
+  }
+  if (c < cols) {
+    const int ob0 = (r0 + 16 * q) / 2;               // first output byte of the run
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (2 * (ob0 + e) < rows) out[(int64_t)c * ldo + ob0 + e] = ob[e];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_transpose_u4(const uint8_t* in, int64_t ldi, uint8_t* out, int64_t ldo,
+                               int64_t rows, int64_t cols, hipStream_t stream) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  const int64_t tiles_r = (rows + kT - 1) / kT, tiles_c = (cols + kT - 1) / kT;
+  hipLaunchKernelGGL(transpose_u4_kernel, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0,
+                     stream, in, ldi, out, ldo, (int)rows, (int)cols, (int)tiles_c);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose_u8(const uint8_t* in, int64_t ldi, uint8_t* out, int64_t ldo,
                                int64_t rows, int64_t cols, hipStream_t stream) {

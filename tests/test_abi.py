@@ -250,9 +250,7 @@ def test_fp4_validation(lib):
     assert q(ldq=112) == INVALID                       # ldq < k/2 bytes
     assert q(ldq=136) == MISALIGNED
     assert q(k=48) == NOT_SUPPORTED                    # MX: k % 32
-    need = F.fp8gemm_workspace_size_kn(64, 64, 128, 2)
-    assert lib.fp8gemm_run_kn(64, 64, 128, P, 64, 4, P2, 64, 4, 2, P3, P3 + 256, 0, 0,
-                              P3 + 4096, 64, 1, P3 + (1 << 20), need, None) == NOT_SUPPORTED
+    # (row-major FP4 B: test_row_major_b_fp4_validation)
 
 
 def test_grouped_fp4_validation(lib):
@@ -340,6 +338,24 @@ def test_row_major_b_validation(lib):
     assert run(wsb=need - 16) == WORKSPACE
     assert run(ws=P3 + (1 << 20) + 8) == MISALIGNED
     assert run(K=120) == NOT_SUPPORTED
+
+
+def test_row_major_b_fp4_validation(lib):
+    """fp8gemm_run_kn with MXFP4 operands (always the transposing form): B packs two
+    codes per byte along N, so ldb >= N/2; MX only, FP4 with FP4 only, no FP6."""
+    need = F.fp8gemm_workspace_size_kn(64, 64, 128, 2)
+    assert need >= 64 * 128 // 2 + 64 * 4
+    def run(ldb=32, fa=4, fb=4, mode=2, K=128, wsb=need, **kw):
+        return lib.fp8gemm_run_kn(kw.get("M", 64), 64, K, P, 64, fa, P2, ldb, fb, mode, P3,
+                                  P3 + 256, 0, 0, P3 + 4096, 64, 1, P3 + (1 << 20), wsb, None)
+    assert run(M=0) == SUCCESS
+    assert run(ldb=16) == INVALID                                  # 2 * ldb < N
+    assert run(ldb=40) == MISALIGNED
+    assert run(mode=1) == NOT_SUPPORTED                            # FP4: MX scales only
+    assert run(fb=0) == NOT_SUPPORTED and run(fa=0) == NOT_SUPPORTED
+    assert run(fa=2, fb=2) == NOT_SUPPORTED                        # FP6: no row-major B
+    assert run(K=112) == NOT_SUPPORTED                              # K % 32
+    assert run(wsb=need - 16) == WORKSPACE
 
 
 @pytest.mark.parametrize("shape,ld,fa,fb,mode,path", [

@@ -202,3 +202,32 @@ def test_gemm_row_major_b_in_kernel_wide_pitch():
                            b_layout="kn"))
         Cr, Ar = O.gemm_reference(qa, sa, qb, sb, mode)
         assert_within_bound(C, Cr, Ar, "bf16", f"row-major B wide pitch {mode}")
+
+
+def _fp4_operands(M, N, K, seed):
+    A, B = random_inputs(M, N, K, seed, "mx_block")
+    qa, sa = Q.quantize(A, "mx32", "e2m1")
+    qb, sb = Q.quantize(B, "mx32", "e2m1")
+    return qa, sa, qb, sb
+
+
+@pytest.mark.parametrize("shape", [(33, 70, 64), (257, 262, 4160), (128, 4096, 4096),
+                                   (512, 1024, 2048)])
+def test_gemm_row_major_b_fp4(shape):
+    """MXFP4 with B row-major: the oracle's [N, K] codes transposed to [K, N] and
+    packed two per byte along N (low nibble first); the library nibble-transposes
+    them back into the K-contiguous FP4 rows of its GEMM."""
+    M, N, K = shape
+    qa, sa, qb, sb = _fp4_operands(M, N, K, seed=M + 3 * N + K)
+    announce("gemm row-major B fp4", shape)
+    qb_kn = O.pack_fp4(np.ascontiguousarray(qb.T))                 # [K, N/2]
+    C = F.gemm(to_dev(O.pack_fp4(qa), 16), scale_to_dev(sa, "mx32"), to_dev(qb_kn, 16),
+               torch.from_numpy(np.ascontiguousarray(np.asarray(sb, np.uint8).T)).to(DEV),
+               "mx32", "bf16", fmt_a="e2m1", fmt_b="e2m1", b_layout="kn")
+    torch.cuda.synchronize()
+    Cr, Ar = O.gemm_reference(qa, sa, qb, sb, "mx32", fmt_a="e2m1", fmt_b="e2m1")
+    assert_within_bound(to_host(C), Cr, Ar, "bf16", f"row-major B fp4 {shape}")
+    # the same products as the K-contiguous FP4 GEMM, in the same order: equal bits
+    Cnk = F.gemm(to_dev(O.pack_fp4(qa), 16), scale_to_dev(sa, "mx32"), to_dev(O.pack_fp4(qb), 16),
+                 scale_to_dev(sb, "mx32"), "mx32", "bf16", fmt_a="e2m1", fmt_b="e2m1")
+    assert torch.equal(C, Cnk)
