@@ -384,7 +384,11 @@ def main():
 
     if kn:   # resident row-major weights: quantised and laid out once, before timing
         F.quantize(Bd, w.mode, out=qb, scales=sb, workspace=ws_b, fmt=fmt_b)
-        qb_kn = qb.t().contiguous()
+        if fp4:   # packed [N, K/2] along K -> [K, N/2] packed along N (low nibble first)
+            codes = torch.stack((qb & 15, qb >> 4), dim=2).reshape(rows_b, w.K).t()
+            qb_kn = (codes[:, 0::2] | (codes[:, 1::2] << 4)).contiguous()
+        else:
+            qb_kn = qb.t().contiguous()
         sb_kn = sb.t().contiguous() if w.mode == "mx32" else sb
         torch.cuda.synchronize()
     for _ in range(args.warmup):

@@ -30,6 +30,7 @@ FORMAT_UNITS = [("gemm.hip", ("FP8GEMM_FMT_A=1", "FP8GEMM_FMT_B=1"), ".e5m2_e5m2
                 ("gemm.hip", ("FP8GEMM_KN=1", "FP8GEMM_FMT_A=1", "FP8GEMM_FMT_B=1"), ".kn_e5m2_e5m2"),
                 ("gemm.hip", ("FP8GEMM_KN=1", "FP8GEMM_FMT_A=0", "FP8GEMM_FMT_B=1"), ".kn_e4m3_e5m2"),
                 ("gemm.hip", ("FP8GEMM_KN=1", "FP8GEMM_FMT_A=1", "FP8GEMM_FMT_B=0"), ".kn_e5m2_e4m3"),
+                ("gemm.hip", ("FP8GEMM_KN=1", "FP8GEMM_FMT_A=4", "FP8GEMM_FMT_B=4"), ".kn_e2m1_e2m1"),
                 ("grouped.hip", ("FP8GEMM_FMT_A=4", "FP8GEMM_FMT_B=4"), ".e2m1_e2m1")]
 
 ARCH = "gfx950"

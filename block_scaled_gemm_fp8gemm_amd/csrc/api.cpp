@@ -414,12 +414,16 @@ int64_t kn_code_bytes(int64_t N, int64_t K, int mode) {
 }
 // Whether fp8gemm_run_kn reads the row-major B inside the GEMM kernels
 // (transposing LDS reads) instead of making it K-contiguous in the workspace
-// first: FP8 codes, MX code rows of whole 16-byte chunks, and a shape the
-// in-kernel form takes (K % 128 == 0, MX K % 512 == 0, 32-bit spans).
+// first: FP8 codes or MXFP4 (even N: whole bytes per K-row), MX code rows of
+// whole 16-byte chunks, and a shape the in-kernel form takes (K % 128 == 0, MX
+// K % 512 == 0, 32-bit spans).
 bool kn_in_kernel(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int a_format,
                   int b_format, int mode) {
-  return code_bits(a_format) == 8 && code_bits(b_format) == 8 && (mode != kMx32 || N % 16 == 0) &&
-         fp8gemm::choose_path_kn(M, N, K, lda, ldb, mode) != fp8gemm::kPathNone;
+  const bool fp8 = code_bits(a_format) == 8 && code_bits(b_format) == 8;
+  const bool fp4 = a_format == FP8GEMM_FORMAT_E2M1 && b_format == FP8GEMM_FORMAT_E2M1 &&
+                   N % 2 == 0;
+  return (fp8 || fp4) && (mode != kMx32 || N % 16 == 0) &&
+         fp8gemm::choose_path_kn(M, N, K, lda, ldb, mode, fp4) != fp8gemm::kPathNone;
 }
 }  // namespace
 
@@ -451,9 +455,9 @@ fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A,
   if (!aligned(B, 16) || ldb % 16 != 0) return FP8GEMM_ERROR_MISALIGNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (kn_in_kernel(M, N, K, lda, ldb, a_format, b_format, mode)) {
-    // B's own checks passed above; K stands in for the pitch of a K-contiguous B
-    fp8gemm_status st = check_gemm_common(M, N, K, A, lda, B, K, mode, scale_a, scale_b, C, ldc,
-                                          out_dtype);
+    // B's own checks passed above; the row of a K-contiguous B stands in for its pitch
+    fp8gemm_status st = check_gemm_common(M, N, K, A, lda, B, fp4 ? K / 2 : K, mode, scale_a,
+                                          scale_b, C, ldc, out_dtype, fp4 ? 4 : 8);
     if (st != FP8GEMM_SUCCESS) return st;
     if (bias && !aligned(bias, 4)) return FP8GEMM_ERROR_MISALIGNED;
     const size_t need = fp8gemm_workspace_size(M, N, K, mode);
@@ -462,7 +466,7 @@ fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A,
     fp8gemm::GemmProblem p;
     p.M = (int)M;
     p.N = (int)N;
-    p.K = (int)K;
+    p.K = (int)(fp4 ? K / 2 : K);        // FP4: the kernels walk K in bytes of A
     p.A = A;
     p.lda = lda;
     p.B = B;
@@ -474,6 +478,7 @@ fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A,
     p.workspace = need > 0 ? workspace : nullptr;
     p.bias = bias;
     p.act = activation;
+    if (fp4) return from_hip(fp8gemm::launch_gemm_kn_e2m1_e2m1(p, mode, out_dtype, s));
     if (a_format == FP8GEMM_FORMAT_E5M2 && b_format == FP8GEMM_FORMAT_E5M2)
       return from_hip(fp8gemm::launch_gemm_kn_e5m2_e5m2(p, mode, out_dtype, s));
     if (a_format == FP8GEMM_FORMAT_E5M2)
@@ -602,7 +607,7 @@ int fp8gemm_run_kn_path(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ld
       N <= 0 || K <= 0 || lda < 0 || ldb < 0)
     return FP8GEMM_PATH_NONE;
   if (!kn_in_kernel(M, N, K, lda, ldb, a_format, b_format, mode)) return FP8GEMM_PATH_NONE;
-  return fp8gemm::choose_path_kn(M, N, K, lda, ldb, mode);
+  return fp8gemm::choose_path_kn(M, N, K, lda, ldb, mode, a_format == FP8GEMM_FORMAT_E2M1);
 }
 
 const char* fp8gemm_status_string(int status) {

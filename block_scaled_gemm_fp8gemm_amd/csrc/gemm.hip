@@ -39,7 +39,7 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void gemm_kernel(G
   op.A = p.A + (int64_t)m0 * p.lda;
   op.lda = p.lda;
   op.a_rows = p.M - m0;
-  op.B = kKn ? p.B + n0 : p.B + (int64_t)n0 * p.ldb;
+  op.B = kKn ? p.B + (kF4 ? n0 / 2 : n0) : p.B + (int64_t)n0 * p.ldb;
   op.ldb = p.ldb;
   op.b_rows = p.N - n0;
   op.K = p.K;
@@ -218,7 +218,9 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void splitk_kernel
   op.A = p.A + (int64_t)m0 * p.lda + k0;
   op.lda = p.lda;
   op.a_rows = p.M - m0;
-  op.B = kKn ? p.B + (int64_t)k0 * p.ldb + n0 : p.B + (int64_t)n0 * p.ldb + k0;
+  // (row-major FP4 B: K-rows 2 k0 on, columns n0 on in bytes n0 / 2)
+  op.B = kKn ? p.B + (int64_t)(kF4 ? 2 * k0 : k0) * p.ldb + (kF4 ? n0 / 2 : n0)
+             : p.B + (int64_t)n0 * p.ldb + k0;
   op.ldb = p.ldb;
   op.b_rows = p.N - n0;
   op.K = kslice;
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void splitk_kernel
   if (MODE == kMx32) {
     op.sa = static_cast<const uint8_t*>(p.scale_a) + (int64_t)m0 * op.sld + k0 / kBlkBytes;
     op.sb = static_cast<const uint8_t*>(p.scale_b) +
-            (kKn ? (int64_t)(k0 / 32) * p.N + n0 : (int64_t)n0 * op.sld + k0 / kBlkBytes);
+            (kKn ? (int64_t)(k0 / kBlkBytes) * p.N + n0 : (int64_t)n0 * op.sld + k0 / kBlkBytes);
   }
   if (MODE == kRowwise) {
     op.ra = fsa + m0;
@@ -340,7 +342,9 @@ hipError_t launch_split(const GemmProblem& p, const SplitPlan& plan, hipStream_t
 template <int MODE, typename OutT, bool FUSED>
 hipError_t launch_plan(const GemmProblem& p, hipStream_t stream) {
   constexpr bool kNoStream = FUSED || std::is_same<OutT, uint8_t>::value;
-  const GemmPath path = kKn ? choose_path_kn(p.M, p.N, p.K, p.lda, p.ldb, MODE)
+  // (K of the problem counts bytes for FP4, elements for the row-major form's plan)
+  const GemmPath path = kKn ? choose_path_kn(p.M, p.N, kF4 ? 2 * (int64_t)p.K : p.K, p.lda,
+                                             p.ldb, MODE, kF4)
                             : choose_path(p.M, p.N, p.K, p.lda, p.ldb, MODE, kF4, kNoStream);
   // row-major B outside the in-kernel form: the caller transposes B first
   if (kKn && path == kPathNone && p.M > 0 && p.N > 0) return hipErrorInvalidValue;
@@ -383,6 +387,8 @@ hipError_t launch_any(const GemmProblem& p, hipStream_t stream) {
 #define FP8GEMM_LAUNCH_NAME launch_gemm_kn_e4m3_e5m2
 #elif FP8GEMM_KN && FP8GEMM_FMT_A == 1 && FP8GEMM_FMT_B == 0
 #define FP8GEMM_LAUNCH_NAME launch_gemm_kn_e5m2_e4m3
+#elif FP8GEMM_KN && FP8GEMM_FMT_A == 4 && FP8GEMM_FMT_B == 4
+#define FP8GEMM_LAUNCH_NAME launch_gemm_kn_e2m1_e2m1
 #elif FP8GEMM_FMT_A == 0 && FP8GEMM_FMT_B == 0
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int mode) {
   return (size_t)gemm_workspace_need(M, N, K, mode);
@@ -403,8 +409,10 @@ hipError_t FP8GEMM_LAUNCH_NAME(const GemmProblem& p, int mode, int out, hipStrea
   // MXFP4: E8M0 block scales only; K, lda and ldb count bytes (two codes each)
   if (mode != kMx32) return hipErrorInvalidValue;
   if (out == kF16) return launch_any<kMx32, _Float16>(p, stream);
+#if !FP8GEMM_KN
   if (out == kE4M3Mx) return launch_any<kMx32, uint8_t>(p, stream);
   if (out == kF32Max) return launch_plan<kMx32, float, true>(p, stream);
+#endif
   return launch_any<kMx32, __bf16>(p, stream);
 #else
 #if !FP8GEMM_KN

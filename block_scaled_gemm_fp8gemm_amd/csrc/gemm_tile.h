@@ -183,6 +183,18 @@ __device__ __forceinline__ int kn_swz(int k) {
   return 2 * ((k / (256 / BN)) & (BN / 32 - 1));
 }
 
+// The same for packed FP4 B: a K-row holds BN / 2 bytes (two codes per byte),
+// a 32-column fragment is one 16-byte chunk, and a transposing read
+// (ds_read_b64_tr_b4; probed on gfx950: in each 16-lane group, 4-bit element j
+// of lane i is element i of the 16 addressed by lane j) takes 16 K-rows at one
+// fragment (both 8-byte halves).  Chunk c of K-row k sits at c ^ kn4_swz(k): the
+// 16 rows of a half-wave's read land on 16 distinct 16-byte bank groups for BN =
+// 64, 128 and 256 (period 16 in k).
+template <int BN>
+__device__ __forceinline__ int kn4_swz(int k) {
+  return (k / (512 / BN)) & (BN / 32 - 1);
+}
+
 __device__ __forceinline__ void lds_dma16(const uint8_t* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
@@ -712,8 +724,12 @@ __device__ __forceinline__ bool interior_tile(const TileOperands& op) {
 // by lane 2 j + i / 8).  Lanes 2 m and 2 m + 1 of a group address K-row kb + m at
 // the group's 16 columns, so lane i receives column i at K-rows kb .. kb + 7: the
 // eight K bytes of operand bytes 8 q .. 8 q + 7 (kb = 32 (q / 2) + 16 h + 8 (q % 2)
-// within the 64-K step).  MX codes of B come as [K/32][N] and sit in LDS as [16
-// blocks][BN] per group.  Tiles cut by M or N run here too: A rows past the edge
+// within the 64-K step).  Packed FP4 B (two codes per byte along N): a K tile is
+// 256 K-rows of BN / 2 bytes, a fragment step four ds_read_b64_tr_b4 of 16
+// K-rows each (lane w of a 16-lane group addresses K-row kb + w at the 8-byte
+// half G of the fragment's chunk; see kn4_swz), and its two codes per step are
+// two bytes in two registers.  MX codes of B come as [K/32][N] and sit in LDS as
+// [16 blocks][BN] per group.  Tiles cut by M or N run here too: A rows past the edge
 // read as zero (the copy range ends at the last valid row) and B columns past N
 // hold whatever the copy finds there; neither is ever stored.
 template <class Cfg, int MODE, int NS = 2, bool KN = false>
@@ -736,9 +752,15 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   static_assert(kTile % (1024 * Cfg::kWaves) == 0, "equal copy share per wave");
   static_assert(kLoads % 2 == 0, "copy blocks of both swizzle phases per wave");
   static_assert((NS - 1) * kLoads + kCodeLoads < 64, "vmcnt range");
-  // KN: K-rows per B copy instruction, 16-byte chunks per K-row
-  constexpr int kKRows = 1024 / Cfg::BN, kChunks = Cfg::BN / 16;
-  static_assert(!KN || !kF4, "row-major B: one code per byte");
+  // KN: bytes per B K-row in LDS (FP4: two codes per byte), K-rows of B per K
+  // tile, K-rows per B copy instruction, 16-byte chunks per K-row; the MX code
+  // rows of B hold one byte per column whatever the format
+  constexpr int kBRowB = kF4 ? Cfg::BN / 2 : Cfg::BN;
+  constexpr int kKTileRows = kF4 ? 2 * kRowB : kRowB;
+  constexpr int kKRows = 1024 / kBRowB, kChunks = kBRowB / 16;
+  constexpr int kCRows = 1024 / Cfg::BN, kCChunks = Cfg::BN / 16;
+  constexpr int kSwzPeriod = kF4 ? 16 : 8;
+  auto swz_b = [](int k) { return kF4 ? kn4_swz<Cfg::BN>(k) : kn_swz<Cfg::BN>(k); };
   // ring slots reachable from one base register through the 16-bit offset field
   // (KN: the B reads add up to 104 K-rows of BN bytes)
   constexpr int kMaxFrag0 = ((FM > FN ? FM : FN) - 1) * 32 * kRowB;
@@ -756,6 +778,11 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   const int ncode = nblk / 16;                     // 16-byte code groups per row
   constexpr int kGroupTiles = 16 * kBlkBytes / kRowB;   // K tiles per code group (4, FP4 2)
   constexpr int kCodes = 1;                        // code reads per fragment and step
+  // B code registers per fragment and step: row-major FP4 B keeps its two codes
+  // (rows BN bytes apart) in two registers, each the MFMA's byte 0, rather than
+  // joining them into one with a VALU op that would wait on both reads
+  constexpr bool kCodePair = KN && kF4;
+  constexpr int kCodesB = kCodePair ? 2 : 1;
 
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -772,7 +799,8 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   const int a_tile = op.a_rows < Cfg::BM ? op.a_rows : Cfg::BM;
   const int b_tile = op.b_rows < Cfg::BN ? op.b_rows : Cfg::BN;
   const uint32_t nrA = (uint32_t)((a_tile - 1) * op.lda + op.K);
-  const uint32_t nrB = KN ? (uint32_t)((op.K - 1) * op.ldb + b_tile)
+  const uint32_t nrB = KN ? (uint32_t)((op.K / kRowB * kKTileRows - 1) * op.ldb +
+                                       (kF4 ? (b_tile + 1) / 2 : b_tile))
                           : (uint32_t)((b_tile - 1) * op.ldb + op.K);
   const __amdgpu_buffer_rsrc_t rsA = buffer_rsrc(op.A, nrA);
   const __amdgpu_buffer_rsrc_t rsB = buffer_rsrc(op.B, nrB);
@@ -788,7 +816,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   // (lane % kChunks) ^ kn_swz(K-row); kn_swz has period 8 in the K-row and every
   // wave's first B instruction starts at a multiple of 8 K-rows, so at most two
   // distinct lane offsets remain
-  static_assert(!KN || ((kLoads * kKRows) % 8 == 0 && (nA * kKRows) % 8 == 0),
+  static_assert(!KN || ((kLoads * kKRows) % kSwzPeriod == 0 && (nA * kKRows) % kSwzPeriod == 0),
                 "B copy blocks start on the swizzle period");
   int voff[kLoads];
 #pragma unroll
@@ -796,7 +824,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
     const bool isA = g0 + j < nA;
     if (KN && !isA) {
       const int kr = lane / kChunks;
-      voff[j] = kr * ldb + 16 * ((lane % kChunks) ^ kn_swz<Cfg::BN>(((j * kKRows) & 7) + kr));
+      voff[j] = kr * ldb + 16 * ((lane % kChunks) ^ swz_b(((j * kKRows) & (kSwzPeriod - 1)) + kr));
     } else {
       voff[j] = crow * (isA ? lda : ldb) + ((j & 1) ? sw1 : sw0);
     }
@@ -817,10 +845,10 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   const bool wave_a = g0 < nA;
   const v4u_rs ws_t = wave_a ? wsA : wsB;
   const int t_row = wave_a ? 8 * lda : kKRows * ldb;
-  const int t_kt = wave_a ? kRowB : kRowB * ldb;
+  const int t_kt = wave_a ? kRowB : kKTileRows * ldb;
   const int t_base = wave_a ? 0 : -nA * kKRows * ldb;
-  // KN, MX: B code copy jj covers code rows (32-K blocks) kKRows li .. + kKRows - 1
-  // of the group, lane -> block lane / kChunks, 16 columns at 16 (lane % kChunks);
+  // KN, MX: B code copy jj covers code rows (32-K blocks) kCRows li .. + kCRows - 1
+  // of the group, lane -> block lane / kCChunks, 16 columns at 16 (lane % kCChunks);
   // A code copies as in the K-contiguous layout.  soff = grp * c_grp + c_base.
   int cv[kCodeLoads], c_grp[kCodeLoads], c_base[kCodeLoads];
   v4u_rs wc[kCodeLoads];
@@ -831,7 +859,7 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
     const bool code_a = ci < Cfg::BM / 64;
     const int li = code_a ? ci : ci - Cfg::BM / 64;
     cv[jj] = code_a ? lane * op.sld
-                    : (li * kKRows + lane / kChunks) * op.sldb + 16 * (lane % kChunks);
+                    : (li * kCRows + lane / kCChunks) * op.sldb + 16 * (lane % kCChunks);
     c_grp[jj] = code_a ? 16 : 16 * op.sldb;
     c_base[jj] = code_a ? li * 64 * op.sld : 0;
     wc[jj] = code_a ? wcA : wcB;
@@ -883,8 +911,22 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   // 32 j + 16 G + 8 (w % 2) of fragment j: chunk 2 j' + G, j' = this wave's
   // fragment column / 32, at (2 j' + G) ^ kn_swz(w / 2) (kb % 8 == 0 leaves the
   // swizzle to the lane); base per fragment, K offsets in the offset field
+  // (FP4: lane (G, w) addresses K-row 64 h + w of the step's 128 at 8-byte half G
+  // of the fragment's chunk j' = this wave's fragment column / 32, which sits at
+  // j' ^ kn4_swz(w); the four reads of a fragment start 16 K-rows apart)
   int bk[kBases][KN ? FN : 1];
-  if constexpr (KN) {
+  if constexpr (KN && kF4) {
+    const int w = lane & 15, G = (lane >> 4) & 1;
+    const int swz = kn4_swz<Cfg::BN>(w);
+#pragma unroll
+    for (int s = 0; s < kBases; ++s)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int c1 = (wn * Cfg::WN + 32 * j) / 32;
+        bk[s][j] = opaque(s * kPerBase * kTile + Cfg::BM * kRowB + (64 * h + w) * kBRowB +
+                          16 * (c1 ^ swz) + 8 * G);
+      }
+  } else if constexpr (KN) {
     const int w = lane & 15, G = (lane >> 4) & 1;
     const int swz = kn_swz<Cfg::BN>(w >> 1);
 #pragma unroll
@@ -903,7 +945,8 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
   int cbuf = 0;                                        // buffer index of the current group
   if (kMx) {
     cur_a = opaque(kCodeOff + (wm * Cfg::WM + (lane & 31)) * 16 + (kF4 ? 2 * h : h));
-    cur_b = KN ? opaque(kCodeOff + Cfg::BM * 16 + h * Cfg::BN + wn * Cfg::WN + (lane & 31))
+    cur_b = KN ? opaque(kCodeOff + Cfg::BM * 16 + (kF4 ? 2 * h : h) * Cfg::BN + wn * Cfg::WN +
+                        (lane & 31))
                : opaque(kCodeOff + (Cfg::BM + wn * Cfg::WN + (lane & 31)) * 16 + (kF4 ? 2 * h : h));
     nxt_a = opaque(cur_a + kCodeBuf);
     nxt_b = opaque(cur_b + kCodeBuf);
@@ -911,9 +954,10 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
 
   auto rd16 = [&](int addr) { return *reinterpret_cast<const v4i*>(lds + addr); };
   auto rdtr = [&](int addr) {
-    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-        reinterpret_cast<__attribute__((address_space(3))) v2i*>(
-            (__attribute__((address_space(3))) uint8_t*)(lds + addr)));
+    auto* a = reinterpret_cast<__attribute__((address_space(3))) v2i*>(
+        (__attribute__((address_space(3))) uint8_t*)(lds + addr));
+    if constexpr (kF4) return __builtin_amdgcn_ds_read_tr4_b64_v2i32(a);
+    else return __builtin_amdgcn_ds_read_tr8_b64_v2i32(a);
   };
   // a step's LDS reads: 16-byte reads of A (and of B), KN: four 8-byte
   // transposing reads per B fragment
@@ -929,6 +973,9 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
     const int c = d & 1;
     if (d < kReadsA) {
       r.rd[d] = rd16(ba[b][p][c] + o + (d >> 1) * 32 * kRowB);
+    } else if constexpr (KN && kF4) {
+      const int e = d - kReadsA, q = e & 3;
+      r.rt[e] = rdtr(bk[b][e >> 2] + o + (128 * p + 16 * q) * kBRowB);
     } else if constexpr (KN) {
       const int e = d - kReadsA, q = e & 3;
       r.rt[e] = rdtr(bk[b][e >> 2] + o + (64 * p + 32 * (q >> 1) + 8 * (q & 1)) * Cfg::BN);
@@ -953,23 +1000,28 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
       }
     }
   };
-  uint32_t ca[2][kCodes][FM], cb[2][kCodes][FN];      // codes: [register set][MFMA][fragment]
+  uint32_t ca[2][kCodes][FM], cb[2][kCodesB][FN];     // codes: [register set][MFMA][fragment]
 #pragma unroll
   for (int z = 0; z < 2; ++z)
 #pragma unroll
-    for (int c = 0; c < kCodes; ++c) {
+    for (int c = 0; c < kCodesB; ++c) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) ca[z][c][i] = 0;
+      for (int i = 0; i < FM; ++i)
+        if (c < kCodes) ca[z][c][i] = 0;
 #pragma unroll
       for (int j = 0; j < FN; ++j) cb[z][c][j] = 0;
     }
   // the e-th code byte read of a step: K tile u with u % kGroupTiles == q, half p
   auto read_code = [&](int base_a, int base_b, int q, int p, int e,
-                       uint32_t (&a)[kCodes][FM], uint32_t (&b)[kCodes][FN]) {
+                       uint32_t (&a)[kCodes][FM], uint32_t (&b)[kCodesB][FN]) {
     const int c = e / (FM + FN), f = e % (FM + FN);
     if constexpr (kF4) {           // the two adjacent code bytes of the step's MFMAs
       const int off = 8 * q + 4 * p;
       if (f < FM) a[c][f] = *reinterpret_cast<const uint16_t*>(lds + base_a + off + f * 32 * 16);
+      else if (KN) {               // code rows of B: blocks off + 2 h and + 1 at one column
+        b[0][f - FM] = lds[base_b + off * Cfg::BN + (f - FM) * 32];
+        b[kCodesB - 1][f - FM] = lds[base_b + (off + 1) * Cfg::BN + (f - FM) * 32];
+      }
       else b[c][f - FM] = *reinterpret_cast<const uint16_t*>(lds + base_b + off + (f - FM) * 32 * 16);
     } else {
       const int off = 4 * q + 2 * p;
@@ -1062,7 +1114,8 @@ __device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_
             lo16(fb[j]), lo16(fa[i]), acc[i][j], kFmtB, kFmtA, 0, (int)cb[Z][0][j], 0,
             (int)ca[Z][0][i]);
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            hi16(fb[j]), hi16(fa[i]), acc[i][j], kFmtB, kFmtA, 1, (int)cb[Z][0][j], 1,
+            hi16(fb[j]), hi16(fa[i]), acc[i][j], kFmtB, kFmtA, kCodePair ? 0 : 1,
+            (int)cb[Z][kCodesB - 1][j], 1,
             (int)ca[Z][0][i]);
       } else if (kMx) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(

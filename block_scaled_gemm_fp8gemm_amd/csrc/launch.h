@@ -78,6 +78,9 @@ hipError_t launch_gemm_kn(const GemmProblem& p, int mode, int out, hipStream_t s
 hipError_t launch_gemm_kn_e5m2_e5m2(const GemmProblem& p, int mode, int out, hipStream_t stream);
 hipError_t launch_gemm_kn_e4m3_e5m2(const GemmProblem& p, int mode, int out, hipStream_t stream);
 hipError_t launch_gemm_kn_e5m2_e4m3(const GemmProblem& p, int mode, int out, hipStream_t stream);
+// MXFP4 with row-major B: K and lda as launch_gemm_e2m1_e2m1 (bytes), B K-rows of
+// ldb bytes holding two codes per byte along N (mode kMx32, 16-bit outputs).
+hipError_t launch_gemm_kn_e2m1_e2m1(const GemmProblem& p, int mode, int out, hipStream_t stream);
 // MXFP4 x MXFP4 (mode kMx32 only): K, lda and ldb of the problem count bytes
 // (two e2m1 codes each), the E8M0 codes stay one per 32 elements.
 hipError_t launch_gemm_e2m1_e2m1(const GemmProblem& p, int mode, int out, hipStream_t stream);

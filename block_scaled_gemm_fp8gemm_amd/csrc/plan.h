@@ -119,13 +119,17 @@ inline GemmPath choose_path(int64_t M, int64_t N, int64_t K, int64_t lda, int64_
 // stream.  kPathNone (with M, N > 0) where that form does not apply: K % 128 != 0
 // (MX: K % 512 != 0, whole code groups) or spans past 32-bit buffer offsets; the
 // caller then makes B K-contiguous first.
+// K counts elements; fp4: MXFP4 operands (A rows of K / 2 bytes, B K-rows of
+// packed pairs along N; MX only), planned like the K-contiguous FP4 GEMM.
 inline GemmPath choose_path_kn(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
-                               int mode) {
+                               int mode, bool fp4 = false) {
   if (M <= 0 || N <= 0) return kPathNone;
+  if (fp4 && mode != kMx32) return kPathNone;
   if (K % (mode == kMx32 ? 512 : 128) != 0) return kPathNone;
-  if (!spans_fit(kBigTile, lda, K) || !spans_fit(K, ldb, kBigTile)) return kPathNone;
+  const int64_t ka = fp4 ? K / 2 : K;               // bytes of an A row
+  if (!spans_fit(kBigTile, lda, ka) || !spans_fit(K, ldb, kBigTile)) return kPathNone;
   if (mode == kMx32 && !spans_fit(K / 32, N, kBigTile)) return kPathNone;
-  if (plan_split(M, N, K, mode, 32).splits > 1) return kPathSplitK;
+  if (plan_split(M, N, ka, mode, fp4 ? 16 : 32).splits > 1) return kPathSplitK;
   const int64_t big_tiles = ((M + kBigTile - 1) / kBigTile) * ((N + kBigTile - 1) / kBigTile);
   return big_tiles >= 256 ? kPathTile256 : kPathTile128;
 }

@@ -285,17 +285,17 @@ fp8gemm_status fp8gemm_run_qout(int64_t M, int64_t N, int64_t K, const uint8_t* 
 /* Everything else (A, C, formats, scale_a, bias, activation, accuracy, errors) */
 /* as fp8gemm_run_ex; FP6 operands are NOT_SUPPORTED here.                     */
 /* Two forms, chosen per call (fp8gemm_run_kn_path tells which):                 */
-/*   in-kernel : (FP8 codes) the GEMM kernels read B row-major and form the      */
-/*               K-major MFMA operand with transposing LDS reads (no extra pass  */
-/*               over B).                                                        */
-/*               Taken when K % 128 == 0 (MX: K % 512 == 0 and N % 16 == 0) and  */
-/*               the operand spans fit 32-bit offsets (K * ldb < 2^31 - 256).    */
+/*   in-kernel : the GEMM kernels read B row-major and form the K-major MFMA     */
+/*               operand with transposing LDS reads (ds_read_b64_tr_b8, FP4:     */
+/*               tr_b4; no extra pass over B).  Taken when K % 128 == 0 (MX: K % */
+/*               512 == 0 and N % 16 == 0) and the operand spans fit 32-bit      */
+/*               offsets (K * ldb < 2^31 - 256).                                 */
 /*               Workspace: fp8gemm_workspace_size(M, N, K, mode) bytes (NULL    */
 /*               when that is 0).                                                */
-/*   transposing: otherwise (and for E2M1) the call first copies B and its MX   */
-/*               codes into the K-contiguous layout in the workspace (one HBM    */
-/*               pass over B; FP4 codes by a nibble transpose), then runs the    */
-/*               GEMM.  Workspace never NULL: the copy lives there.              */
+/*   transposing: otherwise the call first copies B and its MX codes into the   */
+/*               K-contiguous layout in the workspace (one HBM pass over B; FP4  */
+/*               codes by a nibble transpose), then runs the GEMM.  Workspace    */
+/*               never NULL: the copy lives there.                               */
 /* fp8gemm_workspace_size_kn() bytes, 16-byte aligned and zero-filled before    */
 /* its first use, serve either form.  Its first 4 KiB are the counters of       */
 /* fp8gemm_run (left at zero); the copies come after the GEMM's own workspace,  */

@@ -371,7 +371,13 @@ def test_row_major_b_fp4_validation(lib):
     ((2048, 4100, 1024), (1024, 4112), "e4m3", "e4m3", "mx32", "none"),    # MX: N % 16
     ((2048, 4100, 1024), (1024, 4112), "e4m3", "e4m3", "tensor", "tile128"),
     ((256, 256, 1 << 19), (1 << 19, 8192), "e4m3", "e4m3", "tensor", "none"),  # K * ldb >= 2^31
-    ((128, 4096, 4096), None, "e2m1", "e2m1", "mx32", "none"),             # FP4: transposing form refused
+    ((128, 4096, 4096), (2048, 2048), "e2m1", "e2m1", "mx32", "splitk"),   # MXFP4 (packed rows)
+    ((4096, 4096, 4096), (2048, 2048), "e2m1", "e2m1", "mx32", "tile256"),
+    ((300, 528, 1024), (512, 272), "e2m1", "e2m1", "mx32", "tile128"),
+    ((2048, 4096, 4160), (2080, 2048), "e2m1", "e2m1", "mx32", "none"),    # K % 512
+    ((2048, 4098, 1024), (512, 2064), "e2m1", "e2m1", "mx32", "none"),     # odd bytes: N % 16
+    ((2048, 4096, 1024), (512, 2048), "e2m1", "e2m1", "rowwise", "none"),  # FP4: MX only
+    ((2048, 4096, 1024), (768, 3072), "e2m3", "e2m3", "mx32", "none"),     # no FP6 here
     ((0, 4096, 4096), None, "e4m3", "e4m3", "tensor", "none"),
 ])
 def test_row_major_b_in_kernel_rules(lib, shape, ld, fa, fb, mode, path):

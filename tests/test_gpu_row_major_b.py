@@ -211,16 +211,25 @@ def _fp4_operands(M, N, K, seed):
     return qa, sa, qb, sb
 
 
-@pytest.mark.parametrize("shape", [(33, 70, 64), (257, 262, 4160), (128, 4096, 4096),
-                                   (512, 1024, 2048)])
-def test_gemm_row_major_b_fp4(shape):
+@pytest.mark.parametrize("shape,path", [((33, 70, 64), "none"), ((257, 262, 4160), "none"),
+                                        ((128, 4096, 4096), "splitk"),
+                                        ((512, 1024, 2048), "splitk"),
+                                        ((2048, 1024, 2048), "tile128"),
+                                        ((300, 528, 1024), "tile128"),
+                                        ((100, 2000, 4096), "splitk")])
+def test_gemm_row_major_b_fp4(shape, path):
     """MXFP4 with B row-major: the oracle's [N, K] codes transposed to [K, N] and
-    packed two per byte along N (low nibble first); the library nibble-transposes
-    them back into the K-contiguous FP4 rows of its GEMM."""
+    packed two per byte along N (low nibble first).  With K % 512 == 0 and N % 16
+    == 0 the GEMM kernels read them as they are (ds_read_b64_tr_b4), else the
+    library nibble-transposes them into K-contiguous FP4 rows first; either way
+    the products and their order are those of the K-contiguous FP4 GEMM."""
     M, N, K = shape
     qa, sa, qb, sb = _fp4_operands(M, N, K, seed=M + 3 * N + K)
-    announce("gemm row-major B fp4", shape)
+    announce("gemm row-major B fp4", shape, path)
     qb_kn = O.pack_fp4(np.ascontiguousarray(qb.T))                 # [K, N/2]
+    ldb = (N // 2 + 15) // 16 * 16
+    assert F.fp8gemm_run_kn_path(M, N, K, (K // 2 + 15) // 16 * 16, ldb, F.FORMATS["e2m1"],
+                                 F.FORMATS["e2m1"], F.SCALE_MODES["mx32"]) == path
     C = F.gemm(to_dev(O.pack_fp4(qa), 16), scale_to_dev(sa, "mx32"), to_dev(qb_kn, 16),
                torch.from_numpy(np.ascontiguousarray(np.asarray(sb, np.uint8).T)).to(DEV),
                "mx32", "bf16", fmt_a="e2m1", fmt_b="e2m1", b_layout="kn")
@@ -231,3 +240,31 @@ def test_gemm_row_major_b_fp4(shape):
     Cnk = F.gemm(to_dev(O.pack_fp4(qa), 16), scale_to_dev(sa, "mx32"), to_dev(O.pack_fp4(qb), 16),
                  scale_to_dev(sb, "mx32"), "mx32", "bf16", fmt_a="e2m1", fmt_b="e2m1")
     assert torch.equal(C, Cnk)
+
+
+@pytest.mark.parametrize("shape", [(4096, 4096, 512), (4352, 4160, 1024)])
+def test_gemm_row_major_b_fp4_large_tile(shape):
+    """MXFP4 row-major B on 256 x 256 tiles, full and cut by M and N (sampled
+    128 x 128 blocks, and bit-equality with the K-contiguous FP4 GEMM where that
+    takes the same tile path: it keeps cut shapes on 128 x 128 tiles)."""
+    M, N, K = shape
+    qa, sa, qb, sb = _fp4_operands(M, N, K, seed=K + 7)
+    announce("gemm row-major B fp4 large tile", shape)
+    assert F.fp8gemm_run_kn_path(M, N, K, K // 2, N // 2, F.FORMATS["e2m1"], F.FORMATS["e2m1"],
+                                 F.SCALE_MODES["mx32"]) == "tile256"
+    qad, sad = to_dev(O.pack_fp4(qa), 16), scale_to_dev(sa, "mx32")
+    C = F.gemm(qad, sad, to_dev(O.pack_fp4(np.ascontiguousarray(qb.T)), 16),
+               torch.from_numpy(np.ascontiguousarray(np.asarray(sb, np.uint8).T)).to(DEV),
+               "mx32", "bf16", fmt_a="e2m1", fmt_b="e2m1", b_layout="kn")
+    Cnk = F.gemm(qad, sad, to_dev(O.pack_fp4(qb), 16), scale_to_dev(sb, "mx32"), "mx32", "bf16",
+                 fmt_a="e2m1", fmt_b="e2m1")
+    torch.cuda.synchronize()
+    for r0, c0 in ((0, 0), (M - 128, N - 128), (2048, 1024)):
+        ri, ci = np.arange(r0, r0 + 128), np.arange(c0, c0 + 128)
+        Cr, Ar = O.gemm_reference(qa, sa, qb, sb, "mx32", rows=ri, cols=ci, fmt_a="e2m1",
+                                  fmt_b="e2m1")
+        assert_within_bound(to_host(C[r0:r0 + 128, c0:c0 + 128]), Cr, Ar, "bf16",
+                            f"row-major B fp4 {shape} block {(r0, c0)}")
+    if F.fp8gemm_run_path(M, N, K, K // 2, K // 2, F.FORMATS["e2m1"], F.FORMATS["e2m1"],
+                          F.SCALE_MODES["mx32"], 0) == "tile256":
+        assert torch.equal(C, Cnk)
