@@ -450,9 +450,10 @@ def gemm_mxout(qa, sa, qb, sb, mode: str = "tensor", out=None, out_scales=None,
 def gemm_qout(qa, sa, qb, sb, mode: str = "tensor", out_mode: str = "rowwise",
               out_fmt: str = "e4m3", out=None, out_scales=None, workspace=None,
               fmt_a: str = "e4m3", fmt_b: str = "e4m3", bias=None, activation: str = "none"):
-    """(codes uint8 [M, N], scales float32 [M] or [1]): y = act(dq(qa) @ dq(qb) +
-    bias) quantised for the next layer with a fresh scale per row (out_mode
-    "rowwise") or for the whole output ("tensor"), by the rule of ``quantize``;
+    """(codes uint8 [M, N], scales float32 [M] or [1]): the bf16 output of ``gemm``
+    (act(dq(qa) @ dq(qb) + bias)) quantised for the next layer with a fresh scale
+    per row (out_mode "rowwise") or for the whole output ("tensor"), by the rule
+    of ``quantize`` (bit-identical to ``quantize(gemm(...).float(), out_mode)``);
     out_fmt "e4m3" or "e5m2"; N must be a multiple of 16.  Operands as ``gemm``
     (qb [N, K], K contiguous).  The row scales are the scale_a of a row-wise GEMM
     that takes the codes as its A operand."""

@@ -159,7 +159,7 @@ namespace {
 
 // The dense GEMM behind fp8gemm_run_ex (16-bit outputs), fp8gemm_run_mxout
 // (out_dtype kE4M3Mx: e4m3 codes to C, E8M0 codes to cs) and fp8gemm_run_qout
-// (kF32Max: fp32 y to C, ldc in floats, its maxima to cs).
+// (kBF16Max: the bf16 output to C and its maxima to cs).
 fp8gemm_status run_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                          int a_format, const uint8_t* B, int64_t ldb, int b_format, int mode,
                          const void* scale_a, const void* scale_b, const float* bias,
@@ -167,8 +167,8 @@ fp8gemm_status run_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int6
                          int64_t ldcs, void* workspace, size_t workspace_bytes, void* stream,
                          bool dry_run = false) {
   const bool qout = out_dtype == fp8gemm::kE4M3Mx;
-  const bool f32max = out_dtype == fp8gemm::kF32Max;     // fp32 y + maxima (requantised output)
-  if (!valid_mode(mode) || !(valid_out(out_dtype) || qout || f32max) || !valid_format(a_format) ||
+  const bool bfmax = out_dtype == fp8gemm::kBF16Max;     // bf16 y + maxima (requantised output)
+  if (!valid_mode(mode) || !(valid_out(out_dtype) || qout || bfmax) || !valid_format(a_format) ||
       !valid_format(b_format) || !valid_act(activation) || M < 0 || N < 0 || K <= 0)
     return FP8GEMM_ERROR_INVALID_VALUE;
   // FP4 pairs with FP4 only, FP6 with FP6 (e2m3 / e3m2 in any pairing), both
@@ -263,8 +263,8 @@ namespace {
 
 // Workspace of the requantised output: the dense GEMM's own first (never less
 // than its 4 KiB of split-K counters, so that no call of another shape finds y
-// there), then the maxima (M words, zeroed by each call), then y in fp32 with
-// rows of 256-byte multiples.
+// there), then the maxima (M words, zeroed by each call), then y in bf16 with
+// rows of 128-byte multiples.
 struct QoutLayout {
   size_t maxima, y, total;
   int64_t ldy;
@@ -278,7 +278,7 @@ QoutLayout qout_layout(int64_t M, int64_t N, int64_t K, int mode) {
   l.maxima = up(g, 256);
   l.y = l.maxima + up((size_t)M * 4, 256);
   l.ldy = (int64_t)up((size_t)N, 64);
-  l.total = l.y + (size_t)M * (size_t)l.ldy * 4;
+  l.total = l.y + (size_t)M * (size_t)l.ldy * 2;
   return l;
 }
 
@@ -300,7 +300,7 @@ fp8gemm_status fp8gemm_run_qout(int64_t M, int64_t N, int64_t K, const uint8_t* 
   // every check of the GEMM itself, with the codes standing in for its output
   fp8gemm_status st =
       run_dense(M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias,
-                activation, C, ldc, fp8gemm::kF32Max, nullptr, 0, nullptr, 0, stream, true);
+                activation, C, ldc, fp8gemm::kBF16Max, nullptr, 0, nullptr, 0, stream, true);
   if (st != FP8GEMM_SUCCESS || M == 0 || N == 0) return st;
   if (c_format != FP8GEMM_FORMAT_E4M3 && c_format != FP8GEMM_FORMAT_E5M2)
     return FP8GEMM_ERROR_NOT_SUPPORTED;
@@ -314,12 +314,12 @@ fp8gemm_status fp8gemm_run_qout(int64_t M, int64_t N, int64_t K, const uint8_t* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* maxima = reinterpret_cast<uint32_t*>(ws + l.maxima);
-  float* y = reinterpret_cast<float*>(ws + l.y);
+  uint16_t* y = reinterpret_cast<uint16_t*>(ws + l.y);
   const bool per_row = out_mode == kRowwise;
   hipError_t e = fp8gemm::launch_zero_words(maxima, per_row ? M : 1, s);
   if (e != hipSuccess) return FP8GEMM_ERROR_LAUNCH;
   st = run_dense(M, N, K, A, lda, a_format, B, ldb, b_format, mode, scale_a, scale_b, bias,
-                 activation, y, l.ldy, fp8gemm::kF32Max, reinterpret_cast<uint8_t*>(maxima),
+                 activation, y, l.ldy, fp8gemm::kBF16Max, reinterpret_cast<uint8_t*>(maxima),
                  per_row ? 1 : 0, workspace, l.maxima, stream);
   if (st != FP8GEMM_SUCCESS) return st;
   return from_hip(fp8gemm::launch_requant(

@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "launch.h"
 
 namespace fp8gemm {
@@ -159,6 +161,28 @@ __device__ __forceinline__ _Float16 to_out<_Float16>(float v) {
 template <>
 __device__ __forceinline__ __bf16 to_out<__bf16>(float v) {
   return (__bf16)v;
+}
+
+// bf16 output whose magnitudes the epilogue also folds into maxima (the first
+// half of the requantised output): stored exactly as __bf16.
+struct bf16_max {
+  uint16_t bits;
+};
+template <typename OutT>
+constexpr bool kTrackMax = std::is_same<OutT, bf16_max>::value;
+
+template <>
+__device__ __forceinline__ bf16_max to_out<bf16_max>(float v) {
+  return __builtin_bit_cast(bf16_max, (__bf16)v);
+}
+
+// Largest magnitude of the bf16 values packed in n 32-bit words (two per word).
+__device__ __forceinline__ float absmax_bf16(const uint32_t* w, int n) {
+  float a = 0.0f;
+  for (int i = 0; i < n; ++i)
+    a = fmaxf(a, fmaxf(fabsf(__uint_as_float(w[i] << 16)),
+                       fabsf(__uint_as_float(w[i] & 0xffff0000u))));
+  return a;
 }
 
 // Four consecutive outputs packed into 8 bytes.

@@ -127,7 +127,8 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void gemm_persistent_kernel(GemmP
                  __attribute__((always_inline)) {
     int m0, n0;
     src.coords(i, m0, n0);
-    epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, p.ldc, m0, n0, ts, rbuf);
+    epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, p.ldc, m0, n0, ts, rbuf, nullptr, kActNone, p.cs,
+                                     p.ldcs);
   };
   // epilogue_direct issues two 16-byte stores per 32 x 32 block and lane
   if (count > 0)
@@ -328,7 +329,8 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void splitk_kernel
     epilogue_fused<Cfg, MODE, OutT>(sum, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N, ts,
                                     p.bias, p.act, p.cs, p.ldcs);
   else
-    epilogue<Cfg, MODE, OutT>(sum, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N, ts);
+    epilogue<Cfg, MODE, OutT>(sum, lds, static_cast<OutT*>(p.C), p.ldc, m0, p.M, n0, p.N, ts, p.cs,
+                              p.ldcs);
 }
 
 template <int MODE, typename OutT, bool FUSED>
@@ -411,17 +413,17 @@ hipError_t FP8GEMM_LAUNCH_NAME(const GemmProblem& p, int mode, int out, hipStrea
   if (out == kF16) return launch_any<kMx32, _Float16>(p, stream);
 #if !FP8GEMM_KN
   if (out == kE4M3Mx) return launch_any<kMx32, uint8_t>(p, stream);
-  if (out == kF32Max) return launch_plan<kMx32, float, true>(p, stream);
+  if (out == kBF16Max) return launch_any<kMx32, bf16_max>(p, stream);
 #endif
   return launch_any<kMx32, __bf16>(p, stream);
 #else
 #if !FP8GEMM_KN
-  // the fp32 output with its maxima always takes the fused kernels (their
-  // epilogues carry the atomic maxima)
-  if (out == kF32Max) {
-    if (mode == kTensor) return launch_plan<kTensor, float, true>(p, stream);
-    if (mode == kRowwise) return launch_plan<kRowwise, float, true>(p, stream);
-    return launch_plan<kMx32, float, true>(p, stream);
+  // the bf16 output with its maxima: the same kernels and epilogue arithmetic as
+  // the plain bf16 output (so its values are those of fp8gemm_run_ex)
+  if (out == kBF16Max) {
+    if (mode == kTensor) return launch_any<kTensor, bf16_max>(p, stream);
+    if (mode == kRowwise) return launch_any<kRowwise, bf16_max>(p, stream);
+    return launch_any<kMx32, bf16_max>(p, stream);
   }
 #endif
   if (out == kE4M3Mx) {

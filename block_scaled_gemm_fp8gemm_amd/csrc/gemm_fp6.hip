@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void fp6_kernel(GemmProblem p, int tiles_m,
     epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, p.ldc, m0, p.M, n0, p.N, 1.0f, p.bias, p.act,
                                     p.cs, p.ldcs);
   else
-    epilogue<Cfg, MODE, OutT>(acc, lds, C, p.ldc, m0, p.M, n0, p.N, 1.0f);
+    epilogue<Cfg, MODE, OutT>(acc, lds, C, p.ldc, m0, p.M, n0, p.N, 1.0f, p.cs, p.ldcs);
 }
 
 // ---------------------------------------------------------------------------
@@ -486,7 +486,9 @@ template <int FA, int FB>
 hipError_t launch_formats(const GemmProblem& p, int out, hipStream_t stream) {
   const bool fused = p.bias != nullptr || p.act != kActNone;
   if (out == kE4M3Mx) return launch_typed<FA, FB, uint8_t, true>(p, stream);
-  if (out == kF32Max) return launch_typed<FA, FB, float, true>(p, stream);
+  if (out == kBF16Max)
+    return fused ? launch_typed<FA, FB, bf16_max, true>(p, stream)
+                 : launch_typed<FA, FB, bf16_max, false>(p, stream);
   if (out == kF16)
     return fused ? launch_typed<FA, FB, _Float16, true>(p, stream)
                  : launch_typed<FA, FB, _Float16, false>(p, stream);

@@ -1624,10 +1624,48 @@ __device__ __forceinline__ float activate(float v, int act) {
   return v;
 }
 
+// Maxima of the requantised output (OutT = bf16_max): cs holds them as uint32_t
+// (the bits of a non-negative float order like the float); ldcs != 0: one per
+// row of C, else one for the whole output.  fold_row_max reduces a value over the
+// `width` consecutive lanes that hold pieces of row m and lets the group's first
+// lane fold it into that row (valid rows only); with one maximum it returns the
+// running maximum instead, which fold_tensor_max folds once per wave.  Every lane
+// of the wave takes part in both (shuffles).
+__device__ __forceinline__ float fold_row_max(uint8_t* cs, int64_t ldcs, int m, bool valid, float a,
+                                              int width, int lane, float run) {
+  if (ldcs != 0) {
+    a = group_max(a, width);
+    if (lane % width == 0 && valid && a > 0.0f)
+      atomicMax(reinterpret_cast<uint32_t*>(cs) + m, __float_as_uint(a));
+    return run;
+  }
+  return fmaxf(run, a);
+}
+
+__device__ __forceinline__ void fold_tensor_max(uint8_t* cs, int64_t ldcs, float run, int lane) {
+  if (ldcs == 0) {
+    run = wave_max(run);
+    if (lane == 0 && run > 0.0f) atomicMax(reinterpret_cast<uint32_t*>(cs), __float_as_uint(run));
+  }
+}
+
+// The same for the register epilogues, where row r's values sit in lanes r and
+// r + 32 (h = lane / 32): the pair's maximum, folded by the low lane.
+__device__ __forceinline__ float fold_pair_max(uint8_t* cs, int64_t ldcs, int m, float a, int h,
+                                               float run) {
+  if (ldcs != 0) {
+    a = fmaxf(a, __shfl_xor(a, 32, 64));
+    if (h == 0 && a > 0.0f) atomicMax(reinterpret_cast<uint32_t*>(cs) + m, __float_as_uint(a));
+    return run;
+  }
+  return fmaxf(run, a);
+}
+
 template <class Cfg, int MODE, typename OutT>
 __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN], uint8_t* lds,
                                          OutT* C, int64_t ldc, int m0, int m_end, int n0, int N,
-                                         float tensor_scale) {
+                                         float tensor_scale, uint8_t* cs = nullptr,
+                                         int64_t ldcs = 0) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   constexpr int kChunksPerRow = Cfg::WN * 2 / 16;        // 16-byte chunks of a staged row
   constexpr int kRowsPerInst = 64 / kChunksPerRow;
@@ -1639,6 +1677,7 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFr
   const int h = lane >> 5;
   uint8_t* stage = lds + wave * 32 * Cfg::kStagePitch;
   const float* rsc = reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff);
+  float run = 0.0f;                                      // bf16_max, one maximum: this wave's
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int r = lane & 31;                             // staged row of this lane
@@ -1670,21 +1709,33 @@ __device__ __forceinline__ void epilogue(const v16f (&acc)[Cfg::kFragM][Cfg::kFr
       const v4i val = *reinterpret_cast<const v4i*>(stage + rr * Cfg::kStagePitch + ch * 16);
       const int m = m0 + wm * Cfg::WM + i * 32 + rr;
       const int n = n0 + wn * Cfg::WN + ch * 8;
+      float a = 0.0f;
       if (m < m_end) {
         OutT* dst = C + (int64_t)m * ldc + n;
         if (n + 8 <= N) {
           *reinterpret_cast<v4i*>(dst) = val;
+          if constexpr (kTrackMax<OutT>)
+            a = absmax_bf16(reinterpret_cast<const uint32_t*>(&val), 4);
         } else {
           OutT o[8];
           __builtin_memcpy(o, &val, 16);
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (n + e < N) dst[e] = o[e];
+            if (n + e < N) {
+              dst[e] = o[e];
+              if constexpr (kTrackMax<OutT>) {
+                const uint32_t b = (uint32_t)__builtin_bit_cast(uint16_t, o[e]);
+                a = fmaxf(a, absmax_bf16(&b, 1));
+              }
+            }
         }
       }
+      if constexpr (kTrackMax<OutT>)
+        run = fold_row_max(cs, ldcs, m, m < m_end, a, kChunksPerRow, lane, run);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);                  // reads done before the next block
   }
+  if constexpr (kTrackMax<OutT>) fold_tensor_max(cs, ldcs, run, lane);
 }
 
 // Bias (and ReLU) epilogue of a full tile from registers, the layout of
@@ -1695,7 +1746,8 @@ template <class Cfg, int MODE, typename OutT, int ACT>
 __device__ __forceinline__ void epilogue_direct_bias(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                      uint8_t* lds, OutT* C, int64_t ldc,
                                                      int m0, int n0, float tensor_scale,
-                                                     const float* bias) {
+                                                     const float* bias, uint8_t* cs,
+                                                     int64_t ldcs) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -1707,6 +1759,9 @@ __device__ __forceinline__ void epilogue_direct_bias(const v16f (&acc)[Cfg::kFra
   float* bl = reinterpret_cast<float*>(lds) + wave * Cfg::WN;
 #pragma unroll
   for (int c = lane; c < Cfg::WN; c += 64) bl[c] = bias != nullptr ? bias[nw + c] : 0.0f;
+  float am[FM];                                          // bf16_max: row maxima of the lane
+#pragma unroll
+  for (int i = 0; i < FM; ++i) am[i] = 0.0f;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -1734,6 +1789,7 @@ __device__ __forceinline__ void epilogue_direct_bias(const v16f (&acc)[Cfg::kFra
             v[e] = activate(v[e] + bv[e], ACT);
           }
           w[q] = pack4<OutT>(v[0], v[1], v[2], v[3]);
+          if constexpr (kTrackMax<OutT>) am[i] = fmaxf(am[i], absmax_bf16(&w[q].x, 2));
         }
         const auto sx = __builtin_amdgcn_permlane32_swap(w[0].x, w[1].x, false, false);
         const auto sy = __builtin_amdgcn_permlane32_swap(w[0].y, w[1].y, false, false);
@@ -1741,6 +1797,13 @@ __device__ __forceinline__ void epilogue_direct_bias(const v16f (&acc)[Cfg::kFra
         *reinterpret_cast<v4i*>(crow + j * 32 + 16 * k + 8 * h) = out;
       }
     }
+  }
+  if constexpr (kTrackMax<OutT>) {
+    float run = 0.0f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      run = fold_pair_max(cs, ldcs, m0 + wm * Cfg::WM + i * 32 + (lane & 31), am[i], h, run);
+    fold_tensor_max(cs, ldcs, run, lane);
   }
 }
 
@@ -1758,18 +1821,23 @@ template <class Cfg, int MODE, typename OutT, bool BIAS = false>
 __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                 uint8_t* lds, OutT* C, int64_t ldc, int m0,
                                                 int n0, float tensor_scale, int rbuf = 0,
-                                                const float* bias = nullptr, int act = kActNone) {
+                                                const float* bias = nullptr, int act = kActNone,
+                                                uint8_t* cs = nullptr, int64_t ldcs = 0) {
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   static_assert(sizeof(OutT) == 2, "16-bit outputs");
   if constexpr (BIAS) {
     if (act == kActGelu)
-      epilogue_direct_bias<Cfg, MODE, OutT, kActGelu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias);
+      epilogue_direct_bias<Cfg, MODE, OutT, kActGelu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias,
+                                                      cs, ldcs);
     else if (act == kActSilu)
-      epilogue_direct_bias<Cfg, MODE, OutT, kActSilu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias);
+      epilogue_direct_bias<Cfg, MODE, OutT, kActSilu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias,
+                                                      cs, ldcs);
     else if (act == kActRelu)
-      epilogue_direct_bias<Cfg, MODE, OutT, kActRelu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias);
+      epilogue_direct_bias<Cfg, MODE, OutT, kActRelu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias,
+                                                      cs, ldcs);
     else
-      epilogue_direct_bias<Cfg, MODE, OutT, kActNone>(acc, lds, C, ldc, m0, n0, tensor_scale, bias);
+      epilogue_direct_bias<Cfg, MODE, OutT, kActNone>(acc, lds, C, ldc, m0, n0, tensor_scale, bias,
+                                                      cs, ldcs);
     return;
   }
   const int lane = threadIdx.x & 63;
@@ -1778,6 +1846,7 @@ __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][C
   const int h = lane >> 5;
   const float* rsc =
       reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff + rbuf * (Cfg::BM + Cfg::BN) * 4);
+  float run = 0.0f;                                      // bf16_max, one maximum: this wave's
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int r = wm * Cfg::WM + i * 32 + (lane & 31);   // tile row of this lane
@@ -1785,6 +1854,7 @@ __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][C
     if (MODE == kTensor) fa = tensor_scale;
     if (MODE == kRowwise) fa = rsc[r];
     OutT* crow = C + (int64_t)(m0 + r) * ldc + n0 + wn * Cfg::WN;
+    float am = 0.0f;                                     // bf16_max: this lane's row maximum
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -1803,6 +1873,7 @@ __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][C
             for (int e = 0; e < 4; ++e) v[e] *= fb[e];
           }
           w[q] = pack4<OutT>(v[0], v[1], v[2], v[3]);
+          if constexpr (kTrackMax<OutT>) am = fmaxf(am, absmax_bf16(&w[q].x, 2));
         }
         // low half keeps group 2k and takes the high half's; high half keeps 2k + 1
         const auto sx = __builtin_amdgcn_permlane32_swap(w[0].x, w[1].x, false, false);
@@ -1811,73 +1882,9 @@ __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][C
         *reinterpret_cast<v4i*>(crow + j * 32 + 16 * k + 8 * h) = out;
       }
     }
+    if constexpr (kTrackMax<OutT>) run = fold_pair_max(cs, ldcs, m0 + r, am, h, run);
   }
-}
-
-// fp32 output of a full tile straight from registers, with the bias, the
-// activation ACT and the maxima of the staged epilogue's float output (cs as
-// uint32_t maxima; ldcs != 0: one per row, else one for the whole output).  A
-// lane stores each of its groups of four consecutive columns as one 16-byte
-// piece (lanes r and r + 32 together cover 32 bytes of row r per store, the
-// four groups of a block 128 bytes); its row maximum is its own values and its
-// partner lane's.  The bias is copied into a wave-private stretch of the free
-// ring first, as in epilogue_direct_bias.
-template <class Cfg, int MODE, int ACT>
-__device__ __forceinline__ void epilogue_direct_f32(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
-                                                    uint8_t* lds, float* C, int64_t ldc, int m0,
-                                                    int n0, float tensor_scale, const float* bias,
-                                                    uint8_t* cs, int64_t ldcs) {
-  constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
-  const int h = lane >> 5;
-  const float* rsc = reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff);
-  const int nw = n0 + wn * Cfg::WN;                      // first column of this wave
-  static_assert(Cfg::kWaves * Cfg::WN * 4 <= Cfg::kSlots * Cfg::kSlotBytes, "bias fits the ring");
-  float* bl = reinterpret_cast<float*>(lds) + wave * Cfg::WN;
-#pragma unroll
-  for (int c = lane; c < Cfg::WN; c += 64) bl[c] = bias != nullptr ? bias[nw + c] : 0.0f;
-  uint32_t* amax = reinterpret_cast<uint32_t*>(cs);
-  float run = 0.0f;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int r = wm * Cfg::WM + i * 32 + (lane & 31);   // tile row of this lane
-    float fa = 1.0f;
-    if (MODE == kTensor) fa = tensor_scale;
-    if (MODE == kRowwise) fa = rsc[r];
-    float* crow = C + (int64_t)(m0 + r) * ldc + nw;
-    float a = 0.0f;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = j * 32 + 8 * g + 4 * h;             // wave-local column of value 0
-        v4f fb{1.0f, 1.0f, 1.0f, 1.0f};
-        if (MODE == kRowwise) fb = *reinterpret_cast<const v4f*>(rsc + Cfg::BM + wn * Cfg::WN + c);
-        const v4f bv = *reinterpret_cast<const v4f*>(bl + c);
-        v4f v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = acc[i][j][4 * g + e] * fa;
-          if (MODE == kRowwise) x *= fb[e];
-          v[e] = activate(x + bv[e], ACT);
-          a = fmaxf(a, fabsf(v[e]));
-        }
-        *reinterpret_cast<v4f*>(crow + c) = v;
-      }
-    }
-    if (ldcs != 0) {
-      a = fmaxf(a, __shfl_xor(a, 32, 64));               // the other half of the row
-      if (h == 0 && a > 0.0f) atomicMax(amax + m0 + r, __float_as_uint(a));
-    } else {
-      run = fmaxf(run, a);
-    }
-  }
-  if (ldcs == 0) {
-    run = wave_max(run);
-    if (lane == 0 && run > 0.0f) atomicMax(amax, __float_as_uint(run));
-  }
+  if constexpr (kTrackMax<OutT>) fold_tensor_max(cs, ldcs, run, lane);
 }
 
 // The output quantised for the next layer, straight from registers (interior
@@ -1961,11 +1968,8 @@ __device__ __forceinline__ void epilogue_direct_q(const v16f (&acc)[Cfg::kFragM]
 // the quantisers), written to cs[m * ldcs + n / 32]; N % 32 == 0.  The 32
 // columns of a block are the four-column pieces of 8 consecutive lanes, so the
 // block maximum takes three xor-shuffles.
-// With OutT = float the fp32 result is stored as it is and its magnitudes are
-// folded into the maxima at cs (read as uint32_t: the bits of a non-negative
-// float order like the float): ldcs != 0, one maximum per row of C (the lanes
-// of a row reduce by xor-shuffles, then one atomic max per row and block of 32
-// rows); ldcs == 0, one maximum for the whole output (one atomic per wave).
+// With OutT = bf16_max the stored bf16 values' magnitudes are also folded into
+// the maxima at cs (see fold_row_max).
 template <class Cfg, int MODE, typename OutT>
 __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
                                                uint8_t* lds, OutT* C, int64_t ldc, int m0,
@@ -1973,7 +1977,6 @@ __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cf
                                                const float* bias, int act,
                                                uint8_t* cs = nullptr, int64_t ldcs = 0) {
   constexpr bool kQ = std::is_same<OutT, uint8_t>::value;
-  constexpr bool kF = std::is_same<OutT, float>::value;
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   constexpr int kPitch = Cfg::WN + 4;                    // staged fp32 row (+16 bytes)
   constexpr int kPiecesPerRow = Cfg::WN / 4;
@@ -1982,7 +1985,7 @@ __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cf
                 "fp32 staging fits in the ring");
   static_assert((32 * kPiecesPerRow) % 64 == 0, "whole store instructions");
   static_assert(64 % kPiecesPerRow == 0, "a lane keeps its columns over the store loop");
-  static_assert(sizeof(OutT) == 2 || kQ || kF, "16-bit or fp32 outputs or e4m3 codes");
+  static_assert(sizeof(OutT) == 2 || kQ, "16-bit outputs or e4m3 codes");
   static_assert(!kQ || kPiecesPerRow % 8 == 0, "32-column blocks inside one lane group");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -1999,8 +2002,7 @@ __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cf
     for (int e = 0; e < 4; ++e) bv[e] = n + e < N ? bias[n + e] : 0.0f;
   }
   const float* rsc = reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff);
-  uint32_t* amax = reinterpret_cast<uint32_t*>(cs);      // kF: the maxima
-  float run = 0.0f;                                      // kF, one maximum: this wave's
+  float run = 0.0f;                                      // bf16_max, one maximum: this wave's
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int r = lane & 31;
@@ -2045,46 +2047,33 @@ __device__ __forceinline__ void epilogue_fused(const v16f (&acc)[Cfg::kFragM][Cf
           *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(C) + (int64_t)m * ldc + n) = w;
           if ((lane & 7) == 0) cs[(int64_t)m * ldcs + (n >> 5)] = (uint8_t)code;
         }
-      } else if constexpr (kF) {
+      } else {
+        const uint2 w = pack4<OutT>(v[0], v[1], v[2], v[3]);
         float a = 0.0f;
         if (m < m_end) {
-          float* dst = reinterpret_cast<float*>(C) + (int64_t)m * ldc + n;
+          OutT* dst = C + (int64_t)m * ldc + n;
           if (n + 4 <= N) {
-            *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};
-            a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+            *reinterpret_cast<uint2*>(dst) = w;
+            if constexpr (kTrackMax<OutT>) a = absmax_bf16(&w.x, 2);
           } else {
             for (int e = 0; e < 4; ++e)
               if (n + e < N) {
-                dst[e] = v[e];
-                a = fmaxf(a, fabsf(v[e]));
+                const OutT o = to_out<OutT>(v[e]);
+                dst[e] = o;
+                if constexpr (kTrackMax<OutT>) {
+                  const uint32_t b = (uint32_t)__builtin_bit_cast(uint16_t, o);
+                  a = fmaxf(a, absmax_bf16(&b, 1));
+                }
               }
           }
         }
-        if (ldcs != 0) {
-          a = group_max(a, kPiecesPerRow);               // the lanes of row m
-          if (lane % kPiecesPerRow == 0 && m < m_end && a > 0.0f)
-            atomicMax(amax + m, __float_as_uint(a));
-        } else {
-          run = fmaxf(run, a);
-        }
-      } else if (m < m_end) {
-        OutT* dst = C + (int64_t)m * ldc + n;
-        if (n + 4 <= N) {
-          *reinterpret_cast<uint2*>(dst) = pack4<OutT>(v[0], v[1], v[2], v[3]);
-        } else {
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) dst[e] = to_out<OutT>(v[e]);
-        }
+        if constexpr (kTrackMax<OutT>)
+          run = fold_row_max(cs, ldcs, m, m < m_end, a, kPiecesPerRow, lane, run);
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);                  // reads done before the next block
   }
-  if constexpr (kF) {
-    if (ldcs == 0) {
-      run = wave_max(run);
-      if (lane == 0 && run > 0.0f) atomicMax(amax, __float_as_uint(run));
-    }
-  }
+  if constexpr (kTrackMax<OutT>) fold_tensor_max(cs, ldcs, run, lane);
 }
 
 // Epilogue of a full interior tile (every row and column valid): straight from
@@ -2095,21 +2084,9 @@ __device__ __forceinline__ void epilogue_full_tile(const v16f (&acc)[Cfg::kFragM
                                                    int m_end, int n0, int N, float tensor_scale,
                                                    const float* bias, int act, uint8_t* cs,
                                                    int64_t ldcs) {
-  if constexpr (std::is_same<OutT, float>::value) {
-    if (act == kActGelu)
-      epilogue_direct_f32<Cfg, MODE, kActGelu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias, cs,
-                                               ldcs);
-    else if (act == kActSilu)
-      epilogue_direct_f32<Cfg, MODE, kActSilu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias, cs,
-                                               ldcs);
-    else if (act == kActRelu)
-      epilogue_direct_f32<Cfg, MODE, kActRelu>(acc, lds, C, ldc, m0, n0, tensor_scale, bias, cs,
-                                               ldcs);
-    else
-      epilogue_direct_f32<Cfg, MODE, kActNone>(acc, lds, C, ldc, m0, n0, tensor_scale, bias, cs,
-                                               ldcs);
-  } else if constexpr (FUSED && !std::is_same<OutT, uint8_t>::value) {
-    epilogue_direct<Cfg, MODE, OutT, true>(acc, lds, C, ldc, m0, n0, tensor_scale, 0, bias, act);
+  if constexpr (FUSED && !std::is_same<OutT, uint8_t>::value) {
+    epilogue_direct<Cfg, MODE, OutT, true>(acc, lds, C, ldc, m0, n0, tensor_scale, 0, bias, act,
+                                           cs, ldcs);
   } else if constexpr (FUSED) {
     epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act,
                                     cs, ldcs);
@@ -2117,9 +2094,10 @@ __device__ __forceinline__ void epilogue_full_tile(const v16f (&acc)[Cfg::kFragM
     epilogue_direct_q<Cfg, MODE>(acc, lds, C, ldc, m0, n0, tensor_scale, cs, ldcs);
   } else {
 #if FP8GEMM_DIRECT_EPILOGUE
-    epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, n0, tensor_scale);
+    epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, n0, tensor_scale, 0, nullptr, kActNone,
+                                     cs, ldcs);
 #else
-    epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
+    epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, cs, ldcs);
 #endif
   }
 }
@@ -2135,7 +2113,7 @@ __device__ __forceinline__ void epilogue_any_tile(const v16f (&acc)[Cfg::kFragM]
     epilogue_fused<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, bias, act,
                                     cs, ldcs);
   else
-    epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale);
+    epilogue<Cfg, MODE, OutT>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale, cs, ldcs);
 }
 
 // One output tile: the interior mainloop when the tile qualifies, else the

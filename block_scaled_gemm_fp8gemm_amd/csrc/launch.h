@@ -27,11 +27,12 @@ hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t k, int64_t l
 enum ScaleMode : int { kTensor = 0, kRowwise = 1, kMx32 = 2 };
 // kE4M3Mx: e4m3 codes with an E8M0 scale per 32 columns of each row (the fused
 // epilogue quantises the output for the next layer; codes to C, scales to cs).
-// kF32Max: the fp32 result to C (ldc in floats) and the maxima of its magnitudes
-// folded into cs, read as uint32_t (atomic max on the bits of non-negative
-// floats): one per row when ldcs != 0, one for the whole output when ldcs == 0;
-// the first half of the requantised output (launch_requant encodes).
-enum OutType : int { kF16 = 0, kBF16 = 1, kE4M3Mx = 2, kF32Max = 3 };
+// kBF16Max: the bf16 result to C exactly as kBF16 writes it, and the maxima of
+// the stored values' magnitudes folded into cs, read as uint32_t (atomic max on
+// the bits of non-negative floats): one per row when ldcs != 0, one for the whole
+// output when ldcs == 0; the first half of the requantised output
+// (launch_requant encodes).
+enum OutType : int { kF16 = 0, kBF16 = 1, kE4M3Mx = 2, kBF16Max = 3 };
 // Element formats of the codes; the values are the operand-format fields of the
 // F8F6F4 MFMA (e2m3 / e3m2 = FP6, four codes in three bytes; e2m1 = FP4, two
 // codes per byte; the narrow formats take MX scales only).
@@ -52,7 +53,7 @@ struct GemmProblem {
   void* workspace;      // split-K partials and tile counters (gemm_workspace_bytes)
   const float* bias;    // fused epilogue: fp32 [N] added after the scales, or null
   int act;              // fused epilogue: Activation applied last
-  uint8_t* cs = nullptr;  // kE4M3Mx: E8M0 codes of C, cs[m * ldcs + n / 32]; kF32Max: maxima
+  uint8_t* cs = nullptr;  // kE4M3Mx: E8M0 codes of C, cs[m * ldcs + n / 32]; kBF16Max: maxima
   int64_t ldcs = 0;
 };
 
@@ -103,13 +104,13 @@ struct GroupedProblem {
   int64_t ldc;
 };
 
-// Second half of the requantised output: y fp32 [rows][n] (pitch ldy floats) to
-// codes q (fmt kE4M3 or kE5M2, pitch ldq bytes) with s = fl32(amax / max of the
-// format) (1 if amax = 0) and q = RNE_sat(fl32(y / s)), the quantisers' rule.
-// per_row: amax[r] (uint32_t bits of a non-negative float) for row r and
-// scales[r] = s; else amax[0] and scales[0] for every row.  n % 4 == 0 (whole
-// 4-byte code groups).
-hipError_t launch_requant(const float* y, int64_t rows, int64_t n, int64_t ldy,
+// Second half of the requantised output: y bf16 [rows][n] (pitch ldy elements,
+// a multiple of 8) to codes q (fmt kE4M3 or kE5M2, pitch ldq bytes) with s =
+// fl32(amax / max of the format) (1 if amax = 0) and q = RNE_sat(fl32(y / s)),
+// the quantisers' rule on y's values.  per_row: amax[r] (uint32_t bits of a
+// non-negative float) for row r and scales[r] = s; else amax[0] and scales[0] for
+// every row.  n % 8 == 0 (whole 8-byte code groups).
+hipError_t launch_requant(const uint16_t* y, int64_t rows, int64_t n, int64_t ldy,
                           const uint32_t* amax, bool per_row, uint8_t* q, int64_t ldq,
                           float* scales, int fmt, hipStream_t stream);
 // p[0 .. count) = 0 with a kernel (no memset node, so the call can be captured).

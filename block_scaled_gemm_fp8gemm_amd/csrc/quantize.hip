@@ -289,14 +289,18 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const float* __restr
 }
 
 // ---- the requantised GEMM output: maxima from the GEMM epilogue, then encode ---
-// The GEMM kernels stored y in fp32 and folded |y| into amax (per row or one for
-// the output; zeroed by zero_words_kernel before the GEMM); this pass derives
-// the scales by the per-tensor / row-wise rule above and encodes.  One
-// wavefront per row (rows dealt to wavefronts in turn), 1024 columns per step
-// as in load_unit.
+// The GEMM kernels stored y in bf16 and folded the stored values' magnitudes into
+// amax (per row or one for the output; zeroed by zero_words_kernel before the
+// GEMM); this pass derives the scales by the per-tensor / row-wise rule above and
+// encodes y's values (exact in fp32) with it, as quantising the bf16 output
+// would.  One wavefront per row (rows dealt to wavefronts in turn), 1024 columns
+// per step: lane l takes the 8 values at columns 512 j + 8 l (j = 0, 1), so each
+// 16-byte load and 8-byte code store instruction covers one contiguous run.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 template <int FMT, bool PER_ROW>
-__global__ __launch_bounds__(kThreads) void requant_kernel(const float* __restrict__ y, int rows,
-                                                           int n, int64_t ldy,
+__global__ __launch_bounds__(kThreads) void requant_kernel(const uint16_t* __restrict__ y,
+                                                           int rows, int n, int64_t ldy,
                                                            const uint32_t* __restrict__ amax,
                                                            uint8_t* __restrict__ q, int64_t ldq,
                                                            float* __restrict__ scales) {
@@ -315,12 +319,26 @@ __global__ __launch_bounds__(kThreads) void requant_kernel(const float* __restri
       s = (m == 0.0f) ? 1.0f : m / elem_max<FMT>();
       if (lane == 0) scales[r] = s;
     }
-    const float* yr = y + (int64_t)r * ldy;
+    const uint16_t* yr = y + (int64_t)r * ldy;
     uint8_t* qr = q + (int64_t)r * ldq;
     for (int c0 = 0; c0 < n; c0 += 1024) {
-      uint32_t w[4];
-      encode_unit_div<FMT>(load_unit(yr, c0, n, lane), s, w);
-      store_codes(qr, c0, n, lane, w);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = c0 + 512 * j + 8 * lane;
+        if (c < n) {
+          const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(yr + c));
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[2 * e] = __uint_as_float(w[e] << 16);
+            x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+          }
+          uint2 o;
+          o.x = encode4<FMT>(x[0] / s, x[1] / s, x[2] / s, x[3] / s);
+          o.y = encode4<FMT>(x[4] / s, x[5] / s, x[6] / s, x[7] / s);
+          *reinterpret_cast<uint2*>(qr + c) = o;
+        }
+      }
     }
   }
 }
@@ -389,8 +407,9 @@ hipError_t quantize_mx_fmt(const float* x, int64_t rows, int64_t k, int64_t ldx,
 }
 
 template <int FMT>
-hipError_t requant_fmt(const float* y, int64_t rows, int64_t n, int64_t ldy, const uint32_t* amax,
-                       bool per_row, uint8_t* q, int64_t ldq, float* scales, hipStream_t stream) {
+hipError_t requant_fmt(const uint16_t* y, int64_t rows, int64_t n, int64_t ldy,
+                       const uint32_t* amax, bool per_row, uint8_t* q, int64_t ldq, float* scales,
+                       hipStream_t stream) {
   const int grid = grid_for((uint64_t)rows, kWaves, 16384);
   if (per_row)
     hipLaunchKernelGGL((requant_kernel<FMT, true>), dim3(grid), dim3(kThreads), 0, stream, y,
@@ -433,7 +452,7 @@ hipError_t launch_zero_words(uint32_t* p, int64_t count, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_requant(const float* y, int64_t rows, int64_t n, int64_t ldy,
+hipError_t launch_requant(const uint16_t* y, int64_t rows, int64_t n, int64_t ldy,
                           const uint32_t* amax, bool per_row, uint8_t* q, int64_t ldq,
                           float* scales, int fmt, hipStream_t stream) {
   if (fmt == kE5M2)

@@ -233,34 +233,37 @@ fp8gemm_status fp8gemm_run_mxout(int64_t M, int64_t N, int64_t K, const uint8_t*
 /* fresh per-tensor or per-row scale (the Cutlass-named Triton FP8 post fuses    */
 /* epilogues to save a round trip of C; the JAX/Triton Blackwell FP8 GEMM post's */
 /* operands are E4M3 codes with their scale factors, the form this produces).    */
-/* y = act(scaled GEMM + bias) as fp8gemm_run_ex computes it in fp32, then the   */
-/* rule of fp8gemm_quantize_ex applied to y:                                    */
-/*   out_mode TENSOR : s = fl32(amax/fmax) over all of y (1 if amax = 0),        */
+/* The layer's output C16 is the bf16 result fp8gemm_run_ex computes (scaled     */
+/* GEMM + bias, activation, RNE to bf16); the codes are the rule of             */
+/* fp8gemm_quantize_ex applied to C16's values:                                 */
+/*   out_mode TENSOR : s = fl32(amax/fmax) over all of C16 (1 if amax = 0),      */
 /*                     c_scales -> float[1];                                    */
-/*   out_mode ROWWISE: the same per row of C, c_scales -> float[M] (the scale_a  */
-/*                     of a row-wise GEMM that takes C as its A operand);       */
-/*   q = RNE_sat(fl32(y/s)), fmax = 448 (c_format E4M3) or 57344 (E5M2).        */
-/* The GEMM kernels store y in fp32 to the workspace and fold |y| into per-row  */
-/* (or one) atomic maxima in their epilogue; a second, HBM-streaming kernel     */
-/* derives the scales and encodes (the maxima are zeroed by a small kernel     */
-/* before the GEMM, so no memset node is recorded under graph capture).         */
+/*   out_mode ROWWISE: the same per row, c_scales -> float[M] (the scale_a of a  */
+/*                     row-wise GEMM that takes C as its A operand);            */
+/*   q = RNE_sat(fl32(C16/s)), fmax = 448 (c_format E4M3) or 57344 (E5M2).      */
+/* The result is bit-identical to fp8gemm_run_ex with bf16 output followed by   */
+/* fp8gemm_quantize_ex on that output (as fp32).  The GEMM kernels store C16 to  */
+/* the workspace and fold its magnitudes into per-row (or one) atomic maxima in */
+/* their epilogue; a second, HBM-streaming kernel derives the scales and encodes */
+/* (the maxima are zeroed by a small kernel first, so no memset node is        */
+/* recorded under graph capture).                                               */
 /*   C       : device uint8 codes, element (m,n) at C[m*ldc+n]; ldc >= N, a      */
 /*             multiple of 16; 16-byte aligned.  N % 16 == 0 (else              */
 /*             NOT_SUPPORTED).  c_scales 4-byte aligned.                         */
 /*   c_format: E4M3 or E5M2 (another format is NOT_SUPPORTED); out_mode TENSOR   */
 /*             or ROWWISE (else INVALID_VALUE).                                 */
-/*   workspace: fp8gemm_qout_workspace_size(M, N, K, mode) bytes (4-byte words  */
-/*             for the maxima and M x N fp32 values for y, after the GEMM's own */
-/*             workspace), 16-byte aligned; zero-fill it before its first use   */
-/*             (the GEMM's split-K counters, left at zero by every call).  One  */
-/*             workspace serves calls of every shape one after another; calls   */
-/*             that may overlap need their own.                                 */
+/*   workspace: fp8gemm_qout_workspace_size(M, N, K, mode) bytes (M 4-byte      */
+/*             maxima and C16, M x N bf16, after the GEMM's own workspace),     */
+/*             16-byte aligned; zero-fill it before its first use (the GEMM's   */
+/*             split-K counters, left at zero by every call).  One workspace    */
+/*             serves calls of every shape one after another; calls that may    */
+/*             overlap need their own.                                          */
 /* A, B, formats (FP8, FP4 and FP6 pairs as fp8gemm_run_ex), mode, scales, bias, */
 /* activation and the other errors as fp8gemm_run_ex.                          */
-/* Accuracy: s lies between the scales of the largest |y_ref| minus and plus    */
-/* the fp8gemm_run_ex bound (tol), and each code dequantises (value times s) to */
-/* within tol plus half a spacing of the format at its magnitude (and the       */
-/* saturation of the maximum itself) of y_ref.                                 */
+/* Accuracy: with tol the fp8gemm_run_ex bound plus half a bf16 ulp, s lies     */
+/* between the scales of the largest |y_ref| minus and plus tol, and each code  */
+/* dequantises (value times s) to within tol plus half a spacing of the format  */
+/* at its magnitude (and the saturation of the maximum itself) of y_ref.        */
 /* ------------------------------------------------------------------------- */
 size_t fp8gemm_qout_workspace_size(int64_t M, int64_t N, int64_t K, int mode);
 

@@ -205,7 +205,8 @@ def within_bound(C_test, C_ref, abs_ref, out: str) -> np.ndarray:
 
 
 def round_to_output(x: np.ndarray, out: str) -> np.ndarray:
-    """Round-to-nearest-even of float64 values onto the output format (diagnostics).
+    """Round-to-nearest-even of float64 values onto the output format (the 16-bit
+    layer output in references; diagnostics).
 
     Values whose rounding exceeds the largest finite number become +-inf.
     """
@@ -270,21 +271,23 @@ def mx_output_within_bound(q, codes, out_ref, tol_y) -> np.ndarray:
 
 # ---- output quantised for the next layer with a fresh per-tensor / per-row scale
 # The same saving of a C round trip, with the output's scale chosen afresh from
-# y itself: one for the whole output or one per row (the scale_a of a row-wise
-# GEMM that takes the codes as its A operand).  Reading: y = act(C + bias) is
-# rounded to binary32 and quantised with the per-tensor or row-wise rule of
+# the layer's output itself: one for the whole output or one per row (the
+# scale_a of a row-wise GEMM that takes the codes as its A operand).  Reading:
+# the layer's output is the GEMM's bf16 result (the pages' kernels accumulate in
+# fp32 and cast the tile to a 16-bit type on store), and the next layer's
+# operand is that tensor quantised with the per-tensor or row-wise rule of
 # ``quant.quantize_tensor`` / ``quant.quantize_rowwise``.
 
 def scaled_output_reference(out_ref: np.ndarray, out_mode: str, fmt: str = "e4m3"):
     """(codes uint8 [M,N], scales float32 [M] or ()): the row-wise ("rowwise") or
-    per-tensor ("tensor") quantisation of the binary32 rounding of the exact
-    epilogue output."""
+    per-tensor ("tensor") quantisation of the bf16 rounding of the exact epilogue
+    output (bf16 values are exact in binary32)."""
     from .quant import quantize_rowwise, quantize_tensor
-    y32 = np.asarray(out_ref, np.float64).astype(np.float32)
+    y16 = round_to_output(np.asarray(out_ref, np.float64), "bf16").astype(np.float32)
     if out_mode == "rowwise":
-        return quantize_rowwise(y32, fmt)
+        return quantize_rowwise(y16, fmt)
     if out_mode == "tensor":
-        return quantize_tensor(y32, fmt)
+        return quantize_tensor(y16, fmt)
     raise ValueError(f"unknown output scale mode {out_mode!r}")
 
 
@@ -304,23 +307,24 @@ def scaled_output_within_bound(q, scales, out_ref, tol_y, out_mode: str,
                                fmt: str = "e4m3") -> np.ndarray:
     """Which outputs of a result quantised with fresh scales (q [M,N] codes,
     scales float [M] for "rowwise" or one value for "tensor") are acceptable
-    against the exact output out_ref with tolerance tol_y.
+    against the exact output out_ref, given the GEMM's tolerance tol_y.
 
-    A computed y' lies within tol_y of out_ref, its maximum magnitude amax'
-    between those of |out_ref| - tol_y and |out_ref| + tol_y (over the row or the
-    whole output), so its scale fl32(amax' / max) lies between the scales of
-    those two bounds (binary32 rounding is monotone), or is 1 where the lower
-    bound is 0.  A code then dequantises (value times the scale s) to within
-    tol_y, half a spacing of the format at the scaled magnitude (|out_ref| +
-    tol_y) / s, the binary32 rounding of the quotient (2^-24 relative) and, for
-    values beyond max * s, the saturation distance, of out_ref.  The mask is
-    False for every output of a row (or of the output) whose scale is out of
-    range."""
+    A computed output y' lies within tol_y of out_ref and its bf16 rounding y16
+    within t = tol_y + half a bf16 ulp at |out_ref| + tol_y; the maximum of |y16|
+    over the row (or the whole output) lies between those of |out_ref| - t and
+    |out_ref| + t, so its scale fl32(amax / max) lies between the scales of those
+    two bounds (binary32 rounding is monotone), or is 1 where the lower bound is
+    0.  A code then dequantises (value times the scale s) to within t, half a
+    spacing of the format at the scaled magnitude (|out_ref| + t) / s, the
+    binary32 rounding of the quotient (2^-24 relative) and, for values beyond
+    max * s, the saturation distance, of out_ref.  The mask is False for every
+    output of a row (or of the output) whose scale is out of range."""
     from .formats import FORMATS
     y = np.asarray(out_ref, np.float64)
-    t = np.asarray(tol_y, np.float64) * np.ones_like(y)
-    fmax = float(FORMATS[fmt]["max"])
     a = np.abs(y)
+    t0 = np.asarray(tol_y, np.float64) * np.ones_like(y)
+    t = t0 + 0.5 * output_ulp(a + t0, "bf16")
+    fmax = float(FORMATS[fmt]["max"])
     lo_v = np.maximum(a - t, 0.0)
     hi_v = a + t
     if out_mode == "rowwise":

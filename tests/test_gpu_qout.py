@@ -1,13 +1,16 @@
 """GPU parity of the GEMM whose output is quantised for the next layer with a fresh
-per-tensor or per-row scale (fp8gemm_run_qout): the GEMM kernels store y in fp32
-and fold |y| into atomic maxima in their epilogue (registers on full tiles, the
-staged loop on edge tiles and after the split-K reduction), a second kernel
-derives the scales and encodes.  Covered: every input scale mode, both output
-scale modes, e4m3 and e5m2 codes, ragged M, 256- and 128-wide tiles, split-K,
-bias + activation, FP4 and FP6 operands, all-zero rows, workspace reuse across
-shapes, and the codes feeding a row-wise GEMM as its A operand.  Checked
-against the oracle's bound (the GEMM bound plus the format's rounding at the
-scale; the scale itself within the band the GEMM bound allows)."""
+per-tensor or per-row scale (fp8gemm_run_qout): the GEMM kernels store the bf16
+output exactly as fp8gemm_run_ex does and fold the stored values' magnitudes into
+atomic maxima in their epilogue (registers on full tiles, the staged loops on
+edge tiles and after the split-K reduction), a second kernel derives the scales
+and encodes.  Every case is checked twice: bit for bit against the library's own
+two-step path (the bf16 GEMM, then the quantiser on its output), and against the
+oracle's bound (the GEMM bound plus the bf16 and format roundings at the scale;
+the scale itself within the band the bound allows).  Covered: every input scale
+mode, both output scale modes, e4m3 and e5m2 codes, ragged M, 256- and 128-wide
+tiles, split-K, the persistent grid, bias + activation, FP4 and FP6 operands,
+all-zero rows, workspace reuse across shapes, and the codes feeding a row-wise
+GEMM as its A operand."""
 import numpy as np
 import pytest
 import torch
@@ -38,13 +41,23 @@ def _pack(fmt):
 
 
 def _run(qa, sa, qb, sb, mode, fmt, out_mode, cfmt="e4m3", bias=None, act="none",
-         workspace=None):
+         workspace=None, two_step=True):
     bd = None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).to(DEV)
-    q, s = F.gemm_qout(to_dev(_pack(fmt)(qa), 16), scale_to_dev(sa, mode),
-                       to_dev(_pack(fmt)(qb), 16), scale_to_dev(sb, mode), mode, out_mode, cfmt,
-                       fmt_a=fmt, fmt_b=fmt, bias=bd, activation=act, workspace=workspace)
+    ops = (to_dev(_pack(fmt)(qa), 16), scale_to_dev(sa, mode), to_dev(_pack(fmt)(qb), 16),
+           scale_to_dev(sb, mode))
+    q, s = F.gemm_qout(*ops, mode, out_mode, cfmt, fmt_a=fmt, fmt_b=fmt, bias=bd,
+                       activation=act, workspace=workspace)
     torch.cuda.synchronize()
-    return to_host(q), to_host(s)
+    q, s = to_host(q), to_host(s)
+    if two_step:
+        # the library's own path in two calls: bf16 GEMM, then the quantiser on C
+        C = F.gemm(*ops, mode, "bf16", fmt_a=fmt, fmt_b=fmt, bias=bd, activation=act)
+        q2, s2 = F.quantize(C.float().contiguous(), out_mode, fmt=cfmt)
+        q2, s2 = to_host(q2), to_host(s2).reshape(s.shape)
+        bad = np.argwhere(q != q2)
+        assert bad.size == 0, f"{len(bad)} codes differ from quantize(gemm); first {tuple(bad[0])}"
+        assert np.array_equal(s, s2), "scales differ from quantize(gemm)"
+    return q, s
 
 
 def _check(qa, sa, qb, sb, mode, fmt, out_mode, q, s, cfmt="e4m3", rows=None, bias=None,
@@ -165,16 +178,17 @@ def test_qout_feeds_a_rowwise_gemm():
     assert ok.all(), f"{int((~ok).sum())} outputs of the second GEMM outside the bound"
 
 
-def test_qout_matches_the_quantiser_on_the_gemm_output():
-    """Against the library's own path in two steps (the GEMM to fp32 through a
-    bf16-free route is not offered, so through the oracle): the per-tensor
-    scale equals fl32(amax / 448) of the exact output to within the GEMM bound
-    and at least 99% of the codes equal the oracle's codes exactly."""
-    M, N, K = 384, 512, 2048
-    qa, sa, qb, sb = _operands(M, N, K, "rowwise", "e4m3", seed=77, dist="normal")
-    announce("gemm qout vs quantiser", (M, N, K))
-    q, s = _run(qa, sa, qb, sb, "rowwise", "e4m3", "tensor")
-    Cr, _ = O.gemm_reference(qa, sa, qb, sb, "rowwise")
-    qr, sr = O.scaled_output_reference(Cr, "tensor")
-    assert abs(float(s[0]) / float(sr) - 1) < 1e-4
-    assert np.mean(q == qr) > 0.99
+@pytest.mark.parametrize("mode,out_mode", [("tensor", "tensor"), ("mx32", "rowwise")])
+def test_qout_persistent_grid(mode, out_mode):
+    """A shape with 2048 tiles of 256 x 256 takes the persistent copy-stream grid,
+    whose register epilogue folds the maxima too (sampled rows against the
+    oracle; every code against the two-step path)."""
+    M, N, K = 16384, 8192, 512
+    assert F.fp8gemm_run_path(M, N, K, K, K, 0, 0, F.SCALE_MODES[mode], 0) == "persistent"
+    qa, sa, qb, sb = _operands(M, N, K, mode, "e4m3", seed=61)
+    announce("gemm qout persistent", mode, out_mode, (M, N, K))
+    q, s = _run(qa, sa, qb, sb, mode, "e4m3", out_mode)
+    if out_mode == "rowwise":
+        rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(1).integers(0, M, 24)]))
+        _check(qa, sa, qb, sb, mode, "e4m3", out_mode, q, s, rows=rows,
+               what=f"qout persistent {mode} {out_mode}")
