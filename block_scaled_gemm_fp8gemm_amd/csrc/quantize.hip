@@ -293,9 +293,9 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const float* __restr
 // amax (per row or one for the output; zeroed by zero_words_kernel before the
 // GEMM); this pass derives the scales by the per-tensor / row-wise rule above and
 // encodes y's values (exact in fp32) with it, as quantising the bf16 output
-// would.  One wavefront per row (rows dealt to wavefronts in turn), 1024 columns
-// per step: lane l takes the 8 values at columns 512 j + 8 l (j = 0, 1), so each
-// 16-byte load and 8-byte code store instruction covers one contiguous run.
+// would.  One wavefront per row (rows dealt to wavefronts in turn), 2048 columns
+// per step: lane l takes the 8 values at columns 512 j + 8 l (j = 0 .. 3), so
+// each 16-byte load and 8-byte code store instruction covers one contiguous run.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 template <int FMT, bool PER_ROW>
@@ -321,17 +321,23 @@ __global__ __launch_bounds__(kThreads) void requant_kernel(const uint16_t* __res
     }
     const uint16_t* yr = y + (int64_t)r * ldy;
     uint8_t* qr = q + (int64_t)r * ldq;
-    for (int c0 = 0; c0 < n; c0 += 1024) {
+    // 2048 columns per step: the four loads go out before any is used
+    for (int c0 = 0; c0 < n; c0 += 2048) {
+      u32x4 w[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + 512 * j + 8 * lane;
+        w[j] = c < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(yr + c)) : u32x4{};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
         const int c = c0 + 512 * j + 8 * lane;
         if (c < n) {
-          const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(yr + c));
           float x[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            x[2 * e] = __uint_as_float(w[e] << 16);
-            x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+            x[2 * e] = __uint_as_float(w[j][e] << 16);
+            x[2 * e + 1] = __uint_as_float(w[j][e] & 0xffff0000u);
           }
           uint2 o;
           o.x = encode4<FMT>(x[0] / s, x[1] / s, x[2] / s, x[3] / s);
