@@ -1887,6 +1887,66 @@ __device__ __forceinline__ void epilogue_direct(const v16f (&acc)[Cfg::kFragM][C
   if constexpr (kTrackMax<OutT>) fold_tensor_max(cs, ldcs, run, lane);
 }
 
+// The register epilogue for tiles of which only the first `rows` rows are stored
+// (tiles cut by M inside a copy stream; no bias, 16-bit outputs): the stores go
+// through a buffer descriptor whose range ends at the last valid row, so the
+// hardware drops the others and every wave still issues all its stores (the
+// stream's waits count them).  Rows 0 .. BM-1 of the tile must be addressable
+// with 32-bit offsets: BM * ldc * sizeof(OutT) < 2^31.
+template <class Cfg, int MODE, typename OutT>
+__device__ __forceinline__ void epilogue_direct_rows(const v16f (&acc)[Cfg::kFragM][Cfg::kFragN],
+                                                     const uint8_t* lds, OutT* C, int64_t ldc,
+                                                     int m0, int n0, float tensor_scale, int rbuf,
+                                                     int rows) {
+  constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
+  static_assert(sizeof(OutT) == 2 && !kTrackMax<OutT>, "16-bit outputs");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
+  const int h = lane >> 5;
+  const float* rsc =
+      reinterpret_cast<const float*>(lds + Cfg::kRowScaleOff + rbuf * (Cfg::BM + Cfg::BN) * 4);
+  const int vr = rows < Cfg::BM ? rows : Cfg::BM;
+  const __amdgpu_buffer_rsrc_t rs =
+      buffer_rsrc(C + (int64_t)m0 * ldc, (uint32_t)(vr * (int)ldc * (int)sizeof(OutT)));
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = wm * Cfg::WM + i * 32 + (lane & 31);   // tile row of this lane
+    float fa = 1.0f;
+    if (MODE == kTensor) fa = tensor_scale;
+    if (MODE == kRowwise) fa = rsc[r];
+    const int vrow = (r * (int)ldc + n0 + wn * Cfg::WN + 8 * h) * (int)sizeof(OutT);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        uint2 w[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int g = 2 * k + q;
+          const int c = j * 32 + 8 * g + 4 * h;           // wave-local column of value 0
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * fa;
+          if (MODE == kRowwise) {
+            const v4f fb = *reinterpret_cast<const v4f*>(rsc + Cfg::BM + wn * Cfg::WN + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] *= fb[e];
+          }
+          w[q] = pack4<OutT>(v[0], v[1], v[2], v[3]);
+        }
+        // low half keeps group 2k and takes the high half's; high half keeps 2k + 1
+        const auto sx = __builtin_amdgcn_permlane32_swap(w[0].x, w[1].x, false, false);
+        const auto sy = __builtin_amdgcn_permlane32_swap(w[0].y, w[1].y, false, false);
+        typedef unsigned v4u_st __attribute__((ext_vector_type(4)));
+        const v4u_st out{sx[0], sy[0], sx[1], sy[1]};
+        __builtin_amdgcn_raw_buffer_store_b128(out, rs,
+                                               vrow + (j * 32 + 16 * k) * (int)sizeof(OutT), 0, 0);
+      }
+    }
+  }
+}
+
 // The output quantised for the next layer, straight from registers (interior
 // tiles without bias or activation): e4m3 codes with one E8M0 code per 32
 // consecutive columns of a row, by the quantisers' MX rule.  A 32 x 32 block j

@@ -20,7 +20,9 @@
 //     first instead shares the weights but makes each XCD stream ~1 MB of
 //     distinct activations per 128-deep K step, which measured 2.3x slower;
 //   * each tile uses the dense mainloop and epilogue, with rows past the expert's
-//     end clamped on load and masked on store (ragged experts, empty experts).
+//     end masked on store (ragged experts, empty experts); with K % 512 == 0 the
+//     tiles cut by an expert's last row stay in the copy stream unless they
+//     reach past the end of A.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -129,17 +131,26 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void grouped_kerne
   const float* fsa = static_cast<const float*>(p.scale_a);
   const float* fsb = static_cast<const float*>(p.scale_b);
   OutT* C = static_cast<OutT*>(p.C);
-  // full tiles with K % 512 == 0 run as copy streams (one per run of such tiles);
-  // tiles cut by an expert's last row take the general path (FP4: every tile)
+  // with K % 512 == 0, tiles whole in N run as copy streams (one per run of such
+  // tiles); so do tiles cut by an expert's last row whose BM rows still lie
+  // inside A: they read the next expert's rows (and their row scales or codes)
+  // as a whole tile would and store only their own rows.  Tiles cut by N or by
+  // the end of A take the general path (FP4: every tile).
   constexpr bool kStream = KALIGNED && Cfg::kSlots == 4 && !kF4;
+  // (their stores address a tile's rows with 32-bit offsets)
+  const bool ranged = (int64_t)Cfg::BM * p.ldc * (int64_t)sizeof(OutT) < ((int64_t)1 << 31);
   auto streamable = [&](int i) __attribute__((always_inline)) {
-    return kStream && p.K % 512 == 0 && interior_tile<Cfg, MODE>(src.op(i));
+    if (!kStream || p.K % 512 != 0 || !ranged) return false;
+    const auto w = src.where(i);
+    const TileOperands op = src.op_at(w);
+    return op.b_rows >= Cfg::BN && w.m0 + Cfg::BM <= p.total_m && interior_k<Cfg, MODE>(op);
   };
   auto epi = [&](const v16f (&acc)[Cfg::kFragM][Cfg::kFragN], int i, int rbuf)
                  __attribute__((always_inline)) {
     const auto w = src.where(i);
     const float ts = (MODE == kTensor) ? fsa[0] * fsb[w.g] : 1.0f;
-    epilogue_direct<Cfg, MODE, OutT>(acc, lds, C, p.ldc, w.m0, w.n0, ts, rbuf);
+    epilogue_direct_rows<Cfg, MODE, OutT>(acc, lds, C, p.ldc, w.m0, w.n0, ts, rbuf,
+                                          w.m_end - w.m0);
   };
 
   int i = 0;

@@ -60,6 +60,51 @@ def test_grouped_small(mode, out, counts, N, K):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("out", ["bf16", "f16"])
+def test_grouped_cut_tiles_in_stream(mode, out):
+    """K % 512 == 0, N a multiple of 256: tiles cut by an expert's last row with
+    at least a tile of rows of A after them run inside the copy stream and store
+    only their own rows (cuts of 1, 44, 255, 1 and 40 rows); the cuts of the last
+    two experts (188 and 3 rows) reach past A and take the general path.  With
+    352 tiles, some workgroups stream two.  Every expert's rows equal, bit for
+    bit, the same expert run alone (its cut tile then on the general path); the
+    oracle bound holds everywhere; rows around C and the columns past N keep
+    their canaries."""
+    rng = np.random.default_rng(4242)
+    counts = np.array([1, 300, 0, 255, 257, 40, 700, 3])
+    N, K = 8192, 1024
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    total = int(off[-1])
+    x = normal(rng, total, K)
+    W = np.stack([normal(rng, N, K, 0.02) for _ in counts])
+    qa, sa = Q.quantize(x, mode)
+    qw, sw = _quant_experts(W, mode)
+    announce("grouped cut tiles in stream", mode, out, counts.tolist(), N, K)
+    tdt = torch.float16 if out == "f16" else torch.bfloat16
+    pad, ldc = 16, N + 64
+    buf = torch.full((total + 2 * pad, ldc), -7.0, dtype=tdt, device=DEV)
+    C = F.grouped_gemm(to_dev(qa, 16), scale_to_dev(sa, mode), torch.from_numpy(off).to(DEV),
+                       _dev3(qw), torch.from_numpy(np.ascontiguousarray(sw)).to(DEV), mode, out,
+                       out=buf[pad:pad + total, :N])
+    torch.cuda.synchronize()
+    assert bool((buf[:pad] == -7.0).all()) and bool((buf[pad + total:] == -7.0).all())
+    assert bool((buf[:, N:] == -7.0).all())
+    Cr, Ar = O.grouped_reference(qa, sa, off, qw, sw, mode)
+    assert_within_bound(to_host(C), Cr, Ar, out, f"grouped cut {mode}/{out}")
+    for g, c in enumerate(counts):
+        if c == 0:
+            continue
+        r0, r1 = int(off[g]), int(off[g + 1])
+        sa_g = sa if mode == "tensor" else np.ascontiguousarray(np.asarray(sa)[r0:r1])
+        sw_g = np.ascontiguousarray(sw[g:g + 1])
+        Cg = F.grouped_gemm(to_dev(np.ascontiguousarray(qa[r0:r1]), 16), scale_to_dev(sa_g, mode),
+                            torch.tensor([0, r1 - r0], dtype=torch.int32, device=DEV),
+                            _dev3(qw[g:g + 1]), torch.from_numpy(sw_g).to(DEV), mode, out)
+        torch.cuda.synchronize()
+        assert torch.equal(C[r0:r1], Cg), f"expert {g} ({c} rows)"
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_grouped_one_expert_equals_dense(mode):
     rng = np.random.default_rng(77)
     M, N, K = 700, 600, 512
