@@ -61,18 +61,19 @@ def test_grouped_small(mode, out, counts, N, K):
 
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("out", ["bf16", "f16"])
-def test_grouped_cut_tiles_in_stream(mode, out):
+@pytest.mark.parametrize("N,K", [(8192, 1024), (768, 512)])
+def test_grouped_cut_tiles_in_stream(mode, out, N, K):
     """K % 512 == 0, N a multiple of 256: tiles cut by an expert's last row with
     at least a tile of rows of A after them run inside the copy stream and store
     only their own rows (cuts of 1, 44, 255, 1 and 40 rows); the cuts of the last
     two experts (188 and 3 rows) reach past A and take the general path.  With
-    352 tiles, some workgroups stream two.  Every expert's rows equal, bit for
-    bit, the same expert run alone (its cut tile then on the general path); the
-    oracle bound holds everywhere; rows around C and the columns past N keep
-    their canaries."""
-    rng = np.random.default_rng(4242)
+    N = 8192 (352 tiles) some workgroups stream two; with K = 512 (four K tiles,
+    the stream's shortest) every workgroup streams one.  Every expert's rows
+    equal, bit for bit, the same expert run alone (its cut tile then on the
+    general path); the oracle bound holds everywhere; rows around C and the
+    columns past N keep their canaries."""
+    rng = np.random.default_rng(4242 + K)
     counts = np.array([1, 300, 0, 255, 257, 40, 700, 3])
-    N, K = 8192, 1024
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     total = int(off[-1])
     x = normal(rng, total, K)
