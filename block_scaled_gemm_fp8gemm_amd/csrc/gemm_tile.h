@@ -173,6 +173,43 @@ struct TileOperands {
   int sldb = 0;
 };
 
+// A copy of a tile's operand description with every field read from the first
+// lane.  The values are wave-uniform by construction; where they come through a
+// data-dependent search (grouped tiles) or a struct the compiler keeps in memory,
+// its divergence analysis may no longer see that, and it would then compute the
+// copy offsets in vector registers and wrap every copy in a loop over the lanes'
+// distinct descriptors.  For values already in scalar registers this is free.
+template <class T>
+__device__ __forceinline__ T first_lane_ptr(T p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<T>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int64_t first_lane_i64(int64_t v) {
+  const uint64_t a = (uint64_t)v;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ TileOperands first_lane(const TileOperands& o) {
+  TileOperands u;
+  u.A = first_lane_ptr(o.A);
+  u.lda = first_lane_i64(o.lda);
+  u.a_rows = __builtin_amdgcn_readfirstlane(o.a_rows);
+  u.B = first_lane_ptr(o.B);
+  u.ldb = first_lane_i64(o.ldb);
+  u.b_rows = __builtin_amdgcn_readfirstlane(o.b_rows);
+  u.sa = first_lane_ptr(o.sa);
+  u.sb = first_lane_ptr(o.sb);
+  u.ra = first_lane_ptr(o.ra);
+  u.rb = first_lane_ptr(o.rb);
+  u.K = __builtin_amdgcn_readfirstlane(o.K);
+  u.sld = __builtin_amdgcn_readfirstlane(o.sld);
+  u.sldb = __builtin_amdgcn_readfirstlane(o.sldb);
+  return u;
+}
+
 // Row-major B in LDS: a 128-K tile is 128 K-rows of BN bytes; 16-byte chunk c of
 // K-row k sits at chunk c ^ kn_swz(k).  A transposing read takes 8 K-rows at one
 // 32-column fragment (two chunks, both halves): with this XOR the 32 lanes of a
@@ -733,8 +770,9 @@ __device__ __forceinline__ bool interior_tile(const TileOperands& op) {
 // read as zero (the copy range ends at the last valid row) and B columns past N
 // hold whatever the copy finds there; neither is ever stored.
 template <class Cfg, int MODE, int NS = 2, bool KN = false>
-__device__ __forceinline__ void mainloop_interior(const TileOperands& op, uint8_t* lds,
+__device__ __forceinline__ void mainloop_interior(const TileOperands& op_in, uint8_t* lds,
                                                   v16f (&acc)[Cfg::kFragM][Cfg::kFragN]) {
+  const TileOperands op = first_lane(op_in);
   constexpr int FM = Cfg::kFragM, FN = Cfg::kFragN;
   constexpr bool kMx = MODE == kMx32;
   constexpr int kRowB = 128;                          // bytes per LDS row (one K tile)
@@ -2205,6 +2243,22 @@ __device__ __forceinline__ void gemm_tile(const TileOperands& op, uint8_t* lds, 
   mainloop<Cfg, MODE, KALIGNED && !kF4>(op, lds, acc);
   epilogue_any_tile<Cfg, MODE, OutT, FUSED>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale,
                                             bias, act, cs, ldcs);
+}
+
+// One output tile on the interior mainloop, whole or cut by M or N (the caller
+// guarantees interior_k(op)); plain 16-bit epilogue.
+template <class Cfg, int MODE, typename OutT>
+__device__ __forceinline__ void gemm_tile_interior(const TileOperands& op, uint8_t* lds, OutT* C,
+                                                   int64_t ldc, int m0, int m_end, int n0, int N,
+                                                   float tensor_scale) {
+  v16f acc[Cfg::kFragM][Cfg::kFragN];
+  mainloop_interior<Cfg, MODE>(op, lds, acc);
+  if (op.a_rows >= Cfg::BM && op.b_rows >= Cfg::BN)
+    epilogue_full_tile<Cfg, MODE, OutT, false>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale,
+                                               nullptr, kActNone, nullptr, 0);
+  else
+    epilogue_any_tile<Cfg, MODE, OutT, false>(acc, lds, C, ldc, m0, m_end, n0, N, tensor_scale,
+                                              nullptr, kActNone, nullptr, 0);
 }
 
 // One output tile with row-major B ([K][N]): the interior mainloop in its KN

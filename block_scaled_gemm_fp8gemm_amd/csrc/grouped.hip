@@ -96,7 +96,10 @@ struct GroupedTiles {
   __device__ TileOperands op(int i) const { return op_at(where(i)); }
 };
 
-template <class Cfg, int MODE, typename OutT, bool KALIGNED>
+// ALL_INTERIOR: every tile runs the interior mainloop (MXFP4 experts with K a
+// multiple of 512 and 32-bit spans; the launch checks), so the kernel carries no
+// edge path.
+template <class Cfg, int MODE, typename OutT, bool KALIGNED, bool ALL_INTERIOR = false>
 __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void grouped_kernel(GroupedProblem p,
                                                                                  int tiles_n) {
   // One LDS object holds the tile ring and the expert tables: with several LDS
@@ -169,8 +172,16 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kWavesPerEu) void grouped_kerne
     if (!streamed) {
       const auto w = src.where(i);
       const float ts = (MODE == kTensor) ? fsa[0] * fsb[w.g] : 1.0f;
-      gemm_tile<Cfg, MODE, OutT, KALIGNED, false, false>(src.op_at(w), lds, C, p.ldc, w.m0,
-                                                         w.m_end, w.n0, p.N, ts);
+      // tiles cut by an expert's last row (or by N): with ALL_INTERIOR on the
+      // interior loop too, their copies ending at the last valid row or column;
+      // otherwise on the edge path (FP8: tiles that did not stream above; an
+      // interior instance here would inflate the stream's loop)
+      if constexpr (ALL_INTERIOR)
+        gemm_tile_interior<Cfg, MODE, OutT>(src.op_at(w), lds, C, p.ldc, w.m0, w.m_end, w.n0,
+                                            p.N, ts);
+      else
+        gemm_tile<Cfg, MODE, OutT, KALIGNED, false, false>(src.op_at(w), lds, C, p.ldc, w.m0,
+                                                           w.m_end, w.n0, p.N, ts);
       ++i;
     }
   }
@@ -190,7 +201,16 @@ hipError_t launch_cfg(const GroupedProblem& p, hipStream_t stream) {
   const int64_t slots = (int64_t)cus * Cfg::kWgPerCu;
   const int grid = (int)(max_tiles < slots ? max_tiles : slots);
   if (grid <= 0) return hipSuccess;
-  if (p.K % 128 == 0)
+  // MXFP4 with whole 512-element code groups (K counts bytes) and 32-bit spans:
+  // every tile interior
+  constexpr bool kAllInterior = kF4 && Cfg::BM == 256;
+  const bool all_interior = kAllInterior && MODE == kMx32 && p.K % 256 == 0 &&
+                            (int64_t)Cfg::BM * p.lda + p.K < ((int64_t)1 << 31) &&
+                            (int64_t)Cfg::BN * p.ldb + p.K < ((int64_t)1 << 31);
+  if (all_interior)
+    hipLaunchKernelGGL((grouped_kernel<Cfg, MODE, OutT, true, kAllInterior>),
+                       dim3(grid), dim3(Cfg::kThreads), 0, stream, p, tiles_n);
+  else if (p.K % 128 == 0)
     hipLaunchKernelGGL((grouped_kernel<Cfg, MODE, OutT, true>), dim3(grid), dim3(Cfg::kThreads), 0,
                        stream, p, tiles_n);
   else
@@ -203,8 +223,9 @@ hipError_t launch_cfg(const GroupedProblem& p, hipStream_t stream) {
 
 #if FP8GEMM_FMT_A == 4 && FP8GEMM_FMT_B == 4
 // MXFP4 experts (K, lda, ldb and stride_b in bytes): the large tile, one tile at
-// a time (full tiles take the interior mainloop, tiles cut by an expert's last
-// row read their codes into registers); a K tail takes 128 x 128 tiles.
+// a time; with K % 512 == 0 every tile on the interior mainloop (tiles cut by an
+// expert's last row or by N included), else full tiles only; a K tail takes
+// 128 x 128 tiles.
 hipError_t launch_grouped_gemm_e2m1_e2m1(const GroupedProblem& p, int mode, int out,
                                          hipStream_t stream) {
   if (mode != kMx32) return hipErrorInvalidValue;

@@ -183,3 +183,43 @@ def test_grouped_fp4(out, counts, N, K):
                        fmt="e2m1")
     Cr, Ar = O.grouped_reference(qa, sa, off, qw, sw, "mx32", fmt="e2m1")
     assert_within_bound(to_host(C), Cr, Ar, out, f"grouped e2m1/{out} {counts.tolist()}")
+
+
+@pytest.mark.parametrize("out", ["bf16", "f16"])
+def test_grouped_fp4_cut_tiles_interior(out):
+    """MXFP4 experts with K % 512 == 0 run every tile on the interior mainloop,
+    tiles cut by an expert's last row or by N included (their copies end at the
+    last valid row or column): the oracle bound holds, rows around C and the
+    columns past N keep their canaries, and one expert of 700 rows equals the
+    dense MXFP4 GEMM of the same operands bit for bit."""
+    rng = np.random.default_rng(909)
+    counts = np.array([1, 300, 0, 255, 257, 40, 700, 3])
+    N, K = 600, 1024
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    total = int(off[-1])
+    x = normal(rng, total, K)
+    W = np.stack([normal(rng, N, K, 0.02) for _ in counts])
+    qa, sa = Q.quantize(x, "mx32", "e2m1")
+    qs, ss = zip(*[Q.quantize(W[g], "mx32", "e2m1") for g in range(len(counts))])
+    qw, sw = np.stack(qs), np.stack(ss)
+    announce("grouped e2m1 cut tiles", out, counts.tolist(), N, K)
+    tdt = torch.float16 if out == "f16" else torch.bfloat16
+    pad, ldc = 16, N + 40
+    buf = torch.full((total + 2 * pad, ldc), -7.0, dtype=tdt, device=DEV)
+    C = F.grouped_gemm(to_dev(O.pack_fp4(qa), 16), scale_to_dev(sa, "mx32"),
+                       torch.from_numpy(off).to(DEV), _dev3(O.pack_fp4(qw)),
+                       torch.from_numpy(np.ascontiguousarray(sw)).to(DEV), "mx32", out,
+                       out=buf[pad:pad + total, :N], fmt="e2m1")
+    torch.cuda.synchronize()
+    assert bool((buf[:pad] == -7.0).all()) and bool((buf[pad + total:] == -7.0).all())
+    assert bool((buf[:, N:] == -7.0).all())
+    Cr, Ar = O.grouped_reference(qa, sa, off, qw, sw, "mx32", fmt="e2m1")
+    assert_within_bound(to_host(C), Cr, Ar, out, f"grouped e2m1 cut/{out}")
+    g = 6                                           # 700 rows: two whole tile rows and a cut one
+    r0, r1 = int(off[g]), int(off[g + 1])
+    Cd = F.gemm(to_dev(O.pack_fp4(np.ascontiguousarray(qa[r0:r1])), 16),
+                scale_to_dev(np.ascontiguousarray(sa[r0:r1]), "mx32"),
+                to_dev(O.pack_fp4(qw[g]), 16), scale_to_dev(sw[g], "mx32"), "mx32", out,
+                fmt_a="e2m1", fmt_b="e2m1")
+    torch.cuda.synchronize()
+    assert torch.equal(C[r0:r1], Cd)
