@@ -99,9 +99,12 @@ inline GemmPath choose_path(int64_t M, int64_t N, int64_t K, int64_t lda, int64_
   const bool big_interior = M % kBigTile == 0 && N % kBigTile == 0 &&
                             spans_fit(kBigTile, lda, K) && spans_fit(kBigTile, ldb, K);
   if (fp4) {
-    // FP4: the large tile only when every tile is interior (its edge tiles would
-    // read their codes into registers and spill), and no persistent stream
-    if (big_tiles >= 256 && big_interior && K % (16 * blk) == 0) return kPathTile256;
+    // FP4: the large tile only when every tile runs the interior mainloop (K a whole
+    // number of code groups, 32-bit spans; tiles cut by M or N included): its other
+    // edge tiles would read their codes into registers and spill; no persistent stream
+    if (big_tiles >= 256 && K % (16 * blk) == 0 && spans_fit(kBigTile, lda, K) &&
+        spans_fit(kBigTile, ldb, K))
+      return kPathTile256;
     return kPathTile128;
   }
   // MX with K % 128 != 0 reads its codes into registers: the large tile would spill

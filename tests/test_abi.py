@@ -86,7 +86,8 @@ def test_workspace_queries(lib):
     ((4096, 4096, 4160), None, "e4m3", "mx32", 0, "tile128"),       # MX K tail: codes in registers
     ((8192, 8192, 8192), None, "e2m1", "mx32", 0, "tile256"),       # FP4: never persistent
     ((16384, 8192, 1024), None, "e2m1", "mx32", 0, "tile256"),
-    ((4000, 4096, 8192), None, "e2m1", "mx32", 0, "tile128"),
+    ((4000, 4100, 8192), None, "e2m1", "mx32", 0, "tile256"),       # cut tiles, interior
+    ((4000, 4096, 8192 + 256), None, "e2m1", "mx32", 0, "tile128"),  # K % 512 != 0
     ((128, 4096, 4096), None, "e2m1", "mx32", 0, "splitk"),
     ((128, 4096, 4096), None, "e2m1", "tensor", 0, "none"),        # FP4 takes MX scales only
 ])

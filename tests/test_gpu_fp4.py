@@ -109,15 +109,19 @@ def test_gemm_fp4_small(out, shape):
 
 
 @pytest.mark.parametrize("shape", [(512, 512, 1024), (4096, 4096, 1024), (4096, 4096, 1536),
-                                   (128, 4096, 4096), (96, 1000, 6144)])
+                                   (4000, 4100, 1024), (128, 4096, 4096), (96, 1000, 6144)])
 def test_gemm_fp4_interior(shape):
     """Full tiles: 128 x 128 tiles (16 tiles) and 256 x 256 tiles (256 tiles), K a
-    whole number of code groups, in two and in three groups; and split-K shapes
-    with few output tiles (decode-like M = 128, and ragged M and N with three
-    code groups per K slice)."""
+    whole number of code groups, in two and in three groups; 256 x 256 tiles cut by
+    M and N (272 tiles, the last tile row 160 rows, the last column 4, on the
+    interior mainloop); and split-K shapes with few output tiles (decode-like
+    M = 128, and ragged M and N with three code groups per K slice)."""
     M, N, K = shape
     qa, sa, qb, sb = _operands(M, N, K, seed=N + K)
     announce("gemm e2m1 interior", shape)
+    if shape == (4000, 4100, 1024):
+        assert F.fp8gemm_run_path(M, N, K, K // 2, K // 2, F.FORMATS["e2m1"], F.FORMATS["e2m1"],
+                                  F.SCALE_MODES["mx32"], 0) == "tile256"
     C = _run(qa, sa, qb, sb)
     torch.cuda.synchronize()
     rng = np.random.default_rng(K)
