@@ -30,9 +30,14 @@ __device__ __forceinline__ int xcd_linear(int id, int total) {
 __device__ __forceinline__ void grouped_tile(int linear, int tiles_m, int tiles_n, int group_m,
                                              int* tm, int* tn) {
   const int per_group = group_m * tiles_n;
-  const int gid = linear / per_group;
+  // a single tile row left over joins the last full group (a one-row group would
+  // give each XCD a 1 x 32 block of tiles reading 33 bands instead of about 12)
+  const int full = tiles_m / group_m;
+  int gid = linear / per_group;
+  if (tiles_m % group_m == 1 && full > 0 && gid >= full - 1) gid = full - 1;
   const int first_m = gid * group_m;
-  const int rows = min(tiles_m - first_m, group_m);
+  const int rows = (tiles_m % group_m == 1 && full > 0 && gid == full - 1)
+                       ? group_m + 1 : min(tiles_m - first_m, group_m);
   const int in_group = linear - gid * per_group;
   *tm = first_m + in_group % rows;
   *tn = in_group / rows;

@@ -49,9 +49,12 @@ def test_gemm_small_shapes(mode, out, shape):
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("shape", [(4096, 4096, 256), (4000, 4100, 192)])
+@pytest.mark.parametrize("shape", [(4096, 4096, 256), (4000, 4100, 192), (4352, 4096, 256),
+                                   (4300, 4000, 128)])
 def test_gemm_big_tiles(mode, shape):
-    """Shapes with >= 256 tiles of 256 x 256 take the large-tile kernel (ragged edges too)."""
+    """Shapes with >= 256 tiles of 256 x 256 take the large-tile kernel (ragged edges
+    too); with 17 tile rows the last one joins the last group of four in the tile
+    order.  Every output element is checked."""
     M, N, K = shape
     qa, sa, qb, sb = _oracle_operands(M, N, K, mode, seed=11, dist="mx_block")
     announce("gemm big", mode, shape)
