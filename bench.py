@@ -3,8 +3,10 @@
 One step = the whole path over one batch of synthetic input already resident in
 HBM: quantise A and B (amax / scale and e4m3 encoding) and run the GEMM (MFMA
 mainloop, scale/cast epilogue, tile scheduling); the grouped workload runs the
-grouped GEMM instead.  W untimed warm-up steps, then K timed steps between two
-``torch.cuda.synchronize()``; one JSON line goes to stdout.
+grouped GEMM instead.  Untimed steps for at least --settle-ms (a GPU that was
+idle runs its first ~25 ms of load up to 15 % slower, so a short run would time
+that ramp rather than the kernels), then W untimed warm-up steps, then K timed
+steps between two ``torch.cuda.synchronize()``; one JSON line goes to stdout.
 
 ``value`` is 2*M*N*K per step over the wall time of the timed steps (TFLOP/s,
 the formula of the Cutlass-named Triton FP8 post's monitoring list).  The
@@ -245,6 +247,10 @@ def main():
                     help="kn: B row-major [K, N] (fp8gemm_run_kn, its transposing copy timed "
                          "with the GEMM); B is then quantised once before timing (resident "
                          "weights) and a step is quantise A + GEMM")
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="before the warm-up steps, run untimed steps for at least this long "
+                         "(a GPU that was idle runs its first ~25 ms of load up to 15 %% "
+                         "slower); 0: none")
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="rows of A / columns of B in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -391,10 +397,22 @@ def main():
             qb_kn = qb.t().contiguous()
         sb_kn = sb.t().contiguous() if w.mode == "mx32" else sb
         torch.cuda.synchronize()
+    # settle: untimed steps until the GPU has run the hot path for settle_ms, so
+    # that the timed steps see its steady state whatever the warm-up count
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while args.settle_ms > 0:
+        for _ in range(8):
+            step()
+        settle_steps += 8
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t_settle) * 1e3 >= args.settle_ms:
+            break
+    settle_ms = (time.perf_counter() - t_settle) * 1e3 if settle_steps else 0.0
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"warm-up done ({args.warmup} steps)")
+    log(f"settled ({settle_steps} steps, {settle_ms:.0f} ms), warm-up done ({args.warmup} steps)")
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -507,6 +525,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"steps": settle_steps, "ms": round(settle_ms, 1),
+                   "note": "untimed steps before the warm-up, until the GPU has run the hot "
+                           "path for --settle-ms (steady state)"},
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
