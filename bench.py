@@ -170,7 +170,7 @@ def gemm_bytes_mxout(w, code_bytes: float = 1.0) -> int:
 
 def gemm_bytes_qout(w, code_bytes: float = 1.0) -> int:
     """The same with the output as e4m3 codes plus fp32 scales (one per row; the
-    per-tensor case counts the same): the result's own bytes, not the fp32 y the
+    per-tensor case counts the same): the result's own bytes, not the bf16 y the
     implementation writes and reads back between its two kernels."""
     return gemm_bytes(w, code_bytes) - 2 * w.M * w.N + w.M * w.N + 4 * w.M
 
