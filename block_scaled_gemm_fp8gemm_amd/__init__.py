@@ -367,10 +367,11 @@ def gemm(qa, sa, qb, sb, mode: str = "tensor", out_dtype: str = "bf16", out=None
     """C [M, N] = act(dq(qa [M, K]) @ dq(qb) + bias), returned as fp16 / bf16.
 
     qb is [N, K] (K contiguous, b_layout "nk") or [K, N] (N contiguous, "kn"; its
-    MX codes sb then [K/32, N]); fmt_a / fmt_b: element formats of the codes
-    ("e4m3" or "e5m2"; or "e2m1" for both, FP4 packed two per byte so that qa is
-    [M, K/2] and qb [N, K/2] (or [K, N/2] with b_layout "kn", N even), mode "mx32"; or "e2m3" / "e3m2" for both, FP6 with
-    four codes in three bytes, [M, 3K/4] and [N, 3K/4], mode "mx32", K % 128 == 0);
+    MX codes sb then [K/32, N]).  fmt_a / fmt_b: element formats of the codes:
+    "e4m3" or "e5m2" in any pairing; "e2m1" for both (FP4 packed two per byte, so
+    qa is [M, K/2] and qb [N, K/2], or [K, N/2] with b_layout "kn" and N even;
+    mode "mx32"); or "e2m3" / "e3m2" for both (FP6, four codes in three bytes:
+    [M, 3K/4] and [N, 3K/4]; mode "mx32", K % 128 == 0).
     bias: float32 [N] CUDA tensor or None;
     activation: "none", "relu", "gelu" or "silu".
     """
