@@ -326,7 +326,8 @@ fp8gemm_status fp8gemm_run_kn(int64_t M, int64_t N, int64_t K, const uint8_t* A,
 /*   TENSOR : scale_a float[1], scale_b float[num_groups].                      */
 /*   ROWWISE: scale_a float[total_m], scale_b float[num_groups*N] (expert-major).*/
 /*   MX32   : scale_a uint8 [total_m][K/32], scale_b uint8 [num_groups][N][K/32]. */
-/* num_groups >= 1, total_m >= 0, other rules as fp8gemm_run.                   */
+/* 1 <= num_groups <= 1024 (more: NOT_SUPPORTED; the persistent kernel keeps   */
+/* per-expert tables in LDS), total_m >= 0, other rules as fp8gemm_run.        */
 /* ------------------------------------------------------------------------- */
 size_t fp8gemm_grouped_workspace_size(int32_t num_groups, int64_t total_m, int64_t N, int64_t K,
                                       int mode);

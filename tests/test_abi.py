@@ -435,6 +435,7 @@ def _grouped(lib, G=8, total_m=256, N=64, K=128, A=P, lda=128, off=P3 + 8192, B=
 def test_grouped_validation(lib):
     assert _grouped(lib, G=0) == INVALID
     assert _grouped(lib, G=2000) == NOT_SUPPORTED
+    assert _grouped(lib, G=1025) == NOT_SUPPORTED          # the documented maximum is 1024
     assert _grouped(lib, mode=5) == INVALID
     assert _grouped(lib, total_m=-1) == INVALID
     assert _grouped(lib, total_m=0) == SUCCESS

@@ -223,3 +223,27 @@ def test_grouped_fp4_cut_tiles_interior(out):
                 fmt_a="e2m1", fmt_b="e2m1")
     torch.cuda.synchronize()
     assert torch.equal(C[r0:r1], Cd)
+
+
+@pytest.mark.parametrize("mode", ["rowwise", "mx32"])
+def test_grouped_max_experts(mode):
+    """The largest expert count the library takes (1024; more return
+    NOT_SUPPORTED): the per-expert tables fill their LDS space; counts of 0 to 12
+    rows (a third of the experts empty), so every tile is cut by its expert's
+    last row."""
+    G = 1024
+    rng = np.random.default_rng(1024)
+    counts = rng.integers(1, 13, G)
+    counts[rng.random(G) < 1 / 3] = 0
+    N, K = 256, 128
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    total = int(off[-1])
+    x = normal(rng, total, K)
+    W = normal(rng, G * N, K, 0.02).reshape(G, N, K)
+    qa, sa = Q.quantize(x, mode)
+    qw, sw = _quant_experts(W, mode)
+    announce("grouped max experts", mode, G, total, N, K)
+    C = F.grouped_gemm(to_dev(qa, 16), scale_to_dev(sa, mode), torch.from_numpy(off).to(DEV),
+                       _dev3(qw), torch.from_numpy(np.ascontiguousarray(sw)).to(DEV), mode, "bf16")
+    Cr, Ar = O.grouped_reference(qa, sa, off, qw, sw, mode)
+    assert_within_bound(to_host(C), Cr, Ar, "bf16", f"grouped {G} experts {mode}")
