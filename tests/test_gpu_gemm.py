@@ -346,3 +346,26 @@ def test_gemm_splitk_growing_tile_count():
         C = to_host(_run_gpu(qa, sa, qb, sb, "rowwise", "bf16"))
         Cr, Ar = O.gemm_reference(qa, sa, qb, sb, "rowwise")
         assert_within_bound(C, Cr, Ar, "bf16", f"split-K after other shapes {(M, N, K)}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape,path", [((300, 256, 256), "tile128"), ((128, 4096, 1024), "splitk")])
+def test_gemm_spans_past_32_bit_offsets(mode, shape, path):
+    """A row pitch of 32 MiB + 64 bytes: the rows of one tile of A (64 for the
+    split-K tiles, 128 for the others) span more than 2^31 bytes, past the 32-bit
+    offsets of the interior mainloop's buffer descriptors, so the tiles take the
+    general mainloop (64-bit row addresses).  Every output element is checked
+    against the oracle."""
+    M, N, K = shape
+    lda = (1 << 25) + 64
+    assert F.fp8gemm_run_path(M, N, K, lda, K, 0, 0, F.SCALE_MODES[mode], 0) == path
+    qa, sa, qb, sb = _oracle_operands(M, N, K, mode, seed=M + N + K)
+    announce("gemm 32-bit spans", mode, shape, lda)
+    a_buf = torch.zeros((M, lda), dtype=torch.uint8, device=DEV)   # 4 GiB or 9.4 GiB
+    a_buf[:, :K] = torch.from_numpy(qa).to(DEV)
+    C = F.gemm(a_buf[:, :K], scale_to_dev(sa, mode), to_dev(qb, 16), scale_to_dev(sb, mode),
+               mode, "bf16")
+    torch.cuda.synchronize()
+    del a_buf
+    Cr, Ar = O.gemm_reference(qa, sa, qb, sb, mode)
+    assert_within_bound(to_host(C), Cr, Ar, "bf16", f"spans {mode} {shape}")
