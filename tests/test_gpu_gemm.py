@@ -349,19 +349,20 @@ def test_gemm_splitk_growing_tile_count():
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("shape,path", [((300, 256, 256), "tile128"), ((128, 4096, 1024), "splitk")])
-def test_gemm_spans_past_32_bit_offsets(mode, shape, path):
-    """A row pitch of 32 MiB + 64 bytes: the rows of one tile of A (64 for the
-    split-K tiles, 128 for the others) span more than 2^31 bytes, past the 32-bit
-    offsets of the interior mainloop's buffer descriptors, so the tiles take the
-    general mainloop (64-bit row addresses).  Every output element is checked
-    against the oracle."""
+@pytest.mark.parametrize("shape,path,lda", [((300, 256, 256), "tile128", (1 << 25) + 64),
+                                            ((128, 4096, 1024), "splitk", (1 << 25) + 64),
+                                            ((4096, 4096, 128), "tile256", (1 << 23) + 64)])
+def test_gemm_spans_past_32_bit_offsets(mode, shape, path, lda):
+    """Row pitches of 32 MiB + 64 bytes (8 MiB + 64 for the 256-row tiles): the
+    rows of one tile of A span more than 2^31 bytes, past the 32-bit offsets of
+    the interior mainloop's buffer descriptors, so the tiles take the general
+    mainloop (64-bit row addresses).  Every output element is checked against
+    the oracle."""
     M, N, K = shape
-    lda = (1 << 25) + 64
     assert F.fp8gemm_run_path(M, N, K, lda, K, 0, 0, F.SCALE_MODES[mode], 0) == path
     qa, sa, qb, sb = _oracle_operands(M, N, K, mode, seed=M + N + K)
     announce("gemm 32-bit spans", mode, shape, lda)
-    a_buf = torch.zeros((M, lda), dtype=torch.uint8, device=DEV)   # 4 GiB or 9.4 GiB
+    a_buf = torch.zeros((M, lda), dtype=torch.uint8, device=DEV)   # 4 to 32 GiB
     a_buf[:, :K] = torch.from_numpy(qa).to(DEV)
     C = F.gemm(a_buf[:, :K], scale_to_dev(sa, mode), to_dev(qb, 16), scale_to_dev(sb, mode),
                mode, "bf16")
