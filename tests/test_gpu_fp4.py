@@ -184,3 +184,25 @@ def test_quantize_fp4_block_maxima_at_binade_edges():
             rows.append(row)
     x = np.stack(rows).astype(np.float32)
     _check_quant(x, "binade edges")
+
+
+@pytest.mark.parametrize("shape,path,lda", [((300, 256, 512), "tile128", (1 << 25) + 64),
+                                            ((4096, 4096, 512), "tile128", (1 << 23) + 64)])
+def test_gemm_fp4_spans_past_32_bit_offsets(shape, path, lda):
+    """MXFP4 A with a row pitch whose tile rows span more than 2^31 bytes: the
+    large tile is not planned (its interior mainloop needs 32-bit spans) and the
+    128-row tiles take the general mainloop with 64-bit row addresses."""
+    M, N, K = shape
+    assert F.fp8gemm_run_path(M, N, K, lda, K // 2, 4, 4, F.SCALE_MODES["mx32"], 0) == path
+    qa, sa, qb, sb = _operands(M, N, K, seed=M + N + K)
+    announce("fp4 32-bit spans", shape, lda)
+    pa = O.pack_fp4(qa)
+    a_buf = torch.zeros((M, lda), dtype=torch.uint8, device=DEV)   # 9.4 or 32 GiB
+    a_buf[:, :K // 2] = torch.from_numpy(pa).to(DEV)
+    C = F.gemm(a_buf[:, :K // 2], scale_to_dev(sa, "mx32"), to_dev(O.pack_fp4(qb), 16),
+               scale_to_dev(sb, "mx32"), "mx32", "bf16", fmt_a="e2m1", fmt_b="e2m1")
+    torch.cuda.synchronize()
+    del a_buf
+    torch.cuda.empty_cache()
+    Cr, Ar = O.gemm_reference(qa, sa, qb, sb, "mx32", fmt_a="e2m1", fmt_b="e2m1")
+    _assert(to_host(C), Cr, Ar, "bf16", f"fp4 spans {shape}")
