@@ -247,3 +247,37 @@ def test_grouped_max_experts(mode):
                        _dev3(qw), torch.from_numpy(np.ascontiguousarray(sw)).to(DEV), mode, "bf16")
     Cr, Ar = O.grouped_reference(qa, sa, off, qw, sw, mode)
     assert_within_bound(to_host(C), Cr, Ar, "bf16", f"grouped {G} experts {mode}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_grouped_spans_past_32_bit_offsets(mode):
+    """A with an 8 MiB + 64 byte row pitch and C with a 4 Mi + 64 element one: a
+    tile's rows of A, and its rows of C, span more than 2^31 bytes, so no tile
+    streams (K % 512 == 0 would allow it) and every tile takes the general
+    mainloop and the staged epilogue with 64-bit row addresses; cut tiles and an
+    empty expert included.  Checked against the oracle; the columns past N keep
+    their canaries."""
+    counts = np.array([300, 0, 257])
+    N, K = 256, 512
+    lda, ldc = (1 << 23) + 64, (1 << 22) + 64
+    rng = np.random.default_rng(2 ** 23)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    total = int(off[-1])
+    x = normal(rng, total, K)
+    W = np.stack([normal(rng, N, K, 0.02) for _ in counts])
+    qa, sa = Q.quantize(x, mode)
+    qw, sw = _quant_experts(W, mode)
+    announce("grouped 32-bit spans", mode, counts.tolist(), lda, ldc)
+    a_buf = torch.zeros((total, lda), dtype=torch.uint8, device=DEV)          # 4.7 GiB
+    a_buf[:, :K] = torch.from_numpy(qa).to(DEV)
+    c_buf = torch.full((total, ldc), -7.0, dtype=torch.bfloat16, device=DEV)  # 4.7 GiB
+    C = F.grouped_gemm(a_buf[:, :K], scale_to_dev(sa, mode), torch.from_numpy(off).to(DEV),
+                       _dev3(qw), torch.from_numpy(np.ascontiguousarray(sw)).to(DEV), mode, "bf16",
+                       out=c_buf[:, :N])
+    torch.cuda.synchronize()
+    assert bool((c_buf[:, N:N + 64] == -7.0).all())
+    Ch = to_host(C)
+    del a_buf, c_buf, C
+    torch.cuda.empty_cache()
+    Cr, Ar = O.grouped_reference(qa, sa, off, qw, sw, mode)
+    assert_within_bound(Ch, Cr, Ar, "bf16", f"grouped spans {mode}")
