@@ -73,3 +73,42 @@ def test_hot_path_graph_replays(mode, shape):
         torch.cuda.synchronize()
         assert torch.equal(C, ref[4])
     del graph
+
+
+def test_grouped_graph_follows_device_offsets():
+    """The grouped GEMM reads its expert offsets on the device, so one captured
+    graph serves changing expert counts: after new offsets are copied into the
+    same tensor, a replay gives the eager result for the new counts, bit for bit."""
+    G, N, K, total = 8, 512, 512, 2048
+    gen = torch.Generator(device=DEV).manual_seed(8)
+    qa, sa = F.quantize(torch.randn(total, K, device=DEV, generator=gen), "rowwise")
+    w = torch.randn(G * N, K, device=DEV, generator=gen) * 0.02
+    qw, sw = F.quantize(w, "rowwise")
+    qw, sw = qw.reshape(G, N, K), sw.reshape(G, N)
+    sets = [np.array([256, 256, 256, 256, 256, 256, 256, 256]),
+            np.array([1, 700, 0, 300, 47, 600, 250, 150]),
+            np.array([2048, 0, 0, 0, 0, 0, 0, 0])]
+    offs = [torch.from_numpy(np.concatenate([[0], np.cumsum(c)]).astype(np.int32)).to(DEV)
+            for c in sets]
+    announce("grouped graph", [c.tolist() for c in sets])
+    eager = [F.grouped_gemm(qa, sa, o, qw, sw, "rowwise", "bf16") for o in offs]
+    offsets = offs[0].clone()
+    C = torch.empty((total, N), dtype=torch.bfloat16, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        F.grouped_gemm(qa, sa, offsets, qw, sw, "rowwise", "bf16", out=C)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        F.grouped_gemm(qa, sa, offsets, qw, sw, "rowwise", "bf16", out=C)
+    torch.cuda.synchronize()
+    for r in (0, 1, 2, 1, 0):
+        offsets.copy_(offs[r])
+        C.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C, eager[r]), f"counts {sets[r].tolist()}"
+    del graph
